@@ -1,0 +1,383 @@
+"""Pins for the CPU oracle: each check ties an oracle step to something other
+than the oracle itself -- closed forms, brute-force enumeration, a library
+routine (torch scaled-dot-product attention in float64), hand-derived golden
+fixtures.  A plausible mistake in any oracle step (dropped term, wrong sign or
+index, transposed operand, wrong summation order, wrong tie-break, '>' for
+'>=') fails at least one of them.  CPU only.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bf(x):
+    return synth.to_bf16(np.asarray(x, np.float32))
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding used by the projection (round to nearest, ties to even)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("x,bits", [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),                  # exact midpoint, even below
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),              # exact midpoint, even above
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),     # just above the midpoint
+    (-1.0 - 2.0 ** -8 - 2.0 ** -20, 0xBF81),
+    (0.0, 0x0000),
+    (-0.0, 0x8000),
+])
+def test_bf16_rne(x, bits):
+    assert oracle.f32_to_bf16(np.float32(x)) == bits
+
+
+# --------------------------------------------------------------------------
+# projection: fp32 FMA chain over d ascending, one bf16 rounding
+# --------------------------------------------------------------------------
+
+def test_projection_integer_inputs_equal_exact_matmul():
+    # small integers: every partial sum is exact in fp32, so the chain equals
+    # the integer product; catches dropped terms, wrong index, transposed W
+    g = np.random.default_rng(0)
+    x = g.integers(-3, 4, (37, 64)).astype(np.float32)
+    W = g.integers(-2, 3, (64, 16)).astype(np.float32)
+    got = synth.from_bf16(oracle.project(x, W))
+    exact = (x.astype(np.int64) @ W.astype(np.int64)).astype(np.float32)
+    np.testing.assert_array_equal(got, synth.from_bf16(bf(exact)))
+
+
+def test_projection_selector_picks_low_frequency_coordinates():
+    # noise-free selector W: column 2m reads dim D/2-8+m, column 2m+1 reads
+    # dim D-8+m, so q_low is the bf16 of those coordinates exactly
+    for D in (64, 128):
+        W = np.zeros((D, 16), np.float32)
+        dims = synth.low_freq_dims(D)
+        W[dims, np.arange(16)] = 1.0
+        x = np.random.default_rng(D).standard_normal((5, D)).astype(np.float32)
+        got = oracle.project(x, W)
+        np.testing.assert_array_equal(got, bf(x[:, dims]))
+        assert list(dims[:4]) == [D // 2 - 8, D - 8, D // 2 - 7, D - 7]
+
+
+def test_projection_order_is_d_ascending():
+    # x = [2^24, 1, -2^24]: ascending chain gives fl(2^24 + 1) = 2^24 (tie to
+    # even), then 0; any other order or a wider accumulator gives 1
+    x = np.zeros((1, 64), np.float32)
+    x[0, :3] = [2.0 ** 24, 1.0, -(2.0 ** 24)]
+    W = np.zeros((64, 16), np.float32)
+    W[:3, :] = 1.0
+    assert np.all(synth.from_bf16(oracle.project(x, W)) == 0.0)
+    x[0, :3] = [-(2.0 ** 24), 1.0, 2.0 ** 24]      # reversed: exact partial sums
+    assert np.all(synth.from_bf16(oracle.project(x, W)) == 1.0)
+
+
+def test_projection_is_fused():
+    # acc = -(1+2^-11); x*w = (1+2^-12)^2 = 1 + 2^-11 + 2^-24.
+    # fused: acc + x*w = 2^-24 exactly.  Unfused: fl(x*w) = 1 + 2^-11 (tie to
+    # even), giving 0.
+    x = np.zeros((1, 64), np.float32)
+    W = np.zeros((64, 16), np.float32)
+    x[0, 0], W[0, :] = -(1.0 + 2.0 ** -11), 1.0
+    x[0, 1], W[1, :] = 1.0 + 2.0 ** -12, 1.0 + 2.0 ** -12
+    got = synth.from_bf16(oracle.project(x, W))
+    assert np.all(got == np.float32(2.0 ** -24))
+
+
+# --------------------------------------------------------------------------
+# indexer scores: fp32 chain over c = 0..15 of exact bf16 products
+# --------------------------------------------------------------------------
+
+def test_scores_integer_equal_exact_dot():
+    g = np.random.default_rng(1)
+    q = g.integers(-8, 9, 16).astype(np.float32)
+    k = g.integers(-8, 9, (100, 16)).astype(np.float32)
+    d = oracle.scores(bf(q), bf(k))
+    np.testing.assert_array_equal(d, (k.astype(np.int64) @ q.astype(np.int64)).astype(np.float32))
+
+
+def test_scores_order_is_c_ascending():
+    q = np.zeros(16, np.float32)
+    q[:3] = [2.0 ** 24, 1.0, -(2.0 ** 24)]
+    k = np.ones((2, 16), np.float32)
+    k[1, :3] = [-1.0, 1.0, -1.0]   # reversed signs: -2^24 + 1 - (-2^24)... see below
+    d = oracle.scores(bf(q), bf(k))
+    assert d[0] == 0.0             # fl(2^24 + 1) = 2^24, then 0
+    # row 1: products [-2^24, 1, 2^24]: -2^24 + 1 is exact, then + 2^24 = 1
+    assert d[1] == 1.0
+
+
+def test_scores_product_exactness_guard():
+    q = np.zeros(16, np.float32)
+    q[0] = 2.0 ** -100
+    k = np.zeros((1, 16), np.float32)
+    k[0, 0] = 2.0 ** -100          # product underflows fp32: not exact
+    with pytest.raises(ArithmeticError):
+        oracle.scores(bf(q), bf(k))
+
+
+def test_scores_fma_equals_mul_add_on_workload_data():
+    # bf16 x bf16 products are exact in fp32, so a mul-then-add chain gives
+    # the same bits as the fused chain on real workload data
+    w = synth.small(2)
+    r, h = 0, w.ret_heads[0]
+    g = w.kv_head(h)
+    q_low = oracle.project(w.q[0, h][None], w.w_q[r])[0]
+    k_low = oracle.project(w.k[0][:500, g, :], w.w_k[r])
+    d = oracle.scores(q_low, k_low)
+    qf = synth.from_bf16(q_low)
+    kf = synth.from_bf16(k_low)
+    acc = np.zeros(500, np.float32)
+    for c in range(16):
+        acc = (acc + (qf[c] * kf[:, c]).astype(np.float32)).astype(np.float32)
+    np.testing.assert_array_equal(d, acc)
+
+
+# --------------------------------------------------------------------------
+# top-p selection
+# --------------------------------------------------------------------------
+
+def test_topp_golden_closed_forms():
+    with open(os.path.join(GOLDEN, "topp_closed_form.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        d = np.asarray(case["d"], np.float32)
+        for p, want in case["select"]:
+            sel, order, cum = oracle.topp(d, case["s"], p)
+            assert list(sel) == want, (case["d"], p)
+            np.testing.assert_allclose(cum, case["cum"], rtol=2e-7)
+
+
+def _brute(d, s, p):
+    """Minimal cardinality reaching mass p, by enumerating every subset."""
+    n = len(d)
+    w = np.exp(s * (d.astype(np.float64) - d.max()))
+    Z = w.sum()
+    for k in range(1, n + 1):
+        best, best_sets = -1.0, []
+        for sub in itertools.combinations(range(n), k):
+            m = w[list(sub)].sum()
+            if m > best + 1e-15:
+                best, best_sets = m, [sub]
+            elif abs(m - best) <= 1e-15:
+                best_sets.append(sub)
+        if best / Z >= p:
+            return k, best / Z, min(best_sets)
+    return n, 1.0, tuple(range(n))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topp_brute_force_tiny(seed):
+    # integer scores with frequent ties; every subset is enumerated.  The
+    # oracle's set must have the minimal size reaching p, maximal mass for that
+    # size, and among equal-mass sets the one with the lowest indices.
+    g = np.random.default_rng(seed)
+    n = int(g.integers(1, 11))
+    d = g.integers(-3, 4, n).astype(np.float32) * 2.0
+    s = [0.25, 0.5, 1.0][seed % 3]
+    for p in (0.05, 0.3, 0.5, 0.62, 0.9, 0.97, 1.0):
+        k, mass, lexmin = _brute(d, s, np.float32(p))
+        sel, order, cum = oracle.topp(d, s, p)
+        if np.any(np.abs(np.asarray(cum) - np.float32(p)) < 1e-12):
+            continue                      # a cumulative mass sits on p: skip
+        assert len(sel) == k
+        assert tuple(sel) == lexmin
+        w = np.exp(s * (d.astype(np.float64) - d.max()))
+        assert abs(w[sel].sum() / w.sum() - mass) < 1e-12
+
+
+def test_topp_invariants_on_workload_scores():
+    w = synth.small(5)
+    t, r = 3, 1
+    h = w.ret_heads[r]
+    g = w.kv_head(h)
+    pos = w.row_pos(t)
+    res = oracle.retrieval_row(w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], w.w_q[r], w.w_k[r],
+                               pos, w.idx_scale, 0.9, w.attn_scale)
+    d = res["d"]
+    prev = None
+    for p in (1e-7, 0.3, 0.8, 0.9, 0.95, 0.99, 0.999, 1.0):
+        sel, order, cum = oracle.topp(d, 0.25, p)
+        k = len(sel)
+        # C_k >= p > C_{k-1}
+        if p < 1:
+            assert cum[k - 1] >= np.float32(p)
+            if k > 1:
+                assert cum[k - 2] < np.float32(p)
+        else:
+            assert k == len(d)
+        # the set is the first k of the rank order, ascending
+        assert list(sel) == sorted(order[:k])
+        # rank order: scores descending, ties by lower index
+        ds = d[order]
+        assert np.all(ds[:-1] >= ds[1:])
+        tie = ds[:-1] == ds[1:]
+        assert np.all(order[:-1][tie] < order[1:][tie])
+        # nesting in p
+        if prev is not None:
+            assert set(prev) <= set(sel)
+        prev = sel
+    # p -> 0 keeps only the best key, lowest index among equals
+    sel, _, _ = oracle.topp(d, 0.25, 1e-7)
+    assert list(sel) == [int(np.flatnonzero(d == d.max())[0])]
+    # cumulative mass is increasing and ends at 1
+    assert np.all(np.diff(cum) >= 0) and abs(cum[-1] - 1.0) < 1e-12
+
+
+def test_topp_p_one_keeps_all_and_rejects_bad_p():
+    d = np.asarray([0.0, 1.0, -5.0, 1.0], np.float32)
+    sel, _, _ = oracle.topp(d, 0.25, 1.0)
+    assert list(sel) == [0, 1, 2, 3]
+    for bad in (0.0, -0.5, float("nan")):
+        with pytest.raises(ValueError):
+            oracle.topp(d, 0.25, bad)
+
+
+def test_topp_negative_zero_equals_positive_zero():
+    d = np.asarray([-0.0, 0.0, -1.0], np.float32)
+    sel, order, _ = oracle.topp(d, 0.25, 0.3)
+    assert list(order[:2]) == [0, 1] and list(sel) == [0]
+
+
+def test_identity_projection_ranks_like_full_attention():
+    # D = 16 and W = I: the indexer sees q and k themselves.  With
+    # idx_scale = attn_scale = 1/4 its top-p set must be the top-p set of the
+    # exact attention probabilities (torch softmax, float64).
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(7)
+    eye = np.eye(16, dtype=np.float32)
+    for trial in range(20):
+        L = int(g.integers(5, 300))
+        q = g.integers(-4, 5, 16).astype(np.float32)
+        K = g.integers(-4, 5, (L, 16)).astype(np.float32)
+        V = g.standard_normal((L, 16)).astype(np.float32)
+        q_low = oracle.project(q[None], eye)[0]
+        k_low = oracle.project(K, eye)
+        np.testing.assert_array_equal(synth.from_bf16(k_low), K)
+        d = oracle.scores(q_low, k_low)
+        probs = torch.softmax(torch.from_numpy(K.astype(np.float64)) @ torch.from_numpy(
+            q.astype(np.float64)) * 0.25, dim=0).numpy()
+        rank = sorted(range(L), key=lambda j: (-probs[j], j))
+        for p in (0.5, 0.9, 0.95):
+            sel, order, cum = oracle.topp(d, 0.25, p)
+            acc, k = 0.0, 0
+            while acc < np.float32(p) and k < L:
+                acc += probs[rank[k]]
+                k += 1
+            if min(abs(np.cumsum(probs[rank]) - np.float32(p))) < 1e-9:
+                continue
+            assert list(sel) == sorted(rank[:k])
+            out = oracle.attend(q, K, V, sel, 0.25)
+            mask = torch.full((1, L), float("-inf"), dtype=torch.float64)
+            mask[0, torch.from_numpy(sel.astype(np.int64))] = 0.0
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q.astype(np.float64))[None, None, None],
+                torch.from_numpy(K.astype(np.float64))[None, None],
+                torch.from_numpy(V.astype(np.float64))[None, None],
+                attn_mask=mask[None, None], scale=0.25)[0, 0, 0].numpy()
+            np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# attention over a set, window sets, dense
+# --------------------------------------------------------------------------
+
+def _sdpa(q, K, V, idx, scale):
+    torch = pytest.importorskip("torch")
+    L = K.shape[0]
+    mask = torch.full((1, L), float("-inf"), dtype=torch.float64)
+    mask[0, torch.from_numpy(np.asarray(idx, np.int64))] = 0.0
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(np.asarray(q, np.float64))[None, None, None],
+        torch.from_numpy(np.asarray(K, np.float64))[None, None],
+        torch.from_numpy(np.asarray(V, np.float64))[None, None],
+        attn_mask=mask[None, None], scale=scale)[0, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_attend_matches_torch_sdpa(D):
+    g = np.random.default_rng(D)
+    L = 700
+    q = g.standard_normal(D).astype(np.float32)
+    K = (g.standard_normal((L, D)) * 2).astype(np.float32)
+    V = g.standard_normal((L, D)).astype(np.float32)
+    scale = 1 / math.sqrt(D)
+    for idx in (np.arange(L), np.sort(g.choice(L, 37, replace=False)), oracle.window_set(L - 1, 64, 4)):
+        out = oracle.attend(q, K, V, idx.astype(np.int32), scale)
+        np.testing.assert_allclose(out, _sdpa(q, K, V, idx, scale), rtol=1e-12, atol=1e-13)
+
+
+def test_attend_single_key_and_equal_keys():
+    g = np.random.default_rng(3)
+    K = g.standard_normal((50, 64)).astype(np.float32)
+    V = g.standard_normal((50, 64)).astype(np.float32)
+    q = g.standard_normal(64).astype(np.float32)
+    out = oracle.attend(q, K, V, np.asarray([17], np.int32), 0.125)
+    np.testing.assert_array_equal(out, V[17].astype(np.float64))
+    K[:] = K[0]
+    idx = np.asarray([1, 5, 9, 30], np.int32)
+    out = oracle.attend(q, K, V, idx, 0.125)
+    np.testing.assert_allclose(out, V[idx].astype(np.float64).mean(0), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("pos,W,Ns,want", [
+    (10, 3, 2, [0, 1, 8, 9, 10]),
+    (3, 3, 2, [0, 1, 2, 3]),
+    (0, 5, 4, [0]),
+    (6, 1, 0, [6]),
+    (6, 100, 0, list(range(7))),
+    (9, 2, 9, list(range(10))),
+])
+def test_window_set_closed_forms(pos, W, Ns, want):
+    assert list(oracle.window_set(pos, W, Ns)) == want
+
+
+def test_p_one_is_dense_and_long_window_is_dense():
+    # p = 1 keeps every key and a window at least as long as the sequence
+    # covers every key: both reproduce dense causal attention bit for bit
+    w = synth.small(2)
+    t, r = 1, 2
+    h = w.ret_heads[r]
+    g = w.kv_head(h)
+    pos = w.row_pos(t)
+    K, V = w.k[t][:, g, :], w.v[t][:, g, :]
+    dense = oracle.dense_row(w.q[t, h], K, V, pos, w.attn_scale)
+    res = oracle.retrieval_row(w.q[t, h], K, V, w.w_q[r], w.w_k[r], pos, w.idx_scale, 1.0,
+                               w.attn_scale)
+    assert len(res["sel"]) == pos + 1
+    np.testing.assert_array_equal(res["out"], dense)
+    for win in (pos + 1, pos + 1000):
+        np.testing.assert_array_equal(oracle.local_row(w.q[t, h], K, V, pos, win, 3, w.attn_scale),
+                                      dense)
+    np.testing.assert_allclose(dense, _sdpa(synth.as_f32(w.q[t, h]), synth.as_f32(K[: pos + 1]),
+                                            synth.as_f32(V[: pos + 1]), np.arange(pos + 1),
+                                            w.attn_scale), rtol=1e-11, atol=1e-12)
+
+
+def test_needles_are_found_exactly():
+    # fp32 needle workload: the 8 needle keys are identical, so they tie in
+    # score; when their mass reaches p they are exactly the selected set
+    w = synth.small(1)
+    found = 0
+    for r, h in enumerate(w.ret_heads):
+        g = w.kv_head(h)
+        res = oracle.retrieval_row(w.q[0, h], w.k[0][:, g, :], w.v[0][:, g, :], w.w_q[r],
+                                   w.w_k[r], w.row_pos(0), w.idx_scale, 0.9, w.attn_scale)
+        nd = w.info["needles"][(0, h)]
+        d = res["d"]
+        assert np.all(d[nd] == d[nd[0]])               # exact tie group
+        assert d[nd[0]] == d.max()
+        if res["cum"][len(nd) - 1] >= np.float32(0.9):
+            assert list(res["sel"]) == list(nd)
+            found += 1
+        else:
+            assert set(nd) <= set(res["sel"])
+    assert found >= 1
