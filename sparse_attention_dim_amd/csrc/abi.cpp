@@ -1,0 +1,377 @@
+// abi.cpp -- the extern "C" entry points of librtp: host-side argument checks,
+// workspace layout and kernel launches on the caller's stream.  No entry point
+// allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/rtp.h"
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+rtp_status fail(rtp_status code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+rtp_status ok() {
+    g_err.clear();
+    return RTP_OK;
+}
+
+rtp_status hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(RTP_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+constexpr int kMaxLen = 1 << 22;          // longest supported context
+constexpr int kMaxDecodeRows = 4096;      // decode rows (batch * num_ret) of the sparse kernel
+constexpr int kWinSplit = 256;            // keys per workgroup, local-head decode
+constexpr int kDenseSplit = 512;          // keys per workgroup, dense decode
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+rtp_status check_layer(const rtp_layer* L) {
+    if (!L) return fail(RTP_EINVAL, "layer is NULL");
+    if (L->num_q_heads < 1 || L->num_kv_heads < 1 || L->num_q_heads % L->num_kv_heads)
+        return fail(RTP_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                    L->num_q_heads, L->num_kv_heads);
+    if (L->num_q_heads > 256) return fail(RTP_EUNSUPPORTED, "num_q_heads > 256");
+    if (L->num_q_heads / L->num_kv_heads > 8) return fail(RTP_EUNSUPPORTED, "more than 8 query heads per KV head");
+    if (L->head_dim != 64 && L->head_dim != 128)
+        return fail(RTP_EUNSUPPORTED, "head_dim %d (supported: 64, 128)", L->head_dim);
+    if (L->dtype != RTP_F32 && L->dtype != RTP_BF16) return fail(RTP_EINVAL, "dtype %d", L->dtype);
+    if (L->num_ret < 1 || L->num_ret > RTP_MAX_RET)
+        return fail(RTP_EINVAL, "num_ret %d out of [1, %d]", L->num_ret, RTP_MAX_RET);
+    for (int r = 0; r < L->num_ret; ++r) {
+        const int h = L->ret_heads[r];
+        if (h < 0 || h >= L->num_q_heads) return fail(RTP_EINVAL, "ret_heads[%d] = %d out of range", r, h);
+        if (r && h <= L->ret_heads[r - 1]) return fail(RTP_EINVAL, "ret_heads must be strictly ascending");
+    }
+    if (L->window < 1) return fail(RTP_EINVAL, "window %d < 1", L->window);
+    if (L->num_sinks < 0) return fail(RTP_EINVAL, "num_sinks %d < 0", L->num_sinks);
+    if (!(L->attn_scale > 0.0f) || !std::isfinite(L->attn_scale)) return fail(RTP_EINVAL, "attn_scale");
+    if (!(L->idx_scale > 0.0f) || !std::isfinite(L->idx_scale)) return fail(RTP_EINVAL, "idx_scale");
+    return RTP_OK;
+}
+
+rtp_status check_cache(const rtp_cache* C) {
+    if (!C) return fail(RTP_EINVAL, "cache is NULL");
+    if (!C->k || !C->v || !C->k_low || !C->block_table || !C->seq_lens)
+        return fail(RTP_EINVAL, "cache has a NULL pointer");
+    if (C->batch < 1) return fail(RTP_EINVAL, "batch %d < 1", C->batch);
+    if (C->max_seq_len < 1 || C->max_seq_len > kMaxLen)
+        return fail(RTP_EUNSUPPORTED, "max_seq_len %d out of [1, %d]", C->max_seq_len, kMaxLen);
+    if (C->max_blocks < 1 || (int64_t)C->max_blocks * RTP_BLOCK < C->max_seq_len)
+        return fail(RTP_EINVAL, "max_blocks %d cannot hold max_seq_len %d", C->max_blocks, C->max_seq_len);
+    return RTP_OK;
+}
+
+rtp_status check_query(const rtp_cache* C, const rtp_query* Q) {
+    if (!Q) return fail(RTP_EINVAL, "query is NULL");
+    if (!Q->q) return fail(RTP_EINVAL, "query q is NULL");
+    if (Q->n_tok < 1) return fail(RTP_EINVAL, "n_tok %d < 1", Q->n_tok);
+    if (Q->kind == RTP_DECODE) {
+        if (Q->n_tok != C->batch) return fail(RTP_EINVAL, "decode n_tok %d != batch %d", Q->n_tok, C->batch);
+    } else if (Q->kind == RTP_CHUNK) {
+        if (Q->seq < 0 || Q->seq >= C->batch) return fail(RTP_EINVAL, "chunk seq %d out of range", Q->seq);
+        if (Q->pos0 < 0 || (int64_t)Q->pos0 + Q->n_tok > C->max_seq_len)
+            return fail(RTP_EINVAL, "chunk rows [%d, %d) exceed max_seq_len %d", Q->pos0, Q->pos0 + Q->n_tok,
+                        C->max_seq_len);
+    } else {
+        return fail(RTP_EINVAL, "query kind %d", Q->kind);
+    }
+    return RTP_OK;
+}
+
+rtp_status check_all(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
+    rtp_status s = check_layer(L);
+    if (s) return s;
+    if ((s = check_cache(C))) return s;
+    return check_query(C, Q);
+}
+
+rtp::Geo make_geo(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
+    rtp::Geo g;
+    std::memset(&g, 0, sizeof g);
+    g.Hq = L->num_q_heads;
+    g.Hkv = L->num_kv_heads;
+    g.D = L->head_dim;
+    g.group = g.Hq / g.Hkv;
+    g.n_ret = L->num_ret;
+    for (int r = 0; r < L->num_ret; ++r) {
+        g.ret_heads[r] = L->ret_heads[r];
+        g.is_ret[L->ret_heads[r]] = 1;
+    }
+    g.window = L->window;
+    g.sinks = L->num_sinks;
+    g.attn_scale = L->attn_scale;
+    g.idx_scale = L->idx_scale;
+    if (Q) {
+        g.kind = Q->kind;
+        g.seq = Q->seq;
+        g.pos0 = Q->pos0;
+        g.n_tok = Q->n_tok;
+    }
+    g.batch = C->batch;
+    g.max_blocks = C->max_blocks;
+    g.max_seq_len = C->max_seq_len;
+    g.block_table = C->block_table;
+    g.seq_lens = C->seq_lens;
+    return g;
+}
+
+// keys of the longest row of the call
+int64_t max_keys(const rtp_cache* C, const rtp_query* Q) {
+    return Q->kind == RTP_DECODE ? C->max_seq_len : (int64_t)Q->pos0 + Q->n_tok;
+}
+
+// ---- selection workspace ----------------------------------------------------
+
+constexpr size_t kScoreBudget = (size_t)4 << 30;   // bytes of scores per row group
+
+struct SelPlan {
+    int rows_total, group_rows, nchunk;
+    int64_t lpad;
+    size_t off_scores, off_cmax, off_qlow, off_hmass, off_hcnt, off_st, off_ctr, off_ctr2, off_gctr,
+        off_cand, off_cand_n, off_chunk, total;
+};
+
+SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
+    SelPlan p;
+    p.rows_total = Q->n_tok * L->num_ret;
+    const int64_t keys = max_keys(C, Q);
+    p.nchunk = (int)((keys + rtp::kChunk - 1) / rtp::kChunk);
+    p.lpad = (int64_t)p.nchunk * rtp::kChunk;
+    const int64_t by_budget = std::max<int64_t>(1, (int64_t)(kScoreBudget / ((size_t)p.lpad * 4)));
+    p.group_rows = (int)std::min<int64_t>({(int64_t)p.rows_total, by_budget, (int64_t)65535});
+    const size_t G = (size_t)p.group_rows;
+    size_t o = 0;
+    p.off_scores = o; o = align256(o + G * (size_t)p.lpad * 4);
+    p.off_cmax = o; o = align256(o + G * (size_t)p.nchunk * 4);
+    p.off_qlow = o; o = align256(o + G * 16 * 2);
+    p.off_hmass = o; o = align256(o + G * rtp::kNB1 * 8);
+    p.off_hcnt = o; o = align256(o + G * rtp::kNB1 * 4);
+    p.off_st = o; o = align256(o + G * sizeof(rtp::RowState));
+    p.off_ctr = o; o = align256(o + G * 4);
+    p.off_ctr2 = o; o = align256(o + G * 4);
+    p.off_gctr = o; o = align256(o + 4);
+    p.off_cand = o; o = align256(o + G * rtp::kCand * 8);
+    p.off_cand_n = o; o = align256(o + G * 4);
+    p.off_chunk = o; o = align256(o + G * (size_t)p.nchunk * 4);
+    p.total = o;
+    return p;
+}
+
+rtp::SelWs sel_ws(const SelPlan& p, char* base) {
+    rtp::SelWs w;
+    w.scores = (float*)(base + p.off_scores);
+    w.score_ld = p.lpad;
+    w.cmax = (uint32_t*)(base + p.off_cmax);
+    w.qlow = (uint16_t*)(base + p.off_qlow);
+    w.hmass = (unsigned long long*)(base + p.off_hmass);
+    w.hcnt = (uint32_t*)(base + p.off_hcnt);
+    w.st = (rtp::RowState*)(base + p.off_st);
+    w.ctr = (uint32_t*)(base + p.off_ctr);
+    w.ctr2 = (uint32_t*)(base + p.off_ctr2);
+    w.gctr = (uint32_t*)(base + p.off_gctr);
+    w.cand = (unsigned long long*)(base + p.off_cand);
+    w.cand_n = (uint32_t*)(base + p.off_cand_n);
+    w.chunk_cnt = (uint32_t*)(base + p.off_chunk);
+    w.nchunk = p.nchunk;
+    w.rows = p.group_rows;
+    return w;
+}
+
+// ---- decode attention workspaces --------------------------------------------
+
+int64_t sparse_max_items(const rtp_layer* L, const rtp_query* Q, int64_t capacity) {
+    const int64_t rows = (int64_t)Q->n_tok * L->num_ret;
+    return rows + capacity / 128 + 1;
+}
+
+int win_keys(const rtp_layer* L, const rtp_cache* C, int dense) {
+    if (dense) return C->max_seq_len;
+    return (int)std::min<int64_t>((int64_t)L->window + L->num_sinks, C->max_seq_len);
+}
+
+size_t win_ws_bytes(const rtp_layer* L, const rtp_cache* C, int dense) {
+    const int split = dense ? kDenseSplit : kWinSplit;
+    const int nsplit = (win_keys(L, C, dense) + split - 1) / split;
+    return align256((size_t)C->batch * L->num_q_heads * nsplit * (L->head_dim + 2) * 4);
+}
+
+rtp_status window_like(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q, void* out, void* ws,
+                       size_t ws_bytes, void* stream, int dense) {
+    rtp_status s = check_all(L, C, Q);
+    if (s) return s;
+    if (!out) return fail(RTP_EINVAL, "out is NULL");
+    if (Q->kind != RTP_DECODE)
+        return fail(RTP_EUNSUPPORTED, "%s attention of chunked queries is not built in this library version",
+                    dense ? "dense" : "window");
+    const size_t need = win_ws_bytes(L, C, dense);
+    if (!ws || ws_bytes < need) return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+    const rtp::Geo g = make_geo(L, C, Q);
+    const int split = dense ? kDenseSplit : kWinSplit;
+    const int nsplit = (win_keys(L, C, dense) + split - 1) / split;
+    return hip_status(rtp::launch_window_decode(g, Q->q, C->k, C->v, out, (float*)ws, nsplit, split, dense,
+                                                L->dtype, (hipStream_t)stream),
+                      dense ? "dense decode launch" : "window decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int rtp_version(void) { return RTP_VERSION; }
+
+const char* rtp_last_error(void) { return g_err.c_str(); }
+
+rtp_status rtp_indexer_append(const rtp_layer* layer, const rtp_cache* cache, const void* w_k,
+                              const int32_t* seq_id, const int32_t* pos, int32_t n, void* stream) {
+    rtp_status s = check_layer(layer);
+    if (s) return s;
+    if ((s = check_cache(cache))) return s;
+    if (n < 0) return fail(RTP_EINVAL, "n %d < 0", n);
+    if (n == 0) return ok();
+    if (!w_k || !seq_id || !pos) return fail(RTP_EINVAL, "NULL w_k / seq_id / pos");
+    const rtp::Geo g = make_geo(layer, cache, nullptr);
+    return hip_status(rtp::launch_indexer_append(g, cache->k, cache->k_low, w_k, seq_id, pos, n, layer->dtype,
+                                                 (hipStream_t)stream),
+                      "indexer append launch");
+}
+
+size_t rtp_topp_select_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
+    if (check_all(layer, cache, query)) return 0;
+    return plan_select(layer, cache, query).total;
+}
+
+rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                           const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    if (!w_q || !top_p) return fail(RTP_EINVAL, "NULL w_q / top_p");
+    if (!sel || !sel->row_ptr || !sel->status || (sel->capacity > 0 && !sel->idx) || sel->capacity < 0)
+        return fail(RTP_EINVAL, "bad selection buffers");
+    const SelPlan p = plan_select(layer, cache, query);
+    if (!workspace || workspace_bytes < p.total)
+        return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, p.total);
+    const rtp::Geo g = make_geo(layer, cache, query);
+    rtp::SelOut out{sel->row_ptr, sel->idx, sel->capacity, sel->status};
+    rtp::SelWs w = sel_ws(p, (char*)workspace);
+    for (int row0 = 0; row0 < p.rows_total; row0 += p.group_rows) {
+        w.rows = std::min(p.group_rows, p.rows_total - row0);
+        hipError_t e = rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p, row0, w, out,
+                                          p.rows_total, layer->dtype, 0, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e, "top-p select launch");
+    }
+    return ok();
+}
+
+rtp_status rtp_indexer_scores(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                              const void* w_q, uint16_t* q_low, float* scores, int64_t score_ld,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    if (!w_q || !q_low || !scores) return fail(RTP_EINVAL, "NULL w_q / q_low / scores");
+    if (score_ld < max_keys(cache, query)) return fail(RTP_EINVAL, "score_ld %lld too small", (long long)score_ld);
+    const SelPlan p = plan_select(layer, cache, query);
+    rtp::SelWs w;
+    std::memset(&w, 0, sizeof w);
+    w.scores = scores;
+    w.score_ld = score_ld;
+    w.qlow = q_low;
+    w.nchunk = p.nchunk;
+    w.rows = p.rows_total;
+    if (p.rows_total > 65535) return fail(RTP_EUNSUPPORTED, "more than 65535 rows");
+    rtp::SelOut out{nullptr, nullptr, 0, nullptr};
+    const rtp::Geo g = make_geo(layer, cache, query);
+    return hip_status(rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, nullptr, 0, w, out,
+                                         p.rows_total, layer->dtype, 1, (hipStream_t)stream),
+                      "indexer score launch");
+}
+
+size_t rtp_sparse_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                 int64_t capacity) {
+    if (check_all(layer, cache, query) || capacity < 0) return 0;
+    const int64_t rows = (int64_t)query->n_tok * layer->num_ret;
+    const int64_t items = sparse_max_items(layer, query, capacity);
+    return align256((size_t)items * (layer->head_dim + 2) * 4) + align256((size_t)(rows + 1) * 4);
+}
+
+rtp_status rtp_sparse_attn_decode(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                  const rtp_sel* sel, void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    if (query->kind != RTP_DECODE) return fail(RTP_EINVAL, "rtp_sparse_attn_decode needs RTP_DECODE queries");
+    if (!sel || !sel->row_ptr || !sel->status || !out) return fail(RTP_EINVAL, "NULL selection / out");
+    if (sel->capacity > 0 && !sel->idx) return fail(RTP_EINVAL, "NULL idx");
+    const int rows = query->n_tok * layer->num_ret;
+    if (rows > kMaxDecodeRows) return fail(RTP_EUNSUPPORTED, "batch * num_ret %d > %d", rows, kMaxDecodeRows);
+    const size_t need = rtp_sparse_attn_workspace(layer, cache, query, sel->capacity);
+    if (!workspace || workspace_bytes < need)
+        return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    const int64_t items = sparse_max_items(layer, query, sel->capacity);
+    rtp::AttnWs w;
+    w.part = (float*)workspace;
+    w.item_start = (int32_t*)((char*)workspace + align256((size_t)items * (layer->head_dim + 2) * 4));
+    w.max_items = items;
+    const rtp::Geo g = make_geo(layer, cache, query);
+    return hip_status(rtp::launch_sparse_decode(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
+                                                sel->status, out, w, rows, layer->dtype, (hipStream_t)stream),
+                      "sparse decode launch");
+}
+
+rtp_status rtp_sparse_attn_prefill(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                   const rtp_sel* sel, void* out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+    (void)sel;
+    (void)out;
+    (void)workspace;
+    (void)workspace_bytes;
+    (void)stream;
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    if (query->kind != RTP_CHUNK) return fail(RTP_EINVAL, "rtp_sparse_attn_prefill needs RTP_CHUNK queries");
+    return fail(RTP_EUNSUPPORTED, "sparse prefill attention is not built in this library version");
+}
+
+size_t rtp_window_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
+    if (check_all(layer, cache, query)) return 0;
+    return win_ws_bytes(layer, cache, 0);
+}
+
+size_t rtp_dense_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
+    if (check_all(layer, cache, query)) return 0;
+    return win_ws_bytes(layer, cache, 1);
+}
+
+rtp_status rtp_window_attn(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    return window_like(layer, cache, query, out, workspace, workspace_bytes, stream, 0);
+}
+
+rtp_status rtp_dense_attn(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query, void* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return window_like(layer, cache, query, out, workspace, workspace_bytes, stream, 1);
+}
+
+}  // extern "C"

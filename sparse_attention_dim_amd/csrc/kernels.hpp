@@ -1,0 +1,105 @@
+// kernels.hpp -- launch parameters shared by the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rtp {
+
+constexpr int kMaxRet = 64;
+
+// Geometry of one call (host-filled, passed by value to kernels).
+struct Geo {
+    int Hq, Hkv, D, group;        // group = Hq / Hkv
+    int n_ret;
+    int ret_heads[kMaxRet];
+    int is_ret[256];              // 1 if query head h retrieves (Hq <= 256)
+    int window, sinks;
+    float attn_scale, idx_scale;
+    int kind, seq, pos0, n_tok;   // query rows
+    int batch, max_blocks;
+    int max_seq_len;              // host bound; device lengths are clamped to [1, max_seq_len]
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+};
+
+// Position of query token t (keys 0..pos visible) and its sequence.
+__device__ __forceinline__ int row_seq(const Geo& g, int t) { return g.kind == 0 ? t : g.seq; }
+__device__ __forceinline__ int seq_len(const Geo& g, int b) {
+    return min(max(g.seq_lens[b], 1), g.max_seq_len);
+}
+__device__ __forceinline__ int row_pos(const Geo& g, int t) {
+    return g.kind == 0 ? seq_len(g, t) - 1 : g.pos0 + t;
+}
+
+// Per-row state of the top-p selection (device workspace).
+struct RowState {
+    float m;                      // row maximum score
+    int b1;                       // level-1 cut bin (kNB1 = keep every key)
+    unsigned long long Z;         // total mass (fixed point)
+    unsigned long long target;    // ceil(p * Z)
+    unsigned long long S_above;   // mass of bins < b1
+    uint32_t cnt_above;           // keys in bins < b1
+    uint32_t cnt_b1;              // keys in bin b1
+    uint32_t Tkey;                // key of the last selected key of bin b1
+    int32_t jT;                   // its index (ties: every key == Tkey with j <= jT is taken)
+    int32_t L;                    // keys of the row
+    int32_t count;                // selected keys
+};
+
+constexpr int kChunk = 4096;      // keys per workgroup in the selection passes
+constexpr int kCand = 8192;       // in-bin candidates resolved by one sort
+
+// Device workspace of the selection, for `rows` rows of at most Lpad keys.
+struct SelWs {
+    float* scores;                // [rows][Lpad]
+    int64_t score_ld;
+    uint32_t* cmax;               // [rows][nchunk] ordered keys of chunk maxima
+    uint16_t* qlow;               // [rows][16]
+    unsigned long long* hmass;    // [rows][kNB1]
+    uint32_t* hcnt;               // [rows][kNB1]
+    RowState* st;                 // [rows]
+    uint32_t* ctr;                // [rows] last-block counters (pass 2)
+    uint32_t* ctr2;               // [rows] last-block counters (pass 3)
+    uint32_t* gctr;               // [1]   last-row counter (pass 3)
+    unsigned long long* cand;     // [rows][kCand]
+    uint32_t* cand_n;             // [rows]
+    uint32_t* chunk_cnt;          // [rows][nchunk] selected keys per chunk, then offsets
+    int nchunk;
+    int rows;                     // rows of this group
+};
+
+struct SelOut {
+    int64_t* row_ptr;
+    int32_t* idx;
+    int64_t capacity;
+    int32_t* status;
+};
+
+// Launchers (defined in the .hip files; return hipError_t of the launches).
+hipError_t launch_indexer_append(const Geo& g, const void* k, void* k_low, const void* w_k,
+                                 const int32_t* seq_id, const int32_t* pos, int n, int dtype,
+                                 hipStream_t s);
+
+// Selection of rows [row0, row0 + ws.rows) of the call.  `stage` = 1 runs only
+// the projection and scoring (for rtp_indexer_scores).
+hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
+                         const float* top_p, int row0, const SelWs& ws, const SelOut& out,
+                         int total_rows, int dtype, int scores_only, hipStream_t s);
+
+// Split-K partial attention of retrieval rows over their selected sets and the combine.
+struct AttnWs {
+    float* part;                  // [items][D + 2]
+    int32_t* item_start;          // [rows + 1]
+    int64_t max_items;
+};
+hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, const void* v,
+                                const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
+                                void* out, const AttnWs& ws, int rows, int dtype, hipStream_t s);
+
+// Local-head (window) or dense decode attention, split over keys, then combine.
+hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,
+                                float* part, int nsplit, int split_keys, int dense, int dtype,
+                                hipStream_t s);
+
+}  // namespace rtp

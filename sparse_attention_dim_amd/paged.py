@@ -1,0 +1,93 @@
+"""Paged KV-cache construction for librtp (plumbing: torch allocates and copies).
+
+Turns per-sequence logical arrays [L_b, Hkv, D] into the page pools of
+``include/rtp.h`` -- k, v as [num_blocks, Hkv, 256, D], k_low as bf16
+[num_blocks, num_ret, 256, 16] -- with a block table whose page ids may be
+permuted.  Arrays of dtype uint16 hold bf16 bit patterns.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import RTP_BLOCK, RTP_BF16, RTP_F32, make_cache
+
+BLOCK = RTP_BLOCK
+
+
+def torch_dtype(dtype: str):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def rtp_dtype(dtype: str) -> int:
+    return RTP_BF16 if dtype == "bf16" else RTP_F32
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays become bfloat16 with the same bits."""
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """bfloat16 device tensor -> numpy uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class PagedCache:
+    """Device pages of K, V and K_low for a batch of sequences."""
+
+    def __init__(self, k_list, v_list, n_ret: int, dtype: str, device="cuda", permute_seed=None,
+                 spare_blocks: int = 0):
+        B = len(k_list)
+        Hkv, D = k_list[0].shape[1], k_list[0].shape[2]
+        lens = [int(k.shape[0]) for k in k_list]
+        nblk = [(L + BLOCK - 1) // BLOCK for L in lens]
+        total = sum(nblk) + spare_blocks
+        ids = np.arange(total, dtype=np.int64)
+        if permute_seed is not None:
+            ids = np.random.default_rng(permute_seed).permutation(total)
+        self.max_blocks = max(nblk)
+        table = np.zeros((B, self.max_blocks), np.int32)
+        off = 0
+        for b in range(B):
+            table[b, :nblk[b]] = ids[off: off + nblk[b]]
+            off += nblk[b]
+        td = torch_dtype(dtype)
+        self.k = torch.zeros((total, Hkv, BLOCK, D), dtype=td, device=device)
+        self.v = torch.zeros((total, Hkv, BLOCK, D), dtype=td, device=device)
+        self.k_low = torch.zeros((total, n_ret, BLOCK, 16), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            pages = torch.from_numpy(table[b, :nblk[b]].astype(np.int64)).to(device)
+            for pool, src in ((self.k, k_list[b]), (self.v, v_list[b])):
+                x = to_device(src, device)
+                pad = nblk[b] * BLOCK - lens[b]
+                if pad:
+                    x = torch.cat([x, torch.zeros((pad, Hkv, D), dtype=td, device=device)])
+                x = x.view(nblk[b], BLOCK, Hkv, D).permute(0, 2, 1, 3).contiguous()
+                pool.index_copy_(0, pages, x)
+                del x
+        self.block_table = torch.from_numpy(table).to(device)
+        self.seq_lens = torch.tensor(lens, dtype=torch.int32, device=device)
+        self.lens = lens
+        self.max_seq_len = max(lens)
+        self.Hkv, self.D, self.n_ret, self.dtype = Hkv, D, n_ret, dtype
+        self.table = table
+
+    def cache(self, max_seq_len: int | None = None):
+        return make_cache(self.k, self.v, self.k_low, self.block_table, self.seq_lens,
+                          self.max_seq_len if max_seq_len is None else max_seq_len)
+
+    def k_low_logical(self, b: int, r: int) -> np.ndarray:
+        """bf16 bits [L_b, 16] of retrieval head r's indexer keys of sequence b."""
+        L = self.lens[b]
+        nb = (L + BLOCK - 1) // BLOCK
+        pages = torch.from_numpy(self.table[b, :nb].astype(np.int64)).to(self.k_low.device)
+        x = self.k_low.index_select(0, pages)[:, r]             # [nb, 256, 16]
+        return bf16_bits(x.reshape(nb * BLOCK, 16))[:L]
+
+    def all_positions(self, b: int, device="cuda"):
+        L = self.lens[b]
+        return (torch.full((L,), b, dtype=torch.int32, device=device),
+                torch.arange(L, dtype=torch.int32, device=device))

@@ -290,6 +290,9 @@ def cluster_decode(seed=2, lens=(131072,) * 8, Hq=32, Hkv=8, D=128, n_ret=6, p=0
         for r, h in enumerate(ret):
             gen = rng(seed, 2, b, h)
             n = _draw_size(gen, size_dist, L)
+            sizes[(b, h)] = n
+            if n == 0:
+                continue
             pos = gen.choice(L - 1, size=n, replace=False)
             u = gen.standard_normal(16)
             u /= np.linalg.norm(u)
@@ -300,7 +303,6 @@ def cluster_decode(seed=2, lens=(131072,) * 8, Hq=32, Hkv=8, D=128, n_ret=6, p=0
             qf = as_f32(q[b, h]).copy()
             _plant(qf, dims, a, u, gen.standard_normal(16))
             q[b, h] = to_storage(qf, dtype)
-            sizes[(b, h)] = n
     w_q, w_k = projections(seed, len(ret), D, dtype)
     return Workload(q=q, k=K, v=V, w_q=w_q, w_k=w_k, info=dict(sizes=sizes, amplitude=amps), **cfg)
 
@@ -315,7 +317,7 @@ def _draw_size(gen, size_dist, L):
         w = support ** (-ex)
         cdf = np.cumsum(w) / w.sum()
         n = int(support[min(np.searchsorted(cdf, gen.uniform()), len(support) - 1)])
-    return max(1, min(n, L // 2))
+    return min(n, L // 2)
 
 
 def cluster_chunk(seed=3, L=131072, C=4096, Hq=32, Hkv=8, D=128, n_ret=6, p=0.95, window=2048,
