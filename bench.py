@@ -1,0 +1,295 @@
+"""Benchmark of the RTPurbo hot path on one MI355X.
+
+One step = one decode step of one attention layer for the whole batch: the
+indexer append of the new tokens, top-p selection for every retrieval head,
+sparse attention over the selected rows, and window attention for the local
+heads (decode bf16, batch 8, context 131072, 32 query / 8 KV heads, head dim
+128, 6 retrieval heads, top-p 0.95, window 2048 + 64 sinks).  Inputs are
+synthetic and resident in HBM before timing; four independent layer instances
+are rotated so that the 256 MB last-level cache cannot hold a layer's indexer
+keys between its steps.
+
+Prints one JSON line.  Extra fields: per-call times, the dense same-GPU
+baseline and the speedup, the whole-step algorithmic bandwidth, and the oracle
+timed on a bounded sample on the host (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "decode µs/step/layer + prefill tokens/s/layer at 128K–1M ctx; % HBM/MFMA peak"
+COUNTERS = os.path.join(ROOT, "profiles", "k_sel_score_decode_bf16_B8_L131072_counters.json")
+SCORE_SRC = os.path.join(ROOT, "sparse_attention_dim_amd", "csrc", "select.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_counters():
+    """HBM bytes per launch of the score kernel from the committed rocprofv3
+    counter summary, or None if the kernel source changed since."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except OSError:
+        return None
+    if c.get("source_sha256_16") != source_hash(SCORE_SRC):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, n_seq: int, threads: int):
+    """Time the oracle (as it stands) on the first n_seq sequences of one
+    decode step; the indexer keys of the context are computed untimed."""
+    import concurrent.futures as cf
+
+    import numpy as np
+
+    import oracle
+
+    jobs_kl = [(b, r) for b in range(n_seq) for r in range(w.n_ret)]
+
+    def fill(br):
+        b, r = br
+        g = w.kv_head(w.ret_heads[r])
+        return br, oracle.project(w.k[b][:, g, :], w.w_k[r])
+
+    with cf.ThreadPoolExecutor(threads) as ex:
+        k_low = dict(ex.map(fill, jobs_kl))
+    kf = {}
+    for b in range(n_seq):
+        for g in range(w.Hkv):
+            kf[(b, g)] = (np.ascontiguousarray(oracle.as_f32(w.k[b][:, g, :])),
+                          np.ascontiguousarray(oracle.as_f32(w.v[b][:, g, :])))
+
+    def ret_job(br):
+        b, r = br
+        h = w.ret_heads[r]
+        K, V = kf[(b, w.kv_head(h))]
+        return oracle.retrieval_row(w.q[b, h], K, V, w.w_q[r], w.w_k[r], w.row_pos(b), w.idx_scale,
+                                    float(w.top_p[b]), w.attn_scale, k_low=k_low[(b, r)],
+                                    want_order=False)["sel"].size
+
+    def loc_job(bh):
+        b, h = bh
+        K, V = kf[(b, w.kv_head(h))]
+        return oracle.local_row(w.q[b, h], K, V, w.row_pos(b), w.window, w.sinks, w.attn_scale)[0]
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(threads) as ex:
+        sizes = list(ex.map(ret_job, jobs_kl))
+        list(ex.map(loc_job, [(b, h) for b in range(n_seq) for h in w.local_heads()]))
+    dt = time.perf_counter() - t0
+    return dt, sizes
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_attention_dim_amd as rtp
+    import synth
+    from sparse_attention_dim_amd.paged import PagedCache, rtp_dtype, to_device
+
+    rtp.load()
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = synth.config(2)
+    log("[bench] generated %s in %.1fs" % (w.name, time.time() - t0))
+    B, L = w.B, int(w.seq_lens.max())
+    layer = rtp.make_layer(w.Hq, w.Hkv, w.D, rtp_dtype(w.dtype), w.ret_heads, w.window, w.sinks,
+                           w.attn_scale, w.idx_scale)
+
+    inst = []
+    for i in range(args.instances):
+        pc = PagedCache(w.k, w.v, w.n_ret, w.dtype, device=dev, permute_seed=100 + i)
+        cache = pc.cache(L)
+        q = to_device(w.q, dev)
+        w_q, w_k = to_device(w.w_q, dev), to_device(w.w_k, dev)
+        top_p = torch.from_numpy(w.top_p).to(dev)
+        query = rtp.make_query(q, rtp.RTP_DECODE)
+        for b in range(B):
+            sid, pos = pc.all_positions(b, dev)
+            rtp.indexer_append(layer, cache, w_k, sid, pos)
+        new_sid = torch.arange(B, dtype=torch.int32, device=dev)
+        new_pos = (pc.seq_lens - 1).to(torch.int32)
+        rows = B * w.n_ret
+        cap = rows * L
+        row_ptr = torch.zeros(rows + 1, dtype=torch.int64, device=dev)
+        idx = torch.empty(cap, dtype=torch.int32, device=dev)
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        sel = rtp.make_sel(row_ptr, idx, status)
+        ws_sel = torch.empty(rtp.topp_select_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
+        ws_sp = torch.empty(rtp.sparse_attn_workspace(layer, cache, query, cap), dtype=torch.uint8, device=dev)
+        ws_win = torch.empty(rtp.window_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
+        out = torch.zeros_like(q)
+        inst.append(dict(pc=pc, cache=cache, q=q, w_q=w_q, w_k=w_k, top_p=top_p, query=query,
+                         sid=new_sid, pos=new_pos, sel=sel, row_ptr=row_ptr, idx=idx, status=status,
+                         ws_sel=ws_sel, ws_sp=ws_sp, ws_win=ws_win, out=out))
+    torch.cuda.synchronize()
+    log("[bench] %d layer instances resident (%.1f GB allocated)" %
+        (args.instances, torch.cuda.memory_allocated() / 1e9))
+
+    calls = ("append", "select", "sparse", "window")
+
+    def step(I, ev=None):
+        if ev is not None:
+            ev[0].record()
+        rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"])
+        if ev is not None:
+            ev[1].record()
+        rtp.topp_select(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
+        if ev is not None:
+            ev[2].record()
+        rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"])
+        if ev is not None:
+            ev[3].record()
+        rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"])
+        if ev is not None:
+            ev[4].record()
+
+    for s in range(args.warmup):
+        step(inst[s % len(inst)])
+    torch.cuda.synchronize()
+    assert all(int(I["status"].item()) == 0 for I in inst), "selection capacity overflow"
+
+    # --- timed region: exactly `steps` steps -------------------------------
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(inst[s % len(inst)], evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    per_call = {c: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
+                for i, c in enumerate(calls)}
+
+    # --- algorithmic bytes of one step ---------------------------------------
+    rp = inst[0]["row_ptr"].cpu().numpy()
+    n_sel = int(rp[-1])
+    sizes = np.diff(rp)
+    lens = w.seq_lens.astype(np.int64)
+    kv_row = w.D * 2 * 2                          # one K row + one V row, bf16
+    bytes_klow = int(sum(lens[b] for b in range(B)) * w.n_ret * 32)
+    bytes_sparse = n_sel * kv_row + n_sel * 8
+    win_keys = [min(w.window + w.sinks, int(l)) for l in lens]
+    bytes_win = int(sum(win_keys) * w.Hkv * kv_row)
+    step_bytes = bytes_klow + bytes_sparse + bytes_win
+
+    # --- the dominant kernel: the indexer score pass, timed on its own ------
+    I = inst[0]
+    rows = B * w.n_ret
+    qlow_buf = torch.empty((rows, 16), dtype=torch.int16, device=dev)
+    score_bufs = [torch.empty((rows, L), dtype=torch.float32, device=dev) for _ in inst]
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for s in range(args.steps):
+        J = inst[s % len(inst)]
+        kev[s][0].record()
+        rtp.indexer_scores(layer, J["cache"], J["query"], J["w_q"], qlow_buf, score_bufs[s % len(inst)])
+        kev[s][1].record()
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    k_achieved = bytes_klow / (k_ms * 1e-3) / 1e9
+
+    # --- dense baseline on the same GPU --------------------------------------
+    ws_dense = torch.empty(rtp.dense_attn_workspace(layer, I["cache"], I["query"]), dtype=torch.uint8,
+                           device=dev)
+    dense_out = torch.zeros_like(I["q"])
+    for s in range(3):
+        rtp.dense_attn(layer, inst[s % len(inst)]["cache"], inst[s % len(inst)]["query"], dense_out, ws_dense)
+    torch.cuda.synchronize()
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nd = 10
+    d0.record()
+    for s in range(nd):
+        J = inst[s % len(inst)]
+        rtp.dense_attn(layer, J["cache"], J["query"], dense_out, ws_dense)
+    d1.record()
+    torch.cuda.synchronize()
+    dense_ms = d0.elapsed_time(d1) / nd
+    dense_bytes = int(sum(int(l) for l in lens) * w.Hkv * kv_row)
+
+    # calibration copy of known size for the HBM counter runs (1 GiB read, 1 GiB write)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+    # --- the oracle on the host, on a bounded sample --------------------------
+    cpu = None
+    if not args.no_cpu:
+        threads = min(os.cpu_count() or 1, 16)
+        ns = min(args.cpu_seqs, B)
+        dt, _ = cpu_baseline(w, ns, threads)
+        cpu = {"value": dt / ns * B * 1e6, "unit": "µs/step/layer", "cores": threads, "kind": "oracle",
+               "sample": "retrieval rows and local heads of %d of the %d sequences of one decode step "
+                         "(indexer keys of the context precomputed untimed), scaled x%d to the batch"
+                         % (ns, B, B // ns)}
+
+    res = {
+        "metric": METRIC,
+        "value": round(ms * 1e3, 2),
+        "unit": "µs/step/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "kind": "decode", "batch": B, "context": L, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "retrieval_heads": w.n_ret, "top_p": 0.95,
+                   "window": w.window, "sinks": w.sinks, "layer_instances": args.instances},
+        "roofline": {"kernel": "k_sel_score (indexer scores, decode)", "bound": "hbm",
+                     "achieved": round(k_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(),
+                     "algorithmic_bytes": bytes_klow, "avg_launch_us": round(k_ms * 1e3, 2)},
+        "cpu_baseline": cpu,
+        "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "selected_per_row": {"min": int(sizes.min()), "median": int(np.median(sizes)),
+                             "max": int(sizes.max()), "total": n_sel},
+        "dense_us": round(dense_ms * 1e3, 2),
+        "dense_hbm_frac": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "speedup_vs_dense": round(dense_ms / ms, 3),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

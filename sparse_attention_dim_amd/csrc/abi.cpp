@@ -40,8 +40,8 @@ rtp_status hip_status(hipError_t e, const char* what) {
 
 constexpr int kMaxLen = 1 << 22;          // longest supported context
 constexpr int kMaxDecodeRows = 4096;      // decode rows (batch * num_ret) of the sparse kernel
-constexpr int kWinSplit = 256;            // keys per workgroup, local-head decode
-constexpr int kDenseSplit = 512;          // keys per workgroup, dense decode
+constexpr int kWinSplit = 64;             // keys per workgroup, local-head decode
+constexpr int kDenseSplit = 1024;         // keys per workgroup, dense decode
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -147,7 +147,7 @@ constexpr size_t kScoreBudget = (size_t)4 << 30;   // bytes of scores per row gr
 struct SelPlan {
     int rows_total, group_rows, nchunk;
     int64_t lpad;
-    size_t off_scores, off_cmax, off_qlow, off_hmass, off_hcnt, off_st, off_ctr, off_ctr2, off_gctr,
+    size_t off_scores, off_cmax, off_qlow, off_hmass, off_hcnt, off_st,
         off_cand, off_cand_n, off_chunk, total;
 };
 
@@ -167,9 +167,6 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     p.off_hmass = o; o = align256(o + G * rtp::kNB1 * 8);
     p.off_hcnt = o; o = align256(o + G * rtp::kNB1 * 4);
     p.off_st = o; o = align256(o + G * sizeof(rtp::RowState));
-    p.off_ctr = o; o = align256(o + G * 4);
-    p.off_ctr2 = o; o = align256(o + G * 4);
-    p.off_gctr = o; o = align256(o + 4);
     p.off_cand = o; o = align256(o + G * rtp::kCand * 8);
     p.off_cand_n = o; o = align256(o + G * 4);
     p.off_chunk = o; o = align256(o + G * (size_t)p.nchunk * 4);
@@ -186,9 +183,6 @@ rtp::SelWs sel_ws(const SelPlan& p, char* base) {
     w.hmass = (unsigned long long*)(base + p.off_hmass);
     w.hcnt = (uint32_t*)(base + p.off_hcnt);
     w.st = (rtp::RowState*)(base + p.off_st);
-    w.ctr = (uint32_t*)(base + p.off_ctr);
-    w.ctr2 = (uint32_t*)(base + p.off_ctr2);
-    w.gctr = (uint32_t*)(base + p.off_gctr);
     w.cand = (unsigned long long*)(base + p.off_cand);
     w.cand_n = (uint32_t*)(base + p.off_cand_n);
     w.chunk_cnt = (uint32_t*)(base + p.off_chunk);

@@ -7,11 +7,13 @@
 // post "RTPurbo: Turning Dense LLMs into Sparse Attention Models ...", "Three
 // Key Insights" item 1.
 //
-// Both are flash-decoding style: the key set of a row is split into chunks,
-// each workgroup produces (max, sum, unnormalised output) for its chunk, and a
-// combine kernel merges the chunks in a fixed order (deterministic).  A key row
-// is read as 16-byte slices by a group of lanes (16 lanes for bf16/D=128), so
-// every gathered 256-byte row is one contiguous burst.
+// Flash-decoding on one wavefront per work item.  A key row (D elements) is
+// read by a group of LPK lanes, 16 bytes each, so one load instruction reads
+// 64/LPK whole rows (1 KiB, coalesced).  Each group runs its own online
+// softmax over the keys it reads (q.k partials are summed across the group's
+// lanes with DPP row operations; no LDS, no barriers in the loop); the groups
+// of the wave are merged at the end, and a combine kernel merges the work
+// items of a row in a fixed order, so results are deterministic.
 #include <algorithm>
 
 #include "device.hpp"
@@ -22,35 +24,42 @@ namespace rtp {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kItem = 128;          // selected keys per sparse work item
 
-template <typename T, int D>
-struct Lay {
-    static constexpr int EPL = 16 / (int)sizeof(T);    // elements per lane (16 B)
-    static constexpr int LPK = D / EPL;                 // lanes per key row
-    static constexpr int KPW = 64 / LPK;                // key rows per wave step
+template <typename T>
+struct Pack;                        // 16-byte vector of T unpacked to floats
+template <>
+struct Pack<bf16_t> {
+    static constexpr int N = 8;
+    __device__ static __forceinline__ void unpack(const uint4& a, float* f) {
+        f[0] = __uint_as_float(a.x << 16); f[1] = __uint_as_float(a.x & 0xFFFF0000u);
+        f[2] = __uint_as_float(a.y << 16); f[3] = __uint_as_float(a.y & 0xFFFF0000u);
+        f[4] = __uint_as_float(a.z << 16); f[5] = __uint_as_float(a.z & 0xFFFF0000u);
+        f[6] = __uint_as_float(a.w << 16); f[7] = __uint_as_float(a.w & 0xFFFF0000u);
+    }
+};
+template <>
+struct Pack<float> {
+    static constexpr int N = 4;
+    __device__ static __forceinline__ void unpack(const uint4& a, float* f) {
+        f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y);
+        f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+    }
 };
 
-template <typename T, int N>
-__device__ __forceinline__ void load_slice(const T* p, float* f);
-template <>
-__device__ __forceinline__ void load_slice<bf16_t, 8>(const bf16_t* p, float* f) {
-    const uint4 a = *reinterpret_cast<const uint4*>(p);
-    f[0] = __uint_as_float(a.x << 16); f[1] = __uint_as_float(a.x & 0xFFFF0000u);
-    f[2] = __uint_as_float(a.y << 16); f[3] = __uint_as_float(a.y & 0xFFFF0000u);
-    f[4] = __uint_as_float(a.z << 16); f[5] = __uint_as_float(a.z & 0xFFFF0000u);
-    f[6] = __uint_as_float(a.w << 16); f[7] = __uint_as_float(a.w & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ void load_slice<float, 4>(const float* p, float* f) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+// Sum over aligned groups of LPK lanes; every lane of a group gets the same
+// bits (each step adds a value and its mirror image, which commutes).
 template <int LPK>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = 1; o < LPK; o <<= 1) v += __shfl_xor(v, o);
+    if (LPK >= 2) v += dpp<0xB1>(v);      // quad_perm [1,0,3,2]
+    if (LPK >= 4) v += dpp<0x4E>(v);      // quad_perm [2,3,0,1]
+    if (LPK >= 8) v += dpp<0x141>(v);     // row_half_mirror
+    if (LPK >= 16) v += dpp<0x140>(v);    // row_mirror
+    if (LPK >= 32) v += __shfl_xor(v, 16);
     return v;
 }
 
@@ -58,58 +67,172 @@ __device__ __forceinline__ size_t kv_off(const Geo& g, int page, int kvh, int sl
     return (((size_t)page * g.Hkv + kvh) * kBlk + slot) * (size_t)D;
 }
 
-// ---------------------------------------------------------------------------
-// Sparse decode: persistent workgroups over (row, chunk of kItem selected keys).
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_sparse_dec_part(Geo g, const T* __restrict__ q,
-                                                         const T* __restrict__ kc,
-                                                         const T* __restrict__ vc,
-                                                         const int64_t* __restrict__ row_ptr,
-                                                         const int32_t* __restrict__ idx,
-                                                         const int32_t* __restrict__ status,
-                                                         AttnWs ws, int rows) {
-    using LY = Lay<T, D>;
-    constexpr int EPL = LY::EPL, LPK = LY::LPK, KPW = LY::KPW;
-    if (*status != 0) return;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    extern __shared__ int32_t istart[];   // rows + 1
-    __shared__ float lg[kItem];
-    __shared__ int32_t jj[kItem];
-    __shared__ float red[4];
-    __shared__ float ored[4][D];
+template <typename T, int D, int NH>
+struct Stream {
+    static constexpr int EPV = Pack<T>::N;      // elements per lane slice
+    static constexpr int LPK = D / EPV;         // lanes per key row
+    static constexpr int GPW = 64 / LPK;        // key rows per load instruction
+    static constexpr int U = NH > 4 ? 4 : 8;    // rows per group per iteration
 
-    // items per row and their prefix (every workgroup recomputes it)
-    {
-        constexpr int kPer = 16;                 // rows per thread (rows <= 4096)
-        __shared__ unsigned long long scan_sh[5];
-        int cnt[kPer];
-        unsigned long long loc = 0;
-        for (int i = 0; i < kPer; ++i) {
-            const int r = tid * kPer + i;
-            cnt[i] = 0;
-            if (r < rows) {
-                const int64_t n = row_ptr[r + 1] - row_ptr[r];
-                cnt[i] = (int)((n + kItem - 1) / kItem);
+    float q[NH][EPV];
+    float m[NH], l[NH], o[NH][EPV];
+
+    __device__ void init() {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            m[h] = -INFINITY;
+            l[h] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) o[h][e] = 0.0f;
+        }
+    }
+
+    // Keys 0..n-1 of a work item; off(i) is the element offset of key i's row
+    // (valid for 0 <= i < n).  Group g of the wave takes keys g, g + GPW, ...
+    template <typename F>
+    __device__ void run(int n, int nh, F off, const T* __restrict__ kc, const T* __restrict__ vc) {
+        const int lane = threadIdx.x & 63;
+        const int g = lane / LPK, sl = (lane % LPK) * EPV;
+        for (int base = 0; base < n; base += GPW * U) {
+            size_t ro[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) ro[u] = off(min(base + u * GPW + g, n - 1));
+            uint4 kb[U], vb[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) kb[u] = *reinterpret_cast<const uint4*>(kc + ro[u] + sl);
+#pragma unroll
+            for (int u = 0; u < U; ++u) vb[u] = *reinterpret_cast<const uint4*>(vc + ro[u] + sl);
+            float s[U][NH];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float f[EPV];
+                Pack<T>::unpack(kb[u], f);
+                const bool ok = base + u * GPW + g < n;
+#pragma unroll
+                for (int h = 0; h < NH; ++h) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) acc = __builtin_fmaf(q[h][e], f[e], acc);
+                    acc = group_sum<LPK>(acc);
+                    s[u][h] = ok ? acc : -INFINITY;
+                }
             }
-            loc += (unsigned long long)cnt[i];
+#pragma unroll
+            for (int h = 0; h < NH; ++h) {
+                if (h >= nh) continue;
+                float cm = s[0][h];
+#pragma unroll
+                for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u][h]);
+                const float mn = fmaxf(m[h], cm);
+                if (mn == -INFINITY) continue;           // the group has no key yet
+                const float corr = exp2f(m[h] - mn);
+                m[h] = mn;
+                l[h] *= corr;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) o[h][e] *= corr;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float p = exp2f(s[u][h] - mn);
+                    l[h] += p;
+                    float f[EPV];
+                    Pack<T>::unpack(vb[u], f);
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) o[h][e] = __builtin_fmaf(p, f[e], o[h][e]);
+                }
+            }
         }
-        unsigned long long tot;
-        unsigned long long run = block_excl_scan_u64<256>(loc, &tot, scan_sh);
-        for (int i = 0; i < kPer; ++i) {
-            const int r = tid * kPer + i;
-            if (r < rows) istart[r] = (int)run;
-            run += (unsigned long long)cnt[i];
+    }
+
+    // Merge the groups of the wave; afterwards lanes 0..LPK-1 hold head h's
+    // output slices and every lane holds the merged (m, l).
+    __device__ void merge(int nh) {
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+            if (h >= nh) continue;
+            float M = m[h];
+            for (int off = LPK; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
+            const float sc = M == -INFINITY ? 0.0f : exp2f(m[h] - M);
+            float L = l[h] * sc;
+            for (int off = LPK; off < 64; off <<= 1) L += __shfl_xor(L, off);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                float x = o[h][e] * sc;
+                for (int off = LPK; off < 64; off <<= 1) x += __shfl_xor(x, off);
+                o[h][e] = x;
+            }
+            m[h] = M;
+            l[h] = L;
         }
-        if (tid == 0) istart[rows] = (int)tot;
+    }
+
+    __device__ void write(int h, float* pp) const {
+        const int lane = threadIdx.x & 63;
+        if (lane < LPK) {
+            const int sl = lane * EPV;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) pp[sl + e] = o[h][e];
+            if (lane == 0) {
+                pp[D] = m[h];
+                pp[D + 1] = l[h];
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Sparse decode: one wavefront per (row, piece of kItem selected keys); the
+// pieces of all rows form one flat list walked by a fixed grid.
+// ---------------------------------------------------------------------------
+constexpr int kItem = 128;
+
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restrict__ q,
+                                                        const T* __restrict__ kc,
+                                                        const T* __restrict__ vc,
+                                                        const int64_t* __restrict__ row_ptr,
+                                                        const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ status,
+                                                        AttnWs ws, int rows) {
+    using S = Stream<T, D, 1>;
+    if (*status != 0) return;
+    const int lane = threadIdx.x;
+    extern __shared__ int64_t dyn[];
+    int64_t* rp = dyn;                                    // rows + 1
+    int32_t* istart = reinterpret_cast<int32_t*>(dyn + rows + 1);   // rows + 1
+    __shared__ uint32_t joff[kItem];                      // page-resolved row offsets / D
+    {   // pieces per row and their prefix (every workgroup recomputes it; rows <= 4096)
+        for (int r = lane; r <= rows; r += 64) rp[r] = row_ptr[r];
+        __syncthreads();
+        const int per = (rows + 63) / 64;
+        const int r0 = lane * per;
+        int run = 0;
+        for (int i = 0; i < per; ++i) {
+            const int r = r0 + i;
+            if (r < rows) run += (int)((rp[r + 1] - rp[r] + kItem - 1) / kItem);
+        }
+        int ex = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(ex, o);
+            if (lane >= o) ex += y;
+        }
+        const int total = __shfl(ex, 63);
+        ex -= run;
+        for (int i = 0; i < per; ++i) {
+            const int r = r0 + i;
+            if (r < rows) {
+                istart[r] = ex;
+                ex += (int)((rp[r + 1] - rp[r] + kItem - 1) / kItem);
+            }
+        }
+        if (lane == 0) istart[rows] = total;
     }
     __syncthreads();
     if (blockIdx.x == 0)
-        for (int r = tid; r <= rows; r += 256) ws.item_start[r] = istart[r];
+        for (int r = lane; r <= rows; r += 64) ws.item_start[r] = istart[r];
     const int total = istart[rows];
-    const int sub = lane / LPK;          // key row within the wave step
-    const int e0 = (lane % LPK) * EPL;   // first element of this lane's slice
     const float sc = g.attn_scale * kLog2e;
+    constexpr int EPV = S::EPV, LPK = S::LPK;
 
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
         int lo = 0, hi = rows - 1;       // last row with istart <= item
@@ -120,80 +243,67 @@ __global__ __launch_bounds__(256) void k_sparse_dec_part(Geo g, const T* __restr
         const int row = lo;
         const int t = row / g.n_ret, r = row - t * g.n_ret;
         const int h = g.ret_heads[r], kvh = h / g.group;
-        const int b = t;
-        const int64_t k0 = row_ptr[row] + (int64_t)(item - istart[row]) * kItem;
-        const int n = (int)min<int64_t>(kItem, row_ptr[row + 1] - k0);
-        const int32_t* bt = g.block_table + (size_t)b * g.max_blocks;
+        const int64_t k0 = rp[row] + (int64_t)(item - istart[row]) * kItem;
+        const int n = (int)min<int64_t>(kItem, rp[row + 1] - k0);
+        const int32_t* bt = g.block_table + (size_t)t * g.max_blocks;
+        // resolve the item's rows once: index -> page -> row offset (in units of D)
+        int jl[kItem / 64];
+#pragma unroll
+        for (int i = 0; i < kItem / 64; ++i) jl[i] = idx[k0 + min(lane + 64 * i, n - 1)];
+        int pg[kItem / 64];
+#pragma unroll
+        for (int i = 0; i < kItem / 64; ++i) pg[i] = bt[jl[i] >> 8];
+#pragma unroll
+        for (int i = 0; i < kItem / 64; ++i)
+            joff[lane + 64 * i] = (uint32_t)(((size_t)pg[i] * g.Hkv + kvh) * kBlk + (jl[i] & 255));
+        S st;
+        st.init();
+        const int sl = (lane % LPK) * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) st.q[0][e] = ld(q + ((size_t)t * g.Hq + h) * D + sl + e) * sc;
+        __syncthreads();
+        auto off = [&](int i) { return (size_t)joff[i] * D; };
+        st.run(n, 1, off, kc, vc);
+        st.merge(1);
+        st.write(0, ws.part + (size_t)item * (D + 2));
+        __syncthreads();
+    }
+}
 
-        float qv[EPL];
-        load_slice<T, EPL>(q + ((size_t)t * g.Hq + h) * D + e0, qv);
-        for (int i = tid; i < n; i += 256) jj[i] = idx[k0 + i];
-        __syncthreads();
-        // logits (log2 units)
-        for (int s0 = wid * KPW; s0 < n; s0 += 4 * KPW) {
-            const int kk = s0 + sub;
-            float dot = 0.0f;
-            if (kk < n) {
-                const int j = jj[kk];
-                float kv[EPL];
-                load_slice<T, EPL>(kc + kv_off(g, bt[j >> 8], kvh, j & 255, D) + e0, kv);
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kv[e], dot);
-            }
-            dot = group_sum<LPK>(dot);
-            if (kk < n && (lane % LPK) == 0) lg[kk] = dot * sc;
+constexpr int kMaxParts = 4096;   // partial weights kept in LDS; more are recomputed
+
+// Merge `n` partial results (stride D + 2: output[D], max, sum) in order.
+template <typename T, int D>
+__device__ void combine_parts(const float* __restrict__ base, int n, T* __restrict__ o, float* wsh) {
+    const int tid = threadIdx.x;
+    __shared__ float red[4];
+    float mx = -INFINITY;
+    for (int i = tid; i < n; i += blockDim.x) mx = fmaxf(mx, base[(size_t)i * (D + 2) + D]);
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) red[tid >> 6] = mx;
+    __syncthreads();
+    float M = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+    float ls = 0.0f;
+    for (int i = tid; i < n; i += blockDim.x) {
+        const float w = exp2f(base[(size_t)i * (D + 2) + D] - M);
+        if (i < kMaxParts) wsh[i] = w;
+        ls += w * base[(size_t)i * (D + 2) + D + 1];
+    }
+    ls = wave_sum(ls);
+    if ((tid & 63) == 0) red[tid >> 6] = ls;
+    __syncthreads();
+    float L = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) L += red[w];
+    for (int d = tid; d < D; d += blockDim.x) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) {
+            const float w = i < kMaxParts ? wsh[i] : exp2f(base[(size_t)i * (D + 2) + D] - M);
+            acc = __builtin_fmaf(base[(size_t)i * (D + 2) + d], w, acc);
         }
-        __syncthreads();
-        float mx = -INFINITY;
-        for (int i = tid; i < n; i += 256) mx = fmaxf(mx, lg[i]);
-        mx = wave_max(mx);
-        if (lane == 0) red[wid] = mx;
-        __syncthreads();
-        mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-        __syncthreads();
-        float sm = 0.0f;
-        for (int i = tid; i < n; i += 256) {
-            const float p = exp2f(lg[i] - mx);
-            lg[i] = p;
-            sm += p;
-        }
-        sm = wave_sum(sm);
-        if (lane == 0) red[wid] = sm;
-        __syncthreads();
-        sm = red[0] + red[1] + red[2] + red[3];
-        // weighted values
-        float o[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = 0.0f;
-        for (int s0 = wid * KPW; s0 < n; s0 += 4 * KPW) {
-            const int kk = s0 + sub;
-            if (kk < n) {
-                const int j = jj[kk];
-                float vv[EPL];
-                load_slice<T, EPL>(vc + kv_off(g, bt[j >> 8], kvh, j & 255, D) + e0, vv);
-                const float p = lg[kk];
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) o[e] = __builtin_fmaf(p, vv[e], o[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float x = o[e];
-            for (int off = LPK; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            o[e] = x;
-        }
-        if (sub == 0) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) ored[wid][e0 + e] = o[e];
-        }
-        __syncthreads();
-        float* pp = ws.part + (size_t)item * (D + 2);
-        for (int d = tid; d < D; d += 256) pp[d] = ored[0][d] + ored[1][d] + ored[2][d] + ored[3][d];
-        if (tid == 0) {
-            pp[D] = mx;
-            pp[D + 1] = sm;
-        }
-        __syncthreads();
+        st<T>(o + d, acc / L);
     }
 }
 
@@ -201,38 +311,24 @@ template <typename T, int D>
 __global__ __launch_bounds__(128) void k_sparse_dec_combine(Geo g, const int32_t* __restrict__ status,
                                                             AttnWs ws, T* __restrict__ out) {
     if (*status != 0) return;
+    __shared__ float wsh[kMaxParts];
     const int row = blockIdx.x;
     const int t = row / g.n_ret, r = row - t * g.n_ret;
     const int h = g.ret_heads[r];
     const int i0 = ws.item_start[row], i1 = ws.item_start[row + 1];
+    T* o = out + ((size_t)t * g.Hq + h) * D;
     if (i1 <= i0) {
-        for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(out + ((size_t)t * g.Hq + h) * D + d, 0.0f);
+        for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
         return;
     }
-    float M = -INFINITY;
-    for (int i = i0; i < i1; ++i) M = fmaxf(M, ws.part[(size_t)i * (D + 2) + D]);
-    float l = 0.0f;
-    for (int i = i0; i < i1; ++i) {
-        const float* pp = ws.part + (size_t)i * (D + 2);
-        l += pp[D + 1] * exp2f(pp[D] - M);
-    }
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float acc = 0.0f;
-        for (int i = i0; i < i1; ++i) {
-            const float* pp = ws.part + (size_t)i * (D + 2);
-            acc += pp[d] * exp2f(pp[D] - M);
-        }
-        st<T>(out + ((size_t)t * g.Hq + h) * D + d, acc / l);
-    }
+    combine_parts<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, wsh);
 }
 
 // ---------------------------------------------------------------------------
-// Window / dense decode: grid (nsplit, batch * Hkv).  One workgroup reads each
-// key and value row of its split once and serves every head of the KV group
-// that needs it (the local heads, or all heads when dense).
+// Window / dense decode: grid (nsplit, batch * Hkv), one wavefront each.  The
+// wavefront serves every head of the KV group that needs it (the local heads,
+// or all heads when dense), reading each key and value row once.
 // ---------------------------------------------------------------------------
-constexpr int kMaxGroup = 8;
-
 __device__ __forceinline__ int win_count(const Geo& g, int pos, int dense, int* ns_end, int* w_start) {
     if (dense) {
         *ns_end = pos + 1;
@@ -246,14 +342,14 @@ __device__ __forceinline__ int win_count(const Geo& g, int pos, int dense, int* 
     return ne + (pos - ws + 1);
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_win_dec_part(Geo g, const T* __restrict__ q,
-                                                      const T* __restrict__ kc,
-                                                      const T* __restrict__ vc, float* __restrict__ part,
-                                                      int nsplit, int split_keys, int dense) {
-    using LY = Lay<T, D>;
-    constexpr int EPL = LY::EPL, LPK = LY::LPK, KPW = LY::KPW;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+template <typename T, int D, int NH>
+__global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict__ q,
+                                                     const T* __restrict__ kc,
+                                                     const T* __restrict__ vc, float* __restrict__ part,
+                                                     int nsplit, int split_keys, int dense) {
+    using S = Stream<T, D, NH>;
+    constexpr int EPV = S::EPV, LPK = S::LPK;
+    const int lane = threadIdx.x;
     const int b = blockIdx.y / g.Hkv, kvh = blockIdx.y % g.Hkv;
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
@@ -262,159 +358,80 @@ __global__ __launch_bounds__(256) void k_win_dec_part(Geo g, const T* __restrict
     if (v0 >= n_all) return;
     const int n = min(split_keys, n_all - v0);
 
-    // heads of this KV group that this call computes
-    int heads[kMaxGroup];
+    int heads[NH];
     int nh = 0;
-    for (int i = 0; i < g.group; ++i) {
-        const int h = kvh * g.group + i;
-        if (dense || !g.is_ret[h]) heads[nh++] = h;
+    for (int i = 0; i < g.group && nh < NH; ++i) {
+        const int hh = kvh * g.group + i;
+        if (dense || !g.is_ret[hh]) heads[nh++] = hh;
     }
     if (nh == 0) return;
-
-    extern __shared__ float lgs[];         // [kMaxGroup][split_keys]
-    __shared__ float red[kMaxGroup][4];
-    __shared__ float ored[4][D];
-    const int sub = lane / LPK;
-    const int e0 = (lane % LPK) * EPL;
     const float sc = g.attn_scale * kLog2e;
+    const int sl = (lane % LPK) * EPV;
+    S st;
+    st.init();
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            st.q[i][e] = i < nh ? ld(q + ((size_t)b * g.Hq + heads[i]) * D + sl + e) * sc : 0.0f;
+    }
     const int32_t* bt = g.block_table + (size_t)b * g.max_blocks;
-
-    float qv[kMaxGroup][EPL];
-#pragma unroll
-    for (int i = 0; i < kMaxGroup; ++i)
-        if (i < nh) load_slice<T, EPL>(q + ((size_t)b * g.Hq + heads[i]) * D + e0, qv[i]);
-
-    for (int s0 = wid * KPW; s0 < n; s0 += 4 * KPW) {
-        const int kk = s0 + sub;
-        float kv[EPL];
-        if (kk < n) {
-            const int vi = v0 + kk;
-            const int j = vi < ns_end ? vi : w_start + (vi - ns_end);
-            load_slice<T, EPL>(kc + kv_off(g, bt[j >> 8], kvh, j & 255, D) + e0, kv);
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) kv[e] = 0.0f;
-        }
-#pragma unroll
-        for (int i = 0; i < kMaxGroup; ++i) {
-            if (i < nh) {
-                float dot = 0.0f;
-#pragma unroll
-                for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[i][e], kv[e], dot);
-                dot = group_sum<LPK>(dot);
-                if (kk < n && (lane % LPK) == 0) lgs[i * split_keys + kk] = dot * sc;
-            }
-        }
-    }
-    __syncthreads();
-    float mxh[kMaxGroup], smh[kMaxGroup];
-    for (int i = 0; i < nh; ++i) {
-        float mx = -INFINITY;
-        for (int x = tid; x < n; x += 256) mx = fmaxf(mx, lgs[i * split_keys + x]);
-        mx = wave_max(mx);
-        if (lane == 0) red[i][wid] = mx;
-    }
-    __syncthreads();
-    for (int i = 0; i < nh; ++i) mxh[i] = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
-    __syncthreads();
-    for (int i = 0; i < nh; ++i) {
-        float sm = 0.0f;
-        for (int x = tid; x < n; x += 256) {
-            const float p = exp2f(lgs[i * split_keys + x] - mxh[i]);
-            lgs[i * split_keys + x] = p;
-            sm += p;
-        }
-        sm = wave_sum(sm);
-        if (lane == 0) red[i][wid] = sm;
-    }
-    __syncthreads();
-    for (int i = 0; i < nh; ++i) smh[i] = red[i][0] + red[i][1] + red[i][2] + red[i][3];
-
-    float o[kMaxGroup][EPL];
-#pragma unroll
-    for (int i = 0; i < kMaxGroup; ++i)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[i][e] = 0.0f;
-    for (int s0 = wid * KPW; s0 < n; s0 += 4 * KPW) {
-        const int kk = s0 + sub;
-        if (kk < n) {
-            const int vi = v0 + kk;
-            const int j = vi < ns_end ? vi : w_start + (vi - ns_end);
-            float vv[EPL];
-            load_slice<T, EPL>(vc + kv_off(g, bt[j >> 8], kvh, j & 255, D) + e0, vv);
-#pragma unroll
-            for (int i = 0; i < kMaxGroup; ++i) {
-                if (i < nh) {
-                    const float p = lgs[i * split_keys + kk];
-#pragma unroll
-                    for (int e = 0; e < EPL; ++e) o[i][e] = __builtin_fmaf(p, vv[e], o[i][e]);
-                }
-            }
-        }
-    }
-    for (int i = 0; i < nh; ++i) {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float x = o[i][e];
-            for (int off = LPK; off < 64; off <<= 1) x += __shfl_xor(x, off);
-            o[i][e] = x;
-        }
-        if (sub == 0) {
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) ored[wid][e0 + e] = o[i][e];
-        }
-        __syncthreads();
-        float* pp = part + (((size_t)b * g.Hq + heads[i]) * nsplit + blockIdx.x) * (D + 2);
-        for (int d = tid; d < D; d += 256) pp[d] = ored[0][d] + ored[1][d] + ored[2][d] + ored[3][d];
-        if (tid == 0) {
-            pp[D] = mxh[i];
-            pp[D + 1] = smh[i];
-        }
-        __syncthreads();
-    }
+    auto off = [&](int i) {
+        const int vi = v0 + i;
+        const int j = vi < ns_end ? vi : w_start + (vi - ns_end);
+        return kv_off(g, bt[j >> 8], kvh, j & 255, D);
+    };
+    st.run(n, nh, off, kc, vc);
+    st.merge(nh);
+    for (int i = 0; i < nh; ++i)
+        st.write(i, part + (((size_t)b * g.Hq + heads[i]) * nsplit + blockIdx.x) * (D + 2));
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(128) void k_win_dec_combine(Geo g, const float* __restrict__ part,
                                                          T* __restrict__ out, int nsplit, int split_keys,
                                                          int dense) {
+    __shared__ float wsh[kMaxParts];
     const int b = blockIdx.y, h = blockIdx.x;
     if (!dense && g.is_ret[h]) return;
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
     const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
     const int ns = min(nsplit, (n_all + split_keys - 1) / split_keys);
-    const float* base = part + ((size_t)b * g.Hq + h) * nsplit * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, base[(size_t)s * (D + 2) + D]);
-    float l = 0.0f;
-    for (int s = 0; s < ns; ++s) l += base[(size_t)s * (D + 2) + D + 1] * exp2f(base[(size_t)s * (D + 2) + D] - M);
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float acc = 0.0f;
-        for (int s = 0; s < ns; ++s)
-            acc += base[(size_t)s * (D + 2) + d] * exp2f(base[(size_t)s * (D + 2) + D] - M);
-        st<T>(out + ((size_t)b * g.Hq + h) * D + d, acc / l);
-    }
+    combine_parts<T, D>(part + ((size_t)b * g.Hq + h) * nsplit * (D + 2), ns,
+                        out + ((size_t)b * g.Hq + h) * D, wsh);
 }
 
 template <typename T, int D>
 hipError_t sparse_dec(const Geo& g, const void* q, const void* k, const void* v, const int64_t* row_ptr,
                       const int32_t* idx, const int32_t* status, void* out, const AttnWs& ws, int rows,
                       hipStream_t s) {
-    const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 2048);
-    const size_t shmem = sizeof(int32_t) * (rows + 1);
-    hipLaunchKernelGGL((k_sparse_dec_part<T, D>), dim3((unsigned)grid), dim3(256), shmem, s, g,
+    const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
+    const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
+    hipLaunchKernelGGL((k_sparse_dec_part<T, D>), dim3((unsigned)grid), dim3(64), shmem, s, g,
                        (const T*)q, (const T*)k, (const T*)v, row_ptr, idx, status, ws, rows);
     hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(128), 0, s, g, status, ws, (T*)out);
     return hipGetLastError();
 }
 
+template <typename T, int D, int NH>
+void win_dec_part(const Geo& g, const void* q, const void* k, const void* v, float* part, int nsplit,
+                  int split_keys, int dense, hipStream_t s) {
+    hipLaunchKernelGGL((k_win_dec_part<T, D, NH>), dim3(nsplit, g.batch * g.Hkv), dim3(64), 0, s, g,
+                       (const T*)q, (const T*)k, (const T*)v, part, nsplit, split_keys, dense);
+}
+
 template <typename T, int D>
 hipError_t win_dec(const Geo& g, const void* q, const void* k, const void* v, void* out, float* part,
                    int nsplit, int split_keys, int dense, hipStream_t s) {
-    const size_t shmem = sizeof(float) * kMaxGroup * split_keys;
-    hipLaunchKernelGGL((k_win_dec_part<T, D>), dim3(nsplit, g.batch * g.Hkv), dim3(256), shmem, s, g,
-                       (const T*)q, (const T*)k, (const T*)v, part, nsplit, split_keys, dense);
+    if (g.group <= 1)
+        win_dec_part<T, D, 1>(g, q, k, v, part, nsplit, split_keys, dense, s);
+    else if (g.group <= 2)
+        win_dec_part<T, D, 2>(g, q, k, v, part, nsplit, split_keys, dense, s);
+    else if (g.group <= 4)
+        win_dec_part<T, D, 4>(g, q, k, v, part, nsplit, split_keys, dense, s);
+    else
+        win_dec_part<T, D, 8>(g, q, k, v, part, nsplit, split_keys, dense, s);
     hipLaunchKernelGGL((k_win_dec_combine<T, D>), dim3(g.Hq, g.batch), dim3(128), 0, s, g, part, (T*)out,
                        nsplit, split_keys, dense);
     return hipGetLastError();

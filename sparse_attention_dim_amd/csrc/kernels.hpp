@@ -59,9 +59,6 @@ struct SelWs {
     unsigned long long* hmass;    // [rows][kNB1]
     uint32_t* hcnt;               // [rows][kNB1]
     RowState* st;                 // [rows]
-    uint32_t* ctr;                // [rows] last-block counters (pass 2)
-    uint32_t* ctr2;               // [rows] last-block counters (pass 3)
-    uint32_t* gctr;               // [1]   last-row counter (pass 3)
     unsigned long long* cand;     // [rows][kCand]
     uint32_t* cand_n;             // [rows]
     uint32_t* chunk_cnt;          // [rows][nchunk] selected keys per chunk, then offsets

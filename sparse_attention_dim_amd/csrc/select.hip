@@ -12,13 +12,16 @@
 //
 // Passes (one row = one (query token, retrieval head) pair):
 //   1 score:   q_low, fp32 chain scores of every key, chunk maxima
-//   2 hist:    exact fixed-point mass per level-1 bin; the row's last chunk
-//              workgroup finds the bin b1 where the cumulative mass reaches p
+//   2 hist:    exact fixed-point mass per level-1 bin (device atomics)
+//   2b cut:    per row, the bin b1 where the cumulative mass reaches p
 //   3 refine:  per-chunk count of keys above b1; keys of bin b1 gathered
 //   4 resolve: one workgroup per row ranks bin b1 exactly (score desc, index
-//              asc), fixes the last selected key, the per-chunk output offsets,
-//              and (last row) the CSR row pointers and the capacity check
+//              asc), fixes the last selected key and the per-chunk offsets
+//   4b rowptr: CSR row pointers and the capacity check
 //   5 emit:    ordered compaction of the selected indices
+// Workgroups of one pass never wait on each other: every hand-off between
+// workgroups is a kernel boundary (a device-scope fence per workgroup costs an
+// L2 write-back and invalidate on this multi-XCD part).
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -81,15 +84,10 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         for (int i = chunk * 256 + tid; i < ws.nchunk; i += nthr)
             ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + i] = 0u;
         if (chunk == 0 && tid == 0) {
-            ws.ctr[ri.lrow] = 0u;
-            ws.ctr2[ri.lrow] = 0u;
             ws.cand_n[ri.lrow] = 0u;
-            if (ri.lrow == 0) {
-                *ws.gctr = 0u;
-                if (row0 == 0) {
-                    *out.status = 0;
-                    out.row_ptr[0] = 0;
-                }
+            if (ri.lrow == 0 && row0 == 0) {
+                *out.status = 0;
+                out.row_ptr[0] = 0;
             }
         }
     }
@@ -97,12 +95,42 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 
     __shared__ float qs[kIdx];
     __shared__ float wmax[4];
-    if (tid < kIdx) {
+    __shared__ float qrow[128];
+    __shared__ float wq[128 * kIdx];
+    const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
+    float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
+    const int jbase = chunk * kChunk;
+
+    // Issue the first group of indexer-key loads, then build q_low while they
+    // are in flight (the query row and W_q are staged through LDS so that the
+    // fixed-order chain runs on LDS operands).
+    uint4 buf[8];
+    // Unconditional loads: page ids are uniform per 256-key step (clamped to the
+    // row's last page) and slots past the row's end are read but never used.
+    const int last_page = (ri.L - 1) >> 8;
+    auto load_group = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int pi = min((jbase >> 8) + k0 + u, last_page);
+            const int page = bt[pi];
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                k_low + (((size_t)page * g.n_ret + ri.r) * kBlk + tid) * kIdx);
+            buf[2 * u] = kp[0];
+            buf[2 * u + 1] = kp[1];
+        }
+    };
+    load_group(0);
+    {
         const int h = g.ret_heads[ri.r];
         const T* qp = q + ((size_t)ri.t * g.Hq + h) * g.D;
-        const T* wp = w_q + (size_t)ri.r * g.D * kIdx + tid;
+        const T* wp = w_q + (size_t)ri.r * g.D * kIdx;
+        for (int x = tid; x < g.D; x += 256) qrow[x] = ld(qp + x);
+        for (int x = tid; x < g.D * kIdx; x += 256) wq[x] = ld(wp + x);
+    }
+    __syncthreads();
+    if (tid < kIdx) {
         float acc = 0.0f;
-        for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(ld(qp + d), ld(wp + d * kIdx), acc);
+        for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(qrow[d], wq[d * kIdx + tid], acc);
         const bf16_t qb = f2bf(acc);
         qs[tid] = bf2f(qb);
         if (chunk == 0) ws.qlow[(size_t)ri.lrow * kIdx + tid] = qb;
@@ -112,27 +140,10 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 #pragma unroll
     for (int c = 0; c < kIdx; ++c) qv[c] = qs[c];
 
-    const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
-    float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int jbase = chunk * kChunk;
     float mx = -INFINITY;
 #pragma unroll 1
     for (int k0 = 0; k0 < 16; k0 += 4) {
-        uint4 buf[8];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = jbase + (k0 + u) * 256 + tid;
-            if (j < ri.L) {
-                const int page = bt[j >> 8];
-                const uint4* kp = reinterpret_cast<const uint4*>(
-                    k_low + (((size_t)page * g.n_ret + ri.r) * kBlk + (j & 255)) * kIdx);
-                buf[2 * u] = kp[0];
-                buf[2 * u + 1] = kp[1];
-            } else {
-                buf[2 * u] = make_uint4(0, 0, 0, 0);
-                buf[2 * u + 1] = make_uint4(0, 0, 0, 0);
-            }
-        }
+        if (k0) load_group(k0);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = jbase + (k0 + u) * 256 + tid;
@@ -159,47 +170,56 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2.  Level-1 histogram of exact fixed-point mass, then the cut bin.
+// Pass 2.  Level-1 histogram of exact fixed-point mass.  grid (nhist, rows):
+// a workgroup covers kHistKeys keys (four score chunks), accumulates in LDS and
+// adds its non-empty bins to the row's histogram with device atomics (integer,
+// so the result does not depend on their order).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_sel_hist(Geo g, const float* __restrict__ top_p, int row0,
-                                                  SelWs ws) {
-    const int tid = threadIdx.x;
-    const int chunk = blockIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (chunk >= ri.nch) return;
-    __shared__ unsigned long long hm[kNB1];
-    __shared__ uint32_t hc[kNB1];
-    __shared__ uint32_t red[4];
-    __shared__ unsigned long long scan_sh[5];
-    __shared__ int s_last, s_b1;
+constexpr int kHistKeys = 4 * kChunk;
 
-    // row maximum from the chunk maxima
+__device__ __forceinline__ float row_max(const SelWs& ws, int lrow, int nch, uint32_t* red) {
+    const int tid = threadIdx.x;
     uint32_t mk = 0u;
-    for (int c = tid; c < ri.nch; c += 256) {
-        uint32_t v = ws.cmax[(size_t)ri.lrow * ws.nchunk + c];
+    for (int c = tid; c < nch; c += 256) {
+        const uint32_t v = ws.cmax[(size_t)lrow * ws.nchunk + c];
         mk = v > mk ? v : mk;
     }
     mk = wave_max_u32(mk);
     if ((tid & 63) == 0) red[tid >> 6] = mk;
+    __syncthreads();
+    mk = red[0];
+    for (int w = 1; w < 4; ++w) mk = red[w] > mk ? red[w] : mk;
+    __syncthreads();
+    return key_score(mk);
+}
+
+__global__ __launch_bounds__(256) void k_sel_hist(Geo g, int row0, SelWs ws) {
+    const int tid = threadIdx.x;
+    const RowInfo ri = row_info(g, row0, blockIdx.y);
+    const int jbase = blockIdx.x * kHistKeys;
+    if (jbase >= ri.L) return;
+    __shared__ unsigned long long hm[kNB1];
+    __shared__ uint32_t hc[kNB1];
+    __shared__ uint32_t red[4];
     for (int i = tid; i < kNB1; i += 256) {
         hm[i] = 0ull;
         hc[i] = 0u;
     }
-    __syncthreads();
-    mk = red[0];
-    for (int w = 1; w < 4; ++w) mk = red[w] > mk ? red[w] : mk;
-    const float m = key_score(mk);
+    const float m = row_max(ws, ri.lrow, ri.nch, red);
     const float s = g.idx_scale;
-
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int jbase = chunk * kChunk;
-#pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-        const int j = jbase + k * 256 + tid;
-        if (j < ri.L) {
-            const WeightBin wb = weight_bin(srow[j], m, s);
-            atomicAdd(&hm[wb.bin], wb.w);
-            atomicAdd(&hc[wb.bin], 1u);
+    for (int k0 = 0; k0 < kHistKeys / 256; k0 += 16) {
+        float dv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + (k0 + k) * 256 + tid, ri.L - 1)];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int j = jbase + (k0 + k) * 256 + tid;
+            if (j < ri.L) {
+                const WeightBin wb = weight_bin(dv[k], m, s);
+                atomicAdd(&hm[wb.bin], wb.w);
+                atomicAdd(&hc[wb.bin], 1u);
+            }
         }
     }
     __syncthreads();
@@ -209,29 +229,35 @@ __global__ __launch_bounds__(256) void k_sel_hist(Geo g, const float* __restrict
             atomicAdd(&ws.hcnt[(size_t)ri.lrow * kNB1 + i], hc[i]);
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(&ws.ctr[ri.lrow], 1u) == (uint32_t)(ri.nch - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
 
-    // The last chunk workgroup of the row: total mass and the cut bin.
+// ---------------------------------------------------------------------------
+// Pass 2b.  One workgroup per row: total mass, target ceil(p Z) and the bin b1
+// where the cumulative mass (highest scores first) reaches it.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sel_cut(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
+    const int tid = threadIdx.x;
+    const RowInfo ri = row_info(g, row0, blockIdx.x);
+    __shared__ uint32_t red[4], red2[4];
+    __shared__ unsigned long long scan_sh[5];
+    __shared__ int s_b1;
+    const float m = row_max(ws, ri.lrow, ri.nch, red);
     unsigned long long lm[8];
     uint32_t lc[8];
     unsigned long long msum = 0;
+#pragma unroll
     for (int i = 0; i < 8; ++i) {
-        lm[i] = ld_acquire(&ws.hmass[(size_t)ri.lrow * kNB1 + tid * 8 + i]);
-        lc[i] = ld_acquire(&ws.hcnt[(size_t)ri.lrow * kNB1 + tid * 8 + i]);
+        lm[i] = ws.hmass[(size_t)ri.lrow * kNB1 + tid * 8 + i];
+        lc[i] = ws.hcnt[(size_t)ri.lrow * kNB1 + tid * 8 + i];
         msum += lm[i];
     }
     unsigned long long Z;
     const unsigned long long before = block_excl_scan_u64<256>(msum, &Z, scan_sh);
     const float p = top_p[ri.b];
     unsigned long long target = Z;
-    int keep_all = !(p < 1.0f);
+    const int keep_all = !(p < 1.0f);
     if (!keep_all) {
-        double pz = ceil((double)p * (double)Z);
+        const double pz = ceil((double)p * (double)Z);
         target = (unsigned long long)pz;
         if (target > Z) target = Z;
         if (target < 1ull) target = 1ull;
@@ -250,17 +276,14 @@ __global__ __launch_bounds__(256) void k_sel_hist(Geo g, const float* __restrict
     }
     __syncthreads();
     const int b1 = s_b1;
-    // counts and mass above b1
     uint32_t ca = 0;
     unsigned long long sa = 0;
     for (int i = 0; i < 8; ++i) {
-        const int bi = tid * 8 + i;
-        if (bi < b1) {
+        if (tid * 8 + i < b1) {
             ca += lc[i];
             sa += lm[i];
         }
     }
-    __shared__ uint32_t red2[4];
     const uint32_t cnt_above = block_sum_u32<256>(ca, red2);
     unsigned long long S_above;
     (void)block_excl_scan_u64<256>(sa, &S_above, scan_sh);
@@ -272,7 +295,7 @@ __global__ __launch_bounds__(256) void k_sel_hist(Geo g, const float* __restrict
         st.target = target;
         st.S_above = S_above;
         st.cnt_above = cnt_above;
-        st.cnt_b1 = b1 < kNB1 ? ld_acquire(&ws.hcnt[(size_t)ri.lrow * kNB1 + b1]) : 0u;
+        st.cnt_b1 = b1 < kNB1 ? ws.hcnt[(size_t)ri.lrow * kNB1 + b1] : 0u;
         st.Tkey = 0u;
         st.jT = -1;
         st.L = ri.L;
@@ -300,10 +323,14 @@ __global__ __launch_bounds__(256) void k_sel_refine(Geo g, int row0, SelWs ws) {
         above = (uint32_t)min(kChunk, ri.L - jbase);
     } else {
         const bool gather = st.cnt_b1 <= (uint32_t)kCand;
+        float dv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + k * 256 + tid, ri.L - 1)];
+#pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int j = jbase + k * 256 + tid;
             if (j < ri.L) {
-                const float d = srow[j];
+                const float d = dv[k];
                 const int bn = bin_of(d, st.m, s);
                 if (bn < st.b1) {
                     ++above;
@@ -311,7 +338,7 @@ __global__ __launch_bounds__(256) void k_sel_refine(Geo g, int row0, SelWs ws) {
                     const uint32_t slot = atomicAdd(&ws.cand_n[ri.lrow], 1u);
                     if (slot < (uint32_t)kCand)
                         ws.cand[(size_t)ri.lrow * kCand + slot] =
-                        ((unsigned long long)score_key(d) << 32) | (unsigned long long)(~(uint32_t)j);
+                            ((unsigned long long)score_key(d) << 32) | (unsigned long long)(~(uint32_t)j);
                 }
             }
         }
@@ -383,7 +410,7 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws, 
     __shared__ uint32_t ccount[1024];          // per-chunk selected keys of bin b1
     __shared__ unsigned long long hmb[kNB1];
     __shared__ uint32_t hcb[kNB1];
-    __shared__ int s_idx, s_last;
+    __shared__ int s_idx;
     __shared__ uint32_t s_klo, s_khi, s_n;
     __shared__ unsigned long long s_S;
     RowState st = ws.st[ri.lrow];
@@ -526,41 +553,42 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws, 
         st.jT = jT;
     }
     __syncthreads();
-    // per-chunk output offsets of this row
-    if (tid == 0) {
-        uint32_t run = 0;
-        for (int c = 0; c < nch; ++c) {
-            uint32_t n_c;
+    // per-chunk output offsets of this row (nch <= 1024 chunks)
+    {
+        unsigned long long n_c = 0;
+        if (tid < nch) {
             if (st.b1 >= kNB1)
-                n_c = (uint32_t)min(kChunk, ri.L - c * kChunk);
+                n_c = (unsigned long long)min(kChunk, ri.L - tid * kChunk);
             else
-                n_c = ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + c] + ccount[c];
-            ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + c] = run;
-            run += n_c;
+                n_c = ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] + ccount[tid];
         }
-        st.count = (int32_t)run;
-        ws.st[ri.lrow] = st;
+        unsigned long long tot;
+        const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
+        if (tid < nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)ex;
+        if (tid == 0) {
+            st.count = (int32_t)tot;
+            ws.st[ri.lrow] = st;
+        }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) s_last = (atomicAdd(ws.gctr, 1u) == (uint32_t)(ws.rows - 1));
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    // Last row of the group: CSR row pointers and the capacity check.
-    const int64_t base = ld_acquire(&out.row_ptr[row0]);
-    int64_t carry = base;
+    (void)total_rows;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 4b.  CSR row pointers of the group's rows and the capacity check.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut out) {
+    const int tid = threadIdx.x;
+    __shared__ unsigned long long scan_sh[kRT / 64 + 1];
+    int64_t carry = out.row_ptr[row0];
     for (int i0 = 0; i0 < ws.rows; i0 += kRT) {
         const int i = i0 + tid;
-        const unsigned long long c =
-            i < ws.rows ? (unsigned long long)ld_acquire(&ws.st[i].count) : 0ull;
+        const unsigned long long c = i < ws.rows ? (unsigned long long)ws.st[i].count : 0ull;
         unsigned long long tot;
         const unsigned long long ex = block_excl_scan_u64<kRT>(c, &tot, scan_sh);
         if (i < ws.rows) out.row_ptr[row0 + i + 1] = carry + (int64_t)(ex + c);
         carry += (int64_t)tot;
     }
-    if (tid == 0 && carry > out.capacity) atomicExch(out.status, 1);
-    (void)total_rows;
+    if (tid == 0 && carry > out.capacity) *out.status = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -579,6 +607,9 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
     int64_t base = out.row_ptr[ri.row] + ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
     const int jbase = chunk * kChunk;
     const int lane = tid & 63, wid = tid >> 6;
+    float dv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + k * 256 + tid, ri.L - 1)];
     for (int k = 0; k < 16; ++k) {
         if (jbase + k * 256 >= ri.L) break;
         const int j = jbase + k * 256 + tid;
@@ -587,7 +618,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
             if (st.b1 >= kNB1) {
                 sel = true;
             } else {
-                const float d = srow[j];
+                const float d = dv[k];
                 const int bn = bin_of(d, st.m, s);
                 if (bn < st.b1) {
                     sel = true;
@@ -624,9 +655,12 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
         hipLaunchKernelGGL(k_sel_score<bf16_t>, grid, dim3(256), 0, s, g, (const bf16_t*)q,
                            (const bf16_t*)w_q, k_low, row0, ws, out, scores_only);
     if (scores_only) return hipGetLastError();
-    hipLaunchKernelGGL(k_sel_hist, grid, dim3(256), 0, s, g, top_p, row0, ws);
+    const int nhist = (ws.nchunk + 3) / 4;
+    hipLaunchKernelGGL(k_sel_hist, dim3(nhist, ws.rows), dim3(256), 0, s, g, row0, ws);
+    hipLaunchKernelGGL(k_sel_cut, dim3(ws.rows), dim3(256), 0, s, g, top_p, row0, ws);
     hipLaunchKernelGGL(k_sel_refine, grid, dim3(256), 0, s, g, row0, ws);
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws, out, total_rows);
+    hipLaunchKernelGGL(k_sel_rowptr, dim3(1), dim3(kRT), 0, s, row0, ws, out);
     hipLaunchKernelGGL(k_sel_emit, grid, dim3(256), 0, s, g, row0, ws, out);
     return hipGetLastError();
 }
