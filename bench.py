@@ -3,7 +3,9 @@
 One step = one decode step of one attention layer for the whole batch: the
 indexer append of the new tokens, top-p selection for every retrieval head,
 sparse attention over the selected rows, and window attention for the local
-heads (decode bf16, batch 8, context 131072, 32 query / 8 KV heads, head dim
+heads (on a second stream, overlapping the retrieval heads' work).  The same
+step captured as one HIP graph per layer instance is timed too and reported
+beside it. (decode bf16, batch 8, context 131072, 32 query / 8 KV heads, head dim
 128, 6 retrieval heads, top-p 0.95, window 2048 + 64 sinks).  Inputs are
 synthetic and resident in HBM before timing; four independent layer instances
 are rotated so that the 256 MB last-level cache cannot hold a layer's indexer
@@ -106,6 +108,8 @@ def main():
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--contiguous", action="store_true", help="pages in order instead of permuted")
+    ap.add_argument("--graph", action="store_true", help="time HIP graph replays instead of eager launches")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -130,7 +134,8 @@ def main():
 
     inst = []
     for i in range(args.instances):
-        pc = PagedCache(w.k, w.v, w.n_ret, w.dtype, device=dev, permute_seed=100 + i)
+        pc = PagedCache(w.k, w.v, w.n_ret, w.dtype, device=dev,
+                        permute_seed=None if args.contiguous else 100 + i)
         cache = pc.cache(L)
         q = to_device(w.q, dev)
         w_q, w_k = to_device(w.w_q, dev), to_device(w.w_k, dev)
@@ -176,23 +181,59 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    # The local heads do not depend on the retrieval heads' selection: they run
+    # on a second stream, forked from and joined back into the main stream.
+    side = torch.cuda.Stream()
+
+    def step_overlap(I):
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side)
+        rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"])
+        rtp.topp_select(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
+        rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"])
+        main.wait_stream(side)
+
     for s in range(args.warmup):
         step(inst[s % len(inst)])
+        step_overlap(inst[s % len(inst)])
     torch.cuda.synchronize()
     assert all(int(I["status"].item()) == 0 for I in inst), "selection capacity overflow"
 
-    # --- timed region: exactly `steps` steps -------------------------------
+    # per-call breakdown: sequential eager launches with events between calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
     for s in range(args.steps):
         step(inst[s % len(inst)], evs[s])
-    end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
     per_call = {c: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3
                 for i, c in enumerate(calls)}
+
+    def timed(fn):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for s in range(args.steps):
+            fn(s)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    eager_ms = timed(lambda s: step_overlap(inst[s % len(inst)]))
+
+    # one HIP graph per layer instance, replayed round-robin
+    graphs = []
+    for I in inst:
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph):
+            step_overlap(I)
+        graphs.append(gph)
+    for s in range(len(graphs) * 2):
+        graphs[s % len(graphs)].replay()
+    torch.cuda.synchronize()
+    graph_ms = timed(lambda s: graphs[s % len(graphs)].replay())
+    ms = graph_ms if args.graph else eager_ms
+    launch = "hip_graph" if args.graph else "eager, two streams"
 
     # --- algorithmic bytes of one step ---------------------------------------
     rp = inst[0]["row_ptr"].cpu().numpy()
@@ -280,6 +321,10 @@ def main():
                      "algorithmic_bytes": bytes_klow, "avg_launch_us": round(k_ms * 1e3, 2)},
         "cpu_baseline": cpu,
         "per_call_us": {k: round(v, 2) for k, v in per_call.items()},
+        "launch": launch,
+        "eager_overlap_us": round(eager_ms * 1e3, 2),
+        "graph_overlap_us": round(graph_ms * 1e3, 2),
+        "pages": "contiguous" if args.contiguous else "permuted",
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "selected_per_row": {"min": int(sizes.min()), "median": int(np.median(sizes)),

@@ -371,15 +371,42 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
     st.init();
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
+        if (i < nh) {
+            float f[EPV];
+            Pack<T>::unpack(*reinterpret_cast<const uint4*>(q + ((size_t)b * g.Hq + heads[i]) * D + sl), f);
 #pragma unroll
-        for (int e = 0; e < EPV; ++e)
-            st.q[i][e] = i < nh ? ld(q + ((size_t)b * g.Hq + heads[i]) * D + sl + e) * sc : 0.0f;
+            for (int e = 0; e < EPV; ++e) st.q[i][e] = f[e] * sc;
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) st.q[i][e] = 0.0f;
+        }
     }
+    // Page ids of the split, resolved once into LDS.  The split's virtual keys
+    // [v0, v0 + n) are a run of sink positions followed by a run of window
+    // positions; each run covers consecutive pages.
+    __shared__ int pgs[64];
     const int32_t* bt = g.block_table + (size_t)b * g.max_blocks;
+    const int vS1 = min(v0 + n, ns_end);
+    const int pS0 = v0 >> 8;
+    const int nPS = vS1 > v0 ? ((vS1 - 1) >> 8) - pS0 + 1 : 0;
+    const int jW0 = w_start + max(v0, ns_end) - ns_end;
+    const int jW1 = w_start + (v0 + n) - ns_end;
+    const int pW0 = jW0 >> 8;
+    const int nPW = jW1 > jW0 ? ((jW1 - 1) >> 8) - pW0 + 1 : 0;
+    if (lane < nPS) pgs[lane] = bt[pS0 + lane];
+    else if (lane < nPS + nPW) pgs[lane] = bt[pW0 + lane - nPS];
+    __syncthreads();
     auto off = [&](int i) {
         const int vi = v0 + i;
-        const int j = vi < ns_end ? vi : w_start + (vi - ns_end);
-        return kv_off(g, bt[j >> 8], kvh, j & 255, D);
+        int j, pi;
+        if (vi < ns_end) {
+            j = vi;
+            pi = (j >> 8) - pS0;
+        } else {
+            j = w_start + (vi - ns_end);
+            pi = nPS + (j >> 8) - pW0;
+        }
+        return kv_off(g, pgs[pi], kvh, j & 255, D);
     };
     st.run(n, nh, off, kc, vc);
     st.merge(nh);
