@@ -203,7 +203,8 @@ int win_keys(const rtp_layer* L, const rtp_cache* C, int dense) {
     return (int)std::min<int64_t>((int64_t)L->window + L->num_sinks, C->max_seq_len);
 }
 
-size_t win_ws_bytes(const rtp_layer* L, const rtp_cache* C, int dense) {
+size_t win_ws_bytes(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q, int dense) {
+    if (Q->kind == RTP_CHUNK) return 0;     // the prefill kernel needs no workspace
     const int split = dense ? kDenseSplit : kWinSplit;
     const int nsplit = (win_keys(L, C, dense) + split - 1) / split;
     return align256((size_t)C->batch * L->num_q_heads * nsplit * (L->head_dim + 2) * 4);
@@ -214,10 +215,18 @@ rtp_status window_like(const rtp_layer* L, const rtp_cache* C, const rtp_query* 
     rtp_status s = check_all(L, C, Q);
     if (s) return s;
     if (!out) return fail(RTP_EINVAL, "out is NULL");
-    if (Q->kind != RTP_DECODE)
-        return fail(RTP_EUNSUPPORTED, "%s attention of chunked queries is not built in this library version",
-                    dense ? "dense" : "window");
-    const size_t need = win_ws_bytes(L, C, dense);
+    if (Q->kind == RTP_CHUNK) {
+        if (L->dtype != RTP_BF16 || L->head_dim != 128)
+            return fail(RTP_EUNSUPPORTED, "chunked %s attention is built for bf16, head_dim 128",
+                        dense ? "dense" : "window");
+        rtp::Geo g = make_geo(L, C, Q);
+        g.n_hlist = 0;
+        for (int h = 0; h < L->num_q_heads; ++h)
+            if (dense || !g.is_ret[h]) g.hlist[g.n_hlist++] = h;
+        return hip_status(rtp::launch_prefill_attn(g, Q->q, C->k, C->v, out, dense, (hipStream_t)stream),
+                          dense ? "dense prefill launch" : "window prefill launch");
+    }
+    const size_t need = win_ws_bytes(L, C, Q, dense);
     if (!ws || ws_bytes < need) return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     const rtp::Geo g = make_geo(L, C, Q);
     const int split = dense ? kDenseSplit : kWinSplit;
@@ -330,32 +339,47 @@ rtp_status rtp_sparse_attn_decode(const rtp_layer* layer, const rtp_cache* cache
     w.max_items = items;
     const rtp::Geo g = make_geo(layer, cache, query);
     return hip_status(rtp::launch_sparse_decode(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
-                                                sel->status, out, w, rows, layer->dtype, (hipStream_t)stream),
+                                                sel->status, out, w, 0, rows, layer->dtype, (hipStream_t)stream),
                       "sparse decode launch");
 }
 
 rtp_status rtp_sparse_attn_prefill(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                                    const rtp_sel* sel, void* out, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-    (void)sel;
-    (void)out;
-    (void)workspace;
-    (void)workspace_bytes;
-    (void)stream;
     rtp_status s = check_all(layer, cache, query);
     if (s) return s;
     if (query->kind != RTP_CHUNK) return fail(RTP_EINVAL, "rtp_sparse_attn_prefill needs RTP_CHUNK queries");
-    return fail(RTP_EUNSUPPORTED, "sparse prefill attention is not built in this library version");
+    if (!sel || !sel->row_ptr || !sel->status || !out) return fail(RTP_EINVAL, "NULL selection / out");
+    if (sel->capacity > 0 && !sel->idx) return fail(RTP_EINVAL, "NULL idx");
+    const size_t need = rtp_sparse_attn_workspace(layer, cache, query, sel->capacity);
+    if (!workspace || workspace_bytes < need)
+        return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    const int rows = query->n_tok * layer->num_ret;
+    const int64_t items = sparse_max_items(layer, query, sel->capacity);
+    rtp::AttnWs w;
+    w.part = (float*)workspace;
+    w.item_start = (int32_t*)((char*)workspace + align256((size_t)items * (layer->head_dim + 2) * 4));
+    w.max_items = items;
+    const rtp::Geo g = make_geo(layer, cache, query);
+    // rows are processed in groups of at most kMaxDecodeRows; groups run in
+    // stream order and reuse the same partial buffer
+    for (int row0 = 0; row0 < rows; row0 += kMaxDecodeRows) {
+        const int nr = std::min(kMaxDecodeRows, rows - row0);
+        hipError_t e = rtp::launch_sparse_decode(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
+                                                 sel->status, out, w, row0, nr, layer->dtype, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_status(e, "sparse prefill launch");
+    }
+    return ok();
 }
 
 size_t rtp_window_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
     if (check_all(layer, cache, query)) return 0;
-    return win_ws_bytes(layer, cache, 0);
+    return win_ws_bytes(layer, cache, query, 0);
 }
 
 size_t rtp_dense_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
     if (check_all(layer, cache, query)) return 0;
-    return win_ws_bytes(layer, cache, 1);
+    return win_ws_bytes(layer, cache, query, 1);
 }
 
 rtp_status rtp_window_attn(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query, void* out,

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
                                                         const int64_t* __restrict__ row_ptr,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ status,
-                                                        AttnWs ws, int rows) {
+                                                        AttnWs ws, int row0, int rows) {
     using S = Stream<T, D, 1>;
     if (*status != 0) return;
     const int lane = threadIdx.x;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
     int32_t* istart = reinterpret_cast<int32_t*>(dyn + rows + 1);   // rows + 1
     __shared__ uint32_t joff[kItem];                      // page-resolved row offsets / D
     {   // pieces per row and their prefix (every workgroup recomputes it; rows <= 4096)
-        for (int r = lane; r <= rows; r += 64) rp[r] = row_ptr[r];
+        for (int r = lane; r <= rows; r += 64) rp[r] = row_ptr[row0 + r];
         __syncthreads();
         const int per = (rows + 63) / 64;
         const int r0 = lane * per;
@@ -241,11 +241,12 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
             if (istart[mid] <= item) lo = mid; else hi = mid - 1;
         }
         const int row = lo;
-        const int t = row / g.n_ret, r = row - t * g.n_ret;
+        const int grow = row0 + row;
+        const int t = grow / g.n_ret, r = grow - t * g.n_ret;
         const int h = g.ret_heads[r], kvh = h / g.group;
         const int64_t k0 = rp[row] + (int64_t)(item - istart[row]) * kItem;
         const int n = (int)min<int64_t>(kItem, rp[row + 1] - k0);
-        const int32_t* bt = g.block_table + (size_t)t * g.max_blocks;
+        const int32_t* bt = g.block_table + (size_t)row_seq(g, t) * g.max_blocks;
         // resolve the item's rows once: index -> page -> row offset (in units of D)
         int jl[kItem / 64];
 #pragma unroll
@@ -309,11 +310,12 @@ __device__ void combine_parts(const float* __restrict__ base, int n, T* __restri
 
 template <typename T, int D>
 __global__ __launch_bounds__(128) void k_sparse_dec_combine(Geo g, const int32_t* __restrict__ status,
-                                                            AttnWs ws, T* __restrict__ out) {
+                                                            AttnWs ws, T* __restrict__ out, int row0) {
     if (*status != 0) return;
     __shared__ float wsh[kMaxParts];
     const int row = blockIdx.x;
-    const int t = row / g.n_ret, r = row - t * g.n_ret;
+    const int grow = row0 + row;
+    const int t = grow / g.n_ret, r = grow - t * g.n_ret;
     const int h = g.ret_heads[r];
     const int i0 = ws.item_start[row], i1 = ws.item_start[row + 1];
     T* o = out + ((size_t)t * g.Hq + h) * D;
@@ -431,13 +433,13 @@ __global__ __launch_bounds__(128) void k_win_dec_combine(Geo g, const float* __r
 
 template <typename T, int D>
 hipError_t sparse_dec(const Geo& g, const void* q, const void* k, const void* v, const int64_t* row_ptr,
-                      const int32_t* idx, const int32_t* status, void* out, const AttnWs& ws, int rows,
-                      hipStream_t s) {
+                      const int32_t* idx, const int32_t* status, void* out, const AttnWs& ws, int row0,
+                      int rows, hipStream_t s) {
     const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
     const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
     hipLaunchKernelGGL((k_sparse_dec_part<T, D>), dim3((unsigned)grid), dim3(64), shmem, s, g,
-                       (const T*)q, (const T*)k, (const T*)v, row_ptr, idx, status, ws, rows);
-    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(128), 0, s, g, status, ws, (T*)out);
+                       (const T*)q, (const T*)k, (const T*)v, row_ptr, idx, status, ws, row0, rows);
+    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(128), 0, s, g, status, ws, (T*)out, row0);
     return hipGetLastError();
 }
 
@@ -468,11 +470,11 @@ hipError_t win_dec(const Geo& g, const void* q, const void* k, const void* v, vo
 
 hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, const void* v,
                                 const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
-                                void* out, const AttnWs& ws, int rows, int dtype, hipStream_t s) {
-    if (dtype == 0 && g.D == 64) return sparse_dec<float, 64>(g, q, k, v, row_ptr, idx, status, out, ws, rows, s);
-    if (dtype == 0 && g.D == 128) return sparse_dec<float, 128>(g, q, k, v, row_ptr, idx, status, out, ws, rows, s);
-    if (dtype == 1 && g.D == 64) return sparse_dec<bf16_t, 64>(g, q, k, v, row_ptr, idx, status, out, ws, rows, s);
-    return sparse_dec<bf16_t, 128>(g, q, k, v, row_ptr, idx, status, out, ws, rows, s);
+                                void* out, const AttnWs& ws, int row0, int rows, int dtype, hipStream_t s) {
+    if (dtype == 0 && g.D == 64) return sparse_dec<float, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (dtype == 0 && g.D == 128) return sparse_dec<float, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (dtype == 1 && g.D == 64) return sparse_dec<bf16_t, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    return sparse_dec<bf16_t, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
 }
 
 hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,

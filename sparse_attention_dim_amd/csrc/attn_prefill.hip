@@ -1,0 +1,250 @@
+// attn_prefill.hip -- chunked-prefill attention of the local heads (sinks +
+// causal sliding window) and dense causal attention, on gfx950 bf16 MFMA.
+//
+// Method: arXiv 2605.16928 abstract obs. (1) (most heads use a restricted
+// window); zhichai.net forum post "RTPurbo: Turning Dense LLMs into Sparse
+// Attention Models ...", "Three Key Insights" item 1.  Dense causal attention
+// is the same-GPU baseline of the speedup.
+//
+// Flash attention, one workgroup per (128 query rows, query head), four
+// wavefronts of 32 rows.  Per 64-key tile:
+//   S^T[key][q] = K . Q^T   v_mfma_f32_32x32x16_bf16, A = K rows from LDS,
+//                            B = Q^T held in registers (each lane one query)
+//   online softmax           in-lane: a lane holds 16 keys of one query; the
+//                            two half-waves hold the other 16 (one xor-32 swap)
+//   O^T[d][q] += V^T . P^T   A = V^T from a transposed LDS tile, B = P^T taken
+//                            straight from the S^T registers
+// The key order inside the second product is a fixed permutation that matches
+// the register layout of S^T, so P never moves between lanes.  A 64-key tile
+// of one KV head is one contiguous 16 KiB run of a page (pages hold 256 keys).
+#include <algorithm>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace rtp {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBM = 128;           // query rows per workgroup
+constexpr int kBN = 64;            // keys per tile
+constexpr int kD = 128;            // head dim of this kernel
+constexpr int kKsLd = kD + 8;      // K row stride in LDS (bf16), 272 B: conflict-free row reads
+constexpr int kVtLd = kBN + 4;     // V^T row stride in LDS (bf16), 136 B
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+struct TileRange {
+    int a0, a1;    // first run of tiles [a0, a1) (sinks), key positions
+    int b0, b1;    // second run [b0, b1) (window / causal), key positions
+};
+
+__device__ __forceinline__ TileRange tile_range(const Geo& g, int p_min, int p_max, int dense) {
+    TileRange r;
+    if (dense) {
+        r.a0 = 0;
+        r.a1 = 0;
+        r.b0 = 0;
+        r.b1 = p_max + 1;
+        return r;
+    }
+    r.a0 = 0;
+    r.a1 = min(((g.sinks + kBN - 1) / kBN) * kBN, p_max + 1);
+    int lo = max(p_min - g.window + 1, 0);
+    lo = (lo / kBN) * kBN;
+    r.b0 = max(lo, r.a1);
+    r.b1 = p_max + 1;
+    if (r.b0 >= r.b1) r.b0 = r.b1;
+    return r;
+}
+
+// grid (ceil(n_tok / kBM), n_heads): heads[] lists the query heads to compute.
+__global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restrict__ q,
+                                                    const bf16_t* __restrict__ kc,
+                                                    const bf16_t* __restrict__ vc, bf16_t* __restrict__ out,
+                                                    int dense) {
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[kBN * kKsLd];
+    __shared__ __attribute__((aligned(16))) bf16_t Vt[kD * kVtLd];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int hq = g.hlist[blockIdx.y];
+    const int kvh = hq / g.group;
+    const int t0 = blockIdx.x * kBM;
+    const int n_valid = min(kBM, g.n_tok - t0);
+    const int p_min = g.pos0 + t0, p_max = g.pos0 + t0 + n_valid - 1;
+    const int hh = lane >> 5;                        // half-wave
+    const int qi = lane & 31;                        // query of this lane within the wave
+    const int t = t0 + wid * 32 + qi;                // query row
+    const bool qok = t < g.n_tok;
+    const int pq = g.pos0 + t;                       // its position
+    const float sc = g.attn_scale * kLog2e;
+    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
+
+    // Q^T operand: lane holds Q[t][16 kk + 8 hh + 0..7] for kk = 0..7
+    uint4 qreg[8];
+    {
+        const bf16_t* qp = q + ((size_t)min(t, g.n_tok - 1) * g.Hq + hq) * kD + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) qreg[kk] = qok ? *reinterpret_cast<const uint4*>(qp + 16 * kk)
+                                                      : make_uint4(0, 0, 0, 0);
+    }
+    f32x16_t oacc[4];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dd][i] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const TileRange tr = tile_range(g, p_min, p_max, dense);
+    const int na = (tr.a1 - tr.a0 + kBN - 1) / kBN;
+    const int nb = (tr.b1 - tr.b0 + kBN - 1) / kBN;
+    const int ntiles = na + nb;
+
+    // tile loads: 16 KiB of K and of V per tile, four 16-byte vectors per thread each
+    uint4 kv_k[4], kv_v[4];
+    auto tile_key0 = [&](int it) { return it < na ? tr.a0 + it * kBN : tr.b0 + (it - na) * kBN; };
+    auto load_tile = [&](int it) {
+        const int k0 = tile_key0(it);
+        const int page = bt[k0 >> 8];
+        const size_t base = (((size_t)page * g.Hkv + kvh) * kBlk + (k0 & 255)) * kD;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            kv_k[j] = reinterpret_cast<const uint4*>(kc + base)[tid + 256 * j];
+            kv_v[j] = reinterpret_cast<const uint4*>(vc + base)[tid + 256 * j];
+        }
+    };
+    if (ntiles > 0) load_tile(0);
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int k0 = tile_key0(it);
+        __syncthreads();                              // previous tile's LDS reads are done
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e = (tid + 256 * j) * 8;        // element of the 64 x 128 tile
+            const int r = e >> 7, c = e & 127;
+            *reinterpret_cast<uint4*>(&Ks[r * kKsLd + c]) = kv_k[j];
+            // keys past the last query position may be unwritten cache slots:
+            // store zeros so that p = 0 never meets a non-finite value
+            const bool live = k0 + r <= p_max;
+            const uint32_t w[4] = {live ? kv_v[j].x : 0u, live ? kv_v[j].y : 0u, live ? kv_v[j].z : 0u,
+                                   live ? kv_v[j].w : 0u};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                Vt[(c + 2 * x) * kVtLd + r] = (bf16_t)(w[x] & 0xFFFFu);
+                Vt[(c + 2 * x + 1) * kVtLd + r] = (bf16_t)(w[x] >> 16);
+            }
+        }
+        __syncthreads();
+        if (it + 1 < ntiles) load_tile(it + 1);       // prefetch while computing
+
+        // S^T for the two 32-key halves of the tile
+        f32x16_t s[2];
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[sh][i] = 0.0f;
+            const bf16_t* krow = &Ks[(32 * sh + qi) * kKsLd + 8 * hh];
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const uint4 a = *reinterpret_cast<const uint4*>(krow + 16 * kk);
+                s[sh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[sh], 0, 0, 0);
+            }
+        }
+        // scale, mask, tile maximum of this lane's query
+        float mt = -INFINITY;
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = k0 + 32 * sh + (i >> 2) * 8 + 4 * hh + (i & 3);
+                bool ok = qok && key <= pq;
+                if (!dense) ok = ok && (key < g.sinks || key > pq - g.window);
+                const float v = ok ? s[sh][i] * sc : -INFINITY;
+                s[sh][i] = v;
+                mt = fmaxf(mt, v);
+            }
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);
+        uint32_t pb[2][8];                           // P^T as bf16 pairs, per half and kk
+        if (m_new == -INFINITY) {
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pb[sh][x] = 0u;
+        } else {
+            const float corr = exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= corr;
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dd][i] *= corr;
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) {
+                float p[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    p[i] = exp2f(s[sh][i] - m_new);
+                    l_run += p[i];
+                }
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pb[sh][x] = pack2(p[2 * x], p[2 * x + 1]);
+            }
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint4 bp = make_uint4(pb[sh][4 * kk], pb[sh][4 * kk + 1], pb[sh][4 * kk + 2], pb[sh][4 * kk + 3]);
+                const int kc0 = 32 * sh + 16 * kk + 4 * hh;
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd) {
+                    const bf16_t* vr = &Vt[(32 * dd + qi) * kVtLd + kc0];
+                    const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                    const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    oacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), oacc[dd], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // normalise and store: lane holds O[t][32 dd + 8 (i/4) + 4 hh + (i%4)]
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (qok) {
+        const float inv = 1.0f / l_tot;
+        bf16_t* op = out + ((size_t)t * g.Hq + hq) * kD;
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * dd + 8 * r4 + 4 * hh;
+                uint2 v;
+                v.x = pack2(oacc[dd][4 * r4 + 0] * inv, oacc[dd][4 * r4 + 1] * inv);
+                v.y = pack2(oacc[dd][4 * r4 + 2] * inv, oacc[dd][4 * r4 + 3] * inv);
+                *reinterpret_cast<uint2*>(op + d0) = v;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn(const Geo& g, const void* q, const void* k, const void* v, void* out,
+                               int dense, hipStream_t s) {
+    if (g.n_hlist == 0) return hipSuccess;
+    const dim3 grid((g.n_tok + kBM - 1) / kBM, g.n_hlist);
+    hipLaunchKernelGGL(k_fa_prefill, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)k,
+                       (const bf16_t*)v, (bf16_t*)out, dense);
+    return hipGetLastError();
+}
+
+}  // namespace rtp

@@ -19,6 +19,8 @@ struct Geo {
     int kind, seq, pos0, n_tok;   // query rows
     int batch, max_blocks;
     int max_seq_len;              // host bound; device lengths are clamped to [1, max_seq_len]
+    int n_hlist;                  // heads computed by a prefill attention launch
+    int hlist[256];
     const int32_t* block_table;
     const int32_t* seq_lens;
 };
@@ -90,9 +92,15 @@ struct AttnWs {
     int32_t* item_start;          // [rows + 1]
     int64_t max_items;
 };
+// Rows [row0, row0 + rows) of the call (rows <= 4096); row_ptr is the full CSR array.
 hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, const void* v,
                                 const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
-                                void* out, const AttnWs& ws, int rows, int dtype, hipStream_t s);
+                                void* out, const AttnWs& ws, int row0, int rows, int dtype, hipStream_t s);
+
+// Chunked-prefill attention (bf16, D = 128) of the heads g.hlist[0..n_hlist):
+// sinks + causal window, or dense causal.
+hipError_t launch_prefill_attn(const Geo& g, const void* q, const void* k, const void* v, void* out,
+                               int dense, hipStream_t s);
 
 // Local-head (window) or dense decode attention, split over keys, then combine.
 hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,
