@@ -258,8 +258,16 @@ rtp_status rtp_indexer_append(const rtp_layer* layer, const rtp_cache* cache, co
                       "indexer append launch");
 }
 
+// Prefill chunks in bf16 take the tiled selection (the rows of one retrieval
+// head share every indexer-key tile); decode rows and fp32 chunks take the
+// per-row passes.
+bool tiled_select(const rtp_layer* L, const rtp_query* Q) {
+    return Q->kind == RTP_CHUNK && L->dtype == RTP_BF16;
+}
+
 size_t rtp_topp_select_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
     if (check_all(layer, cache, query)) return 0;
+    if (tiled_select(layer, query)) return rtp::chunk_select_ws_bytes(query->n_tok * layer->num_ret);
     return plan_select(layer, cache, query).total;
 }
 
@@ -271,11 +279,19 @@ rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const
     if (!w_q || !top_p) return fail(RTP_EINVAL, "NULL w_q / top_p");
     if (!sel || !sel->row_ptr || !sel->status || (sel->capacity > 0 && !sel->idx) || sel->capacity < 0)
         return fail(RTP_EINVAL, "bad selection buffers");
+    const rtp::Geo g = make_geo(layer, cache, query);
+    rtp::SelOut out{sel->row_ptr, sel->idx, sel->capacity, sel->status};
+    if (tiled_select(layer, query)) {
+        const size_t need = rtp::chunk_select_ws_bytes(query->n_tok * layer->num_ret);
+        if (!workspace || workspace_bytes < need)
+            return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+        return hip_status(rtp::launch_chunk_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p,
+                                                   workspace, out, (hipStream_t)stream),
+                          "chunk select launch");
+    }
     const SelPlan p = plan_select(layer, cache, query);
     if (!workspace || workspace_bytes < p.total)
         return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, p.total);
-    const rtp::Geo g = make_geo(layer, cache, query);
-    rtp::SelOut out{sel->row_ptr, sel->idx, sel->capacity, sel->status};
     rtp::SelWs w = sel_ws(p, (char*)workspace);
     for (int row0 = 0; row0 < p.rows_total; row0 += p.group_rows) {
         w.rows = std::min(p.group_rows, p.rows_total - row0);

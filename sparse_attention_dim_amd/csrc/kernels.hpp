@@ -97,6 +97,13 @@ hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, cons
                                 const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
                                 void* out, const AttnWs& ws, int row0, int rows, int dtype, hipStream_t s);
 
+// Top-p selection of the rows of one prefill chunk (bf16, D <= 128): indexer
+// scores of 32-row x 32-key tiles by MFMA as a filter, exact fixed-order
+// scores only where they decide the set; same result as launch_select.
+size_t chunk_select_ws_bytes(int rows);
+hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
+                               const float* top_p, void* ws, const SelOut& out, hipStream_t s);
+
 // Chunked-prefill attention (bf16, D = 128) of the heads g.hlist[0..n_hlist):
 // sinks + causal window, or dense causal.
 hipError_t launch_prefill_attn(const Geo& g, const void* q, const void* k, const void* v, void* out,

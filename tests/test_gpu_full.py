@@ -178,5 +178,21 @@ def test_full_prefill_128k():
 
 
 def test_full_prefill_1m():
-    pytest.skip("top-p selection of the 1M-context chunk needs the tiled prefill selection; "
-                "the per-row selection pass stores every score (about 200 GB at this size)")
+    rows_t = [0, 1, 4095, 8191] + [int(x) for x in np.random.default_rng(4).choice(8192, 3, replace=False)]
+    w, d, out = _prefill_case(4, rows_t)
+    say("[gpu-full] %s: select + sparse prefill" % w.name)
+    cap = int(w.n_tok * w.n_ret * 16384)
+    st, rp, sets = d.select(capacity=cap)
+    if st == 1:
+        # the selection did not fit: rerun with the exact total it reported
+        cap = int(rp[-1])
+        say("   capacity %d" % cap)
+        st, rp, sets = d.select(capacity=cap)
+    assert st == 0
+    d.sparse()
+    out = out_f32(d.out)
+    res = _check_rows(w, d, [(t, r) for t in rows_t for r in range(w.n_ret)], sets, out, {})
+    sizes = [n for *_, n in res]
+    say("   budgets of checked rows: min %d median %d max %d" % (min(sizes), int(np.median(sizes)), max(sizes)))
+    del d
+    _free()
