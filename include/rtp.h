@@ -94,7 +94,8 @@ typedef struct rtp_cache {
     const int32_t *seq_lens;        /* [batch] tokens in the cache, incl. those appended this step */
     int32_t batch;
     int32_t max_blocks;             /* row stride of block_table */
-    int32_t max_seq_len;            /* [host] upper bound of every seq_lens[b]; sizes grids and workspaces */
+    int32_t max_seq_len;            /* [host] upper bound of every seq_lens[b], at most 2^20 (the exact
+                                       fixed-point mass sums hold 2^20 keys); sizes grids and workspaces */
 } rtp_cache;
 
 /* [host] struct: the query rows of one call. */
@@ -112,7 +113,8 @@ typedef struct rtp_sel {
     int32_t *idx;                   /* [capacity] */
     int64_t capacity;               /* [host] entries available in idx */
     int32_t *status;                /* one int: 0 = ok, 1 = capacity overflow (then idx is not written
-                                       and row_ptr[rows] holds the capacity needed) */
+                                       and row_ptr[rows] holds the capacity needed), 2 = selection not
+                                       certified (nothing written) */
 } rtp_sel;
 
 /* Library version (RTP_VERSION). */
@@ -132,8 +134,14 @@ const char *rtp_last_error(void);
 rtp_status rtp_indexer_append(const rtp_layer *layer, const rtp_cache *cache, const void *w_k,
                               const int32_t *seq_id, const int32_t *pos, int32_t n, void *stream);
 
-/* Workspace bytes needed by rtp_topp_select / rtp_indexer_scores for this query. */
+/* Workspace bytes needed by rtp_topp_select / rtp_indexer_scores for this query.
+ * For a bf16 RTP_CHUNK query this size holds a candidate buffer of 8192 keys
+ * per row; rtp_topp_select also accepts any workspace down to
+ * rtp_topp_select_workspace_min, and then resolves the rows whose candidate
+ * set does not fit the smaller buffer by extra passes over the keys (same
+ * result, more time).  For other queries both functions return the same size. */
 size_t rtp_topp_select_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query);
+size_t rtp_topp_select_workspace_min(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query);
 
 /*
  * a2-a4. Indexer query projection, indexer scores over every causal key, and
@@ -150,7 +158,9 @@ size_t rtp_topp_select_workspace(const rtp_layer *layer, const rtp_cache *cache,
  *   exact-arithmetic one only where a cumulative mass lies within 1e-6 of p.
  * top_p: device float[batch], each in (0, 1] (device values are not checked).
  * On overflow (total > sel->capacity) *status = 1, row_ptr is complete and
- * idx is untouched.
+ * idx is untouched.  *status = 2 means the chunk selection could not certify
+ * a row's cut (an internal error bound was violated): nothing is written and
+ * row_ptr is not meaningful.
  */
 rtp_status rtp_topp_select(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
                            const void *w_q, const float *top_p, const rtp_sel *sel,

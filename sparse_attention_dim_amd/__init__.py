@@ -23,6 +23,7 @@ RTP_MAX_RET = 64
 
 ENTRY_POINTS = (
     "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_topp_select_workspace",
+    "rtp_topp_select_workspace_min",
     "rtp_topp_select", "rtp_indexer_scores", "rtp_sparse_attn_workspace",
     "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_window_attn_workspace",
     "rtp_dense_attn_workspace", "rtp_window_attn", "rtp_dense_attn",
@@ -79,6 +80,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_last_error": ([], ctypes.c_char_p),
         "rtp_indexer_append": ([pl, pc, P, P, P, i32, P], ctypes.c_int),
         "rtp_topp_select_workspace": ([pl, pc, pq], S),
+        "rtp_topp_select_workspace_min": ([pl, pc, pq], S),
         "rtp_topp_select": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
         "rtp_indexer_scores": ([pl, pc, pq, P, P, P, i64, P, S, P], ctypes.c_int),
         "rtp_sparse_attn_workspace": ([pl, pc, pq, i64], S),
@@ -160,6 +162,10 @@ def indexer_append(layer, cache, w_k, seq_id, pos, stream=None):
 
 def topp_select_workspace(layer, cache, query) -> int:
     return load().rtp_topp_select_workspace(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query))
+
+
+def topp_select_workspace_min(layer, cache, query) -> int:
+    return load().rtp_topp_select_workspace_min(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query))
 
 
 def topp_select(layer, cache, query, w_q, top_p, sel, ws, stream=None):

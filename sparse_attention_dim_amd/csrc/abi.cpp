@@ -38,7 +38,7 @@ rtp_status hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
-constexpr int kMaxLen = 1 << 22;          // longest supported context
+constexpr int kMaxLen = 1 << 20;          // longest supported context: fixed-point masses of every key fit 2^63
 constexpr int kMaxDecodeRows = 4096;      // decode rows (batch * num_ret) of the sparse kernel
 constexpr int kWinSplit = 64;             // keys per workgroup, local-head decode
 constexpr int kDenseSplit = 1024;         // keys per workgroup, dense decode
@@ -151,6 +151,13 @@ struct SelPlan {
         off_cand, off_cand_n, off_chunk, total;
 };
 
+// Prefill chunks in bf16 take the tiled selection (the rows of one retrieval
+// head share every indexer-key tile); decode rows and fp32 chunks take the
+// per-row passes.
+bool tiled_select(const rtp_layer* L, const rtp_query* Q) {
+    return Q->kind == RTP_CHUNK && L->dtype == RTP_BF16;
+}
+
 SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
     SelPlan p;
     p.rows_total = Q->n_tok * L->num_ret;
@@ -258,16 +265,18 @@ rtp_status rtp_indexer_append(const rtp_layer* layer, const rtp_cache* cache, co
                       "indexer append launch");
 }
 
-// Prefill chunks in bf16 take the tiled selection (the rows of one retrieval
-// head share every indexer-key tile); decode rows and fp32 chunks take the
-// per-row passes.
-bool tiled_select(const rtp_layer* L, const rtp_query* Q) {
-    return Q->kind == RTP_CHUNK && L->dtype == RTP_BF16;
-}
-
 size_t rtp_topp_select_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
     if (check_all(layer, cache, query)) return 0;
-    if (tiled_select(layer, query)) return rtp::chunk_select_ws_bytes(query->n_tok * layer->num_ret);
+    if (tiled_select(layer, query))
+        return rtp::chunk_select_ws_bytes(query->n_tok * layer->num_ret, layer->num_ret, query->pos0 + query->n_tok);
+    return plan_select(layer, cache, query).total;
+}
+
+size_t rtp_topp_select_workspace_min(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {
+    if (check_all(layer, cache, query)) return 0;
+    if (tiled_select(layer, query))
+        return rtp::chunk_select_head_bytes(query->n_tok * layer->num_ret, layer->num_ret,
+                                            query->pos0 + query->n_tok);
     return plan_select(layer, cache, query).total;
 }
 
@@ -282,11 +291,12 @@ rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const
     const rtp::Geo g = make_geo(layer, cache, query);
     rtp::SelOut out{sel->row_ptr, sel->idx, sel->capacity, sel->status};
     if (tiled_select(layer, query)) {
-        const size_t need = rtp::chunk_select_ws_bytes(query->n_tok * layer->num_ret);
+        const size_t need = rtp::chunk_select_head_bytes(query->n_tok * layer->num_ret, layer->num_ret,
+                                                         query->pos0 + query->n_tok);
         if (!workspace || workspace_bytes < need)
             return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
         return hip_status(rtp::launch_chunk_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p,
-                                                   workspace, out, (hipStream_t)stream),
+                                                   workspace, workspace_bytes, out, (hipStream_t)stream),
                           "chunk select launch");
     }
     const SelPlan p = plan_select(layer, cache, query);

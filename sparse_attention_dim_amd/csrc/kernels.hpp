@@ -100,9 +100,12 @@ hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, cons
 // Top-p selection of the rows of one prefill chunk (bf16, D <= 128): indexer
 // scores of 32-row x 32-key tiles by MFMA as a filter, exact fixed-order
 // scores only where they decide the set; same result as launch_select.
-size_t chunk_select_ws_bytes(int rows);
+// Workspace: chunk_select_head_bytes at least; the rest is a pool of
+// candidate entries, chunk_select_ws_bytes recommends 4096 per row.
+size_t chunk_select_head_bytes(int rows, int n_ret, int n_keys);
+size_t chunk_select_ws_bytes(int rows, int n_ret, int n_keys);
 hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
-                               const float* top_p, void* ws, const SelOut& out, hipStream_t s);
+                               const float* top_p, void* ws, size_t ws_bytes, const SelOut& out, hipStream_t s);
 
 // Chunked-prefill attention (bf16, D = 128) of the heads g.hlist[0..n_hlist):
 // sinks + causal window, or dense causal.

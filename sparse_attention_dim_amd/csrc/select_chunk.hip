@@ -8,24 +8,30 @@
 // d = fp32 chain over c = 0..15 of q_low[c] * k_low[c] (exact bf16 products),
 // ranked by (d descending, index ascending), cut where the indexer-softmax mass
 // reaches p.  Prefill rows of one retrieval head share every key, so the
-// 16-wide contraction of a 32-row x 32-key tile is one
-// v_mfma_f32_32x32x16_bf16.  The MFMA sum is not the fixed-order chain, but
-// it lies within delta = 2^-16 |q_low| max|k_low| of it (the chain's own
+// 16-wide contraction of a 32-key x 32-row tile is one
+// v_mfma_f32_32x32x16_bf16.  The MFMA sum e is not the fixed-order chain, but
+// |e - d| <= delta / 8 with delta = 2^-16 |q_low| max|k_low| (the chain's own
 // rounding is at most ~2^-20 sum|q_c k_c| and the measured MFMA deviation is
-// below 2^-21 sum|q_c k_c|), so
-//   * the row maximum is bounded by m' = max(MFMA score) + delta;
-//   * an approximate mass histogram over MFMA scores locates the cut, with the
-//     target raised by a margin that covers the approximation; every key that
-//     can rank above the exact cut lies in the set U of keys whose approximate
-//     bin is at most one past that cut bin (bins are 1 / (2 s) wide in score,
-//     far wider than delta);
-//   * exact scores and exact fixed-point masses are computed for U only and
-//     refined by radix levels on the exact score until the cut is resolved;
-//   * keys outside U enter the total mass with their approximate weights
-//     (they hold at most the 1 - p tail, so the relative error of the
-//     cumulative mass stays far inside 1e-6).
-// Kernels: main (passes + resolve, one workgroup per 32 rows of one head),
-// row pointers, emit (ordered, exact near the cut, ties by lowest index).
+// below 2^-21 sum|q_c k_c|).  Passes of one workgroup over its 32 rows x all
+// keys of one head:
+//   P1  row maxima of e: m' = max e + delta >= max d (the largest key norm
+//       comes from a pre-pass over the head's indexer keys);
+//   P2  mass and count histograms over x = s (m' - e) in bins of 1/4 (weights
+//       exp(-x) summed in fp64 LDS atomics); the cut bin with a target raised
+//       by a margin that covers the approximation; U = bins <= cut + 1.  Bins
+//       are far wider than s delta, so every key ranked at or above the exact
+//       cut is in U;
+//   P3  exact scores and exact fixed-point weights of U's keys only: the
+//       exact mass of U, and U's (score, index) pairs into a segment of a
+//       shared pool, sized by the count histogram.  Keys outside U enter the
+//       total with their approximate fp64 weights (they hold at most the
+//       1 - p tail; their relative error is below s delta / 8).
+// A row with a segment is resolved by one workgroup that sorts it; a row
+// whose U is too large for a segment (or finds the pool full) is narrowed by
+// radix levels on the exact score inside the main kernel (extra passes behind
+// the MFMA filter), then emitted by a rescan.  Every result is certified: the
+// cut score must lie above every exact score that a key outside U can have,
+// else the call reports status 2.
 #include <algorithm>
 
 #include "device.hpp"
@@ -39,22 +45,39 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTR = 32;          // rows per workgroup
-constexpr int kNB = 64;          // bins per histogram level
-constexpr int kCapC = 128;       // exact candidates resolved by one sort per row
+constexpr int kHB = 128;         // P2 histogram bins
+constexpr int kHBP = kHB + 1;    // padded row stride, spreads rows over LDS banks
+constexpr float kBinsPerX = 4.0f;
+constexpr int kNB = 64;          // radix buckets per level
+constexpr int kNBP = kNB + 1;
+constexpr int kCapC = 128;       // candidates of one cut bucket sorted in LDS
+constexpr int kSmallU = 8192;    // U sorted by the per-row resolve kernel
+constexpr int kSegMax = 16384;   // largest U given a pool segment (sorted by the large-row kernel)
+constexpr int kPoolPerRow = 4096;   // pool entries per row in the recommended workspace
+constexpr int kNormKeys = 4096;  // keys per block of the key-norm pre-pass
 constexpr int kQ = 64;           // exact-work queue length per wave
-constexpr float kBin1 = 2.0f;    // level-1 bins per unit of x = s (m' - e)
 constexpr float kLog2eF = 1.4426950408889634f;
+constexpr unsigned long long kNoSeg = ~0ull;
+
+// modes of a row
+constexpr int kAll = 0;          // p >= 1: every key
+constexpr int kLevel = 2;        // threshold found by radix levels (rescan emit)
+constexpr int kBuf = 3;          // U held in the buffer (sorted by the resolve kernel)
 
 // Per-row result of the main kernel (device workspace).
 struct CRow {
     float mp;        // m' (upper bound of the row's exact maximum)
-    float delta;     // |MFMA - exact| bound of the row
-    float T;         // exact score of the cut
-    int mode;        // 0 keep all, 1 all of U, 2 threshold
-    int u_end;       // last level-1 bin of U
-    int n_tie;       // keys with d == T taken (lowest indices)
-    int count;       // selected keys
-    int pad;
+    float delta;     // 8x the |MFMA - exact| bound of the row
+    float mpB;       // m' s kBinsPerX: bin argument x = mpB - e s kBinsPerX
+    float T;         // exact score of the cut (kLevel)
+    float d_edge;    // exact scores of keys outside U are <= d_edge
+    int mode;
+    int u_end;       // last P2 bin of U
+    int n_tie;       // keys with d == T taken, lowest indices first (kLevel)
+    int count;       // selected keys (kLevel) or U entries in the segment (kBuf)
+    int bad;         // certification failed
+    unsigned long long target;   // fixed-point mass to reach
+    unsigned long long seg;      // pool offset of the row's segment (kBuf)
 };
 
 // orders this wave's LDS writes before its following LDS reads (other lanes)
@@ -84,23 +107,49 @@ __device__ __forceinline__ float exact_score(const float* q16, uint4 k0, uint4 k
     return acc;
 }
 
-// approximate weight in fixed point: exp(-x) * 2^43 (x >= 0), truncated
-__device__ __forceinline__ unsigned long long approx_w(float x) {
-    const float f = exp2f(-x * kLog2eF) * 8796093022208.0f;
-    if (!(f >= 1.0f)) return 0ull;
-    const uint32_t u = __float_as_uint(f);
-    const int e = (int)(u >> 23) - 150;
-    const unsigned long long m = (u & 0x7FFFFFu) | 0x800000u;
-    return e >= 0 ? (m << e) : (m >> (-e));
+// P2 bin argument of an MFMA score, x = (m' - e) s kBinsPerX >= 0 (m' - e >=
+// delta, far above the rounding of m' s kBinsPerX), and its bin.  The same
+// operations run in every pass, so a pair's bin never changes.
+__device__ __forceinline__ float bin_x(float e, float sB, float mpB) { return __builtin_fmaf(-e, sB, mpB); }
+__device__ __forceinline__ int bin_of(float x) {
+    return (int)__builtin_amdgcn_fmed3f(x, 0.0f, (float)(kHB - 1));
 }
 
-__device__ __forceinline__ int bin1_of(float x) {
-    return (int)fminf(x * kBin1, (float)(kNB - 1));
+// Visits tiles first, first + stride, ... < ntile (a wave-uniform sequence)
+// with D tile loads in flight: the A operand of tile it + D stride is
+// requested before tile it is processed.
+template <int D, typename Load, typename Body>
+__device__ __forceinline__ void tile_loop(int first, int stride, int ntile, Load load, Body body) {
+    uint4 ring[D];
+#pragma unroll
+    for (int x = 0; x < D; ++x) {
+        const int it = first + x * stride;
+        ring[x] = it < ntile ? load(it) : make_uint4(0, 0, 0, 0);
+    }
+    for (int it0 = first; it0 < ntile; it0 += D * stride) {
+#pragma unroll
+        for (int x = 0; x < D; ++x) {
+            const int it = it0 + x * stride;
+            if (it < ntile) {
+                const uint4 cur = ring[x];
+                if (it + D * stride < ntile) ring[x] = load(it + D * stride);
+                body(it, cur);
+            }
+        }
+    }
 }
+constexpr int kPre = 8;          // tile loads in flight per wave
 
-struct Tile {
-    int page_off;    // element offset of the tile's first key row in k_low
-};
+// LDS layout: the q projection weights, the P2 histogram and the level
+// structures are live at different times and share one buffer.
+constexpr int kHistBytes = kTR * kHBP * 8 + kTR * kHBP * 4;
+constexpr int kHmBytes = kTR * kNBP * 8;
+constexpr int kHcBytes = kTR * kNBP * 4;
+constexpr int kCandBytes = kTR * kCapC * 8;
+constexpr int kLevelBytes = kHmBytes + kHcBytes + kCandBytes;
+constexpr int kSmemBytes = kLevelBytes > kHistBytes ? kLevelBytes : kHistBytes;
+static_assert(128 * 16 * 4 <= kSmemBytes, "q projection weights fit the shared buffer");
+static_assert(kHmBytes % 16 == 0 && (kHmBytes + kHcBytes) % 8 == 0, "aligned level structures");
 
 // ---------------------------------------------------------------------------
 // Main kernel.  grid (ceil(n_tok / 32), n_ret), 256 threads.
@@ -109,59 +158,70 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                                                    const bf16_t* __restrict__ w_q,
                                                    const bf16_t* __restrict__ k_low,
                                                    const float* __restrict__ top_p, CRow* __restrict__ rows_out,
-                                                   uint16_t* __restrict__ qlow_out) {
+                                                   uint16_t* __restrict__ qlow_out,
+                                                   const float* __restrict__ knorm, int nblk,
+                                                   unsigned long long* __restrict__ pool,
+                                                   unsigned long long* __restrict__ pool_ctr,
+                                                   unsigned long long pool_cap) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int r = blockIdx.y;
     const int t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     const int h_q = g.ret_heads[r];
     const float s = g.idx_scale;
+    const float sB = s * kBinsPerX;
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
 
-    __shared__ float qs[kTR][16];                       // q_low as floats
-    __shared__ unsigned long long hm[kTR][kNB];
-    __shared__ uint32_t hc[kTR][kNB];
-    __shared__ unsigned long long cand[kTR][kCapC];
-    __shared__ uint32_t cand_n[kTR];
+    __shared__ __align__(16) unsigned char smem[kSmemBytes];
+    float* wq = reinterpret_cast<float*>(smem);
+    double(*hist)[kHBP] = reinterpret_cast<double(*)[kHBP]>(smem);
+    uint32_t(*hcnt)[kHBP] = reinterpret_cast<uint32_t(*)[kHBP]>(smem + kTR * kHBP * 8);
+    unsigned long long(*hm)[kNBP] = reinterpret_cast<unsigned long long(*)[kNBP]>(smem);
+    uint32_t(*hc)[kNBP] = reinterpret_cast<uint32_t(*)[kNBP]>(smem + kHmBytes);
+    unsigned long long(*cand)[kCapC] = reinterpret_cast<unsigned long long(*)[kCapC]>(smem + kHmBytes + kHcBytes);
+
+    __shared__ float qs[kTR][16];                        // q_low as floats
     __shared__ uint32_t rmax[kTR];                       // ordered keys of the row maxima
     __shared__ uint32_t kmax_bits;
+    __shared__ uint32_t cand_n[kTR], ucnt[kTR];
     __shared__ unsigned long long zu[kTR];               // exact mass of U
-    // per-row refinement state
-    __shared__ float r_mp[kTR], r_delta[kTR], r_T[kTR];
-    __shared__ int r_mode[kTR], r_uend[kTR], r_ntie[kTR], r_done[kTR], r_gather[kTR];
+    __shared__ float r_mp[kTR], r_delta[kTR], r_mpB[kTR], r_T[kTR], r_edge[kTR];
+    __shared__ uint32_t r_ucount[kTR];
+    __shared__ unsigned long long r_seg[kTR];
+    __shared__ int r_mode[kTR], r_uend[kTR], r_ntie[kTR], r_done[kTR], r_gather[kTR], r_bad[kTR];
     __shared__ uint32_t r_klo[kTR], r_khi[kTR], r_shift[kTR], r_cnthi[kTR];
-    __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_zlight[kTR];
+    __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_light[kTR];
     __shared__ int s_any;
     __shared__ uint32_t qpair[4][kQ];                    // per-wave exact-work queue: (row << 26) | key
 
     // ---- q_low of the 32 rows: fixed-order fp32 chain over d, bf16 rounding
+    for (int x = tid; x < g.D * 16; x += 256) wq[x] = bf2f(w_q[(size_t)r * g.D * 16 + x]);
+    __syncthreads();
+    for (int o = tid; o < kTR * 16; o += 256) {
+        const int lr = o >> 4, c = o & 15;
+        float acc = 0.0f;
+        if (lr < n_valid) {
+            const bf16_t* qp = q + ((size_t)(t0 + lr) * g.Hq + h_q) * g.D;
+            for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(bf2f(qp[d]), wq[d * 16 + c], acc);
+        }
+        const bf16_t qb = f2bf(acc);
+        qs[lr][c] = bf2f(qb);
+        if (lr < n_valid) qlow_out[((size_t)(t0 + lr) * g.n_ret + r) * 16 + c] = qb;
+    }
+    if (tid < kTR) {
+        rmax[tid] = 0u;
+        zu[tid] = 0ull;
+        cand_n[tid] = 0u;
+        ucnt[tid] = 0u;
+        r_target[tid] = 0ull;
+    }
+    if (tid == 0) kmax_bits = 0u;
+    __syncthreads();
     {
-        __shared__ float wq[128 * 16];
-        const bf16_t* wp = w_q + (size_t)r * g.D * 16;
-        for (int x = tid; x < g.D * 16; x += 256) wq[x] = bf2f(wp[x]);
-        __syncthreads();
-        for (int o = tid; o < kTR * 16; o += 256) {
-            const int lr = o >> 4, c = o & 15;
-            float acc = 0.0f;
-            if (lr < n_valid) {
-                const bf16_t* qp = q + ((size_t)(t0 + lr) * g.Hq + h_q) * g.D;
-                for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(bf2f(qp[d]), wq[d * 16 + c], acc);
-            }
-            const bf16_t qb = f2bf(acc);
-            qs[lr][c] = bf2f(qb);
-            if (lr < n_valid) qlow_out[((size_t)(t0 + lr) * g.n_ret + r) * 16 + c] = qb;
-        }
-        for (int x = tid; x < kTR * kNB; x += 256) {
-            (&hm[0][0])[x] = 0ull;
-            (&hc[0][0])[x] = 0u;
-        }
-        if (tid < kTR) {
-            rmax[tid] = 0u;
-            zu[tid] = 0ull;
-            cand_n[tid] = 0u;
-        }
-        if (tid == 0) kmax_bits = 0u;
-        __syncthreads();
+        float kn = 0.0f;
+        for (int b = tid; b < nblk; b += 256) kn = fmaxf(kn, knorm[(size_t)r * nblk + b]);
+        kn = wave_max(kn);
+        if (lane == 0) atomicMax(&kmax_bits, __float_as_uint(kn));
     }
 
     // lane roles in the MFMA tiles: row lr = lane % 32, half hh = lane / 32
@@ -173,16 +233,17 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         uint32_t w4[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-            w4[x] = (__float_as_uint(qs[lr][8 * hh + 2 * x]) >> 16) | (__float_as_uint(qs[lr][8 * hh + 2 * x + 1]) & 0xFFFF0000u);
+            w4[x] = (__float_as_uint(qs[lr][8 * hh + 2 * x]) >> 16) |
+                    (__float_as_uint(qs[lr][8 * hh + 2 * x + 1]) & 0xFFFF0000u);
         qb = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
     const int L_max = g.pos0 + t0 + n_valid;             // keys of the longest row
     const int ntile = (L_max + 31) / 32;
+    const int nfull = (g.pos0 + t0 + 1) / 32;            // tiles every row sees whole
 
-    // load the A operand of tile `it`: k_low[key it*32 + lr][8 hh .. 8 hh + 7]
+    // A operand of tile `it`: k_low[key it*32 + lr][8 hh .. 8 hh + 7]
     auto load_a = [&](int it) {
-        const int key = it * 32 + lr;
-        const int kk = min(key, L_max - 1);
+        const int kk = min(it * 32 + lr, L_max - 1);
         const int page = bt[kk >> 8];
         return *reinterpret_cast<const uint4*>(
             k_low + (((size_t)page * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
@@ -195,128 +256,174 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     };
     auto key_of = [&](int it, int i) { return it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3); };
 
-    // ---- pass 1: row maxima of the MFMA scores, largest key norm
+    // ---- P1: row maxima of the MFMA scores
     {
-        float m_e = -INFINITY, kn = 0.0f;
-        uint4 a = ntile > wid ? load_a(wid) : make_uint4(0, 0, 0, 0);
-        for (int it = wid; it < ntile; it += 4) {
-            const uint4 cur = a;
-            if (it + 4 < ntile) a = load_a(it + 4);
-            float kf[8];
-            unpack8(cur, kf);
-            float n2 = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) n2 = __builtin_fmaf(kf[e], kf[e], n2);
-            n2 += __shfl_xor(n2, 32);
-            kn = fmaxf(kn, n2);
+        float m_e = -INFINITY;
+        tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
+            if (it < nfull) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (key_of(it, i) <= pos) m_e = fmaxf(m_e, sc[i]);
-        }
+                for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, sc[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, key_of(it, i) <= pos ? sc[i] : -INFINITY);
+            }
+        });
         m_e = fmaxf(m_e, __shfl_xor(m_e, 32));
-        kn = wave_max(kn);
         if (row_ok && hh == 0 && m_e > -INFINITY) atomicMax(&rmax[lr], score_key(m_e));
-        if (lane == 0) atomicMax(&kmax_bits, __float_as_uint(kn));
+        for (int x = tid; x < kTR * kHBP; x += 256) {
+            (&hist[0][0])[x] = 0.0;
+            (&hcnt[0][0])[x] = 0u;
+        }
         __syncthreads();
         if (tid < kTR) {
             float qn2 = 0.0f;
             for (int c = 0; c < 16; ++c) qn2 = __builtin_fmaf(qs[tid][c], qs[tid][c], qn2);
-            const float delta = 0x1.0p-16f * sqrtf(qn2) * sqrtf(__uint_as_float(kmax_bits)) * 1.0009765625f;
             // delta exceeds the true deviation bound by a factor >= 8, far more
             // than the rounding of this sum: m' >= every exact score of the row
-            r_mp[tid] = key_score(rmax[tid]) + delta;
+            const float delta = 0x1.0p-16f * sqrtf(qn2) * sqrtf(__uint_as_float(kmax_bits)) * 1.0009765625f;
+            const float mp = key_score(rmax[tid]) + delta;
+            r_mp[tid] = mp;
             r_delta[tid] = delta;
+            r_mpB[tid] = mp * sB;
         }
         __syncthreads();
     }
-    const float mp = r_mp[lr];
-    const float delta = r_delta[lr];
+    const float mpB = r_mpB[lr];
 
-    // ---- pass 2: approximate level-1 mass histogram (mass only)
+    // ---- P2: mass and count histograms of the approximate weights exp(-x / 4)
     {
-        uint4 a = ntile > wid ? load_a(wid) : make_uint4(0, 0, 0, 0);
-        for (int it = wid; it < ntile; it += 4) {
-            const uint4 cur = a;
-            if (it + 4 < ntile) a = load_a(it + 4);
+        constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
+        double* hrow = hist[lr];
+        uint32_t* crow = hcnt[lr];
+        tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
-            if (row_ok) {
+            if (it < nfull) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float x = bin_x(sc[i], sB, mpB);
+                    const int b = bin_of(x);
+                    atomicAdd(&hrow[b], (double)__builtin_amdgcn_exp2f(x * kW));
+                    atomicAdd(&crow[b], 1u);
+                }
+            } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     if (key_of(it, i) <= pos) {
-                        const float x = s * (mp - sc[i]);
-                        atomicAdd(&hm[lr][bin1_of(x)], approx_w(x));
+                        const float x = bin_x(sc[i], sB, mpB);
+                        const int b = bin_of(x);
+                        atomicAdd(&hrow[b], (double)__builtin_amdgcn_exp2f(x * kW));
+                        atomicAdd(&crow[b], 1u);
                     }
                 }
             }
-        }
+        });
         __syncthreads();
         // cut bin of the approximate masses, U = bins <= cut + 1.  The target
         // carries a margin eta that covers the relative error of the
-        // approximate weights (|s (MFMA - exact)| <= s delta / 8) and their
-        // fixed-point truncation; U is everything when the bins are not wide
-        // against delta.
+        // approximate weights (<= s delta / 8 plus the exp2 rounding); U is every
+        // key when the bins are not wide against delta.
         if (tid < kTR) {
             const int row = tid;
             const float p = top_p[g.seq];
-            r_mode[row] = 2;
+            r_mode[row] = kLevel;
             r_done[row] = 0;
             r_gather[row] = 0;
-            r_uend[row] = kNB - 1;
+            r_bad[row] = 0;
+            r_uend[row] = kHB - 1;
+            r_ntie[row] = 0;
+            r_T[row] = 0.0f;
+            r_edge[row] = -INFINITY;
+            r_light[row] = 0ull;
+            r_ucount[row] = 0u;
+            r_seg[row] = kNoSeg;
             if (row >= n_valid) {
                 r_done[row] = 1;
             } else if (!(p < 1.0f)) {
-                r_mode[row] = 0;
+                r_mode[row] = kAll;
                 r_done[row] = 1;
             } else {
                 const double sd = (double)s * (double)r_delta[row];
-                unsigned long long Z = 0;
-                for (int b = 0; b < kNB; ++b) Z += hm[row][b];
-                const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * (double)Z;
-                int bc = kNB - 1;
-                unsigned long long cum = 0;
-                for (int b = 0; b < kNB; ++b) {
-                    cum += hm[row][b];
-                    if ((double)cum >= tgt_a) {
+                double Z = 0.0;
+                for (int b = 0; b < kHB; ++b) Z += hist[row][b];
+                const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * Z;
+                int bc = kHB - 1;
+                double cum = 0.0;
+                for (int b = 0; b < kHB; ++b) {
+                    cum += hist[row][b];
+                    if (cum >= tgt_a) {
                         bc = b;
                         break;
                     }
                 }
-                const int ue = (sd < 1.0 / 16.0) ? min(bc + 1, kNB - 1) : kNB - 1;
-                unsigned long long zl = 0;
-                for (int b = ue + 1; b < kNB; ++b) zl += hm[row][b];
+                const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
+                double light = 0.0;
+                for (int b = ue + 1; b < kHB; ++b) light += hist[row][b];
+                uint32_t uc = 0;
+                for (int b = 0; b <= ue; ++b) uc += hcnt[row][b];
+                r_ucount[row] = uc;
                 r_uend[row] = ue;
-                r_zlight[row] = zl;
-                // first exact level: the whole key range of U in exact-score space
-                // (keys of U have MFMA scores above m' - (ue + 1) / (2 s), exact
-                // scores within delta of them)
-                if (ue == kNB - 1) {
-                    r_klo[row] = 0u;
+                r_light[row] = (unsigned long long)__double2ll_rn(light * kFix);
+                const double mp = (double)r_mp[row];
+                if (ue == kHB - 1) {
+                    r_klo[row] = 0u;                      // every key is in U
                 } else {
-                    const double dlo = (double)r_mp[row] - (double)(ue + 1) / ((double)kBin1 * (double)s) * 1.001 -
-                                       2.0 * (double)r_delta[row];
-                    r_klo[row] = score_key(__double2float_rd(dlo));
+                    // keys of U: x < (ue + 1) / 4, so e > m' - (ue + 1) / (4 s);
+                    // keys outside: the reverse.  The margin covers the float
+                    // rounding of the bin argument and the MFMA deviation.
+                    const double span = (double)(ue + 1) / ((double)kBinsPerX * (double)s);
+                    const double marg = 0x1.0p-18 * (span + 2.0 * fabs(mp)) + 2.0 * (double)r_delta[row];
+                    r_klo[row] = score_key(__double2float_rd(mp - span - marg));
+                    r_edge[row] = __double2float_ru(mp - span + marg);
                 }
                 r_khi[row] = score_key(r_mp[row]);
-                const uint32_t span = r_khi[row] - r_klo[row];
-                const int bits = span ? 32 - __clz(span) : 0;
+                const uint32_t spn = r_khi[row] - r_klo[row];
+                const int bits = spn ? 32 - __clz(spn) : 0;
                 r_shift[row] = bits > 6 ? bits - 6 : 0;
                 r_shi[row] = 0ull;
                 r_cnthi[row] = 0u;
             }
         }
         __syncthreads();
+        // pool segments for the rows whose U is small enough (one allocation
+        // per workgroup; a full pool sends the rows to the radix levels)
+        if (tid == 0) {
+            unsigned long long tot = 0;
+            for (int row = 0; row < n_valid; ++row)
+                if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)kSegMax) tot += r_ucount[row];
+            if (tot) {
+                const unsigned long long base = atomicAdd(pool_ctr, tot);
+                if (base + tot <= pool_cap) {
+                    unsigned long long off = base;
+                    for (int row = 0; row < n_valid; ++row)
+                        if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)kSegMax) {
+                            r_seg[row] = off;
+                            off += r_ucount[row];
+                        }
+                }
+            }
+        }
+        // the histograms are dead: the level structures take their place
+        for (int x = tid; x < kTR * kNBP; x += 256) {
+            (&hm[0][0])[x] = 0ull;
+            (&hc[0][0])[x] = 0u;
+        }
+        __syncthreads();
     }
     const int u_end = r_uend[lr];
 
-    // ---- exact levels: radix on the order-preserving key of the exact score
-    // of U's keys, 64 buckets per level, highest scores first; then one gather
-    // pass collects the cut bucket's keys for the final sort.
+    // ---- P3 and the radix levels on the exact score.  P3 (level 0) computes
+    // the exact score and weight of every key of U: the mass of U, and U's
+    // pairs into the row's segment, or for a row without one the level-0
+    // radix histogram.  Rows without a segment narrow the cut bucket by
+    // further levels (64 buckets each, highest scores first) and finally
+    // gather its keys for one sort.
     for (int level = 0; level < 8; ++level) {
-        // clear the level histograms
-        for (int x = tid; x < kTR * kNB; x += 256) {
-            (&hm[0][0])[x] = 0ull;
-            (&hc[0][0])[x] = 0u;
+        if (level > 0) {
+            for (int x = tid; x < kTR * kNBP; x += 256) {
+                (&hm[0][0])[x] = 0ull;
+                (&hc[0][0])[x] = 0u;
+            }
         }
         if (tid == 0) s_any = 0;
         __syncthreads();
@@ -324,10 +431,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         __syncthreads();
         if (!s_any) break;
 
-        uint4 a = ntile > wid ? load_a(wid) : make_uint4(0, 0, 0, 0);
         int qbase = 0;                                    // wave-uniform queue fill
-        // process the queued pairs of this wave: exact score, then either a
-        // histogram update (level pass) or a gather into the candidates
+        // process the queued pairs of this wave
         auto drain = [&](int n) {
             wave_lds_sync();
             if (lane < n) {
@@ -346,41 +451,42 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                     }
                 } else {
                     const unsigned long long w = weight_bin(d, r_mp[row], s).w;
-                    if (level == 0) atomicAdd(&zu[row], w);
-                    if (kd > r_khi[row]) {
-                        // above the range: counted by earlier levels
-                    } else if (kd >= r_klo[row]) {
+                    const unsigned long long sg = r_seg[row];
+                    if (level == 0) {
+                        atomicAdd(&zu[row], w);
+                        const uint32_t slot = atomicAdd(&ucnt[row], 1u);
+                        if (sg != kNoSeg && slot < r_ucount[row])
+                            pool[sg + slot] = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
+                    }
+                    if (sg == kNoSeg && kd >= r_klo[row] && kd <= r_khi[row]) {
                         const uint32_t bk = min((r_khi[row] - kd) >> r_shift[row], (uint32_t)(kNB - 1));
                         atomicAdd(&hm[row][bk], w);
                         atomicAdd(&hc[row][bk], 1u);
                     }
-                    // below the range: ranks below the cut, mass already in zu
+                    // above the range: counted by earlier levels; below: ranks below the cut
                 }
             }
             wave_lds_sync();
         };
-        for (int it = wid; it < ntile; it += 4) {
-            const uint4 cur = a;
-            if (it + 4 < ntile) a = load_a(it + 4);
+        const bool active = row_ok && !r_done[lr];
+        const bool ranged = active && (r_gather[lr] || level > 0);
+        const float lo = ranged ? key_score(r_klo[lr]) : 0.0f, hi = ranged ? key_score(r_khi[lr]) : 0.0f;
+        const float dl = r_delta[lr];
+        tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
             // which of this lane's pairs need an exact score
             uint32_t need = 0;
-            if (row_ok && !r_done[lr]) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (key_of(it, i) > pos) continue;
-                    const float x = s * (mp - sc[i]);
-                    if (bin1_of(x) > u_end) continue;        // not in U
-                    if (r_gather[lr] || level > 0) {
-                        // only pairs whose exact score can fall inside [klo, khi]
-                        const float lo = key_score(r_klo[lr]), hi = key_score(r_khi[lr]);
-                        if (sc[i] + delta < lo || sc[i] - delta > hi) continue;
-                    }
-                    need |= 1u << i;
-                }
+            for (int i = 0; i < 16; ++i) {
+                bool in = active && bin_of(bin_x(sc[i], sB, mpB)) <= u_end;
+                if (it >= nfull) in = in && key_of(it, i) <= pos;
+                // only pairs whose exact score can fall inside [lo, hi]
+                if (ranged) in = in && !(sc[i] + dl < lo) && !(sc[i] - dl > hi);
+                need |= (uint32_t)in << i;
             }
-            // append to the wave queue in order, draining when full
-            int cnt = __popc(need);
+            if (__ballot(need != 0u) == 0ull) return;
+            // append to the wave queue, draining when full
+            const int cnt = __popc(need);
             int pre = cnt;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -398,7 +504,6 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             int done = 0;
             while (done < total) {
                 const int take = min(kQ - base, total - done);
-                // lanes write their pairs with ordinal in [done, done + take)
                 uint32_t m = need;
                 int ord = pre;
                 while (m) {
@@ -416,7 +521,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 }
             }
             qbase = base;
-        }
+        });
         drain(qbase);
         __syncthreads();
 
@@ -424,17 +529,21 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         if (tid < kTR) {
             const int row = tid;
             if (!r_done[row]) {
-                const float p = top_p[g.seq];
-                if (r_gather[row]) {
-                    // final sort of the cut bucket's keys
+                if (level == 0) {
+                    const float p = top_p[g.seq];
+                    const unsigned long long Z = zu[row] + r_light[row];
+                    unsigned long long tgt = (unsigned long long)ceil((double)p * (double)Z);
+                    if (tgt > Z) tgt = Z;
+                    if (tgt < 1ull) tgt = 1ull;
+                    r_target[row] = tgt;
+                }
+                if (level == 0 && r_seg[row] != kNoSeg) {
+                    r_mode[row] = kBuf;                  // resolved from its segment
                     r_done[row] = 1;
+                    if (ucnt[row] != r_ucount[row]) r_bad[row] = 1;   // P2 and P3 disagree on U
+                } else if (r_gather[row]) {
+                    r_done[row] = 1;                     // final sort of the cut bucket's keys below
                 } else {
-                    if (level == 0) {
-                        const unsigned long long Z = zu[row] + r_zlight[row];
-                        unsigned long long tgt = (unsigned long long)ceil((double)p * (double)Z);
-                        if (tgt < 1ull) tgt = 1ull;
-                        r_target[row] = tgt;
-                    }
                     unsigned long long cum = r_shi[row];
                     uint32_t ch = r_cnthi[row];
                     int bc = -1;
@@ -448,16 +557,14 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                         ch += hc[row][b];
                     }
                     if (bc < 0) {
-                        // U does not reach the target (its mass is within rounding
-                        // of p): every key of U is selected
-                        r_mode[row] = 1;
+                        // U does not reach the target: the approximation bound failed
+                        r_bad[row] = 1;
                         r_done[row] = 1;
-                        r_ntie[row] = 0;
                     } else {
                         r_shi[row] = cum;
                         r_cnthi[row] = ch;
                         const uint32_t khi = r_khi[row] - ((uint32_t)bc << r_shift[row]);
-                        const uint32_t wdt = r_shift[row] >= 32 ? 0xFFFFFFFFu : ((1u << r_shift[row]) - 1u);
+                        const uint32_t wdt = (1u << r_shift[row]) - 1u;
                         const uint32_t klo = (khi - r_klo[row] > wdt) ? khi - wdt : r_klo[row];
                         r_khi[row] = khi;
                         r_klo[row] = klo;
@@ -468,15 +575,14 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                             const unsigned long long need = r_target[row] - cum;
                             r_T[row] = key_score(khi);
                             r_ntie[row] = (int)((need + wT - 1ull) / wT);
-                            r_mode[row] = 2;
                             r_done[row] = 1;
                             r_gather[row] = 2;               // resolved without candidates
                         } else if (n_c <= (uint32_t)kCapC) {
                             r_gather[row] = 1;
                             cand_n[row] = 0u;
                         } else {
-                            const uint32_t span = khi - klo;
-                            const int bits = span ? 32 - __clz(span) : 0;
+                            const uint32_t spn = khi - klo;
+                            const int bits = spn ? 32 - __clz(spn) : 0;
                             r_shift[row] = bits > 6 ? bits - 6 : 0;
                         }
                     }
@@ -486,78 +592,99 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         __syncthreads();
     }
 
-    // ---- final sort of each row's candidates and the per-row result
+    // ---- per-row results; rows resolved by levels sort their candidates here
     if (wid == 0) {
         for (int row = 0; row < n_valid; ++row) {
             CRow out;
             out.mp = r_mp[row];
             out.delta = r_delta[row];
+            out.mpB = r_mpB[row];
+            out.seg = r_seg[row];
+            out.d_edge = r_edge[row];
             out.u_end = r_uend[row];
             out.mode = r_mode[row];
             out.T = 0.0f;
             out.n_tie = 0;
-            out.count = 0;                                    // counted by the emit pass
-            out.pad = 0;
-            if (out.mode == 2 && r_gather[row] == 2) {
-                out.T = r_T[row];
-                out.n_tie = r_ntie[row];
-            } else if (out.mode == 2) {
-                const int n = min((int)cand_n[row], kCapC);
-                if (n == 0 || r_gather[row] != 1 || !r_done[row]) {
-                    out.mode = 1;                             // unresolved: all of U
+            out.count = 0;
+            out.target = r_target[row];
+            int bad = r_bad[row];
+            if (out.mode == kBuf) {
+                out.count = (int)ucnt[row];
+            } else if (out.mode == kLevel && !bad) {
+                if (r_gather[row] == 2) {
+                    out.T = r_T[row];
+                    out.n_tie = r_ntie[row];
+                    out.count = (int)r_cnthi[row] + r_ntie[row];
                 } else {
-                    // bitonic sort (descending) of the candidates, two per lane
-                    unsigned long long* cr = cand[row];
-                    for (int x = lane + n; x < kCapC; x += 64) cr[x] = 0ull;
-                    wave_lds_sync();
-                    for (int k = 2; k <= kCapC; k <<= 1)
-                        for (int j = k >> 1; j > 0; j >>= 1) {
-                            for (int i = lane; i < kCapC; i += 64) {
-                                const int ixj = i ^ j;
-                                if (ixj > i) {
-                                    const unsigned long long x = cr[i], y = cr[ixj];
-                                    const bool desc = (i & k) == 0;
-                                    if (desc ? (x < y) : (x > y)) {
-                                        cr[i] = y;
-                                        cr[ixj] = x;
+                    const int n = min((int)cand_n[row], kCapC);
+                    if (n == 0 || r_gather[row] != 1 || !r_done[row]) {
+                        bad = 1;
+                    } else {
+                        // bitonic sort (descending) of the candidates, two per lane
+                        unsigned long long* cr = cand[row];
+                        for (int x = lane + n; x < kCapC; x += 64) cr[x] = 0ull;
+                        wave_lds_sync();
+                        for (int k = 2; k <= kCapC; k <<= 1)
+                            for (int j = k >> 1; j > 0; j >>= 1) {
+                                for (int i = lane; i < kCapC; i += 64) {
+                                    const int ixj = i ^ j;
+                                    if (ixj > i) {
+                                        const unsigned long long x = cr[i], y = cr[ixj];
+                                        const bool desc = (i & k) == 0;
+                                        if (desc ? (x < y) : (x > y)) {
+                                            cr[i] = y;
+                                            cr[ixj] = x;
+                                        }
                                     }
                                 }
+                                wave_lds_sync();
                             }
-                            wave_lds_sync();
+                        // cumulative exact mass in rank order; the lane holds
+                        // ranks 2 lane and 2 lane + 1
+                        const int i0 = 2 * lane, i1 = 2 * lane + 1;
+                        const float mpr = r_mp[row];
+                        const unsigned long long w0 =
+                            i0 < n ? weight_bin(key_score((uint32_t)(cr[i0] >> 32)), mpr, s).w : 0ull;
+                        const unsigned long long w1 =
+                            i1 < n ? weight_bin(key_score((uint32_t)(cr[i1] >> 32)), mpr, s).w : 0ull;
+                        unsigned long long incl = w0 + w1;
+#pragma unroll
+                        for (int o = 1; o < 64; o <<= 1) {
+                            const unsigned long long y = __shfl_up(incl, o);
+                            if (lane >= o) incl += y;
                         }
-                    // cumulative exact mass in rank order; the lane holds ranks
-                    // 2 lane and 2 lane + 1
-                    const int i0 = 2 * lane, i1 = 2 * lane + 1;
-                    const float mpr = r_mp[row];
-                    const unsigned long long w0 =
-                        i0 < n ? weight_bin(key_score((uint32_t)(cr[i0] >> 32)), mpr, s).w : 0ull;
-                    const unsigned long long w1 =
-                        i1 < n ? weight_bin(key_score((uint32_t)(cr[i1] >> 32)), mpr, s).w : 0ull;
-                    unsigned long long incl = w0 + w1;
+                        const unsigned long long c0 = r_shi[row] + incl - w1;   // through rank i0
+                        const unsigned long long c1 = c0 + w1;                  // through rank i1
+                        const unsigned long long tgt = r_target[row];
+                        int first = 1 << 30;
+                        if (i0 < n && c0 >= tgt) first = i0;
+                        else if (i1 < n && c1 >= tgt) first = i1;
 #pragma unroll
-                    for (int o = 1; o < 64; o <<= 1) {
-                        const unsigned long long y = __shfl_up(incl, o);
-                        if (lane >= o) incl += y;
+                        for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+                        if (first >= n) bad = 1;
+                        const int ic = first < n ? first : n - 1;
+                        const uint32_t kT = (uint32_t)(cr[ic] >> 32);
+                        int tie = 0, above = 0;
+                        if (i0 <= ic) {
+                            if ((uint32_t)(cr[i0] >> 32) == kT) ++tie; else ++above;
+                        }
+                        if (i1 <= ic) {
+                            if ((uint32_t)(cr[i1] >> 32) == kT) ++tie; else ++above;
+                        }
+#pragma unroll
+                        for (int o = 32; o > 0; o >>= 1) {
+                            tie += __shfl_xor(tie, o);
+                            above += __shfl_xor(above, o);
+                        }
+                        out.T = key_score(kT);
+                        out.n_tie = tie;
+                        out.count = (int)r_cnthi[row] + above + tie;
                     }
-                    const unsigned long long c0 = r_shi[row] + incl - w1;   // through rank i0
-                    const unsigned long long c1 = c0 + w1;                  // through rank i1
-                    const unsigned long long tgt = r_target[row];
-                    int first = 1 << 30;
-                    if (i0 < n && c0 >= tgt) first = i0;
-                    else if (i1 < n && c1 >= tgt) first = i1;
-#pragma unroll
-                    for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
-                    const int ic = first < n ? first : n - 1;
-                    const uint32_t kT = (uint32_t)(cr[ic] >> 32);
-                    int tie = 0;
-                    if (i0 <= ic && (uint32_t)(cr[i0] >> 32) == kT) ++tie;
-                    if (i1 <= ic && (uint32_t)(cr[i1] >> 32) == kT) ++tie;
-#pragma unroll
-                    for (int o = 32; o > 0; o >>= 1) tie += __shfl_xor(tie, o);
-                    out.T = key_score(kT);
-                    out.n_tie = tie;
                 }
+                // certification: no key outside U can reach the cut
+                if (!(out.T > out.d_edge)) bad = 1;
             }
+            out.bad = bad;
             if (lane == 0) rows_out[(size_t)(t0 + row) * g.n_ret + r] = out;
             wave_lds_sync();
         }
@@ -565,24 +692,212 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Emit.  grid (ceil(n_tok / 32), n_ret), one wavefront: keys in index order,
-// selected keys written ascending at row_ptr[row].
+// Resolve of a row held in a pool segment: sort U by (exact score descending,
+// index ascending), cut at the first rank whose cumulative exact mass reaches
+// the target, certify the cut, sort the selected indices ascending and store
+// them over the segment.  Writes the row's count (-1 if certification
+// failed).  NT threads, U of up to CAP keys sorted in LDS.
+// ---------------------------------------------------------------------------
+template <int CAP, int NT>
+__device__ void resolve_row(const Geo& g, const CRow& cr, unsigned long long* __restrict__ pool,
+                            int* __restrict__ count_out, unsigned long long* sk, unsigned long long* scan_sh,
+                            int* s_first) {
+    const int tid = threadIdx.x;
+    const int n = cr.count;
+    unsigned long long* ub = pool + cr.seg;
+    int N = 64;
+    while (N < n) N <<= 1;
+    for (int i = tid; i < N; i += NT) sk[i] = i < n ? ub[i] : 0ull;
+    __syncthreads();
+    // bitonic sort, descending
+    for (int k = 2; k <= N; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < N; i += NT) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const unsigned long long x = sk[i], y = sk[ixj];
+                    const bool desc = (i & k) == 0;
+                    if (desc ? (x < y) : (x > y)) {
+                        sk[i] = y;
+                        sk[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    // exact masses in rank order: each thread a run of consecutive ranks
+    const float s = g.idx_scale;
+    const int per = (N + NT - 1) / NT;
+    const int r0 = tid * per;
+    const int r1 = min(r0 + per, n);
+    unsigned long long loc = 0;
+    for (int i = r0; i < r1; ++i) loc += weight_bin(key_score((uint32_t)(sk[i] >> 32)), cr.mp, s).w;
+    unsigned long long tot;
+    const unsigned long long ex = block_excl_scan_u64<NT>(loc, &tot, scan_sh);
+    if (tid == 0) *s_first = 1 << 30;
+    __syncthreads();
+    {
+        unsigned long long run = ex;
+        for (int i = r0; i < r1; ++i) {
+            run += weight_bin(key_score((uint32_t)(sk[i] >> 32)), cr.mp, s).w;
+            if (run >= cr.target) {
+                atomicMin(s_first, i);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const int first = *s_first;
+    const bool ok = first < n && key_score((uint32_t)(sk[first < n ? first : 0] >> 32)) > cr.d_edge;
+    const int cnt = first < n ? first + 1 : n;
+    // selected indices ascending; the index lives in the low word as its complement
+    int N2 = 64;
+    while (N2 < cnt) N2 <<= 1;
+    uint32_t mine[CAP / NT];
+#pragma unroll
+    for (int x = 0; x < CAP / NT; ++x) {
+        const int i = tid + x * NT;
+        mine[x] = i < cnt ? ~(uint32_t)sk[i] : 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    uint32_t* si = reinterpret_cast<uint32_t*>(sk);
+#pragma unroll
+    for (int x = 0; x < CAP / NT; ++x) {
+        const int i = tid + x * NT;
+        if (i < N2) si[i] = mine[x];
+    }
+    __syncthreads();
+    for (int k = 2; k <= N2; k <<= 1)
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < N2; i += NT) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const uint32_t x = si[i], y = si[ixj];
+                    const bool asc = (i & k) == 0;
+                    if (asc ? (x > y) : (x < y)) {
+                        si[i] = y;
+                        si[ixj] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    uint32_t* ubi = reinterpret_cast<uint32_t*>(ub);
+    for (int i = tid; i < cnt; i += NT) ubi[i] = si[i];
+    if (tid == 0) *count_out = ok ? cnt : -1;
+    __syncthreads();
+}
+
+// Rows with U up to kSmallU in a segment, and the counts of the rows that have
+// no segment.  grid (rows), 512 threads.
+constexpr int kRT = 512;
+__global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restrict__ rows,
+                                                      unsigned long long* __restrict__ pool,
+                                                      int* __restrict__ counts) {
+    const int row = blockIdx.x;
+    const CRow cr = rows[row];
+    if (cr.mode != kBuf) {
+        if (threadIdx.x == 0) {
+            const int L = g.pos0 + row / g.n_ret + 1;
+            counts[row] = cr.bad ? -1 : (cr.mode == kAll ? L : cr.count);
+        }
+        return;
+    }
+    if (cr.count > kSmallU) return;
+    if (cr.bad) {
+        if (threadIdx.x == 0) counts[row] = -1;
+        return;
+    }
+    __shared__ unsigned long long sk[kSmallU];
+    __shared__ unsigned long long scan_sh[kRT / 64 + 1];
+    __shared__ int s_first;
+    resolve_row<kSmallU, kRT>(g, cr, pool, &counts[row], sk, scan_sh, &s_first);
+}
+
+// Rows with U in (kSmallU, kSegMax]: a fixed grid of 1024-thread workgroups
+// walks the rows.
+constexpr int kRTL = 1024;
+__global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* __restrict__ rows, int n_rows,
+                                                             unsigned long long* __restrict__ pool,
+                                                             int* __restrict__ counts) {
+    __shared__ unsigned long long sk[kSegMax];
+    __shared__ unsigned long long scan_sh[kRTL / 64 + 1];
+    __shared__ int s_first;
+    for (int row = blockIdx.x; row < n_rows; row += gridDim.x) {
+        const CRow cr = rows[row];
+        if (cr.mode != kBuf || cr.count <= kSmallU) continue;
+        if (cr.bad) {
+            if (threadIdx.x == 0) counts[row] = -1;
+            continue;
+        }
+        resolve_row<kSegMax, kRTL>(g, cr, pool, &counts[row], sk, scan_sh, &s_first);
+    }
+}
+
+// CSR row pointers over all rows of the call, the certification and the
+// capacity check.
+__global__ __launch_bounds__(1024) void k_csel_rowptr(const int* __restrict__ counts, int rows,
+                                                      int64_t* __restrict__ row_ptr, int64_t capacity,
+                                                      int32_t* __restrict__ status) {
+    const int tid = threadIdx.x;
+    __shared__ unsigned long long scan_sh[1024 / 64 + 1];
+    __shared__ int s_bad;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    int64_t carry = 0;
+    if (tid == 0) row_ptr[0] = 0;
+    for (int i0 = 0; i0 < rows; i0 += 1024) {
+        const int i = i0 + tid;
+        const int c = i < rows ? counts[i] : 0;
+        if (c < 0) s_bad = 1;
+        const unsigned long long cu = c > 0 ? (unsigned long long)c : 0ull;
+        unsigned long long tot;
+        const unsigned long long ex = block_excl_scan_u64<1024>(cu, &tot, scan_sh);
+        if (i < rows) row_ptr[i + 1] = carry + (int64_t)(ex + cu);
+        carry += (int64_t)tot;
+    }
+    __syncthreads();
+    if (tid == 0) *status = s_bad ? 2 : (carry > capacity ? 1 : 0);
+}
+
+// Rows held in a segment and keep-all rows: copy into idx.  grid (rows), 256 threads.
+__global__ __launch_bounds__(256) void k_csel_copy(const CRow* __restrict__ rows,
+                                                   const unsigned long long* __restrict__ pool,
+                                                   const int64_t* __restrict__ row_ptr, int32_t* __restrict__ idx,
+                                                   const int32_t* __restrict__ status) {
+    const int row = blockIdx.x;
+    if (*status != 0) return;
+    const int mode = rows[row].mode;
+    if (mode == kLevel) return;
+    const int64_t b = row_ptr[row], n = row_ptr[row + 1] - b;
+    if (mode == kAll) {
+        for (int64_t i = threadIdx.x; i < n; i += 256) idx[b + i] = (int32_t)i;
+    } else {
+        const uint32_t* ubi = reinterpret_cast<const uint32_t*>(pool + rows[row].seg);
+        for (int64_t i = threadIdx.x; i < n; i += 256) idx[b + i] = (int32_t)ubi[i];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Rescan emit of the rows resolved by levels.  grid (ceil(n_tok / 32), n_ret),
+// one wavefront: keys in index order, selected keys written ascending at
+// row_ptr[row].
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restrict__ k_low,
                                                   const uint16_t* __restrict__ qlow, const CRow* __restrict__ rows,
                                                   const int64_t* __restrict__ row_ptr, int32_t* __restrict__ idx,
-                                                  int64_t capacity, const int32_t* __restrict__ status,
-                                                  int* __restrict__ counts, int pass) {
+                                                  const int32_t* __restrict__ status) {
     const int lane = threadIdx.x;
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     const int lr = lane & 31, hh = lane >> 5;
-    const bool row_ok = lr < n_valid;
     const int row = (t0 + min(lr, n_valid - 1)) * g.n_ret + r;
     const int pos = g.pos0 + t0 + lr;
-    if (pass == 1 && *status != 0) return;
+    if (*status != 0) return;
     const CRow cr = rows[row];
-    const float s = g.idx_scale;
+    const bool row_ok = lr < n_valid && cr.mode == kLevel;
+    if (__ballot(row_ok) == 0ull) return;
+    const float sB = g.idx_scale * kBinsPerX;
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     float q16[16];
     uint4 qb;
@@ -595,7 +910,8 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
     }
     const int L_max = g.pos0 + t0 + n_valid;
     const int ntile = (L_max + 31) / 32;
-    int64_t wpos = (pass == 1 && row_ok) ? row_ptr[row] : 0;
+    const int64_t wpos = row_ok ? row_ptr[row] : 0;
+    const int64_t lim = row_ok ? row_ptr[row + 1] - wpos : 0;
     int run_sel = 0, run_tie = 0;
     auto load_a = [&](int it) {
         const int kk = min(it * 32 + lr, L_max - 1);
@@ -603,145 +919,170 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
         return *reinterpret_cast<const uint4*>(
             k_low + (((size_t)page * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
     };
-    constexpr int kPre = 4;                               // tiles in flight
-    uint4 ring[kPre];
-#pragma unroll
-    for (int x = 0; x < kPre; ++x) ring[x] = load_a(min(x, ntile - 1));
-    for (int it0 = 0; it0 < ntile; it0 += kPre) {
-#pragma unroll
-    for (int x = 0; x < kPre; ++x) {
-        const int it = it0 + x;
-        if (it >= ntile) break;
-        const uint4 a = ring[x];
-        if (it + kPre < ntile) ring[x] = load_a(it + kPre);
+    tile_loop<kPre>(0, 1, ntile, load_a, [&](int it, const uint4& cur) {
         f32x16_t sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qb), sc, 0, 0, 0);
-        uint32_t sel = 0, tie = 0;
-        if (row_ok) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qb), sc, 0, 0, 0);
+        // certain selections, and the pairs whose exact score decides
+        uint32_t sel = 0, amb = 0;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16; ++i) {
+            const int kj = it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
+            const bool in = row_ok && kj <= pos && bin_of(bin_x(sc[i], sB, cr.mpB)) <= cr.u_end;
+            const bool hi = sc[i] - cr.delta > cr.T;
+            const bool near = !hi && !(sc[i] + cr.delta < cr.T);
+            sel |= (uint32_t)(in && hi) << i;
+            amb |= (uint32_t)(in && near) << i;
+        }
+        uint32_t tie = 0;
+        if (__ballot(amb != 0u) != 0ull) {
+            uint32_t m = amb;
+            while (m) {
+                const int i = __ffs(m) - 1;
+                m &= m - 1;
                 const int kj = it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
-                if (kj > pos) continue;
-                if (cr.mode == 0) {
-                    sel |= 1u << i;
-                    continue;
-                }
-                const float x = s * (cr.mp - sc[i]);
-                if (bin1_of(x) > cr.u_end) continue;          // outside U
-                if (cr.mode == 1) {
-                    sel |= 1u << i;
-                    continue;
-                }
-                if (sc[i] - cr.delta > cr.T) {
-                    sel |= 1u << i;
-                } else if (sc[i] + cr.delta >= cr.T) {
-                    const int pg = bt[kj >> 8];
-                    const uint4* kp = reinterpret_cast<const uint4*>(
-                        k_low + (((size_t)pg * g.n_ret + r) * kBlk + (kj & 255)) * 16);
-                    const float d = exact_score(q16, kp[0], kp[1]);
-                    if (d > cr.T) sel |= 1u << i;
-                    else if (d == cr.T) tie |= 1u << i;
-                }
+                const int pg = bt[kj >> 8];
+                const uint4* kp = reinterpret_cast<const uint4*>(
+                    k_low + (((size_t)pg * g.n_ret + r) * kBlk + (kj & 255)) * 16);
+                const float d = exact_score(q16, kp[0], kp[1]);
+                if (d > cr.T) sel |= 1u << i;
+                else if (d == cr.T) tie |= 1u << i;
             }
         }
         // ties in index order: groups of four keys alternate between the halves
-        uint32_t tc[4], tp[4];
+        if (__ballot(tie != 0u) != 0ull) {
+            uint32_t tc[4], tp[4];
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) tc[gq] = __popc((tie >> (4 * gq)) & 0xFu);
+            for (int gq = 0; gq < 4; ++gq) tc[gq] = __popc((tie >> (4 * gq)) & 0xFu);
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) tp[gq] = __shfl_xor(tc[gq], 32);
-        // ordinal of this lane's first tie in each of its groups
-        int acc = run_tie;
+            for (int gq = 0; gq < 4; ++gq) tp[gq] = __shfl_xor(tc[gq], 32);
+            int acc = run_tie;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int mine = hh ? (int)tp[gq] : 0;        // the partner's group comes first for hh = 1
-            const int start = acc + mine;
-            int o = start;
+            for (int gq = 0; gq < 4; ++gq) {
+                int o = acc + (hh ? (int)tp[gq] : 0);     // the partner's group comes first for hh = 1
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * gq + e;
-                if ((tie >> i) & 1u) {
-                    if (o < cr.n_tie) sel |= 1u << i;
-                    ++o;
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 4 * gq + e;
+                    if ((tie >> i) & 1u) {
+                        if (o < cr.n_tie) sel |= 1u << i;
+                        ++o;
+                    }
                 }
+                acc += (int)tc[gq] + (int)tp[gq];
             }
-            acc += (int)tc[gq] + (int)tp[gq];
+            run_tie = acc;
         }
-        run_tie = acc;
         // ordered write of the selected keys
-        uint32_t sc4[4], sp4[4];
+        if (__ballot(sel != 0u) != 0ull) {
+            // counts of the four groups of this half packed in 3-bit fields
+            uint32_t pk = 0;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) sc4[gq] = __popc((sel >> (4 * gq)) & 0xFu);
+            for (int gq = 0; gq < 4; ++gq) pk |= (uint32_t)__popc((sel >> (4 * gq)) & 0xFu) << (3 * gq);
+            const uint32_t pp = __shfl_xor(pk, 32);
+            int acc = run_sel;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) sp4[gq] = __shfl_xor(sc4[gq], 32);
-        int accs = run_sel;
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            int o = accs + (hh ? (int)sp4[gq] : 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * gq + e;
-                if ((sel >> i) & 1u) {
-                    if (pass == 1 && row_ok && wpos + o < capacity)
-                        idx[wpos + o] = it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
+            for (int gq = 0; gq < 4; ++gq) {
+                const int c_m = (pk >> (3 * gq)) & 7, c_p = (pp >> (3 * gq)) & 7;
+                int o = acc + (hh ? c_p : 0);
+                uint32_t m = (sel >> (4 * gq)) & 0xFu;
+                while (m) {
+                    const int e = __ffs(m) - 1;
+                    m &= m - 1;
+                    if (o < lim) idx[wpos + o] = it * 32 + gq * 8 + 4 * hh + e;
                     ++o;
                 }
+                acc += c_m + c_p;
             }
-            accs += (int)sc4[gq] + (int)sp4[gq];
+            run_sel = acc;
         }
-        run_sel = accs;
-    }
-    }
-    if (pass == 0 && row_ok && hh == 0) counts[row] = run_sel;
+    });
 }
 
-// CSR row pointers over all rows of the call and the capacity check.
-__global__ __launch_bounds__(1024) void k_csel_rowptr(const int* __restrict__ counts, int rows,
-                                                      int64_t* __restrict__ row_ptr, int64_t capacity,
-                                                      int32_t* __restrict__ status) {
-    const int tid = threadIdx.x;
-    __shared__ unsigned long long scan_sh[1024 / 64 + 1];
-    int64_t carry = 0;
-    if (tid == 0) row_ptr[0] = 0;
-    for (int i0 = 0; i0 < rows; i0 += 1024) {
-        const int i = i0 + tid;
-        const unsigned long long c = i < rows ? (unsigned long long)counts[i] : 0ull;
-        unsigned long long tot;
-        const unsigned long long ex = block_excl_scan_u64<1024>(c, &tot, scan_sh);
-        if (i < rows) row_ptr[i + 1] = carry + (int64_t)(ex + c);
-        carry += (int64_t)tot;
+// Largest squared indexer-key norm of each block of kNormKeys keys of the
+// chunk's sequence, per retrieval head, and the pool counter reset.
+// grid (nblk, n_ret), 256 threads.
+__global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restrict__ k_low, int n_keys,
+                                                    float* __restrict__ knorm, int nblk,
+                                                    unsigned long long* __restrict__ pool_ctr) {
+    const int r = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+    if (blk == 0 && r == 0 && tid == 0) *pool_ctr = 0ull;
+    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
+    float kn = 0.0f;
+    for (int i = tid; i < kNormKeys; i += 256) {
+        const int key = blk * kNormKeys + i;
+        if (key >= n_keys) break;
+        const int page = bt[key >> 8];
+        const uint4* kp = reinterpret_cast<const uint4*>(k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
+        float kf[16];
+        unpack8(kp[0], kf);
+        unpack8(kp[1], kf + 8);
+        float n2 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) n2 = __builtin_fmaf(kf[c], kf[c], n2);
+        kn = fmaxf(kn, n2);
     }
-    if (tid == 0) *status = carry > capacity ? 1 : 0;
+    __shared__ float red[4];
+    kn = wave_max(kn);
+    if ((tid & 63) == 0) red[tid >> 6] = kn;
+    __syncthreads();
+    if (tid == 0) knorm[(size_t)r * nblk + blk] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+struct ChunkWs {
+    size_t crow, qlow, counts, knorm, ctr, pool, head;
+    int nblk;
+};
+
+ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    ChunkWs w;
+    w.nblk = (n_keys + kNormKeys - 1) / kNormKeys;
+    w.crow = 0;
+    w.qlow = w.crow + up((size_t)rows * sizeof(CRow));
+    w.counts = w.qlow + up((size_t)rows * 16 * 2);
+    w.knorm = w.counts + up((size_t)rows * 4);
+    w.ctr = w.knorm + up((size_t)n_ret * w.nblk * 4);
+    w.pool = w.ctr + 256;
+    w.head = w.pool;
+    return w;
 }
 
 }  // namespace
 
-size_t chunk_select_ws_bytes(int rows) {
-    return ((size_t)rows * sizeof(CRow) + 255) / 256 * 256 + ((size_t)rows * 16 * 2 + 255) / 256 * 256 +
-           ((size_t)rows * 4 + 255) / 256 * 256;
+size_t chunk_select_head_bytes(int rows, int n_ret, int n_keys) { return chunk_ws(rows, n_ret, n_keys).head; }
+
+size_t chunk_select_ws_bytes(int rows, int n_ret, int n_keys) {
+    return chunk_select_head_bytes(rows, n_ret, n_keys) + (size_t)rows * kPoolPerRow * 8;
 }
 
 hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
-                               const float* top_p, void* ws, const SelOut& out, hipStream_t s) {
+                               const float* top_p, void* ws, size_t ws_bytes, const SelOut& out, hipStream_t s) {
     const int rows = g.n_tok * g.n_ret;
+    const int n_keys = g.pos0 + g.n_tok;
+    const ChunkWs w = chunk_ws(rows, g.n_ret, n_keys);
+    if (g.D > 128 || ws_bytes < w.head) return hipErrorInvalidValue;
     char* base = (char*)ws;
-    CRow* crow = (CRow*)base;
-    base += ((size_t)rows * sizeof(CRow) + 255) / 256 * 256;
-    uint16_t* qlow = (uint16_t*)base;
-    base += ((size_t)rows * 16 * 2 + 255) / 256 * 256;
-    int* counts = (int*)base;
+    CRow* crow = (CRow*)(base + w.crow);
+    uint16_t* qlow = (uint16_t*)(base + w.qlow);
+    int* counts = (int*)(base + w.counts);
+    float* knorm = (float*)(base + w.knorm);
+    unsigned long long* ctr = (unsigned long long*)(base + w.ctr);
+    unsigned long long* pool = (unsigned long long*)(base + w.pool);
+    const unsigned long long pool_cap = (ws_bytes - w.head) / 8;
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
+    hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
+                       w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
-                       (const bf16_t*)k_low, top_p, crow, qlow);
-    // counting pass (rows of mode "all of U" are counted here too), row pointers, writing pass
-    hipLaunchKernelGGL(k_csel_emit, grid, dim3(64), 0, s, g, (const bf16_t*)k_low, qlow, crow, out.row_ptr,
-                       out.idx, out.capacity, out.status, counts, 0);
+                       (const bf16_t*)k_low, top_p, crow, qlow, knorm, w.nblk, pool, ctr, pool_cap);
+    hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, pool, counts);
+    hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 512)), dim3(kRTL), 0, s, g, crow, rows, pool,
+                       counts);
     hipLaunchKernelGGL(k_csel_rowptr, dim3(1), dim3(1024), 0, s, counts, rows, out.row_ptr, out.capacity,
                        out.status);
+    hipLaunchKernelGGL(k_csel_copy, dim3(rows), dim3(256), 0, s, crow, pool, out.row_ptr, out.idx, out.status);
     hipLaunchKernelGGL(k_csel_emit, grid, dim3(64), 0, s, g, (const bf16_t*)k_low, qlow, crow, out.row_ptr,
-                       out.idx, out.capacity, out.status, counts, 1);
+                       out.idx, out.status);
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ class Dev:
     def rows(self) -> int:
         return self.w.n_tok * self.w.n_ret
 
-    def select(self, capacity: int | None = None):
+    def select(self, capacity: int | None = None, ws_bytes: int | None = None):
         w = self.w
         if capacity is None:
             capacity = sum(min(w.row_pos(t) + 1, 1 << 30) for t in range(w.n_tok)) * w.n_ret
@@ -64,7 +64,8 @@ class Dev:
         self.idx = torch.full((max(capacity, 1),), -1, dtype=torch.int32, device="cuda")
         self.status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
         self.sel = rtp.make_sel(self.row_ptr, self.idx, self.status)
-        ws_bytes = rtp.topp_select_workspace(self.layer, self.cache, self.query)
+        if ws_bytes is None:
+            ws_bytes = rtp.topp_select_workspace(self.layer, self.cache, self.query)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         rtp.topp_select(self.layer, self.cache, self.query, self.w_q, self.top_p, self.sel, ws)
         torch.cuda.synchronize()

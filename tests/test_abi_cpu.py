@@ -107,7 +107,7 @@ def test_layer_checks(kw, code):
     (dict(null="k_low"), {}, rtp.RTP_EINVAL),
     (dict(batch=0), {}, rtp.RTP_EINVAL),
     (dict(max_blocks=3, max_seq_len=1000), {}, rtp.RTP_EINVAL),       # 3 pages < 1000 tokens
-    (dict(max_seq_len=(1 << 22) + 1, max_blocks=20000), {}, rtp.RTP_EUNSUPPORTED),
+    (dict(max_seq_len=(1 << 20) + 1, max_blocks=20000), {}, rtp.RTP_EUNSUPPORTED),
     ({}, dict(n_tok=3), rtp.RTP_EINVAL),                               # decode n_tok != batch
     ({}, dict(kind=rtp.RTP_CHUNK, n_tok=10, seq=2), rtp.RTP_EINVAL),   # seq out of range
     ({}, dict(kind=rtp.RTP_CHUNK, n_tok=10, pos0=995), rtp.RTP_EINVAL),  # rows past max_seq_len
@@ -166,3 +166,21 @@ def test_workspace_sizes_grow_with_context():
                                         ctypes.byref(_query()))
     assert big > small > 0
     assert lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(_cache(batch=0)), ctypes.byref(_query())) == 0
+
+
+def test_chunk_select_minimum_workspace():
+    # a bf16 prefill chunk: the recommended size holds a candidate buffer per
+    # row; anything down to the minimum is accepted, below it is rejected
+    lib = rtp.load()
+    L = _layer()
+    C = _cache(max_blocks=64, max_seq_len=16384)
+    Q = _query(kind=rtp.RTP_CHUNK, n_tok=300, pos0=5000)
+    full = lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    low = lib.rtp_topp_select_workspace_min(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    rows = 300 * 3
+    assert 0 < low < full and full - low == rows * 4096 * 8
+    assert _select(L, C, Q, _sel(), ws_bytes=low - 1) == rtp.RTP_EWORKSPACE
+    # decode queries: one size
+    D = _query()
+    assert (lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(D)) ==
+            lib.rtp_topp_select_workspace_min(ctypes.byref(L), ctypes.byref(C), ctypes.byref(D)))

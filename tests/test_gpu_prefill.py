@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import sparse_attention_dim_amd as rtp
 import synth
 from gpu_util import Dev, band_accept, check_out, oracle_k_low, out_f32, say
 
@@ -65,6 +66,26 @@ def test_selection_matches_oracle(dev, orc):
         assert ok, (t, r, len(sets[t * w.n_ret + r]), len(res["sel"]))
         exact += ex
     assert exact >= len(orc["rows"]) - 2
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.01])
+def test_selection_radix_level_path(dev, orc, frac):
+    # a workspace below the recommended size: the rows whose candidate set does
+    # not fit the smaller per-row buffer are resolved by radix levels on the
+    # exact score and emitted by a rescan (frac 0: every row); same sets
+    w = dev.w
+    say("[gpu] prefill top-p select, reduced workspace", frac, w.name)
+    full = rtp.topp_select_workspace(dev.layer, dev.cache, dev.query)
+    low = rtp.topp_select_workspace_min(dev.layer, dev.cache, dev.query)
+    st, rp, ref_sets = dev.select()
+    assert st == 0
+    st, rp, sets = dev.select(ws_bytes=low + int((full - low) * frac))
+    assert st == 0
+    for i in range(dev.rows):
+        np.testing.assert_array_equal(sets[i], ref_sets[i])
+    for (t, r), res in orc["rows"].items():
+        ok, _ = band_accept(sets[t * w.n_ret + r], res["order"], res["cum"], float(w.top_p[0]))
+        assert ok, (t, r)
 
 
 def test_sparse_prefill_matches_oracle(dev, orc):
@@ -133,7 +154,6 @@ def test_prefill_last_row_equals_decode(dev):
     dev.sparse()
     dev.window()
     pre = out_f32(dev.out)[w.n_tok - 1]
-    import sparse_attention_dim_amd as rtp
     q_dec = dev.q[w.n_tok - 1:].contiguous()
     qd = rtp.make_query(q_dec, rtp.RTP_DECODE)
     rows = w.n_ret
