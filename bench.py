@@ -3,7 +3,13 @@
 One step = one decode step of one attention layer for the whole batch: the
 indexer append of the new tokens, top-p selection for every retrieval head,
 sparse attention over the selected rows, and window attention for the local
-heads (on a second stream, overlapping the retrieval heads' work).  The same
+heads (on a second stream, overlapping the retrieval heads' work).
+
+The prefill leg times one chunk of one layer the same way (top-p selection of
+every chunk row, sparse prefill attention, window prefill attention on the
+second stream) at two sizes: 4096 rows at context 131072 and 8192 rows at
+context 1048576, next to dense causal attention of the same chunk on the same
+GPU, and reports tokens/s/layer and the speedup.  The same
 step captured as one HIP graph per layer instance is timed too and reported
 beside it. (decode bf16, batch 8, context 131072, 32 query / 8 KV heads, head dim
 128, 6 retrieval heads, top-p 0.95, window 2048 + 64 sinks).  Inputs are
@@ -28,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0          # dense bf16
 METRIC = "decode µs/step/layer + prefill tokens/s/layer at 128K–1M ctx; % HBM/MFMA peak"
 COUNTERS = os.path.join(ROOT, "profiles", "k_sel_score_decode_bf16_B8_L131072_counters.json")
 SCORE_SRC = os.path.join(ROOT, "sparse_attention_dim_amd", "csrc", "select.hip")
@@ -100,6 +107,126 @@ def cpu_baseline(w, n_seq: int, threads: int):
     return dt, sizes
 
 
+def prefill_leg(cfg: int, steps: int):
+    """One prefill chunk of one layer: eager select + sparse prefill on the
+    main stream, window prefill on a second stream; dense causal attention of
+    the same chunk for comparison."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_dim_amd as rtp
+    import synth
+    from sparse_attention_dim_amd.paged import PagedCache, rtp_dtype, to_device
+
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    w = synth.config(cfg)
+    L = int(w.seq_lens[0])
+    log("[bench] prefill %s generated in %.1fs" % (w.name, time.time() - t0))
+    layer = rtp.make_layer(w.Hq, w.Hkv, w.D, rtp_dtype(w.dtype), w.ret_heads, w.window, w.sinks,
+                           w.attn_scale, w.idx_scale)
+    pc = PagedCache(w.k, w.v, w.n_ret, w.dtype, device=dev, permute_seed=100)
+    cache = pc.cache(L)
+    q = to_device(w.q, dev)
+    w_q, w_k = to_device(w.w_q, dev), to_device(w.w_k, dev)
+    top_p = torch.from_numpy(w.top_p).to(dev)
+    query = rtp.make_query(q, rtp.RTP_CHUNK, w.chunk_seq, w.chunk_pos0)
+    sid, pos = pc.all_positions(0, dev)
+    rtp.indexer_append(layer, cache, w_k, sid, pos)
+    rows = w.n_tok * w.n_ret
+    cap = rows * 16384
+    row_ptr = torch.zeros(rows + 1, dtype=torch.int64, device=dev)
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sel = rtp.make_sel(row_ptr, idx, status)
+    ws_sel = torch.empty(rtp.topp_select_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
+    ws_sp = torch.empty(rtp.sparse_attn_workspace(layer, cache, query, cap), dtype=torch.uint8, device=dev)
+    ws_win = torch.empty(rtp.window_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
+    out = torch.zeros_like(q)
+    side = torch.cuda.Stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(times=None):
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            if times is not None:
+                ev[2].record(side)
+            rtp.window_attn(layer, cache, query, out, ws_win, stream=side)
+            if times is not None:
+                ev[3].record(side)
+        if times is not None:
+            ev[0].record()
+        rtp.topp_select(layer, cache, query, w_q, top_p, sel, ws_sel)
+        if times is not None:
+            ev[1].record()
+        rtp.sparse_attn_prefill(layer, cache, query, sel, out, ws_sp)
+        main.wait_stream(side)
+
+    step()
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "selection status %d" % int(status.item())
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    step_ms = a.elapsed_time(b) / steps
+    # per-call times, sequential
+    sel_ms, sp_ms, win_ms = [], [], []
+    for _ in range(2):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        rtp.topp_select(layer, cache, query, w_q, top_p, sel, ws_sel)
+        e[1].record()
+        rtp.sparse_attn_prefill(layer, cache, query, sel, out, ws_sp)
+        e[2].record()
+        rtp.window_attn(layer, cache, query, out, ws_win)
+        e[3].record()
+        torch.cuda.synchronize()
+        sel_ms.append(e[0].elapsed_time(e[1]))
+        sp_ms.append(e[1].elapsed_time(e[2]))
+        win_ms.append(e[2].elapsed_time(e[3]))
+    rp = row_ptr.cpu().numpy()
+    sizes = np.diff(rp)
+    n_sel = int(rp[-1])
+    ws_d = torch.empty(rtp.dense_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
+    dout = torch.zeros_like(q)
+    rtp.dense_attn(layer, cache, query, dout, ws_d)
+    torch.cuda.synchronize()
+    a.record()
+    nd = 2
+    for _ in range(nd):
+        rtp.dense_attn(layer, cache, query, dout, ws_d)
+    b.record()
+    torch.cuda.synchronize()
+    dense_ms = a.elapsed_time(b) / nd
+    # algorithmic flops: QK and PV, 2 D flops each per (query head, key) pair
+    f_pair = 4 * w.D
+    sp_flops = n_sel * f_pair
+    win_pairs = sum(min(w.window + w.sinks, w.row_pos(t) + 1) for t in range(w.n_tok)) * (w.Hq - w.n_ret)
+    dense_pairs = sum(w.row_pos(t) + 1 for t in range(w.n_tok)) * w.Hq
+    sp_t, win_t = float(np.median(sp_ms)), float(np.median(win_ms))
+    res = {
+        "workload": w.name, "chunk_rows": w.n_tok, "context": L, "top_p": float(w.top_p[0]),
+        "tokens_per_s": round(w.n_tok / (step_ms * 1e-3), 1), "step_ms": round(step_ms, 3),
+        "select_ms": round(float(np.median(sel_ms)), 3), "sparse_ms": round(sp_t, 3),
+        "window_ms": round(win_t, 3),
+        "selected_per_row": {"min": int(sizes.min()), "median": int(np.median(sizes)),
+                             "mean": round(float(sizes.mean()), 1), "max": int(sizes.max())},
+        "sparse_tflops": round(sp_flops / (sp_t * 1e-3) / 1e12, 2),
+        "sparse_mfma_frac": round(sp_flops / (sp_t * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 5),
+        "window_tflops": round(win_pairs * f_pair / (win_t * 1e-3) / 1e12, 2),
+        "dense_ms": round(dense_ms, 3),
+        "dense_tflops": round(dense_pairs * f_pair / (dense_ms * 1e-3) / 1e12, 2),
+        "speedup_vs_dense": round(dense_ms / step_ms, 3),
+    }
+    del pc, cache, idx, ws_sel, ws_sp, ws_win, ws_d
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +237,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--contiguous", action="store_true", help="pages in order instead of permuted")
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays instead of eager launches")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -299,6 +428,10 @@ def main():
                          "(indexer keys of the context precomputed untimed), scaled x%d to the batch"
                          % (ns, B, B // ns)}
 
+    prefill = None
+    if not args.no_prefill:
+        prefill = {"128k": prefill_leg(3, args.prefill_steps), "1m": prefill_leg(4, max(1, args.prefill_steps // 2))}
+
     res = {
         "metric": METRIC,
         "value": round(ms * 1e3, 2),
@@ -332,6 +465,7 @@ def main():
         "dense_us": round(dense_ms * 1e3, 2),
         "dense_hbm_frac": round(dense_bytes / (dense_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "speedup_vs_dense": round(dense_ms / ms, 3),
+        "prefill": prefill,
     }
     print(json.dumps(res), flush=True)
 

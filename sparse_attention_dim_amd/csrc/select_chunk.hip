@@ -46,7 +46,6 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTR = 32;          // rows per workgroup
 constexpr int kHB = 128;         // P2 histogram bins
-constexpr int kHBP = kHB + 1;    // padded row stride, spreads rows over LDS banks
 constexpr float kBinsPerX = 4.0f;
 constexpr int kNB = 64;          // radix buckets per level
 constexpr int kNBP = kNB + 1;
@@ -68,7 +67,7 @@ constexpr int kBuf = 3;          // U held in the buffer (sorted by the resolve 
 struct CRow {
     float mp;        // m' (upper bound of the row's exact maximum)
     float delta;     // 8x the |MFMA - exact| bound of the row
-    float mpB;       // m' s kBinsPerX: bin argument x = mpB - e s kBinsPerX
+    float e_thr;     // a pair is in U iff its MFMA score e >= e_thr
     float T;         // exact score of the cut (kLevel)
     float d_edge;    // exact scores of keys outside U are <= d_edge
     int mode;
@@ -142,7 +141,9 @@ constexpr int kPre = 8;          // tile loads in flight per wave
 
 // LDS layout: the q projection weights, the P2 histogram and the level
 // structures are live at different times and share one buffer.
-constexpr int kHistBytes = kTR * kHBP * 8 + kTR * kHBP * 4;
+// P2 histograms are bin-major, so the bank of a lane's atomic depends on its
+// row (mass, fp64 [bin][row]) or on the lane (count, u32 [bin][lane]) only.
+constexpr int kHistBytes = kHB * kTR * 8 + kHB * 64 * 4;
 constexpr int kHmBytes = kTR * kNBP * 8;
 constexpr int kHcBytes = kTR * kNBP * 4;
 constexpr int kCandBytes = kTR * kCapC * 8;
@@ -174,8 +175,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 
     __shared__ __align__(16) unsigned char smem[kSmemBytes];
     float* wq = reinterpret_cast<float*>(smem);
-    double(*hist)[kHBP] = reinterpret_cast<double(*)[kHBP]>(smem);
-    uint32_t(*hcnt)[kHBP] = reinterpret_cast<uint32_t(*)[kHBP]>(smem + kTR * kHBP * 8);
+    double(*hist)[kTR] = reinterpret_cast<double(*)[kTR]>(smem);
+    uint32_t(*hcnt)[64] = reinterpret_cast<uint32_t(*)[64]>(smem + kHB * kTR * 8);
     unsigned long long(*hm)[kNBP] = reinterpret_cast<unsigned long long(*)[kNBP]>(smem);
     uint32_t(*hc)[kNBP] = reinterpret_cast<uint32_t(*)[kNBP]>(smem + kHmBytes);
     unsigned long long(*cand)[kCapC] = reinterpret_cast<unsigned long long(*)[kCapC]>(smem + kHmBytes + kHcBytes);
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     __shared__ uint32_t kmax_bits;
     __shared__ uint32_t cand_n[kTR], ucnt[kTR];
     __shared__ unsigned long long zu[kTR];               // exact mass of U
-    __shared__ float r_mp[kTR], r_delta[kTR], r_mpB[kTR], r_T[kTR], r_edge[kTR];
+    __shared__ float r_mp[kTR], r_delta[kTR], r_mpB[kTR], r_T[kTR], r_edge[kTR], r_ethr[kTR];
     __shared__ uint32_t r_ucount[kTR];
     __shared__ unsigned long long r_seg[kTR];
     __shared__ int r_mode[kTR], r_uend[kTR], r_ntie[kTR], r_done[kTR], r_gather[kTR], r_bad[kTR];
@@ -271,10 +272,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         });
         m_e = fmaxf(m_e, __shfl_xor(m_e, 32));
         if (row_ok && hh == 0 && m_e > -INFINITY) atomicMax(&rmax[lr], score_key(m_e));
-        for (int x = tid; x < kTR * kHBP; x += 256) {
-            (&hist[0][0])[x] = 0.0;
-            (&hcnt[0][0])[x] = 0u;
-        }
+        for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
+        for (int x = tid; x < kHB * 64; x += 256) (&hcnt[0][0])[x] = 0u;
         __syncthreads();
         if (tid < kTR) {
             float qn2 = 0.0f;
@@ -294,8 +293,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     // ---- P2: mass and count histograms of the approximate weights exp(-x / 4)
     {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
-        double* hrow = hist[lr];
-        uint32_t* crow = hcnt[lr];
+        double* hrow = &hist[0][lr];
+        uint32_t* crow = &hcnt[0][lane];
         tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
             if (it < nfull) {
@@ -303,8 +302,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 for (int i = 0; i < 16; ++i) {
                     const float x = bin_x(sc[i], sB, mpB);
                     const int b = bin_of(x);
-                    atomicAdd(&hrow[b], (double)__builtin_amdgcn_exp2f(x * kW));
-                    atomicAdd(&crow[b], 1u);
+                    atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
+                    atomicAdd(&crow[b * 64], 1u);
                 }
             } else {
 #pragma unroll
@@ -312,8 +311,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                     if (key_of(it, i) <= pos) {
                         const float x = bin_x(sc[i], sB, mpB);
                         const int b = bin_of(x);
-                        atomicAdd(&hrow[b], (double)__builtin_amdgcn_exp2f(x * kW));
-                        atomicAdd(&crow[b], 1u);
+                        atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
+                        atomicAdd(&crow[b * 64], 1u);
                     }
                 }
             }
@@ -337,6 +336,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             r_light[row] = 0ull;
             r_ucount[row] = 0u;
             r_seg[row] = kNoSeg;
+            r_ethr[row] = -INFINITY;
             if (row >= n_valid) {
                 r_done[row] = 1;
             } else if (!(p < 1.0f)) {
@@ -345,12 +345,12 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             } else {
                 const double sd = (double)s * (double)r_delta[row];
                 double Z = 0.0;
-                for (int b = 0; b < kHB; ++b) Z += hist[row][b];
+                for (int b = 0; b < kHB; ++b) Z += hist[b][row];
                 const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * Z;
                 int bc = kHB - 1;
                 double cum = 0.0;
                 for (int b = 0; b < kHB; ++b) {
-                    cum += hist[row][b];
+                    cum += hist[b][row];
                     if (cum >= tgt_a) {
                         bc = b;
                         break;
@@ -358,9 +358,9 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 }
                 const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
                 double light = 0.0;
-                for (int b = ue + 1; b < kHB; ++b) light += hist[row][b];
+                for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
                 uint32_t uc = 0;
-                for (int b = 0; b <= ue; ++b) uc += hcnt[row][b];
+                for (int b = 0; b <= ue; ++b) uc += hcnt[b][row] + hcnt[b][row + 32];
                 r_ucount[row] = uc;
                 r_uend[row] = ue;
                 r_light[row] = (unsigned long long)__double2ll_rn(light * kFix);
@@ -368,6 +368,15 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 if (ue == kHB - 1) {
                     r_klo[row] = 0u;                      // every key is in U
                 } else {
+                    // the smallest MFMA score whose bin is <= ue (the bin is
+                    // monotone in the score, so U is e >= e_thr)
+                    const float mpBr = r_mpB[row];
+                    uint32_t klo = score_key(-INFINITY), khi = score_key(r_mp[row]);
+                    while (klo < khi) {
+                        const uint32_t mid = klo + ((khi - klo) >> 1);
+                        if (bin_of(bin_x(key_score(mid), sB, mpBr)) <= ue) khi = mid; else klo = mid + 1;
+                    }
+                    r_ethr[row] = key_score(khi);
                     // keys of U: x < (ue + 1) / 4, so e > m' - (ue + 1) / (4 s);
                     // keys outside: the reverse.  The margin covers the float
                     // rounding of the bin argument and the MFMA deviation.
@@ -410,7 +419,6 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         }
         __syncthreads();
     }
-    const int u_end = r_uend[lr];
 
     // ---- P3 and the radix levels on the exact score.  P3 (level 0) computes
     // the exact score and weight of every key of U: the mass of U, and U's
@@ -469,6 +477,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             wave_lds_sync();
         };
         const bool active = row_ok && !r_done[lr];
+        const float e_thr = r_ethr[lr];
         const bool ranged = active && (r_gather[lr] || level > 0);
         const float lo = ranged ? key_score(r_klo[lr]) : 0.0f, hi = ranged ? key_score(r_khi[lr]) : 0.0f;
         const float dl = r_delta[lr];
@@ -478,7 +487,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             uint32_t need = 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                bool in = active && bin_of(bin_x(sc[i], sB, mpB)) <= u_end;
+                bool in = active && sc[i] >= e_thr;
                 if (it >= nfull) in = in && key_of(it, i) <= pos;
                 // only pairs whose exact score can fall inside [lo, hi]
                 if (ranged) in = in && !(sc[i] + dl < lo) && !(sc[i] - dl > hi);
@@ -598,7 +607,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             CRow out;
             out.mp = r_mp[row];
             out.delta = r_delta[row];
-            out.mpB = r_mpB[row];
+            out.e_thr = r_ethr[row];
             out.seg = r_seg[row];
             out.d_edge = r_edge[row];
             out.u_end = r_uend[row];
@@ -897,7 +906,6 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
     const CRow cr = rows[row];
     const bool row_ok = lr < n_valid && cr.mode == kLevel;
     if (__ballot(row_ok) == 0ull) return;
-    const float sB = g.idx_scale * kBinsPerX;
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     float q16[16];
     uint4 qb;
@@ -929,7 +937,7 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int kj = it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
-            const bool in = row_ok && kj <= pos && bin_of(bin_x(sc[i], sB, cr.mpB)) <= cr.u_end;
+            const bool in = row_ok && kj <= pos && sc[i] >= cr.e_thr;
             const bool hi = sc[i] - cr.delta > cr.T;
             const bool near = !hi && !(sc[i] + cr.delta < cr.T);
             sel |= (uint32_t)(in && hi) << i;
