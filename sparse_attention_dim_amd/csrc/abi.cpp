@@ -147,8 +147,8 @@ constexpr size_t kScoreBudget = (size_t)4 << 30;   // bytes of scores per row gr
 struct SelPlan {
     int rows_total, group_rows, nchunk;
     int64_t lpad;
-    size_t off_scores, off_cmax, off_qlow, off_hmass, off_hcnt, off_st,
-        off_cand, off_cand_n, off_chunk, total;
+    size_t off_scores, off_cmax, off_qlow, off_chist, off_st, off_sel, off_chunk, off_ubuf, off_rown, off_cbase,
+        off_cn, total;
 };
 
 // Prefill chunks in bf16 take the tiled selection (the rows of one retrieval
@@ -164,19 +164,23 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     const int64_t keys = max_keys(C, Q);
     p.nchunk = (int)((keys + rtp::kChunk - 1) / rtp::kChunk);
     p.lpad = (int64_t)p.nchunk * rtp::kChunk;
-    const int64_t by_budget = std::max<int64_t>(1, (int64_t)(kScoreBudget / ((size_t)p.lpad * 4)));
+    const size_t per_row =
+        (size_t)p.lpad * 4 + (size_t)p.nchunk * (4 + 4 + 4 + 4 + rtp::kCB * 8) + rtp::kCand * 12 + 1024;
+    const int64_t by_budget = std::max<int64_t>(1, (int64_t)(kScoreBudget / per_row));
     p.group_rows = (int)std::min<int64_t>({(int64_t)p.rows_total, by_budget, (int64_t)65535});
     const size_t G = (size_t)p.group_rows;
     size_t o = 0;
     p.off_scores = o; o = align256(o + G * (size_t)p.lpad * 4);
     p.off_cmax = o; o = align256(o + G * (size_t)p.nchunk * 4);
     p.off_qlow = o; o = align256(o + G * 16 * 2);
-    p.off_hmass = o; o = align256(o + G * rtp::kNB1 * 8);
-    p.off_hcnt = o; o = align256(o + G * rtp::kNB1 * 4);
+    p.off_chist = o; o = align256(o + G * (size_t)p.nchunk * rtp::kCB * 8);
     p.off_st = o; o = align256(o + G * sizeof(rtp::RowState));
-    p.off_cand = o; o = align256(o + G * rtp::kCand * 8);
-    p.off_cand_n = o; o = align256(o + G * 4);
+    p.off_sel = o; o = align256(o + G * rtp::kCand * 4);
     p.off_chunk = o; o = align256(o + G * (size_t)p.nchunk * 4);
+    p.off_ubuf = o; o = align256(o + G * rtp::kCand * 8);
+    p.off_rown = o; o = align256(o + G * 4);
+    p.off_cbase = o; o = align256(o + G * (size_t)p.nchunk * 4);
+    p.off_cn = o; o = align256(o + G * (size_t)p.nchunk * 4);
     p.total = o;
     return p;
 }
@@ -187,12 +191,14 @@ rtp::SelWs sel_ws(const SelPlan& p, char* base) {
     w.score_ld = p.lpad;
     w.cmax = (uint32_t*)(base + p.off_cmax);
     w.qlow = (uint16_t*)(base + p.off_qlow);
-    w.hmass = (unsigned long long*)(base + p.off_hmass);
-    w.hcnt = (uint32_t*)(base + p.off_hcnt);
+    w.chist = (unsigned long long*)(base + p.off_chist);
     w.st = (rtp::RowState*)(base + p.off_st);
-    w.cand = (unsigned long long*)(base + p.off_cand);
-    w.cand_n = (uint32_t*)(base + p.off_cand_n);
+    w.sel = (uint32_t*)(base + p.off_sel);
     w.chunk_cnt = (uint32_t*)(base + p.off_chunk);
+    w.ubuf = (unsigned long long*)(base + p.off_ubuf);
+    w.row_n = (uint32_t*)(base + p.off_rown);
+    w.chunk_base = (uint32_t*)(base + p.off_cbase);
+    w.chunk_n = (uint32_t*)(base + p.off_cn);
     w.nchunk = p.nchunk;
     w.rows = p.group_rows;
     return w;

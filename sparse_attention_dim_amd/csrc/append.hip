@@ -4,9 +4,11 @@
 // into Sparse Attention Models ...", "Three Key Insights" item 2).
 //
 // One thread per output (token, retrieval head, c): an fp32 FMA chain over the
-// head dimension, d ascending from +0, rounded once to bf16.  A workgroup of
-// 256 threads covers 16 tokens of one retrieval head; the key rows and the
-// head's projection are staged in LDS, so the chains run on LDS operands.
+// head dimension, d ascending from +0, rounded once to bf16.  Bulk appends: a
+// workgroup of 256 threads covers 16 tokens of one retrieval head, with the
+// key rows and the head's projection staged in LDS.  A few tokens (a decode
+// step): one wavefront per (token, four retrieval heads) with the chain's
+// operands in registers, which shortens the dependent path.
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -53,10 +55,41 @@ __global__ __launch_bounds__(256) void k_append(Geo g, const T* __restrict__ kc,
 }
 
 template <typename T, int D>
+__global__ __launch_bounds__(64) void k_append_few(Geo g, const T* __restrict__ kc, bf16_t* __restrict__ k_low,
+                                                   const T* __restrict__ w_k, const int32_t* __restrict__ seq_id,
+                                                   const int32_t* __restrict__ pos) {
+    // grid (n, ceil(num_ret / 4)): lane 16 h + c serves retrieval head 4 blockIdx.y + h
+    const int lane = threadIdx.x;
+    const int i = blockIdx.x;
+    const int r = blockIdx.y * 4 + (lane >> 4), c = lane & 15;
+    if (r >= g.n_ret) return;
+    const int b = seq_id[i], j = pos[i];
+    if (b < 0 || b >= g.batch || j < 0 || j >= g.max_blocks * kBlk) return;
+    const int page = g.block_table[(size_t)b * g.max_blocks + (j >> 8)];
+    const int kvh = g.ret_heads[r] / g.group;
+    const T* kr = kc + (((size_t)page * g.Hkv + kvh) * kBlk + (j & 255)) * D;
+    const T* wc = w_k + (size_t)r * D * kIdx + c;
+    float kv[D], wv[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        kv[d] = ld(kr + d);
+        wv[d] = ld(wc + d * kIdx);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc = __builtin_fmaf(kv[d], wv[d], acc);
+    k_low[(((size_t)page * g.n_ret + r) * kBlk + (j & 255)) * kIdx + c] = f2bf(acc);
+}
+
+template <typename T, int D>
 hipError_t append(const Geo& g, const void* k, void* k_low, const void* w_k, const int32_t* seq_id,
                   const int32_t* pos, int n, hipStream_t s) {
-    hipLaunchKernelGGL((k_append<T, D>), dim3((unsigned)((n + 15) / 16), g.n_ret), dim3(256), 0, s, g,
-                       (const T*)k, (bf16_t*)k_low, (const T*)w_k, seq_id, pos, n);
+    if (n <= 256)
+        hipLaunchKernelGGL((k_append_few<T, D>), dim3((unsigned)n, (g.n_ret + 3) / 4), dim3(64), 0, s, g,
+                           (const T*)k, (bf16_t*)k_low, (const T*)w_k, seq_id, pos);
+    else
+        hipLaunchKernelGGL((k_append<T, D>), dim3((unsigned)((n + 15) / 16), g.n_ret), dim3(256), 0, s, g,
+                           (const T*)k, (bf16_t*)k_low, (const T*)w_k, seq_id, pos, n);
     return hipGetLastError();
 }
 

@@ -76,6 +76,7 @@ struct Stream {
 
     float q[NH][EPV];
     float m[NH], l[NH], o[NH][EPV];
+    bool act[NH];                               // slot h in use (indexed with constants only)
 
     __device__ void init() {
 #pragma unroll
@@ -90,7 +91,7 @@ struct Stream {
     // Keys 0..n-1 of a work item; off(i) is the element offset of key i's row
     // (valid for 0 <= i < n).  Group g of the wave takes keys g, g + GPW, ...
     template <typename F>
-    __device__ void run(int n, int nh, F off, const T* __restrict__ kc, const T* __restrict__ vc) {
+    __device__ void run(int n, F off, const T* __restrict__ kc, const T* __restrict__ vc) {
         const int lane = threadIdx.x & 63;
         const int g = lane / LPK, sl = (lane % LPK) * EPV;
         for (int base = 0; base < n; base += GPW * U) {
@@ -119,7 +120,7 @@ struct Stream {
             }
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-                if (h >= nh) continue;
+                if (!act[h]) continue;
                 float cm = s[0][h];
 #pragma unroll
                 for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u][h]);
@@ -145,10 +146,10 @@ struct Stream {
 
     // Merge the groups of the wave; afterwards lanes 0..LPK-1 hold head h's
     // output slices and every lane holds the merged (m, l).
-    __device__ void merge(int nh) {
+    __device__ void merge() {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
-            if (h >= nh) continue;
+            if (!act[h]) continue;
             float M = m[h];
             for (int off = LPK; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off));
             const float sc = M == -INFINITY ? 0.0f : exp2f(m[h] - M);
@@ -264,8 +265,9 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
         for (int e = 0; e < EPV; ++e) st.q[0][e] = ld(q + ((size_t)t * g.Hq + h) * D + sl + e) * sc;
         __syncthreads();
         auto off = [&](int i) { return (size_t)joff[i] * D; };
-        st.run(n, 1, off, kc, vc);
-        st.merge(1);
+        st.act[0] = true;
+        st.run(n, off, kc, vc);
+        st.merge();
         st.write(0, ws.part + (size_t)item * (D + 2));
         __syncthreads();
     }
@@ -360,22 +362,22 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
     if (v0 >= n_all) return;
     const int n = min(split_keys, n_all - v0);
 
-    int heads[NH];
-    int nh = 0;
-    for (int i = 0; i < g.group && nh < NH; ++i) {
-        const int hh = kvh * g.group + i;
-        if (dense || !g.is_ret[hh]) heads[nh++] = hh;
-    }
-    if (nh == 0) return;
+    // slot i serves query head kvh * group + i (group <= NH) if that head
+    // needs this kernel; slots are indexed with constants only, so the
+    // per-head state stays in registers
     const float sc = g.attn_scale * kLog2e;
     const int sl = (lane % LPK) * EPV;
     S st;
     st.init();
+    bool any = false;
 #pragma unroll
     for (int i = 0; i < NH; ++i) {
-        if (i < nh) {
+        const int hh = kvh * g.group + i;
+        st.act[i] = i < g.group && (dense || !g.is_ret[hh]);
+        any = any || st.act[i];
+        if (st.act[i]) {
             float f[EPV];
-            Pack<T>::unpack(*reinterpret_cast<const uint4*>(q + ((size_t)b * g.Hq + heads[i]) * D + sl), f);
+            Pack<T>::unpack(*reinterpret_cast<const uint4*>(q + ((size_t)b * g.Hq + hh) * D + sl), f);
 #pragma unroll
             for (int e = 0; e < EPV; ++e) st.q[i][e] = f[e] * sc;
         } else {
@@ -383,6 +385,7 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
             for (int e = 0; e < EPV; ++e) st.q[i][e] = 0.0f;
         }
     }
+    if (!any) return;
     // Page ids of the split, resolved once into LDS.  The split's virtual keys
     // [v0, v0 + n) are a run of sink positions followed by a run of window
     // positions; each run covers consecutive pages.
@@ -410,10 +413,11 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
         }
         return kv_off(g, pgs[pi], kvh, j & 255, D);
     };
-    st.run(n, nh, off, kc, vc);
-    st.merge(nh);
-    for (int i = 0; i < nh; ++i)
-        st.write(i, part + (((size_t)b * g.Hq + heads[i]) * nsplit + blockIdx.x) * (D + 2));
+    st.run(n, off, kc, vc);
+    st.merge();
+#pragma unroll
+    for (int i = 0; i < NH; ++i)
+        if (st.act[i]) st.write(i, part + (((size_t)b * g.Hq + kvh * g.group + i) * nsplit + blockIdx.x) * (D + 2));
 }
 
 template <typename T, int D>

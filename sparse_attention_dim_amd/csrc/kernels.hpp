@@ -37,20 +37,18 @@ __device__ __forceinline__ int row_pos(const Geo& g, int t) {
 // Per-row state of the top-p selection (device workspace).
 struct RowState {
     float m;                      // row maximum score
-    int b1;                       // level-1 cut bin (kNB1 = keep every key)
-    unsigned long long Z;         // total mass (fixed point)
-    unsigned long long target;    // ceil(p * Z)
-    unsigned long long S_above;   // mass of bins < b1
-    uint32_t cnt_above;           // keys in bins < b1
-    uint32_t cnt_b1;              // keys in bin b1
-    uint32_t Tkey;                // key of the last selected key of bin b1
-    int32_t jT;                   // its index (ties: every key == Tkey with j <= jT is taken)
+    int32_t mode;                 // 0 every key, 1 ordered list in SelWs::sel, 2 threshold (Tkey, jT)
+    uint32_t Tkey;                // threshold: keys with score key > Tkey, or == Tkey and index <= jT
+    int32_t jT;
     int32_t L;                    // keys of the row
     int32_t count;                // selected keys
+    unsigned long long target;    // ceil(p Z), fixed point
+    float d_thr;                  // U = keys with score >= d_thr
 };
 
-constexpr int kChunk = 4096;      // keys per workgroup in the selection passes
-constexpr int kCand = 8192;       // in-bin candidates resolved by one sort
+constexpr int kChunk = 4096;      // keys per workgroup of the scoring pass
+constexpr int kCB = 128;          // mass-histogram bins per chunk (1/4 unit of s (m_c - d) each)
+constexpr int kCand = 8192;       // candidates ranked by one sort
 
 // Device workspace of the selection, for `rows` rows of at most Lpad keys.
 struct SelWs {
@@ -58,12 +56,14 @@ struct SelWs {
     int64_t score_ld;
     uint32_t* cmax;               // [rows][nchunk] ordered keys of chunk maxima
     uint16_t* qlow;               // [rows][16]
-    unsigned long long* hmass;    // [rows][kNB1]
-    uint32_t* hcnt;               // [rows][kNB1]
+    unsigned long long* chist;    // [rows][nchunk][kCB] chunk mass histograms
     RowState* st;                 // [rows]
-    unsigned long long* cand;     // [rows][kCand]
-    uint32_t* cand_n;             // [rows]
-    uint32_t* chunk_cnt;          // [rows][nchunk] selected keys per chunk, then offsets
+    uint32_t* sel;                // [rows][kCand] selected indices, ascending (mode 1)
+    unsigned long long* ubuf;     // [rows][kCand] gathered U: (score key << 32) | ~index
+    uint32_t* row_n;              // [rows] entries gathered
+    uint32_t* chunk_base;         // [rows][nchunk] block of each chunk in ubuf
+    uint32_t* chunk_n;            // [rows][nchunk] its length
+    uint32_t* chunk_cnt;          // [rows][nchunk] output offsets per chunk (mode 2)
     int nchunk;
     int rows;                     // rows of this group
 };

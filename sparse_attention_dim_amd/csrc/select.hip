@@ -7,18 +7,28 @@
 // Turning Dense LLMs into Sparse Attention Models ...", "Three Key Insights"
 // items 2-3 (low-frequency projection; cumulative top-p).  The forum's
 // "Open Questions and Limitations" notes that per-query token counts are
-// unfriendly to GPU parallelism; here every pass is split into fixed
-// 4096-key chunks so variable budgets never change the launch shape.
+// unfriendly to GPU parallelism; here the scoring pass is split into fixed
+// 4096-key chunks so variable budgets never change its launch shape.
 //
 // Passes (one row = one (query token, retrieval head) pair):
-//   1 score:   q_low, fp32 chain scores of every key, chunk maxima
-//   2 hist:    exact fixed-point mass per level-1 bin (device atomics)
-//   2b cut:    per row, the bin b1 where the cumulative mass reaches p
-//   3 refine:  per-chunk count of keys above b1; keys of bin b1 gathered
-//   4 resolve: one workgroup per row ranks bin b1 exactly (score desc, index
-//              asc), fixes the last selected key and the per-chunk offsets
-//   4b rowptr: CSR row pointers and the capacity check
-//   5 emit:    ordered compaction of the selected indices
+//   qlow:    q_low = bf16(fp32 chain over d of q . W_q), once per row
+//   score:   fp32 chain scores of every key of a chunk, the chunk maximum m_c,
+//            and the chunk's cumulative mass histogram: exact fixed-point
+//            weights exp(s (d - m_c)) summed over bins of x_c = s (m_c - d)
+//            (1/4 wide)
+//   resolve: one workgroup per row.  Row maximum m and total mass
+//            Z = sum_c exp(s (m_c - m)) Z_c; every chunk bin whose upper edge
+//            lies below a threshold X on the row's x axis certainly holds
+//            keys with x < X, which gives a lower bound of the mass above
+//            any X.  The smallest X whose bound reaches the target fixes the
+//            candidate set U = {d >= m - X / s}: it holds every key ranked at
+//            or above the cut.  U is gathered from the scores into LDS and the
+//            cut is found by radix selection over its score keys with exact
+//            masses per bucket (ties: lowest indices first); when U does not
+//            fit LDS the same selection runs over the row's scores.  U is
+//            gathered in index order, so the selected keys are its filter.
+//   rowptr:  CSR row pointers and the capacity check
+//   emit:    ordered compaction of every chunk's selected indices
 // Workgroups of one pass never wait on each other: every hand-off between
 // workgroups is a kernel boundary (a device-scope fence per workgroup costs an
 // L2 write-back and invalidate on this multi-XCD part).
@@ -29,14 +39,11 @@ namespace rtp {
 
 namespace {
 
-// level-1 bin only: identical arithmetic to weight_bin's bin
-__device__ __forceinline__ int bin_of(float d, float m, float s) {
-    float t = d - m;
-    float y = s * t;
-    float x = -y * kBinsPerUnit;
-    x = fminf(x, (float)(kNB1 - 1));
-    return (int)x;
-}
+constexpr float kCBPerUnit = 4.0f;   // chunk histogram bins per unit of x
+constexpr int kGB = 256;             // row threshold grid (same width), X = k / 4
+constexpr int kRT = 1024;            // resolve workgroup
+constexpr int kNR = 2048;            // radix buckets of the narrowing fallback
+constexpr int kMaxChunks = 256;      // 2^20 keys
 
 __device__ __forceinline__ void unpack8(uint4 a, float* f) {
     f[0] = __uint_as_float(a.x << 16); f[1] = __uint_as_float(a.x & 0xFFFF0000u);
@@ -63,50 +70,58 @@ __device__ __forceinline__ RowInfo row_info(const Geo& g, int row0, int lrow) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 1.  grid (nchunk, rows), 256 threads.  Thread i of chunk c scores keys
+// q_low of every row of the group.  grid (ceil(rows / 4)), 64 threads: lane
+// 16 w + c runs the fixed-order chain of component c of row 4 blockIdx + w with
+// its operands in registers.
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_sel_qlow(Geo g, const T* __restrict__ q, const T* __restrict__ w_q,
+                                                 int row0, int rows, uint16_t* __restrict__ qlow) {
+    const int lane = threadIdx.x;
+    const int lrow = blockIdx.x * 4 + (lane >> 4), c = lane & 15;
+    if (lrow >= rows) return;
+    const RowInfo ri = row_info(g, row0, lrow);
+    const int h = g.ret_heads[ri.r];
+    const T* qp = q + ((size_t)ri.t * g.Hq + h) * D;
+    const T* wp = w_q + (size_t)ri.r * D * kIdx + c;
+    float qv[D], wv[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        qv[d] = ld(qp + d);
+        wv[d] = ld(wp + d * kIdx);
+    }
+    float acc = 0.0f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qv[d], wv[d], acc);
+    qlow[(size_t)lrow * kIdx + c] = f2bf(acc);
+}
+
+// ---------------------------------------------------------------------------
+// Scores.  grid (nchunk, rows), 256 threads.  Thread i of chunk c scores keys
 // c*4096 + 256*k + i, k = 0..15, i.e. slot i of the chunk's 16 pages: every
 // iteration reads one page's 8 KiB run of the head's indexer keys, coalesced.
+// STATS: also the chunk maximum and the chunk's mass histogram.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ q,
-                                                   const T* __restrict__ w_q,
-                                                   const bf16_t* __restrict__ k_low, int row0,
-                                                   SelWs ws, SelOut out, int scores_only) {
+template <int STATS>
+__global__ __launch_bounds__(256) void k_sel_score(Geo g, const bf16_t* __restrict__ k_low, int row0, SelWs ws,
+                                                   SelOut out) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (!scores_only) {
-        const int nthr = gridDim.x * 256;
-        for (int i = chunk * 256 + tid; i < kNB1; i += nthr) {
-            ws.hmass[(size_t)ri.lrow * kNB1 + i] = 0ull;
-            ws.hcnt[(size_t)ri.lrow * kNB1 + i] = 0u;
-        }
-        for (int i = chunk * 256 + tid; i < ws.nchunk; i += nthr)
-            ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + i] = 0u;
-        if (chunk == 0 && tid == 0) {
-            ws.cand_n[ri.lrow] = 0u;
-            if (ri.lrow == 0 && row0 == 0) {
-                *out.status = 0;
-                out.row_ptr[0] = 0;
-            }
-        }
+    if (STATS && chunk == 0 && tid == 0 && ri.lrow == 0 && row0 == 0) {
+        *out.status = 0;
+        out.row_ptr[0] = 0;
     }
     if (chunk >= ri.nch) return;
-
-    __shared__ float qs[kIdx];
     __shared__ float wmax[4];
-    __shared__ float qrow[128];
-    __shared__ float wq[128 * kIdx];
+    __shared__ unsigned long long hist[kCB];
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int jbase = chunk * kChunk;
 
-    // Issue the first group of indexer-key loads, then build q_low while they
-    // are in flight (the query row and W_q are staged through LDS so that the
-    // fixed-order chain runs on LDS operands).
-    uint4 buf[8];
     // Unconditional loads: page ids are uniform per 256-key step (clamped to the
     // row's last page) and slots past the row's end are read but never used.
+    uint4 buf[8];
     const int last_page = (ri.L - 1) >> 8;
     auto load_group = [&](int k0) {
 #pragma unroll
@@ -120,28 +135,17 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         }
     };
     load_group(0);
-    {
-        const int h = g.ret_heads[ri.r];
-        const T* qp = q + ((size_t)ri.t * g.Hq + h) * g.D;
-        const T* wp = w_q + (size_t)ri.r * g.D * kIdx;
-        for (int x = tid; x < g.D; x += 256) qrow[x] = ld(qp + x);
-        for (int x = tid; x < g.D * kIdx; x += 256) wq[x] = ld(wp + x);
-    }
-    __syncthreads();
-    if (tid < kIdx) {
-        float acc = 0.0f;
-        for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(qrow[d], wq[d * kIdx + tid], acc);
-        const bf16_t qb = f2bf(acc);
-        qs[tid] = bf2f(qb);
-        if (chunk == 0) ws.qlow[(size_t)ri.lrow * kIdx + tid] = qb;
-    }
-    __syncthreads();
     float qv[kIdx];
-#pragma unroll
-    for (int c = 0; c < kIdx; ++c) qv[c] = qs[c];
+    {
+        const uint4* qp = reinterpret_cast<const uint4*>(ws.qlow + (size_t)ri.lrow * kIdx);
+        unpack8(qp[0], qv);
+        unpack8(qp[1], qv + 8);
+    }
+    if (STATS && tid < kCB) hist[tid] = 0ull;
 
+    float dv[16];
     float mx = -INFINITY;
-#pragma unroll 1
+#pragma unroll
     for (int k0 = 0; k0 < 16; k0 += 4) {
         if (k0) load_group(k0);
 #pragma unroll
@@ -153,428 +157,484 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             float acc = 0.0f;
 #pragma unroll
             for (int c = 0; c < kIdx; ++c) acc = __builtin_fmaf(qv[c], kf[c], acc);
+            dv[k0 + u] = acc;
             if (j < ri.L) {
                 srow[j] = acc;
                 mx = fmaxf(mx, acc);
             }
         }
     }
-    if (scores_only) return;
+    if (!STATS) return;
     mx = wave_max(mx);
     if ((tid & 63) == 0) wmax[tid >> 6] = mx;
     __syncthreads();
-    if (tid == 0) {
-        float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-        ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk] = score_key(m);
+    const float mc = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (tid == 0) ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk] = score_key(mc);
+    const float s = g.idx_scale;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int j = jbase + k * 256 + tid;
+        if (j < ri.L) {
+            const WeightBin wb = weight_bin(dv[k], mc, s);
+            atomicAdd(&hist[wb.bin >> 4], wb.w);         // 64 level-1 bins per unit -> 4 per unit
+        }
+    }
+    __syncthreads();
+    // cumulative over bins (the mass of keys with x_c < (b + 1) / 4)
+    if (tid < 64) {
+        const unsigned long long a = hist[2 * tid], b = hist[2 * tid + 1];
+        unsigned long long incl = a + b;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long y = __shfl_up(incl, o);
+            if (tid >= o) incl += y;
+        }
+        unsigned long long* ch = ws.chist + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
+        ch[2 * tid] = incl - b;
+        ch[2 * tid + 1] = incl;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2.  Level-1 histogram of exact fixed-point mass.  grid (nhist, rows):
-// a workgroup covers kHistKeys keys (four score chunks), accumulates in LDS and
-// adds its non-empty bins to the row's histogram with device atomics (integer,
-// so the result does not depend on their order).
+// Resolve.  One 1024-thread workgroup per row.
 // ---------------------------------------------------------------------------
-constexpr int kHistKeys = 4 * kChunk;
+// Radix selection of the cut among keys with score key in [klo, khi] (the
+// candidate list cand[0..n) if n >= 0, else every key of the row): exact
+// fixed-point masses per 2048-bucket level, the mass ranked above khi is S_hi.
+// Returns the cut key Tkey and jT: a key is selected iff its score key >
+// Tkey, or == Tkey and its index <= jT.
+struct Cut {
+    uint32_t Tkey;
+    int32_t jT;
+};
 
-__device__ __forceinline__ float row_max(const SelWs& ws, int lrow, int nch, uint32_t* red) {
+__device__ Cut radix_cut(const unsigned long long* cand, int n, const float* srow, int L, uint32_t klo,
+                         uint32_t khi, unsigned long long S_hi, unsigned long long target, float m, float s,
+                         unsigned long long* hmb, uint32_t* hcb, unsigned long long* scan_sh, uint32_t* s_u,
+                         unsigned long long* s_S, int* s_i) {
     const int tid = threadIdx.x;
+    const bool from_list = n >= 0;
+    const int cnt = from_list ? n : L;
+    auto key_at = [&](int i, int* j) -> uint32_t {
+        if (from_list) {
+            *j = (int)~(uint32_t)cand[i];
+            return (uint32_t)(cand[i] >> 32);
+        }
+        *j = i;
+        return score_key(srow[i]);
+    };
+    for (int level = 0; level < 4; ++level) {
+        const uint32_t span = khi - klo;
+        const int bits = span ? 32 - __clz(span) : 0;
+        const int shift = bits > 11 ? bits - 11 : 0;
+        for (int i = tid; i < kNR; i += kRT) {
+            hmb[i] = 0ull;
+            hcb[i] = 0u;
+        }
+        __syncthreads();
+        for (int i = tid; i < cnt; i += kRT) {
+            int j;
+            const uint32_t key = key_at(i, &j);
+            if (key < klo || key > khi) continue;
+            const uint32_t bk = (khi - key) >> shift;         // bucket 0 holds the highest keys
+            atomicAdd(&hmb[bk], weight_bin(key_score(key), m, s).w);
+            atomicAdd(&hcb[bk], 1u);
+        }
+        __syncthreads();
+        // first bucket (highest keys first) whose cumulative mass reaches target
+        unsigned long long loc = hmb[2 * tid] + hmb[2 * tid + 1];
+        unsigned long long tot;
+        const unsigned long long ex = S_hi + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
+        if (tid == 0) *s_i = kNR;
+        __syncthreads();
+        if (ex + hmb[2 * tid] >= target && hcb[2 * tid]) atomicMin(s_i, 2 * tid);
+        else if (ex + loc >= target && hcb[2 * tid + 1]) atomicMin(s_i, 2 * tid + 1);
+        __syncthreads();
+        const int nb = (int)(span >> shift) + 1;
+        int bk = *s_i;
+        // the mass ranked above the bucket, from the thread that holds it
+        if (bk < kNR && (bk >> 1) == tid) {
+            *s_S = (bk & 1) ? ex + hmb[2 * tid] : ex;
+            *s_u = hcb[bk];
+        }
+        if (bk >= kNR && tid == 0) {
+            // the target is not reached (rounding): the last bucket
+            *s_S = S_hi + tot - hmb[nb - 1];
+            *s_u = hcb[nb - 1];
+        }
+        if (bk >= kNR) bk = nb - 1;
+        __syncthreads();
+        const unsigned long long S_b = *s_S;
+        const uint32_t n_b = *s_u;
+        const uint32_t nkhi = khi - ((uint32_t)bk << shift);
+        const uint32_t wdt = shift >= 32 ? 0xFFFFFFFFu : ((1u << shift) - 1u);
+        const uint32_t nklo = (nkhi - klo > wdt) ? nkhi - wdt : klo;
+        __syncthreads();
+        klo = nklo;
+        khi = nkhi;
+        S_hi = S_b;
+        if (klo == khi) {
+            // one score value: its tie group takes the lowest indices first
+            const unsigned long long wT = weight_bin(key_score(klo), m, s).w;
+            const unsigned long long need = target - S_hi;
+            const uint32_t ntie = (uint32_t)min((need + wT - 1ull) / wT, (unsigned long long)n_b);
+            Cut c;
+            c.Tkey = klo;
+            if (ntie >= n_b) {
+                // every tie is taken: jT = the largest tie index
+                if (tid == 0) *s_i = -1;
+                __syncthreads();
+                for (int i = tid; i < cnt; i += kRT) {
+                    int j;
+                    if (key_at(i, &j) == klo) atomicMax(s_i, j);
+                }
+                __syncthreads();
+                c.jT = *s_i;
+            } else {
+                // the ntie-th smallest tie index, by an ordered scan of the row
+                if (tid == 0) {
+                    *s_u = 0u;
+                    *s_i = -1;
+                }
+                __syncthreads();
+                for (int j0 = 0; j0 < L; j0 += kRT) {
+                    const int j = j0 + tid;
+                    const bool is_tie = j < L && score_key(srow[j]) == klo;
+                    const uint32_t before_blk = *s_u;
+                    unsigned long long t2;
+                    const unsigned long long rank = block_excl_scan_u64<kRT>(is_tie ? 1ull : 0ull, &t2, scan_sh);
+                    if (is_tie && before_blk + rank + 1ull == ntie) *s_i = j;
+                    __syncthreads();
+                    if (tid == 0) *s_u = before_blk + (uint32_t)t2;
+                    __syncthreads();
+                    if (*s_i >= 0) break;
+                }
+                c.jT = *s_i;
+            }
+            __syncthreads();
+            return c;
+        }
+    }
+    // unreachable for 32-bit keys (each level fixes at least 11 bits)
+    Cut c;
+    c.Tkey = khi;
+    c.jT = L;
+    return c;
+}
+
+// Ordered visit of the row's keys that satisfy pred(d): the row is split into
+// kRT / 64 contiguous wave segments, each lane reads four consecutive scores
+// per step (four steps in flight), and emit(pos, j, d) receives each hit with
+// its rank among the segment's hits (from base[w]).  Returns the lane's hit
+// count accumulated over the wave's segment (every lane holds the wave total).
+template <typename Pred, typename Emit>
+__device__ uint32_t scan_segment(const float* __restrict__ srow, int L, uint32_t base, Pred pred, Emit emit) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    constexpr int NW = kRT / 64;
+    const int seg = ((L + NW * 256 - 1) / (NW * 256)) * 256;
+    const int j_beg = w * seg, j_end = min(L, j_beg + seg);
+    uint32_t run = base;
+    for (int j0 = j_beg; j0 < j_end; j0 += 4 * 256) {
+        float4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * 256 + 4 * lane;
+            v[u] = j < j_end ? *reinterpret_cast<const float4*>(srow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u * 256 + 4 * lane;
+            const float dv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            bool hit[4];
+            uint32_t c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hit[e] = j + e < j_end && pred(dv[e]);
+                c += hit[e] ? 1u : 0u;
+            }
+            uint32_t incl = c;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            uint32_t pos = run + incl - c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (hit[e]) emit(pos++, j + e, dv[e]);
+            run += __shfl(incl, 63);
+        }
+    }
+    return run - base;
+}
+
+// Plan.  One 1024-thread workgroup per row: row maximum, total mass, target,
+// and the threshold of U from the chunk histograms.
+__global__ __launch_bounds__(kRT) void k_sel_plan(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
+    const int tid = threadIdx.x;
+    const RowInfo ri = row_info(g, row0, blockIdx.x);
+    __shared__ double part[4][kGB];
+    __shared__ double fch[kMaxChunks], dch[kMaxChunks];
+    __shared__ double dred[kRT / 64];
+    __shared__ uint32_t ured[kRT / 64];
+    __shared__ int s_i;
+    const float s = g.idx_scale;
+    const int nch = ri.nch;
+    const unsigned long long* chist = ws.chist + (size_t)ri.lrow * ws.nchunk * kCB;
+    RowState st;
+    st.L = ri.L;
+    st.Tkey = 0u;
+    st.jT = ri.L;
+    st.count = 0;
+
+    // ---- row maximum and the per-chunk rescaling to it
     uint32_t mk = 0u;
-    for (int c = tid; c < nch; c += 256) {
-        const uint32_t v = ws.cmax[(size_t)lrow * ws.nchunk + c];
+    for (int c = tid; c < nch; c += kRT) {
+        const uint32_t v = ws.cmax[(size_t)ri.lrow * ws.nchunk + c];
         mk = v > mk ? v : mk;
     }
     mk = wave_max_u32(mk);
-    if ((tid & 63) == 0) red[tid >> 6] = mk;
+    if ((tid & 63) == 0) ured[tid >> 6] = mk;
     __syncthreads();
-    mk = red[0];
-    for (int w = 1; w < 4; ++w) mk = red[w] > mk ? red[w] : mk;
+    mk = 0u;
+    for (int w = 0; w < kRT / 64; ++w) mk = ured[w] > mk ? ured[w] : mk;
+    const float m = key_score(mk);
+    st.m = m;
+    for (int c = tid; c < nch; c += kRT) {
+        const double dc = (double)s * ((double)m - (double)key_score(ws.cmax[(size_t)ri.lrow * ws.nchunk + c]));
+        dch[c] = dc;
+        fch[c] = exp(-dc);
+    }
     __syncthreads();
-    return key_score(mk);
+    // ---- total mass and the lower bound LB(k) of the mass of keys with x < k / 4:
+    // chunk bin b counts once (b + 1) / 4 + dc <= k / 4, i.e. b <= k - 1 - 4 dc
+    {
+        const int k = tid & (kGB - 1), cg = tid >> 8;
+        double acc = 0.0, z = 0.0;
+        for (int c = cg; c < nch; c += kRT / kGB) {
+            const double bmax = floor((double)(k - 1) - (double)kCBPerUnit * dch[c]);
+            if (bmax >= 0.0) acc += fch[c] * (double)chist[(size_t)c * kCB + (int)fmin(bmax, (double)(kCB - 1))];
+            if (k == 0) z += fch[c] * (double)chist[(size_t)c * kCB + kCB - 1];
+        }
+        part[cg][k] = acc;
+        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+        if ((tid & 63) == 0) dred[tid >> 6] = z;
+    }
+    __syncthreads();
+    double Z = 0.0;
+    for (int w = 0; w < kRT / 64; ++w) Z += dred[w];
+    const float p = top_p[ri.b];
+    if (!(p < 1.0f)) {
+        if (tid == 0) {
+            st.mode = 0;
+            st.count = ri.L;
+            st.target = 0ull;
+            st.d_thr = -INFINITY;
+            ws.st[ri.lrow] = st;
+            ws.row_n[ri.lrow] = 0u;
+        }
+        return;
+    }
+    unsigned long long target = (unsigned long long)ceil((double)p * Z);
+    if ((double)target > Z) target = (unsigned long long)Z;
+    if (target < 1ull) target = 1ull;
+    st.target = target;
+    // smallest k whose bound reaches the target with room for the per-key
+    // rounding of the fixed-point weights (one unit per key)
+    if (tid == 0) s_i = kGB;
+    __syncthreads();
+    if (tid < kGB) {
+        const double lb = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+        const double need = (double)target * (1.0 + 0x1.0p-40) + (double)ri.L + 1.0;
+        if (lb >= need) atomicMin(&s_i, tid);
+    }
+    __syncthreads();
+    const int ks = s_i;
+    // U = {d >= d_thr}; the margin covers the float rounding of the chunk bins
+    float d_thr = -INFINITY;
+    if (ks < kGB) {
+        const double X = (double)ks / (double)kCBPerUnit;
+        const double xm = X + 0x1.0p-18 * (X + 1.0);
+        d_thr = __double2float_rd((double)m - xm / (double)s - 0x1.0p-20 * fabs((double)m));
+    }
+    if (tid == 0) {
+        st.mode = 1;
+        st.d_thr = d_thr;
+        ws.st[ri.lrow] = st;
+        ws.row_n[ri.lrow] = 0u;
+    }
 }
 
-__global__ __launch_bounds__(256) void k_sel_hist(Geo g, int row0, SelWs ws) {
+// Gather.  grid (nchunk, rows), 256 threads: the chunk's keys of U in index
+// order, as one block of the row's candidate list (blocks are placed by one
+// atomic per chunk; the resolve pass puts them back in chunk order).
+__global__ __launch_bounds__(256) void k_sel_gather(Geo g, int row0, SelWs ws) {
     const int tid = threadIdx.x;
+    const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
-    const int jbase = blockIdx.x * kHistKeys;
-    if (jbase >= ri.L) return;
-    __shared__ unsigned long long hm[kNB1];
-    __shared__ uint32_t hc[kNB1];
-    __shared__ uint32_t red[4];
-    for (int i = tid; i < kNB1; i += 256) {
-        hm[i] = 0ull;
-        hc[i] = 0u;
-    }
-    const float m = row_max(ws, ri.lrow, ri.nch, red);
-    const float s = g.idx_scale;
+    if (chunk >= ri.nch) return;
+    const RowState st = ws.st[ri.lrow];
+    if (st.mode == 0) return;
+    __shared__ unsigned long long scan_sh[256 / 64 + 1];
+    __shared__ uint32_t s_base;
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    for (int k0 = 0; k0 < kHistKeys / 256; k0 += 16) {
-        float dv[16];
+    const int j0 = chunk * kChunk + 16 * tid;             // 16 consecutive keys per thread
+    float dv[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + (k0 + k) * 256 + tid, ri.L - 1)];
+    for (int u = 0; u < 4; ++u) {
+        const float4 v = *reinterpret_cast<const float4*>(srow + j0 + 4 * u);
+        dv[4 * u] = v.x;
+        dv[4 * u + 1] = v.y;
+        dv[4 * u + 2] = v.z;
+        dv[4 * u + 3] = v.w;
+    }
+    uint32_t c = 0;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int j = jbase + (k0 + k) * 256 + tid;
-            if (j < ri.L) {
-                const WeightBin wb = weight_bin(dv[k], m, s);
-                atomicAdd(&hm[wb.bin], wb.w);
-                atomicAdd(&hc[wb.bin], 1u);
-            }
-        }
+    for (int e = 0; e < 16; ++e) c += (j0 + e < ri.L && dv[e] >= st.d_thr) ? 1u : 0u;
+    unsigned long long tot;
+    uint32_t o = (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
+    if (tid == 0) {
+        const uint32_t b = tot ? atomicAdd(&ws.row_n[ri.lrow], (uint32_t)tot) : 0u;
+        s_base = b;
+        ws.chunk_base[(size_t)ri.lrow * ws.nchunk + chunk] = b;
+        ws.chunk_n[(size_t)ri.lrow * ws.nchunk + chunk] = (uint32_t)tot;
     }
     __syncthreads();
-    for (int i = tid; i < kNB1; i += 256) {
-        if (hc[i]) {
-            atomicAdd(&ws.hmass[(size_t)ri.lrow * kNB1 + i], hm[i]);
-            atomicAdd(&ws.hcnt[(size_t)ri.lrow * kNB1 + i], hc[i]);
-        }
+    const uint32_t b = s_base;
+    if (b + tot > (unsigned long long)kCand) return;      // the list overflows: the row takes the long path
+    unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand + b;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int j = j0 + e;
+        if (j < ri.L && dv[e] >= st.d_thr)
+            ub[o++] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)j);
     }
 }
 
-// ---------------------------------------------------------------------------
-// Pass 2b.  One workgroup per row: total mass, target ceil(p Z) and the bin b1
-// where the cumulative mass (highest scores first) reaches it.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_sel_cut(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
+// Resolve.  One 1024-thread workgroup per row: U back in index order, the
+// radix cut, and the selected indices in order (or, for a list that did not
+// fit, the cut over the row's scores and per-chunk counts).
+__global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) {
     const int tid = threadIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.x);
-    __shared__ uint32_t red[4], red2[4];
-    __shared__ unsigned long long scan_sh[5];
-    __shared__ int s_b1;
-    const float m = row_max(ws, ri.lrow, ri.nch, red);
-    unsigned long long lm[8];
-    uint32_t lc[8];
-    unsigned long long msum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        lm[i] = ws.hmass[(size_t)ri.lrow * kNB1 + tid * 8 + i];
-        lc[i] = ws.hcnt[(size_t)ri.lrow * kNB1 + tid * 8 + i];
-        msum += lm[i];
-    }
-    unsigned long long Z;
-    const unsigned long long before = block_excl_scan_u64<256>(msum, &Z, scan_sh);
-    const float p = top_p[ri.b];
-    unsigned long long target = Z;
-    const int keep_all = !(p < 1.0f);
-    if (!keep_all) {
-        const double pz = ceil((double)p * (double)Z);
-        target = (unsigned long long)pz;
-        if (target > Z) target = Z;
-        if (target < 1ull) target = 1ull;
-    }
-    if (tid == 0) s_b1 = kNB1;
-    __syncthreads();
-    if (!keep_all) {
-        unsigned long long run = before;
-        for (int i = 0; i < 8; ++i) {
-            run += lm[i];
-            if (run >= target) {
-                atomicMin(&s_b1, tid * 8 + i);
-                break;
+    RowState st = ws.st[ri.lrow];
+    if (st.mode == 0) return;
+    __shared__ unsigned long long cand[kCand];
+    __shared__ unsigned long long scan_sh[kRT / 64 + 1];
+    __shared__ unsigned long long hmb[kNR];
+    __shared__ uint32_t hcb[kNR];
+    __shared__ uint32_t ccount[kMaxChunks];
+    __shared__ uint32_t cb_sorted[kMaxChunks], cb_chunk[kMaxChunks], cpre[kMaxChunks];
+    __shared__ int s_i;
+    __shared__ uint32_t s_n;
+    __shared__ unsigned long long s_S;
+    const float s = g.idx_scale;
+    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
+    const int nch = ri.nch;
+    const float m = st.m, d_thr = st.d_thr;
+    const unsigned long long target = st.target;
+    const int lane = tid & 63;
+    const int nU = (int)ws.row_n[ri.lrow];
+    if (nU <= kCand) {
+        // blocks of the list in chunk order: chunk c's block starts at cpre[c]
+        // in the ordered list and at chunk_base[c] in the gathered one
+        uint32_t* cbase = hcb;                             // LDS copies (the radix buffers are free here)
+        uint32_t* cn = hcb + kMaxChunks;
+        if (tid < nch) {
+            cbase[tid] = ws.chunk_base[(size_t)ri.lrow * ws.nchunk + tid];
+            cn[tid] = ws.chunk_n[(size_t)ri.lrow * ws.nchunk + tid];
+        }
+        __syncthreads();
+        unsigned long long n_c = tid < nch ? cn[tid] : 0ull;
+        unsigned long long tot;
+        const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
+        if (tid < nch) cpre[tid] = (uint32_t)ex;
+        // chunks with entries, ordered by their gathered position
+        if (tid < nch) {
+            const uint32_t bt = cbase[tid];
+            uint32_t rank = 0;
+            if (n_c) {
+                for (int c = 0; c < nch; ++c)
+                    if (cn[c] && (cbase[c] < bt || (cbase[c] == bt && c < tid))) ++rank;
+                cb_sorted[rank] = bt;
+                cb_chunk[rank] = (uint32_t)tid;
             }
         }
+        if (tid == 0) s_i = 0;
+        __syncthreads();
+        if (tid < nch && n_c) atomicAdd(&s_i, 1);
+        __syncthreads();
+        const int nblk = s_i;
+        const unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand;
+        for (int i = tid; i < nU; i += kRT) {
+            // the block holding gathered position i
+            int lo = 0, hi = nblk - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (cb_sorted[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
+            }
+            const uint32_t c = cb_chunk[lo];
+            cand[cpre[c] + ((uint32_t)i - cb_sorted[lo])] = ub[i];
+        }
+        __syncthreads();
+    }
+    for (int c = tid; c < kMaxChunks; c += kRT) ccount[c] = 0u;
+    const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
+    const Cut cut = radix_cut(cand, nU <= kCand ? nU : -1, srow, ri.L, klo, khi, 0ull, target, m, s, hmb, hcb,
+                              scan_sh, &s_n, &s_S, &s_i);
+
+    const auto selected = [&](uint32_t key, int j) { return key > cut.Tkey || (key == cut.Tkey && j <= cut.jT); };
+    if (nU <= kCand) {
+        // ---- U is in index order: its selected entries, in order, into the row's list
+        constexpr int per = kCand / kRT;
+        uint32_t c = 0;
+#pragma unroll
+        for (int x = 0; x < per; ++x) {
+            const int i = tid * per + x;
+            if (i < nU && selected((uint32_t)(cand[i] >> 32), (int)~(uint32_t)cand[i])) ++c;
+        }
+        unsigned long long tot;
+        uint32_t o = (uint32_t)block_excl_scan_u64<kRT>(c, &tot, scan_sh);
+        uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
+#pragma unroll
+        for (int x = 0; x < per; ++x) {
+            const int i = tid * per + x;
+            if (i < nU) {
+                const int j = (int)~(uint32_t)cand[i];
+                if (selected((uint32_t)(cand[i] >> 32), j)) sl[o++] = (uint32_t)j;
+            }
+        }
+        if (tid == 0) {
+            st.mode = 1;
+            st.Tkey = cut.Tkey;
+            st.jT = cut.jT;
+            st.count = (int32_t)tot;
+            ws.st[ri.lrow] = st;
+        }
+        return;
+    }
+    // ---- U too large for LDS: selected keys per chunk for the ordered compaction
+    for (int j = tid; j < ri.L; j += kRT) {
+        const bool sel = selected(score_key(srow[j]), j);
+        const unsigned long long b = __ballot(sel);
+        if (lane == 0 && b) atomicAdd(&ccount[j / kChunk], (uint32_t)__popcll(b));
     }
     __syncthreads();
-    const int b1 = s_b1;
-    uint32_t ca = 0;
-    unsigned long long sa = 0;
-    for (int i = 0; i < 8; ++i) {
-        if (tid * 8 + i < b1) {
-            ca += lc[i];
-            sa += lm[i];
-        }
-    }
-    const uint32_t cnt_above = block_sum_u32<256>(ca, red2);
-    unsigned long long S_above;
-    (void)block_excl_scan_u64<256>(sa, &S_above, scan_sh);
+    unsigned long long n_c = tid < nch ? ccount[tid] : 0ull;
+    unsigned long long tot;
+    const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
+    if (tid < nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)ex;
     if (tid == 0) {
-        RowState st;
-        st.m = m;
-        st.b1 = b1;
-        st.Z = Z;
-        st.target = target;
-        st.S_above = S_above;
-        st.cnt_above = cnt_above;
-        st.cnt_b1 = b1 < kNB1 ? ws.hcnt[(size_t)ri.lrow * kNB1 + b1] : 0u;
-        st.Tkey = 0u;
-        st.jT = -1;
-        st.L = ri.L;
-        st.count = keep_all ? ri.L : 0;
+        st.mode = 2;
+        st.Tkey = cut.Tkey;
+        st.jT = cut.jT;
+        st.count = (int32_t)tot;
         ws.st[ri.lrow] = st;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3.  Keys above the cut bin are counted per chunk; keys of the cut bin
-// are gathered as (score key << 32 | ~index) for the exact ranking.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_sel_refine(Geo g, int row0, SelWs ws) {
-    const int tid = threadIdx.x;
-    const int chunk = blockIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (chunk >= ri.nch) return;
-    __shared__ uint32_t red[4];
-    const RowState st = ws.st[ri.lrow];
-    const float s = g.idx_scale;
-    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int jbase = chunk * kChunk;
-    uint32_t above = 0;
-    if (st.b1 >= kNB1) {
-        above = (uint32_t)min(kChunk, ri.L - jbase);
-    } else {
-        const bool gather = st.cnt_b1 <= (uint32_t)kCand;
-        float dv[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + k * 256 + tid, ri.L - 1)];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int j = jbase + k * 256 + tid;
-            if (j < ri.L) {
-                const float d = dv[k];
-                const int bn = bin_of(d, st.m, s);
-                if (bn < st.b1) {
-                    ++above;
-                } else if (bn == st.b1 && gather) {
-                    const uint32_t slot = atomicAdd(&ws.cand_n[ri.lrow], 1u);
-                    if (slot < (uint32_t)kCand)
-                        ws.cand[(size_t)ri.lrow * kCand + slot] =
-                            ((unsigned long long)score_key(d) << 32) | (unsigned long long)(~(uint32_t)j);
-                }
-            }
-        }
-    }
-    const uint32_t tot = block_sum_u32<256>(above, red);
-    if (tid == 0) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk] = tot;
-}
-
-// ---------------------------------------------------------------------------
-// Pass 4.  One 1024-thread workgroup per row: exact ranking inside bin b1.
-// ---------------------------------------------------------------------------
-constexpr int kRT = 1024;
-
-__device__ void bitonic_desc(unsigned long long* a, int n) {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += kRT) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const unsigned long long x = a[i], y = a[ixj];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (x < y) : (x > y)) {
-                        a[i] = y;
-                        a[ixj] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// Given candidates cand[0..n) sorted by rank, the mass S0 ranked before them and
-// the target, find the first candidate whose cumulative mass reaches target.
-__device__ int first_reaching(const unsigned long long* cand, int n, float m, float s,
-                              unsigned long long S0, unsigned long long target,
-                              unsigned long long* scan_sh, int* s_idx) {
-    constexpr int per = kCand / kRT;   // 8 candidates per thread
-    unsigned long long wv[per];
-    unsigned long long loc = 0;
-    for (int i = 0; i < per; ++i) {
-        const int c = threadIdx.x * per + i;
-        wv[i] = 0;
-        if (c < n) wv[i] = weight_bin(key_score((uint32_t)(cand[c] >> 32)), m, s).w;
-        loc += wv[i];
-    }
-    unsigned long long tot;
-    unsigned long long run = S0 + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
-    if (threadIdx.x == 0) *s_idx = n - 1;   // mass of the bin reaches target by construction
-    __syncthreads();
-    for (int i = 0; i < per; ++i) {
-        const int c = threadIdx.x * per + i;
-        run += wv[i];
-        if (c < n && run >= target) {
-            atomicMin(s_idx, c);
-            break;
-        }
-    }
-    __syncthreads();
-    return *s_idx;
-}
-
-__global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws, SelOut out,
-                                                     int total_rows) {
-    const int tid = threadIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.x);
-    __shared__ unsigned long long cand[kCand];
-    __shared__ unsigned long long scan_sh[kRT / 64 + 1];
-    __shared__ uint32_t ccount[1024];          // per-chunk selected keys of bin b1
-    __shared__ unsigned long long hmb[kNB1];
-    __shared__ uint32_t hcb[kNB1];
-    __shared__ int s_idx;
-    __shared__ uint32_t s_klo, s_khi, s_n;
-    __shared__ unsigned long long s_S;
-    RowState st = ws.st[ri.lrow];
-    const float s = g.idx_scale;
-    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int nch = ri.nch;
-
-    for (int c = tid; c < 1024; c += kRT) ccount[c] = 0u;
-    __syncthreads();
-
-    if (st.b1 < kNB1) {
-        uint32_t Tkey = 0u;
-        int32_t jT = -1;
-        bool have_cands = false;
-        bool whole_bin = false;            // the candidates are every key of bin b1
-        int n = 0, ic = -1;
-        unsigned long long S0 = st.S_above;
-        if (st.cnt_b1 <= (uint32_t)kCand) {
-            n = (int)st.cnt_b1;
-            for (int i = tid; i < n; i += kRT) cand[i] = ws.cand[(size_t)ri.lrow * kCand + i];
-            have_cands = true;
-            whole_bin = true;
-        } else {
-            // Many keys share bin b1: narrow the score-key range with 2048-bucket
-            // histograms over the row until it fits the sort or is one tie group.
-            uint32_t klo = 0u, khi = 0xFFFFFFFFu;
-            unsigned long long S_hi = st.S_above;
-            for (int iter = 0; iter < 4; ++iter) {
-                const uint32_t span = khi - klo;
-                const int bits = span ? 32 - __clz(span) : 0;
-                const int shift = bits > 11 ? bits - 11 : 0;
-                for (int i = tid; i < kNB1; i += kRT) {
-                    hmb[i] = 0ull;
-                    hcb[i] = 0u;
-                }
-                __syncthreads();
-                for (int j = tid; j < ri.L; j += kRT) {
-                    const float d = srow[j];
-                    if (bin_of(d, st.m, s) != st.b1) continue;
-                    const uint32_t key = score_key(d);
-                    if (key < klo || key > khi) continue;
-                    const uint32_t bk = (key - klo) >> shift;
-                    atomicAdd(&hmb[bk], weight_bin(d, st.m, s).w);
-                    atomicAdd(&hcb[bk], 1u);
-                }
-                __syncthreads();
-                if (tid == 0) {
-                    // buckets rank from the highest key down
-                    const uint32_t nb = (span >> shift) + 1u;
-                    unsigned long long run = S_hi;
-                    uint32_t kb = 0;
-                    for (int32_t bk = (int32_t)nb - 1; bk >= 0; --bk) {
-                        if (run + hmb[bk] >= st.target && hcb[bk]) {
-                            kb = (uint32_t)bk;
-                            break;
-                        }
-                        run += hmb[bk];
-                    }
-                    s_S = run;
-                    s_klo = klo + (kb << shift);
-                    const uint32_t top = s_klo + ((1u << shift) - 1u);
-                    s_khi = (shift == 32 || top < s_klo || top > khi) ? khi : top;
-                    s_n = hcb[kb];
-                }
-                __syncthreads();
-                klo = s_klo;
-                khi = s_khi;
-                S_hi = s_S;
-                if (s_n <= (uint32_t)kCand) {
-                    // gather the bucket's keys and rank them by sorting
-                    if (tid == 0) s_n = 0u;
-                    __syncthreads();
-                    for (int j = tid; j < ri.L; j += kRT) {
-                        const float d = srow[j];
-                        if (bin_of(d, st.m, s) != st.b1) continue;
-                        const uint32_t key = score_key(d);
-                        if (key < klo || key > khi) continue;
-                        const uint32_t slot = atomicAdd(&s_n, 1u);
-                        if (slot < (uint32_t)kCand)
-                            cand[slot] = ((unsigned long long)key << 32) | (unsigned long long)(~(uint32_t)j);
-                    }
-                    __syncthreads();
-                    n = min((int)s_n, kCand);
-                    S0 = S_hi;
-                    have_cands = true;
-                    break;
-                }
-                if (klo == khi) {
-                    // one tie group: take its lowest-index members until the mass is reached
-                    const unsigned long long wT = weight_bin(key_score(klo), st.m, s).w;
-                    const unsigned long long need = st.target - S_hi;
-                    const unsigned long long ntie = (need + wT - 1ull) / wT;
-                    if (tid == 0) s_n = 0u;
-                    if (tid == 0) s_idx = -1;
-                    __syncthreads();
-                    // ordered scan in index order, kRT keys at a time
-                    for (int j0 = 0; j0 < ri.L; j0 += kRT) {
-                        const int j = j0 + tid;
-                        const bool is_tie = j < ri.L && score_key(srow[j]) == klo &&
-                                            bin_of(srow[j], st.m, s) == st.b1;
-                        const uint32_t before_blk = s_n;
-                        unsigned long long tot;
-                        const unsigned long long rank =
-                            block_excl_scan_u64<kRT>(is_tie ? 1ull : 0ull, &tot, scan_sh);
-                        if (is_tie && before_blk + rank + 1ull == ntie) s_idx = j;
-                        __syncthreads();
-                        if (tid == 0) s_n = before_blk + (uint32_t)tot;
-                        __syncthreads();
-                        if (s_idx >= 0) break;
-                    }
-                    Tkey = klo;
-                    jT = s_idx;
-                    break;
-                }
-            }
-        }
-        if (have_cands) {
-            int np2 = 1;
-            while (np2 < n) np2 <<= 1;
-            for (int i = n + tid; i < np2; i += kRT) cand[i] = 0ull;
-            __syncthreads();
-            bitonic_desc(cand, np2);
-            ic = first_reaching(cand, n, st.m, s, S0, st.target, scan_sh, &s_idx);
-            Tkey = (uint32_t)(cand[ic] >> 32);
-            jT = (int32_t)(~(uint32_t)cand[ic]);
-        }
-        // selected keys of bin b1 per chunk
-        if (whole_bin) {
-            for (int i = tid; i <= ic; i += kRT)
-                atomicAdd(&ccount[(int)(~(uint32_t)cand[i]) / kChunk], 1u);
-        } else {
-            for (int j = tid; j < ri.L; j += kRT) {
-                const float d = srow[j];
-                if (bin_of(d, st.m, s) != st.b1) continue;
-                const uint32_t key = score_key(d);
-                if (key > Tkey || (key == Tkey && j <= jT)) atomicAdd(&ccount[j / kChunk], 1u);
-            }
-        }
-        st.Tkey = Tkey;
-        st.jT = jT;
-    }
-    __syncthreads();
-    // per-chunk output offsets of this row (nch <= 1024 chunks)
-    {
-        unsigned long long n_c = 0;
-        if (tid < nch) {
-            if (st.b1 >= kNB1)
-                n_c = (unsigned long long)min(kChunk, ri.L - tid * kChunk);
-            else
-                n_c = ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] + ccount[tid];
-        }
-        unsigned long long tot;
-        const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
-        if (tid < nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)ex;
-        if (tid == 0) {
-            st.count = (int32_t)tot;
-            ws.st[ri.lrow] = st;
-        }
-    }
-    (void)total_rows;
-}
-
-// ---------------------------------------------------------------------------
-// Pass 4b.  CSR row pointers of the group's rows and the capacity check.
+// CSR row pointers of the group's rows and the capacity check.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut out) {
     const int tid = threadIdx.x;
@@ -592,7 +652,9 @@ __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut o
 }
 
 // ---------------------------------------------------------------------------
-// Pass 5.  Ordered compaction of the selected indices of each chunk.
+// Emit.  grid (nchunk, rows), 256 threads: the part of a row's output that
+// belongs to one 4096-key chunk (a slice of the sorted list, or the ordered
+// compaction of the chunk's selected keys).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, SelOut out) {
     const int tid = threadIdx.x;
@@ -600,12 +662,21 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
     const RowInfo ri = row_info(g, row0, blockIdx.y);
     if (chunk >= ri.nch) return;
     if (*out.status != 0) return;
-    __shared__ uint32_t wcnt[4];
     const RowState st = ws.st[ri.lrow];
-    const float s = g.idx_scale;
-    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    int64_t base = out.row_ptr[ri.row] + ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
+    const int64_t rbase = out.row_ptr[ri.row];
     const int jbase = chunk * kChunk;
+    if (st.mode == 0) {
+        for (int k = tid; k < kChunk && jbase + k < ri.L; k += 256) out.idx[rbase + jbase + k] = jbase + k;
+        return;
+    }
+    if (st.mode == 1) {
+        const uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
+        for (int k = tid; k < kChunk && jbase + k < st.count; k += 256) out.idx[rbase + jbase + k] = (int32_t)sl[jbase + k];
+        return;
+    }
+    __shared__ uint32_t wcnt[4];
+    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
+    int64_t base = rbase + ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
     const int lane = tid & 63, wid = tid >> 6;
     float dv[16];
 #pragma unroll
@@ -615,18 +686,8 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
         const int j = jbase + k * 256 + tid;
         bool sel = false;
         if (j < ri.L) {
-            if (st.b1 >= kNB1) {
-                sel = true;
-            } else {
-                const float d = dv[k];
-                const int bn = bin_of(d, st.m, s);
-                if (bn < st.b1) {
-                    sel = true;
-                } else if (bn == st.b1) {
-                    const uint32_t key = score_key(d);
-                    sel = key > st.Tkey || (key == st.Tkey && j <= st.jT);
-                }
-            }
+            const uint32_t key = score_key(dv[k]);
+            sel = key > st.Tkey || (key == st.Tkey && j <= st.jT);
         }
         const unsigned long long bal = __ballot(sel);
         const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
@@ -647,19 +708,29 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
                          int total_rows, int dtype, int scores_only, hipStream_t s) {
-    const dim3 grid(ws.nchunk, ws.rows);
-    if (dtype == 0)
-        hipLaunchKernelGGL(k_sel_score<float>, grid, dim3(256), 0, s, g, (const float*)q,
-                           (const float*)w_q, k_low, row0, ws, out, scores_only);
+    (void)total_rows;
+    const dim3 gq((ws.rows + 3) / 4);
+    if (dtype == 0 && g.D == 64)
+        hipLaunchKernelGGL((k_sel_qlow<float, 64>), gq, dim3(64), 0, s, g, (const float*)q, (const float*)w_q, row0,
+                           ws.rows, ws.qlow);
+    else if (dtype == 0)
+        hipLaunchKernelGGL((k_sel_qlow<float, 128>), gq, dim3(64), 0, s, g, (const float*)q, (const float*)w_q, row0,
+                           ws.rows, ws.qlow);
+    else if (g.D == 64)
+        hipLaunchKernelGGL((k_sel_qlow<bf16_t, 64>), gq, dim3(64), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
+                           row0, ws.rows, ws.qlow);
     else
-        hipLaunchKernelGGL(k_sel_score<bf16_t>, grid, dim3(256), 0, s, g, (const bf16_t*)q,
-                           (const bf16_t*)w_q, k_low, row0, ws, out, scores_only);
-    if (scores_only) return hipGetLastError();
-    const int nhist = (ws.nchunk + 3) / 4;
-    hipLaunchKernelGGL(k_sel_hist, dim3(nhist, ws.rows), dim3(256), 0, s, g, row0, ws);
-    hipLaunchKernelGGL(k_sel_cut, dim3(ws.rows), dim3(256), 0, s, g, top_p, row0, ws);
-    hipLaunchKernelGGL(k_sel_refine, grid, dim3(256), 0, s, g, row0, ws);
-    hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws, out, total_rows);
+        hipLaunchKernelGGL((k_sel_qlow<bf16_t, 128>), gq, dim3(64), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
+                           row0, ws.rows, ws.qlow);
+    const dim3 grid(ws.nchunk, ws.rows);
+    if (scores_only) {
+        hipLaunchKernelGGL(k_sel_score<0>, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, row0, ws, out);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_sel_score<1>, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, row0, ws, out);
+    hipLaunchKernelGGL(k_sel_plan, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws);
+    hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, row0, ws);
+    hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
     hipLaunchKernelGGL(k_sel_rowptr, dim3(1), dim3(kRT), 0, s, row0, ws, out);
     hipLaunchKernelGGL(k_sel_emit, grid, dim3(256), 0, s, g, row0, ws, out);
     return hipGetLastError();
