@@ -62,6 +62,51 @@ def traffic_from_counters():
     return c.get("hbm_bytes_per_launch")
 
 
+def summarize(kind: str, paths, command: str, out: str):
+    """Write a short profile summary under profiles/ from rocprofv3 CSV output.
+
+    kind "stats":    paths = [kernel_stats.csv]; a table of per-kernel calls
+                     and durations.
+    kind "counters": paths = [FETCH_SIZE counter_collection.csv, WRITE_SIZE
+                     counter_collection.csv]; the score kernel's HBM bytes per
+                     launch, each counter scaled by what it reads for the
+                     bench's 1 GiB calibration copy (the last dispatch)."""
+    import csv
+    import re
+
+    if kind == "stats":
+        rows = list(csv.DictReader(open(paths[0])))
+        lines = ["# rocprofv3 kernel statistics", "", "Command (from the repository root):", "",
+                 "    " + command, "", "| kernel | calls | avg us | min us | max us | total % |",
+                 "|---|---|---|---|---|---|"]
+        for r in rows[:25]:
+            name = r["Name"].replace("rtp::(anonymous namespace)::", "").replace("(anonymous namespace)::", "")
+            name = re.sub(r"\(.*", "", name)
+            lines.append("| %s | %s | %.2f | %.2f | %.2f | %.1f |" % (
+                name[:70], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+        open(out, "w").write("\n".join(lines) + "\n")
+        return
+    res = {}
+    for cname, path in zip(("FETCH_SIZE", "WRITE_SIZE"), paths):
+        rows = list(csv.DictReader(open(path)))
+        calib = float(rows[-1]["Counter_Value"])           # KiB for 1 GiB moved
+        scale = (1 << 20) / calib
+        ks = [float(r["Counter_Value"]) for r in rows if re.search(r"k_sel_score<unsigned short, 0>", r["Kernel_Name"])]
+        res[cname] = {"calibration_kib_per_gib": calib, "scale": scale,
+                      "score_kernel_kib_raw": sum(ks) / len(ks), "dispatches": len(ks),
+                      "score_kernel_bytes": sum(ks) / len(ks) * scale * 1024}
+    summary = {
+        "kernel": "k_sel_score<bf16, scores only> (decode bf16 B=8 L=131072, 6 retrieval heads)",
+        "command": command,
+        "counters": res,
+        "hbm_bytes_per_launch": int(res["FETCH_SIZE"]["score_kernel_bytes"] + res["WRITE_SIZE"]["score_kernel_bytes"]),
+        "algorithmic_read_bytes": 8 * 131072 * 6 * 32,
+        "source_sha256_16": source_hash(SCORE_SRC),
+    }
+    json.dump(summary, open(out, "w"), indent=1)
+
+
 def cpu_baseline(w, n_seq: int, threads: int):
     """Time the oracle (as it stands) on the first n_seq sequences of one
     decode step; the indexer keys of the context are computed untimed."""
@@ -239,9 +284,15 @@ def main():
     ap.add_argument("--graph", action="store_true", help="time HIP graph replays instead of eager launches")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="KIND OUT COMMAND CSV...: write a profile summary from rocprofv3 output and exit")
     args = ap.parse_args()
+    if args.summarize:
+        kind, out, command, *paths = args.summarize
+        summarize(kind, paths, command, out)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -448,7 +499,7 @@ def main():
         "config": {"workload": w.name, "kind": "decode", "batch": B, "context": L, "q_heads": w.Hq,
                    "kv_heads": w.Hkv, "head_dim": w.D, "retrieval_heads": w.n_ret, "top_p": 0.95,
                    "window": w.window, "sinks": w.sinks, "layer_instances": args.instances},
-        "roofline": {"kernel": "k_sel_score (indexer scores, decode)", "bound": "hbm",
+        "roofline": {"kernel": "k_sel_score<bf16, scores only> (rtp_indexer_scores, decode)", "bound": "hbm",
                      "achieved": round(k_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(),
                      "algorithmic_bytes": bytes_klow, "avg_launch_us": round(k_ms * 1e3, 2)},

@@ -11,8 +11,9 @@
 // 4096-key chunks so variable budgets never change its launch shape.
 //
 // Passes (one row = one (query token, retrieval head) pair):
-//   qlow:    q_low = bf16(fp32 chain over d of q . W_q), once per row
-//   score:   fp32 chain scores of every key of a chunk, the chunk maximum m_c,
+//   score:   q_low = bf16(fp32 chain over d of q . W_q) (every workgroup of the
+//            row forms it while its first indexer-key loads are in flight),
+//            fp32 chain scores of every key of a chunk, the chunk maximum m_c,
 //            and the chunk's cumulative mass histogram: exact fixed-point
 //            weights exp(s (d - m_c)) summed over bins of x_c = s (m_c - d)
 //            (1/4 wide)
@@ -70,40 +71,14 @@ __device__ __forceinline__ RowInfo row_info(const Geo& g, int row0, int lrow) {
 }
 
 // ---------------------------------------------------------------------------
-// q_low of every row of the group.  grid (ceil(rows / 4)), 64 threads: lane
-// 16 w + c runs the fixed-order chain of component c of row 4 blockIdx + w with
-// its operands in registers.
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(64) void k_sel_qlow(Geo g, const T* __restrict__ q, const T* __restrict__ w_q,
-                                                 int row0, int rows, uint16_t* __restrict__ qlow) {
-    const int lane = threadIdx.x;
-    const int lrow = blockIdx.x * 4 + (lane >> 4), c = lane & 15;
-    if (lrow >= rows) return;
-    const RowInfo ri = row_info(g, row0, lrow);
-    const int h = g.ret_heads[ri.r];
-    const T* qp = q + ((size_t)ri.t * g.Hq + h) * D;
-    const T* wp = w_q + (size_t)ri.r * D * kIdx + c;
-    float qv[D], wv[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-        qv[d] = ld(qp + d);
-        wv[d] = ld(wp + d * kIdx);
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int d = 0; d < D; ++d) acc = __builtin_fmaf(qv[d], wv[d], acc);
-    qlow[(size_t)lrow * kIdx + c] = f2bf(acc);
-}
-
-// ---------------------------------------------------------------------------
 // Scores.  grid (nchunk, rows), 256 threads.  Thread i of chunk c scores keys
 // c*4096 + 256*k + i, k = 0..15, i.e. slot i of the chunk's 16 pages: every
 // iteration reads one page's 8 KiB run of the head's indexer keys, coalesced.
 // STATS: also the chunk maximum and the chunk's mass histogram.
 // ---------------------------------------------------------------------------
-template <int STATS>
-__global__ __launch_bounds__(256) void k_sel_score(Geo g, const bf16_t* __restrict__ k_low, int row0, SelWs ws,
+template <typename T, int STATS>
+__global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ q, const T* __restrict__ w_q,
+                                                   const bf16_t* __restrict__ k_low, int row0, SelWs ws,
                                                    SelOut out) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
@@ -115,6 +90,9 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const bf16_t* __restri
     if (chunk >= ri.nch) return;
     __shared__ float wmax[4];
     __shared__ unsigned long long hist[kCB];
+    __shared__ float qrow[128];
+    __shared__ float wq[128 * kIdx];
+    __shared__ float qs[kIdx];
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int jbase = chunk * kChunk;
@@ -135,13 +113,29 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const bf16_t* __restri
         }
     };
     load_group(0);
-    float qv[kIdx];
+    // q_low: the query row and W_q staged through LDS, the fixed-order chain
+    // over d run by 16 lanes while the first loads are in flight
     {
-        const uint4* qp = reinterpret_cast<const uint4*>(ws.qlow + (size_t)ri.lrow * kIdx);
-        unpack8(qp[0], qv);
-        unpack8(qp[1], qv + 8);
+        const int h = g.ret_heads[ri.r];
+        const T* qp = q + ((size_t)ri.t * g.Hq + h) * g.D;
+        const T* wp = w_q + (size_t)ri.r * g.D * kIdx;
+        for (int x = tid; x < g.D; x += 256) qrow[x] = ld(qp + x);
+        for (int x = tid; x < g.D * kIdx; x += 256) wq[x] = ld(wp + x);
     }
     if (STATS && tid < kCB) hist[tid] = 0ull;
+    __syncthreads();
+    if (tid < kIdx) {
+        float acc = 0.0f;
+#pragma unroll 16
+        for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(qrow[d], wq[d * kIdx + tid], acc);
+        const bf16_t qb = f2bf(acc);
+        qs[tid] = bf2f(qb);
+        if (chunk == 0) ws.qlow[(size_t)ri.lrow * kIdx + tid] = qb;
+    }
+    __syncthreads();
+    float qv[kIdx];
+#pragma unroll
+    for (int c = 0; c < kIdx; ++c) qv[c] = qs[c];
 
     float dv[16];
     float mx = -INFINITY;
@@ -709,25 +703,21 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
                          int total_rows, int dtype, int scores_only, hipStream_t s) {
     (void)total_rows;
-    const dim3 gq((ws.rows + 3) / 4);
-    if (dtype == 0 && g.D == 64)
-        hipLaunchKernelGGL((k_sel_qlow<float, 64>), gq, dim3(64), 0, s, g, (const float*)q, (const float*)w_q, row0,
-                           ws.rows, ws.qlow);
-    else if (dtype == 0)
-        hipLaunchKernelGGL((k_sel_qlow<float, 128>), gq, dim3(64), 0, s, g, (const float*)q, (const float*)w_q, row0,
-                           ws.rows, ws.qlow);
-    else if (g.D == 64)
-        hipLaunchKernelGGL((k_sel_qlow<bf16_t, 64>), gq, dim3(64), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
-                           row0, ws.rows, ws.qlow);
-    else
-        hipLaunchKernelGGL((k_sel_qlow<bf16_t, 128>), gq, dim3(64), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
-                           row0, ws.rows, ws.qlow);
     const dim3 grid(ws.nchunk, ws.rows);
-    if (scores_only) {
-        hipLaunchKernelGGL(k_sel_score<0>, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, row0, ws, out);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL(k_sel_score<1>, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, row0, ws, out);
+    const bf16_t* kl = (const bf16_t*)k_low;
+    if (dtype == 0 && scores_only)
+        hipLaunchKernelGGL((k_sel_score<float, 0>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q, kl,
+                           row0, ws, out);
+    else if (dtype == 0)
+        hipLaunchKernelGGL((k_sel_score<float, 1>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q, kl,
+                           row0, ws, out);
+    else if (scores_only)
+        hipLaunchKernelGGL((k_sel_score<bf16_t, 0>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
+                           (const bf16_t*)w_q, kl, row0, ws, out);
+    else
+        hipLaunchKernelGGL((k_sel_score<bf16_t, 1>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
+                           (const bf16_t*)w_q, kl, row0, ws, out);
+    if (scores_only) return hipGetLastError();
     hipLaunchKernelGGL(k_sel_plan, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws);
     hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, row0, ws);
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
