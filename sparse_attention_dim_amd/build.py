@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librtp.so")
-SOURCES = ["abi.cpp", "append.hip", "select.hip", "select_chunk.hip", "attn_decode.hip", "attn_prefill.hip"]
+SOURCES = ["abi.cpp", "append.hip", "select.hip", "select_chunk.hip", "attn_decode.hip", "attn_prefill.hip", "attn_sparse_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

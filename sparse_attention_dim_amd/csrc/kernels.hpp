@@ -107,6 +107,14 @@ size_t chunk_select_ws_bytes(int rows, int n_ret, int n_keys);
 hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                                const float* top_p, void* ws, size_t ws_bytes, const SelOut& out, hipStream_t s);
 
+// Sparse attention of the retrieval heads of a prefill chunk (bf16, D = 128):
+// MFMA over the union of 64 consecutive rows' selected sets, masked per row.
+// Workspace: per-row window offsets and, with more than one 2^16-key window,
+// the windows' partial results.
+size_t sparse_prefill_ws_bytes(int rows, int n_keys);
+hipError_t launch_sparse_prefill(const Geo& g, const void* q, const void* k, const void* v, const int64_t* row_ptr,
+                                 const int32_t* idx, const int32_t* status, void* out, void* ws, hipStream_t s);
+
 // Chunked-prefill attention (bf16, D = 128) of the heads g.hlist[0..n_hlist):
 // sinks + causal window, or dense causal.
 hipError_t launch_prefill_attn(const Geo& g, const void* q, const void* k, const void* v, void* out,
