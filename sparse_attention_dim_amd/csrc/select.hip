@@ -17,7 +17,9 @@
 //            and the chunk's cumulative mass histogram: exact fixed-point
 //            weights exp(s (d - m_c)) summed over bins of x_c = s (m_c - d)
 //            (1/4 wide)
-//   resolve: one workgroup per row.  Row maximum m and total mass
+//   gather / resolve: every workgroup of the gather pass forms its row's plan
+//            (below) and gathers its chunk's part of U; one workgroup per row
+//            then resolves the cut.  Row maximum m and total mass
 //            Z = sum_c exp(s (m_c - m)) Z_c; every chunk bin whose upper edge
 //            lies below a threshold X on the row's x axis certainly holds
 //            keys with x < X, which gives a lower bound of the mass above
@@ -28,8 +30,8 @@
 //            masses per bucket (ties: lowest indices first); when U does not
 //            fit LDS the same selection runs over the row's scores.  U is
 //            gathered in index order, so the selected keys are its filter.
-//   rowptr:  CSR row pointers and the capacity check
-//   emit:    ordered compaction of every chunk's selected indices
+//   emit:    CSR row pointers, the capacity check, and the selected indices
+//            of every row
 // Workgroups of one pass never wait on each other: every hand-off between
 // workgroups is a kernel boundary (a device-scope fence per workgroup costs an
 // L2 write-back and invalidate on this multi-XCD part).
@@ -83,9 +85,12 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (STATS && chunk == 0 && tid == 0 && ri.lrow == 0 && row0 == 0) {
-        *out.status = 0;
-        out.row_ptr[0] = 0;
+    if (STATS && chunk == 0 && tid == 0) {
+        ws.row_n[ri.lrow] = 0u;
+        if (ri.lrow == 0 && row0 == 0) {
+            *out.status = 0;
+            out.row_ptr[0] = 0;
+        }
     }
     if (chunk >= ri.nch) return;
     __shared__ float wmax[4];
@@ -316,161 +321,104 @@ __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* sro
     return c;
 }
 
-// Ordered visit of the row's keys that satisfy pred(d): the row is split into
-// kRT / 64 contiguous wave segments, each lane reads four consecutive scores
-// per step (four steps in flight), and emit(pos, j, d) receives each hit with
-// its rank among the segment's hits (from base[w]).  Returns the lane's hit
-// count accumulated over the wave's segment (every lane holds the wave total).
-template <typename Pred, typename Emit>
-__device__ uint32_t scan_segment(const float* __restrict__ srow, int L, uint32_t base, Pred pred, Emit emit) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    constexpr int NW = kRT / 64;
-    const int seg = ((L + NW * 256 - 1) / (NW * 256)) * 256;
-    const int j_beg = w * seg, j_end = min(L, j_beg + seg);
-    uint32_t run = base;
-    for (int j0 = j_beg; j0 < j_end; j0 += 4 * 256) {
-        float4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u * 256 + 4 * lane;
-            v[u] = j < j_end ? *reinterpret_cast<const float4*>(srow + j) : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u * 256 + 4 * lane;
-            const float dv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            bool hit[4];
-            uint32_t c = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hit[e] = j + e < j_end && pred(dv[e]);
-                c += hit[e] ? 1u : 0u;
-            }
-            uint32_t incl = c;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const uint32_t y = __shfl_up(incl, o);
-                if (lane >= o) incl += y;
-            }
-            uint32_t pos = run + incl - c;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (hit[e]) emit(pos++, j + e, dv[e]);
-            run += __shfl(incl, 63);
-        }
-    }
-    return run - base;
-}
+// Plan of one row, computed by every workgroup of the gather pass (256
+// threads): row maximum m, total mass Z = sum_c exp(s (m_c - m)) Z_c, the
+// target, and the threshold d_thr of the candidate set U.  Every chunk bin
+// whose upper edge, moved to the row's axis, lies below X = k / 4 certainly
+// holds keys with s (m - d) < X: that gives a lower bound LB(k) of the mass
+// above any k; the smallest k whose bound reaches the target (plus one unit
+// of rounding per key) fixes U = {d >= m - X / s}.
+struct Plan {
+    float m, d_thr;
+    unsigned long long target;
+    int all;                                          // p >= 1: every key
+};
 
-// Plan.  One 1024-thread workgroup per row: row maximum, total mass, target,
-// and the threshold of U from the chunk histograms.
-__global__ __launch_bounds__(kRT) void k_sel_plan(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
+__device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const float* __restrict__ top_p,
+                         double* fch, double* dch, double* dred, uint32_t* ured, int* s_k) {
     const int tid = threadIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.x);
-    __shared__ double part[4][kGB];
-    __shared__ double fch[kMaxChunks], dch[kMaxChunks];
-    __shared__ double dred[kRT / 64];
-    __shared__ uint32_t ured[kRT / 64];
-    __shared__ int s_i;
-    const float s = g.idx_scale;
     const int nch = ri.nch;
+    const float s = g.idx_scale;
     const unsigned long long* chist = ws.chist + (size_t)ri.lrow * ws.nchunk * kCB;
-    RowState st;
-    st.L = ri.L;
-    st.Tkey = 0u;
-    st.jT = ri.L;
-    st.count = 0;
-
-    // ---- row maximum and the per-chunk rescaling to it
+    const uint32_t* cmax = ws.cmax + (size_t)ri.lrow * ws.nchunk;
     uint32_t mk = 0u;
-    for (int c = tid; c < nch; c += kRT) {
-        const uint32_t v = ws.cmax[(size_t)ri.lrow * ws.nchunk + c];
-        mk = v > mk ? v : mk;
-    }
+    for (int c = tid; c < nch; c += 256) mk = max(mk, cmax[c]);
     mk = wave_max_u32(mk);
     if ((tid & 63) == 0) ured[tid >> 6] = mk;
+    if (tid == 0) {
+        s_k[0] = kGB;
+        s_k[1] = 16;
+    }
     __syncthreads();
-    mk = 0u;
-    for (int w = 0; w < kRT / 64; ++w) mk = ured[w] > mk ? ured[w] : mk;
-    const float m = key_score(mk);
-    st.m = m;
-    for (int c = tid; c < nch; c += kRT) {
-        const double dc = (double)s * ((double)m - (double)key_score(ws.cmax[(size_t)ri.lrow * ws.nchunk + c]));
+    mk = max(max(ured[0], ured[1]), max(ured[2], ured[3]));
+    Plan pl;
+    pl.m = key_score(mk);
+    double z = 0.0;
+    for (int c = tid; c < nch; c += 256) {
+        const double dc = (double)s * ((double)pl.m - (double)key_score(cmax[c]));
+        const double f = exp(-dc);
         dch[c] = dc;
-        fch[c] = exp(-dc);
+        fch[c] = f;
+        z += f * (double)chist[(size_t)c * kCB + kCB - 1];
     }
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+    if ((tid & 63) == 0) dred[tid >> 6] = z;
     __syncthreads();
-    // ---- total mass and the lower bound LB(k) of the mass of keys with x < k / 4:
-    // chunk bin b counts once (b + 1) / 4 + dc <= k / 4, i.e. b <= k - 1 - 4 dc
-    {
-        const int k = tid & (kGB - 1), cg = tid >> 8;
-        double acc = 0.0, z = 0.0;
-        for (int c = cg; c < nch; c += kRT / kGB) {
-            const double bmax = floor((double)(k - 1) - (double)kCBPerUnit * dch[c]);
-            if (bmax >= 0.0) acc += fch[c] * (double)chist[(size_t)c * kCB + (int)fmin(bmax, (double)(kCB - 1))];
-            if (k == 0) z += fch[c] * (double)chist[(size_t)c * kCB + kCB - 1];
-        }
-        part[cg][k] = acc;
-        for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
-        if ((tid & 63) == 0) dred[tid >> 6] = z;
-    }
-    __syncthreads();
-    double Z = 0.0;
-    for (int w = 0; w < kRT / 64; ++w) Z += dred[w];
+    const double Z = dred[0] + dred[1] + dred[2] + dred[3];
     const float p = top_p[ri.b];
-    if (!(p < 1.0f)) {
-        if (tid == 0) {
-            st.mode = 0;
-            st.count = ri.L;
-            st.target = 0ull;
-            st.d_thr = -INFINITY;
-            ws.st[ri.lrow] = st;
-            ws.row_n[ri.lrow] = 0u;
-        }
-        return;
-    }
+    pl.all = !(p < 1.0f);
     unsigned long long target = (unsigned long long)ceil((double)p * Z);
     if ((double)target > Z) target = (unsigned long long)Z;
     if (target < 1ull) target = 1ull;
-    st.target = target;
-    // smallest k whose bound reaches the target with room for the per-key
-    // rounding of the fixed-point weights (one unit per key)
-    if (tid == 0) s_i = kGB;
+    pl.target = target;
+    pl.d_thr = -INFINITY;
+    if (pl.all) return pl;
+    // LB(k) is non-decreasing in k: first at the 16 points k = 16 i + 15, then
+    // at the 16 values up to the first point that reaches.  16 lanes share one
+    // k (chunk bin b counts once (b + 1) / 4 + dc <= k / 4).
+    const double need = (double)target * (1.0 + 0x1.0p-40) + (double)ri.L + 1.0;
+    const int grp = tid >> 4, sub = tid & 15;
+    const auto lb_reaches = [&](int k) {
+        double lb = 0.0;
+        for (int c = sub; c < nch; c += 16) {
+            const double bmax = floor((double)(k - 1) - (double)kCBPerUnit * dch[c]);
+            if (bmax >= 0.0) lb += fch[c] * (double)chist[(size_t)c * kCB + (int)fmin(bmax, (double)(kCB - 1))];
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) lb += __shfl_xor(lb, o);
+        return sub == 0 && lb >= need;
+    };
+    if (lb_reaches(16 * grp + 15)) atomicMin(&s_k[1], grp);
     __syncthreads();
-    if (tid < kGB) {
-        const double lb = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
-        const double need = (double)target * (1.0 + 0x1.0p-40) + (double)ri.L + 1.0;
-        if (lb >= need) atomicMin(&s_i, tid);
-    }
+    const int ic = s_k[1];
+    if (ic < 16 && lb_reaches(16 * ic + grp)) atomicMin(&s_k[0], 16 * ic + grp);
     __syncthreads();
-    const int ks = s_i;
-    // U = {d >= d_thr}; the margin covers the float rounding of the chunk bins
-    float d_thr = -INFINITY;
+    const int ks = s_k[0];
     if (ks < kGB) {
+        // the margin covers the float rounding of the chunk bins
         const double X = (double)ks / (double)kCBPerUnit;
         const double xm = X + 0x1.0p-18 * (X + 1.0);
-        d_thr = __double2float_rd((double)m - xm / (double)s - 0x1.0p-20 * fabs((double)m));
+        pl.d_thr = __double2float_rd((double)pl.m - xm / (double)s - 0x1.0p-20 * fabs((double)pl.m));
     }
-    if (tid == 0) {
-        st.mode = 1;
-        st.d_thr = d_thr;
-        ws.st[ri.lrow] = st;
-        ws.row_n[ri.lrow] = 0u;
-    }
+    return pl;
 }
 
-// Gather.  grid (nchunk, rows), 256 threads: the chunk's keys of U in index
-// order, as one block of the row's candidate list (blocks are placed by one
-// atomic per chunk; the resolve pass puts them back in chunk order).
-__global__ __launch_bounds__(256) void k_sel_gather(Geo g, int row0, SelWs ws) {
+// Gather.  grid (nchunk, rows), 256 threads: the row's plan, then the chunk's
+// keys of U in index order as one block of the row's candidate list (blocks
+// are placed by one atomic per chunk; the resolve pass puts them back in
+// chunk order).  The first chunk's workgroup records the plan.
+__global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
     if (chunk >= ri.nch) return;
-    const RowState st = ws.st[ri.lrow];
-    if (st.mode == 0) return;
+    __shared__ double fch[kMaxChunks], dch[kMaxChunks];
+    __shared__ double dred[4];
+    __shared__ uint32_t ured[4];
+    __shared__ int s_k[2];
     __shared__ unsigned long long scan_sh[256 / 64 + 1];
     __shared__ uint32_t s_base;
+    // the chunk's scores, loaded while the plan is formed
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int j0 = chunk * kChunk + 16 * tid;             // 16 consecutive keys per thread
     float dv[16];
@@ -482,9 +430,23 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, int row0, SelWs ws) {
         dv[4 * u + 2] = v.z;
         dv[4 * u + 3] = v.w;
     }
+    const Plan pl = row_plan(g, ri, ws, top_p, fch, dch, dred, ured, s_k);
+    if (chunk == 0 && tid == 0) {
+        RowState st;
+        st.m = pl.m;
+        st.L = ri.L;
+        st.Tkey = 0u;
+        st.jT = ri.L;
+        st.target = pl.target;
+        st.d_thr = pl.d_thr;
+        st.mode = pl.all ? 0 : 1;
+        st.count = pl.all ? ri.L : 0;
+        ws.st[ri.lrow] = st;
+    }
+    if (pl.all) return;
     uint32_t c = 0;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) c += (j0 + e < ri.L && dv[e] >= st.d_thr) ? 1u : 0u;
+    for (int e = 0; e < 16; ++e) c += (j0 + e < ri.L && dv[e] >= pl.d_thr) ? 1u : 0u;
     unsigned long long tot;
     uint32_t o = (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
     if (tid == 0) {
@@ -500,25 +462,169 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, int row0, SelWs ws) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int j = j0 + e;
-        if (j < ri.L && dv[e] >= st.d_thr)
+        if (j < ri.L && dv[e] >= pl.d_thr)
             ub[o++] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)j);
     }
 }
 
-// Resolve.  One 1024-thread workgroup per row: U back in index order, the
-// radix cut, and the selected indices in order (or, for a list that did not
-// fit, the cut over the row's scores and per-chunk counts).
+// Cut among a candidate list held in LDS (cand = (score key << 32) | ~index,
+// wgt = exact fixed-point weights): radix levels of 2048 buckets with exact
+// masses; once the cut bucket holds at most 64 keys, one wavefront sorts them
+// in registers (score key descending, index ascending) and finds the first
+// whose cumulative mass reaches the target.
+__device__ Cut list_cut(const unsigned long long* cand, const unsigned long long* wgt, int n, const float* srow,
+                        int L, uint32_t klo, uint32_t khi, unsigned long long target, float m, float s,
+                        unsigned long long* hmb, uint32_t* hcb, unsigned long long* scan_sh, uint32_t* s_u,
+                        unsigned long long* s_S, int* s_i, unsigned long long* small_v, unsigned long long* small_w,
+                        Cut* s_cut) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    unsigned long long S_hi = 0ull;
+    for (int level = 0; level < 4; ++level) {
+        const uint32_t span = khi - klo;
+        const int bits = span ? 32 - __clz(span) : 0;
+        const int shift = bits > 11 ? bits - 11 : 0;
+        for (int i = tid; i < kNR; i += kRT) {
+            hmb[i] = 0ull;
+            hcb[i] = 0u;
+        }
+        __syncthreads();
+        for (int i = tid; i < n; i += kRT) {
+            const uint32_t key = (uint32_t)(cand[i] >> 32);
+            if (key < klo || key > khi) continue;
+            const uint32_t bk = (khi - key) >> shift;         // bucket 0 holds the highest keys
+            atomicAdd(&hmb[bk], wgt[i]);
+            atomicAdd(&hcb[bk], 1u);
+        }
+        __syncthreads();
+        const unsigned long long loc = hmb[2 * tid] + hmb[2 * tid + 1];
+        unsigned long long tot;
+        const unsigned long long ex = S_hi + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
+        if (tid == 0) *s_i = kNR;
+        __syncthreads();
+        if (ex + hmb[2 * tid] >= target && hcb[2 * tid]) atomicMin(s_i, 2 * tid);
+        else if (ex + loc >= target && hcb[2 * tid + 1]) atomicMin(s_i, 2 * tid + 1);
+        __syncthreads();
+        const int nb = (int)(span >> shift) + 1;
+        int bk = *s_i;
+        if (bk < kNR && (bk >> 1) == tid) {
+            *s_S = (bk & 1) ? ex + hmb[2 * tid] : ex;
+            *s_u = hcb[bk];
+        }
+        if (bk >= kNR && tid == 0) {
+            *s_S = S_hi + tot - hmb[nb - 1];
+            *s_u = hcb[nb - 1];
+        }
+        if (bk >= kNR) bk = nb - 1;
+        __syncthreads();
+        S_hi = *s_S;
+        const uint32_t n_b = *s_u;
+        const uint32_t nkhi = khi - ((uint32_t)bk << shift);
+        const uint32_t wdt = shift >= 32 ? 0xFFFFFFFFu : ((1u << shift) - 1u);
+        const uint32_t nklo = (nkhi - klo > wdt) ? nkhi - wdt : klo;
+        klo = nklo;
+        khi = nkhi;
+        __syncthreads();
+        if (n_b <= 64u) {
+            // the bucket's keys into a wavefront, sorted in registers
+            if (tid == 0) *s_u = 0u;
+            __syncthreads();
+            for (int i = tid; i < n; i += kRT) {
+                const uint32_t key = (uint32_t)(cand[i] >> 32);
+                if (key < klo || key > khi) continue;
+                const uint32_t slot = atomicAdd(s_u, 1u);
+                if (slot < 64u) {
+                    small_v[slot] = cand[i];
+                    small_w[slot] = wgt[i];
+                }
+            }
+            __syncthreads();
+            if (tid < 64) {
+                const int nbk = (int)min(*s_u, 64u);
+                unsigned long long v = lane < nbk ? small_v[lane] : 0ull;
+                unsigned long long w = lane < nbk ? small_w[lane] : 0ull;
+#pragma unroll
+                for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+                    for (int j = k >> 1; j > 0; j >>= 1) {
+                        const unsigned long long ov = __shfl_xor(v, j), ow = __shfl_xor(w, j);
+                        const bool desc = (lane & k) == 0 || k == 64;
+                        const bool lower = (lane & j) == 0;
+                        const bool take = desc == lower ? ov > v : ov < v;
+                        if (take) {
+                            v = ov;
+                            w = ow;
+                        }
+                    }
+                unsigned long long incl = w;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned long long y = __shfl_up(incl, o);
+                    if (lane >= o) incl += y;
+                }
+                const unsigned long long reach = __ballot(lane < nbk && S_hi + incl >= target);
+                const int ic = reach ? __ffsll((long long)reach) - 1 : nbk - 1;
+                const unsigned long long vc = __shfl(v, ic);
+                if (lane == 0) {
+                    s_cut->Tkey = (uint32_t)(vc >> 32);
+                    s_cut->jT = (int32_t)~(uint32_t)vc;
+                }
+            }
+            __syncthreads();
+            return *s_cut;
+        }
+        if (klo == khi) {
+            // one score value with more than 64 keys: its lowest indices first
+            const unsigned long long wT = weight_bin(key_score(klo), m, s).w;
+            const unsigned long long need = target - S_hi;
+            const uint32_t ntie = (uint32_t)min((need + wT - 1ull) / wT, (unsigned long long)n_b);
+            Cut c;
+            c.Tkey = klo;
+            // the list is in index order: the ntie-th tie of the list
+            if (tid == 0) {
+                *s_u = 0u;
+                *s_i = -1;
+            }
+            __syncthreads();
+            for (int i0 = 0; i0 < n; i0 += kRT) {
+                const int i = i0 + tid;
+                const bool is_tie = i < n && (uint32_t)(cand[i] >> 32) == klo;
+                const uint32_t before_blk = *s_u;
+                unsigned long long t2;
+                const unsigned long long rank = block_excl_scan_u64<kRT>(is_tie ? 1ull : 0ull, &t2, scan_sh);
+                if (is_tie && before_blk + rank + 1ull == ntie) *s_i = (int)~(uint32_t)cand[i];
+                __syncthreads();
+                if (tid == 0) *s_u = before_blk + (uint32_t)t2;
+                __syncthreads();
+                if (*s_i >= 0) break;
+            }
+            c.jT = *s_i;
+            __syncthreads();
+            return c;
+        }
+    }
+    Cut c;
+    c.Tkey = khi;
+    c.jT = L;
+    return c;
+}
+
+// Resolve.  One 1024-thread workgroup per row: U back in index order with its
+// exact weights, the cut, and the selected indices in order (a list that did
+// not fit: the cut over the row's scores and per-chunk counts).
 __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) {
     const int tid = threadIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.x);
     RowState st = ws.st[ri.lrow];
     if (st.mode == 0) return;
     __shared__ unsigned long long cand[kCand];
+    __shared__ unsigned long long wgt[kCand];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
     __shared__ unsigned long long hmb[kNR];
     __shared__ uint32_t hcb[kNR];
     __shared__ uint32_t ccount[kMaxChunks];
     __shared__ uint32_t cb_sorted[kMaxChunks], cb_chunk[kMaxChunks], cpre[kMaxChunks];
+    __shared__ unsigned long long small_v[64], small_w[64];
+    __shared__ Cut s_cut;
     __shared__ int s_i;
     __shared__ uint32_t s_n;
     __shared__ unsigned long long s_S;
@@ -529,6 +635,8 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
     const unsigned long long target = st.target;
     const int lane = tid & 63;
     const int nU = (int)ws.row_n[ri.lrow];
+    const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
+    const auto selected_by = [](const Cut& c, uint32_t key, int j) { return key > c.Tkey || (key == c.Tkey && j <= c.jT); };
     if (nU <= kCand) {
         // blocks of the list in chunk order: chunk c's block starts at cpre[c]
         // in the ordered list and at chunk_base[c] in the gathered one
@@ -543,16 +651,14 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
         unsigned long long tot;
         const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
         if (tid < nch) cpre[tid] = (uint32_t)ex;
-        // chunks with entries, ordered by their gathered position
-        if (tid < nch) {
+        if (tid < nch && n_c) {
+            // chunks with entries, ordered by their gathered position
             const uint32_t bt = cbase[tid];
             uint32_t rank = 0;
-            if (n_c) {
-                for (int c = 0; c < nch; ++c)
-                    if (cn[c] && (cbase[c] < bt || (cbase[c] == bt && c < tid))) ++rank;
-                cb_sorted[rank] = bt;
-                cb_chunk[rank] = (uint32_t)tid;
-            }
+            for (int c = 0; c < nch; ++c)
+                if (cn[c] && (cbase[c] < bt || (cbase[c] == bt && c < tid))) ++rank;
+            cb_sorted[rank] = bt;
+            cb_chunk[rank] = (uint32_t)tid;
         }
         if (tid == 0) s_i = 0;
         __syncthreads();
@@ -561,55 +667,55 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
         const int nblk = s_i;
         const unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand;
         for (int i = tid; i < nU; i += kRT) {
-            // the block holding gathered position i
             int lo = 0, hi = nblk - 1;
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
                 if (cb_sorted[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
             }
             const uint32_t c = cb_chunk[lo];
-            cand[cpre[c] + ((uint32_t)i - cb_sorted[lo])] = ub[i];
+            const unsigned long long e = ub[i];
+            const uint32_t dst = cpre[c] + ((uint32_t)i - cb_sorted[lo]);
+            cand[dst] = e;
+            wgt[dst] = weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
         }
         __syncthreads();
-    }
-    for (int c = tid; c < kMaxChunks; c += kRT) ccount[c] = 0u;
-    const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
-    const Cut cut = radix_cut(cand, nU <= kCand ? nU : -1, srow, ri.L, klo, khi, 0ull, target, m, s, hmb, hcb,
-                              scan_sh, &s_n, &s_S, &s_i);
-
-    const auto selected = [&](uint32_t key, int j) { return key > cut.Tkey || (key == cut.Tkey && j <= cut.jT); };
-    if (nU <= kCand) {
-        // ---- U is in index order: its selected entries, in order, into the row's list
+        const Cut cut = list_cut(cand, wgt, nU, srow, ri.L, klo, khi, target, m, s, hmb, hcb, scan_sh, &s_n, &s_S,
+                                 &s_i, small_v, small_w, &s_cut);
+        // U is in index order: its selected entries, in order, into the row's list
         constexpr int per = kCand / kRT;
         uint32_t c = 0;
 #pragma unroll
         for (int x = 0; x < per; ++x) {
             const int i = tid * per + x;
-            if (i < nU && selected((uint32_t)(cand[i] >> 32), (int)~(uint32_t)cand[i])) ++c;
+            if (i < nU && selected_by(cut, (uint32_t)(cand[i] >> 32), (int)~(uint32_t)cand[i])) ++c;
         }
-        unsigned long long tot;
-        uint32_t o = (uint32_t)block_excl_scan_u64<kRT>(c, &tot, scan_sh);
+        unsigned long long tot2;
+        uint32_t o = (uint32_t)block_excl_scan_u64<kRT>(c, &tot2, scan_sh);
         uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
 #pragma unroll
         for (int x = 0; x < per; ++x) {
             const int i = tid * per + x;
             if (i < nU) {
                 const int j = (int)~(uint32_t)cand[i];
-                if (selected((uint32_t)(cand[i] >> 32), j)) sl[o++] = (uint32_t)j;
+                if (selected_by(cut, (uint32_t)(cand[i] >> 32), j)) sl[o++] = (uint32_t)j;
             }
         }
         if (tid == 0) {
             st.mode = 1;
             st.Tkey = cut.Tkey;
             st.jT = cut.jT;
-            st.count = (int32_t)tot;
+            st.count = (int32_t)tot2;
             ws.st[ri.lrow] = st;
         }
         return;
     }
-    // ---- U too large for LDS: selected keys per chunk for the ordered compaction
+    // ---- U too large for LDS: the cut over the row's scores, selected keys per
+    // chunk for the ordered compaction
+    for (int c = tid; c < kMaxChunks; c += kRT) ccount[c] = 0u;
+    const Cut cut = radix_cut(cand, -1, srow, ri.L, klo, khi, 0ull, target, m, s, hmb, hcb, scan_sh, &s_n, &s_S,
+                              &s_i);
     for (int j = tid; j < ri.L; j += kRT) {
-        const bool sel = selected(score_key(srow[j]), j);
+        const bool sel = selected_by(cut, score_key(srow[j]), j);
         const unsigned long long b = __ballot(sel);
         if (lane == 0 && b) atomicAdd(&ccount[j / kChunk], (uint32_t)__popcll(b));
     }
@@ -628,8 +734,11 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
 }
 
 // ---------------------------------------------------------------------------
-// CSR row pointers of the group's rows and the capacity check.
+// CSR row pointers of the group's rows and the capacity check (groups of more
+// than kRowsInEmit rows; smaller groups are handled inside the emit pass).
 // ---------------------------------------------------------------------------
+constexpr int kRowsInEmit = 1024;
+
 __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut out) {
     const int tid = threadIdx.x;
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
@@ -647,17 +756,46 @@ __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut o
 
 // ---------------------------------------------------------------------------
 // Emit.  grid (nchunk, rows), 256 threads: the part of a row's output that
-// belongs to one 4096-key chunk (a slice of the sorted list, or the ordered
-// compaction of the chunk's selected keys).
+// belongs to one 4096-key chunk (a slice of the ordered list, or the ordered
+// compaction of the chunk's selected keys).  ROWPTR: the group is small, so
+// every workgroup sums the counts before its row itself, writes its row
+// pointer, and checks the capacity.
 // ---------------------------------------------------------------------------
+template <int ROWPTR>
 __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, SelOut out) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
+    const RowState st = ws.st[ri.lrow];
+    int64_t rbase;
+    if (ROWPTR) {
+        __shared__ unsigned long long red[8];
+        unsigned long long before = 0, all = 0;
+        for (int i = tid; i < ws.rows; i += 256) {
+            const unsigned long long c = (unsigned long long)ws.st[i].count;
+            all += c;
+            if (i < ri.lrow) before += c;
+        }
+        before = wave_sum_u64(before);
+        all = wave_sum_u64(all);
+        if ((tid & 63) == 0) {
+            red[tid >> 6] = before;
+            red[4 + (tid >> 6)] = all;
+        }
+        __syncthreads();
+        const int64_t carry = out.row_ptr[row0];
+        rbase = carry + (int64_t)(red[0] + red[1] + red[2] + red[3]);
+        const int64_t total = carry + (int64_t)(red[4] + red[5] + red[6] + red[7]);
+        if (chunk == 0 && tid == 0) out.row_ptr[ri.row + 1] = rbase + st.count;
+        if (total > out.capacity) {
+            if (chunk == 0 && tid == 0 && ri.lrow == 0) *out.status = 1;
+            return;
+        }
+    } else {
+        rbase = out.row_ptr[ri.row];
+    }
     if (chunk >= ri.nch) return;
     if (*out.status != 0) return;
-    const RowState st = ws.st[ri.lrow];
-    const int64_t rbase = out.row_ptr[ri.row];
     const int jbase = chunk * kChunk;
     if (st.mode == 0) {
         for (int k = tid; k < kChunk && jbase + k < ri.L; k += 256) out.idx[rbase + jbase + k] = jbase + k;
@@ -718,11 +856,14 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
         hipLaunchKernelGGL((k_sel_score<bf16_t, 1>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
                            (const bf16_t*)w_q, kl, row0, ws, out);
     if (scores_only) return hipGetLastError();
-    hipLaunchKernelGGL(k_sel_plan, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws);
-    hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, row0, ws);
+    hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, top_p, row0, ws);
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
-    hipLaunchKernelGGL(k_sel_rowptr, dim3(1), dim3(kRT), 0, s, row0, ws, out);
-    hipLaunchKernelGGL(k_sel_emit, grid, dim3(256), 0, s, g, row0, ws, out);
+    if (ws.rows <= kRowsInEmit) {
+        hipLaunchKernelGGL(k_sel_emit<1>, grid, dim3(256), 0, s, g, row0, ws, out);
+    } else {
+        hipLaunchKernelGGL(k_sel_rowptr, dim3(1), dim3(kRT), 0, s, row0, ws, out);
+        hipLaunchKernelGGL(k_sel_emit<0>, grid, dim3(256), 0, s, g, row0, ws, out);
+    }
     return hipGetLastError();
 }
 
