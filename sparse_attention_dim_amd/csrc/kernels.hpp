@@ -59,10 +59,9 @@ struct SelWs {
     unsigned long long* chist;    // [rows][nchunk][kCB] chunk mass histograms
     RowState* st;                 // [rows]
     uint32_t* sel;                // [rows][kCand] selected indices, ascending (mode 1)
-    unsigned long long* ubuf;     // [rows][kCand] gathered U: (score key << 32) | ~index
-    uint32_t* row_n;              // [rows] entries gathered
-    uint32_t* chunk_base;         // [rows][nchunk] block of each chunk in ubuf
-    uint32_t* chunk_n;            // [rows][nchunk] its length
+    unsigned long long* ubuf;     // [rows][kCand] U in index order: (score key << 32) | ~index
+    unsigned* ccnt;               // [rows][nchunk][kCB] cumulative key counts of the chunk bins
+    uint32_t* row_n;              // [rows] size of U
     uint32_t* chunk_cnt;          // [rows][nchunk] output offsets per chunk (mode 2)
     int nchunk;
     int rows;                     // rows of this group

@@ -85,16 +85,14 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (STATS && chunk == 0 && tid == 0) {
-        ws.row_n[ri.lrow] = 0u;
-        if (ri.lrow == 0 && row0 == 0) {
-            *out.status = 0;
-            out.row_ptr[0] = 0;
-        }
+    if (STATS && chunk == 0 && tid == 0 && ri.lrow == 0 && row0 == 0) {
+        *out.status = 0;
+        out.row_ptr[0] = 0;
     }
     if (chunk >= ri.nch) return;
     __shared__ float wmax[4];
     __shared__ unsigned long long hist[kCB];
+    __shared__ unsigned hcnt[kCB];
     __shared__ float qrow[128];
     __shared__ float wq[128 * kIdx];
     __shared__ float qs[kIdx];
@@ -127,7 +125,10 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         for (int x = tid; x < g.D; x += 256) qrow[x] = ld(qp + x);
         for (int x = tid; x < g.D * kIdx; x += 256) wq[x] = ld(wp + x);
     }
-    if (STATS && tid < kCB) hist[tid] = 0ull;
+    if (STATS && tid < kCB) {
+        hist[tid] = 0ull;
+        hcnt[tid] = 0u;
+    }
     __syncthreads();
     if (tid < kIdx) {
         float acc = 0.0f;
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         if (j < ri.L) {
             const WeightBin wb = weight_bin(dv[k], mc, s);
             atomicAdd(&hist[wb.bin >> 4], wb.w);         // 64 level-1 bins per unit -> 4 per unit
+            atomicAdd(&hcnt[wb.bin >> 4], 1u);
         }
     }
     __syncthreads();
@@ -191,6 +193,18 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         unsigned long long* ch = ws.chist + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
         ch[2 * tid] = incl - b;
         ch[2 * tid + 1] = incl;
+    } else if (tid < 128) {
+        const int t = tid - 64;
+        const unsigned a = hcnt[2 * t], b = hcnt[2 * t + 1];
+        unsigned incl = a + b;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const unsigned y = __shfl_up(incl, o);
+            if (t >= o) incl += y;
+        }
+        unsigned* cc = ws.ccnt + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
+        cc[2 * t] = incl - b;
+        cc[2 * t + 1] = incl;
     }
 }
 
@@ -332,6 +346,7 @@ struct Plan {
     float m, d_thr;
     unsigned long long target;
     int all;                                          // p >= 1: every key
+    int ks;                                           // X = ks / 4, or kGB if no grid point suffices
 };
 
 __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const float* __restrict__ top_p,
@@ -372,6 +387,7 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     if (target < 1ull) target = 1ull;
     pl.target = target;
     pl.d_thr = -INFINITY;
+    pl.ks = kGB;
     if (pl.all) return pl;
     // LB(k) is non-decreasing in k: first at the 16 points k = 16 i + 15, then
     // at the 16 values up to the first point that reaches.  16 lanes share one
@@ -394,6 +410,7 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     if (ic < 16 && lb_reaches(16 * ic + grp)) atomicMin(&s_k[0], 16 * ic + grp);
     __syncthreads();
     const int ks = s_k[0];
+    pl.ks = ks;
     if (ks < kGB) {
         // the margin covers the float rounding of the chunk bins
         const double X = (double)ks / (double)kCBPerUnit;
@@ -404,9 +421,8 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
 }
 
 // Gather.  grid (nchunk, rows), 256 threads: the row's plan, then the chunk's
-// keys of U in index order as one block of the row's candidate list (blocks
-// are placed by one atomic per chunk; the resolve pass puts them back in
-// chunk order).  The first chunk's workgroup records the plan.
+// keys of U written at the chunk's place in the row's index-ordered list.
+// The first chunk's workgroup records the plan and the size of U.
 __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
@@ -431,6 +447,38 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
         dv[4 * u + 3] = v.w;
     }
     const Plan pl = row_plan(g, ri, ws, top_p, fch, dch, dred, ured, s_k);
+    if (pl.all) {
+        if (chunk == 0 && tid == 0) {
+            RowState st;
+            st.m = pl.m;
+            st.L = ri.L;
+            st.Tkey = 0u;
+            st.jT = ri.L;
+            st.target = pl.target;
+            st.d_thr = pl.d_thr;
+            st.mode = 0;
+            st.count = ri.L;
+            ws.st[ri.lrow] = st;
+        }
+        return;
+    }
+    // U: in chunk c, the keys whose chunk bin is at most bsel(c) = ks + 1 - 4 dc
+    // (a quarter unit beyond the bins that LB(ks) counts, so U holds every key
+    // with s (m - d) < ks / 4 and the cut lies inside it).  The cumulative
+    // counts give every chunk's share of U, hence its place in the index-ordered
+    // list, without atomics.
+    const unsigned* ccnt = ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB;
+    const auto bsel = [&](int c) {
+        return pl.ks >= kGB ? kCB - 1 : (int)fmin(floor((double)(pl.ks + 1) - (double)kCBPerUnit * dch[c]), (double)(kCB - 1));
+    };
+    unsigned long long cnt_c = 0ull;
+    if (tid < ri.nch) {
+        const int b = bsel(tid);
+        cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
+    }
+    unsigned long long nU;
+    const unsigned long long off_c = block_excl_scan_u64<256>(cnt_c, &nU, scan_sh);
+    if (tid == chunk) s_base = (uint32_t)off_c;
     if (chunk == 0 && tid == 0) {
         RowState st;
         st.m = pl.m;
@@ -439,32 +487,31 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
         st.jT = ri.L;
         st.target = pl.target;
         st.d_thr = pl.d_thr;
-        st.mode = pl.all ? 0 : 1;
-        st.count = pl.all ? ri.L : 0;
+        st.mode = 1;
+        st.count = 0;
         ws.st[ri.lrow] = st;
+        ws.row_n[ri.lrow] = (uint32_t)nU;                 // at most 2^20
     }
-    if (pl.all) return;
-    uint32_t c = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) c += (j0 + e < ri.L && dv[e] >= pl.d_thr) ? 1u : 0u;
-    unsigned long long tot;
-    uint32_t o = (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
-    if (tid == 0) {
-        const uint32_t b = tot ? atomicAdd(&ws.row_n[ri.lrow], (uint32_t)tot) : 0u;
-        s_base = b;
-        ws.chunk_base[(size_t)ri.lrow * ws.nchunk + chunk] = b;
-        ws.chunk_n[(size_t)ri.lrow * ws.nchunk + chunk] = (uint32_t)tot;
-    }
-    __syncthreads();
-    const uint32_t b = s_base;
-    if (b + tot > (unsigned long long)kCand) return;      // the list overflows: the row takes the long path
-    unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand + b;
+    if (nU > (unsigned long long)kCand) return;           // the row takes the long path
+    const int bmine = bsel(chunk);
+    if (bmine < 0) return;
+    const float mc = key_score(ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk]);
+    const float s = g.idx_scale;
+    uint32_t inU = 0u, c = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-        const int j = j0 + e;
-        if (j < ri.L && dv[e] >= pl.d_thr)
-            ub[o++] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)j);
+        const bool in = j0 + e < ri.L && (weight_bin(dv[e], mc, s).bin >> 4) <= bmine;
+        inU |= in ? 1u << e : 0u;
+        c += in ? 1u : 0u;
     }
+    __syncthreads();
+    unsigned long long tot;
+    uint32_t o = s_base + (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
+    unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+        if (inU & (1u << e))
+            ub[o++] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)(j0 + e));
 }
 
 // Cut among a candidate list held in LDS (cand = (score key << 32) | ~index,
@@ -608,9 +655,9 @@ __device__ Cut list_cut(const unsigned long long* cand, const unsigned long long
     return c;
 }
 
-// Resolve.  One 1024-thread workgroup per row: U back in index order with its
-// exact weights, the cut, and the selected indices in order (a list that did
-// not fit: the cut over the row's scores and per-chunk counts).
+// Resolve.  One 1024-thread workgroup per row: U with its exact weights, the
+// cut, and the selected indices in order (a list that did not fit: the cut
+// over the row's scores and per-chunk counts).
 __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) {
     const int tid = threadIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.x);
@@ -622,7 +669,6 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
     __shared__ unsigned long long hmb[kNR];
     __shared__ uint32_t hcb[kNR];
     __shared__ uint32_t ccount[kMaxChunks];
-    __shared__ uint32_t cb_sorted[kMaxChunks], cb_chunk[kMaxChunks], cpre[kMaxChunks];
     __shared__ unsigned long long small_v[64], small_w[64];
     __shared__ Cut s_cut;
     __shared__ int s_i;
@@ -638,45 +684,11 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
     const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
     const auto selected_by = [](const Cut& c, uint32_t key, int j) { return key > c.Tkey || (key == c.Tkey && j <= c.jT); };
     if (nU <= kCand) {
-        // blocks of the list in chunk order: chunk c's block starts at cpre[c]
-        // in the ordered list and at chunk_base[c] in the gathered one
-        uint32_t* cbase = hcb;                             // LDS copies (the radix buffers are free here)
-        uint32_t* cn = hcb + kMaxChunks;
-        if (tid < nch) {
-            cbase[tid] = ws.chunk_base[(size_t)ri.lrow * ws.nchunk + tid];
-            cn[tid] = ws.chunk_n[(size_t)ri.lrow * ws.nchunk + tid];
-        }
-        __syncthreads();
-        unsigned long long n_c = tid < nch ? cn[tid] : 0ull;
-        unsigned long long tot;
-        const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
-        if (tid < nch) cpre[tid] = (uint32_t)ex;
-        if (tid < nch && n_c) {
-            // chunks with entries, ordered by their gathered position
-            const uint32_t bt = cbase[tid];
-            uint32_t rank = 0;
-            for (int c = 0; c < nch; ++c)
-                if (cn[c] && (cbase[c] < bt || (cbase[c] == bt && c < tid))) ++rank;
-            cb_sorted[rank] = bt;
-            cb_chunk[rank] = (uint32_t)tid;
-        }
-        if (tid == 0) s_i = 0;
-        __syncthreads();
-        if (tid < nch && n_c) atomicAdd(&s_i, 1);
-        __syncthreads();
-        const int nblk = s_i;
         const unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand;
         for (int i = tid; i < nU; i += kRT) {
-            int lo = 0, hi = nblk - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (cb_sorted[mid] <= (uint32_t)i) lo = mid; else hi = mid - 1;
-            }
-            const uint32_t c = cb_chunk[lo];
             const unsigned long long e = ub[i];
-            const uint32_t dst = cpre[c] + ((uint32_t)i - cb_sorted[lo]);
-            cand[dst] = e;
-            wgt[dst] = weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
+            cand[i] = e;
+            wgt[i] = weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
         }
         __syncthreads();
         const Cut cut = list_cut(cand, wgt, nU, srow, ri.L, klo, khi, target, m, s, hmb, hcb, scan_sh, &s_n, &s_S,
@@ -767,6 +779,9 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
     const RowState st = ws.st[ri.lrow];
+    if (chunk >= ri.nch) return;
+    const int jbase = chunk * kChunk;
+    if (chunk > 0 && st.mode == 1 && jbase >= st.count) return;   // nothing of this row here
     int64_t rbase;
     if (ROWPTR) {
         __shared__ unsigned long long red[8];
@@ -794,9 +809,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
     } else {
         rbase = out.row_ptr[ri.row];
     }
-    if (chunk >= ri.nch) return;
     if (*out.status != 0) return;
-    const int jbase = chunk * kChunk;
     if (st.mode == 0) {
         for (int k = tid; k < kChunk && jbase + k < ri.L; k += 256) out.idx[rbase + jbase + k] = jbase + k;
         return;
