@@ -362,16 +362,21 @@ def main():
             ev[4].record()
 
     # The local heads do not depend on the retrieval heads' selection: they run
-    # on a second stream, forked from and joined back into the main stream.
+    # on a second stream, forked from the main stream once the selection's pass
+    # over the indexer keys is done (so the two bandwidth-bound passes do not
+    # share HBM, and the window overlaps the latency-bound rest of the
+    # selection and the sparse attention), and joined back at the end.
     side = torch.cuda.Stream()
 
     def step_overlap(I):
         main = torch.cuda.current_stream()
+        sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
+        rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"])
+        rtp.topp_select_begin(*sel_args)
         side.wait_stream(main)
         with torch.cuda.stream(side):
             rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side)
-        rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"])
-        rtp.topp_select(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
+        rtp.topp_select_end(*sel_args)
         rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"])
         main.wait_stream(side)
 

@@ -167,6 +167,27 @@ rtp_status rtp_topp_select(const rtp_layer *layer, const rtp_cache *cache, const
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * rtp_topp_select in two phases, for callers that overlap other work with the
+ * latency-bound second phase (e.g. the local heads' window attention on a
+ * second stream, started once _begin's work on `stream` is done).
+ *   _begin: q_low, the indexer scores and their per-chunk statistics (the pass
+ *           over the indexer keys) into the workspace;
+ *   _end:   the cut and the selected sets, from that workspace.
+ * Both take the arguments of rtp_topp_select and must get the same ones, on
+ * the same stream, _begin first; the workspace must not be touched in
+ * between.  Together they launch exactly the kernels of rtp_topp_select and
+ * give the same result.  When the rows do not fit one workspace pass (or for
+ * bf16 RTP_CHUNK queries) _begin launches nothing and _end does all the work.
+ * Errors as for rtp_topp_select.
+ */
+rtp_status rtp_topp_select_begin(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                                 const void *w_q, const float *top_p, const rtp_sel *sel,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+rtp_status rtp_topp_select_end(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                               const void *w_q, const float *top_p, const rtp_sel *sel,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * a2-a3 only, for inspection: q_low (bf16 [rows][16]) and the fp32 indexer
  * scores [rows][score_ld] (entries beyond a row's pos are not written).
  * score_ld >= max position + 1 of the call.

@@ -24,7 +24,8 @@ RTP_MAX_RET = 64
 ENTRY_POINTS = (
     "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_topp_select_workspace",
     "rtp_topp_select_workspace_min",
-    "rtp_topp_select", "rtp_indexer_scores", "rtp_sparse_attn_workspace",
+    "rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end", "rtp_indexer_scores",
+    "rtp_sparse_attn_workspace",
     "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_window_attn_workspace",
     "rtp_dense_attn_workspace", "rtp_window_attn", "rtp_dense_attn",
 )
@@ -82,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_topp_select_workspace": ([pl, pc, pq], S),
         "rtp_topp_select_workspace_min": ([pl, pc, pq], S),
         "rtp_topp_select": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
+        "rtp_topp_select_begin": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
+        "rtp_topp_select_end": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
         "rtp_indexer_scores": ([pl, pc, pq, P, P, P, i64, P, S, P], ctypes.c_int),
         "rtp_sparse_attn_workspace": ([pl, pc, pq, i64], S),
         "rtp_sparse_attn_decode": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
@@ -172,6 +175,20 @@ def topp_select(layer, cache, query, w_q, top_p, sel, ws, stream=None):
     _check(load().rtp_topp_select(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
                                   _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _ptr(ws),
                                   0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def topp_select_begin(layer, cache, query, w_q, top_p, sel, ws, stream=None):
+    """First phase of topp_select (the pass over the indexer keys); same arguments."""
+    _check(load().rtp_topp_select_begin(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
+                                        _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def topp_select_end(layer, cache, query, w_q, top_p, sel, ws, stream=None):
+    """Second phase of topp_select (cut and selected sets); same arguments as the first."""
+    _check(load().rtp_topp_select_end(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
+                                      _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _ptr(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def indexer_scores(layer, cache, query, w_q, q_low, scores, stream=None):

@@ -283,9 +283,11 @@ size_t rtp_topp_select_workspace_min(const rtp_layer* layer, const rtp_cache* ca
     return plan_select(layer, cache, query).total;
 }
 
-rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
-                           const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+// phase: 0 the whole selection, 1 the scoring pass of the first row group
+// (when every row fits one group), 2 the rest.
+static rtp_status topp_select_phase(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                    const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
+                                    size_t workspace_bytes, void* stream, int phase) {
     rtp_status s = check_all(layer, cache, query);
     if (s) return s;
     if (!w_q || !top_p) return fail(RTP_EINVAL, "NULL w_q / top_p");
@@ -298,6 +300,7 @@ rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const
                                                          query->pos0 + query->n_tok);
         if (!workspace || workspace_bytes < need)
             return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+        if (phase == 1) return ok();
         return hip_status(rtp::launch_chunk_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p,
                                                    workspace, workspace_bytes, out, (hipStream_t)stream),
                           "chunk select launch");
@@ -306,13 +309,39 @@ rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const
     if (!workspace || workspace_bytes < p.total)
         return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, p.total);
     rtp::SelWs w = sel_ws(p, (char*)workspace);
+    const bool one_group = p.group_rows >= p.rows_total;
     for (int row0 = 0; row0 < p.rows_total; row0 += p.group_rows) {
         w.rows = std::min(p.group_rows, p.rows_total - row0);
+        int stage = rtp::kSelAll;
+        if (phase == 1) {
+            if (!one_group) break;
+            stage = rtp::kSelScorePass;
+        } else if (phase == 2 && one_group) {
+            stage = rtp::kSelFinish;
+        }
         hipError_t e = rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p, row0, w, out,
-                                          p.rows_total, layer->dtype, 0, (hipStream_t)stream);
+                                          p.rows_total, layer->dtype, stage, (hipStream_t)stream);
         if (e != hipSuccess) return hip_status(e, "top-p select launch");
     }
     return ok();
+}
+
+rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                           const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 0);
+}
+
+rtp_status rtp_topp_select_begin(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                 const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 1);
+}
+
+rtp_status rtp_topp_select_end(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                               const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 2);
 }
 
 rtp_status rtp_indexer_scores(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
@@ -336,7 +365,7 @@ rtp_status rtp_indexer_scores(const rtp_layer* layer, const rtp_cache* cache, co
     rtp::SelOut out{nullptr, nullptr, 0, nullptr};
     const rtp::Geo g = make_geo(layer, cache, query);
     return hip_status(rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, nullptr, 0, w, out,
-                                         p.rows_total, layer->dtype, 1, (hipStream_t)stream),
+                                         p.rows_total, layer->dtype, rtp::kSelScoresOnly, (hipStream_t)stream),
                       "indexer score launch");
 }
 

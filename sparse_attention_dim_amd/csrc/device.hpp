@@ -123,7 +123,7 @@ __device__ __forceinline__ WeightBin weight_bin(float d, float m, float s) {
 
 template <int NT>
 __device__ unsigned long long block_excl_scan_u64(unsigned long long v, unsigned long long* total,
-                                                  unsigned long long* sh /* NT/64 + 1 */) {
+                                                  unsigned long long* sh /* NT/64 */) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     unsigned long long x = v;
 #pragma unroll
@@ -133,20 +133,17 @@ __device__ unsigned long long block_excl_scan_u64(unsigned long long v, unsigned
     }
     if (lane == 63) sh[wid] = x;
     __syncthreads();
-    if (threadIdx.x == 0) {
-        unsigned long long run = 0;
-        for (int w = 0; w < NT / 64; ++w) {
-            unsigned long long t = sh[w];
-            sh[w] = run;
-            run += t;
-        }
-        sh[NT / 64] = run;
+    // every thread sums the wave totals itself (broadcast LDS reads)
+    unsigned long long before = 0ull, all = 0ull;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        const unsigned long long t = sh[w];
+        before += w < wid ? t : 0ull;
+        all += t;
     }
+    *total = all;
     __syncthreads();
-    unsigned long long r = sh[wid] + x - v;
-    *total = sh[NT / 64];
-    __syncthreads();
-    return r;
+    return before + x - v;
 }
 
 template <int NT>

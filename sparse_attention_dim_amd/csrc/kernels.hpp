@@ -79,11 +79,16 @@ hipError_t launch_indexer_append(const Geo& g, const void* k, void* k_low, const
                                  const int32_t* seq_id, const int32_t* pos, int n, int dtype,
                                  hipStream_t s);
 
-// Selection of rows [row0, row0 + ws.rows) of the call.  `stage` = 1 runs only
-// the projection and scoring (for rtp_indexer_scores).
+// Selection of rows [row0, row0 + ws.rows) of the call, all of it or one stage.
+enum SelStage {
+    kSelAll = 0,                  // scoring pass with statistics, then gather, cut, emit
+    kSelScoresOnly = 1,           // projection and scores only (rtp_indexer_scores)
+    kSelScorePass = 2,            // the first part of kSelAll
+    kSelFinish = 3,               // the rest of kSelAll
+};
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
-                         int total_rows, int dtype, int scores_only, hipStream_t s);
+                         int total_rows, int dtype, int stage, hipStream_t s);
 
 // Split-K partial attention of retrieval rows over their selected sets and the combine.
 struct AttnWs {

@@ -803,7 +803,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
         const int64_t total = carry + (int64_t)(red[4] + red[5] + red[6] + red[7]);
         if (chunk == 0 && tid == 0) out.row_ptr[ri.row + 1] = rbase + st.count;
         if (total > out.capacity) {
-            if (chunk == 0 && tid == 0 && ri.lrow == 0) *out.status = 1;
+            if (chunk == 0 && tid == 0 && ri.lrow == 0 && *out.status == 0) *out.status = 1;
             return;
         }
     } else {
@@ -852,23 +852,26 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
 
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
-                         int total_rows, int dtype, int scores_only, hipStream_t s) {
+                         int total_rows, int dtype, int stage, hipStream_t s) {
     (void)total_rows;
     const dim3 grid(ws.nchunk, ws.rows);
     const bf16_t* kl = (const bf16_t*)k_low;
-    if (dtype == 0 && scores_only)
-        hipLaunchKernelGGL((k_sel_score<float, 0>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q, kl,
-                           row0, ws, out);
-    else if (dtype == 0)
-        hipLaunchKernelGGL((k_sel_score<float, 1>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q, kl,
-                           row0, ws, out);
-    else if (scores_only)
-        hipLaunchKernelGGL((k_sel_score<bf16_t, 0>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
-                           (const bf16_t*)w_q, kl, row0, ws, out);
-    else
-        hipLaunchKernelGGL((k_sel_score<bf16_t, 1>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
-                           (const bf16_t*)w_q, kl, row0, ws, out);
-    if (scores_only) return hipGetLastError();
+    const bool scores_only = stage == kSelScoresOnly;
+    if (stage != kSelFinish) {
+        if (dtype == 0 && scores_only)
+            hipLaunchKernelGGL((k_sel_score<float, 0>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q,
+                               kl, row0, ws, out);
+        else if (dtype == 0)
+            hipLaunchKernelGGL((k_sel_score<float, 1>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q,
+                               kl, row0, ws, out);
+        else if (scores_only)
+            hipLaunchKernelGGL((k_sel_score<bf16_t, 0>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
+                               (const bf16_t*)w_q, kl, row0, ws, out);
+        else
+            hipLaunchKernelGGL((k_sel_score<bf16_t, 1>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
+                               (const bf16_t*)w_q, kl, row0, ws, out);
+    }
+    if (scores_only || stage == kSelScorePass) return hipGetLastError();
     hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, top_p, row0, ws);
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
     if (ws.rows <= kRowsInEmit) {

@@ -56,7 +56,7 @@ class Dev:
     def rows(self) -> int:
         return self.w.n_tok * self.w.n_ret
 
-    def select(self, capacity: int | None = None, ws_bytes: int | None = None):
+    def select(self, capacity: int | None = None, ws_bytes: int | None = None, phased: bool = False):
         w = self.w
         if capacity is None:
             capacity = sum(min(w.row_pos(t) + 1, 1 << 30) for t in range(w.n_tok)) * w.n_ret
@@ -67,7 +67,22 @@ class Dev:
         if ws_bytes is None:
             ws_bytes = rtp.topp_select_workspace(self.layer, self.cache, self.query)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-        rtp.topp_select(self.layer, self.cache, self.query, self.w_q, self.top_p, self.sel, ws)
+        if phased:
+            # the two phases, with the local heads' window attention on a second
+            # stream between them (started once the first phase is done)
+            args = (self.layer, self.cache, self.query, self.w_q, self.top_p, self.sel, ws)
+            main = torch.cuda.current_stream()
+            side = torch.cuda.Stream()
+            wsw = torch.empty(rtp.window_attn_workspace(self.layer, self.cache, self.query), dtype=torch.uint8,
+                              device="cuda")
+            rtp.topp_select_begin(*args)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                rtp.window_attn(self.layer, self.cache, self.query, self.out, wsw, stream=side)
+            rtp.topp_select_end(*args)
+            main.wait_stream(side)
+        else:
+            rtp.topp_select(self.layer, self.cache, self.query, self.w_q, self.top_p, self.sel, ws)
         torch.cuda.synchronize()
         del ws
         return self.sets()

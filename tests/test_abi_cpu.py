@@ -79,10 +79,10 @@ def _window(layer, cache, query, ws_bytes=1 << 30):
                                ws_bytes, None)
 
 
-def _select(layer, cache, query, sel, ws_bytes=1 << 40):
+def _select(layer, cache, query, sel, ws_bytes=1 << 40, fn="rtp_topp_select"):
     lib = rtp.load()
-    return lib.rtp_topp_select(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), FAKE, FAKE,
-                               ctypes.byref(sel), FAKE, ws_bytes, None)
+    return getattr(lib, fn)(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), FAKE, FAKE,
+                            ctypes.byref(sel), FAKE, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -128,13 +128,16 @@ def test_workspace_too_small():
     assert _select(L, C, Q, _sel(), ws_bytes=sel_need - 1) == rtp.RTP_EWORKSPACE
 
 
-def test_select_checks():
+@pytest.mark.parametrize("fn", ["rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end"])
+def test_select_checks(fn):
     L, C, Q = _layer(), _cache(), _query()
     bad = _sel()
     bad.status = None
-    assert _select(L, C, Q, bad) == rtp.RTP_EINVAL
+    assert _select(L, C, Q, bad, fn=fn) == rtp.RTP_EINVAL
     bad = _sel(capacity=-1)
-    assert _select(L, C, Q, bad) == rtp.RTP_EINVAL
+    assert _select(L, C, Q, bad, fn=fn) == rtp.RTP_EINVAL
+    sel_need = rtp.load().rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    assert _select(L, C, Q, _sel(), ws_bytes=sel_need - 1, fn=fn) == rtp.RTP_EWORKSPACE
 
 
 def test_sparse_entry_points_check_query_kind():

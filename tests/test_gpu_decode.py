@@ -128,6 +128,17 @@ def test_deterministic(dev):
     assert torch.equal(o1, dev.out)
 
 
+def test_two_phase_select_equals_single_call(dev):
+    """topp_select_begin / _end with window attention on a second stream in
+    between: the same row pointers and sets as one topp_select call."""
+    say("[gpu] two-phase select", dev.w.name)
+    _, rp1, s1 = dev.select()
+    _, rp2, s2 = dev.select(phased=True)
+    np.testing.assert_array_equal(rp1, rp2)
+    for a, b in zip(s1, s2):
+        np.testing.assert_array_equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------

@@ -68,6 +68,15 @@ def test_selection_matches_oracle(dev, orc):
     assert exact >= len(orc["rows"]) - 2
 
 
+def test_two_phase_select_equals_single_call(dev):
+    say("[gpu] prefill two-phase select", dev.w.name)
+    _, rp1, s1 = dev.select()
+    _, rp2, s2 = dev.select(phased=True)
+    np.testing.assert_array_equal(rp1, rp2)
+    for a, b in zip(s1, s2):
+        np.testing.assert_array_equal(a, b)
+
+
 @pytest.mark.parametrize("frac", [0.0, 0.01])
 def test_selection_radix_level_path(dev, orc, frac):
     # a workspace below the recommended size: the rows whose candidate set does
