@@ -365,20 +365,39 @@ def main():
     # on a second stream, forked from the main stream once the selection's pass
     # over the indexer keys is done (so the two bandwidth-bound passes do not
     # share HBM, and the window overlaps the latency-bound rest of the
-    # selection and the sparse attention), and joined back at the end.
+    # selection and the sparse attention), and joined back at the end.  The
+    # library calls are prepared once per layer instance and stream (their
+    # arguments marshalled once), so the host enqueues a step faster than the
+    # GPU runs it.
     side = torch.cuda.Stream()
 
-    def step_overlap(I):
-        main = torch.cuda.current_stream()
+    def make_step(I, main):
         sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
-        rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"])
-        rtp.topp_select_begin(*sel_args)
-        side.wait_stream(main)
-        with torch.cuda.stream(side):
-            rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side)
-        rtp.topp_select_end(*sel_args)
-        rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"])
-        main.wait_stream(side)
+        append = rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"], stream=main, prepare=True)
+        begin = rtp.topp_select_begin(*sel_args, stream=main, prepare=True)
+        end = rtp.topp_select_end(*sel_args, stream=main, prepare=True)
+        sparse = rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"], stream=main,
+                                        prepare=True)
+        window = rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side, prepare=True)
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+
+        def run():
+            append()
+            begin()
+            fork.record(main)
+            side.wait_event(fork)
+            window()
+            end()
+            sparse()
+            join.record(side)
+            main.wait_event(join)
+        return run
+
+    main_stream = torch.cuda.current_stream()
+    steps_overlap = [make_step(I, main_stream) for I in inst]
+
+    def step_overlap(I):
+        steps_overlap[inst.index(I)]()
 
     for s in range(args.warmup):
         step(inst[s % len(inst)])
@@ -404,14 +423,14 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / args.steps
 
-    eager_ms = timed(lambda s: step_overlap(inst[s % len(inst)]))
+    eager_ms = timed(lambda s: steps_overlap[s % len(inst)]())
 
     # one HIP graph per layer instance, replayed round-robin
     graphs = []
     for I in inst:
         gph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gph):
-            step_overlap(I)
+            make_step(I, torch.cuda.current_stream())()
         graphs.append(gph)
     for s in range(len(graphs) * 2):
         graphs[s % len(graphs)].replay()

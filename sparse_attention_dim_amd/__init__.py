@@ -107,6 +107,38 @@ def _check(code: int) -> None:
         raise RtpError(code, load().rtp_last_error().decode())
 
 
+class Call:
+    """One library call with its arguments marshalled once: struct references,
+    device pointer values, sizes and the stream handle.  Calling the object
+    issues the call again with the same arguments (on the stream fixed when it
+    was made), costing one ctypes call; errors raise RtpError.  The object keeps
+    the argument structs alive; the tensors behind the pointers must outlive it."""
+
+    __slots__ = ("fn", "args", "keep")
+
+    def __init__(self, name: str, args: tuple, keep: tuple):
+        self.fn = getattr(load(), name)
+        self.args = args
+        self.keep = keep
+
+    def __call__(self) -> None:
+        code = self.fn(*self.args)
+        if code != RTP_OK:
+            _check(code)
+
+
+def _run(name: str, args: tuple, keep: tuple, prepare: bool):
+    c = Call(name, args, keep)
+    if prepare:
+        return c
+    c()
+    return None
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
@@ -158,9 +190,9 @@ def version() -> int:
     return load().rtp_version()
 
 
-def indexer_append(layer, cache, w_k, seq_id, pos, stream=None):
-    _check(load().rtp_indexer_append(ctypes.byref(layer), ctypes.byref(cache), _ptr(w_k),
-                                     _ptr(seq_id), _ptr(pos), seq_id.numel(), _stream(stream)))
+def indexer_append(layer, cache, w_k, seq_id, pos, stream=None, prepare=False):
+    return _run("rtp_indexer_append", (ctypes.byref(layer), ctypes.byref(cache), _ptr(w_k), _ptr(seq_id),
+                                       _ptr(pos), seq_id.numel(), _stream(stream)), (layer, cache), prepare)
 
 
 def topp_select_workspace(layer, cache, query) -> int:
@@ -171,24 +203,24 @@ def topp_select_workspace_min(layer, cache, query) -> int:
     return load().rtp_topp_select_workspace_min(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query))
 
 
-def topp_select(layer, cache, query, w_q, top_p, sel, ws, stream=None):
-    _check(load().rtp_topp_select(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                  _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _ptr(ws),
-                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+def topp_select(layer, cache, query, w_q, top_p, sel, ws, stream=None, prepare=False):
+    return _run("rtp_topp_select", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                            _ptr(top_p), ctypes.byref(sel), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
 
 
-def topp_select_begin(layer, cache, query, w_q, top_p, sel, ws, stream=None):
+def topp_select_begin(layer, cache, query, w_q, top_p, sel, ws, stream=None, prepare=False):
     """First phase of topp_select (the pass over the indexer keys); same arguments."""
-    _check(load().rtp_topp_select_begin(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                        _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _ptr(ws),
-                                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return _run("rtp_topp_select_begin", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                            _ptr(top_p), ctypes.byref(sel), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
 
 
-def topp_select_end(layer, cache, query, w_q, top_p, sel, ws, stream=None):
+def topp_select_end(layer, cache, query, w_q, top_p, sel, ws, stream=None, prepare=False):
     """Second phase of topp_select (cut and selected sets); same arguments as the first."""
-    _check(load().rtp_topp_select_end(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                      _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _ptr(ws),
-                                      0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+    return _run("rtp_topp_select_end", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                            _ptr(top_p), ctypes.byref(sel), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
 
 
 def indexer_scores(layer, cache, query, w_q, q_low, scores, stream=None):
@@ -202,18 +234,16 @@ def sparse_attn_workspace(layer, cache, query, capacity: int) -> int:
                                             ctypes.byref(query), capacity)
 
 
-def sparse_attn_decode(layer, cache, query, sel, out, ws, stream=None):
-    _check(load().rtp_sparse_attn_decode(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                         ctypes.byref(sel), _ptr(out), _ptr(ws),
-                                         0 if ws is None else ws.numel() * ws.element_size(),
-                                         _stream(stream)))
+def sparse_attn_decode(layer, cache, query, sel, out, ws, stream=None, prepare=False):
+    return _run("rtp_sparse_attn_decode", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
+                                           ctypes.byref(sel), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
 
 
-def sparse_attn_prefill(layer, cache, query, sel, out, ws, stream=None):
-    _check(load().rtp_sparse_attn_prefill(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                          ctypes.byref(sel), _ptr(out), _ptr(ws),
-                                          0 if ws is None else ws.numel() * ws.element_size(),
-                                          _stream(stream)))
+def sparse_attn_prefill(layer, cache, query, sel, out, ws, stream=None, prepare=False):
+    return _run("rtp_sparse_attn_prefill", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
+                                            ctypes.byref(sel), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
 
 
 def window_attn_workspace(layer, cache, query) -> int:
@@ -224,13 +254,11 @@ def dense_attn_workspace(layer, cache, query) -> int:
     return load().rtp_dense_attn_workspace(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query))
 
 
-def window_attn(layer, cache, query, out, ws, stream=None):
-    _check(load().rtp_window_attn(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(out),
-                                  _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                  _stream(stream)))
+def window_attn(layer, cache, query, out, ws, stream=None, prepare=False):
+    return _run("rtp_window_attn", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(out),
+                                    _ptr(ws), _nbytes(ws), _stream(stream)), (layer, cache, query), prepare)
 
 
-def dense_attn(layer, cache, query, out, ws, stream=None):
-    _check(load().rtp_dense_attn(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(out),
-                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
-                                 _stream(stream)))
+def dense_attn(layer, cache, query, out, ws, stream=None, prepare=False):
+    return _run("rtp_dense_attn", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(out),
+                                   _ptr(ws), _nbytes(ws), _stream(stream)), (layer, cache, query), prepare)

@@ -75,12 +75,18 @@ class Dev:
             side = torch.cuda.Stream()
             wsw = torch.empty(rtp.window_attn_workspace(self.layer, self.cache, self.query), dtype=torch.uint8,
                               device="cuda")
-            rtp.topp_select_begin(*args)
-            side.wait_stream(main)
-            with torch.cuda.stream(side):
-                rtp.window_attn(self.layer, self.cache, self.query, self.out, wsw, stream=side)
-            rtp.topp_select_end(*args)
-            main.wait_stream(side)
+            # prepared calls (arguments marshalled once), as a serving loop would
+            begin = rtp.topp_select_begin(*args, stream=main, prepare=True)
+            end = rtp.topp_select_end(*args, stream=main, prepare=True)
+            window = rtp.window_attn(self.layer, self.cache, self.query, self.out, wsw, stream=side, prepare=True)
+            fork, join = torch.cuda.Event(), torch.cuda.Event()
+            begin()
+            fork.record(main)
+            side.wait_event(fork)
+            window()
+            end()
+            join.record(side)
+            main.wait_event(join)
         else:
             rtp.topp_select(self.layer, self.cache, self.query, self.w_q, self.top_p, self.sel, ws)
         torch.cuda.synchronize()

@@ -140,6 +140,21 @@ def test_select_checks(fn):
     assert _select(L, C, Q, _sel(), ws_bytes=sel_need - 1, fn=fn) == rtp.RTP_EWORKSPACE
 
 
+def test_prepared_call_reports_the_same_errors():
+    # a prepared call checks its arguments on every call, like the direct one
+    L, C, Q = _layer(), _cache(), _query()
+    bad = _sel()
+    bad.status = None
+    call = rtp.topp_select(L, C, Q, None, None, bad, None, stream=0, prepare=True)
+    assert isinstance(call, rtp.Call)
+    for _ in range(2):
+        with pytest.raises(rtp.RtpError) as e:
+            call()
+        assert e.value.code == rtp.RTP_EINVAL
+    with pytest.raises(rtp.RtpError):
+        rtp.topp_select(L, C, Q, None, None, bad, None, stream=0)
+
+
 def test_sparse_entry_points_check_query_kind():
     lib = rtp.load()
     L, C = _layer(), _cache()
