@@ -51,10 +51,11 @@ constexpr int kNB = 64;          // radix buckets per level
 constexpr int kNBP = kNB + 1;
 constexpr int kCapC = 128;       // candidates of one cut bucket sorted in LDS
 constexpr int kSmallU = 8192;    // U sorted by the per-row resolve kernel
-constexpr int kSegMax = 16384;   // largest U given a pool segment (sorted by the large-row kernel)
+constexpr int kSegMax = 16384;   // largest segment (U plus padding), sorted by the large-row kernel
+constexpr int kSegBlk = 16;      // segment slots reserved at a time by one lane of the third pass
+constexpr int kSegPad = 8 * kSegBlk;   // 8 writers per row (4 waves x 2 halves): their last blocks' slack
 constexpr int kPoolPerRow = 4096;   // pool entries per row in the recommended workspace
 constexpr int kNormKeys = 4096;  // keys per block of the key-norm pre-pass
-constexpr int kQ = 64;           // exact-work queue length per wave
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr unsigned long long kNoSeg = ~0ull;
 
@@ -73,10 +74,11 @@ struct CRow {
     int mode;
     int u_end;       // last P2 bin of U
     int n_tie;       // keys with d == T taken, lowest indices first (kLevel)
-    int count;       // selected keys (kLevel) or U entries in the segment (kBuf)
+    int count;       // selected keys (kLevel) or used slots of the segment (kBuf)
     int bad;         // certification failed
-    unsigned long long target;   // fixed-point mass to reach
+    unsigned long long target;   // fixed-point mass to reach (kLevel)
     unsigned long long seg;      // pool offset of the row's segment (kBuf)
+    unsigned long long light;    // approximate fixed-point mass of the keys outside U (kBuf)
 };
 
 // orders this wave's LDS writes before its following LDS reads (other lanes)
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     __shared__ float qs[kTR][16];                        // q_low as floats
     __shared__ uint32_t rmax[kTR];                       // ordered keys of the row maxima
     __shared__ uint32_t kmax_bits;
-    __shared__ uint32_t cand_n[kTR], ucnt[kTR];
+    __shared__ uint32_t cand_n[kTR], ucnt[kTR], ureal[kTR];
     __shared__ unsigned long long zu[kTR];               // exact mass of U
     __shared__ float r_mp[kTR], r_delta[kTR], r_mpB[kTR], r_T[kTR], r_edge[kTR], r_ethr[kTR];
     __shared__ uint32_t r_ucount[kTR];
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     __shared__ uint32_t r_klo[kTR], r_khi[kTR], r_shift[kTR], r_cnthi[kTR];
     __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_light[kTR];
     __shared__ int s_any;
-    __shared__ uint32_t qpair[4][kQ];                    // per-wave exact-work queue: (row << 26) | key
+    __shared__ uint4 ktile[4][32][2];                    // per wave: the 32 keys of the current tile
 
     // ---- q_low of the 32 rows: fixed-order fp32 chain over d, bf16 rounding
     for (int x = tid; x < g.D * 16; x += 256) wq[x] = bf2f(w_q[(size_t)r * g.D * 16 + x]);
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         zu[tid] = 0ull;
         cand_n[tid] = 0u;
         ucnt[tid] = 0u;
+        ureal[tid] = 0u;
         r_target[tid] = 0ull;
     }
     if (tid == 0) kmax_bits = 0u;
@@ -399,15 +402,16 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         if (tid == 0) {
             unsigned long long tot = 0;
             for (int row = 0; row < n_valid; ++row)
-                if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)kSegMax) tot += r_ucount[row];
+                if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad))
+                    tot += r_ucount[row] + kSegPad;
             if (tot) {
                 const unsigned long long base = atomicAdd(pool_ctr, tot);
                 if (base + tot <= pool_cap) {
                     unsigned long long off = base;
                     for (int row = 0; row < n_valid; ++row)
-                        if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)kSegMax) {
+                        if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad)) {
                             r_seg[row] = off;
-                            off += r_ucount[row];
+                            off += r_ucount[row] + kSegPad;
                         }
                 }
             }
@@ -439,48 +443,29 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         __syncthreads();
         if (!s_any) break;
 
-        int qbase = 0;                                    // wave-uniform queue fill
-        // process the queued pairs of this wave
-        auto drain = [&](int n) {
-            wave_lds_sync();
-            if (lane < n) {
-                const uint32_t e = qpair[wid][lane];
-                const int row = (int)(e >> 26), key = (int)(e & 0x3FFFFFFu);
-                const int page = bt[key >> 8];
-                const uint4* kp = reinterpret_cast<const uint4*>(
-                    k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
-                const float d = exact_score(qs[row], kp[0], kp[1]);
-                const uint32_t kd = score_key(d);
-                if (r_gather[row]) {
-                    if (kd >= r_klo[row] && kd <= r_khi[row]) {
-                        const uint32_t slot = atomicAdd(&cand_n[row], 1u);
-                        if (slot < (uint32_t)kCapC)
-                            cand[row][slot] = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
-                    }
-                } else {
-                    const unsigned long long w = weight_bin(d, r_mp[row], s).w;
-                    const unsigned long long sg = r_seg[row];
-                    if (level == 0) {
-                        atomicAdd(&zu[row], w);
-                        const uint32_t slot = atomicAdd(&ucnt[row], 1u);
-                        if (sg != kNoSeg && slot < r_ucount[row])
-                            pool[sg + slot] = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
-                    }
-                    if (sg == kNoSeg && kd >= r_klo[row] && kd <= r_khi[row]) {
-                        const uint32_t bk = min((r_khi[row] - kd) >> r_shift[row], (uint32_t)(kNB - 1));
-                        atomicAdd(&hm[row][bk], w);
-                        atomicAdd(&hc[row][bk], 1u);
-                    }
-                    // above the range: counted by earlier levels; below: ranks below the cut
-                }
-            }
-            wave_lds_sync();
-        };
+        // Each lane owns one row (lr).  A row with a pool segment only records
+        // the keys of U at level 0 (index per slot; slots reserved kSegBlk at a
+        // time, the slack of the last block marked empty); its exact scores
+        // are formed by the resolve pass.  Other rows score their own pairs
+        // here: the row's state sits in registers, the tile's keys are copied
+        // to LDS when some lane of the wave needs an exact score, U's mass
+        // accumulates per lane.
         const bool active = row_ok && !r_done[lr];
         const float e_thr = r_ethr[lr];
-        const bool ranged = active && (r_gather[lr] || level > 0);
+        const int gath = r_gather[lr];
+        const bool ranged = active && (gath || level > 0);
         const float lo = ranged ? key_score(r_klo[lr]) : 0.0f, hi = ranged ? key_score(r_khi[lr]) : 0.0f;
         const float dl = r_delta[lr];
+        const uint32_t klo = r_klo[lr], khi = r_khi[lr], shift = r_shift[lr];
+        const unsigned long long sg = r_seg[lr];
+        const bool fast = level == 0 && !gath && sg != kNoSeg;
+        const uint32_t scap = r_ucount[lr] + kSegPad;
+        const float mp_row = r_mp[lr];
+        float qv[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) qv[c] = qs[lr][c];
+        unsigned long long zacc = 0ull;
+        uint32_t bp = 0u, be = 0u, nreal = 0u;            // the lane's reserved block [bp, be)
         tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
             // which of this lane's pairs need an exact score
@@ -494,44 +479,63 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 need |= (uint32_t)in << i;
             }
             if (__ballot(need != 0u) == 0ull) return;
-            // append to the wave queue, draining when full
-            const int cnt = __popc(need);
-            int pre = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(pre, o);
-                if (lane >= o) pre += y;
-            }
-            const int total = __shfl(pre, 63);
-            pre -= cnt;
-            int base = qbase;
-            if (base + total > kQ) {
-                drain(base);
-                base = 0;
-            }
-            // total <= 64 * 16 may exceed the queue: spill in rounds of kQ
-            int done = 0;
-            while (done < total) {
-                const int take = min(kQ - base, total - done);
-                uint32_t m = need;
-                int ord = pre;
-                while (m) {
-                    const int i = __ffs(m) - 1;
-                    m &= m - 1;
-                    if (ord >= done && ord < done + take)
-                        qpair[wid][base + ord - done] = ((uint32_t)lr << 26) | (uint32_t)key_of(it, i);
-                    ++ord;
-                }
-                done += take;
-                base += take;
-                if (base == kQ) {
-                    drain(kQ);
-                    base = 0;
+            if (fast) {
+                while (need) {
+                    const int i = __ffs(need) - 1;
+                    need &= need - 1u;
+                    if (bp == be) {
+                        bp = atomicAdd(&ucnt[lr], (uint32_t)kSegBlk);
+                        be = bp + kSegBlk;
+                    }
+                    if (bp < scap) pool[sg + bp] = (unsigned long long)(uint32_t)key_of(it, i);
+                    ++bp;
+                    ++nreal;
                 }
             }
-            qbase = base;
+            const bool stage = __ballot(need != 0u) != 0ull;
+            if (!stage) return;
+            ktile[wid][lr][hh] = cur;                     // key it*32 + lr, dims 8 hh .. 8 hh + 7
+            wave_lds_sync();
+            uint32_t slot = 0u;
+            if (level == 0 && !gath && need) slot = atomicAdd(&ucnt[lr], (uint32_t)__popc(need));
+            while (need) {
+                const int i = __ffs(need) - 1;
+                need &= need - 1u;
+                const int kl = (i >> 2) * 8 + 4 * hh + (i & 3);
+                const int key = it * 32 + kl;
+                const float d = exact_score(qv, ktile[wid][kl][0], ktile[wid][kl][1]);
+                const uint32_t kd = score_key(d);
+                if (gath) {
+                    if (kd >= klo && kd <= khi) {
+                        const uint32_t cs = atomicAdd(&cand_n[lr], 1u);
+                        if (cs < (uint32_t)kCapC)
+                            cand[lr][cs] = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
+                    }
+                } else {
+                    const unsigned long long w = weight_bin(d, mp_row, s).w;
+                    if (level == 0) {
+                        zacc += w;
+                        ++slot;
+                    }
+                    if (kd >= klo && kd <= khi) {
+                        const uint32_t bk = min((khi - kd) >> shift, (uint32_t)(kNB - 1));
+                        atomicAdd(&hm[lr][bk], w);
+                        atomicAdd(&hc[lr][bk], 1u);
+                    }
+                    // above the range: counted by earlier levels; below: ranks below the cut
+                }
+            }
+            wave_lds_sync();                              // the tile's keys are read before the next copy
         });
-        drain(qbase);
+        if (fast) {
+            for (uint32_t x = bp; x < be; ++x)
+                if (x < scap) pool[sg + x] = ~0ull;       // unused slots of the last block
+            if (nreal) atomicAdd(&ureal[lr], nreal);
+        }
+        if (level == 0) {
+            zacc += __shfl_xor(zacc, 32);
+            if (hh == 0 && zacc) atomicAdd(&zu[lr], zacc);
+        }
         __syncthreads();
 
         // per-row step: resolve, narrow, or switch to gathering
@@ -549,7 +553,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 if (level == 0 && r_seg[row] != kNoSeg) {
                     r_mode[row] = kBuf;                  // resolved from its segment
                     r_done[row] = 1;
-                    if (ucnt[row] != r_ucount[row]) r_bad[row] = 1;   // P2 and P3 disagree on U
+                    // P2 and P3 disagree on U, or the slots overflow the segment
+                    if (ureal[row] != r_ucount[row] || ucnt[row] > r_ucount[row] + kSegPad) r_bad[row] = 1;
                 } else if (r_gather[row]) {
                     r_done[row] = 1;                     // final sort of the cut bucket's keys below
                 } else {
@@ -616,6 +621,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             out.n_tie = 0;
             out.count = 0;
             out.target = r_target[row];
+            out.light = r_light[row];
             int bad = r_bad[row];
             if (out.mode == kBuf) {
                 out.count = (int)ucnt[row];
@@ -701,23 +707,62 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Resolve of a row held in a pool segment: sort U by (exact score descending,
-// index ascending), cut at the first rank whose cumulative exact mass reaches
-// the target, certify the cut, sort the selected indices ascending and store
-// them over the segment.  Writes the row's count (-1 if certification
+// Resolve of a row held in a pool segment (the key indices of U, empty slots
+// marked ~0): the exact fixed-order score and exact fixed-point weight of
+// every key of U, the target from U's exact mass plus the approximate mass of
+// the keys outside U, a sort of U by (exact score descending, index
+// ascending), the cut at the first rank whose cumulative exact mass reaches
+// the target, its certification, and the selected indices sorted ascending,
+// stored over the segment.  Writes the row's count (-1 if certification
 // failed).  NT threads, U of up to CAP keys sorted in LDS.
 // ---------------------------------------------------------------------------
 template <int CAP, int NT>
-__device__ void resolve_row(const Geo& g, const CRow& cr, unsigned long long* __restrict__ pool,
-                            int* __restrict__ count_out, unsigned long long* sk, unsigned long long* scan_sh,
-                            int* s_first) {
+__device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t* __restrict__ k_low,
+                            const uint16_t* __restrict__ qlow, const float* __restrict__ top_p,
+                            unsigned long long* __restrict__ pool, int* __restrict__ count_out,
+                            unsigned long long* sk, unsigned long long* scan_sh, int* s_first) {
     const int tid = threadIdx.x;
-    const int n = cr.count;
+    const int slots = cr.count;
+    const float s = g.idx_scale;
     unsigned long long* ub = pool + cr.seg;
+    const int r = row % g.n_ret;
+    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
+    float q16[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) q16[c] = bf2f(qlow[(size_t)row * 16 + c]);
     int N = 64;
-    while (N < n) N <<= 1;
-    for (int i = tid; i < N; i += NT) sk[i] = i < n ? ub[i] : 0ull;
-    __syncthreads();
+    while (N < slots) N <<= 1;
+    // exact scores and weights; empty slots sort last as 0
+    unsigned long long zl = 0ull, nl = 0ull;
+    for (int i = tid; i < N; i += NT) {
+        unsigned long long e = 0ull;
+        if (i < slots) {
+            const unsigned long long v = ub[i];
+            if (v != ~0ull) {
+                const int key = (int)v;
+                const int page = bt[key >> 8];
+                const uint4* kp = reinterpret_cast<const uint4*>(
+                    k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
+                const float d = exact_score(q16, kp[0], kp[1]);
+                zl += weight_bin(d, cr.mp, s).w;
+                ++nl;
+                e = ((unsigned long long)score_key(d) << 32) | (unsigned long long)(~(uint32_t)key);
+            }
+        }
+        sk[i] = e;
+    }
+    unsigned long long zu, n64;
+    block_excl_scan_u64<NT>(zl, &zu, scan_sh);
+    block_excl_scan_u64<NT>(nl, &n64, scan_sh);
+    const int n = (int)n64;
+    unsigned long long target;
+    {
+        const float p = top_p[g.seq];
+        const unsigned long long Z = zu + cr.light;
+        target = (unsigned long long)ceil((double)p * (double)Z);
+        if (target > Z) target = Z;
+        if (target < 1ull) target = 1ull;
+    }
     // bitonic sort, descending
     for (int k = 2; k <= N; k <<= 1)
         for (int j = k >> 1; j > 0; j >>= 1) {
@@ -735,7 +780,6 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, unsigned long long* __
             __syncthreads();
         }
     // exact masses in rank order: each thread a run of consecutive ranks
-    const float s = g.idx_scale;
     const int per = (N + NT - 1) / NT;
     const int r0 = tid * per;
     const int r1 = min(r0 + per, n);
@@ -749,7 +793,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, unsigned long long* __
         unsigned long long run = ex;
         for (int i = r0; i < r1; ++i) {
             run += weight_bin(key_score((uint32_t)(sk[i] >> 32)), cr.mp, s).w;
-            if (run >= cr.target) {
+            if (run >= target) {
                 atomicMin(s_first, i);
                 break;
             }
@@ -801,6 +845,9 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, unsigned long long* __
 // no segment.  grid (rows), 512 threads.
 constexpr int kRT = 512;
 __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restrict__ rows,
+                                                      const bf16_t* __restrict__ k_low,
+                                                      const uint16_t* __restrict__ qlow,
+                                                      const float* __restrict__ top_p,
                                                       unsigned long long* __restrict__ pool,
                                                       int* __restrict__ counts) {
     const int row = blockIdx.x;
@@ -820,13 +867,16 @@ __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restr
     __shared__ unsigned long long sk[kSmallU];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
     __shared__ int s_first;
-    resolve_row<kSmallU, kRT>(g, cr, pool, &counts[row], sk, scan_sh, &s_first);
+    resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, &s_first);
 }
 
 // Rows with U in (kSmallU, kSegMax]: a fixed grid of 1024-thread workgroups
 // walks the rows.
 constexpr int kRTL = 1024;
 __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* __restrict__ rows, int n_rows,
+                                                             const bf16_t* __restrict__ k_low,
+                                                             const uint16_t* __restrict__ qlow,
+                                                             const float* __restrict__ top_p,
                                                              unsigned long long* __restrict__ pool,
                                                              int* __restrict__ counts) {
     __shared__ unsigned long long sk[kSegMax];
@@ -839,7 +889,7 @@ __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* 
             if (threadIdx.x == 0) counts[row] = -1;
             continue;
         }
-        resolve_row<kSegMax, kRTL>(g, cr, pool, &counts[row], sk, scan_sh, &s_first);
+        resolve_row<kSegMax, kRTL>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, &s_first);
     }
 }
 
@@ -1083,9 +1133,10 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
                        (const bf16_t*)k_low, top_p, crow, qlow, knorm, w.nblk, pool, ctr, pool_cap);
-    hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, pool, counts);
-    hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 512)), dim3(kRTL), 0, s, g, crow, rows, pool,
-                       counts);
+    hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, (const bf16_t*)k_low, qlow, top_p,
+                       pool, counts);
+    hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 512)), dim3(kRTL), 0, s, g, crow, rows,
+                       (const bf16_t*)k_low, qlow, top_p, pool, counts);
     hipLaunchKernelGGL(k_csel_rowptr, dim3(1), dim3(1024), 0, s, counts, rows, out.row_ptr, out.capacity,
                        out.status);
     hipLaunchKernelGGL(k_csel_copy, dim3(rows), dim3(256), 0, s, crow, pool, out.row_ptr, out.idx, out.status);
