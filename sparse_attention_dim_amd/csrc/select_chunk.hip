@@ -710,18 +710,31 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 // Resolve of a row held in a pool segment (the key indices of U, empty slots
 // marked ~0): the exact fixed-order score and exact fixed-point weight of
 // every key of U, the target from U's exact mass plus the approximate mass of
-// the keys outside U, a sort of U by (exact score descending, index
-// ascending), the cut at the first rank whose cumulative exact mass reaches
-// the target, its certification, and the selected indices sorted ascending,
-// stored over the segment.  Writes the row's count (-1 if certification
-// failed).  NT threads, U of up to CAP keys sorted in LDS.
+// the keys outside U, the cut by radix selection over U's score keys (levels
+// of kRB buckets with exact masses per bucket, highest scores first; once the
+// cut bucket holds at most 64 keys one wavefront sorts them in registers;
+// ties: lowest indices first), its certification, and the selected indices
+// sorted ascending, stored over the segment.  Writes the row's count (-1 if
+// certification failed).  NT threads, U of up to CAP keys in LDS.
 // ---------------------------------------------------------------------------
+constexpr int kRB = 1024;        // radix buckets per level of the resolve
+
+struct ResolveSmem {
+    unsigned long long hm[kRB];
+    uint32_t hc[kRB];
+    unsigned long long small_v[64], small_w[64];
+    uint32_t kmin, kmax, s_u, tkey;
+    int s_i, ntie, fail;
+    unsigned long long s_S;
+};
+
 template <int CAP, int NT>
 __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t* __restrict__ k_low,
                             const uint16_t* __restrict__ qlow, const float* __restrict__ top_p,
                             unsigned long long* __restrict__ pool, int* __restrict__ count_out,
-                            unsigned long long* sk, unsigned long long* scan_sh, int* s_first) {
-    const int tid = threadIdx.x;
+                            unsigned long long* sk, unsigned long long* scan_sh, ResolveSmem& sm) {
+    constexpr int PER = CAP / NT;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int slots = cr.count;
     const float s = g.idx_scale;
     unsigned long long* ub = pool + cr.seg;
@@ -730,31 +743,42 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     float q16[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) q16[c] = bf2f(qlow[(size_t)row * 16 + c]);
-    int N = 64;
-    while (N < slots) N <<= 1;
-    // exact scores and weights; empty slots sort last as 0
+    if (tid == 0) {
+        sm.kmin = 0xFFFFFFFFu;
+        sm.kmax = 0u;
+        sm.fail = 0;
+    }
+    __syncthreads();
+    // exact scores and weights; slot i of thread tid is tid + x NT; empty -> 0
     unsigned long long zl = 0ull, nl = 0ull;
-    for (int i = tid; i < N; i += NT) {
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    for (int i = tid; i < slots; i += NT) {
         unsigned long long e = 0ull;
-        if (i < slots) {
-            const unsigned long long v = ub[i];
-            if (v != ~0ull) {
-                const int key = (int)v;
-                const int page = bt[key >> 8];
-                const uint4* kp = reinterpret_cast<const uint4*>(
-                    k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
-                const float d = exact_score(q16, kp[0], kp[1]);
-                zl += weight_bin(d, cr.mp, s).w;
-                ++nl;
-                e = ((unsigned long long)score_key(d) << 32) | (unsigned long long)(~(uint32_t)key);
-            }
+        const unsigned long long v = ub[i];
+        if (v != ~0ull) {
+            const int key = (int)v;
+            const int page = bt[key >> 8];
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
+            const float d = exact_score(q16, kp[0], kp[1]);
+            zl += weight_bin(d, cr.mp, s).w;
+            ++nl;
+            const uint32_t kd = score_key(d);
+            kmn = min(kmn, kd);
+            kmx = max(kmx, kd);
+            e = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
         }
         sk[i] = e;
+    }
+    kmx = wave_max_u32(kmx);
+    kmn = ~wave_max_u32(~kmn);
+    if (lane == 0) {
+        atomicMax(&sm.kmax, kmx);
+        atomicMin(&sm.kmin, kmn);
     }
     unsigned long long zu, n64;
     block_excl_scan_u64<NT>(zl, &zu, scan_sh);
     block_excl_scan_u64<NT>(nl, &n64, scan_sh);
-    const int n = (int)n64;
     unsigned long long target;
     {
         const float p = top_p[g.seq];
@@ -763,15 +787,182 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
         if (target > Z) target = Z;
         if (target < 1ull) target = 1ull;
     }
-    // bitonic sort, descending
-    for (int k = 2; k <= N; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < N; i += NT) {
-                const int ixj = i ^ j;
+    const auto wkey = [&](uint32_t key) { return weight_bin(key_score(key), cr.mp, s).w; };
+    // ---- radix cut: Tkey and the number of ties at Tkey taken (lowest indices)
+    uint32_t klo = sm.kmin, khi = sm.kmax;
+    unsigned long long S_hi = 0ull;
+    bool done = n64 == 0ull || zu < target;             // U cannot reach the target: not certified
+    if (done && tid == 0) sm.fail = 1;
+    for (int level = 0; level < 6 && !done; ++level) {
+        const uint32_t span = khi - klo;
+        const int bits = span ? 32 - __clz(span) : 0;
+        const int shift = bits > 10 ? bits - 10 : 0;
+        for (int b = tid; b < kRB; b += NT) {
+            sm.hm[b] = 0ull;
+            sm.hc[b] = 0u;
+        }
+        __syncthreads();
+        for (int i = tid; i < slots; i += NT) {
+            const unsigned long long v = sk[i];
+            if (!v) continue;
+            const uint32_t key = (uint32_t)(v >> 32);
+            if (key < klo || key > khi) continue;
+            const uint32_t bk = (khi - key) >> shift;      // bucket 0 holds the highest keys
+            atomicAdd(&sm.hm[bk], wkey(key));
+            atomicAdd(&sm.hc[bk], 1u);
+        }
+        __syncthreads();
+        constexpr int BPT = kRB / NT;                       // buckets per thread (1 or 2)
+        unsigned long long loc = 0ull;
+#pragma unroll
+        for (int x = 0; x < BPT; ++x) loc += sm.hm[BPT * tid + x];
+        unsigned long long tot;
+        const unsigned long long ex = S_hi + block_excl_scan_u64<NT>(loc, &tot, scan_sh);
+        if (tid == 0) sm.s_i = kRB;
+        __syncthreads();
+        {
+            unsigned long long run = ex;
+#pragma unroll
+            for (int x = 0; x < BPT; ++x) {
+                const int b = BPT * tid + x;
+                run += sm.hm[b];
+                if (run >= target && sm.hc[b]) {
+                    atomicMin(&sm.s_i, b);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        const int bk = sm.s_i;
+        if (bk >= kRB) {                                     // rounding: U does not reach the target
+            if (tid == 0) sm.fail = 1;
+            done = true;
+            break;
+        }
+        if (bk / BPT == tid) {
+            unsigned long long run = ex;
+            for (int b = BPT * tid; b < bk; ++b) run += sm.hm[b];
+            sm.s_S = run;
+            sm.s_u = sm.hc[bk];
+        }
+        __syncthreads();
+        S_hi = sm.s_S;
+        const uint32_t n_b = sm.s_u;
+        const uint32_t nkhi = khi - ((uint32_t)bk << shift);
+        const uint32_t wdt = (1u << shift) - 1u;
+        const uint32_t nklo = (nkhi - klo > wdt) ? nkhi - wdt : klo;
+        klo = nklo;
+        khi = nkhi;
+        __syncthreads();
+        if (n_b <= 64u) {
+            // the bucket's keys into one wavefront, sorted in registers
+            if (tid == 0) sm.s_u = 0u;
+            __syncthreads();
+            for (int i = tid; i < slots; i += NT) {
+                const unsigned long long v = sk[i];
+                if (!v) continue;
+                const uint32_t key = (uint32_t)(v >> 32);
+                if (key < klo || key > khi) continue;
+                const uint32_t slot = atomicAdd(&sm.s_u, 1u);
+                if (slot < 64u) {
+                    sm.small_v[slot] = v;
+                    sm.small_w[slot] = wkey(key);
+                }
+            }
+            __syncthreads();
+            if (tid < 64) {
+                const int nbk = (int)min(sm.s_u, 64u);
+                unsigned long long v = lane < nbk ? sm.small_v[lane] : 0ull;
+                unsigned long long w = lane < nbk ? sm.small_w[lane] : 0ull;
+#pragma unroll
+                for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+                    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+                        const unsigned long long ov = __shfl_xor(v, jj), ow = __shfl_xor(w, jj);
+                        const bool desc = (lane & k) == 0 || k == 64;
+                        const bool lower = (lane & jj) == 0;
+                        const bool take = desc == lower ? ov > v : ov < v;
+                        if (take) {
+                            v = ov;
+                            w = ow;
+                        }
+                    }
+                unsigned long long incl = w;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const unsigned long long y = __shfl_up(incl, o);
+                    if (lane >= o) incl += y;
+                }
+                const unsigned long long reach = __ballot(lane < nbk && S_hi + incl >= target);
+                const int ic = reach ? __ffsll((long long)reach) - 1 : nbk - 1;
+                const uint32_t tk = (uint32_t)(__shfl(v, ic) >> 32);
+                const unsigned long long tie = __ballot(lane <= ic && lane < nbk && (uint32_t)(v >> 32) == tk);
+                if (lane == 0) {
+                    sm.tkey = tk;
+                    sm.ntie = __popcll(tie);
+                    if (!reach) sm.fail = 1;
+                }
+            }
+            __syncthreads();
+            done = true;
+            break;
+        }
+        if (klo == khi) {
+            // one score value with more than 64 keys: its lowest indices first
+            if (tid == 0) {
+                const unsigned long long wT = wkey(klo);
+                const unsigned long long need = target - S_hi;
+                sm.tkey = klo;
+                sm.ntie = (int)min((need + wT - 1ull) / wT, (unsigned long long)n_b);
+            }
+            __syncthreads();
+            done = true;
+            break;
+        }
+    }
+    if (!done && tid == 0) sm.fail = 1;                  // no level isolated the cut
+    __syncthreads();
+    const uint32_t Tkey = sm.tkey;
+    const int ntie = sm.ntie;
+    const bool ok = !sm.fail && key_score(Tkey) > cr.d_edge;
+    if (!ok) {
+        if (tid == 0) *count_out = -1;
+        __syncthreads();
+        return;
+    }
+    // ---- the keys above the cut and the ties at it, as (index << 1 | tie),
+    // compacted, sorted ascending; then the ties past the first ntie dropped
+    unsigned long long mv[PER];
+    uint32_t c = 0;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+        const int i = tid + x * NT;
+        const unsigned long long v = i < slots ? sk[i] : 0ull;
+        const uint32_t key = (uint32_t)(v >> 32);
+        const bool keep = v != 0ull && key >= Tkey;
+        mv[x] = keep ? (((unsigned long long)(~(uint32_t)v) << 1) | (key == Tkey ? 1ull : 0ull)) : ~0ull;
+        c += keep ? 1u : 0u;
+    }
+    unsigned long long nk;
+    const uint32_t base = (uint32_t)block_excl_scan_u64<NT>(c, &nk, scan_sh);
+    {
+        uint32_t o = base;
+#pragma unroll
+        for (int x = 0; x < PER; ++x)
+            if (mv[x] != ~0ull) sk[o++] = mv[x];
+    }
+    int N2 = 64;
+    while (N2 < (int)nk) N2 <<= 1;
+    for (int i = (int)nk + tid; i < N2; i += NT) sk[i] = ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= N2; k <<= 1)
+        for (int jj = k >> 1; jj > 0; jj >>= 1) {
+            for (int i = tid; i < N2; i += NT) {
+                const int ixj = i ^ jj;
                 if (ixj > i) {
                     const unsigned long long x = sk[i], y = sk[ixj];
-                    const bool desc = (i & k) == 0;
-                    if (desc ? (x < y) : (x > y)) {
+                    const bool asc = (i & k) == 0;
+                    if (asc ? (x > y) : (x < y)) {
                         sk[i] = y;
                         sk[ixj] = x;
                     }
@@ -779,65 +970,35 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
             }
             __syncthreads();
         }
-    // exact masses in rank order: each thread a run of consecutive ranks
-    const int per = (N + NT - 1) / NT;
-    const int r0 = tid * per;
-    const int r1 = min(r0 + per, n);
-    unsigned long long loc = 0;
-    for (int i = r0; i < r1; ++i) loc += weight_bin(key_score((uint32_t)(sk[i] >> 32)), cr.mp, s).w;
-    unsigned long long tot;
-    const unsigned long long ex = block_excl_scan_u64<NT>(loc, &tot, scan_sh);
-    if (tid == 0) *s_first = 1 << 30;
-    __syncthreads();
+    // ties in index order: each thread a contiguous run of the sorted list
+    const int per = (N2 + NT - 1) / NT;
+    const int r0 = min(tid * per, (int)nk), r1 = min(r0 + per, (int)nk);
+    unsigned long long tl = 0ull;
+    for (int i = r0; i < r1; ++i) tl += sk[i] & 1ull;
+    unsigned long long ttot;
+    const unsigned long long tbase = block_excl_scan_u64<NT>(tl, &ttot, scan_sh);
+    unsigned long long kl = 0ull;
     {
-        unsigned long long run = ex;
+        unsigned long long tr = tbase;
         for (int i = r0; i < r1; ++i) {
-            run += weight_bin(key_score((uint32_t)(sk[i] >> 32)), cr.mp, s).w;
-            if (run >= target) {
-                atomicMin(s_first, i);
-                break;
-            }
+            const bool tie = sk[i] & 1ull;
+            if (!tie || tr < (unsigned long long)ntie) ++kl;
+            if (tie) ++tr;
         }
     }
-    __syncthreads();
-    const int first = *s_first;
-    const bool ok = first < n && key_score((uint32_t)(sk[first < n ? first : 0] >> 32)) > cr.d_edge;
-    const int cnt = first < n ? first + 1 : n;
-    // selected indices ascending; the index lives in the low word as its complement
-    int N2 = 64;
-    while (N2 < cnt) N2 <<= 1;
-    uint32_t mine[CAP / NT];
-#pragma unroll
-    for (int x = 0; x < CAP / NT; ++x) {
-        const int i = tid + x * NT;
-        mine[x] = i < cnt ? ~(uint32_t)sk[i] : 0xFFFFFFFFu;
-    }
-    __syncthreads();
-    uint32_t* si = reinterpret_cast<uint32_t*>(sk);
-#pragma unroll
-    for (int x = 0; x < CAP / NT; ++x) {
-        const int i = tid + x * NT;
-        if (i < N2) si[i] = mine[x];
-    }
-    __syncthreads();
-    for (int k = 2; k <= N2; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < N2; i += NT) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t x = si[i], y = si[ixj];
-                    const bool asc = (i & k) == 0;
-                    if (asc ? (x > y) : (x < y)) {
-                        si[i] = y;
-                        si[ixj] = x;
-                    }
-                }
-            }
-            __syncthreads();
-        }
+    unsigned long long cnt;
+    const unsigned long long obase = block_excl_scan_u64<NT>(kl, &cnt, scan_sh);
     uint32_t* ubi = reinterpret_cast<uint32_t*>(ub);
-    for (int i = tid; i < cnt; i += NT) ubi[i] = si[i];
-    if (tid == 0) *count_out = ok ? cnt : -1;
+    {
+        unsigned long long tr = tbase, o = obase;
+        for (int i = r0; i < r1; ++i) {
+            const unsigned long long v = sk[i];
+            const bool tie = v & 1ull;
+            if (!tie || tr < (unsigned long long)ntie) ubi[o++] = (uint32_t)(v >> 1);
+            if (tie) ++tr;
+        }
+    }
+    if (tid == 0) *count_out = (int)cnt;
     __syncthreads();
 }
 
@@ -866,8 +1027,8 @@ __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restr
     }
     __shared__ unsigned long long sk[kSmallU];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
-    __shared__ int s_first;
-    resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, &s_first);
+    __shared__ ResolveSmem sm;
+    resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
 }
 
 // Rows with U in (kSmallU, kSegMax]: a fixed grid of 1024-thread workgroups
@@ -881,7 +1042,7 @@ __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* 
                                                              int* __restrict__ counts) {
     __shared__ unsigned long long sk[kSegMax];
     __shared__ unsigned long long scan_sh[kRTL / 64 + 1];
-    __shared__ int s_first;
+    __shared__ ResolveSmem sm;
     for (int row = blockIdx.x; row < n_rows; row += gridDim.x) {
         const CRow cr = rows[row];
         if (cr.mode != kBuf || cr.count <= kSmallU) continue;
@@ -889,7 +1050,7 @@ __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* 
             if (threadIdx.x == 0) counts[row] = -1;
             continue;
         }
-        resolve_row<kSegMax, kRTL>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, &s_first);
+        resolve_row<kSegMax, kRTL>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
     }
 }
 
