@@ -12,13 +12,17 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librtp.so")
 SOURCES = ["abi.cpp", "append.hip", "select.hip", "select_chunk.hip", "attn_decode.hip", "attn_prefill.hip", "attn_sparse_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Per-file code generation options.  The chunk selection keeps its MFMA
+# results in VGPRs: every pass reads all 16 accumulator lanes of every tile
+# with VALU, and AGPR results would cost a v_accvgpr_read for each.
+FILE_FLAGS = {"select_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))

@@ -466,34 +466,45 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         for (int c = 0; c < 16; ++c) qv[c] = qs[lr][c];
         unsigned long long zacc = 0ull;
         uint32_t bp = 0u, be = 0u, nreal = 0u;            // the lane's reserved block [bp, be)
+        // a pooled row's lane compares against e_fast; other lanes never pass it
+        const float e_fast = active && fast ? e_thr : INFINITY;
+        const bool any_slow = __ballot(active && !fast) != 0ull;
+        const auto record = [&](int key) {
+            if (bp == be) {
+                bp = atomicAdd(&ucnt[lr], (uint32_t)kSegBlk);
+                be = bp + kSegBlk;
+            }
+            if (bp < scap) pool[sg + bp] = (unsigned long long)(uint32_t)key;
+            ++bp;
+            ++nreal;
+        };
         tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
+            if (level == 0) {
+                // pooled rows: one compare per pair, the recording under its mask
+                if (it < nfull) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (sc[i] >= e_fast) record(key_of(it, i));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        if (sc[i] >= e_fast && key_of(it, i) <= pos) record(key_of(it, i));
+                }
+                if (!any_slow) return;
+            }
             // which of this lane's pairs need an exact score
+            const bool slow = active && !fast;
             uint32_t need = 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                bool in = active && sc[i] >= e_thr;
+                bool in = slow && sc[i] >= e_thr;
                 if (it >= nfull) in = in && key_of(it, i) <= pos;
                 // only pairs whose exact score can fall inside [lo, hi]
                 if (ranged) in = in && !(sc[i] + dl < lo) && !(sc[i] - dl > hi);
                 need |= (uint32_t)in << i;
             }
             if (__ballot(need != 0u) == 0ull) return;
-            if (fast) {
-                while (need) {
-                    const int i = __ffs(need) - 1;
-                    need &= need - 1u;
-                    if (bp == be) {
-                        bp = atomicAdd(&ucnt[lr], (uint32_t)kSegBlk);
-                        be = bp + kSegBlk;
-                    }
-                    if (bp < scap) pool[sg + bp] = (unsigned long long)(uint32_t)key_of(it, i);
-                    ++bp;
-                    ++nreal;
-                }
-            }
-            const bool stage = __ballot(need != 0u) != 0ull;
-            if (!stage) return;
             ktile[wid][lr][hh] = cur;                     // key it*32 + lr, dims 8 hh .. 8 hh + 7
             wave_lds_sync();
             uint32_t slot = 0u;
