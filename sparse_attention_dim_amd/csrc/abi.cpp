@@ -205,7 +205,7 @@ rtp::SelWs sel_ws(const SelPlan& p, char* base) {
 
 int64_t sparse_max_items(const rtp_layer* L, const rtp_query* Q, int64_t capacity) {
     const int64_t rows = (int64_t)Q->n_tok * L->num_ret;
-    return rows + capacity / 128 + 1;
+    return rows + capacity / rtp::kSparseItem + 1;
 }
 
 int win_keys(const rtp_layer* L, const rtp_cache* C, int dense) {

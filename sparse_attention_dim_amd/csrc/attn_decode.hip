@@ -184,7 +184,8 @@ struct Stream {
 // Sparse decode: one wavefront per (row, piece of kItem selected keys); the
 // pieces of all rows form one flat list walked by a fixed grid.
 // ---------------------------------------------------------------------------
-constexpr int kItem = 128;
+constexpr int kItem = kSparseItem;
+static_assert(kItem % 64 == 0, "whole wavefronts of selected keys per item");
 
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restrict__ q,

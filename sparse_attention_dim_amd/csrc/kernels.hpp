@@ -90,6 +90,11 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
                          int total_rows, int dtype, int stage, hipStream_t s);
 
+// Selected keys per work item (one wavefront) of the sparse decode: a row of
+// n selected keys makes ceil(n / kSparseItem) partial results, so a call needs
+// at most rows + capacity / kSparseItem + 1 of them.
+constexpr int kSparseItem = 64;
+
 // Split-K partial attention of retrieval rows over their selected sets and the combine.
 struct AttnWs {
     float* part;                  // [items][D + 2]
