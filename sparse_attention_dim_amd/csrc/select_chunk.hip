@@ -12,26 +12,29 @@
 // v_mfma_f32_32x32x16_bf16.  The MFMA sum e is not the fixed-order chain, but
 // |e - d| <= delta / 8 with delta = 2^-16 |q_low| max|k_low| (the chain's own
 // rounding is at most ~2^-20 sum|q_c k_c| and the measured MFMA deviation is
-// below 2^-21 sum|q_c k_c|).  Passes of one workgroup over its 32 rows x all
-// keys of one head:
-//   P1  row maxima of e: m' = max e + delta >= max d (the largest key norm
-//       comes from a pre-pass over the head's indexer keys);
-//   P2  mass and count histograms over x = s (m' - e) in bins of 1/4 (weights
-//       exp(-x) summed in fp64 LDS atomics); the cut bin with a target raised
-//       by a margin that covers the approximation; U = bins <= cut + 1.  Bins
-//       are far wider than s delta, so every key ranked at or above the exact
-//       cut is in U;
-//   P3  exact scores and exact fixed-point weights of U's keys only: the
-//       exact mass of U, and U's (score, index) pairs into a segment of a
-//       shared pool, sized by the count histogram.  Keys outside U enter the
-//       total with their approximate fp64 weights (they hold at most the
-//       1 - p tail; their relative error is below s delta / 8).
-// A row with a segment is resolved by one workgroup that sorts it; a row
-// whose U is too large for a segment (or finds the pool full) is narrowed by
-// radix levels on the exact score inside the main kernel (extra passes behind
-// the MFMA filter), then emitted by a rescan.  Every result is certified: the
-// cut score must lie above every exact score that a key outside U can have,
-// else the call reports status 2.
+// below 2^-21 sum|q_c k_c|).  Passes over the 32 rows x all keys of one head
+// of a workgroup, one kernel each (so each runs at the occupancy its own
+// registers and LDS allow):
+//   P1  (k_csel_max) q_low and the row maxima of e: m' = max e + delta >=
+//       max d (the largest key norm comes from a pre-pass over the head's
+//       indexer keys);
+//   P2  (k_csel_hist) mass and count histograms over x = s (m' - e) in bins of
+//       1/4 (weights exp(-x) summed in fp64 LDS atomics); the cut bin with a
+//       target raised by a margin that covers the approximation;
+//       U = bins <= cut + 1.  Bins are far wider than s delta, so every key
+//       ranked at or above the exact cut is in U.  Rows whose U is small
+//       enough get a segment of a shared pool, sized by the count histogram;
+//   P3  (k_csel_rec) for those rows, the key indices of U into the segment.
+//       The resolve pass forms U's exact scores and exact fixed-point
+//       weights, U's exact mass (keys outside U enter the total with their
+//       approximate fp64 weights: they hold at most the 1 - p tail, with a
+//       relative error below s delta / 8), and the cut by radix selection;
+//   levels (k_csel_main) a row without a segment (U too large, or the pool
+//       full) scores U exactly in-lane and is narrowed by radix levels on the
+//       exact score (extra passes behind the MFMA filter), then emitted by a
+//       rescan.
+// Every result is certified: the cut score must lie above every exact score
+// that a key outside U can have, else the call reports status 2.
 #include <algorithm>
 
 #include "device.hpp"
@@ -154,51 +157,103 @@ constexpr int kSmemBytes = kLevelBytes > kHistBytes ? kLevelBytes : kHistBytes;
 static_assert(128 * 16 * 4 <= kSmemBytes, "q projection weights fit the shared buffer");
 static_assert(kHmBytes % 16 == 0 && (kHmBytes + kHcBytes) % 8 == 0, "aligned level structures");
 
+// Per-row state handed from the histogram pass to the later passes (device
+// workspace, one record per row of the call).
+struct CState {
+    float mp;        // m' (upper bound of the row's exact maximum)
+    float delta;     // 8x the |MFMA - exact| bound of the row
+    float e_thr;     // a pair is in U iff its MFMA score e >= e_thr
+    float edge;      // exact scores of keys outside U are <= edge
+    uint32_t klo, khi, shift;   // exact-score key range of the level path and its first shift
+    uint32_t ucount; // keys of U (count histogram)
+    int mode;        // kAll or kLevel
+    int uend;        // last P2 bin of U
+    int pad0, pad1;
+    unsigned long long seg;     // pool offset of the row's segment, kNoSeg if none
+    unsigned long long light;   // approximate fixed-point mass of the keys outside U
+};
+
+// The MFMA tile view of one workgroup: rows t0 .. t0 + 31 of retrieval head r,
+// lane row lr = lane % 32 and half hh = lane / 32; tile `it` covers keys
+// it*32 .. it*32 + 31 (A operand: k_low[key it*32 + lr][8 hh .. 8 hh + 7],
+// B operand: q_low[lr][8 hh .. 8 hh + 7]).
+struct TileCtx {
+    int r, t0, n_valid, lr, hh, pos, L_max, ntile, nfull;
+    bool row_ok;
+    const int32_t* bt;
+    const bf16_t* k_low;
+    int n_ret;
+    uint4 qb;
+    __device__ uint4 load(int it) const {
+        const int kk = min(it * 32 + lr, L_max - 1);
+        const int page = bt[kk >> 8];
+        return *reinterpret_cast<const uint4*>(k_low + (((size_t)page * n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
+    }
+    __device__ f32x16_t mfma(const uint4& a) const {
+        f32x16_t acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qb), acc, 0, 0, 0);
+    }
+    __device__ int key_of(int it, int i) const { return it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3); }
+};
+
+__device__ TileCtx tile_ctx(const Geo& g, const bf16_t* k_low, const float (*qs)[16]) {
+    TileCtx c;
+    const int lane = threadIdx.x & 63;
+    c.r = blockIdx.y;
+    c.t0 = blockIdx.x * kTR;
+    c.n_valid = min(kTR, g.n_tok - c.t0);
+    c.lr = lane & 31;
+    c.hh = lane >> 5;
+    c.row_ok = c.lr < c.n_valid;
+    c.pos = g.pos0 + c.t0 + c.lr;
+    c.L_max = g.pos0 + c.t0 + c.n_valid;
+    c.ntile = (c.L_max + 31) / 32;
+    c.nfull = (g.pos0 + c.t0 + 1) / 32;
+    c.bt = g.block_table + (size_t)g.seq * g.max_blocks;
+    c.k_low = k_low;
+    c.n_ret = g.n_ret;
+    uint32_t w4[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+        w4[x] = (__float_as_uint(qs[c.lr][8 * c.hh + 2 * x]) >> 16) |
+                (__float_as_uint(qs[c.lr][8 * c.hh + 2 * x + 1]) & 0xFFFF0000u);
+    c.qb = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    return c;
+}
+
+// q_low of the workgroup's rows as floats (zero for rows past the chunk)
+__device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (*qs)[16]) {
+    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
+    const int n_valid = min(kTR, g.n_tok - t0);
+    for (int o = threadIdx.x; o < kTR * 16; o += 256) {
+        const int lr = o >> 4, c = o & 15;
+        qs[lr][c] = lr < n_valid ? bf2f(qlow[((size_t)(t0 + lr) * g.n_ret + r) * 16 + c]) : 0.0f;
+    }
+}
+
 // ---------------------------------------------------------------------------
-// Main kernel.  grid (ceil(n_tok / 32), n_ret), 256 threads.
+// P1.  grid (ceil(n_tok / 32), n_ret), 256 threads: q_low of the rows (fixed-
+// order fp32 chain over d, bf16 rounding) and the row maxima of the MFMA
+// scores: m' = max e + delta >= max d (the largest key norm comes from the
+// key-norm pre-pass).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restrict__ q,
-                                                   const bf16_t* __restrict__ w_q,
-                                                   const bf16_t* __restrict__ k_low,
-                                                   const float* __restrict__ top_p, CRow* __restrict__ rows_out,
-                                                   uint16_t* __restrict__ qlow_out,
-                                                   const float* __restrict__ knorm, int nblk,
-                                                   unsigned long long* __restrict__ pool,
-                                                   unsigned long long* __restrict__ pool_ctr,
-                                                   unsigned long long pool_cap) {
+__global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restrict__ q,
+                                                  const bf16_t* __restrict__ w_q, const bf16_t* __restrict__ k_low,
+                                                  uint16_t* __restrict__ qlow_out, const float* __restrict__ knorm,
+                                                  int nblk, CState* __restrict__ st) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int r = blockIdx.y;
-    const int t0 = blockIdx.x * kTR;
+    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     const int h_q = g.ret_heads[r];
-    const float s = g.idx_scale;
-    const float sB = s * kBinsPerX;
-    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
-
-    __shared__ __align__(16) unsigned char smem[kSmemBytes];
-    float* wq = reinterpret_cast<float*>(smem);
-    double(*hist)[kTR] = reinterpret_cast<double(*)[kTR]>(smem);
-    uint32_t(*hcnt)[64] = reinterpret_cast<uint32_t(*)[64]>(smem + kHB * kTR * 8);
-    unsigned long long(*hm)[kNBP] = reinterpret_cast<unsigned long long(*)[kNBP]>(smem);
-    uint32_t(*hc)[kNBP] = reinterpret_cast<uint32_t(*)[kNBP]>(smem + kHmBytes);
-    unsigned long long(*cand)[kCapC] = reinterpret_cast<unsigned long long(*)[kCapC]>(smem + kHmBytes + kHcBytes);
-
-    __shared__ float qs[kTR][16];                        // q_low as floats
-    __shared__ uint32_t rmax[kTR];                       // ordered keys of the row maxima
+    __shared__ float wq[128 * 16];
+    __shared__ float qs[kTR][16];
+    __shared__ uint32_t rmax[kTR];
     __shared__ uint32_t kmax_bits;
-    __shared__ uint32_t cand_n[kTR], ucnt[kTR], ureal[kTR];
-    __shared__ unsigned long long zu[kTR];               // exact mass of U
-    __shared__ float r_mp[kTR], r_delta[kTR], r_mpB[kTR], r_T[kTR], r_edge[kTR], r_ethr[kTR];
-    __shared__ uint32_t r_ucount[kTR];
-    __shared__ unsigned long long r_seg[kTR];
-    __shared__ int r_mode[kTR], r_uend[kTR], r_ntie[kTR], r_done[kTR], r_gather[kTR], r_bad[kTR];
-    __shared__ uint32_t r_klo[kTR], r_khi[kTR], r_shift[kTR], r_cnthi[kTR];
-    __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_light[kTR];
-    __shared__ int s_any;
-    __shared__ uint4 ktile[4][32][2];                    // per wave: the 32 keys of the current tile
-
-    // ---- q_low of the 32 rows: fixed-order fp32 chain over d, bf16 rounding
     for (int x = tid; x < g.D * 16; x += 256) wq[x] = bf2f(w_q[(size_t)r * g.D * 16 + x]);
+    if (tid < kTR) rmax[tid] = 0u;
+    if (tid == 0) kmax_bits = 0u;
     __syncthreads();
     for (int o = tid; o < kTR * 16; o += 256) {
         const int lr = o >> 4, c = o & 15;
@@ -211,96 +266,81 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         qs[lr][c] = bf2f(qb);
         if (lr < n_valid) qlow_out[((size_t)(t0 + lr) * g.n_ret + r) * 16 + c] = qb;
     }
-    if (tid < kTR) {
-        rmax[tid] = 0u;
-        zu[tid] = 0ull;
-        cand_n[tid] = 0u;
-        ucnt[tid] = 0u;
-        ureal[tid] = 0u;
-        r_target[tid] = 0ull;
-    }
-    if (tid == 0) kmax_bits = 0u;
-    __syncthreads();
     {
         float kn = 0.0f;
         for (int b = tid; b < nblk; b += 256) kn = fmaxf(kn, knorm[(size_t)r * nblk + b]);
         kn = wave_max(kn);
         if (lane == 0) atomicMax(&kmax_bits, __float_as_uint(kn));
     }
-
-    // lane roles in the MFMA tiles: row lr = lane % 32, half hh = lane / 32
-    const int lr = lane & 31, hh = lane >> 5;
-    const bool row_ok = lr < n_valid;
-    const int pos = g.pos0 + t0 + lr;                    // the lane's row position
-    uint4 qb;                                             // B operand: q_low[lr][8 hh .. 8 hh + 7]
-    {
-        uint32_t w4[4];
+    __syncthreads();
+    const TileCtx tc = tile_ctx(g, k_low, qs);
+    float m_e = -INFINITY;
+    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
+        const f32x16_t sc = tc.mfma(cur);
+        if (it < tc.nfull) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
-            w4[x] = (__float_as_uint(qs[lr][8 * hh + 2 * x]) >> 16) |
-                    (__float_as_uint(qs[lr][8 * hh + 2 * x + 1]) & 0xFFFF0000u);
-        qb = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-    const int L_max = g.pos0 + t0 + n_valid;             // keys of the longest row
-    const int ntile = (L_max + 31) / 32;
-    const int nfull = (g.pos0 + t0 + 1) / 32;            // tiles every row sees whole
-
-    // A operand of tile `it`: k_low[key it*32 + lr][8 hh .. 8 hh + 7]
-    auto load_a = [&](int it) {
-        const int kk = min(it * 32 + lr, L_max - 1);
-        const int page = bt[kk >> 8];
-        return *reinterpret_cast<const uint4*>(
-            k_low + (((size_t)page * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
-    };
-    auto mfma_tile = [&](const uint4& a) {
-        f32x16_t acc;
+            for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, sc[i]);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qb), acc, 0, 0, 0);
-    };
-    auto key_of = [&](int it, int i) { return it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3); };
-
-    // ---- P1: row maxima of the MFMA scores
-    {
-        float m_e = -INFINITY;
-        tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
-            const f32x16_t sc = mfma_tile(cur);
-            if (it < nfull) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, sc[i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, key_of(it, i) <= pos ? sc[i] : -INFINITY);
-            }
-        });
-        m_e = fmaxf(m_e, __shfl_xor(m_e, 32));
-        if (row_ok && hh == 0 && m_e > -INFINITY) atomicMax(&rmax[lr], score_key(m_e));
-        for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
-        for (int x = tid; x < kHB * 64; x += 256) (&hcnt[0][0])[x] = 0u;
-        __syncthreads();
-        if (tid < kTR) {
-            float qn2 = 0.0f;
-            for (int c = 0; c < 16; ++c) qn2 = __builtin_fmaf(qs[tid][c], qs[tid][c], qn2);
-            // delta exceeds the true deviation bound by a factor >= 8, far more
-            // than the rounding of this sum: m' >= every exact score of the row
-            const float delta = 0x1.0p-16f * sqrtf(qn2) * sqrtf(__uint_as_float(kmax_bits)) * 1.0009765625f;
-            const float mp = key_score(rmax[tid]) + delta;
-            r_mp[tid] = mp;
-            r_delta[tid] = delta;
-            r_mpB[tid] = mp * sB;
+            for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, tc.key_of(it, i) <= tc.pos ? sc[i] : -INFINITY);
         }
-        __syncthreads();
+    });
+    m_e = fmaxf(m_e, __shfl_xor(m_e, 32));
+    if (tc.row_ok && tc.hh == 0 && m_e > -INFINITY) atomicMax(&rmax[tc.lr], score_key(m_e));
+    __syncthreads();
+    if (tid < n_valid) {
+        float qn2 = 0.0f;
+        for (int c = 0; c < 16; ++c) qn2 = __builtin_fmaf(qs[tid][c], qs[tid][c], qn2);
+        // delta exceeds the true deviation bound by a factor >= 8, far more
+        // than the rounding of this sum: m' >= every exact score of the row
+        const float delta = 0x1.0p-16f * sqrtf(qn2) * sqrtf(__uint_as_float(kmax_bits)) * 1.0009765625f;
+        CState* o = st + (size_t)(t0 + tid) * g.n_ret + r;
+        o->mp = key_score(rmax[tid]) + delta;
+        o->delta = delta;
     }
-    const float mpB = r_mpB[lr];
+}
 
-    // ---- P2: mass and count histograms of the approximate weights exp(-x / 4)
+// ---------------------------------------------------------------------------
+// P2.  Mass and count histograms over x = s (m' - e) in bins of 1/4 (weights
+// exp(-x) summed in fp64 LDS atomics); the cut bin with a target raised by a
+// margin that covers the approximation; U = bins <= cut + 1; pool segments for
+// the rows whose U is small enough.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restrict__ k_low,
+                                                   const float* __restrict__ top_p,
+                                                   const uint16_t* __restrict__ qlow, CState* __restrict__ st,
+                                                   unsigned long long* __restrict__ pool_ctr,
+                                                   unsigned long long pool_cap) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const float s = g.idx_scale;
+    const float sB = s * kBinsPerX;
+    __shared__ double hist[kHB][kTR];
+    __shared__ uint32_t hcnt[kHB][64];
+    __shared__ float qs[kTR][16];
+    __shared__ float r_mp[kTR], r_delta[kTR];
+    __shared__ uint32_t r_ucount[kTR];
+    __shared__ int r_mode[kTR];
+    __shared__ unsigned long long r_seg[kTR];
+    load_qs(g, qlow, qs);
+    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
+    const int n_valid = min(kTR, g.n_tok - t0);
+    if (tid < kTR) {
+        const CState* c = st + (size_t)(t0 + min(tid, n_valid - 1)) * g.n_ret + r;
+        r_mp[tid] = c->mp;
+        r_delta[tid] = c->delta;
+    }
+    for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
+    for (int x = tid; x < kHB * 64; x += 256) (&hcnt[0][0])[x] = 0u;
+    __syncthreads();
+    const TileCtx tc = tile_ctx(g, k_low, qs);
+    const float mpB = r_mp[tc.lr] * sB;
     {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
-        double* hrow = &hist[0][lr];
+        double* hrow = &hist[0][tc.lr];
         uint32_t* crow = &hcnt[0][lane];
-        tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
-            const f32x16_t sc = mfma_tile(cur);
-            if (it < nfull) {
+        tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
+            const f32x16_t sc = tc.mfma(cur);
+            if (it < tc.nfull) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float x = bin_x(sc[i], sB, mpB);
@@ -311,7 +351,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    if (key_of(it, i) <= pos) {
+                    if (tc.key_of(it, i) <= tc.pos) {
                         const float x = bin_x(sc[i], sB, mpB);
                         const int b = bin_of(x);
                         atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
@@ -320,116 +360,270 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 }
             }
         });
-        __syncthreads();
-        // cut bin of the approximate masses, U = bins <= cut + 1.  The target
-        // carries a margin eta that covers the relative error of the
-        // approximate weights (<= s delta / 8 plus the exp2 rounding); U is every
-        // key when the bins are not wide against delta.
-        if (tid < kTR) {
-            const int row = tid;
-            const float p = top_p[g.seq];
-            r_mode[row] = kLevel;
-            r_done[row] = 0;
-            r_gather[row] = 0;
-            r_bad[row] = 0;
-            r_uend[row] = kHB - 1;
-            r_ntie[row] = 0;
-            r_T[row] = 0.0f;
-            r_edge[row] = -INFINITY;
-            r_light[row] = 0ull;
-            r_ucount[row] = 0u;
-            r_seg[row] = kNoSeg;
-            r_ethr[row] = -INFINITY;
-            if (row >= n_valid) {
-                r_done[row] = 1;
-            } else if (!(p < 1.0f)) {
-                r_mode[row] = kAll;
-                r_done[row] = 1;
-            } else {
-                const double sd = (double)s * (double)r_delta[row];
-                double Z = 0.0;
-                for (int b = 0; b < kHB; ++b) Z += hist[b][row];
-                const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * Z;
-                int bc = kHB - 1;
-                double cum = 0.0;
-                for (int b = 0; b < kHB; ++b) {
-                    cum += hist[b][row];
-                    if (cum >= tgt_a) {
-                        bc = b;
-                        break;
-                    }
-                }
-                const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
-                double light = 0.0;
-                for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
-                uint32_t uc = 0;
-                for (int b = 0; b <= ue; ++b) uc += hcnt[b][row] + hcnt[b][row + 32];
-                r_ucount[row] = uc;
-                r_uend[row] = ue;
-                r_light[row] = (unsigned long long)__double2ll_rn(light * kFix);
-                const double mp = (double)r_mp[row];
-                if (ue == kHB - 1) {
-                    r_klo[row] = 0u;                      // every key is in U
-                } else {
-                    // the smallest MFMA score whose bin is <= ue (the bin is
-                    // monotone in the score, so U is e >= e_thr)
-                    const float mpBr = r_mpB[row];
-                    uint32_t klo = score_key(-INFINITY), khi = score_key(r_mp[row]);
-                    while (klo < khi) {
-                        const uint32_t mid = klo + ((khi - klo) >> 1);
-                        if (bin_of(bin_x(key_score(mid), sB, mpBr)) <= ue) khi = mid; else klo = mid + 1;
-                    }
-                    r_ethr[row] = key_score(khi);
-                    // keys of U: x < (ue + 1) / 4, so e > m' - (ue + 1) / (4 s);
-                    // keys outside: the reverse.  The margin covers the float
-                    // rounding of the bin argument and the MFMA deviation.
-                    const double span = (double)(ue + 1) / ((double)kBinsPerX * (double)s);
-                    const double marg = 0x1.0p-18 * (span + 2.0 * fabs(mp)) + 2.0 * (double)r_delta[row];
-                    r_klo[row] = score_key(__double2float_rd(mp - span - marg));
-                    r_edge[row] = __double2float_ru(mp - span + marg);
-                }
-                r_khi[row] = score_key(r_mp[row]);
-                const uint32_t spn = r_khi[row] - r_klo[row];
-                const int bits = spn ? 32 - __clz(spn) : 0;
-                r_shift[row] = bits > 6 ? bits - 6 : 0;
-                r_shi[row] = 0ull;
-                r_cnthi[row] = 0u;
-            }
-        }
-        __syncthreads();
-        // pool segments for the rows whose U is small enough (one allocation
-        // per workgroup; a full pool sends the rows to the radix levels)
-        if (tid == 0) {
-            unsigned long long tot = 0;
-            for (int row = 0; row < n_valid; ++row)
-                if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad))
-                    tot += r_ucount[row] + kSegPad;
-            if (tot) {
-                const unsigned long long base = atomicAdd(pool_ctr, tot);
-                if (base + tot <= pool_cap) {
-                    unsigned long long off = base;
-                    for (int row = 0; row < n_valid; ++row)
-                        if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad)) {
-                            r_seg[row] = off;
-                            off += r_ucount[row] + kSegPad;
-                        }
-                }
-            }
-        }
-        // the histograms are dead: the level structures take their place
-        for (int x = tid; x < kTR * kNBP; x += 256) {
-            (&hm[0][0])[x] = 0ull;
-            (&hc[0][0])[x] = 0u;
-        }
-        __syncthreads();
     }
+    __syncthreads();
+    // cut bin of the approximate masses, U = bins <= cut + 1.  The target
+    // carries a margin eta that covers the relative error of the approximate
+    // weights (<= s delta / 8 plus the exp2 rounding); U is every key when the
+    // bins are not wide against delta.
+    if (tid < n_valid) {
+        const int row = tid;
+        const float p = top_p[g.seq];
+        CState o;
+        o.mp = r_mp[row];
+        o.delta = r_delta[row];
+        o.mode = kLevel;
+        o.uend = kHB - 1;
+        o.edge = -INFINITY;
+        o.light = 0ull;
+        o.ucount = 0u;
+        o.seg = kNoSeg;
+        o.e_thr = -INFINITY;
+        o.klo = 0u;
+        o.khi = 0u;
+        o.shift = 0u;
+        o.pad0 = o.pad1 = 0;
+        if (!(p < 1.0f)) {
+            o.mode = kAll;
+        } else {
+            const double sd = (double)s * (double)r_delta[row];
+            double Z = 0.0;
+            for (int b = 0; b < kHB; ++b) Z += hist[b][row];
+            const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * Z;
+            int bc = kHB - 1;
+            double cum = 0.0;
+            for (int b = 0; b < kHB; ++b) {
+                cum += hist[b][row];
+                if (cum >= tgt_a) {
+                    bc = b;
+                    break;
+                }
+            }
+            const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
+            double light = 0.0;
+            for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
+            uint32_t uc = 0;
+            for (int b = 0; b <= ue; ++b) uc += hcnt[b][row] + hcnt[b][row + 32];
+            o.ucount = uc;
+            o.uend = ue;
+            o.light = (unsigned long long)__double2ll_rn(light * kFix);
+            const double mp = (double)o.mp;
+            if (ue == kHB - 1) {
+                o.klo = 0u;                               // every key is in U
+            } else {
+                // the smallest MFMA score whose bin is <= ue (the bin is
+                // monotone in the score, so U is e >= e_thr)
+                const float mpBr = o.mp * sB;
+                uint32_t klo = score_key(-INFINITY), khi = score_key(o.mp);
+                while (klo < khi) {
+                    const uint32_t mid = klo + ((khi - klo) >> 1);
+                    if (bin_of(bin_x(key_score(mid), sB, mpBr)) <= ue) khi = mid; else klo = mid + 1;
+                }
+                o.e_thr = key_score(khi);
+                // keys of U: x < (ue + 1) / 4, so e > m' - (ue + 1) / (4 s);
+                // keys outside: the reverse.  The margin covers the float
+                // rounding of the bin argument and the MFMA deviation.
+                const double span = (double)(ue + 1) / ((double)kBinsPerX * (double)s);
+                const double marg = 0x1.0p-18 * (span + 2.0 * fabs(mp)) + 2.0 * (double)o.delta;
+                o.klo = score_key(__double2float_rd(mp - span - marg));
+                o.edge = __double2float_ru(mp - span + marg);
+            }
+            o.khi = score_key(o.mp);
+            const uint32_t spn = o.khi - o.klo;
+            const int bits = spn ? 32 - __clz(spn) : 0;
+            o.shift = bits > 6 ? bits - 6 : 0;
+        }
+        r_mode[row] = o.mode;
+        r_ucount[row] = o.ucount;
+        r_seg[row] = kNoSeg;
+        st[(size_t)(t0 + row) * g.n_ret + r] = o;
+    }
+    __syncthreads();
+    // pool segments for the rows whose U is small enough (one allocation per
+    // workgroup; a full pool sends the rows to the radix levels)
+    if (tid == 0) {
+        unsigned long long tot = 0;
+        for (int row = 0; row < n_valid; ++row)
+            if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad)) tot += r_ucount[row] + kSegPad;
+        if (tot) {
+            const unsigned long long base = atomicAdd(pool_ctr, tot);
+            if (base + tot <= pool_cap) {
+                unsigned long long off = base;
+                for (int row = 0; row < n_valid; ++row)
+                    if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad)) {
+                        st[(size_t)(t0 + row) * g.n_ret + r].seg = off;
+                        off += r_ucount[row] + kSegPad;
+                    }
+            }
+        }
+    }
+}
 
-    // ---- P3 and the radix levels on the exact score.  P3 (level 0) computes
-    // the exact score and weight of every key of U: the mass of U, and U's
-    // pairs into the row's segment, or for a row without one the level-0
-    // radix histogram.  Rows without a segment narrow the cut bucket by
-    // further levels (64 buckets each, highest scores first) and finally
-    // gather its keys for one sort.
+// ---------------------------------------------------------------------------
+// P3 for the rows with a pool segment: the key indices of U (MFMA score
+// >= e_thr) into the segment, slots reserved kSegBlk at a time per lane, the
+// slack of each lane's last block marked empty.  The row's result record
+// (mode kBuf) follows; its exact scores are formed by the resolve pass.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restrict__ k_low,
+                                                  const uint16_t* __restrict__ qlow, const CState* __restrict__ st,
+                                                  CRow* __restrict__ rows_out, unsigned long long* __restrict__ pool) {
+    const int tid = threadIdx.x, wid = tid >> 6;
+    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
+    const int n_valid = min(kTR, g.n_tok - t0);
+    __shared__ float qs[kTR][16];
+    __shared__ CState rs[kTR];
+    __shared__ uint32_t ucnt[kTR], ureal[kTR];
+    __shared__ int s_any;
+    if (tid == 0) s_any = 0;
+    __syncthreads();
+    if (tid < n_valid) {
+        rs[tid] = st[(size_t)(t0 + tid) * g.n_ret + r];
+        ucnt[tid] = 0u;
+        ureal[tid] = 0u;
+        if (rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) s_any = 1;
+    }
+    __syncthreads();
+    if (!s_any) return;
+    load_qs(g, qlow, qs);
+    __syncthreads();
+    const TileCtx tc = tile_ctx(g, k_low, qs);
+    const int lr = tc.lr;
+    const bool pooled = tc.row_ok && rs[lr].mode == kLevel && rs[lr].seg != kNoSeg;
+    const unsigned long long sg = pooled ? rs[lr].seg : 0ull;
+    const uint32_t scap = pooled ? rs[lr].ucount + kSegPad : 0u;
+    const float e_fast = pooled ? rs[lr].e_thr : INFINITY;
+    uint32_t bp = 0u, be = 0u, nreal = 0u;              // the lane's reserved block [bp, be)
+    const auto record = [&](int key) {
+        if (bp == be) {
+            bp = atomicAdd(&ucnt[lr], (uint32_t)kSegBlk);
+            be = bp + kSegBlk;
+        }
+        if (bp < scap) pool[sg + bp] = (unsigned long long)(uint32_t)key;
+        ++bp;
+        ++nreal;
+    };
+    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
+        const f32x16_t sc = tc.mfma(cur);
+        if (it < tc.nfull) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (sc[i] >= e_fast) record(tc.key_of(it, i));
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (sc[i] >= e_fast && tc.key_of(it, i) <= tc.pos) record(tc.key_of(it, i));
+        }
+    });
+    for (uint32_t x = bp; x < be; ++x)
+        if (x < scap) pool[sg + x] = ~0ull;               // unused slots of the last block
+    if (nreal) atomicAdd(&ureal[lr], nreal);
+    __syncthreads();
+    if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) {
+        const CState& c = rs[tid];
+        CRow out;
+        out.mp = c.mp;
+        out.delta = c.delta;
+        out.e_thr = c.e_thr;
+        out.T = 0.0f;
+        out.d_edge = c.edge;
+        out.mode = kBuf;
+        out.u_end = c.uend;
+        out.n_tie = 0;
+        out.count = (int)ucnt[tid];
+        // P2 and P3 disagree on U, or the slots overflow the segment
+        out.bad = (ureal[tid] != c.ucount || ucnt[tid] > c.ucount + kSegPad) ? 1 : 0;
+        out.target = 0ull;
+        out.seg = c.seg;
+        out.light = c.light;
+        rows_out[(size_t)(t0 + tid) * g.n_ret + r] = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Radix levels.  grid (ceil(n_tok / 32), n_ret), 256 threads: the rows that
+// have no pool segment (and the keep-all rows' records).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restrict__ k_low,
+                                                   const float* __restrict__ top_p, const uint16_t* __restrict__ qlow,
+                                                   const CState* __restrict__ st, CRow* __restrict__ rows_out) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int r = blockIdx.y;
+    const int t0 = blockIdx.x * kTR;
+    const int n_valid = min(kTR, g.n_tok - t0);
+    const float s = g.idx_scale;
+
+    __shared__ __align__(16) unsigned char smem[kLevelBytes];
+    unsigned long long(*hm)[kNBP] = reinterpret_cast<unsigned long long(*)[kNBP]>(smem);
+    uint32_t(*hc)[kNBP] = reinterpret_cast<uint32_t(*)[kNBP]>(smem + kHmBytes);
+    unsigned long long(*cand)[kCapC] = reinterpret_cast<unsigned long long(*)[kCapC]>(smem + kHmBytes + kHcBytes);
+
+    __shared__ float qs[kTR][16];                        // q_low as floats
+    __shared__ uint32_t cand_n[kTR];
+    __shared__ unsigned long long zu[kTR];               // exact mass of U
+    __shared__ float r_mp[kTR], r_delta[kTR], r_T[kTR], r_edge[kTR], r_ethr[kTR];
+    __shared__ int r_mode[kTR], r_uend[kTR], r_ntie[kTR], r_done[kTR], r_gather[kTR], r_bad[kTR], r_pooled[kTR];
+    __shared__ uint32_t r_klo[kTR], r_khi[kTR], r_shift[kTR], r_cnthi[kTR];
+    __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_light[kTR];
+    __shared__ int s_any;
+    __shared__ uint4 ktile[4][32][2];                    // per wave: the 32 keys of the current tile
+
+    // the rows' state; pooled rows are finished by the recording pass
+    if (tid == 0) s_any = 0;
+    __syncthreads();
+    if (tid < kTR) {
+        const int row = tid;
+        zu[row] = 0ull;
+        cand_n[row] = 0u;
+        r_target[row] = 0ull;
+        r_gather[row] = 0;
+        r_bad[row] = 0;
+        r_ntie[row] = 0;
+        r_T[row] = 0.0f;
+        r_shi[row] = 0ull;
+        r_cnthi[row] = 0u;
+        r_pooled[row] = 0;
+        r_done[row] = 1;
+        r_mode[row] = kLevel;
+        if (row < n_valid) {
+            const CState c = st[(size_t)(t0 + row) * g.n_ret + r];
+            r_mp[row] = c.mp;
+            r_delta[row] = c.delta;
+            r_ethr[row] = c.e_thr;
+            r_edge[row] = c.edge;
+            r_klo[row] = c.klo;
+            r_khi[row] = c.khi;
+            r_shift[row] = c.shift;
+            r_mode[row] = c.mode;
+            r_uend[row] = c.uend;
+            r_light[row] = c.light;
+            r_pooled[row] = c.mode == kLevel && c.seg != kNoSeg;
+            r_done[row] = c.mode != kLevel || r_pooled[row];
+            if (!r_pooled[row]) s_any = 1;                // a record to write here
+        }
+    }
+    for (int x = tid; x < kTR * kNBP; x += 256) {
+        (&hm[0][0])[x] = 0ull;
+        (&hc[0][0])[x] = 0u;
+    }
+    __syncthreads();
+    if (!s_any) return;
+    load_qs(g, qlow, qs);
+    __syncthreads();
+    const TileCtx tc = tile_ctx(g, k_low, qs);
+    const int lr = tc.lr, hh = tc.hh;
+    const bool row_ok = tc.row_ok;
+    const int pos = tc.pos;
+    const int ntile = tc.ntile, nfull = tc.nfull;
+    const auto load_a = [&](int it) { return tc.load(it); };
+    const auto mfma_tile = [&](const uint4& a) { return tc.mfma(a); };
+    const auto key_of = [&](int it, int i) { return tc.key_of(it, i); };
+
+    // ---- P3 and the radix levels on the exact score for the rows without a
+    // pool segment.  Level 0 computes the exact score and weight of every key
+    // of U: the mass of U and the level-0 radix histogram; further levels
+    // (64 buckets each, highest scores first) narrow the cut bucket, and its
+    // keys are finally gathered for one sort.
     for (int level = 0; level < 8; ++level) {
         if (level > 0) {
             for (int x = tid; x < kTR * kNBP; x += 256) {
@@ -443,13 +637,9 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         __syncthreads();
         if (!s_any) break;
 
-        // Each lane owns one row (lr).  A row with a pool segment only records
-        // the keys of U at level 0 (index per slot; slots reserved kSegBlk at a
-        // time, the slack of the last block marked empty); its exact scores
-        // are formed by the resolve pass.  Other rows score their own pairs
-        // here: the row's state sits in registers, the tile's keys are copied
-        // to LDS when some lane of the wave needs an exact score, U's mass
-        // accumulates per lane.
+        // Each lane owns one row (lr) and scores its own pairs: the row's state
+        // sits in registers, the tile's keys are copied to LDS when some lane
+        // of the wave needs an exact score, U's mass accumulates per lane.
         const bool active = row_ok && !r_done[lr];
         const float e_thr = r_ethr[lr];
         const int gath = r_gather[lr];
@@ -457,48 +647,18 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         const float lo = ranged ? key_score(r_klo[lr]) : 0.0f, hi = ranged ? key_score(r_khi[lr]) : 0.0f;
         const float dl = r_delta[lr];
         const uint32_t klo = r_klo[lr], khi = r_khi[lr], shift = r_shift[lr];
-        const unsigned long long sg = r_seg[lr];
-        const bool fast = level == 0 && !gath && sg != kNoSeg;
-        const uint32_t scap = r_ucount[lr] + kSegPad;
         const float mp_row = r_mp[lr];
         float qv[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) qv[c] = qs[lr][c];
         unsigned long long zacc = 0ull;
-        uint32_t bp = 0u, be = 0u, nreal = 0u;            // the lane's reserved block [bp, be)
-        // a pooled row's lane compares against e_fast; other lanes never pass it
-        const float e_fast = active && fast ? e_thr : INFINITY;
-        const bool any_slow = __ballot(active && !fast) != 0ull;
-        const auto record = [&](int key) {
-            if (bp == be) {
-                bp = atomicAdd(&ucnt[lr], (uint32_t)kSegBlk);
-                be = bp + kSegBlk;
-            }
-            if (bp < scap) pool[sg + bp] = (unsigned long long)(uint32_t)key;
-            ++bp;
-            ++nreal;
-        };
         tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
-            if (level == 0) {
-                // pooled rows: one compare per pair, the recording under its mask
-                if (it < nfull) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (sc[i] >= e_fast) record(key_of(it, i));
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (sc[i] >= e_fast && key_of(it, i) <= pos) record(key_of(it, i));
-                }
-                if (!any_slow) return;
-            }
             // which of this lane's pairs need an exact score
-            const bool slow = active && !fast;
             uint32_t need = 0;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                bool in = slow && sc[i] >= e_thr;
+                bool in = active && sc[i] >= e_thr;
                 if (it >= nfull) in = in && key_of(it, i) <= pos;
                 // only pairs whose exact score can fall inside [lo, hi]
                 if (ranged) in = in && !(sc[i] + dl < lo) && !(sc[i] - dl > hi);
@@ -507,8 +667,6 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             if (__ballot(need != 0u) == 0ull) return;
             ktile[wid][lr][hh] = cur;                     // key it*32 + lr, dims 8 hh .. 8 hh + 7
             wave_lds_sync();
-            uint32_t slot = 0u;
-            if (level == 0 && !gath && need) slot = atomicAdd(&ucnt[lr], (uint32_t)__popc(need));
             while (need) {
                 const int i = __ffs(need) - 1;
                 need &= need - 1u;
@@ -524,10 +682,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                     }
                 } else {
                     const unsigned long long w = weight_bin(d, mp_row, s).w;
-                    if (level == 0) {
-                        zacc += w;
-                        ++slot;
-                    }
+                    if (level == 0) zacc += w;
                     if (kd >= klo && kd <= khi) {
                         const uint32_t bk = min((khi - kd) >> shift, (uint32_t)(kNB - 1));
                         atomicAdd(&hm[lr][bk], w);
@@ -538,11 +693,6 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             }
             wave_lds_sync();                              // the tile's keys are read before the next copy
         });
-        if (fast) {
-            for (uint32_t x = bp; x < be; ++x)
-                if (x < scap) pool[sg + x] = ~0ull;       // unused slots of the last block
-            if (nreal) atomicAdd(&ureal[lr], nreal);
-        }
         if (level == 0) {
             zacc += __shfl_xor(zacc, 32);
             if (hh == 0 && zacc) atomicAdd(&zu[lr], zacc);
@@ -561,12 +711,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                     if (tgt < 1ull) tgt = 1ull;
                     r_target[row] = tgt;
                 }
-                if (level == 0 && r_seg[row] != kNoSeg) {
-                    r_mode[row] = kBuf;                  // resolved from its segment
-                    r_done[row] = 1;
-                    // P2 and P3 disagree on U, or the slots overflow the segment
-                    if (ureal[row] != r_ucount[row] || ucnt[row] > r_ucount[row] + kSegPad) r_bad[row] = 1;
-                } else if (r_gather[row]) {
+                if (r_gather[row]) {
                     r_done[row] = 1;                     // final sort of the cut bucket's keys below
                 } else {
                     unsigned long long cum = r_shi[row];
@@ -620,11 +765,12 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     // ---- per-row results; rows resolved by levels sort their candidates here
     if (wid == 0) {
         for (int row = 0; row < n_valid; ++row) {
+            if (r_pooled[row]) continue;                 // written by the recording pass
             CRow out;
             out.mp = r_mp[row];
             out.delta = r_delta[row];
             out.e_thr = r_ethr[row];
-            out.seg = r_seg[row];
+            out.seg = kNoSeg;
             out.d_edge = r_edge[row];
             out.u_end = r_uend[row];
             out.mode = r_mode[row];
@@ -634,9 +780,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             out.target = r_target[row];
             out.light = r_light[row];
             int bad = r_bad[row];
-            if (out.mode == kBuf) {
-                out.count = (int)ucnt[row];
-            } else if (out.mode == kLevel && !bad) {
+            if (out.mode == kLevel && !bad) {
                 if (r_gather[row] == 2) {
                     out.T = r_T[row];
                     out.n_tie = r_ntie[row];
@@ -1260,7 +1404,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, qlow, counts, knorm, ctr, pool, head;
+    size_t crow, cst, qlow, counts, knorm, ctr, pool, head;
     int nblk;
 };
 
@@ -1269,7 +1413,8 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     ChunkWs w;
     w.nblk = (n_keys + kNormKeys - 1) / kNormKeys;
     w.crow = 0;
-    w.qlow = w.crow + up((size_t)rows * sizeof(CRow));
+    w.cst = w.crow + up((size_t)rows * sizeof(CRow));
+    w.qlow = w.cst + up((size_t)rows * sizeof(CState));
     w.counts = w.qlow + up((size_t)rows * 16 * 2);
     w.knorm = w.counts + up((size_t)rows * 4);
     w.ctr = w.knorm + up((size_t)n_ret * w.nblk * 4);
@@ -1294,6 +1439,7 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     if (g.D > 128 || ws_bytes < w.head) return hipErrorInvalidValue;
     char* base = (char*)ws;
     CRow* crow = (CRow*)(base + w.crow);
+    CState* cst = (CState*)(base + w.cst);
     uint16_t* qlow = (uint16_t*)(base + w.qlow);
     int* counts = (int*)(base + w.counts);
     float* knorm = (float*)(base + w.knorm);
@@ -1303,8 +1449,11 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
-    hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
-                       (const bf16_t*)k_low, top_p, crow, qlow, knorm, w.nblk, pool, ctr, pool_cap);
+    hipLaunchKernelGGL(k_csel_max, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
+                       (const bf16_t*)k_low, qlow, knorm, w.nblk, cst);
+    hipLaunchKernelGGL(k_csel_hist, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, ctr, pool_cap);
+    hipLaunchKernelGGL(k_csel_rec, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, qlow, cst, crow, pool);
+    hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
     hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, (const bf16_t*)k_low, qlow, top_p,
                        pool, counts);
     hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 512)), dim3(kRTL), 0, s, g, crow, rows,
