@@ -144,17 +144,13 @@ __device__ __forceinline__ void tile_loop(int first, int stride, int ntile, Load
 }
 constexpr int kPre = 8;          // tile loads in flight per wave
 
-// LDS layout: the q projection weights, the P2 histogram and the level
-// structures are live at different times and share one buffer.
-// P2 histograms are bin-major, so the bank of a lane's atomic depends on its
-// row (mass, fp64 [bin][row]) or on the lane (count, u32 [bin][lane]) only.
-constexpr int kHistBytes = kHB * kTR * 8 + kHB * 64 * 4;
+// LDS of the radix levels: per-row bucket masses and counts and the gathered
+// candidates of the last bucket.  (The P2 histograms are bin-major, [bin][row],
+// so the bank of a lane's atomic depends on its row only.)
 constexpr int kHmBytes = kTR * kNBP * 8;
 constexpr int kHcBytes = kTR * kNBP * 4;
 constexpr int kCandBytes = kTR * kCapC * 8;
 constexpr int kLevelBytes = kHmBytes + kHcBytes + kCandBytes;
-constexpr int kSmemBytes = kLevelBytes > kHistBytes ? kLevelBytes : kHistBytes;
-static_assert(128 * 16 * 4 <= kSmemBytes, "q projection weights fit the shared buffer");
 static_assert(kHmBytes % 16 == 0 && (kHmBytes + kHcBytes) % 8 == 0, "aligned level structures");
 
 // Per-row state handed from the histogram pass to the later passes (device
@@ -315,7 +311,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     const float s = g.idx_scale;
     const float sB = s * kBinsPerX;
     __shared__ double hist[kHB][kTR];
-    __shared__ uint32_t hcnt[kHB][64];
+    __shared__ uint32_t hcnt[kHB][kTR];                 // (52 KB of LDS in all: three workgroups per CU)
     __shared__ float qs[kTR][16];
     __shared__ float r_mp[kTR], r_delta[kTR];
     __shared__ uint32_t r_ucount[kTR];
@@ -330,14 +326,14 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         r_delta[tid] = c->delta;
     }
     for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
-    for (int x = tid; x < kHB * 64; x += 256) (&hcnt[0][0])[x] = 0u;
+    for (int x = tid; x < kHB * kTR; x += 256) (&hcnt[0][0])[x] = 0u;
     __syncthreads();
     const TileCtx tc = tile_ctx(g, k_low, qs);
     const float mpB = r_mp[tc.lr] * sB;
     {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
         double* hrow = &hist[0][tc.lr];
-        uint32_t* crow = &hcnt[0][lane];
+        uint32_t* crow = &hcnt[0][tc.lr];
         tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
             if (it < tc.nfull) {
@@ -346,7 +342,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                     const float x = bin_x(sc[i], sB, mpB);
                     const int b = bin_of(x);
                     atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
-                    atomicAdd(&crow[b * 64], 1u);
+                    atomicAdd(&crow[b * kTR], 1u);
                 }
             } else {
 #pragma unroll
@@ -355,7 +351,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                         const float x = bin_x(sc[i], sB, mpB);
                         const int b = bin_of(x);
                         atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
-                        atomicAdd(&crow[b * 64], 1u);
+                        atomicAdd(&crow[b * kTR], 1u);
                     }
                 }
             }
@@ -403,7 +399,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
             double light = 0.0;
             for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
             uint32_t uc = 0;
-            for (int b = 0; b <= ue; ++b) uc += hcnt[b][row] + hcnt[b][row + 32];
+            for (int b = 0; b <= ue; ++b) uc += hcnt[b][row];
             o.ucount = uc;
             o.uend = ue;
             o.light = (unsigned long long)__double2ll_rn(light * kFix);
