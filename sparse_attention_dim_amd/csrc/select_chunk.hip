@@ -490,12 +490,15 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
     const uint32_t scap = pooled ? rs[lr].ucount + kSegPad : 0u;
     const float e_fast = pooled ? rs[lr].e_thr : INFINITY;
     uint32_t bp = 0u, be = 0u, nreal = 0u;              // the lane's reserved block [bp, be)
+    // entry: (writer << 24) | key.  A writer (wave, half) visits its keys in
+    // increasing order, so its entries, read in slot order, ascend.
+    const unsigned long long wtag = (unsigned long long)(wid * 2 + tc.hh) << 24;
     const auto record = [&](int key) {
         if (bp == be) {
             bp = atomicAdd(&ucnt[lr], (uint32_t)kSegBlk);
             be = bp + kSegBlk;
         }
-        if (bp < scap) pool[sg + bp] = (unsigned long long)(uint32_t)key;
+        if (bp < scap) pool[sg + bp] = wtag | (unsigned long long)(uint32_t)key;
         ++bp;
         ++nreal;
     };
@@ -870,6 +873,14 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kRB = 1024;        // radix buckets per level of the resolve
 
+// Low word of a resolve entry (score key << 32 | low): larger for a smaller
+// key index (ties rank lowest index first), with the writer of the entry in
+// its low 3 bits.  Key indices are below 2^20.
+__device__ __forceinline__ uint32_t lo_word(int key, int writer) {
+    return ((0xFFFFFu - (uint32_t)key) << 3) | (uint32_t)writer;
+}
+__device__ __forceinline__ uint32_t lo_key(uint32_t lo) { return 0xFFFFFu - (lo >> 3); }
+
 struct ResolveSmem {
     unsigned long long hm[kRB];
     uint32_t hc[kRB];
@@ -907,7 +918,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
         unsigned long long e = 0ull;
         const unsigned long long v = ub[i];
         if (v != ~0ull) {
-            const int key = (int)v;
+            const int key = (int)(v & 0xFFFFFFull);
             const int page = bt[key >> 8];
             const uint4* kp = reinterpret_cast<const uint4*>(
                 k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
@@ -917,7 +928,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
             const uint32_t kd = score_key(d);
             kmn = min(kmn, kd);
             kmx = max(kmx, kd);
-            e = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
+            e = ((unsigned long long)kd << 32) | (unsigned long long)lo_word(key, (int)(v >> 24) & 7);
         }
         sk[i] = e;
     }
@@ -1082,57 +1093,120 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
         return;
     }
     // ---- the keys above the cut and the ties at it, as (index << 1 | tie),
-    // compacted, sorted ascending; then the ties past the first ntie dropped
-    unsigned long long mv[PER];
-    uint32_t c = 0;
+    // sorted ascending; then the ties past the first ntie dropped.  Each
+    // writer's entries ascend in slot order, so the kept keys are 8 sorted
+    // runs: every thread takes a contiguous range of slots, the runs are
+    // placed at stride R (odd ones reversed, padded with ~0), and only the
+    // last three levels of a bitonic sort remain.  Runs too long for that
+    // layout take the whole sort.
+    uint32_t* sv = reinterpret_cast<uint32_t*>(sk);     // 2 CAP words
+    const int sp = (slots + NT - 1) / NT;                // <= PER
+    const int s0 = min(tid * sp, slots);
+    uint32_t vals[PER];                                  // (index << 1 | tie) << 4 | writer (8: not kept)
+    unsigned long long clo = 0ull, chi = 0ull;           // kept per writer, 16-bit fields
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
-        const int i = tid + x * NT;
-        const unsigned long long v = i < slots ? sk[i] : 0ull;
+        const int i = s0 + x;
+        const unsigned long long v = (x < sp && i < slots) ? sk[i] : 0ull;
         const uint32_t key = (uint32_t)(v >> 32);
         const bool keep = v != 0ull && key >= Tkey;
-        mv[x] = keep ? (((unsigned long long)(~(uint32_t)v) << 1) | (key == Tkey ? 1ull : 0ull)) : ~0ull;
-        c += keep ? 1u : 0u;
+        const uint32_t lo = (uint32_t)v;
+        const int w = (int)(lo & 7u);
+        vals[x] = (((lo_key(lo) << 1) | (key == Tkey ? 1u : 0u)) << 4) | (keep ? (uint32_t)w : 8u);
+        if (keep) {
+            if (w < 4) clo += 1ull << (16 * w);
+            else chi += 1ull << (16 * (w - 4));
+        }
     }
-    unsigned long long nk;
-    const uint32_t base = (uint32_t)block_excl_scan_u64<NT>(c, &nk, scan_sh);
-    {
-        uint32_t o = base;
+    unsigned long long tlo, thi;
+    const unsigned long long elo = block_excl_scan_u64<NT>(clo, &tlo, scan_sh);
+    const unsigned long long ehi = block_excl_scan_u64<NT>(chi, &thi, scan_sh);
+    const auto field = [](unsigned long long a, unsigned long long b, int w) {
+        return (int)(((w < 4 ? a : b) >> (16 * (w & 3))) & 0xFFFFull);
+    };
+    int nk = 0, rmax = 0;
 #pragma unroll
-        for (int x = 0; x < PER; ++x)
-            if (mv[x] != ~0ull) sk[o++] = mv[x];
+    for (int w = 0; w < 8; ++w) {
+        const int t = field(tlo, thi, w);
+        nk += t;
+        rmax = max(rmax, t);
     }
-    int N2 = 64;
-    while (N2 < (int)nk) N2 <<= 1;
-    for (int i = (int)nk + tid; i < N2; i += NT) sk[i] = ~0ull;
+    int R = 1;
+    while (R < rmax) R <<= 1;
+    const bool runs = 8 * R <= 2 * CAP;
+    int N2 = 1;
+    while (N2 < nk) N2 <<= 1;
+    const int NS = runs ? 8 * R : N2;                    // sorted length
+    {
+        int off[8];
+#pragma unroll
+        for (int w = 0; w < 8; ++w) off[w] = field(elo, ehi, w);
+        // in the whole-sort layout the runs simply follow each other
+        int rb[8];
+        {
+            int acc = 0;
+#pragma unroll
+            for (int w = 0; w < 8; ++w) {
+                rb[w] = acc;
+                acc += field(tlo, thi, w);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+            const int w = (int)(vals[x] & 15u);
+            if (w == 8) continue;
+            int q = 0, b = 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (u == w) {
+                    q = off[u]++;
+                    b = rb[u];
+                }
+            const int p = runs ? (w * R + ((w & 1) ? R - 1 - q : q)) : b + q;
+            sv[p] = vals[x] >> 4;
+        }
+    }
+    // padding: the free end of an ascending run, the free start of a
+    // descending one, or the tail of the whole sort
+    for (int p = tid; p < NS; p += NT) {
+        bool pad;
+        if (runs) {
+            const int w = p / R, o = p - w * R;
+            const int t = field(tlo, thi, w);
+            pad = (w & 1) ? o < R - t : o >= t;
+        } else {
+            pad = p >= nk;
+        }
+        if (pad) sv[p] = 0xFFFFFFFFu;
+    }
     __syncthreads();
-    for (int k = 2; k <= N2; k <<= 1)
+    for (int k = runs ? 2 * R : 2; k <= NS; k <<= 1)
         for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < N2; i += NT) {
+            for (int i = tid; i < NS; i += NT) {
                 const int ixj = i ^ jj;
                 if (ixj > i) {
-                    const unsigned long long x = sk[i], y = sk[ixj];
+                    const uint32_t x = sv[i], y = sv[ixj];
                     const bool asc = (i & k) == 0;
                     if (asc ? (x > y) : (x < y)) {
-                        sk[i] = y;
-                        sk[ixj] = x;
+                        sv[i] = y;
+                        sv[ixj] = x;
                     }
                 }
             }
             __syncthreads();
         }
     // ties in index order: each thread a contiguous run of the sorted list
-    const int per = (N2 + NT - 1) / NT;
-    const int r0 = min(tid * per, (int)nk), r1 = min(r0 + per, (int)nk);
+    const int per = (nk + NT - 1) / NT;
+    const int r0 = min(tid * per, nk), r1 = min(r0 + per, nk);
     unsigned long long tl = 0ull;
-    for (int i = r0; i < r1; ++i) tl += sk[i] & 1ull;
+    for (int i = r0; i < r1; ++i) tl += sv[i] & 1u;
     unsigned long long ttot;
     const unsigned long long tbase = block_excl_scan_u64<NT>(tl, &ttot, scan_sh);
     unsigned long long kl = 0ull;
     {
         unsigned long long tr = tbase;
         for (int i = r0; i < r1; ++i) {
-            const bool tie = sk[i] & 1ull;
+            const bool tie = sv[i] & 1u;
             if (!tie || tr < (unsigned long long)ntie) ++kl;
             if (tie) ++tr;
         }
@@ -1143,9 +1217,9 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     {
         unsigned long long tr = tbase, o = obase;
         for (int i = r0; i < r1; ++i) {
-            const unsigned long long v = sk[i];
-            const bool tie = v & 1ull;
-            if (!tie || tr < (unsigned long long)ntie) ubi[o++] = (uint32_t)(v >> 1);
+            const uint32_t v = sv[i];
+            const bool tie = v & 1u;
+            if (!tie || tr < (unsigned long long)ntie) ubi[o++] = v >> 1;
             if (tie) ++tr;
         }
     }
@@ -1182,9 +1256,9 @@ __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restr
     resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
 }
 
-// Rows with U in (kSmallU, kSegMax]: a fixed grid of 1024-thread workgroups
+// Rows with U in (kSmallU, kSegMax]: a fixed grid of 512-thread workgroups
 // walks the rows.
-constexpr int kRTL = 1024;
+constexpr int kRTL = 512;      // threads of the large-row resolve (two waves per SIMD: room for its registers)
 __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* __restrict__ rows, int n_rows,
                                                              const bf16_t* __restrict__ k_low,
                                                              const uint16_t* __restrict__ qlow,
