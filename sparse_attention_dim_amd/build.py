@@ -12,10 +12,12 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librtp.so")
 SOURCES = ["abi.cpp", "append.hip", "select.hip", "select_chunk.hip", "attn_decode.hip", "attn_prefill.hip", "attn_sparse_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Per-file code generation options.  The chunk selection keeps its MFMA
-# results in VGPRs: every pass reads all 16 accumulator lanes of every tile
-# with VALU, and AGPR results would cost a v_accvgpr_read for each.
-FILE_FLAGS = {"select_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file code generation options.  The chunk selection and the decode window
+# kernel keep their MFMA results in VGPRs: they read (or rescale) every
+# accumulator lane with VALU, and AGPR results would cost a v_accvgpr move for
+# each.
+FILE_FLAGS = {"select_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -15,6 +15,7 @@
 // of the wave are merged at the end, and a combine kernel merges the work
 // items of a row in a fixed order, so results are deterministic.
 #include <algorithm>
+#include <type_traits>
 
 #include "device.hpp"
 #include "kernels.hpp"
@@ -421,6 +422,177 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
         if (st.act[i]) st.write(i, part + (((size_t)b * g.Hq + kvh * g.group + i) * nsplit + blockIdx.x) * (D + 2));
 }
 
+// ---------------------------------------------------------------------------
+// Local-head (or dense) decode on bf16 MFMA, D = 128: one wavefront per
+// (sequence, KV head, split).  The query heads of the KV group are the 32
+// columns of v_mfma_f32_32x32x16_bf16 (heads that do not need the kernel are
+// zero columns), so every K/V row is read once for the group.  Per block of 32
+// keys: S^T[key][head] = K . Q^T with the K rows straight from memory (each
+// lane one key, 16 bytes per k-step); online softmax per head in-lane (a lane
+// holds 16 of the block's keys of its head, the other half-wave the other 16);
+// O^T[d][head] += V^T . P^T with V^T from a transposed LDS tile and P^T taken
+// straight from the S^T registers (a fixed key permutation matches their
+// layout).  Writes the same partials as k_win_dec_part.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+constexpr int kWVtLd = 32 + 4;     // V^T row stride in LDS (bf16): 8-byte aligned 4-key reads
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
+                                                     const bf16_t* __restrict__ vc, float* __restrict__ part,
+                                                     int nsplit, int split_keys, int dense) {
+    constexpr int D = 128;
+    const int lane = threadIdx.x, hh = lane >> 5, col = lane & 31;
+    const int b = blockIdx.y / g.Hkv, kvh = blockIdx.y % g.Hkv;
+    const int pos = seq_len(g, b) - 1;
+    int ns_end, w_start;
+    const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
+    const int v0 = blockIdx.x * split_keys;
+    if (v0 >= n_all) return;
+    const int n = min(split_keys, n_all - v0);
+    const int hq = kvh * g.group + col;
+    const bool act = col < g.group && (dense || !g.is_ret[col < g.group ? hq : 0]);
+    if (__ballot(act) == 0ull) return;
+    // B operand Q^T: lane holds q[hq][16 kk + 8 hh .. +8]
+    uint4 qreg[8];
+    {
+        const bf16_t* qp = q + ((size_t)b * g.Hq + (act ? hq : 0)) * D + 8 * hh;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            qreg[kk] = act ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
+    }
+    // page ids of the split: a run of sink positions, then a run of window positions
+    __shared__ int pgs[64];
+    __shared__ __align__(16) bf16_t Vt[D * kWVtLd];
+    const int32_t* bt = g.block_table + (size_t)b * g.max_blocks;
+    const int vS1 = min(v0 + n, ns_end);
+    const int pS0 = v0 >> 8;
+    const int nPS = vS1 > v0 ? ((vS1 - 1) >> 8) - pS0 + 1 : 0;
+    const int jW0 = w_start + max(v0, ns_end) - ns_end;
+    const int jW1 = w_start + (v0 + n) - ns_end;
+    const int pW0 = jW0 >> 8;
+    const int nPW = jW1 > jW0 ? ((jW1 - 1) >> 8) - pW0 + 1 : 0;
+    if (lane < nPS) pgs[lane] = bt[pS0 + lane];
+    else if (lane < nPS + nPW) pgs[lane] = bt[pW0 + lane - nPS];
+    __syncthreads();
+    auto off = [&](int i) {
+        const int vi = v0 + i;
+        int j, pi;
+        if (vi < ns_end) {
+            j = vi;
+            pi = (j >> 8) - pS0;
+        } else {
+            j = w_start + (vi - ns_end);
+            pi = nPS + (j >> 8) - pW0;
+        }
+        return kv_off(g, pgs[pi], kvh, j & 255, D);
+    };
+    const float sc = g.attn_scale * kLog2e;
+    f32x16_t oacc[4];
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dd][i] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;
+    for (int k0 = 0; k0 < n; k0 += 32) {
+        // this lane's key row: K for the A operand, V for the transposed tile
+        const bool live = k0 + col < n;
+        const size_t ro = off(min(k0 + col, n - 1)) + 8 * hh;
+        uint4 ka[8], va[8];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(kc + ro + 16 * kk);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) va[kk] = *reinterpret_cast<const uint4*>(vc + ro + 16 * kk);
+        f32x16_t s;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kk]), as_bf16x8(qreg[kk]), s, 0, 0, 0);
+        __syncthreads();                                  // the previous block's V^T reads are done
+        // V^T[d][key col]: d = 16 kk + 8 hh + e; rows past the split stored as zeros
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const uint32_t w4[4] = {live ? va[kk].x : 0u, live ? va[kk].y : 0u, live ? va[kk].z : 0u,
+                                    live ? va[kk].w : 0u};
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const int d = 16 * kk + 8 * hh + 2 * x;
+                Vt[d * kWVtLd + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w4[x] & 0xFFFFu));
+                Vt[(d + 1) * kWVtLd + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w4[x] >> 16));
+            }
+        }
+        // scale, mask, block maximum of this lane's head
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = k0 + (i >> 2) * 8 + 4 * hh + (i & 3);
+            const float v = key < n ? s[i] * sc : -INFINITY;
+            s[i] = v;
+            mt = fmaxf(mt, v);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run, mt);             // finite: the block has a live key
+        if (__ballot(m_new > m_run) != 0ull) {            // some head's maximum rose: rescale
+            const float corr = exp2f(m_run - m_new);
+            l_run *= corr;
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[dd][i] *= corr;
+        }
+        m_run = m_new;
+        uint32_t pb[8];
+        {
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                p[i] = exp2f(s[i] - m_new);
+                l_run += p[i];
+            }
+#pragma unroll
+            for (int x = 0; x < 8; ++x) pb[x] = pack_bf2(p[2 * x], p[2 * x + 1]);
+        }
+        __syncthreads();                                  // the V^T tile is written
+        // O^T += V^T P^T; k-step kk covers keys 16 kk + 4 hh + {0..3, 8..11}
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const uint4 bp = make_uint4(pb[4 * kk], pb[4 * kk + 1], pb[4 * kk + 2], pb[4 * kk + 3]);
+            const int kc0 = 16 * kk + 4 * hh;
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                const bf16_t* vr = &Vt[(32 * dd + col) * kWVtLd + kc0];
+                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                oacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), oacc[dd], 0, 0, 0);
+            }
+        }
+    }
+    // partials: lane holds O^T[32 dd + 8 (i/4) + 4 hh + (i%4)][head col]
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (act) {
+        float* pp = part + (((size_t)b * g.Hq + hq) * nsplit + blockIdx.x) * (D + 2);
+#pragma unroll
+        for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * dd + 8 * r4 + 4 * hh;    // partial records are 8-byte aligned
+                *reinterpret_cast<float2*>(pp + d0) = make_float2(oacc[dd][4 * r4], oacc[dd][4 * r4 + 1]);
+                *reinterpret_cast<float2*>(pp + d0 + 2) = make_float2(oacc[dd][4 * r4 + 2], oacc[dd][4 * r4 + 3]);
+            }
+        if (hh == 0) {
+            pp[D] = m_run;
+            pp[D + 1] = l_tot;
+        }
+    }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(128) void k_win_dec_combine(Geo g, const float* __restrict__ part,
                                                          T* __restrict__ out, int nsplit, int split_keys,
@@ -458,7 +630,10 @@ void win_dec_part(const Geo& g, const void* q, const void* k, const void* v, flo
 template <typename T, int D>
 hipError_t win_dec(const Geo& g, const void* q, const void* k, const void* v, void* out, float* part,
                    int nsplit, int split_keys, int dense, hipStream_t s) {
-    if (g.group <= 1)
+    if (std::is_same<T, bf16_t>::value && D == 128 && g.group <= 32)
+        hipLaunchKernelGGL(k_win_dec_mfma, dim3(nsplit, g.batch * g.Hkv), dim3(64), 0, s, g, (const bf16_t*)q,
+                           (const bf16_t*)k, (const bf16_t*)v, part, nsplit, split_keys, dense);
+    else if (g.group <= 1)
         win_dec_part<T, D, 1>(g, q, k, v, part, nsplit, split_keys, dense, s);
     else if (g.group <= 2)
         win_dec_part<T, D, 2>(g, q, k, v, part, nsplit, split_keys, dense, s);
