@@ -40,8 +40,14 @@ rtp_status hip_status(hipError_t e, const char* what) {
 
 constexpr int kMaxLen = 1 << 20;          // longest supported context: fixed-point masses of every key fit 2^63
 constexpr int kMaxDecodeRows = 4096;      // decode rows (batch * num_ret) of the sparse kernel
-constexpr int kWinSplit = 64;             // keys per workgroup, local-head decode
+constexpr int kWinSplit = 64;             // keys per workgroup, local-head decode (VALU kernel)
+constexpr int kWinSplitMfma = 128;        // keys per workgroup, local-head decode (bf16 MFMA kernel, D = 128)
 constexpr int kDenseSplit = 1024;         // keys per workgroup, dense decode
+
+int win_split(const rtp_layer* L, int dense) {
+    if (dense) return kDenseSplit;
+    return (L->dtype == RTP_BF16 && L->head_dim == 128) ? kWinSplitMfma : kWinSplit;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -215,7 +221,7 @@ int win_keys(const rtp_layer* L, const rtp_cache* C, int dense) {
 
 size_t win_ws_bytes(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q, int dense) {
     if (Q->kind == RTP_CHUNK) return 0;     // the prefill kernel needs no workspace
-    const int split = dense ? kDenseSplit : kWinSplit;
+    const int split = win_split(L, dense);
     const int nsplit = (win_keys(L, C, dense) + split - 1) / split;
     return align256((size_t)C->batch * L->num_q_heads * nsplit * (L->head_dim + 2) * 4);
 }
@@ -239,7 +245,7 @@ rtp_status window_like(const rtp_layer* L, const rtp_cache* C, const rtp_query* 
     const size_t need = win_ws_bytes(L, C, Q, dense);
     if (!ws || ws_bytes < need) return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
     const rtp::Geo g = make_geo(L, C, Q);
-    const int split = dense ? kDenseSplit : kWinSplit;
+    const int split = win_split(L, dense);
     const int nsplit = (win_keys(L, C, dense) + split - 1) / split;
     return hip_status(rtp::launch_window_decode(g, Q->q, C->k, C->v, out, (float*)ws, nsplit, split, dense,
                                                 L->dtype, (hipStream_t)stream),
