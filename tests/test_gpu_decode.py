@@ -190,6 +190,34 @@ def test_edge_cases(lens, p, flat):
             assert check_out(out[t, h], ref, w.dtype) <= 1.0
 
 
+@pytest.mark.parametrize("lens,window,sinks", [
+    ((1, 2, 31, 32, 33), 100, 3),            # fewer keys than one 32-key block; block edges
+    ((127, 128, 129, 300), 100, 3),          # one split of window + sinks, ragged last block
+    ((1000, 700), 300, 8),                   # several 128-key splits, sink run then window run
+])
+def test_bf16_d128_window_and_dense_decode(lens, window, sinks):
+    # the bf16 D = 128 local-head and dense decode run on MFMA (GQA 4:1, some
+    # query heads of a group are retrieval heads and stay unwritten)
+    w = _custom(lens, dtype="bf16", Hq=32, Hkv=8, D=128, ret=(0, 5, 9, 14, 22, 31), window=window, sinks=sinks)
+    say("[gpu] bf16 D=128 window/dense decode", lens, window, sinks)
+    d = Dev(w)
+    d.window()
+    out = out_f32(d.out)
+    dense = torch.zeros_like(d.q)
+    d.dense(dense)
+    den = out_f32(dense)
+    for t in range(w.n_tok):
+        for h in range(w.Hq):
+            g = w.kv_head(h)
+            K, V = synth.as_f32(w.k[t][:, g, :]), synth.as_f32(w.v[t][:, g, :])
+            ref_d = oracle.dense_row(w.q[t, h], K, V, w.row_pos(t), w.attn_scale)
+            assert check_out(den[t, h], ref_d, w.dtype) <= 1.0, ("dense", t, h)
+            if h in w.ret_heads:
+                continue
+            ref_w = oracle.local_row(w.q[t, h], K, V, w.row_pos(t), w.window, w.sinks, w.attn_scale)
+            assert check_out(out[t, h], ref_w, w.dtype) <= 1.0, ("window", t, h)
+
+
 def test_capacity_overflow_reports_needed_size():
     w = _custom((3000, 5000), p=0.99)
     say("[gpu] capacity overflow")
