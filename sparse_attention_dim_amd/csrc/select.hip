@@ -35,6 +35,8 @@
 // Workgroups of one pass never wait on each other: every hand-off between
 // workgroups is a kernel boundary (a device-scope fence per workgroup costs an
 // L2 write-back and invalidate on this multi-XCD part).
+#include <algorithm>
+
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -356,9 +358,12 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     const float s = g.idx_scale;
     const unsigned long long* chist = ws.chist + (size_t)ri.lrow * ws.nchunk * kCB;
     const uint32_t* cmax = ws.cmax + (size_t)ri.lrow * ws.nchunk;
-    uint32_t mk = 0u;
-    for (int c = tid; c < nch; c += 256) mk = max(mk, cmax[c]);
-    mk = wave_max_u32(mk);
+    // one round of loads: the chunk's maximum and total mass (one chunk per
+    // thread, nch <= 256) and p
+    const uint32_t cm = tid < nch ? cmax[tid] : 0u;
+    const unsigned long long ztot = tid < nch ? chist[(size_t)tid * kCB + kCB - 1] : 0ull;
+    const float p = top_p[ri.b];
+    uint32_t mk = wave_max_u32(cm);
     if ((tid & 63) == 0) ured[tid >> 6] = mk;
     if (tid == 0) {
         s_k[0] = kGB;
@@ -369,18 +374,17 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     Plan pl;
     pl.m = key_score(mk);
     double z = 0.0;
-    for (int c = tid; c < nch; c += 256) {
-        const double dc = (double)s * ((double)pl.m - (double)key_score(cmax[c]));
+    if (tid < nch) {
+        const double dc = (double)s * ((double)pl.m - (double)key_score(cm));
         const double f = exp(-dc);
-        dch[c] = dc;
-        fch[c] = f;
-        z += f * (double)chist[(size_t)c * kCB + kCB - 1];
+        dch[tid] = dc;
+        fch[tid] = f;
+        z = f * (double)ztot;
     }
     for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
     if ((tid & 63) == 0) dred[tid >> 6] = z;
     __syncthreads();
     const double Z = dred[0] + dred[1] + dred[2] + dred[3];
-    const float p = top_p[ri.b];
     pl.all = !(p < 1.0f);
     unsigned long long target = (unsigned long long)ceil((double)p * Z);
     if ((double)target > Z) target = (unsigned long long)Z;
@@ -767,21 +771,22 @@ __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut o
 }
 
 // ---------------------------------------------------------------------------
-// Emit.  grid (nchunk, rows), 256 threads: the part of a row's output that
-// belongs to one 4096-key chunk (a slice of the ordered list, or the ordered
-// compaction of the chunk's selected keys).  ROWPTR: the group is small, so
-// every workgroup sums the counts before its row itself, writes its row
-// pointer, and checks the capacity.
+// Emit.  grid (min(nchunk, kEmitWG), rows), 256 threads: workgroup x writes the
+// parts of a row's output that belong to 4096-key chunks x, x + kEmitWG, ...
+// (slices of the ordered list, or the ordered compaction of a chunk's selected
+// keys).  ROWPTR: the group is small, so every workgroup sums the counts before
+// its row itself; the first one writes the row pointer and checks the capacity.
 // ---------------------------------------------------------------------------
+constexpr int kEmitWG = 4;
+
 template <int ROWPTR>
 __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, SelOut out) {
     const int tid = threadIdx.x;
-    const int chunk = blockIdx.x;
+    const int first = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
     const RowState st = ws.st[ri.lrow];
-    if (chunk >= ri.nch) return;
-    const int jbase = chunk * kChunk;
-    if (chunk > 0 && st.mode == 1 && jbase >= st.count) return;   // nothing of this row here
+    if (first >= ri.nch) return;
+    if (first > 0 && st.mode == 1 && first * kChunk >= st.count) return;   // nothing of this row here
     int64_t rbase;
     if (ROWPTR) {
         __shared__ unsigned long long red[8];
@@ -801,50 +806,55 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
         const int64_t carry = out.row_ptr[row0];
         rbase = carry + (int64_t)(red[0] + red[1] + red[2] + red[3]);
         const int64_t total = carry + (int64_t)(red[4] + red[5] + red[6] + red[7]);
-        if (chunk == 0 && tid == 0) out.row_ptr[ri.row + 1] = rbase + st.count;
+        if (first == 0 && tid == 0) out.row_ptr[ri.row + 1] = rbase + st.count;
         if (total > out.capacity) {
-            if (chunk == 0 && tid == 0 && ri.lrow == 0 && *out.status == 0) *out.status = 1;
+            if (first == 0 && tid == 0 && ri.lrow == 0 && *out.status == 0) *out.status = 1;
             return;
         }
     } else {
         rbase = out.row_ptr[ri.row];
     }
     if (*out.status != 0) return;
-    if (st.mode == 0) {
-        for (int k = tid; k < kChunk && jbase + k < ri.L; k += 256) out.idx[rbase + jbase + k] = jbase + k;
-        return;
-    }
-    if (st.mode == 1) {
-        const uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
-        for (int k = tid; k < kChunk && jbase + k < st.count; k += 256) out.idx[rbase + jbase + k] = (int32_t)sl[jbase + k];
-        return;
-    }
     __shared__ uint32_t wcnt[4];
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    int64_t base = rbase + ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
     const int lane = tid & 63, wid = tid >> 6;
-    float dv[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + k * 256 + tid, ri.L - 1)];
-    for (int k = 0; k < 16; ++k) {
-        if (jbase + k * 256 >= ri.L) break;
-        const int j = jbase + k * 256 + tid;
-        bool sel = false;
-        if (j < ri.L) {
-            const uint32_t key = score_key(dv[k]);
-            sel = key > st.Tkey || (key == st.Tkey && j <= st.jT);
+    for (int chunk = first; chunk < ri.nch; chunk += gridDim.x) {
+        const int jbase = chunk * kChunk;
+        if (st.mode == 0) {
+            for (int k = tid; k < kChunk && jbase + k < ri.L; k += 256) out.idx[rbase + jbase + k] = jbase + k;
+            continue;
         }
-        const unsigned long long bal = __ballot(sel);
-        const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0) wcnt[wid] = __popcll(bal);
-        __syncthreads();
-        uint32_t wbase = 0;
-        for (int w = 0; w < wid; ++w) wbase += wcnt[w];
-        const uint32_t tot = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-        const int64_t o = base + wbase + before;
-        if (sel && o < out.capacity) out.idx[o] = j;
-        base += tot;
-        __syncthreads();
+        if (st.mode == 1) {
+            if (jbase >= st.count) break;
+            const uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
+            for (int k = tid; k < kChunk && jbase + k < st.count; k += 256)
+                out.idx[rbase + jbase + k] = (int32_t)sl[jbase + k];
+            continue;
+        }
+        int64_t base = rbase + ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
+        float dv[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + k * 256 + tid, ri.L - 1)];
+        for (int k = 0; k < 16; ++k) {
+            if (jbase + k * 256 >= ri.L) break;
+            const int j = jbase + k * 256 + tid;
+            bool sel = false;
+            if (j < ri.L) {
+                const uint32_t key = score_key(dv[k]);
+                sel = key > st.Tkey || (key == st.Tkey && j <= st.jT);
+            }
+            const unsigned long long bal = __ballot(sel);
+            const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+            if (lane == 0) wcnt[wid] = __popcll(bal);
+            __syncthreads();
+            uint32_t wbase = 0;
+            for (int w = 0; w < wid; ++w) wbase += wcnt[w];
+            const uint32_t tot = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+            const int64_t o = base + wbase + before;
+            if (sel && o < out.capacity) out.idx[o] = j;
+            base += tot;
+            __syncthreads();
+        }
     }
 }
 
@@ -874,11 +884,12 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
     if (scores_only || stage == kSelScorePass) return hipGetLastError();
     hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, top_p, row0, ws);
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
+    const dim3 egrid(std::min(ws.nchunk, kEmitWG), ws.rows);
     if (ws.rows <= kRowsInEmit) {
-        hipLaunchKernelGGL(k_sel_emit<1>, grid, dim3(256), 0, s, g, row0, ws, out);
+        hipLaunchKernelGGL(k_sel_emit<1>, egrid, dim3(256), 0, s, g, row0, ws, out);
     } else {
         hipLaunchKernelGGL(k_sel_rowptr, dim3(1), dim3(kRT), 0, s, row0, ws, out);
-        hipLaunchKernelGGL(k_sel_emit<0>, grid, dim3(256), 0, s, g, row0, ws, out);
+        hipLaunchKernelGGL(k_sel_emit<0>, egrid, dim3(256), 0, s, g, row0, ws, out);
     }
     return hipGetLastError();
 }
