@@ -456,15 +456,19 @@ def main():
     rows = B * w.n_ret
     qlow_buf = torch.empty((rows, 16), dtype=torch.int16, device=dev)
     score_bufs = [torch.empty((rows, L), dtype=torch.float32, device=dev) for _ in inst]
-    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    score_calls = [rtp.indexer_scores(layer, J["cache"], J["query"], J["w_q"], qlow_buf, score_bufs[i],
+                                      prepare=True) for i, J in enumerate(inst)]
+    for c in score_calls:
+        c()
+    # back-to-back launches between one pair of events: prepared calls enqueue
+    # faster than a launch runs, so the span is the launches plus their gaps
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
     for s in range(args.steps):
-        J = inst[s % len(inst)]
-        kev[s][0].record()
-        rtp.indexer_scores(layer, J["cache"], J["query"], J["w_q"], qlow_buf, score_bufs[s % len(inst)])
-        kev[s][1].record()
+        score_calls[s % len(inst)]()
+    k1.record()
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in kev]))
+    k_ms = k0.elapsed_time(k1) / args.steps
     k_achieved = bytes_klow / (k_ms * 1e-3) / 1e9
 
     # --- dense baseline on the same GPU --------------------------------------

@@ -223,10 +223,10 @@ def topp_select_end(layer, cache, query, w_q, top_p, sel, ws, stream=None, prepa
                 (layer, cache, query, sel), prepare)
 
 
-def indexer_scores(layer, cache, query, w_q, q_low, scores, stream=None):
-    _check(load().rtp_indexer_scores(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                     _ptr(w_q), _ptr(q_low), _ptr(scores), scores.shape[1], None, 0,
-                                     _stream(stream)))
+def indexer_scores(layer, cache, query, w_q, q_low, scores, stream=None, prepare=False):
+    return _run("rtp_indexer_scores", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                                       _ptr(q_low), _ptr(scores), scores.shape[1], None, 0, _stream(stream)),
+                (layer, cache, query), prepare)
 
 
 def sparse_attn_workspace(layer, cache, query, capacity: int) -> int:

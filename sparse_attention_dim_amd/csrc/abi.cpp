@@ -379,7 +379,7 @@ size_t rtp_sparse_attn_workspace(const rtp_layer* layer, const rtp_cache* cache,
                                  int64_t capacity) {
     if (check_all(layer, cache, query) || capacity < 0) return 0;
     if (query->kind == RTP_CHUNK && layer->dtype == RTP_BF16 && layer->head_dim == 128)
-        return std::max<size_t>(256, rtp::sparse_prefill_ws_bytes(query->n_tok * layer->num_ret,
+        return std::max<size_t>(256, rtp::sparse_prefill_ws_bytes(query->n_tok, layer->num_ret,
                                                                   query->pos0 + query->n_tok));
     const int64_t rows = (int64_t)query->n_tok * layer->num_ret;
     const int64_t items = sparse_max_items(layer, query, capacity);
@@ -424,7 +424,8 @@ rtp_status rtp_sparse_attn_prefill(const rtp_layer* layer, const rtp_cache* cach
     if (layer->dtype == RTP_BF16 && layer->head_dim == 128) {
         const rtp::Geo g = make_geo(layer, cache, query);
         return hip_status(rtp::launch_sparse_prefill(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
-                                                     sel->status, out, workspace, (hipStream_t)stream),
+                                                     sel->capacity, sel->status, out, workspace,
+                                                     (hipStream_t)stream),
                           "sparse prefill launch");
     }
     const int rows = query->n_tok * layer->num_ret;

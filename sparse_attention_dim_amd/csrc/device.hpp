@@ -24,6 +24,30 @@ template <typename T> __device__ __forceinline__ float ld(const T* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }
 
+// Stage n elements (n a multiple of 16 bytes' worth) into LDS as fp32, every
+// thread of a 256-wide group moving 16-byte pieces; falls back to element
+// loads when the source is not 16-byte aligned.  The caller synchronises.
+template <typename T> __device__ __forceinline__ void stage_f32(const T* __restrict__ src, float* dst, int n,
+                                                                int tid) {
+    constexpr int V = 16 / sizeof(T);
+    if (reinterpret_cast<uintptr_t>(src) & 15) {
+        for (int x = tid; x < n; x += 256) dst[x] = ld(src + x);
+        return;
+    }
+    for (int x = tid * V; x < n; x += 256 * V) {
+        const uint4 u = *reinterpret_cast<const uint4*>(src + x);
+        if (sizeof(T) == 4) {
+            *reinterpret_cast<float4*>(dst + x) =
+                make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+        } else {
+            *reinterpret_cast<float4*>(dst + x) = make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                                                              __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+            *reinterpret_cast<float4*>(dst + x + 4) = make_float4(__uint_as_float(u.z << 16), __uint_as_float(u.z & 0xFFFF0000u),
+                                                                  __uint_as_float(u.w << 16), __uint_as_float(u.w & 0xFFFF0000u));
+        }
+    }
+}
+
 template <typename T> __device__ __forceinline__ void st(T* p, float v);
 template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }

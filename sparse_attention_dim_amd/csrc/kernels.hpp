@@ -118,11 +118,13 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
 
 // Sparse attention of the retrieval heads of a prefill chunk (bf16, D = 128):
 // MFMA over the union of 64 consecutive rows' selected sets, masked per row.
-// Workspace: per-row window offsets and, with more than one 2^16-key window,
-// the windows' partial results.
-size_t sparse_prefill_ws_bytes(int rows, int n_keys);
+// Workspace: per-row window offsets, per (tile, window) union bitmaps and
+// sizes, and the partial results of every row, window and split.  idx_n is
+// the number of readable entries of idx (the CSR capacity).
+size_t sparse_prefill_ws_bytes(int n_tok, int n_ret, int n_keys);
 hipError_t launch_sparse_prefill(const Geo& g, const void* q, const void* k, const void* v, const int64_t* row_ptr,
-                                 const int32_t* idx, const int32_t* status, void* out, void* ws, hipStream_t s);
+                                 const int32_t* idx, int64_t idx_n, const int32_t* status, void* out, void* ws,
+                                 hipStream_t s);
 
 // Chunked-prefill attention (bf16, D = 128) of the heads g.hlist[0..n_hlist):
 // sinks + causal window, or dense causal.

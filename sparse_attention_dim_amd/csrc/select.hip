@@ -95,8 +95,8 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     __shared__ float wmax[4];
     __shared__ unsigned long long hist[kCB];
     __shared__ unsigned hcnt[kCB];
-    __shared__ float qrow[128];
-    __shared__ float wq[128 * kIdx];
+    __shared__ __align__(16) float qrow[128];
+    __shared__ __align__(16) float wq[128 * kIdx];
     __shared__ float qs[kIdx];
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         const int h = g.ret_heads[ri.r];
         const T* qp = q + ((size_t)ri.t * g.Hq + h) * g.D;
         const T* wp = w_q + (size_t)ri.r * g.D * kIdx;
-        for (int x = tid; x < g.D; x += 256) qrow[x] = ld(qp + x);
-        for (int x = tid; x < g.D * kIdx; x += 256) wq[x] = ld(wp + x);
+        stage_f32(qp, qrow, g.D, tid);
+        stage_f32(wp, wq, g.D * kIdx, tid);
     }
     if (STATS && tid < kCB) {
         hist[tid] = 0ull;

@@ -243,11 +243,11 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     const int h_q = g.ret_heads[r];
-    __shared__ float wq[128 * 16];
+    __shared__ __align__(16) float wq[128 * 16];
     __shared__ float qs[kTR][16];
     __shared__ uint32_t rmax[kTR];
     __shared__ uint32_t kmax_bits;
-    for (int x = tid; x < g.D * 16; x += 256) wq[x] = bf2f(w_q[(size_t)r * g.D * 16 + x]);
+    stage_f32(w_q + (size_t)r * g.D * 16, wq, g.D * 16, tid);
     if (tid < kTR) rmax[tid] = 0u;
     if (tid == 0) kmax_bits = 0u;
     __syncthreads();
