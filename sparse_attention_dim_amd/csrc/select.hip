@@ -102,15 +102,29 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int jbase = chunk * kChunk;
 
-    // Unconditional loads: page ids are uniform per 256-key step (clamped to the
-    // row's last page) and slots past the row's end are read but never used.
-    uint4 buf[8];
+    // The chunk's 16 page ids, one per lane (clamped to the row's last page;
+    // slots past the row's end are read but never used), then read out by
+    // lane number: the loads of a 4-page group wait on no scalar load.
     const int last_page = (ri.L - 1) >> 8;
+    const int my_page = bt[min((jbase >> 8) + (tid & 15), last_page)];
+    // q and W_q into registers first (16-byte pieces: W_q is at most 512 of
+    // them, q at most 32), so that their wait does not cover the key loads
+    const int h = g.ret_heads[ri.r];
+    const T* qp = q + ((size_t)ri.t * g.Hq + h) * g.D;
+    const T* wp = w_q + (size_t)ri.r * g.D * kIdx;
+    constexpr int V = 16 / sizeof(T);
+    const bool vec = ((reinterpret_cast<uintptr_t>(qp) | reinterpret_cast<uintptr_t>(wp)) & 15) == 0;
+    uint4 wreg[2], qreg = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        wreg[k] = vec && (tid + 256 * k) * V < g.D * kIdx ? reinterpret_cast<const uint4*>(wp)[tid + 256 * k]
+                                                           : make_uint4(0, 0, 0, 0);
+    if (vec && tid * V < g.D) qreg = reinterpret_cast<const uint4*>(qp)[tid];
+    uint4 buf[8];
     auto load_group = [&](int k0) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int pi = min((jbase >> 8) + k0 + u, last_page);
-            const int page = bt[pi];
+            const int page = __builtin_amdgcn_readlane(my_page, k0 + u);
             const uint4* kp = reinterpret_cast<const uint4*>(
                 k_low + (((size_t)page * g.n_ret + ri.r) * kBlk + tid) * kIdx);
             buf[2 * u] = kp[0];
@@ -119,11 +133,24 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     };
     load_group(0);
     // q_low: the query row and W_q staged through LDS, the fixed-order chain
-    // over d run by 16 lanes while the first loads are in flight
-    {
-        const int h = g.ret_heads[ri.r];
-        const T* qp = q + ((size_t)ri.t * g.Hq + h) * g.D;
-        const T* wp = w_q + (size_t)ri.r * g.D * kIdx;
+    // over d run by 16 lanes while the first key loads are in flight
+    if (vec) {
+        const auto put = [&](const uint4& u, float* dst) {
+            if (sizeof(T) == 4) {
+                *reinterpret_cast<float4*>(dst) = make_float4(__uint_as_float(u.x), __uint_as_float(u.y),
+                                                              __uint_as_float(u.z), __uint_as_float(u.w));
+            } else {
+                float f[8];
+                unpack8(u, f);
+                *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+                *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+            }
+        };
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            if ((tid + 256 * k) * V < g.D * kIdx) put(wreg[k], wq + (tid + 256 * k) * V);
+        if (tid * V < g.D) put(qreg, qrow + tid * V);
+    } else {
         stage_f32(qp, qrow, g.D, tid);
         stage_f32(wp, wq, g.D * kIdx, tid);
     }
@@ -160,11 +187,14 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 #pragma unroll
             for (int c = 0; c < kIdx; ++c) acc = __builtin_fmaf(qv[c], kf[c], acc);
             dv[k0 + u] = acc;
-            if (j < ri.L) {
-                srow[j] = acc;
-                mx = fmaxf(mx, acc);
-            }
+            if (j < ri.L) mx = fmaxf(mx, acc);
         }
+    }
+    // the scores, after every key load was issued
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int j = jbase + k * 256 + tid;
+        if (j < ri.L) srow[j] = dv[k];
     }
     if (!STATS) return;
     mx = wave_max(mx);
