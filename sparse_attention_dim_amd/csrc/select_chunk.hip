@@ -121,24 +121,34 @@ __device__ __forceinline__ int bin_of(float x) {
 
 // Visits tiles first, first + stride, ... < ntile (a wave-uniform sequence)
 // with D tile loads in flight: the A operand of tile it + D stride is
-// requested before tile it is processed.
-template <int D, typename Load, typename Body>
-__device__ __forceinline__ void tile_loop(int first, int stride, int ntile, Load load, Body body) {
+// requested before tile it is processed, and the page id that operand's
+// address needs was requested D tiles earlier still (so waiting for it never
+// waits for the operand loads issued since).  page(it) reads the page table;
+// load(it, page) reads the tile's A operand.
+template <int D, typename Page, typename Load, typename Body>
+__device__ __forceinline__ void tile_loop(int first, int stride, int ntile, Page page, Load load, Body body) {
+    // the loads run unconditionally on clamped tile numbers (the few past the
+    // end repeat the last tile), so their waits count exactly
+    const auto cl = [&](int it) { return min(it, ntile - 1); };
+    int pring[D];
     uint4 ring[D];
+#pragma unroll
+    for (int x = 0; x < D; ++x) pring[x] = page(cl(first + x * stride));
 #pragma unroll
     for (int x = 0; x < D; ++x) {
         const int it = first + x * stride;
-        ring[x] = it < ntile ? load(it) : make_uint4(0, 0, 0, 0);
+        ring[x] = load(cl(it), pring[x]);
+        pring[x] = page(cl(it + D * stride));
     }
     for (int it0 = first; it0 < ntile; it0 += D * stride) {
 #pragma unroll
         for (int x = 0; x < D; ++x) {
             const int it = it0 + x * stride;
-            if (it < ntile) {
-                const uint4 cur = ring[x];
-                if (it + D * stride < ntile) ring[x] = load(it + D * stride);
-                body(it, cur);
-            }
+            const uint4 cur = ring[x];
+            const int nxt = it + D * stride;
+            ring[x] = load(cl(nxt), pring[x]);
+            pring[x] = page(cl(nxt + D * stride));
+            if (it < ntile) body(it, cur);
         }
     }
 }
@@ -180,10 +190,10 @@ struct TileCtx {
     const bf16_t* k_low;
     int n_ret;
     uint4 qb;
-    __device__ uint4 load(int it) const {
+    __device__ int page(int it) const { return bt[min(it * 32 + lr, L_max - 1) >> 8]; }
+    __device__ uint4 load(int it, int pg) const {
         const int kk = min(it * 32 + lr, L_max - 1);
-        const int page = bt[kk >> 8];
-        return *reinterpret_cast<const uint4*>(k_low + (((size_t)page * n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
+        return *reinterpret_cast<const uint4*>(k_low + (((size_t)pg * n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
     }
     __device__ f32x16_t mfma(const uint4& a) const {
         f32x16_t acc;
@@ -271,7 +281,8 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
     __syncthreads();
     const TileCtx tc = tile_ctx(g, k_low, qs);
     float m_e = -INFINITY;
-    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
+    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
+                    [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
         const f32x16_t sc = tc.mfma(cur);
         if (it < tc.nfull) {
 #pragma unroll
@@ -334,7 +345,8 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
         double* hrow = &hist[0][tc.lr];
         uint32_t* crow = &hcnt[0][tc.lr];
-        tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
+        tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
+                    [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
             if (it < tc.nfull) {
 #pragma unroll
@@ -502,8 +514,15 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         ++bp;
         ++nreal;
     };
-    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.load(it); }, [&](int it, const uint4& cur) {
+    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
+                    [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
         const f32x16_t sc = tc.mfma(cur);
+        // U is a small part of the keys: one test of the lane's largest score
+        // skips nearly every tile
+        float mx = sc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+        if (!__ballot(mx >= e_fast)) return;
         if (it < tc.nfull) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
@@ -614,7 +633,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     const bool row_ok = tc.row_ok;
     const int pos = tc.pos;
     const int ntile = tc.ntile, nfull = tc.nfull;
-    const auto load_a = [&](int it) { return tc.load(it); };
+    const auto page_a = [&](int it) { return tc.page(it); };
+    const auto load_a = [&](int it, int pg) { return tc.load(it, pg); };
     const auto mfma_tile = [&](const uint4& a) { return tc.mfma(a); };
     const auto key_of = [&](int it, int i) { return tc.key_of(it, i); };
 
@@ -651,7 +671,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 #pragma unroll
         for (int c = 0; c < 16; ++c) qv[c] = qs[lr][c];
         unsigned long long zacc = 0ull;
-        tile_loop<kPre>(wid, 4, ntile, load_a, [&](int it, const uint4& cur) {
+        tile_loop<kPre>(wid, 4, ntile, page_a, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
             // which of this lane's pairs need an exact score
             uint32_t need = 0;
@@ -1357,13 +1377,13 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
     const int64_t wpos = row_ok ? row_ptr[row] : 0;
     const int64_t lim = row_ok ? row_ptr[row + 1] - wpos : 0;
     int run_sel = 0, run_tie = 0;
-    auto load_a = [&](int it) {
+    auto page_a = [&](int it) { return bt[min(it * 32 + lr, L_max - 1) >> 8]; };
+    auto load_a = [&](int it, int pg) {
         const int kk = min(it * 32 + lr, L_max - 1);
-        const int page = bt[kk >> 8];
         return *reinterpret_cast<const uint4*>(
-            k_low + (((size_t)page * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
+            k_low + (((size_t)pg * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
     };
-    tile_loop<kPre>(0, 1, ntile, load_a, [&](int it, const uint4& cur) {
+    tile_loop<kPre>(0, 1, ntile, page_a, load_a, [&](int it, const uint4& cur) {
         f32x16_t sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
