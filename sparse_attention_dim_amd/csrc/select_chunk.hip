@@ -54,6 +54,7 @@ constexpr int kNB = 64;          // radix buckets per level
 constexpr int kNBP = kNB + 1;
 constexpr int kCapC = 128;       // candidates of one cut bucket sorted in LDS
 constexpr int kSmallU = 8192;    // U sorted by the per-row resolve kernel
+constexpr int kTinyU = 1024;     // U sorted by the small-row resolve kernel
 constexpr int kSegMax = 16384;   // largest segment (U plus padding), sorted by the large-row kernel
 constexpr int kSegBlk = 16;      // segment slots reserved at a time by one lane of the third pass
 constexpr int kSegPad = 8 * kSegBlk;   // 8 writers per row (4 waves x 2 halves): their last blocks' slack
@@ -1270,10 +1271,29 @@ __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restr
         if (threadIdx.x == 0) counts[row] = -1;
         return;
     }
+    if (cr.count <= kTinyU) return;                     // the small-row kernel's
     __shared__ unsigned long long sk[kSmallU];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
     __shared__ ResolveSmem sm;
     resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+}
+
+// Rows with U of at most kTinyU keys: the same resolve on 256 threads and a
+// quarter of the LDS, so that several rows share a CU.
+constexpr int kRTS = 256;
+__global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* __restrict__ rows,
+                                                             const bf16_t* __restrict__ k_low,
+                                                             const uint16_t* __restrict__ qlow,
+                                                             const float* __restrict__ top_p,
+                                                             unsigned long long* __restrict__ pool,
+                                                             int* __restrict__ counts) {
+    const int row = blockIdx.x;
+    const CRow cr = rows[row];
+    if (cr.mode != kBuf || cr.bad || cr.count > kTinyU) return;
+    __shared__ unsigned long long sk[kTinyU];
+    __shared__ unsigned long long scan_sh[kRTS / 64 + 1];
+    __shared__ ResolveSmem sm;
+    resolve_row<kTinyU, kRTS>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
 }
 
 // Rows with U in (kSmallU, kSegMax]: a fixed grid of 512-thread workgroups
@@ -1546,6 +1566,8 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
     hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, (const bf16_t*)k_low, qlow, top_p,
                        pool, counts);
+    hipLaunchKernelGGL(k_csel_resolve_small, dim3(rows), dim3(kRTS), 0, s, g, crow, (const bf16_t*)k_low, qlow,
+                       top_p, pool, counts);
     hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 512)), dim3(kRTL), 0, s, g, crow, rows,
                        (const bf16_t*)k_low, qlow, top_p, pool, counts);
     hipLaunchKernelGGL(k_csel_rowptr, dim3(1), dim3(1024), 0, s, counts, rows, out.row_ptr, out.capacity,
