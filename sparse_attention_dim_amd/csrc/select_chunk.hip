@@ -1116,10 +1116,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     // ---- the keys above the cut and the ties at it, as (index << 1 | tie),
     // sorted ascending; then the ties past the first ntie dropped.  Each
     // writer's entries ascend in slot order, so the kept keys are 8 sorted
-    // runs: every thread takes a contiguous range of slots, the runs are
-    // placed at stride R (odd ones reversed, padded with ~0), and only the
-    // last three levels of a bitonic sort remain.  Runs too long for that
-    // layout take the whole sort.
+    // runs (every thread takes a contiguous range of slots), merged by rank.
     uint32_t* sv = reinterpret_cast<uint32_t*>(sk);     // 2 CAP words
     const int sp = (slots + NT - 1) / NT;                // <= PER
     const int s0 = min(tid * sp, slots);
@@ -1145,33 +1142,17 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     const auto field = [](unsigned long long a, unsigned long long b, int w) {
         return (int)(((w < 4 ? a : b) >> (16 * (w & 3))) & 0xFFFFull);
     };
-    int nk = 0, rmax = 0;
+    int nk = 0, cnt8[8], rb[8];                          // block-uniform: kept in scalar registers
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        const int t = field(tlo, thi, w);
-        nk += t;
-        rmax = max(rmax, t);
+        cnt8[w] = __builtin_amdgcn_readfirstlane(field(tlo, thi, w));
+        rb[w] = nk;                                      // run w at sv[rb[w] ..), contiguous
+        nk += cnt8[w];
     }
-    int R = 1;
-    while (R < rmax) R <<= 1;
-    const bool runs = 8 * R <= 2 * CAP;
-    int N2 = 1;
-    while (N2 < nk) N2 <<= 1;
-    const int NS = runs ? 8 * R : N2;                    // sorted length
     {
         int off[8];
 #pragma unroll
         for (int w = 0; w < 8; ++w) off[w] = field(elo, ehi, w);
-        // in the whole-sort layout the runs simply follow each other
-        int rb[8];
-        {
-            int acc = 0;
-#pragma unroll
-            for (int w = 0; w < 8; ++w) {
-                rb[w] = acc;
-                acc += field(tlo, thi, w);
-            }
-        }
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
             const int w = (int)(vals[x] & 15u);
@@ -1183,51 +1164,56 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
                     q = off[u]++;
                     b = rb[u];
                 }
-            const int p = runs ? (w * R + ((w & 1) ? R - 1 - q : q)) : b + q;
-            sv[p] = vals[x] >> 4;
+            sv[b + q] = vals[x] >> 4;
         }
-    }
-    // padding: the free end of an ascending run, the free start of a
-    // descending one, or the tail of the whole sort
-    for (int p = tid; p < NS; p += NT) {
-        bool pad;
-        if (runs) {
-            const int w = p / R, o = p - w * R;
-            const int t = field(tlo, thi, w);
-            pad = (w & 1) ? o < R - t : o >= t;
-        } else {
-            pad = p >= nk;
-        }
-        if (pad) sv[p] = 0xFFFFFFFFu;
     }
     __syncthreads();
-    for (int k = runs ? 2 * R : 2; k <= NS; k <<= 1)
-        for (int jj = k >> 1; jj > 0; jj >>= 1) {
-            for (int i = tid; i < NS; i += NT) {
-                const int ixj = i ^ jj;
-                if (ixj > i) {
-                    const uint32_t x = sv[i], y = sv[ixj];
-                    const bool asc = (i & k) == 0;
-                    if (asc ? (x > y) : (x < y)) {
-                        sv[i] = y;
-                        sv[ixj] = x;
-                    }
-                }
+    // the merged order: a value's place is the count of values below it in
+    // the 8 runs (a binary search in each; the values are distinct indices,
+    // so in its own run that count is its place there).  Written to the
+    // second half of the area.
+    // The searches run in lockstep: the same halving step for all 8 runs (read
+    // positions clamped to each run), so their LDS reads overlap.
+    uint32_t* so = sv + CAP;
+    int top = 1;
+    {
+        int mc = 1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) mc = max(mc, cnt8[u]);
+        while (2 * top <= mc) top <<= 1;
+    }
+    for (int i = tid; i < nk; i += NT) {
+        const uint32_t v = sv[i];
+        int lo[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) lo[u] = 0;
+        for (int step = top; step > 0; step >>= 1) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = lo[u] + step;
+                const int n = cnt8[u];
+                const uint32_t y = n > 0 ? sv[rb[u] + min(t, n) - 1] : 0xFFFFFFFFu;
+                lo[u] = (t <= n && y < v) ? t : lo[u];
             }
-            __syncthreads();
         }
+        int P = 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) P += lo[u];
+        so[P] = v;
+    }
+    __syncthreads();
     // ties in index order: each thread a contiguous run of the sorted list
     const int per = (nk + NT - 1) / NT;
     const int r0 = min(tid * per, nk), r1 = min(r0 + per, nk);
     unsigned long long tl = 0ull;
-    for (int i = r0; i < r1; ++i) tl += sv[i] & 1u;
+    for (int i = r0; i < r1; ++i) tl += so[i] & 1u;
     unsigned long long ttot;
     const unsigned long long tbase = block_excl_scan_u64<NT>(tl, &ttot, scan_sh);
     unsigned long long kl = 0ull;
     {
         unsigned long long tr = tbase;
         for (int i = r0; i < r1; ++i) {
-            const bool tie = sv[i] & 1u;
+            const bool tie = so[i] & 1u;
             if (!tie || tr < (unsigned long long)ntie) ++kl;
             if (tie) ++tr;
         }
@@ -1238,7 +1224,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     {
         unsigned long long tr = tbase, o = obase;
         for (int i = r0; i < r1; ++i) {
-            const uint32_t v = sv[i];
+            const uint32_t v = so[i];
             const bool tie = v & 1u;
             if (!tie || tr < (unsigned long long)ntie) ubi[o++] = v >> 1;
             if (tie) ++tr;
