@@ -9,7 +9,10 @@ The prefill leg times one chunk of one layer the same way (top-p selection of
 every chunk row, sparse prefill attention, window prefill attention on the
 second stream) at two sizes: 4096 rows at context 131072 and 8192 rows at
 context 1048576, next to dense causal attention of the same chunk on the same
-GPU, and reports tokens/s/layer and the speedup.  The same
+GPU, and reports tokens/s/layer and the speedup, plus the share of the sparse
+tiles' rows x union grid the rows' own sets fill; a third run of the 131072
+workload with independent query rows (no runs on one cluster) is the stress
+case of those union tiles.  The same
 step captured as one HIP graph per layer instance is timed too and reported
 beside it. (decode bf16, batch 8, context 131072, 32 query / 8 KV heads, head dim
 128, 6 retrieval heads, top-p 0.95, window 2048 + 64 sinks).  Inputs are
@@ -152,10 +155,27 @@ def cpu_baseline(w, n_seq: int, threads: int):
     return dt, sizes
 
 
-def prefill_leg(cfg: int, steps: int):
+def union_useful(rp, ix, n_tok: int, n_ret: int, m: int = 64) -> float:
+    """Share of the sparse prefill tiles' rows x union grid that the rows'
+    own sets fill: sum |S_i| / sum over tiles of (rows x |union of S_i|),
+    tiles of m consecutive rows of one retrieval head."""
+    import numpy as np
+
+    grid = 0
+    for r in range(n_ret):
+        for t0 in range(0, n_tok, m):
+            rows = [t * n_ret + r for t in range(t0, min(n_tok, t0 + m))]
+            parts = [ix[rp[i]: rp[i + 1]] for i in rows]
+            grid += len(rows) * len(np.unique(np.concatenate(parts)))
+    return float(rp[-1]) / grid if grid else 0.0
+
+
+def prefill_leg(cfg: int, steps: int, run_mean: int | None = None, dense: bool = True):
     """One prefill chunk of one layer: eager select + sparse prefill on the
     main stream, window prefill on a second stream; dense causal attention of
-    the same chunk for comparison."""
+    the same chunk for comparison.  run_mean: the workload's generator with
+    another mean run length of query rows on one cluster (1: independent
+    rows, the stress case of the union tiles)."""
     import numpy as np
     import torch
 
@@ -165,7 +185,11 @@ def prefill_leg(cfg: int, steps: int):
 
     dev = torch.device("cuda:0")
     t0 = time.time()
-    w = synth.config(cfg)
+    if run_mean is None:
+        w = synth.config(cfg)
+    else:
+        assert cfg == 3
+        w = synth.cluster_chunk(seed=1003, run_mean=run_mean, name="prefill_bf16_C4096_L131072_run%d" % run_mean)
     L = int(w.seq_lens[0])
     log("[bench] prefill %s generated in %.1fs" % (w.name, time.time() - t0))
     layer = rtp.make_layer(w.Hq, w.Hkv, w.D, rtp_dtype(w.dtype), w.ret_heads, w.window, w.sinks,
@@ -236,17 +260,21 @@ def prefill_leg(cfg: int, steps: int):
     rp = row_ptr.cpu().numpy()
     sizes = np.diff(rp)
     n_sel = int(rp[-1])
-    ws_d = torch.empty(rtp.dense_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
-    dout = torch.zeros_like(q)
-    rtp.dense_attn(layer, cache, query, dout, ws_d)
-    torch.cuda.synchronize()
-    a.record()
-    nd = 2
-    for _ in range(nd):
+    useful = union_useful(rp, idx[:n_sel].cpu().numpy(), w.n_tok, w.n_ret)
+    dense_ms = None
+    if dense:
+        ws_d = torch.empty(rtp.dense_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
+        dout = torch.zeros_like(q)
         rtp.dense_attn(layer, cache, query, dout, ws_d)
-    b.record()
-    torch.cuda.synchronize()
-    dense_ms = a.elapsed_time(b) / nd
+        torch.cuda.synchronize()
+        a.record()
+        nd = 2
+        for _ in range(nd):
+            rtp.dense_attn(layer, cache, query, dout, ws_d)
+        b.record()
+        torch.cuda.synchronize()
+        dense_ms = a.elapsed_time(b) / nd
+        del ws_d
     # algorithmic flops: QK and PV, 2 D flops each per (query head, key) pair
     f_pair = 4 * w.D
     sp_flops = n_sel * f_pair
@@ -262,12 +290,14 @@ def prefill_leg(cfg: int, steps: int):
                              "mean": round(float(sizes.mean()), 1), "max": int(sizes.max())},
         "sparse_tflops": round(sp_flops / (sp_t * 1e-3) / 1e12, 2),
         "sparse_mfma_frac": round(sp_flops / (sp_t * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 5),
+        "sparse_union_useful": round(useful, 4),
         "window_tflops": round(win_pairs * f_pair / (win_t * 1e-3) / 1e12, 2),
-        "dense_ms": round(dense_ms, 3),
-        "dense_tflops": round(dense_pairs * f_pair / (dense_ms * 1e-3) / 1e12, 2),
-        "speedup_vs_dense": round(dense_ms / step_ms, 3),
     }
-    del pc, cache, idx, ws_sel, ws_sp, ws_win, ws_d
+    if dense_ms is not None:
+        res.update({"dense_ms": round(dense_ms, 3),
+                    "dense_tflops": round(dense_pairs * f_pair / (dense_ms * 1e-3) / 1e12, 2),
+                    "speedup_vs_dense": round(dense_ms / step_ms, 3)})
+    del pc, cache, idx, ws_sel, ws_sp, ws_win
     torch.cuda.empty_cache()
     return res
 
@@ -509,7 +539,8 @@ def main():
 
     prefill = None
     if not args.no_prefill:
-        prefill = {"128k": prefill_leg(3, args.prefill_steps), "1m": prefill_leg(4, max(1, args.prefill_steps // 2))}
+        prefill = {"128k": prefill_leg(3, args.prefill_steps), "1m": prefill_leg(4, max(1, args.prefill_steps // 2)),
+                   "128k_independent_rows": prefill_leg(3, args.prefill_steps, run_mean=1, dense=False)}
 
     res = {
         "metric": METRIC,
