@@ -18,12 +18,13 @@
 //   P1  (k_csel_max) q_low and the row maxima of e: m' = max e + delta >=
 //       max d (the largest key norm comes from a pre-pass over the head's
 //       indexer keys);
-//   P2  (k_csel_hist) mass and count histograms over x = s (m' - e) in bins of
-//       1/4 (weights exp(-x) summed in fp64 LDS atomics); the cut bin with a
+//   P2  (k_csel_hist) mass histograms over x = s (m' - e) in bins of 1/4
+//       (weights exp(-x) summed in fp64 LDS atomics); the cut bin with a
 //       target raised by a margin that covers the approximation;
 //       U = bins <= cut + 1.  Bins are far wider than s delta, so every key
 //       ranked at or above the exact cut is in U.  Rows whose U is small
-//       enough get a segment of a shared pool, sized by the count histogram;
+//       enough get a segment of a shared pool, sized by an upper bound of
+//       U's size from the masses (a key of bin b weighs at least e^-(b+1)/4);
 //   P3  (k_csel_rec) for those rows, the key indices of U into the segment.
 //       The resolve pass forms U's exact scores and exact fixed-point
 //       weights, U's exact mass (keys outside U enter the total with their
@@ -62,6 +63,9 @@ constexpr int kPoolPerRow = 4096;   // pool entries per row in the recommended w
 constexpr int kNormKeys = 4096;  // keys per block of the key-norm pre-pass
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr unsigned long long kNoSeg = ~0ull;
+
+// slots of a row's pool segment for a bound ub of U's size
+__device__ __forceinline__ uint32_t seg_slots(uint32_t ub) { return min(ub, (uint32_t)(kSegMax - kSegPad)) + kSegPad; }
 
 // modes of a row
 constexpr int kAll = 0;          // p >= 1: every key
@@ -172,7 +176,7 @@ struct CState {
     float e_thr;     // a pair is in U iff its MFMA score e >= e_thr
     float edge;      // exact scores of keys outside U are <= edge
     uint32_t klo, khi, shift;   // exact-score key range of the level path and its first shift
-    uint32_t ucount; // keys of U (count histogram)
+    uint32_t ucount; // keys of U: an upper bound from the mass histogram (exact when U is every key)
     int mode;        // kAll or kLevel
     int uend;        // last P2 bin of U
     int pad0, pad1;
@@ -309,10 +313,10 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// P2.  Mass and count histograms over x = s (m' - e) in bins of 1/4 (weights
-// exp(-x) summed in fp64 LDS atomics); the cut bin with a target raised by a
-// margin that covers the approximation; U = bins <= cut + 1; pool segments for
-// the rows whose U is small enough.
+// P2.  Mass histograms over x = s (m' - e) in bins of 1/4 (weights exp(-x)
+// summed in fp64 LDS atomics); the cut bin with a target raised by a margin
+// that covers the approximation; U = bins <= cut + 1; pool segments, sized
+// by a bound of U's size, for the rows whose U is small enough.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restrict__ k_low,
                                                    const float* __restrict__ top_p,
@@ -322,11 +326,10 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const float s = g.idx_scale;
     const float sB = s * kBinsPerX;
-    __shared__ double hist[kHB][kTR];
-    __shared__ uint32_t hcnt[kHB][kTR];                 // (52 KB of LDS in all: three workgroups per CU)
+    __shared__ double hist[kHB][kTR];                   // (36 KB of LDS in all: four workgroups per CU)
     __shared__ float qs[kTR][16];
     __shared__ float r_mp[kTR], r_delta[kTR];
-    __shared__ uint32_t r_ucount[kTR];
+    __shared__ uint32_t r_ucount[kTR], r_ulow[kTR];
     __shared__ int r_mode[kTR];
     __shared__ unsigned long long r_seg[kTR];
     load_qs(g, qlow, qs);
@@ -338,14 +341,12 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         r_delta[tid] = c->delta;
     }
     for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
-    for (int x = tid; x < kHB * kTR; x += 256) (&hcnt[0][0])[x] = 0u;
     __syncthreads();
     const TileCtx tc = tile_ctx(g, k_low, qs);
     const float mpB = r_mp[tc.lr] * sB;
     {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
         double* hrow = &hist[0][tc.lr];
-        uint32_t* crow = &hcnt[0][tc.lr];
         tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
@@ -355,7 +356,6 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                     const float x = bin_x(sc[i], sB, mpB);
                     const int b = bin_of(x);
                     atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
-                    atomicAdd(&crow[b * kTR], 1u);
                 }
             } else {
 #pragma unroll
@@ -364,7 +364,6 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                         const float x = bin_x(sc[i], sB, mpB);
                         const int b = bin_of(x);
                         atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
-                        atomicAdd(&crow[b * kTR], 1u);
                     }
                 }
             }
@@ -411,9 +410,24 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
             const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
             double light = 0.0;
             for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
-            uint32_t uc = 0;
-            for (int b = 0; b <= ue; ++b) uc += hcnt[b][row];
+            // keys of U, bounded from above by the masses: a key of bin b
+            // (x in [b, b + 1)) weighs at least e^-(b+1)/4, up to the exp2
+            // rounding; every key when U is all of them
+            const uint32_t n_keys = (uint32_t)(g.pos0 + t0 + row + 1);
+            uint32_t uc = n_keys, ul = n_keys;
+            if (ue < kHB - 1) {
+                // and from below (a key of bin b weighs at most e^-b/4)
+                double ub = 0.0, lb = 0.0;
+                for (int b = 0; b <= ue; ++b)
+                    if (hist[b][row] > 0.0) {
+                        ub += ceil(hist[b][row] * exp(0.25 * (double)(b + 1)) * (1.0 + 0x1.0p-20)) + 1.0;
+                        lb += floor(hist[b][row] * exp(0.25 * (double)b) * (1.0 - 0x1.0p-20));
+                    }
+                uc = ub < (double)n_keys ? (uint32_t)ub : n_keys;
+                ul = lb < (double)uc ? (uint32_t)lb : uc;
+            }
             o.ucount = uc;
+            r_ulow[row] = ul;
             o.uend = ue;
             o.light = (unsigned long long)__double2ll_rn(light * kFix);
             const double mp = (double)o.mp;
@@ -450,18 +464,21 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     __syncthreads();
     // pool segments for the rows whose U is small enough (one allocation per
     // workgroup; a full pool sends the rows to the radix levels)
+    // A row whose U may fit (its lower bound does) gets a segment of its upper
+    // bound, at most the largest segment; the recording pass sends a row that
+    // overflows it to the radix levels.
     if (tid == 0) {
         unsigned long long tot = 0;
         for (int row = 0; row < n_valid; ++row)
-            if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad)) tot += r_ucount[row] + kSegPad;
+            if (r_mode[row] == kLevel && r_ulow[row] <= (uint32_t)(kSegMax - kSegPad)) tot += seg_slots(r_ucount[row]);
         if (tot) {
             const unsigned long long base = atomicAdd(pool_ctr, tot);
             if (base + tot <= pool_cap) {
                 unsigned long long off = base;
                 for (int row = 0; row < n_valid; ++row)
-                    if (r_mode[row] == kLevel && r_ucount[row] <= (uint32_t)(kSegMax - kSegPad)) {
+                    if (r_mode[row] == kLevel && r_ulow[row] <= (uint32_t)(kSegMax - kSegPad)) {
                         st[(size_t)(t0 + row) * g.n_ret + r].seg = off;
-                        off += r_ucount[row] + kSegPad;
+                        off += seg_slots(r_ucount[row]);
                     }
             }
         }
@@ -475,7 +492,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
 // (mode kBuf) follows; its exact scores are formed by the resolve pass.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restrict__ k_low,
-                                                  const uint16_t* __restrict__ qlow, const CState* __restrict__ st,
+                                                  const uint16_t* __restrict__ qlow, CState* __restrict__ st,
                                                   CRow* __restrict__ rows_out, unsigned long long* __restrict__ pool) {
     const int tid = threadIdx.x, wid = tid >> 6;
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
@@ -500,7 +517,7 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
     const int lr = tc.lr;
     const bool pooled = tc.row_ok && rs[lr].mode == kLevel && rs[lr].seg != kNoSeg;
     const unsigned long long sg = pooled ? rs[lr].seg : 0ull;
-    const uint32_t scap = pooled ? rs[lr].ucount + kSegPad : 0u;
+    const uint32_t scap = pooled ? seg_slots(rs[lr].ucount) : 0u;
     const float e_fast = pooled ? rs[lr].e_thr : INFINITY;
     uint32_t bp = 0u, be = 0u, nreal = 0u;              // the lane's reserved block [bp, be)
     // entry: (writer << 24) | key.  A writer (wave, half) visits its keys in
@@ -538,7 +555,10 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         if (x < scap) pool[sg + x] = ~0ull;               // unused slots of the last block
     if (nreal) atomicAdd(&ureal[lr], nreal);
     __syncthreads();
-    if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) {
+    if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg && ucnt[tid] > seg_slots(rs[tid].ucount)) {
+        // U overflowed the segment: the radix levels take the row
+        st[(size_t)(t0 + tid) * g.n_ret + r].seg = kNoSeg;
+    } else if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) {
         const CState& c = rs[tid];
         CRow out;
         out.mp = c.mp;
@@ -550,8 +570,8 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         out.u_end = c.uend;
         out.n_tie = 0;
         out.count = (int)ucnt[tid];
-        // P2 and P3 disagree on U, or the slots overflow the segment
-        out.bad = (ureal[tid] != c.ucount || ucnt[tid] > c.ucount + kSegPad) ? 1 : 0;
+        // P3 finds more keys in U than P2's bound
+        out.bad = ureal[tid] > c.ucount ? 1 : 0;
         out.target = 0ull;
         out.seg = c.seg;
         out.light = c.light;
