@@ -1162,6 +1162,104 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     const auto field = [](unsigned long long a, unsigned long long b, int w) {
         return (int)(((w < 4 ? a : b) >> (16 * (w & 3))) & 0xFFFFull);
     };
+    // Kept indices spanning at most 64 CAP: a bitmap over their range (the
+    // slots are in registers now, so the area is free) gives the ascending
+    // order without a merge; the ties past the first ntie are cut at the
+    // index of the ntie-th tie, found the same way.
+    {
+        uint32_t imn = 0xFFFFFFFFu, imx = 0u, ntk = 0u;
+#pragma unroll
+        for (int x = 0; x < PER; ++x)
+            if ((vals[x] & 15u) != 8u) {
+                const uint32_t id = vals[x] >> 5;
+                imn = min(imn, id);
+                imx = max(imx, id);
+                ntk += (vals[x] >> 4) & 1u;
+            }
+        imx = wave_max_u32(imx);
+        imn = ~wave_max_u32(~imn);
+        ntk = wave_sum_u32(ntk);
+        if (tid == 0) {
+            sm.kmin = 0xFFFFFFFFu;
+            sm.kmax = 0u;
+            sm.s_u = 0u;
+        }
+        __syncthreads();
+        if (lane == 0) {
+            atomicMin(&sm.kmin, imn);
+            atomicMax(&sm.kmax, imx);
+            atomicAdd(&sm.s_u, ntk);
+        }
+        __syncthreads();
+        const uint32_t bmin = sm.kmin, bmax = sm.kmax, ties_all = sm.s_u;
+        const int nwords = bmax >= bmin ? (int)((bmax - bmin) / 32u + 1u) : 0;
+        if (nwords > 0 && nwords <= 2 * CAP) {
+            uint32_t* bmp = sv;
+            const int wper = (nwords + NT - 1) / NT;
+            const int w0 = min(tid * wper, nwords), w1 = min(w0 + wper, nwords);
+            // (tie mode) 0: no tie kept, 1: ties up to index jlim, 2: every tie
+            int tmode = ntie <= 0 ? 0 : ((uint32_t)ntie >= ties_all ? 2 : 1);
+            uint32_t jlim = 0u;
+            if (tmode == 1) {
+                for (int w = tid; w < nwords; w += NT) bmp[w] = 0u;
+                __syncthreads();
+#pragma unroll
+                for (int x = 0; x < PER; ++x)
+                    if ((vals[x] & 15u) != 8u && ((vals[x] >> 4) & 1u)) {
+                        const uint32_t o = (vals[x] >> 5) - bmin;
+                        atomicOr(&bmp[o >> 5], 1u << (o & 31u));
+                    }
+                __syncthreads();
+                unsigned long long c = 0ull;
+                for (int w = w0; w < w1; ++w) c += __popc(bmp[w]);
+                unsigned long long tt;
+                unsigned long long rk = block_excl_scan_u64<NT>(c, &tt, scan_sh);
+                const unsigned long long want = (unsigned long long)ntie - 1ull;   // rank of the last kept tie
+                if (want >= rk && want < rk + c) {
+                    for (int w = w0; w < w1; ++w) {
+                        uint32_t bits = bmp[w];
+                        const int n = __popc(bits);
+                        if (rk + (unsigned long long)n > want) {
+                            for (unsigned long long k = want - rk; k > 0; --k) bits &= bits - 1u;
+                            sm.s_S = (unsigned long long)(bmin + 32u * (uint32_t)w + (uint32_t)(__ffs(bits) - 1));
+                            break;
+                        }
+                        rk += (unsigned long long)n;
+                    }
+                }
+                __syncthreads();
+                jlim = (uint32_t)sm.s_S;
+            }
+            for (int w = tid; w < nwords; w += NT) bmp[w] = 0u;
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < PER; ++x) {
+                if ((vals[x] & 15u) == 8u) continue;
+                const uint32_t id = vals[x] >> 5;
+                const bool tie = (vals[x] >> 4) & 1u;
+                if (tie && (tmode == 0 || (tmode == 1 && id > jlim))) continue;
+                const uint32_t o = id - bmin;
+                atomicOr(&bmp[o >> 5], 1u << (o & 31u));
+            }
+            __syncthreads();
+            unsigned long long c = 0ull;
+            for (int w = w0; w < w1; ++w) c += __popc(bmp[w]);
+            unsigned long long cnt;
+            unsigned long long o = block_excl_scan_u64<NT>(c, &cnt, scan_sh);
+            uint32_t* ubi = reinterpret_cast<uint32_t*>(ub);
+            for (int w = w0; w < w1; ++w) {
+                uint32_t bits = bmp[w];
+                while (bits) {
+                    const int b = __ffs(bits) - 1;
+                    bits &= bits - 1u;
+                    ubi[o++] = bmin + 32u * (uint32_t)w + (uint32_t)b;
+                }
+            }
+            if (tid == 0) *count_out = (int)cnt;
+            __syncthreads();
+            return;
+        }
+    }
     int nk = 0, cnt8[8], rb[8];                          // block-uniform: kept in scalar registers
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
