@@ -97,6 +97,33 @@ def test_selection_radix_level_path(dev, orc, frac):
         assert ok, (t, r)
 
 
+@pytest.mark.parametrize("p", [0.3, 0.999])
+def test_flat_scores_ties_cut_by_lowest_index(p):
+    # zero key projection: all indexer scores of a row are 0, one tie group;
+    # the set is the lowest indices reaching mass p (every row resolves its
+    # cut inside the tie group)
+    w = synth.small(3)
+    w.w_k = np.zeros_like(w.w_k)
+    w.top_p = np.full_like(w.top_p, p)
+    say("[gpu] prefill flat scores", p)
+    d = Dev(w)
+    st, rp, sets = d.select()
+    assert st == 0
+    K = {g: synth.as_f32(w.k[0][:, g, :]) for g in range(w.Hkv)}
+    V = {g: synth.as_f32(w.v[0][:, g, :]) for g in range(w.Hkv)}
+    k_low = {r: oracle_k_low(w, 0, r) for r in range(w.n_ret)}
+    for t in list(range(0, w.n_tok, 7)) + [w.n_tok - 1]:
+        pos = w.row_pos(t)
+        for r, h in enumerate(w.ret_heads):
+            g = w.kv_head(h)
+            res = oracle.retrieval_row(w.q[t, h], K[g], V[g], w.w_q[r], w.w_k[r], pos, w.idx_scale, p,
+                                       w.attn_scale, k_low=k_low[r])
+            got = sets[t * w.n_ret + r]
+            ok, _ = band_accept(got, res["order"], res["cum"], p)
+            assert ok, (t, r, len(got))
+            np.testing.assert_array_equal(got, np.arange(len(got)))
+
+
 def test_sparse_prefill_matches_oracle(dev, orc):
     w = dev.w
     say("[gpu] sparse prefill", w.name)
