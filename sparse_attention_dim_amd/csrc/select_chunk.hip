@@ -49,7 +49,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTR = 32;          // rows per workgroup
-constexpr int kHB = 128;         // P2 histogram bins
+constexpr int kHB = 128;         // P2 bins of x (the last one open-ended)
+constexpr int kProv = 40;        // P2 flags the key tiles holding a pair with x < kProv (U's tiles when ue < kProv)
+constexpr int kFlagWords = (1 << 20) / 1024;   // flag words of a row tile: one bit per 32-key tile, 2^20 keys
+constexpr int kTileList = 16384; // flagged tiles the recording pass lists in LDS (more: it streams every tile)
 constexpr float kBinsPerX = 4.0f;
 constexpr int kNB = 64;          // radix buckets per level
 constexpr int kNBP = kNB + 1;
@@ -322,11 +325,14 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                                                    const float* __restrict__ top_p,
                                                    const uint16_t* __restrict__ qlow, CState* __restrict__ st,
                                                    unsigned long long* __restrict__ pool_ctr,
-                                                   unsigned long long pool_cap) {
+                                                   unsigned long long pool_cap, uint32_t* __restrict__ tflags,
+                                                   int nfw) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const float s = g.idx_scale;
     const float sB = s * kBinsPerX;
-    __shared__ double hist[kHB][kTR];                   // (36 KB of LDS in all: four workgroups per CU)
+    __shared__ double hist[kHB][kTR];                   // (40 KB of LDS in all: four workgroups per CU)
+    __shared__ uint32_t tflag[kFlagWords];              // key tiles holding a pair with x < kProv
+    __shared__ int s_full;                              // a row's U reaches past kProv: no tile list
     __shared__ float qs[kTR][16];
     __shared__ float r_mp[kTR], r_delta[kTR];
     __shared__ uint32_t r_ucount[kTR], r_ulow[kTR];
@@ -341,6 +347,8 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         r_delta[tid] = c->delta;
     }
     for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
+    for (int x = tid; x < nfw; x += 256) tflag[x] = 0u;
+    if (tid == 0) s_full = 0;
     __syncthreads();
     const TileCtx tc = tile_ctx(g, k_low, qs);
     const float mpB = r_mp[tc.lr] * sB;
@@ -350,6 +358,12 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
+            {
+                float mx = sc[0];
+#pragma unroll
+                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+                if (__ballot(bin_x(mx, sB, mpB) < (float)kProv) && lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
+            }
             if (it < tc.nfull) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -459,6 +473,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         r_mode[row] = o.mode;
         r_ucount[row] = o.ucount;
         r_seg[row] = kNoSeg;
+        if (o.mode == kLevel && o.uend >= kProv) s_full = 1;
         st[(size_t)(t0 + row) * g.n_ret + r] = o;
     }
     __syncthreads();
@@ -483,6 +498,10 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
             }
         }
     }
+    // the row tile's key-tile flags, and (last word) whether they suffice
+    uint32_t* tf = tflags + ((size_t)r * gridDim.x + blockIdx.x) * (nfw + 1);
+    for (int x = tid; x < nfw; x += 256) tf[x] = tflag[x];
+    if (tid == 0) tf[nfw] = (uint32_t)s_full;
 }
 
 // ---------------------------------------------------------------------------
@@ -493,13 +512,16 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restrict__ k_low,
                                                   const uint16_t* __restrict__ qlow, CState* __restrict__ st,
-                                                  CRow* __restrict__ rows_out, unsigned long long* __restrict__ pool) {
+                                                  CRow* __restrict__ rows_out, unsigned long long* __restrict__ pool,
+                                                  const uint32_t* __restrict__ tflags, int nfw) {
     const int tid = threadIdx.x, wid = tid >> 6;
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     __shared__ float qs[kTR][16];
     __shared__ CState rs[kTR];
     __shared__ uint32_t ucnt[kTR], ureal[kTR];
+    __shared__ uint16_t tlist[kTileList];               // the flagged key tiles, ascending
+    __shared__ unsigned long long scan_sh[256 / 64 + 1];
     __shared__ int s_any;
     if (tid == 0) s_any = 0;
     __syncthreads();
@@ -512,6 +534,30 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
     __syncthreads();
     if (!s_any) return;
     load_qs(g, qlow, qs);
+    // The key tiles that can hold a key of U (flagged by the histogram pass),
+    // listed in LDS; every tile when a row's U reaches past the flagged bins
+    // or the list does not fit.
+    const uint32_t* tf = tflags + ((size_t)r * gridDim.x + blockIdx.x) * (nfw + 1);
+    int nlist = -1;                                      // -1: every tile
+    if (tf[nfw] == 0u) {
+        constexpr int kPerT = kFlagWords / 256;          // flag words per thread
+        const int wb = tid * kPerT, we = min(wb + kPerT, nfw);
+        uint32_t c = 0u;
+        for (int w = wb; w < we; ++w) c += __popc(tf[w]);
+        unsigned long long tot;
+        uint32_t o = (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
+        if (tot <= (unsigned long long)kTileList) {
+            for (int w = wb; w < we; ++w) {
+                uint32_t bits = tf[w];
+                while (bits) {
+                    const int b = __ffs(bits) - 1;
+                    bits &= bits - 1u;
+                    tlist[o++] = (uint16_t)(32 * w + b);
+                }
+            }
+            nlist = (int)tot;
+        }
+    }
     __syncthreads();
     const TileCtx tc = tile_ctx(g, k_low, qs);
     const int lr = tc.lr;
@@ -532,8 +578,7 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         ++bp;
         ++nreal;
     };
-    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
-                    [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
+    const auto body = [&](int it, const uint4& cur) {
         const f32x16_t sc = tc.mfma(cur);
         // U is a small part of the keys: one test of the lane's largest score
         // skips nearly every tile
@@ -550,7 +595,16 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
             for (int i = 0; i < 16; ++i)
                 if (sc[i] >= e_fast && tc.key_of(it, i) <= tc.pos) record(tc.key_of(it, i));
         }
-    });
+    };
+    // the listed tiles only (in increasing order per wave, so a writer's
+    // entries still ascend), or every tile
+    const bool use_list = nlist >= 0;
+    const int nvirt = use_list ? nlist : tc.ntile;
+    const auto tile_of = [&](int k) { return use_list ? (int)tlist[min(k, kTileList - 1)] : k; };
+    if (nvirt > 0)
+        tile_loop<kPre>(wid, 4, nvirt, [&](int k) { return tc.page(tile_of(k)); },
+                        [&](int k, int pg) { return tc.load(tile_of(k), pg); },
+                        [&](int k, const uint4& cur) { body(tile_of(k), cur); });
     for (uint32_t x = bp; x < be; ++x)
         if (x < scap) pool[sg + x] = ~0ull;               // unused slots of the last block
     if (nreal) atomicAdd(&ureal[lr], nreal);
@@ -1618,8 +1672,8 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, ctr, pool, head;
-    int nblk;
+    size_t crow, cst, qlow, counts, knorm, tflags, ctr, pool, head;
+    int nblk, nfw;
 };
 
 ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
@@ -1631,7 +1685,9 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.qlow = w.cst + up((size_t)rows * sizeof(CState));
     w.counts = w.qlow + up((size_t)rows * 16 * 2);
     w.knorm = w.counts + up((size_t)rows * 4);
-    w.ctr = w.knorm + up((size_t)n_ret * w.nblk * 4);
+    w.nfw = (n_keys + 1023) / 1024;                     // one bit per 32-key tile
+    w.tflags = w.knorm + up((size_t)n_ret * w.nblk * 4);
+    w.ctr = w.tflags + up((size_t)((rows / n_ret + kTR - 1) / kTR) * n_ret * (w.nfw + 1) * 4);
     w.pool = w.ctr + 256;
     w.head = w.pool;
     return w;
@@ -1658,6 +1714,7 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     int* counts = (int*)(base + w.counts);
     float* knorm = (float*)(base + w.knorm);
     unsigned long long* ctr = (unsigned long long*)(base + w.ctr);
+    uint32_t* tflags = (uint32_t*)(base + w.tflags);
     unsigned long long* pool = (unsigned long long*)(base + w.pool);
     const unsigned long long pool_cap = (ws_bytes - w.head) / 8;
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
@@ -1665,8 +1722,10 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_max, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
                        (const bf16_t*)k_low, qlow, knorm, w.nblk, cst);
-    hipLaunchKernelGGL(k_csel_hist, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, ctr, pool_cap);
-    hipLaunchKernelGGL(k_csel_rec, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, qlow, cst, crow, pool);
+    hipLaunchKernelGGL(k_csel_hist, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, ctr, pool_cap,
+                       tflags, w.nfw);
+    hipLaunchKernelGGL(k_csel_rec, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, qlow, cst, crow, pool, tflags,
+                       w.nfw);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
     hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, (const bf16_t*)k_low, qlow, top_p,
                        pool, counts);
