@@ -212,17 +212,19 @@ struct TileCtx {
     __device__ int key_of(int it, int i) const { return it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3); }
 };
 
-__device__ TileCtx tile_ctx(const Geo& g, const bf16_t* k_low, const float (*qs)[16]) {
+// rows t0 .. t0 + n_valid - 1 with q_low in qs; keys below L_max are visited
+__device__ TileCtx tile_ctx_at(const Geo& g, const bf16_t* k_low, const float (*qs)[16], int t0, int n_valid,
+                               int L_max) {
     TileCtx c;
     const int lane = threadIdx.x & 63;
     c.r = blockIdx.y;
-    c.t0 = blockIdx.x * kTR;
-    c.n_valid = min(kTR, g.n_tok - c.t0);
+    c.t0 = t0;
+    c.n_valid = n_valid;
     c.lr = lane & 31;
     c.hh = lane >> 5;
     c.row_ok = c.lr < c.n_valid;
     c.pos = g.pos0 + c.t0 + c.lr;
-    c.L_max = g.pos0 + c.t0 + c.n_valid;
+    c.L_max = L_max;
     c.ntile = (c.L_max + 31) / 32;
     c.nfull = (g.pos0 + c.t0 + 1) / 32;
     c.bt = g.block_table + (size_t)g.seq * g.max_blocks;
@@ -237,6 +239,11 @@ __device__ TileCtx tile_ctx(const Geo& g, const bf16_t* k_low, const float (*qs)
     return c;
 }
 
+__device__ TileCtx tile_ctx(const Geo& g, const bf16_t* k_low, const float (*qs)[16]) {
+    const int t0 = blockIdx.x * kTR, n_valid = min(kTR, g.n_tok - t0);
+    return tile_ctx_at(g, k_low, qs, t0, n_valid, g.pos0 + t0 + n_valid);
+}
+
 // q_low of the workgroup's rows as floats (zero for rows past the chunk)
 __device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (*qs)[16]) {
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
@@ -248,28 +255,30 @@ __device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (
 }
 
 // ---------------------------------------------------------------------------
-// P1.  grid (ceil(n_tok / 32), n_ret), 256 threads: q_low of the rows (fixed-
+// P1.  grid (ceil(n_tok / 64), n_ret), 256 threads: q_low of the rows (fixed-
 // order fp32 chain over d, bf16 rounding) and the row maxima of the MFMA
 // scores: m' = max e + delta >= max d (the largest key norm comes from the
-// key-norm pre-pass).
+// key-norm pre-pass).  64 rows per workgroup: each key tile read feeds the
+// MFMAs of both 32-row halves.
 // ---------------------------------------------------------------------------
+constexpr int kTR1 = 2 * kTR;
 __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restrict__ q,
                                                   const bf16_t* __restrict__ w_q, const bf16_t* __restrict__ k_low,
                                                   uint16_t* __restrict__ qlow_out, const float* __restrict__ knorm,
                                                   int nblk, CState* __restrict__ st) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
-    const int n_valid = min(kTR, g.n_tok - t0);
+    const int r = blockIdx.y, t0 = blockIdx.x * kTR1;
+    const int n_valid = min(kTR1, g.n_tok - t0);
     const int h_q = g.ret_heads[r];
     __shared__ __align__(16) float wq[128 * 16];
-    __shared__ float qs[kTR][16];
-    __shared__ uint32_t rmax[kTR];
+    __shared__ float qs[kTR1][16];
+    __shared__ uint32_t rmax[kTR1];
     __shared__ uint32_t kmax_bits;
     stage_f32(w_q + (size_t)r * g.D * 16, wq, g.D * 16, tid);
-    if (tid < kTR) rmax[tid] = 0u;
+    if (tid < kTR1) rmax[tid] = 0u;
     if (tid == 0) kmax_bits = 0u;
     __syncthreads();
-    for (int o = tid; o < kTR * 16; o += 256) {
+    for (int o = tid; o < kTR1 * 16; o += 256) {
         const int lr = o >> 4, c = o & 15;
         float acc = 0.0f;
         if (lr < n_valid) {
@@ -287,21 +296,33 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
         if (lane == 0) atomicMax(&kmax_bits, __float_as_uint(kn));
     }
     __syncthreads();
-    const TileCtx tc = tile_ctx(g, k_low, qs);
-    float m_e = -INFINITY;
-    tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
-                    [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
-        const f32x16_t sc = tc.mfma(cur);
-        if (it < tc.nfull) {
+    const int L_max = g.pos0 + t0 + n_valid;
+    const TileCtx ta = tile_ctx_at(g, k_low, qs, t0, min(kTR, n_valid), L_max);
+    const TileCtx tb = tile_ctx_at(g, k_low, qs + kTR, t0 + kTR, max(0, n_valid - kTR), L_max);
+    float ma = -INFINITY, mb = -INFINITY;
+    tile_loop<kPre>(wid, 4, ta.ntile, [&](int it) { return ta.page(it); },
+                    [&](int it, int pg) { return ta.load(it, pg); }, [&](int it, const uint4& cur) {
+        const f32x16_t sa = ta.mfma(cur);
+        const f32x16_t sb = tb.mfma(cur);
+        if (it < ta.nfull) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, sc[i]);
+            for (int i = 0; i < 16; ++i) ma = fmaxf(ma, sa[i]);
         } else {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) m_e = fmaxf(m_e, tc.key_of(it, i) <= tc.pos ? sc[i] : -INFINITY);
+            for (int i = 0; i < 16; ++i) ma = fmaxf(ma, ta.key_of(it, i) <= ta.pos ? sa[i] : -INFINITY);
+        }
+        if (it < tb.nfull) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sb[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mb = fmaxf(mb, tb.key_of(it, i) <= tb.pos ? sb[i] : -INFINITY);
         }
     });
-    m_e = fmaxf(m_e, __shfl_xor(m_e, 32));
-    if (tc.row_ok && tc.hh == 0 && m_e > -INFINITY) atomicMax(&rmax[tc.lr], score_key(m_e));
+    ma = fmaxf(ma, __shfl_xor(ma, 32));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    if (ta.row_ok && ta.hh == 0 && ma > -INFINITY) atomicMax(&rmax[ta.lr], score_key(ma));
+    if (tb.row_ok && tb.hh == 0 && mb > -INFINITY) atomicMax(&rmax[kTR + tb.lr], score_key(mb));
     __syncthreads();
     if (tid < n_valid) {
         float qn2 = 0.0f;
@@ -1720,8 +1741,8 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
-    hipLaunchKernelGGL(k_csel_max, grid, dim3(256), 0, s, g, (const bf16_t*)q, (const bf16_t*)w_q,
-                       (const bf16_t*)k_low, qlow, knorm, w.nblk, cst);
+    hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
+                       (const bf16_t*)w_q, (const bf16_t*)k_low, qlow, knorm, w.nblk, cst);
     hipLaunchKernelGGL(k_csel_hist, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, ctr, pool_cap,
                        tflags, w.nfw);
     hipLaunchKernelGGL(k_csel_rec, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, qlow, cst, crow, pool, tflags,
