@@ -57,8 +57,7 @@ constexpr int kMB = 16;            // blocks per group
 constexpr int kGK = kMB * kBN;     // union keys per group
 constexpr int kPS = kD + 4;        // floats per partial result: O[D], max, mass (16-byte rows)
 constexpr int kMaxSplit = 8;
-constexpr int kItem = 256;         // entries of one row per wave-wide scan item (4 per lane)
-constexpr int kUL = 4;             // items in flight per wave
+constexpr int kUL = 8;             // 4-entry pieces per thread and round of an entry scan
 constexpr int kPoolG = 4;          // groups a (tile, window) may keep in the block pool
 constexpr int kTargetWG = 2048;    // tile workgroups the split aims for
 
@@ -74,21 +73,23 @@ __device__ __forceinline__ uint32_t bf_at(const uint4& u, int e) {
     return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-// The entries of a tile's rows inside one window: row i covers
-// idx[rb[i], re[i]), cut into 256-entry items cp[i] .. cp[i+1]-1 of one flat
-// item sequence.
+// The entries of a tile's rows inside one window, as one flat sequence of
+// 4-entry pieces: row i covers idx[rb[i], re[i]) and is read from the
+// 4-aligned position ra[i]; its pieces are cp[i] .. cp[i+1]-1.
 struct Ranges {
-    int64_t rb[kBM], re[kBM];
+    int64_t rb[kBM], re[kBM], ra[kBM];
     int cp[kBM + 1];
 };
 
-// Lanes 0..63: row i's range [b, e) (b <= e) into R and the item prefix.
+// Lanes 0..63: row i's range [b, e) (b <= e) into R and the piece prefix.
 // The caller synchronises before R is read.
 __device__ __forceinline__ void set_ranges(int64_t b, int64_t e, Ranges& R) {
     const int tid = threadIdx.x;
-    const int n = (int)((e - b + kItem - 1) / kItem);
+    const int64_t a = b & ~(int64_t)3;
+    const int n = e > b ? (int)((e - a + 3) >> 2) : 0;
     R.rb[tid] = b;
     R.re[tid] = e;
+    R.ra[tid] = a;
     int x = n;                                         // inclusive scan over the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -99,34 +100,48 @@ __device__ __forceinline__ void set_ranges(int64_t b, int64_t e, Ranges& R) {
     if (tid == 0) R.cp[0] = 0;
 }
 
-// Visit the tile's entries in the window, a wave per item (256 consecutive
-// entries of one row, 4 per lane, coalesced), kUL items of a wave in flight
-// together.  f(row, k[4], valid bits) runs for every lane of every item; a
-// wave's calls share the row, and a lane's 4 keys ascend.
+// Visit the tile's entries in the window: every thread takes kUL pieces per
+// round (16-byte loads where idx is 16-byte aligned and the piece lies inside
+// idx_n), and f(row, k[4], valid bits) runs per piece; a piece's keys ascend.
 template <typename F>
-__device__ __forceinline__ void for_items(const Ranges& R, const int32_t* __restrict__ idx, F&& f) {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int nitems = R.cp[kBM];
-    const int cpl = R.cp[lane];                       // the row of item x: lanes whose cp <= x, less one
-    for (int x0 = wid * kUL; x0 < nitems; x0 += (kNT / 64) * kUL) {
-        int k[kUL][4], row[kUL];
+__device__ __forceinline__ void for_pieces(const Ranges& R, const int32_t* __restrict__ idx, int64_t idx_n, F&& f) {
+    const int tid = threadIdx.x;
+    const int total = R.cp[kBM];
+    const bool vec = (reinterpret_cast<uintptr_t>(idx) & 15) == 0;
+    for (int base = 0; base < total; base += kNT * kUL) {
+        // the row whose pieces hold piece c: the last i with cp[i] <= c, by six
+        // halving steps run for all kUL pieces together
+        int lo[kUL];
+#pragma unroll
+        for (int u = 0; u < kUL; ++u) lo[u] = 0;
+#pragma unroll
+        for (int step = kBM / 2; step > 0; step >>= 1)
+#pragma unroll
+            for (int u = 0; u < kUL; ++u)
+                if (R.cp[lo[u] + step] <= base + u * kNT + tid) lo[u] += step;
+        int k[kUL][4];
         uint32_t vm[kUL];
 #pragma unroll
         for (int u = 0; u < kUL; ++u) {
-            const int x = x0 + u;
-            row[u] = __popcll(__ballot(cpl <= x)) - 1;
-            const int64_t pos = R.rb[row[u]] + (int64_t)kItem * (x - R.cp[row[u]]) + 4 * lane;
-            const int64_t e = x < nitems ? R.re[row[u]] : 0;
+            const int c = base + u * kNT + tid;
+            const int64_t p = R.ra[lo[u]] + 4 * (int64_t)(c - R.cp[lo[u]]);
+            const int64_t b = R.rb[lo[u]], e = c < total ? R.re[lo[u]] : 0;
             vm[u] = 0u;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bool ok = pos + c < e;
-                vm[u] |= ok ? 1u << c : 0u;
-                k[u][c] = ok ? idx[pos + c] : 0;
+            for (int x = 0; x < 4; ++x) vm[u] |= (p + x >= b && p + x < e) ? 1u << x : 0u;
+            if (vm[u] && vec && p + 4 <= idx_n) {
+                const int4 v = *reinterpret_cast<const int4*>(idx + p);
+                k[u][0] = v.x;
+                k[u][1] = v.y;
+                k[u][2] = v.z;
+                k[u][3] = v.w;
+            } else {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) k[u][x] = (vm[u] >> x) & 1u ? idx[p + x] : 0;
             }
         }
 #pragma unroll
-        for (int u = 0; u < kUL; ++u) f(row[u], k[u], vm[u]);
+        for (int u = 0; u < kUL; ++u) f(lo[u], k[u], vm[u]);
     }
 }
 
@@ -255,7 +270,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
     }
     __syncthreads();
     // the union bitmap
-    for_items(R, idx, [&](int, const int (&k)[4], uint32_t vm) {
+    for_pieces(R, idx, idx_n, [&](int, const int (&k)[4], uint32_t vm) {
         int a[4];
         uint32_t bit[4];
 #pragma unroll
@@ -309,7 +324,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
             if (u < nb * kBN) pool[base + (u >> 6)].kvrow[u & 63] = 0u;
         }
     }
-    for_items(R, idx, [&](int row, const int (&k)[4], uint32_t vm) {
+    for_pieces(R, idx, idx_n, [&](int row, const int (&k)[4], uint32_t vm) {
         int a[4];
         uint32_t bit[4];
 #pragma unroll
@@ -357,8 +372,8 @@ struct TileSmem {
 // in roff) and every row's 64-bit masks of the group's blocks (an entry whose
 // key lies in the group's key range [klo, khi] has its rank in [g0, g1)).
 template <typename S>
-__device__ void build_group(const Geo& g, S& sm, const int32_t* __restrict__ idx, const int32_t* bt, int kvh, int w0,
-                            int g0, int g1) {
+__device__ void build_group(const Geo& g, S& sm, const int32_t* __restrict__ idx, int64_t idx_n, const int32_t* bt,
+                            int kvh, int w0, int g0, int g1) {
     const int tid = threadIdx.x;
     for (int x = tid; x < kMB * kBM * 2; x += kNT) (&sm.memb[0][0][0])[x] = 0u;
     {
@@ -385,7 +400,7 @@ __device__ void build_group(const Geo& g, S& sm, const int32_t* __restrict__ idx
     }
     __syncthreads();
     const int klo = sm.klo, khi = sm.khi;
-    for_items(sm.R, idx, [&](int row, const int (&k)[4], uint32_t vm) {
+    for_pieces(sm.R, idx, idx_n, [&](int row, const int (&k)[4], uint32_t vm) {
         int a[4];
         uint32_t bit[4];
 #pragma unroll
@@ -405,8 +420,8 @@ __device__ void build_group(const Geo& g, S& sm, const int32_t* __restrict__ idx
 __global__ __launch_bounds__(kNT) void k_sp_tile(Geo g, const bf16_t* __restrict__ q,
                                                  const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
                                                  const int64_t* __restrict__ wr, int nwin, int nsplit,
-                                                 const int32_t* __restrict__ idx, const int32_t* __restrict__ status,
-                                                 const uint32_t* __restrict__ tw_n,
+                                                 const int32_t* __restrict__ idx, int64_t idx_n,
+                                                 const int32_t* __restrict__ status, const uint32_t* __restrict__ tw_n,
                                                  const int32_t* __restrict__ tw_off,
                                                  const uint32_t* __restrict__ tw_bm,
                                                  const PoolBlock* __restrict__ pool, float* __restrict__ part) {
@@ -498,7 +513,7 @@ __global__ __launch_bounds__(kNT) void k_sp_tile(Geo g, const bf16_t* __restrict
             }
             __syncthreads();
         } else {
-            build_group(g, sm, idx, bt, kvh, w0, g0, g1);
+            build_group(g, sm, idx, idx_n, bt, kvh, w0, g0, g1);
         }
         const int nb = (nk + kBN - 1) / kBN;
         load_blk(0, nk);
@@ -723,7 +738,7 @@ hipError_t launch_sparse_prefill(const Geo& g, const void* q, const void* k, con
     hipLaunchKernelGGL(k_sp_union, dim3(p.ntile * p.nwin, g.n_ret), dim3(kNT), 0, s, g, row_ptr, p.nwin, p.nsplit,
                        idx, idx_n, status, wr, tw_n, tw_off, tw_bm, ctr, pool, p.pool_blocks, part);
     hipLaunchKernelGGL(k_sp_tile, dim3(p.ntile * p.nwin * p.nsplit, g.n_ret), dim3(kNT), 0, s, g, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, wr, p.nwin, p.nsplit, idx, status, tw_n, tw_off, tw_bm,
+                       (const bf16_t*)k, (const bf16_t*)v, wr, p.nwin, p.nsplit, idx, idx_n, status, tw_n, tw_off, tw_bm,
                        pool, part);
     hipLaunchKernelGGL(k_sp_combine, dim3((rows + 1) / 2), dim3(128), 0, s, g, p.nwin * p.nsplit, part, status,
                        (bf16_t*)out);
