@@ -49,8 +49,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTR = 32;          // rows per workgroup
-constexpr int kHB = 128;         // P2 bins of x (the last one open-ended)
 constexpr int kProv = 40;        // P2 flags the key tiles holding a pair with x < kProv (U's tiles when ue < kProv)
+constexpr int kHB = kProv + 1;   // P2 bins of x: one per unit below kProv, the last one open-ended
 constexpr int kFlagWords = (1 << 20) / 1024;   // flag words of a row tile: one bit per 32-key tile, 2^20 keys
 constexpr int kTileList = 16384; // flagged tiles the recording pass lists in LDS (more: it streams every tile)
 constexpr float kBinsPerX = 4.0f;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const float s = g.idx_scale;
     const float sB = s * kBinsPerX;
-    __shared__ double hist[kHB][kTR];                   // (40 KB of LDS in all: four workgroups per CU)
+    __shared__ double hist[kHB][kTR];
     __shared__ uint32_t tflag[kFlagWords];              // key tiles holding a pair with x < kProv
     __shared__ int s_full;                              // a row's U reaches past kProv: no tile list
     __shared__ float qs[kTR][16];
@@ -375,34 +375,50 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     const float mpB = r_mp[tc.lr] * sB;
     {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
+        // Pairs of the open-ended last bin (x >= kProv, weights below e^-10 of
+        // the row maximum) are summed in registers: a float sum per tile (16
+        // terms, relative error < 2^-20), added to a double per lane.  Only
+        // the pairs below kProv take an LDS atomic of their bin, and a tile
+        // with none of them (no lane maximum below kProv) skips the bins.
         double* hrow = &hist[0][tc.lr];
+        double far = 0.0;
         tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
-            {
-                float mx = sc[0];
+            float mx = sc[0];
 #pragma unroll
-                for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-                if (__ballot(bin_x(mx, sB, mpB) < (float)kProv) && lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
-            }
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+            const bool near = __ballot(bin_x(mx, sB, mpB) < (float)kProv) != 0ull;
+            if (near && lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
+            float f = 0.0f;
             if (it < tc.nfull) {
+                if (!near) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float x = bin_x(sc[i], sB, mpB);
-                    const int b = bin_of(x);
-                    atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
+                    for (int i = 0; i < 16; ++i) f += __builtin_amdgcn_exp2f(bin_x(sc[i], sB, mpB) * kW);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float x = bin_x(sc[i], sB, mpB);
+                        const float w = __builtin_amdgcn_exp2f(x * kW);
+                        const bool nr = x < (float)kProv;
+                        f += nr ? 0.0f : w;
+                        if (nr) atomicAdd(&hrow[bin_of(x) * kTR], (double)w);
+                    }
                 }
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
+                    const float x = bin_x(sc[i], sB, mpB);
+                    const float w = __builtin_amdgcn_exp2f(x * kW);
                     if (tc.key_of(it, i) <= tc.pos) {
-                        const float x = bin_x(sc[i], sB, mpB);
-                        const int b = bin_of(x);
-                        atomicAdd(&hrow[b * kTR], (double)__builtin_amdgcn_exp2f(x * kW));
+                        if (x < (float)kProv) atomicAdd(&hrow[bin_of(x) * kTR], (double)w);
+                        else f += w;
                     }
                 }
             }
+            far += (double)f;
         });
+        atomicAdd(&hrow[(kHB - 1) * kTR], far);
     }
     __syncthreads();
     // cut bin of the approximate masses, U = bins <= cut + 1.  The target
