@@ -13,11 +13,13 @@ LIB = os.path.join(HERE, "librtp.so")
 SOURCES = ["abi.cpp", "append.hip", "select.hip", "select_chunk.hip", "attn_decode.hip", "attn_prefill.hip", "attn_sparse_prefill.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Per-file code generation options.  The chunk selection, the decode window
-# kernel and the sparse prefill tiles keep their MFMA results in VGPRs: they
-# read (or rescale) every accumulator lane with VALU, and AGPR results would
-# cost a v_accvgpr move for each (and, for the tiles, a second wave per SIMD).
+# kernel and the prefill attention tiles keep their MFMA results in VGPRs:
+# they read (or rescale) every accumulator lane with VALU, and AGPR results
+# would cost a v_accvgpr move for each (and, for the tiles, a second wave per
+# SIMD).
 FILE_FLAGS = {"select_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
               "attn_sparse_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

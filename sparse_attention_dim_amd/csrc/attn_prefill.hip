@@ -12,8 +12,9 @@
 //                            B = Q^T held in registers (each lane one query)
 //   online softmax           in-lane: a lane holds 16 keys of one query; the
 //                            two half-waves hold the other 16 (one xor-32 swap)
-//   O^T[d][q] += V^T . P^T   A = V^T from a transposed LDS tile, B = P^T taken
-//                            straight from the S^T registers
+//   O^T[d][q] += V^T . P^T   A = V^T read from the row-major V tile in LDS by
+//                            transposing loads (ds_read_b64_tr_b16), B = P^T
+//                            taken straight from the S^T registers
 // The key order inside the second product is a fixed permutation that matches
 // the register layout of S^T, so P never moves between lanes.  A 64-key tile
 // of one KV head is one contiguous 16 KiB run of a page (pages hold 256 keys).
@@ -34,9 +35,20 @@ constexpr int kBM = 128;           // query rows per workgroup
 constexpr int kBN = 64;            // keys per tile
 constexpr int kD = 128;            // head dim of this kernel
 constexpr int kKsLd = kD + 8;      // K row stride in LDS (bf16), 272 B: conflict-free row reads
-constexpr int kVtLd = kBN + 4;     // V^T row stride in LDS (bf16), 136 B
+constexpr int kVsLd = kD + 32;     // V row stride in LDS (bf16), 320 B: the four rows of a transposing load hit disjoint banks
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS load: within each 16-lane group, lane 4 r + c supplies the
+// address of 4 consecutive 16-bit elements (row r of a 4 x 16 block, columns
+// 4 c .. 4 c + 3); lane i receives column i of the block, rows 0..3.
+__device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
@@ -72,7 +84,7 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
                                                     const bf16_t* __restrict__ vc, bf16_t* __restrict__ out,
                                                     int dense) {
     __shared__ __attribute__((aligned(16))) bf16_t Ks[kBN * kKsLd];
-    __shared__ __attribute__((aligned(16))) bf16_t Vt[kD * kVtLd];
+    __shared__ __attribute__((aligned(16))) bf16_t Vs[kBN * kVsLd];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int hq = g.hlist[blockIdx.y];
     const int kvh = hq / g.group;
@@ -86,6 +98,10 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
     const int pq = g.pos0 + t;                       // its position
     const float sc = g.attn_scale * kLog2e;
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
+    // positions of the wave's 32 queries (all of them valid: wave_full)
+    const int wt0 = t0 + wid * 32;
+    const bool wave_full = wt0 + 31 < g.n_tok;
+    const int wp_min = g.pos0 + wt0, wp_max = wp_min + 31;
 
     // Q^T operand: lane holds Q[t][16 kk + 8 hh + 0..7] for kk = 0..7
     uint4 qreg[8];
@@ -108,41 +124,49 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
     const int ntiles = na + nb;
 
     // tile loads: 16 KiB of K and of V per tile, four 16-byte vectors per thread each
-    uint4 kv_k[4], kv_v[4];
     auto tile_key0 = [&](int it) { return it < na ? tr.a0 + it * kBN : tr.b0 + (it - na) * kBN; };
-    auto load_tile = [&](int it) {
+    // the 16-byte pieces of a tile this thread loads: element offsets of the
+    // K and V tile starts (the tile is one contiguous run of a page)
+    auto tile_base = [&](int it) {
         const int k0 = tile_key0(it);
-        const int page = bt[k0 >> 8];
-        const size_t base = (((size_t)page * g.Hkv + kvh) * kBlk + (k0 & 255)) * kD;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            kv_k[j] = reinterpret_cast<const uint4*>(kc + base)[tid + 256 * j];
-            kv_v[j] = reinterpret_cast<const uint4*>(vc + base)[tid + 256 * j];
-        }
+        return (((size_t)bt[k0 >> 8] * g.Hkv + kvh) * kBlk + (k0 & 255)) * kD;
     };
-    if (ntiles > 0) load_tile(0);
+    uint4 kk0, kk1, kk2, kk3, vv0, vv1, vv2, vv3;
+#define RTP_LOAD_TILE(b)                                                            \
+    {                                                                               \
+        const uint4* kp = reinterpret_cast<const uint4*>(kc + (b)) + tid;           \
+        const uint4* vp = reinterpret_cast<const uint4*>(vc + (b)) + tid;           \
+        kk0 = kp[0]; kk1 = kp[256]; kk2 = kp[512]; kk3 = kp[768];                   \
+        vv0 = vp[0]; vv1 = vp[256]; vv2 = vp[512]; vv3 = vp[768];                   \
+    }
+    if (ntiles > 0) RTP_LOAD_TILE(tile_base(0))
 
     for (int it = 0; it < ntiles; ++it) {
         const int k0 = tile_key0(it);
         __syncthreads();                              // previous tile's LDS reads are done
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int e = (tid + 256 * j) * 8;        // element of the 64 x 128 tile
-            const int r = e >> 7, c = e & 127;
-            *reinterpret_cast<uint4*>(&Ks[r * kKsLd + c]) = kv_k[j];
-            // keys past the last query position may be unwritten cache slots:
-            // store zeros so that p = 0 never meets a non-finite value
-            const bool live = k0 + r <= p_max;
-            const uint32_t w[4] = {live ? kv_v[j].x : 0u, live ? kv_v[j].y : 0u, live ? kv_v[j].z : 0u,
-                                   live ? kv_v[j].w : 0u};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                Vt[(c + 2 * x) * kVtLd + r] = (bf16_t)(w[x] & 0xFFFFu);
-                Vt[(c + 2 * x + 1) * kVtLd + r] = (bf16_t)(w[x] >> 16);
-            }
+        {
+            // thread piece j: element (tid + 256 j) * 8 of the 64 x 128 tile,
+            // row tid / 16 + 16 j, column (tid % 16) * 8.  Keys past the last
+            // query position may be unwritten cache slots: their V rows are
+            // stored as zeros so that p = 0 never meets a non-finite value.
+            const int r = tid >> 4, c = (tid & 15) * 8;
+            // (an AND mask, not a select: a select of two vectors may be
+            // lowered through scratch memory)
+            const auto keep = [&](const uint4& x, int key) {
+                const uint32_t m = key <= p_max ? ~0u : 0u;
+                return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+            };
+            *reinterpret_cast<uint4*>(&Ks[r * kKsLd + c]) = kk0;
+            *reinterpret_cast<uint4*>(&Ks[(r + 16) * kKsLd + c]) = kk1;
+            *reinterpret_cast<uint4*>(&Ks[(r + 32) * kKsLd + c]) = kk2;
+            *reinterpret_cast<uint4*>(&Ks[(r + 48) * kKsLd + c]) = kk3;
+            *reinterpret_cast<uint4*>(&Vs[r * kVsLd + c]) = keep(vv0, k0 + r);
+            *reinterpret_cast<uint4*>(&Vs[(r + 16) * kVsLd + c]) = keep(vv1, k0 + r + 16);
+            *reinterpret_cast<uint4*>(&Vs[(r + 32) * kVsLd + c]) = keep(vv2, k0 + r + 32);
+            *reinterpret_cast<uint4*>(&Vs[(r + 48) * kVsLd + c]) = keep(vv3, k0 + r + 48);
         }
         __syncthreads();
-        if (it + 1 < ntiles) load_tile(it + 1);       // prefetch while computing
+        if (it + 1 < ntiles) RTP_LOAD_TILE(tile_base(it + 1))   // prefetch while computing
 
         // S^T for the two 32-key halves of the tile
         f32x16_t s[2];
@@ -157,18 +181,33 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
                 s[sh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[sh], 0, 0, 0);
             }
         }
-        // scale, mask, tile maximum of this lane's query
+        // scale, mask, tile maximum of this lane's query.  A tile that every
+        // query of the wave sees whole (below the wave's first position, and
+        // a sink tile or inside the window of its last position) skips the
+        // per-key mask.
         float mt = -INFINITY;
+        const bool whole = wave_full && k0 + kBN - 1 <= wp_min &&
+                           (dense || k0 + kBN - 1 < g.sinks || k0 > wp_max - g.window);
+        if (whole) {
 #pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
+            for (int sh = 0; sh < 2; ++sh)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int key = k0 + 32 * sh + (i >> 2) * 8 + 4 * hh + (i & 3);
-                bool ok = qok && key <= pq;
-                if (!dense) ok = ok && (key < g.sinks || key > pq - g.window);
-                const float v = ok ? s[sh][i] * sc : -INFINITY;
-                s[sh][i] = v;
-                mt = fmaxf(mt, v);
+                for (int i = 0; i < 16; ++i) {
+                    s[sh][i] *= sc;
+                    mt = fmaxf(mt, s[sh][i]);
+                }
+        } else {
+#pragma unroll
+            for (int sh = 0; sh < 2; ++sh) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int key = k0 + 32 * sh + (i >> 2) * 8 + 4 * hh + (i & 3);
+                    bool ok = qok && key <= pq;
+                    if (!dense) ok = ok && (key < g.sinks || key > pq - g.window);
+                    const float v = ok ? s[sh][i] * sc : -INFINITY;
+                    s[sh][i] = v;
+                    mt = fmaxf(mt, v);
+                }
             }
         }
         mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -180,26 +219,36 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
 #pragma unroll
                 for (int x = 0; x < 8; ++x) pb[sh][x] = 0u;
         } else {
-            const float corr = exp2f(m_run - m_new);
+            // v_exp_f32 directly: its results below 2^-126 (flushed) weigh
+            // nothing against the running maximum's weight of 1.  The
+            // accumulators are rescaled only when a query of the wave has a
+            // new maximum (for the others the factor is exactly 1).
+            if (__ballot(m_new > m_run) != 0ull) {
+                const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= corr;
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) oacc[dd][i] *= corr;
+            }
             m_run = m_new;
-            l_run *= corr;
-#pragma unroll
-            for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[dd][i] *= corr;
 #pragma unroll
             for (int sh = 0; sh < 2; ++sh) {
                 float p[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    p[i] = exp2f(s[sh][i] - m_new);
+                    p[i] = __builtin_amdgcn_exp2f(s[sh][i] - m_new);
                     l_run += p[i];
                 }
 #pragma unroll
                 for (int x = 0; x < 8; ++x) pb[sh][x] = pack2(p[2 * x], p[2 * x + 1]);
             }
         }
-        // O^T += V^T P^T
+        // O^T += V^T P^T: lane (d = 32 dd + qi, half hh) takes the keys
+        // kc0 + 0..3 and kc0 + 8..11 (the rows of its S^T registers); in the
+        // transposing loads, lane j of a 16-lane group addresses key row
+        // kc0 + j / 4 (+ 8) at columns 32 dd + 16 (group & 1) + 4 (j % 4)
+        const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh) {
 #pragma unroll
@@ -208,15 +257,16 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
                 const int kc0 = 32 * sh + 16 * kk + 4 * hh;
 #pragma unroll
                 for (int dd = 0; dd < 4; ++dd) {
-                    const bf16_t* vr = &Vt[(32 * dd + qi) * kVtLd + kc0];
-                    const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                    const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                    const bf16_t* vr = &Vs[(kc0 + trr) * kVsLd + 32 * dd + trc];
+                    const uint2 lo = lds_tr16(vr);
+                    const uint2 hi = lds_tr16(vr + 8 * kVsLd);
                     const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
                     oacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), oacc[dd], 0, 0, 0);
                 }
             }
         }
     }
+#undef RTP_LOAD_TILE
     // normalise and store: lane holds O[t][32 dd + 8 (i/4) + 4 hh + (i%4)]
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (qok) {

@@ -146,7 +146,7 @@ __device__ __forceinline__ WeightBin weight_bin(float d, float m, float s) {
 // ---- block primitives (NT threads, NT a multiple of 64) ----
 
 template <int NT>
-__device__ unsigned long long block_excl_scan_u64(unsigned long long v, unsigned long long* total,
+__device__ __forceinline__ unsigned long long block_excl_scan_u64(unsigned long long v, unsigned long long* total,
                                                   unsigned long long* sh /* NT/64 */) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     unsigned long long x = v;

@@ -357,8 +357,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     __shared__ float qs[kTR][16];
     __shared__ float r_mp[kTR], r_delta[kTR];
     __shared__ uint32_t r_ucount[kTR], r_ulow[kTR];
-    __shared__ int r_mode[kTR];
-    __shared__ unsigned long long r_seg[kTR];
+    __shared__ int r_mode[kTR], r_uend[kTR];
     load_qs(g, qlow, qs);
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
@@ -508,9 +507,8 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
             o.shift = bits > 6 ? bits - 6 : 0;
         }
         r_mode[row] = o.mode;
+        r_uend[row] = o.uend;
         r_ucount[row] = o.ucount;
-        r_seg[row] = kNoSeg;
-        if (o.mode == kLevel && o.uend >= kProv) s_full = 1;
         st[(size_t)(t0 + row) * g.n_ret + r] = o;
     }
     __syncthreads();
@@ -531,6 +529,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                     if (r_mode[row] == kLevel && r_ulow[row] <= (uint32_t)(kSegMax - kSegPad)) {
                         st[(size_t)(t0 + row) * g.n_ret + r].seg = off;
                         off += seg_slots(r_ucount[row]);
+                        if (r_uend[row] >= kProv) s_full = 1;   // a recorded U past the flagged tiles
                     }
             }
         }
