@@ -127,14 +127,16 @@ struct Stream {
                 for (int u = 1; u < U; ++u) cm = fmaxf(cm, s[u][h]);
                 const float mn = fmaxf(m[h], cm);
                 if (mn == -INFINITY) continue;           // the group has no key yet
-                const float corr = exp2f(m[h] - mn);
+                // raw v_exp_f32: its results below 2^-126 weigh nothing
+                // against the running maximum's weight of 1
+                const float corr = __builtin_amdgcn_exp2f(m[h] - mn);
                 m[h] = mn;
                 l[h] *= corr;
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) o[h][e] *= corr;
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    const float p = exp2f(s[u][h] - mn);
+                    const float p = __builtin_amdgcn_exp2f(s[u][h] - mn);
                     l[h] += p;
                     float f[EPV];
                     Pack<T>::unpack(vb[u], f);
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = fmaxf(m_run, mt);             // finite: the block has a live key
         if (__ballot(m_new > m_run) != 0ull) {            // some head's maximum rose: rescale
-            const float corr = exp2f(m_run - m_new);
+            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= corr;
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd)
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
             float p[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                p[i] = exp2f(s[i] - m_new);
+                p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
                 l_run += p[i];
             }
 #pragma unroll

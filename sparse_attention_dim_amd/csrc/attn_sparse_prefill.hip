@@ -566,8 +566,10 @@ __global__ __launch_bounds__(kNT) void k_sp_tile(Geo g, const bf16_t* __restrict
 #pragma unroll
                 for (int x = 0; x < 8; ++x) pb[x] = 0u;
             } else {
+                // (raw v_exp_f32 below: its results under 2^-126 weigh nothing
+                // against the running maximum's weight of 1)
                 if (__ballot(m_new > m_run)) {        // rescale only when a maximum of the wave moved
-                    const float corr = exp2f(m_run - m_new);
+                    const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
                     l_run *= corr;
 #pragma unroll
                     for (int dd = 0; dd < 4; ++dd)
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(kNT) void k_sp_tile(Geo g, const bf16_t* __restrict
                 float p[16];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    p[i] = exp2f(s[i] - m_new);
+                    p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
                     l_run += p[i];
                 }
 #pragma unroll
