@@ -254,6 +254,17 @@ __device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (
     }
 }
 
+// The histogram pass splits each row tile's key tiles over several
+// workgroups: their histograms and tile flags meet in these device
+// accumulators (zeroed by P1), and the last workgroup of a row tile to
+// arrive takes the epilogue.
+struct HistAcc {
+    double* hist;        // [rows][kHB], rows in result-record order
+    uint32_t* tflags;    // [n_ret][nt32][nfw + 1]
+    uint32_t* arrive;    // [n_ret][nt32]
+    int nt32, nfw, nsplit;
+};
+
 // ---------------------------------------------------------------------------
 // P1.  grid (ceil(n_tok / 64), n_ret), 256 threads: q_low of the rows (fixed-
 // order fp32 chain over d, bf16 rounding) and the row maxima of the MFMA
@@ -265,10 +276,18 @@ constexpr int kTR1 = 2 * kTR;
 __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restrict__ q,
                                                   const bf16_t* __restrict__ w_q, const bf16_t* __restrict__ k_low,
                                                   uint16_t* __restrict__ qlow_out, const float* __restrict__ knorm,
-                                                  int nblk, CState* __restrict__ st) {
+                                                  int nblk, CState* __restrict__ st, HistAcc acc) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int r = blockIdx.y, t0 = blockIdx.x * kTR1;
     const int n_valid = min(kTR1, g.n_tok - t0);
+    // the histogram pass's accumulators of these rows start at zero
+    for (int x = tid; x < n_valid * kHB; x += 256)
+        acc.hist[((size_t)(t0 + x / kHB) * g.n_ret + r) * kHB + x % kHB] = 0.0;
+    for (int hf = 0; hf < 2 && t0 + hf * kTR < g.n_tok; ++hf) {
+        const size_t rt = (size_t)r * acc.nt32 + 2 * blockIdx.x + hf;
+        for (int x = tid; x <= acc.nfw; x += 256) acc.tflags[rt * (acc.nfw + 1) + x] = 0u;
+        if (tid == 0) acc.arrive[rt] = 0u;
+    }
     const int h_q = g.ret_heads[r];
     __shared__ __align__(16) float wq[128 * 16];
     __shared__ float qs[kTR1][16];
@@ -337,21 +356,25 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// P2.  Mass histograms over x = s (m' - e) in bins of 1/4 (weights exp(-x)
-// summed in fp64 LDS atomics); the cut bin with a target raised by a margin
-// that covers the approximation; U = bins <= cut + 1; pool segments, sized
-// by a bound of U's size, for the rows whose U is small enough.
+// P2.  grid (ceil(n_tok / 32), n_ret, nsplit), 256 threads: workgroup z takes
+// the z-th of nsplit equal runs of the row tile's key tiles.  Mass histograms
+// over x = s (m' - e) in bins of 1/4 (weights exp(-x) summed in fp64 LDS
+// atomics, then added into the device accumulators); the last workgroup of
+// the row tile: the cut bin with a target raised by a margin that covers the
+// approximation; U = bins <= cut + 1; pool segments, sized by a bound of U's
+// size, for the rows whose U is small enough.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restrict__ k_low,
                                                    const float* __restrict__ top_p,
                                                    const uint16_t* __restrict__ qlow, CState* __restrict__ st,
                                                    unsigned long long* __restrict__ pool_ctr,
-                                                   unsigned long long pool_cap, uint32_t* __restrict__ tflags,
-                                                   int nfw) {
+                                                   unsigned long long pool_cap, HistAcc acc) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const float s = g.idx_scale;
     const float sB = s * kBinsPerX;
+    const int nfw = acc.nfw;
     __shared__ double hist[kHB][kTR];
+    __shared__ int s_last;
     __shared__ uint32_t tflag[kFlagWords];              // key tiles holding a pair with x < kProv
     __shared__ int s_full;                              // a row's U reaches past kProv: no tile list
     __shared__ float qs[kTR][16];
@@ -372,7 +395,12 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     __syncthreads();
     const TileCtx tc = tile_ctx(g, k_low, qs);
     const float mpB = r_mp[tc.lr] * sB;
-    {
+    // this workgroup's run of key tiles (none when the row tile has fewer
+    // tiles than splits)
+    const int ns = min(acc.nsplit, tc.ntile), z = blockIdx.z;
+    const int tb = z < ns ? (int)((long long)z * tc.ntile / ns) : 0;
+    const int te = z < ns ? (int)((long long)(z + 1) * tc.ntile / ns) : 0;
+    if (te > tb) {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
         // Pairs of the open-ended last bin (x >= kProv, weights below e^-10 of
         // the row maximum) are summed in registers: a float sum per tile (16
@@ -381,7 +409,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         // with none of them (no lane maximum below kProv) skips the bins.
         double* hrow = &hist[0][tc.lr];
         double far = 0.0;
-        tile_loop<kPre>(wid, 4, tc.ntile, [&](int it) { return tc.page(it); },
+        tile_loop<kPre>(tb + wid, 4, te, [&](int it) { return tc.page(it); },
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
             float mx = sc[0];
@@ -420,6 +448,34 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         atomicAdd(&hrow[(kHB - 1) * kTR], far);
     }
     __syncthreads();
+    const size_t rt = (size_t)r * acc.nt32 + blockIdx.x;     // the row tile
+    uint32_t* tf = acc.tflags + rt * (nfw + 1);
+    if (acc.nsplit > 1) {
+        // add this run's histograms and flags into the accumulators; the
+        // last workgroup of the row tile to arrive reads them back
+        for (int x = tid; x < kHB * n_valid; x += 256) {
+            const int b = x / n_valid, row = x - b * n_valid;
+            const double v = hist[b][row];
+            if (v != 0.0) unsafeAtomicAdd(&acc.hist[((size_t)(t0 + row) * g.n_ret + r) * kHB + b], v);
+        }
+        for (int x = tid; x < nfw; x += 256)
+            if (tflag[x]) atomicOr(&tf[x], tflag[x]);
+        __threadfence();
+        __syncthreads();
+        if (tid == 0) s_last = atomicAdd(&acc.arrive[rt], 1u) == (uint32_t)(acc.nsplit - 1);
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();
+        for (int x = tid; x < kHB * kTR; x += 256) {
+            const int b = x / kTR, row = x - b * kTR;
+            hist[b][row] = row < n_valid ? __hip_atomic_load(&acc.hist[((size_t)(t0 + row) * g.n_ret + r) * kHB + b],
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                         : 0.0;
+        }
+        __syncthreads();
+    } else {
+        for (int x = tid; x < nfw; x += 256) tf[x] = tflag[x];
+    }
     // cut bin of the approximate masses, U = bins <= cut + 1.  The target
     // carries a margin eta that covers the relative error of the approximate
     // weights (<= s delta / 8 plus the exp2 rounding); U is every key when the
@@ -534,9 +590,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
             }
         }
     }
-    // the row tile's key-tile flags, and (last word) whether they suffice
-    uint32_t* tf = tflags + ((size_t)r * gridDim.x + blockIdx.x) * (nfw + 1);
-    for (int x = tid; x < nfw; x += 256) tf[x] = tflag[x];
+    // whether the row tile's key-tile flags suffice (last word)
     if (tid == 0) tf[nfw] = (uint32_t)s_full;
 }
 
@@ -1708,7 +1762,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, tflags, ctr, pool, head;
+    size_t crow, cst, qlow, counts, knorm, tflags, hacc, arrive, ctr, pool, head;
     int nblk, nfw;
 };
 
@@ -1723,7 +1777,10 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.knorm = w.counts + up((size_t)rows * 4);
     w.nfw = (n_keys + 1023) / 1024;                     // one bit per 32-key tile
     w.tflags = w.knorm + up((size_t)n_ret * w.nblk * 4);
-    w.ctr = w.tflags + up((size_t)((rows / n_ret + kTR - 1) / kTR) * n_ret * (w.nfw + 1) * 4);
+    const size_t nrt = (size_t)((rows / n_ret + kTR - 1) / kTR) * n_ret;   // row tiles
+    w.hacc = w.tflags + up(nrt * (w.nfw + 1) * 4);
+    w.arrive = w.hacc + up((size_t)rows * kHB * 8);
+    w.ctr = w.arrive + up(nrt * 4);
     w.pool = w.ctr + 256;
     w.head = w.pool;
     return w;
@@ -1754,12 +1811,21 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     unsigned long long* pool = (unsigned long long*)(base + w.pool);
     const unsigned long long pool_cap = (ws_bytes - w.head) / 8;
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
+    // key-tile runs per row tile of the histogram pass: about three waves of
+    // workgroups over the chip (four per CU)
+    HistAcc acc;
+    acc.hist = (double*)(base + w.hacc);
+    acc.tflags = tflags;
+    acc.arrive = (uint32_t*)(base + w.arrive);
+    acc.nt32 = (int)grid.x;
+    acc.nfw = w.nfw;
+    acc.nsplit = std::min(8, std::max(1, (3072 + (int)(grid.x * grid.y) - 1) / (int)(grid.x * grid.y)));
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
-                       (const bf16_t*)w_q, (const bf16_t*)k_low, qlow, knorm, w.nblk, cst);
-    hipLaunchKernelGGL(k_csel_hist, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, ctr, pool_cap,
-                       tflags, w.nfw);
+                       (const bf16_t*)w_q, (const bf16_t*)k_low, qlow, knorm, w.nblk, cst, acc);
+    hipLaunchKernelGGL(k_csel_hist, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, top_p,
+                       qlow, cst, ctr, pool_cap, acc);
     hipLaunchKernelGGL(k_csel_rec, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, qlow, cst, crow, pool, tflags,
                        w.nfw);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
