@@ -1339,29 +1339,33 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
         const int nwords = bmax >= bmin ? (int)((bmax - bmin) / 32u + 1u) : 0;
         if (nwords > 0 && nwords <= 2 * CAP) {
             uint32_t* bmp = sv;
+            // word w of the bitmap sits at w + w / 64: a thread's run of
+            // consecutive words then meets the other lanes' runs in distinct
+            // banks (the area holds 2 CAP + 2 CAP / 64 words)
+            const auto bw = [](int w) { return w + (w >> 6); };
             const int wper = (nwords + NT - 1) / NT;
             const int w0 = min(tid * wper, nwords), w1 = min(w0 + wper, nwords);
             // (tie mode) 0: no tie kept, 1: ties up to index jlim, 2: every tie
             int tmode = ntie <= 0 ? 0 : ((uint32_t)ntie >= ties_all ? 2 : 1);
             uint32_t jlim = 0u;
             if (tmode == 1) {
-                for (int w = tid; w < nwords; w += NT) bmp[w] = 0u;
+                for (int w = tid; w < nwords; w += NT) bmp[bw(w)] = 0u;
                 __syncthreads();
 #pragma unroll
                 for (int x = 0; x < PER; ++x)
                     if ((vals[x] & 15u) != 8u && ((vals[x] >> 4) & 1u)) {
                         const uint32_t o = (vals[x] >> 5) - bmin;
-                        atomicOr(&bmp[o >> 5], 1u << (o & 31u));
+                        atomicOr(&bmp[bw((int)(o >> 5))], 1u << (o & 31u));
                     }
                 __syncthreads();
                 unsigned long long c = 0ull;
-                for (int w = w0; w < w1; ++w) c += __popc(bmp[w]);
+                for (int w = w0; w < w1; ++w) c += __popc(bmp[bw(w)]);
                 unsigned long long tt;
                 unsigned long long rk = block_excl_scan_u64<NT>(c, &tt, scan_sh);
                 const unsigned long long want = (unsigned long long)ntie - 1ull;   // rank of the last kept tie
                 if (want >= rk && want < rk + c) {
                     for (int w = w0; w < w1; ++w) {
-                        uint32_t bits = bmp[w];
+                        uint32_t bits = bmp[bw(w)];
                         const int n = __popc(bits);
                         if (rk + (unsigned long long)n > want) {
                             for (unsigned long long k = want - rk; k > 0; --k) bits &= bits - 1u;
@@ -1374,7 +1378,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
                 __syncthreads();
                 jlim = (uint32_t)sm.s_S;
             }
-            for (int w = tid; w < nwords; w += NT) bmp[w] = 0u;
+            for (int w = tid; w < nwords; w += NT) bmp[bw(w)] = 0u;
             __syncthreads();
 #pragma unroll
             for (int x = 0; x < PER; ++x) {
@@ -1383,16 +1387,16 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
                 const bool tie = (vals[x] >> 4) & 1u;
                 if (tie && (tmode == 0 || (tmode == 1 && id > jlim))) continue;
                 const uint32_t o = id - bmin;
-                atomicOr(&bmp[o >> 5], 1u << (o & 31u));
+                atomicOr(&bmp[bw((int)(o >> 5))], 1u << (o & 31u));
             }
             __syncthreads();
             unsigned long long c = 0ull;
-            for (int w = w0; w < w1; ++w) c += __popc(bmp[w]);
+            for (int w = w0; w < w1; ++w) c += __popc(bmp[bw(w)]);
             unsigned long long cnt;
             unsigned long long o = block_excl_scan_u64<NT>(c, &cnt, scan_sh);
             uint32_t* ubi = reinterpret_cast<uint32_t*>(ub);
             for (int w = w0; w < w1; ++w) {
-                uint32_t bits = bmp[w];
+                uint32_t bits = bmp[bw(w)];
                 while (bits) {
                     const int b = __ffs(bits) - 1;
                     bits &= bits - 1u;
@@ -1520,7 +1524,7 @@ __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restr
         return;
     }
     if (cr.count <= kTinyU) return;                     // the small-row kernel's
-    __shared__ unsigned long long sk[kSmallU];
+    __shared__ unsigned long long sk[kSmallU + kSmallU / 128];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
     __shared__ ResolveSmem sm;
     resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
@@ -1538,7 +1542,7 @@ __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* 
     const int row = blockIdx.x;
     const CRow cr = rows[row];
     if (cr.mode != kBuf || cr.bad || cr.count > kTinyU) return;
-    __shared__ unsigned long long sk[kTinyU];
+    __shared__ unsigned long long sk[kTinyU + kTinyU / 128];
     __shared__ unsigned long long scan_sh[kRTS / 64 + 1];
     __shared__ ResolveSmem sm;
     resolve_row<kTinyU, kRTS>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
@@ -1553,7 +1557,7 @@ __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* 
                                                              const float* __restrict__ top_p,
                                                              unsigned long long* __restrict__ pool,
                                                              int* __restrict__ counts) {
-    __shared__ unsigned long long sk[kSegMax];
+    __shared__ unsigned long long sk[kSegMax + kSegMax / 128];
     __shared__ unsigned long long scan_sh[kRTL / 64 + 1];
     __shared__ ResolveSmem sm;
     for (int row = blockIdx.x; row < n_rows; row += gridDim.x) {
