@@ -1056,7 +1056,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 // sorted ascending, stored over the segment.  Writes the row's count (-1 if
 // certification failed).  NT threads, U of up to CAP keys in LDS.
 // ---------------------------------------------------------------------------
-constexpr int kRB = 1024;        // radix buckets per level of the resolve
+constexpr int kRBits = 10;       // radix bits per level of the resolve (the small-row kernel: 8)
 
 // Low word of a resolve entry (score key << 32 | low): larger for a smaller
 // key index (ties rank lowest index first), with the writer of the entry in
@@ -1066,20 +1066,22 @@ __device__ __forceinline__ uint32_t lo_word(int key, int writer) {
 }
 __device__ __forceinline__ uint32_t lo_key(uint32_t lo) { return 0xFFFFFu - (lo >> 3); }
 
+template <int RB>
 struct ResolveSmem {
-    unsigned long long hm[kRB];
-    uint32_t hc[kRB];
+    unsigned long long hm[RB];
+    uint32_t hc[RB];
     unsigned long long small_v[64], small_w[64];
     uint32_t kmin, kmax, s_u, tkey;
     int s_i, ntie, fail;
     unsigned long long s_S;
 };
 
-template <int CAP, int NT>
+template <int CAP, int NT, int RBITS = kRBits>
 __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t* __restrict__ k_low,
                             const uint16_t* __restrict__ qlow, const float* __restrict__ top_p,
                             unsigned long long* __restrict__ pool, int* __restrict__ count_out,
-                            unsigned long long* sk, unsigned long long* scan_sh, ResolveSmem& sm) {
+                            unsigned long long* sk, unsigned long long* scan_sh, ResolveSmem<1 << RBITS>& sm) {
+    constexpr int kRB = 1 << RBITS;                      // radix buckets per level
     constexpr int PER = CAP / NT;
     const int tid = threadIdx.x, lane = tid & 63;
     const int slots = cr.count;
@@ -1143,7 +1145,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     for (int level = 0; level < 6 && !done; ++level) {
         const uint32_t span = khi - klo;
         const int bits = span ? 32 - __clz(span) : 0;
-        const int shift = bits > 10 ? bits - 10 : 0;
+        const int shift = bits > RBITS ? bits - RBITS : 0;
         for (int b = tid; b < kRB; b += NT) {
             sm.hm[b] = 0ull;
             sm.hc[b] = 0u;
@@ -1160,6 +1162,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
         }
         __syncthreads();
         constexpr int BPT = kRB / NT;                       // buckets per thread (1 or 2)
+        static_assert(BPT >= 1 && kRB % NT == 0, "whole buckets per thread");
         unsigned long long loc = 0ull;
 #pragma unroll
         for (int x = 0; x < BPT; ++x) loc += sm.hm[BPT * tid + x];
@@ -1526,13 +1529,14 @@ __global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restr
     if (cr.count <= kTinyU) return;                     // the small-row kernel's
     __shared__ unsigned long long sk[kSmallU + kSmallU / 128];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
-    __shared__ ResolveSmem sm;
+    __shared__ ResolveSmem<1 << kRBits> sm;
     resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
 }
 
-// Rows with U of at most kTinyU keys: the same resolve on 256 threads and a
-// quarter of the LDS, so that several rows share a CU.
-constexpr int kRTS = 256;
+// Rows with U of at most kTinyU keys: the same resolve on 128 threads with
+// 256-bucket radix levels (12 KB of LDS), so that many rows share a CU.
+constexpr int kRTS = 128;
+constexpr int kRBitsS = 8;
 __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* __restrict__ rows,
                                                              const bf16_t* __restrict__ k_low,
                                                              const uint16_t* __restrict__ qlow,
@@ -1544,8 +1548,8 @@ __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* 
     if (cr.mode != kBuf || cr.bad || cr.count > kTinyU) return;
     __shared__ unsigned long long sk[kTinyU + kTinyU / 128];
     __shared__ unsigned long long scan_sh[kRTS / 64 + 1];
-    __shared__ ResolveSmem sm;
-    resolve_row<kTinyU, kRTS>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+    __shared__ ResolveSmem<1 << kRBitsS> sm;
+    resolve_row<kTinyU, kRTS, kRBitsS>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
 }
 
 // Rows with U in (kSmallU, kSegMax]: a fixed grid of 512-thread workgroups
@@ -1559,7 +1563,7 @@ __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* 
                                                              int* __restrict__ counts) {
     __shared__ unsigned long long sk[kSegMax + kSegMax / 128];
     __shared__ unsigned long long scan_sh[kRTL / 64 + 1];
-    __shared__ ResolveSmem sm;
+    __shared__ ResolveSmem<1 << kRBits> sm;
     for (int row = blockIdx.x; row < n_rows; row += gridDim.x) {
         const CRow cr = rows[row];
         if (cr.mode != kBuf || cr.count <= kSmallU) continue;
@@ -1815,15 +1819,19 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     unsigned long long* pool = (unsigned long long*)(base + w.pool);
     const unsigned long long pool_cap = (ws_bytes - w.head) / 8;
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
-    // key-tile runs per row tile of the histogram pass: about three waves of
-    // workgroups over the chip (four per CU)
+    // key-tile runs per row tile of the histogram pass: about six waves of
+    // workgroups over the chip (four per CU), but runs of at least ~1024 key
+    // tiles (each workgroup's fixed cost: q_low, LDS clears, the merge)
     HistAcc acc;
     acc.hist = (double*)(base + w.hacc);
     acc.tflags = tflags;
     acc.arrive = (uint32_t*)(base + w.arrive);
     acc.nt32 = (int)grid.x;
     acc.nfw = w.nfw;
-    acc.nsplit = std::min(8, std::max(1, (3072 + (int)(grid.x * grid.y) - 1) / (int)(grid.x * grid.y)));
+    {
+        const int nwg = (int)(grid.x * grid.y), max_tiles = (n_keys + 31) / 32;
+        acc.nsplit = std::max(1, std::min({8, (6144 + nwg - 1) / nwg, max_tiles / 1024}));
+    }
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
