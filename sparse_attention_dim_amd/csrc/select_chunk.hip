@@ -136,31 +136,35 @@ __device__ __forceinline__ int bin_of(float x) {
 template <int D, typename Page, typename Load, typename Body>
 __device__ __forceinline__ void tile_loop(int first, int stride, int ntile, Page page, Load load, Body body) {
     // the loads run unconditionally on clamped tile numbers (the few past the
-    // end repeat the last tile), so their waits count exactly
+    // end repeat the last tile), so their waits count exactly.  The operands
+    // sit in a ring of 2 D registers: tile t's operand is in slot t mod 2D
+    // and the load of tile t + D goes to another slot, so no operand is ever
+    // copied between registers (a copy would wait for its load).  The page
+    // ids sit in a ring of 2 D as well, requested 2 D tiles ahead.
     const auto cl = [&](int it) { return min(it, ntile - 1); };
-    int pring[D];
-    uint4 ring[D];
+    constexpr int R = 2 * D;
+    int pring[R];
+    uint4 ring[R];
 #pragma unroll
-    for (int x = 0; x < D; ++x) pring[x] = page(cl(first + x * stride));
+    for (int x = 0; x < R; ++x) pring[x] = page(cl(first + x * stride));
 #pragma unroll
     for (int x = 0; x < D; ++x) {
-        const int it = first + x * stride;
-        ring[x] = load(cl(it), pring[x]);
-        pring[x] = page(cl(it + D * stride));
+        ring[x] = load(cl(first + x * stride), pring[x]);
+        pring[x] = page(cl(first + (x + R) * stride));
     }
-    for (int it0 = first; it0 < ntile; it0 += D * stride) {
+    for (int it0 = first; it0 < ntile; it0 += R * stride) {
 #pragma unroll
-        for (int x = 0; x < D; ++x) {
+        for (int x = 0; x < R; ++x) {
             const int it = it0 + x * stride;
-            const uint4 cur = ring[x];
-            const int nxt = it + D * stride;
-            ring[x] = load(cl(nxt), pring[x]);
-            pring[x] = page(cl(nxt + D * stride));
-            if (it < ntile) body(it, cur);
+            const int s = (x + D) % R;                  // the slot of tile it + D
+            ring[s] = load(cl(it + D * stride), pring[s]);
+            pring[s] = page(cl(it + (D + R) * stride));
+            if (it < ntile) body(it, ring[x]);
         }
     }
 }
-constexpr int kPre = 8;          // tile loads in flight per wave
+constexpr int kPre = 8;          // tile loads requested ahead per wave
+constexpr int kPreHist = 4;      // the same in the histogram, level and emit passes (registers set their occupancy)
 
 // LDS of the radix levels: per-row bucket masses and counts and the gathered
 // candidates of the last bucket.  (The P2 histograms are bin-major, [bin][row],
@@ -409,7 +413,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         // with none of them (no lane maximum below kProv) skips the bins.
         double* hrow = &hist[0][tc.lr];
         double far = 0.0;
-        tile_loop<kPre>(tb + wid, 4, te, [&](int it) { return tc.page(it); },
+        tile_loop<kPreHist>(tb + wid, 4, te, [&](int it) { return tc.page(it); },
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
             float mx = sc[0];
@@ -836,7 +840,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
 #pragma unroll
         for (int c = 0; c < 16; ++c) qv[c] = qs[lr][c];
         unsigned long long zacc = 0ull;
-        tile_loop<kPre>(wid, 4, ntile, page_a, load_a, [&](int it, const uint4& cur) {
+        tile_loop<kPreHist>(wid, 4, ntile, page_a, load_a, [&](int it, const uint4& cur) {
             const f32x16_t sc = mfma_tile(cur);
             // which of this lane's pairs need an exact score
             uint32_t need = 0;
@@ -1659,7 +1663,7 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
         return *reinterpret_cast<const uint4*>(
             k_low + (((size_t)pg * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
     };
-    tile_loop<kPre>(0, 1, ntile, page_a, load_a, [&](int it, const uint4& cur) {
+    tile_loop<kPreHist>(0, 1, ntile, page_a, load_a, [&](int it, const uint4& cur) {
         f32x16_t sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
