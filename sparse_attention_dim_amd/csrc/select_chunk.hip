@@ -59,16 +59,16 @@ constexpr int kNBP = kNB + 1;
 constexpr int kCapC = 128;       // candidates of one cut bucket sorted in LDS
 constexpr int kSmallU = 8192;    // U sorted by the per-row resolve kernel
 constexpr int kTinyU = 1024;     // U sorted by the small-row resolve kernel
-constexpr int kSegMax = 16384;   // largest segment (U plus padding), sorted by the large-row kernel
-constexpr int kSegBlk = 16;      // segment slots reserved at a time by one lane of the third pass
-constexpr int kSegPad = 8 * kSegBlk;   // 8 writers per row (4 waves x 2 halves): their last blocks' slack
+constexpr int kSegBlk = 8;       // segment slots reserved at a time by one lane of the third pass
+constexpr int kSegPad = 8 * kSegBlk;   // 8 writers per row and run (4 waves x 2 halves): their last blocks' slack
+// largest segment (U plus each run's padding), sorted by the large-row kernel:
+// U of up to 16384 keys at the most runs (a multiple of its 512 threads)
+constexpr int kSegMax = 16384 + 8 * kSegPad;
 constexpr int kPoolPerRow = 4096;   // pool entries per row in the recommended workspace
 constexpr int kNormKeys = 4096;  // keys per block of the key-norm pre-pass
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr unsigned long long kNoSeg = ~0ull;
 
-// slots of a row's pool segment for a bound ub of U's size
-__device__ __forceinline__ uint32_t seg_slots(uint32_t ub) { return min(ub, (uint32_t)(kSegMax - kSegPad)) + kSegPad; }
 
 // modes of a row
 constexpr int kAll = 0;          // p >= 1: every key
@@ -183,7 +183,7 @@ struct CState {
     float e_thr;     // a pair is in U iff its MFMA score e >= e_thr
     float edge;      // exact scores of keys outside U are <= edge
     uint32_t klo, khi, shift;   // exact-score key range of the level path and its first shift
-    uint32_t ucount; // keys of U: an upper bound from the mass histogram (exact when U is every key)
+    uint32_t ucount; // keys of U (exact: the runs' counts of pairs of bins <= uend)
     int mode;        // kAll or kLevel
     int uend;        // last P2 bin of U
     int pad0, pad1;
@@ -262,12 +262,23 @@ __device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (
 // workgroups: their histograms and tile flags meet in these device
 // accumulators (zeroed by P1), and the last workgroup of a row tile to
 // arrive takes the epilogue.
+constexpr int kMaxSplit = 8;     // most runs of key tiles per row tile
+
 struct HistAcc {
     double* hist;        // [rows][kHB], rows in result-record order
+    uint32_t* cnt;       // [rows][nsplit][kProv]: pairs per bin below kProv, per run
+    uint32_t* segoff;    // [rows][nsplit]: slot of each run's part of the row's segment
     uint32_t* tflags;    // [n_ret][nt32][nfw + 1]
     uint32_t* arrive;    // [n_ret][nt32]
     int nt32, nfw, nsplit;
 };
+
+// the run of key tiles [tb, te) of split z of a row tile with ntile tiles
+__device__ __forceinline__ void split_run(int z, int nsplit, int ntile, int& tb, int& te) {
+    const int ns = min(nsplit, ntile);
+    tb = z < ns ? (int)((long long)z * ntile / ns) : 0;
+    te = z < ns ? (int)((long long)(z + 1) * ntile / ns) : 0;
+}
 
 // ---------------------------------------------------------------------------
 // P1.  grid (ceil(n_tok / 64), n_ret), 256 threads: q_low of the rows (fixed-
@@ -365,25 +376,29 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
 // over x = s (m' - e) in bins of 1/4 (weights exp(-x) summed in fp64 LDS
 // atomics, then added into the device accumulators); the last workgroup of
 // the row tile: the cut bin with a target raised by a margin that covers the
-// approximation; U = bins <= cut + 1; pool segments, sized by a bound of U's
-// size, for the rows whose U is small enough.
+// approximation; U = bins <= cut + 1; pool segments, sized exactly from the
+// runs' counts of U's pairs (one part per run), and the result records of the
+// rows whose U fits one.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restrict__ k_low,
                                                    const float* __restrict__ top_p,
                                                    const uint16_t* __restrict__ qlow, CState* __restrict__ st,
                                                    unsigned long long* __restrict__ pool_ctr,
-                                                   unsigned long long pool_cap, HistAcc acc) {
+                                                   unsigned long long pool_cap, HistAcc acc,
+                                                   CRow* __restrict__ rows_out) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const float s = g.idx_scale;
     const float sB = s * kBinsPerX;
     const int nfw = acc.nfw;
     __shared__ double hist[kHB][kTR];
+    __shared__ uint32_t hcnt[kProv][kTR];                // pairs per bin below kProv (this run)
     __shared__ int s_last;
     __shared__ uint32_t tflag[kFlagWords];              // key tiles holding a pair with x < kProv
     __shared__ int s_full;                              // a row's U reaches past kProv: no tile list
     __shared__ float qs[kTR][16];
     __shared__ float r_mp[kTR], r_delta[kTR];
-    __shared__ uint32_t r_ucount[kTR], r_ulow[kTR];
+    __shared__ uint32_t r_tot[kTR], r_cz[kTR][kMaxSplit];
+    __shared__ unsigned long long r_seg[kTR];
     __shared__ int r_mode[kTR], r_uend[kTR];
     load_qs(g, qlow, qs);
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
@@ -394,6 +409,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         r_delta[tid] = c->delta;
     }
     for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
+    for (int x = tid; x < kProv * kTR; x += 256) (&hcnt[0][0])[x] = 0u;
     for (int x = tid; x < nfw; x += 256) tflag[x] = 0u;
     if (tid == 0) s_full = 0;
     __syncthreads();
@@ -401,9 +417,9 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     const float mpB = r_mp[tc.lr] * sB;
     // this workgroup's run of key tiles (none when the row tile has fewer
     // tiles than splits)
-    const int ns = min(acc.nsplit, tc.ntile), z = blockIdx.z;
-    const int tb = z < ns ? (int)((long long)z * tc.ntile / ns) : 0;
-    const int te = z < ns ? (int)((long long)(z + 1) * tc.ntile / ns) : 0;
+    const int z = blockIdx.z;
+    int tb, te;
+    split_run(z, acc.nsplit, tc.ntile, tb, te);
     if (te > tb) {
         constexpr float kW = -kLog2eF / kBinsPerX;       // exp(-x / 4) = 2^(x kW)
         // Pairs of the open-ended last bin (x >= kProv, weights below e^-10 of
@@ -433,7 +449,11 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                         const float w = __builtin_amdgcn_exp2f(x * kW);
                         const bool nr = x < (float)kProv;
                         f += nr ? 0.0f : w;
-                        if (nr) atomicAdd(&hrow[bin_of(x) * kTR], (double)w);
+                        if (nr) {
+                            const int b = bin_of(x);
+                            atomicAdd(&hrow[b * kTR], (double)w);
+                            atomicAdd(&hcnt[b][tc.lr], 1u);
+                        }
                     }
                 }
             } else {
@@ -442,8 +462,13 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                     const float x = bin_x(sc[i], sB, mpB);
                     const float w = __builtin_amdgcn_exp2f(x * kW);
                     if (tc.key_of(it, i) <= tc.pos) {
-                        if (x < (float)kProv) atomicAdd(&hrow[bin_of(x) * kTR], (double)w);
-                        else f += w;
+                        if (x < (float)kProv) {
+                            const int b = bin_of(x);
+                            atomicAdd(&hrow[b * kTR], (double)w);
+                            atomicAdd(&hcnt[b][tc.lr], 1u);
+                        } else {
+                            f += w;
+                        }
                     }
                 }
             }
@@ -454,6 +479,11 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     __syncthreads();
     const size_t rt = (size_t)r * acc.nt32 + blockIdx.x;     // the row tile
     uint32_t* tf = acc.tflags + rt * (nfw + 1);
+    for (int x = tid; x < kProv * n_valid; x += 256) {
+        const int row = x / kProv, b = x - row * kProv;
+        acc.cnt[(((size_t)(t0 + row) * g.n_ret + r) * acc.nsplit + z) * kProv + b] = hcnt[b][row];
+    }
+    __syncthreads();                                     // (read back by the epilogue when nsplit == 1)
     if (acc.nsplit > 1) {
         // add this run's histograms and flags into the accumulators; the
         // last workgroup of the row tile to arrive reads them back
@@ -520,24 +550,28 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
             const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
             double light = 0.0;
             for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
-            // keys of U, bounded from above by the masses: a key of bin b
-            // (x in [b, b + 1)) weighs at least e^-(b+1)/4, up to the exp2
-            // rounding; every key when U is all of them
-            const uint32_t n_keys = (uint32_t)(g.pos0 + t0 + row + 1);
-            uint32_t uc = n_keys, ul = n_keys;
-            if (ue < kHB - 1) {
-                // and from below (a key of bin b weighs at most e^-b/4)
-                double ub = 0.0, lb = 0.0;
-                for (int b = 0; b <= ue; ++b)
-                    if (hist[b][row] > 0.0) {
-                        ub += ceil(hist[b][row] * exp(0.25 * (double)(b + 1)) * (1.0 + 0x1.0p-20)) + 1.0;
-                        lb += floor(hist[b][row] * exp(0.25 * (double)b) * (1.0 - 0x1.0p-20));
-                    }
-                uc = ub < (double)n_keys ? (uint32_t)ub : n_keys;
-                ul = lb < (double)uc ? (uint32_t)lb : uc;
+            // the keys of U in each run of key tiles, exactly: the pairs of
+            // bins <= ue counted by every run (every key of the run when U
+            // is all of them); the row's segment holds run after run, each
+            // with kSegPad slots of slack for its writers' last blocks
+            const int pos = g.pos0 + t0 + row;
+            uint32_t uc = 0u, tot = 0u;
+            for (int zz = 0; zz < acc.nsplit; ++zz) {
+                uint32_t c = 0u;
+                if (ue < kHB - 1) {
+                    const uint32_t* cr = acc.cnt + (((size_t)(t0 + row) * g.n_ret + r) * acc.nsplit + zz) * kProv;
+                    for (int b = 0; b <= ue; ++b) c += cr[b];
+                } else {
+                    int rb, re;
+                    split_run(zz, acc.nsplit, tc.ntile, rb, re);
+                    c = (uint32_t)max(0, min(32 * re, pos + 1) - 32 * rb);
+                }
+                r_cz[row][zz] = c;
+                uc += c;
+                tot += c + kSegPad;
             }
             o.ucount = uc;
-            r_ulow[row] = ul;
+            r_tot[row] = tot;
             o.uend = ue;
             o.light = (unsigned long long)__double2ll_rn(light * kFix);
             const double mp = (double)o.mp;
@@ -568,81 +602,131 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         }
         r_mode[row] = o.mode;
         r_uend[row] = o.uend;
-        r_ucount[row] = o.ucount;
+        r_seg[row] = kNoSeg;
         st[(size_t)(t0 + row) * g.n_ret + r] = o;
     }
     __syncthreads();
-    // pool segments for the rows whose U is small enough (one allocation per
-    // workgroup; a full pool sends the rows to the radix levels)
-    // A row whose U may fit (its lower bound does) gets a segment of its upper
-    // bound, at most the largest segment; the recording pass sends a row that
-    // overflows it to the radix levels.
+    // pool segments for the rows whose U fits the largest segment (one
+    // allocation per workgroup; a full pool sends the rows to the radix levels)
     if (tid == 0) {
         unsigned long long tot = 0;
         for (int row = 0; row < n_valid; ++row)
-            if (r_mode[row] == kLevel && r_ulow[row] <= (uint32_t)(kSegMax - kSegPad)) tot += seg_slots(r_ucount[row]);
+            if (r_mode[row] == kLevel && r_tot[row] <= (uint32_t)kSegMax) tot += r_tot[row];
         if (tot) {
             const unsigned long long base = atomicAdd(pool_ctr, tot);
             if (base + tot <= pool_cap) {
                 unsigned long long off = base;
                 for (int row = 0; row < n_valid; ++row)
-                    if (r_mode[row] == kLevel && r_ulow[row] <= (uint32_t)(kSegMax - kSegPad)) {
-                        st[(size_t)(t0 + row) * g.n_ret + r].seg = off;
-                        off += seg_slots(r_ucount[row]);
+                    if (r_mode[row] == kLevel && r_tot[row] <= (uint32_t)kSegMax) {
+                        r_seg[row] = off;
+                        off += r_tot[row];
                         if (r_uend[row] >= kProv) s_full = 1;   // a recorded U past the flagged tiles
                     }
             }
         }
+    }
+    __syncthreads();
+    // each pooled row: its segment, the runs' places in it, and its result
+    // record (the recording pass fills the segment; the resolve reads it)
+    if (tid < n_valid && r_seg[tid] != kNoSeg) {
+        const size_t rg = (size_t)(t0 + tid) * g.n_ret + r;
+        CState* c = st + rg;
+        c->seg = r_seg[tid];
+        uint32_t off = 0u;
+        for (int zz = 0; zz < acc.nsplit; ++zz) {
+            acc.segoff[rg * acc.nsplit + zz] = off;
+            off += r_cz[tid][zz] + kSegPad;
+        }
+        CRow out;
+        out.mp = c->mp;
+        out.delta = c->delta;
+        out.e_thr = c->e_thr;
+        out.T = 0.0f;
+        out.d_edge = c->edge;
+        out.mode = kBuf;
+        out.u_end = c->uend;
+        out.n_tie = 0;
+        out.count = (int)r_tot[tid];
+        out.bad = 0;
+        out.target = 0ull;
+        out.seg = r_seg[tid];
+        out.light = c->light;
+        rows_out[rg] = out;
     }
     // whether the row tile's key-tile flags suffice (last word)
     if (tid == 0) tf[nfw] = (uint32_t)s_full;
 }
 
 // ---------------------------------------------------------------------------
-// P3 for the rows with a pool segment: the key indices of U (MFMA score
-// >= e_thr) into the segment, slots reserved kSegBlk at a time per lane, the
-// slack of each lane's last block marked empty.  The row's result record
-// (mode kBuf) follows; its exact scores are formed by the resolve pass.
+// P3.  grid (ceil(n_tok / 32), n_ret, nsplit), 256 threads: workgroup z
+// records, for the rows with a pool segment, the key indices of U (MFMA score
+// >= e_thr) found in run z of the key tiles (the runs of P2) into that run's
+// part of the segment, slots reserved kSegBlk at a time per lane; the slack
+// of each lane's last block and the part's unused tail are marked empty.
+// A writer (wave, half) visits its keys in increasing order and the runs'
+// parts follow each other in key order, so each writer's entries, read in
+// slot order, ascend.  The rows' result records were written by P2.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restrict__ k_low,
                                                   const uint16_t* __restrict__ qlow, CState* __restrict__ st,
-                                                  CRow* __restrict__ rows_out, unsigned long long* __restrict__ pool,
-                                                  const uint32_t* __restrict__ tflags, int nfw) {
+                                                  unsigned long long* __restrict__ pool, HistAcc acc) {
     const int tid = threadIdx.x, wid = tid >> 6;
-    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
+    const int r = blockIdx.y, t0 = blockIdx.x * kTR, z = blockIdx.z;
     const int n_valid = min(kTR, g.n_tok - t0);
+    const int nfw = acc.nfw;
     __shared__ float qs[kTR][16];
     __shared__ CState rs[kTR];
-    __shared__ uint32_t ucnt[kTR], ureal[kTR];
-    __shared__ uint16_t tlist[kTileList];               // the flagged key tiles, ascending
+    __shared__ uint32_t ucnt[kTR], ucap[kTR];
+    __shared__ unsigned long long ubase[kTR];
+    __shared__ uint16_t tlist[kTileList];               // the flagged key tiles of the run, ascending
     __shared__ unsigned long long scan_sh[256 / 64 + 1];
     __shared__ int s_any;
     if (tid == 0) s_any = 0;
     __syncthreads();
     if (tid < n_valid) {
-        rs[tid] = st[(size_t)(t0 + tid) * g.n_ret + r];
+        const size_t rg = (size_t)(t0 + tid) * g.n_ret + r;
+        rs[tid] = st[rg];
         ucnt[tid] = 0u;
-        ureal[tid] = 0u;
-        if (rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) s_any = 1;
+        ucap[tid] = 0u;
+        ubase[tid] = 0ull;
+        if (rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) {
+            const uint32_t o0 = acc.segoff[rg * acc.nsplit + z];
+            const uint32_t o1 = z + 1 < acc.nsplit ? acc.segoff[rg * acc.nsplit + z + 1]
+                                                   : rs[tid].ucount + (uint32_t)(acc.nsplit * kSegPad);
+            ubase[tid] = rs[tid].seg + o0;
+            ucap[tid] = o1 - o0;
+            s_any = 1;
+        }
     }
     __syncthreads();
     if (!s_any) return;
     load_qs(g, qlow, qs);
-    // The key tiles that can hold a key of U (flagged by the histogram pass),
-    // listed in LDS; every tile when a row's U reaches past the flagged bins
-    // or the list does not fit.
-    const uint32_t* tf = tflags + ((size_t)r * gridDim.x + blockIdx.x) * (nfw + 1);
-    int nlist = -1;                                      // -1: every tile
+    __syncthreads();                                     // qs complete before the tile view reads it
+    const TileCtx tc = tile_ctx(g, k_low, qs);
+    int tb, te;
+    split_run(z, acc.nsplit, tc.ntile, tb, te);
+    // The run's key tiles that can hold a key of U (flagged by the histogram
+    // pass), listed in LDS; every tile of the run when a row's U reaches past
+    // the flagged bins or the list does not fit.
+    const uint32_t* tf = acc.tflags + ((size_t)r * acc.nt32 + blockIdx.x) * (nfw + 1);
+    int nlist = -1;                                      // -1: every tile of the run
     if (tf[nfw] == 0u) {
         constexpr int kPerT = kFlagWords / 256;          // flag words per thread
         const int wb = tid * kPerT, we = min(wb + kPerT, nfw);
+        const auto bits_of = [&](int w) {
+            uint32_t bits = tf[w];
+            const int k0 = 32 * w;                       // keep tiles tb <= k < te
+            if (k0 < tb) bits &= tb - k0 >= 32 ? 0u : ~0u << (tb - k0);
+            if (k0 + 32 > te) bits &= te - k0 <= 0 ? 0u : ~0u >> (32 - (te - k0));
+            return bits;
+        };
         uint32_t c = 0u;
-        for (int w = wb; w < we; ++w) c += __popc(tf[w]);
+        for (int w = wb; w < we; ++w) c += __popc(bits_of(w));
         unsigned long long tot;
         uint32_t o = (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
         if (tot <= (unsigned long long)kTileList) {
             for (int w = wb; w < we; ++w) {
-                uint32_t bits = tf[w];
+                uint32_t bits = bits_of(w);
                 while (bits) {
                     const int b = __ffs(bits) - 1;
                     bits &= bits - 1u;
@@ -653,15 +737,13 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         }
     }
     __syncthreads();
-    const TileCtx tc = tile_ctx(g, k_low, qs);
     const int lr = tc.lr;
     const bool pooled = tc.row_ok && rs[lr].mode == kLevel && rs[lr].seg != kNoSeg;
-    const unsigned long long sg = pooled ? rs[lr].seg : 0ull;
-    const uint32_t scap = pooled ? seg_slots(rs[lr].ucount) : 0u;
+    const unsigned long long sg = pooled ? ubase[lr] : 0ull;
+    const uint32_t scap = pooled ? ucap[lr] : 0u;
     const float e_fast = pooled ? rs[lr].e_thr : INFINITY;
-    uint32_t bp = 0u, be = 0u, nreal = 0u;              // the lane's reserved block [bp, be)
-    // entry: (writer << 24) | key.  A writer (wave, half) visits its keys in
-    // increasing order, so its entries, read in slot order, ascend.
+    uint32_t bp = 0u, be = 0u;                          // the lane's reserved block [bp, be)
+    // entry: (writer << 24) | key
     const unsigned long long wtag = (unsigned long long)(wid * 2 + tc.hh) << 24;
     const auto record = [&](int key) {
         if (bp == be) {
@@ -670,7 +752,6 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         }
         if (bp < scap) pool[sg + bp] = wtag | (unsigned long long)(uint32_t)key;
         ++bp;
-        ++nreal;
     };
     const auto body = [&](int it, const uint4& cur) {
         const f32x16_t sc = tc.mfma(cur);
@@ -691,40 +772,25 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         }
     };
     // the listed tiles only (in increasing order per wave, so a writer's
-    // entries still ascend), or every tile
+    // entries still ascend), or every tile of the run
     const bool use_list = nlist >= 0;
-    const int nvirt = use_list ? nlist : tc.ntile;
-    const auto tile_of = [&](int k) { return use_list ? (int)tlist[min(k, kTileList - 1)] : k; };
+    const int nvirt = use_list ? nlist : te - tb;
+    const auto tile_of = [&](int k) { return use_list ? (int)tlist[min(k, kTileList - 1)] : tb + k; };
     if (nvirt > 0)
         tile_loop<kPre>(wid, 4, nvirt, [&](int k) { return tc.page(tile_of(k)); },
                         [&](int k, int pg) { return tc.load(tile_of(k), pg); },
                         [&](int k, const uint4& cur) { body(tile_of(k), cur); });
     for (uint32_t x = bp; x < be; ++x)
         if (x < scap) pool[sg + x] = ~0ull;               // unused slots of the last block
-    if (nreal) atomicAdd(&ureal[lr], nreal);
     __syncthreads();
-    if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg && ucnt[tid] > seg_slots(rs[tid].ucount)) {
-        // U overflowed the segment: the radix levels take the row
-        st[(size_t)(t0 + tid) * g.n_ret + r].seg = kNoSeg;
-    } else if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg) {
-        const CState& c = rs[tid];
-        CRow out;
-        out.mp = c.mp;
-        out.delta = c.delta;
-        out.e_thr = c.e_thr;
-        out.T = 0.0f;
-        out.d_edge = c.edge;
-        out.mode = kBuf;
-        out.u_end = c.uend;
-        out.n_tie = 0;
-        out.count = (int)ucnt[tid];
-        // P3 finds more keys in U than P2's bound
-        out.bad = ureal[tid] > c.ucount ? 1 : 0;
-        out.target = 0ull;
-        out.seg = c.seg;
-        out.light = c.light;
-        rows_out[(size_t)(t0 + tid) * g.n_ret + r] = out;
+    // the part's unreserved tail; a part that overflowed sends the row to the
+    // radix levels (exact counts: a safeguard)
+    for (int row = 0; row < n_valid; ++row) {
+        if (rs[row].mode != kLevel || rs[row].seg == kNoSeg) continue;
+        for (uint32_t x = ucnt[row] + tid; x < ucap[row]; x += 256) pool[ubase[row] + x] = ~0ull;
     }
+    if (tid < n_valid && rs[tid].mode == kLevel && rs[tid].seg != kNoSeg && ucnt[tid] > ucap[tid])
+        st[(size_t)(t0 + tid) * g.n_ret + r].seg = kNoSeg;
 }
 
 // ---------------------------------------------------------------------------
@@ -1774,9 +1840,17 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, tflags, hacc, arrive, ctr, pool, head;
-    int nblk, nfw;
+    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, ctr, pool, head;
+    int nblk, nfw, nsplit;
 };
+
+// key-tile runs per row tile of the histogram and recording passes: about six
+// waves of workgroups over the chip (four per CU), but runs of at least ~1024
+// key tiles (each workgroup's fixed cost: q_low, LDS clears, the merge)
+int hist_splits(int n_tok, int n_ret, int n_keys) {
+    const int nwg = (n_tok + kTR - 1) / kTR * n_ret, max_tiles = (n_keys + 31) / 32;
+    return std::max(1, std::min({kMaxSplit, (6144 + nwg - 1) / nwg, max_tiles / 1024}));
+}
 
 ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -1790,8 +1864,11 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.nfw = (n_keys + 1023) / 1024;                     // one bit per 32-key tile
     w.tflags = w.knorm + up((size_t)n_ret * w.nblk * 4);
     const size_t nrt = (size_t)((rows / n_ret + kTR - 1) / kTR) * n_ret;   // row tiles
+    w.nsplit = hist_splits(rows / n_ret, n_ret, n_keys);
     w.hacc = w.tflags + up(nrt * (w.nfw + 1) * 4);
-    w.arrive = w.hacc + up((size_t)rows * kHB * 8);
+    w.hcnt = w.hacc + up((size_t)rows * kHB * 8);
+    w.segoff = w.hcnt + up((size_t)rows * w.nsplit * kProv * 4);
+    w.arrive = w.segoff + up((size_t)rows * w.nsplit * 4);
     w.ctr = w.arrive + up(nrt * 4);
     w.pool = w.ctr + 256;
     w.head = w.pool;
@@ -1823,27 +1900,23 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     unsigned long long* pool = (unsigned long long*)(base + w.pool);
     const unsigned long long pool_cap = (ws_bytes - w.head) / 8;
     const dim3 grid((g.n_tok + kTR - 1) / kTR, g.n_ret);
-    // key-tile runs per row tile of the histogram pass: about six waves of
-    // workgroups over the chip (four per CU), but runs of at least ~1024 key
-    // tiles (each workgroup's fixed cost: q_low, LDS clears, the merge)
     HistAcc acc;
     acc.hist = (double*)(base + w.hacc);
+    acc.cnt = (uint32_t*)(base + w.hcnt);
+    acc.segoff = (uint32_t*)(base + w.segoff);
     acc.tflags = tflags;
     acc.arrive = (uint32_t*)(base + w.arrive);
     acc.nt32 = (int)grid.x;
     acc.nfw = w.nfw;
-    {
-        const int nwg = (int)(grid.x * grid.y), max_tiles = (n_keys + 31) / 32;
-        acc.nsplit = std::max(1, std::min({8, (6144 + nwg - 1) / nwg, max_tiles / 1024}));
-    }
+    acc.nsplit = w.nsplit;
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
                        (const bf16_t*)w_q, (const bf16_t*)k_low, qlow, knorm, w.nblk, cst, acc);
     hipLaunchKernelGGL(k_csel_hist, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, top_p,
-                       qlow, cst, ctr, pool_cap, acc);
-    hipLaunchKernelGGL(k_csel_rec, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, qlow, cst, crow, pool, tflags,
-                       w.nfw);
+                       qlow, cst, ctr, pool_cap, acc, crow);
+    hipLaunchKernelGGL(k_csel_rec, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, qlow,
+                       cst, pool, acc);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
     hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, (const bf16_t*)k_low, qlow, top_p,
                        pool, counts);
