@@ -59,11 +59,11 @@ constexpr int kNBP = kNB + 1;
 constexpr int kCapC = 128;       // candidates of one cut bucket sorted in LDS
 constexpr int kSmallU = 8192;    // U sorted by the per-row resolve kernel
 constexpr int kTinyU = 1024;     // U sorted by the small-row resolve kernel
-constexpr int kSegBlk = 8;       // segment slots reserved at a time by one lane of the third pass
+constexpr int kSegBlk = 4;       // segment slots reserved at a time by one lane of the third pass
 constexpr int kSegPad = 8 * kSegBlk;   // 8 writers per row and run (4 waves x 2 halves): their last blocks' slack
 // largest segment (U plus each run's padding), sorted by the large-row kernel:
-// U of up to 16384 keys at the most runs (a multiple of its 512 threads)
-constexpr int kSegMax = 16384 + 8 * kSegPad;
+// U of up to 16384 keys at the most runs, a multiple of its 512 threads
+constexpr int kSegMax = 16384 + 512;
 constexpr int kPoolPerRow = 4096;   // pool entries per row in the recommended workspace
 constexpr int kNormKeys = 4096;  // keys per block of the key-norm pre-pass
 constexpr float kLog2eF = 1.4426950408889634f;
@@ -263,6 +263,7 @@ __device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (
 // accumulators (zeroed by P1), and the last workgroup of a row tile to
 // arrive takes the epilogue.
 constexpr int kMaxSplit = 8;     // most runs of key tiles per row tile
+static_assert(kSegMax >= 16384 + kMaxSplit * kSegPad, "a segment holds U of 16384 keys at the most runs");
 
 struct HistAcc {
     double* hist;        // [rows][kHB], rows in result-record order
@@ -1153,6 +1154,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
                             unsigned long long* sk, unsigned long long* scan_sh, ResolveSmem<1 << RBITS>& sm) {
     constexpr int kRB = 1 << RBITS;                      // radix buckets per level
     constexpr int PER = CAP / NT;
+    static_assert(CAP % NT == 0, "whole slots per thread");
     const int tid = threadIdx.x, lane = tid & 63;
     const int slots = cr.count;
     const float s = g.idx_scale;
