@@ -271,6 +271,8 @@ struct HistAcc {
     uint32_t* segoff;    // [rows][nsplit]: slot of each run's part of the row's segment
     uint32_t* tflags;    // [n_ret][nt32][nfw + 1]
     uint32_t* arrive;    // [n_ret][nt32]
+    uint32_t* lrows;     // result records of the rows with U > kSmallU (the large-row resolve's list)
+    unsigned long long* lctr;   // [0]: entries of lrows; [1]: the large-row resolve's next entry
     int nt32, nfw, nsplit;
 };
 
@@ -653,6 +655,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         out.seg = r_seg[tid];
         out.light = c->light;
         rows_out[rg] = out;
+        if (out.count > kSmallU) acc.lrows[atomicAdd(&acc.lctr[0], 1ull)] = (uint32_t)rg;
     }
     // whether the row tile's key-tile flags suffice (last word)
     if (tid == 0) tf[nfw] = (uint32_t)s_full;
@@ -1624,10 +1627,14 @@ __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* 
     resolve_row<kTinyU, kRTS, kRBitsS>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
 }
 
-// Rows with U in (kSmallU, kSegMax]: a fixed grid of 512-thread workgroups
-// walks the rows.
+// Rows with U in (kSmallU, kSegMax]: one 512-thread workgroup per CU takes
+// the rows the histogram pass listed, one at a time from a shared counter
+// (rows differ several-fold in cost, so a fixed assignment leaves CUs idle).
+// A listed row that the recording pass sent to the radix levels is skipped.
 constexpr int kRTL = 512;      // threads of the large-row resolve (two waves per SIMD: room for its registers)
 __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* __restrict__ rows, int n_rows,
+                                                             const uint32_t* __restrict__ lrows,
+                                                             unsigned long long* __restrict__ lctr,
                                                              const bf16_t* __restrict__ k_low,
                                                              const uint16_t* __restrict__ qlow,
                                                              const float* __restrict__ top_p,
@@ -1636,7 +1643,15 @@ __global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* 
     __shared__ unsigned long long sk[kSegMax + kSegMax / 128];
     __shared__ unsigned long long scan_sh[kRTL / 64 + 1];
     __shared__ ResolveSmem<1 << kRBits> sm;
-    for (int row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    __shared__ unsigned long long s_next;
+    const unsigned long long n_list = min(lctr[0], (unsigned long long)n_rows);
+    for (;;) {
+        __syncthreads();                                 // every thread has read the previous entry number
+        if (threadIdx.x == 0) s_next = atomicAdd(&lctr[1], 1ull);
+        __syncthreads();
+        const unsigned long long e = s_next;
+        if (e >= n_list) break;
+        const int row = (int)lrows[e];
         const CRow cr = rows[row];
         if (cr.mode != kBuf || cr.count <= kSmallU) continue;
         if (cr.bad) {
@@ -1812,13 +1827,14 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
 }
 
 // Largest squared indexer-key norm of each block of kNormKeys keys of the
-// chunk's sequence, per retrieval head, and the pool counter reset.
+// chunk's sequence, per retrieval head, and the resets of the pool counter and
+// the large-row list.
 // grid (nblk, n_ret), 256 threads.
 __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restrict__ k_low, int n_keys,
                                                     float* __restrict__ knorm, int nblk,
                                                     unsigned long long* __restrict__ pool_ctr) {
     const int r = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
-    if (blk == 0 && r == 0 && tid == 0) *pool_ctr = 0ull;
+    if (blk == 0 && r == 0 && tid < 3) pool_ctr[tid] = 0ull;   // pool, large-row list, its queue
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     float kn = 0.0f;
     for (int i = tid; i < kNormKeys; i += 256) {
@@ -1842,7 +1858,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, ctr, pool, head;
+    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, ctr, pool, head;
     int nblk, nfw, nsplit;
 };
 
@@ -1871,7 +1887,8 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.hcnt = w.hacc + up((size_t)rows * kHB * 8);
     w.segoff = w.hcnt + up((size_t)rows * w.nsplit * kProv * 4);
     w.arrive = w.segoff + up((size_t)rows * w.nsplit * 4);
-    w.ctr = w.arrive + up(nrt * 4);
+    w.lrows = w.arrive + up(nrt * 4);
+    w.ctr = w.lrows + up((size_t)rows * 4);
     w.pool = w.ctr + 256;
     w.head = w.pool;
     return w;
@@ -1911,6 +1928,8 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     acc.nt32 = (int)grid.x;
     acc.nfw = w.nfw;
     acc.nsplit = w.nsplit;
+    acc.lrows = (uint32_t*)(base + w.lrows);
+    acc.lctr = ctr + 1;
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
@@ -1924,8 +1943,8 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
                        pool, counts);
     hipLaunchKernelGGL(k_csel_resolve_small, dim3(rows), dim3(kRTS), 0, s, g, crow, (const bf16_t*)k_low, qlow,
                        top_p, pool, counts);
-    hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 512)), dim3(kRTL), 0, s, g, crow, rows,
-                       (const bf16_t*)k_low, qlow, top_p, pool, counts);
+    hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 256)), dim3(kRTL), 0, s, g, crow, rows, acc.lrows,
+                       acc.lctr, (const bf16_t*)k_low, qlow, top_p, pool, counts);
     hipLaunchKernelGGL(k_csel_rowptr, dim3(1), dim3(1024), 0, s, counts, rows, out.row_ptr, out.capacity,
                        out.status);
     hipLaunchKernelGGL(k_csel_copy, dim3(rows), dim3(256), 0, s, crow, pool, out.row_ptr, out.idx, out.status);
