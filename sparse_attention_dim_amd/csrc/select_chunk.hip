@@ -272,7 +272,8 @@ struct HistAcc {
     uint32_t* tflags;    // [n_ret][nt32][nfw + 1]
     uint32_t* arrive;    // [n_ret][nt32]
     uint32_t* lrows;     // result records of the rows with U > kSmallU (the large-row resolve's list)
-    unsigned long long* lctr;   // [0]: entries of lrows; [1]: the large-row resolve's next entry
+    uint32_t* mrows;     // result records of the rows with kTinyU < U <= kSmallU (the per-row resolve's list)
+    unsigned long long* lctr;   // [0], [1]: entries of lrows and the next one taken; [2], [3]: the same of mrows
     int nt32, nfw, nsplit;
 };
 
@@ -655,7 +656,10 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         out.seg = r_seg[tid];
         out.light = c->light;
         rows_out[rg] = out;
-        if (out.count > kSmallU) acc.lrows[atomicAdd(&acc.lctr[0], 1ull)] = (uint32_t)rg;
+        if (out.count > kSmallU)
+            acc.lrows[atomicAdd(&acc.lctr[0], 1ull)] = (uint32_t)rg;
+        else if (out.count > kTinyU)
+            acc.mrows[atomicAdd(&acc.lctr[2], 1ull)] = (uint32_t)rg;
     }
     // whether the row tile's key-tile flags suffice (last word)
     if (tid == 0) tf[nfw] = (uint32_t)s_full;
@@ -1578,38 +1582,40 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     __syncthreads();
 }
 
-// Rows with U up to kSmallU in a segment, and the counts of the rows that have
-// no segment.  grid (rows), 512 threads.
+// Rows with U in (kTinyU, kSmallU]: two 512-thread workgroups per CU (their
+// LDS fills it) take the rows the histogram pass listed from a shared
+// counter, so no LDS is held by workgroups of rows that are not theirs.
 constexpr int kRT = 512;
-__global__ __launch_bounds__(kRT) void k_csel_resolve(Geo g, const CRow* __restrict__ rows,
+__global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(4)))   // two workgroups per CU
+void k_csel_resolve(Geo g, const CRow* __restrict__ rows, int n_rows,
+                                                      const uint32_t* __restrict__ mrows,
+                                                      unsigned long long* __restrict__ mctr,
                                                       const bf16_t* __restrict__ k_low,
                                                       const uint16_t* __restrict__ qlow,
                                                       const float* __restrict__ top_p,
                                                       unsigned long long* __restrict__ pool,
                                                       int* __restrict__ counts) {
-    const int row = blockIdx.x;
-    const CRow cr = rows[row];
-    if (cr.mode != kBuf) {
-        if (threadIdx.x == 0) {
-            const int L = g.pos0 + row / g.n_ret + 1;
-            counts[row] = cr.bad ? -1 : (cr.mode == kAll ? L : cr.count);
-        }
-        return;
-    }
-    if (cr.count > kSmallU) return;
-    if (cr.bad) {
-        if (threadIdx.x == 0) counts[row] = -1;
-        return;
-    }
-    if (cr.count <= kTinyU) return;                     // the small-row kernel's
     __shared__ unsigned long long sk[kSmallU + kSmallU / 128];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
     __shared__ ResolveSmem<1 << kRBits> sm;
-    resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+    __shared__ unsigned long long s_next;
+    const unsigned long long n_list = min(mctr[0], (unsigned long long)n_rows);
+    for (;;) {
+        __syncthreads();                                 // every thread has read the previous entry number
+        if (threadIdx.x == 0) s_next = atomicAdd(&mctr[1], 1ull);
+        __syncthreads();
+        const unsigned long long e = s_next;
+        if (e >= n_list) break;
+        const int row = (int)mrows[e];
+        const CRow cr = rows[row];
+        if (cr.mode != kBuf || cr.bad || cr.count <= kTinyU || cr.count > kSmallU) continue;
+        resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+    }
 }
 
 // Rows with U of at most kTinyU keys: the same resolve on 128 threads with
-// 256-bucket radix levels (12 KB of LDS), so that many rows share a CU.
+// 256-bucket radix levels (12 KB of LDS), so that many rows share a CU; and
+// the counts of the rows that have no segment.  grid (rows).
 constexpr int kRTS = 128;
 constexpr int kRBitsS = 8;
 __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* __restrict__ rows,
@@ -1620,7 +1626,18 @@ __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* 
                                                              int* __restrict__ counts) {
     const int row = blockIdx.x;
     const CRow cr = rows[row];
-    if (cr.mode != kBuf || cr.bad || cr.count > kTinyU) return;
+    if (cr.mode != kBuf) {
+        if (threadIdx.x == 0) {
+            const int L = g.pos0 + row / g.n_ret + 1;
+            counts[row] = cr.bad ? -1 : (cr.mode == kAll ? L : cr.count);
+        }
+        return;
+    }
+    if (cr.bad) {
+        if (threadIdx.x == 0) counts[row] = -1;
+        return;
+    }
+    if (cr.count > kTinyU) return;
     __shared__ unsigned long long sk[kTinyU + kTinyU / 128];
     __shared__ unsigned long long scan_sh[kRTS / 64 + 1];
     __shared__ ResolveSmem<1 << kRBitsS> sm;
@@ -1834,7 +1851,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
                                                     float* __restrict__ knorm, int nblk,
                                                     unsigned long long* __restrict__ pool_ctr) {
     const int r = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
-    if (blk == 0 && r == 0 && tid < 3) pool_ctr[tid] = 0ull;   // pool, large-row list, its queue
+    if (blk == 0 && r == 0 && tid < 5) pool_ctr[tid] = 0ull;   // pool; the large- and per-row lists, their queues
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     float kn = 0.0f;
     for (int i = tid; i < kNormKeys; i += 256) {
@@ -1858,7 +1875,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, ctr, pool, head;
+    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, mrows, ctr, pool, head;
     int nblk, nfw, nsplit;
 };
 
@@ -1888,7 +1905,8 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.segoff = w.hcnt + up((size_t)rows * w.nsplit * kProv * 4);
     w.arrive = w.segoff + up((size_t)rows * w.nsplit * 4);
     w.lrows = w.arrive + up(nrt * 4);
-    w.ctr = w.lrows + up((size_t)rows * 4);
+    w.mrows = w.lrows + up((size_t)rows * 4);
+    w.ctr = w.mrows + up((size_t)rows * 4);
     w.pool = w.ctr + 256;
     w.head = w.pool;
     return w;
@@ -1929,6 +1947,7 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     acc.nfw = w.nfw;
     acc.nsplit = w.nsplit;
     acc.lrows = (uint32_t*)(base + w.lrows);
+    acc.mrows = (uint32_t*)(base + w.mrows);
     acc.lctr = ctr + 1;
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
@@ -1939,8 +1958,8 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     hipLaunchKernelGGL(k_csel_rec, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, qlow,
                        cst, pool, acc);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
-    hipLaunchKernelGGL(k_csel_resolve, dim3(rows), dim3(kRT), 0, s, g, crow, (const bf16_t*)k_low, qlow, top_p,
-                       pool, counts);
+    hipLaunchKernelGGL(k_csel_resolve, dim3(std::min(rows, 512)), dim3(kRT), 0, s, g, crow, rows, acc.mrows,
+                       acc.lctr + 2, (const bf16_t*)k_low, qlow, top_p, pool, counts);
     hipLaunchKernelGGL(k_csel_resolve_small, dim3(rows), dim3(kRTS), 0, s, g, crow, (const bf16_t*)k_low, qlow,
                        top_p, pool, counts);
     hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 256)), dim3(kRTL), 0, s, g, crow, rows, acc.lrows,
