@@ -60,6 +60,8 @@ def lib():
             L.orc_scores.restype = ctypes.c_int
             L.orc_topp.argtypes = [P, i64, f64, f32, P, P, P]
             L.orc_topp.restype = i64
+            L.orc_topk.argtypes = [P, i64, i64, P]
+            L.orc_topk.restype = i64
             L.orc_attend.argtypes = [P, P, P, i64, i32, P, i64, f64, P]
             L.orc_attend.restype = None
             L.orc_window_set.argtypes = [i64, i64, i64, P]
@@ -123,6 +125,18 @@ def topp(d: np.ndarray, s: float, p: float, want_order: bool = True):
     return sel[:k].copy(), order, cum
 
 
+def topk(d: np.ndarray, k: int) -> np.ndarray:
+    """Selected ascending int32: the first min(k, L) keys of the rank order
+    (score descending, index ascending)."""
+    d = np.ascontiguousarray(d, np.float32)
+    L = d.shape[0]
+    sel = np.empty(L, np.int32)
+    n = lib().orc_topk(_p(d), L, int(k), _p(sel))
+    if n < 0:
+        raise ValueError("top-k needs L >= 1 and k >= 1")
+    return sel[:n].copy()
+
+
 def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
            scale: float) -> np.ndarray:
     """double [D]: softmax(scale q.k_j) over idx, weighted sum of v_j.
@@ -159,18 +173,26 @@ def f32_to_bf16(x: float) -> int:
 def retrieval_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, Wq: np.ndarray,
                   Wk: np.ndarray, pos: int, idx_scale: float, p: float,
                   attn_scale: float, k_low: np.ndarray | None = None,
-                  want_order: bool = True) -> dict:
+                  want_order: bool = True, top_k: int = 0, k_max: int = 0) -> dict:
     """One retrieval-head query row at position pos (keys 0..pos).
 
     q: [D]; K, V: [>= pos+1, D] of this row's KV head; Wq, Wk: [D, 16].
     k_low may be passed when it is already known for the whole context.
+    top_k > 0: fixed top-k selection instead of top-p (p is then unused).
+    k_max > 0: the top-p set is capped at its first k_max keys in rank order.
     """
     L = pos + 1
     q_low = project(np.asarray(q).reshape(1, -1), Wq)[0]
     if k_low is None:
         k_low = project(np.asarray(K)[:L], Wk)
     d = scores(q_low, k_low[:L])
-    sel, order, cum = topp(d, idx_scale, p, want_order)
+    if top_k > 0:
+        sel = topk(d, top_k)
+        _, order, cum = topp(d, idx_scale, 1.0, want_order) if want_order else (None, None, None)
+    else:
+        sel, order, cum = topp(d, idx_scale, p, want_order)
+        if k_max > 0 and len(sel) > k_max:
+            sel = topk(d, k_max)
     out = attend(q, np.asarray(K)[:L], np.asarray(V)[:L], sel, attn_scale)
     return dict(q_low=q_low, k_low=k_low, d=d, sel=sel, order=order, cum=cum, out=out)
 

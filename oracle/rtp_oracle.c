@@ -202,6 +202,36 @@ int64_t orc_topp(const float *d, int64_t L, double s, float p,
     return kstar;
 }
 
+/*
+ * Fixed top-k selection over the scores d[0..L-1]: the fixed-budget rule
+ * that the method's dynamic top-p replaces (abstract, observation (3); forum
+ * post, "Three Key Insights" item 3), also used to cap a top-p set at a
+ * budget of k keys.  The selected set is the first min(k, L) keys of the rank
+ * order (d descending, then j ascending; -0 equals +0), written ascending
+ * into sel.  Returns its size, or -1 for L < 1 or k < 1.
+ */
+int64_t orc_topk(const float *d, int64_t L, int64_t k, int32_t *sel)
+{
+    if (L < 1 || k < 1)
+        return -1;
+    ranked *sig = (ranked *)malloc(sizeof(ranked) * (size_t)L);
+    for (int64_t j = 0; j < L; j++) {
+        sig[j].d = d[j];
+        sig[j].j = j;
+    }
+    qsort(sig, (size_t)L, sizeof(ranked), rank_cmp);
+    int64_t n = k < L ? k : L;
+    char *take = (char *)calloc((size_t)L, 1);
+    for (int64_t i = 0; i < n; i++)
+        take[sig[i].j] = 1;
+    int64_t c = 0;
+    for (int64_t j = 0; j < L; j++)
+        if (take[j]) sel[c++] = (int32_t)j;
+    free(take);
+    free(sig);
+    return n;
+}
+
 /* ------------------------------------------------------------------ */
 /* Steps 6-8: exact softmax attention over an index set                */
 /* ------------------------------------------------------------------ */

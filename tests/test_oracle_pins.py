@@ -247,6 +247,73 @@ def test_topp_negative_zero_equals_positive_zero():
     assert list(order[:2]) == [0, 1] and list(sel) == [0]
 
 
+# --------------------------------------------------------------------------
+# fixed top-k (the budget rule top-p replaces) and the top-p budget cap
+# --------------------------------------------------------------------------
+
+def _outranks(d, a, b):
+    """key a ranks before key b: higher score, or equal score and lower index."""
+    return d[a] > d[b] or (d[a] == d[b] and a < b)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_topk_brute_force_tiny(seed):
+    # every k-subset is enumerated; exactly one has no outside key ranking
+    # before an inside key, and the oracle must return it.  Integer scores
+    # with frequent ties (and signed zeros) exercise the index tie-break.
+    g = np.random.default_rng(100 + seed)
+    n = int(g.integers(1, 10))
+    d = g.integers(-2, 3, n).astype(np.float32)
+    d[d == 0] = np.where(g.integers(0, 2, int((d == 0).sum())) == 1, -0.0, 0.0)
+    for k in range(1, n + 2):
+        good = [sub for sub in itertools.combinations(range(n), min(k, n))
+                if not any(_outranks(d, j, i) for i in sub for j in range(n) if j not in sub)]
+        assert len(good) == 1
+        assert tuple(oracle.topk(d, k)) == good[0]
+
+
+def test_topk_equals_topp_at_the_same_size_and_nests():
+    w = synth.small(5)
+    t, r = 2, 0
+    h = w.ret_heads[r]
+    g = w.kv_head(h)
+    res = oracle.retrieval_row(w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], w.w_q[r], w.w_k[r],
+                               w.row_pos(t), w.idx_scale, 0.9, w.attn_scale)
+    d = res["d"]
+    prev = []
+    for p in (1e-7, 0.5, 0.9, 0.99, 0.9999):
+        sel, _, _ = oracle.topp(d, w.idx_scale, p)
+        # the minimal top-p set is the top-k set of its own size
+        np.testing.assert_array_equal(oracle.topk(d, len(sel)), sel)
+    for k in (1, 2, 7, 64, len(d) - 1, len(d), len(d) + 5):
+        s = oracle.topk(d, k)
+        assert len(s) == min(k, len(d))
+        assert set(prev) <= set(s)                    # nesting in k
+        prev = list(s)
+    assert list(oracle.topk(d, 1)) == [int(np.flatnonzero(d == d.max())[0])]
+    with pytest.raises(ValueError):
+        oracle.topk(d, 0)
+
+
+def test_topp_cap_keeps_the_first_k_max_of_the_rank_order():
+    w = synth.small(5)
+    t, r = 3, 1
+    h = w.ret_heads[r]
+    g = w.kv_head(h)
+    args = (w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], w.w_q[r], w.w_k[r], w.row_pos(t), w.idx_scale,
+            0.99, w.attn_scale)
+    full = oracle.retrieval_row(*args)
+    n = len(full["sel"])
+    assert n > 8
+    for kmax in (1, 5, n - 1, n, n + 10):
+        cap = oracle.retrieval_row(*args, k_max=kmax)
+        want = sorted(full["order"][:min(n, kmax)])
+        np.testing.assert_array_equal(cap["sel"], want)
+    # top_k overrides p: the same set whatever p is
+    a = oracle.retrieval_row(*args, top_k=9)["sel"]
+    np.testing.assert_array_equal(a, sorted(full["order"][:9]))
+
+
 def test_identity_projection_ranks_like_full_attention():
     # D = 16 and W = I: the indexer sees q and k themselves.  With
     # idx_scale = attn_scale = 1/4 its top-p set must be the top-p set of the
