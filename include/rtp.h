@@ -51,10 +51,17 @@
 extern "C" {
 #endif
 
-#define RTP_VERSION 1
+#define RTP_VERSION 2
 #define RTP_IDX_DIM 16      /* indexer width (the pages' 16-dimensional indexer) */
 #define RTP_BLOCK 256       /* tokens per KV page */
 #define RTP_MAX_RET 64      /* most retrieval heads per layer */
+#define RTP_MAX_LEN (1 << 20) /* longest context: the exact 2^-43 fixed-point mass sums hold 2^20 keys
+                               (each weight <= 1, so a row's total stays below 2^63) */
+
+/* rtp_layer.flags */
+#define RTP_FLAG_EXACT_MASS 1  /* bf16 chunk selection: sum the indexer-softmax normaliser exactly over
+                                  every key of every row (an extra pass over the indexer keys of each
+                                  row; the selected sets are those of the default, certified route) */
 
 typedef enum {
     RTP_OK = 0,
@@ -83,6 +90,9 @@ typedef struct rtp_layer {
     int32_t num_sinks;              /* local heads: plus positions 0..num_sinks-1, >= 0 */
     float attn_scale;               /* softmax scale of attention, e.g. 1/sqrt(D) */
     float idx_scale;                /* softmax scale of the indexer, e.g. 1/sqrt(16) */
+    int32_t k_max;                  /* top-p budget cap: a row keeps at most the first k_max keys of its
+                                       rank order (a bound on the CSR capacity); 0 = no cap */
+    int32_t flags;                  /* RTP_FLAG_* */
 } rtp_layer;
 
 /* [host] struct of device pointers: the paged KV cache of a batch. */
@@ -94,8 +104,8 @@ typedef struct rtp_cache {
     const int32_t *seq_lens;        /* [batch] tokens in the cache, incl. those appended this step */
     int32_t batch;
     int32_t max_blocks;             /* row stride of block_table */
-    int32_t max_seq_len;            /* [host] upper bound of every seq_lens[b], at most 2^20 (the exact
-                                       fixed-point mass sums hold 2^20 keys); sizes grids and workspaces */
+    int32_t max_seq_len;            /* [host] upper bound of every seq_lens[b], at most RTP_MAX_LEN;
+                                       sizes grids and workspaces */
 } rtp_cache;
 
 /* [host] struct: the query rows of one call. */
@@ -114,7 +124,8 @@ typedef struct rtp_sel {
     int64_t capacity;               /* [host] entries available in idx */
     int32_t *status;                /* one int: 0 = ok, 1 = capacity overflow (then idx is not written
                                        and row_ptr[rows] holds the capacity needed), 2 = selection not
-                                       certified (nothing written) */
+                                       certified (nothing written), 3 = a top_p value is NaN or <= 0
+                                       (nothing written) */
 } rtp_sel;
 
 /* Library version (RTP_VERSION). */
@@ -124,12 +135,18 @@ int rtp_version(void);
 const char *rtp_last_error(void);
 
 /*
- * a1. Indexer key append (the indexer key cache is written when K is appended).
- * For i < n and every retrieval head r with KV head g = ret_heads[r]/(Hq/Hkv):
+ * a1. Indexer key append: the 16-dimensional indexer key of every retrieval
+ * head, written when a token's K enters the cache (abstract, observation (2):
+ * a lightweight 16-dimensional token indexer replaces full-rank similarity;
+ * forum post, "Three Key Insights" item 2: the projection is built on the
+ * low-frequency RoPE dimensions).  For i < n and every retrieval head r with
+ * KV head g = ret_heads[r]/(Hq/Hkv):
  *   k_low[page(seq_id[i], pos[i])][r][slot][c] =
  *       bf16_rne( fp32 FMA chain over d = 0..D-1 from +0 of K[seq_id[i], pos[i], g, d] * w_k[r][d][c] )
- * K is read from the cache, so the token's K must already be stored there.
- * seq_id, pos: device int32[n].  n == 0 is a no-op.
+ * K is read from the cache, so the token's K must already be stored there
+ * (rtp_kv_append stores K and V and writes k_low in one launch).
+ * seq_id, pos: device int32[n] (pos[i] < max_seq_len; not checked on the
+ * device).  n == 0 is a no-op.  Errors: RTP_EINVAL for NULL pointers or n < 0.
  */
 rtp_status rtp_indexer_append(const rtp_layer *layer, const rtp_cache *cache, const void *w_k,
                               const int32_t *seq_id, const int32_t *pos, int32_t n, void *stream);
@@ -152,15 +169,20 @@ size_t rtp_topp_select_workspace_min(const rtp_layer *layer, const rtp_cache *ca
  *   w_j   = exp(idx_scale * (d_j - max d)),  Z = sum w_j
  *   the selected set is the shortest prefix of keys ranked by (d_j descending,
  *   j ascending) whose mass reaches top_p[seq] * Z (all keys if top_p >= 1),
- *   written ascending.  Scores and the ranking are exact (bit for bit the
- *   fixed-order fp32 chain); masses use fp32 exp with an exact argument and
- *   are summed exactly in 2^-43 fixed point, so the set can differ from an
- *   exact-arithmetic one only where a cumulative mass lies within 1e-6 of p.
- * top_p: device float[batch], each in (0, 1] (device values are not checked).
- * On overflow (total > sel->capacity) *status = 1, row_ptr is complete and
- * idx is untouched.  *status = 2 means the chunk selection could not certify
- * a row's cut (an internal error bound was violated): nothing is written and
- * row_ptr is not meaningful.
+ *   cut to its first layer->k_max keys when k_max > 0, written ascending.
+ *   Scores and the ranking are exact (bit for bit the fixed-order fp32
+ *   chain); masses use fp32 exp with an exact argument and are summed exactly
+ *   in 2^-43 fixed point.  The bf16 chunk path sums the mass of the keys far
+ *   from the cut from MFMA scores, bounds the error of that sum, and accepts
+ *   a cut only where the bound cannot move it past the band below; other rows
+ *   are cut again with the normaliser summed exactly over every key.  So on
+ *   every path the set can differ from an exact-arithmetic one only where a
+ *   cumulative mass lies within 1e-6 of p.
+ * top_p: device float[batch] in (0, 1]; a NaN or non-positive value sets
+ * *status = 3.  On overflow (total > sel->capacity) *status = 1, row_ptr is
+ * complete and idx is untouched.  *status = 2 means the chunk selection could
+ * not certify a row's cut (an internal error bound was violated): nothing is
+ * written and row_ptr is not meaningful.
  */
 rtp_status rtp_topp_select(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
                            const void *w_q, const float *top_p, const rtp_sel *sel,
@@ -188,13 +210,42 @@ rtp_status rtp_topp_select_end(const rtp_layer *layer, const rtp_cache *cache, c
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Fixed top-k selection: the fixed-budget rule that the method's dynamic
+ * top-p replaces (abstract, observation (3); forum post, "Three Key Insights"
+ * item 3).  Same arguments, scores, ranking, output and workspace as
+ * rtp_topp_select, with a host count k >= 1 instead of top_p: each row keeps
+ * the first min(k, pos + 1) keys of its rank order (d_j descending, j
+ * ascending), written ascending.  The set is exact (no mass band).  The cut
+ * runs through the same radix machinery with key counts in place of masses.
+ * layer->k_max is not used.
+ */
+rtp_status rtp_topk_select(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                           const void *w_q, int32_t k, const rtp_sel *sel,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Inspection: after rtp_topp_select or rtp_topk_select with the same layer,
+ * cache, query and workspace (and nothing else run on that workspace since),
+ * writes one code per row (int32 [n_tok*num_ret], device) telling how its set
+ * was formed: the low 4 bits name the route -- 1 every key, 2 / 3 / 4 the
+ * bf16 chunk path's candidate buffer of at most 1024 / 8192 / 16384 keys, 5
+ * the chunk path's radix levels over every key tile, 6 the decode path's
+ * candidate list, 7 the decode path's cut over the row's scores -- and the
+ * flags 16 (ordered through a bitmap) / 32 (ordered by merging runs), 64 (the
+ * normaliser summed exactly over every key), 128 (the cut counted keys: top-k
+ * or the k_max cap).  For the decode path and fp32 chunks only when every row
+ * fits one pass of the workspace (RTP_EUNSUPPORTED otherwise).
+ */
+rtp_status rtp_topp_select_paths(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                                 const void *workspace, size_t workspace_bytes, int32_t *paths, void *stream);
+
+/*
  * a2-a3 only, for inspection: q_low (bf16 [rows][16]) and the fp32 indexer
  * scores [rows][score_ld] (entries beyond a row's pos are not written).
- * score_ld >= max position + 1 of the call.
+ * score_ld >= max position + 1 of the call.  Needs no workspace.
  */
 rtp_status rtp_indexer_scores(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
-                              const void *w_q, uint16_t *q_low, float *scores, int64_t score_ld,
-                              void *workspace, size_t workspace_bytes, void *stream);
+                              const void *w_q, uint16_t *q_low, float *scores, int64_t score_ld, void *stream);
 
 /* Workspace bytes for rtp_sparse_attn_decode / _prefill given the CSR capacity. */
 size_t rtp_sparse_attn_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,

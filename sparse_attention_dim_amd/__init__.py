@@ -20,11 +20,19 @@ RTP_F32, RTP_BF16 = 0, 1
 RTP_DECODE, RTP_CHUNK = 0, 1
 RTP_BLOCK = 256
 RTP_MAX_RET = 64
+RTP_MAX_LEN = 1 << 20
+RTP_FLAG_EXACT_MASS = 1
+# selection status word
+SEL_OK, SEL_OVERFLOW, SEL_UNCERTIFIED, SEL_BAD_TOP_P = 0, 1, 2, 3
+# per-row path codes of rtp_topp_select_paths
+PATH_ALL, PATH_TINY, PATH_ROW, PATH_LARGE, PATH_LEVEL, PATH_LIST, PATH_SCAN = 1, 2, 3, 4, 5, 6, 7
+PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT = 16, 32, 64, 128
 
 ENTRY_POINTS = (
     "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_topp_select_workspace",
     "rtp_topp_select_workspace_min",
-    "rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end", "rtp_indexer_scores",
+    "rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end", "rtp_topk_select",
+    "rtp_topp_select_paths", "rtp_indexer_scores",
     "rtp_sparse_attn_workspace",
     "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_window_attn_workspace",
     "rtp_dense_attn_workspace", "rtp_window_attn", "rtp_dense_attn",
@@ -42,7 +50,8 @@ class Layer(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("num_ret", ctypes.c_int32), ("ret_heads", ctypes.c_int32 * RTP_MAX_RET),
                 ("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
-                ("attn_scale", ctypes.c_float), ("idx_scale", ctypes.c_float)]
+                ("attn_scale", ctypes.c_float), ("idx_scale", ctypes.c_float),
+                ("k_max", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -85,7 +94,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_topp_select": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
         "rtp_topp_select_begin": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
         "rtp_topp_select_end": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
-        "rtp_indexer_scores": ([pl, pc, pq, P, P, P, i64, P, S, P], ctypes.c_int),
+        "rtp_topk_select": ([pl, pc, pq, P, i32, ps, P, S, P], ctypes.c_int),
+        "rtp_topp_select_paths": ([pl, pc, pq, P, S, P, P], ctypes.c_int),
+        "rtp_indexer_scores": ([pl, pc, pq, P, P, P, i64, P], ctypes.c_int),
         "rtp_sparse_attn_workspace": ([pl, pc, pq, i64], S),
         "rtp_sparse_attn_decode": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
         "rtp_sparse_attn_prefill": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
@@ -151,7 +162,8 @@ def _stream(stream) -> int | None:
 
 
 def make_layer(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int, ret_heads,
-               window: int, num_sinks: int, attn_scale: float, idx_scale: float) -> Layer:
+               window: int, num_sinks: int, attn_scale: float, idx_scale: float, k_max: int = 0,
+               flags: int = 0) -> Layer:
     L = Layer()
     L.num_q_heads, L.num_kv_heads, L.head_dim, L.dtype = num_q_heads, num_kv_heads, head_dim, dtype
     rh = list(ret_heads)
@@ -160,6 +172,7 @@ def make_layer(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int, r
         L.ret_heads[i] = int(h)
     L.window, L.num_sinks = window, num_sinks
     L.attn_scale, L.idx_scale = attn_scale, idx_scale
+    L.k_max, L.flags = k_max, flags
     return L
 
 
@@ -223,9 +236,22 @@ def topp_select_end(layer, cache, query, w_q, top_p, sel, ws, stream=None, prepa
                 (layer, cache, query, sel), prepare)
 
 
+def topk_select(layer, cache, query, w_q, k: int, sel, ws, stream=None, prepare=False):
+    """Fixed top-k selection (same workspace as topp_select)."""
+    return _run("rtp_topk_select", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                                    int(k), ctypes.byref(sel), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
+
+
+def topp_select_paths(layer, cache, query, ws, paths, stream=None, prepare=False):
+    """Per-row path codes (int32 device tensor [rows]) of the last selection run on ws."""
+    return _run("rtp_topp_select_paths", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(ws),
+                                          _nbytes(ws), _ptr(paths), _stream(stream)), (layer, cache, query), prepare)
+
+
 def indexer_scores(layer, cache, query, w_q, q_low, scores, stream=None, prepare=False):
     return _run("rtp_indexer_scores", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
-                                       _ptr(q_low), _ptr(scores), scores.shape[1], None, 0, _stream(stream)),
+                                       _ptr(q_low), _ptr(scores), scores.shape[1], _stream(stream)),
                 (layer, cache, query), prepare)
 
 

@@ -38,7 +38,7 @@ rtp_status hip_status(hipError_t e, const char* what) {
     return ok();
 }
 
-constexpr int kMaxLen = 1 << 20;          // longest supported context: fixed-point masses of every key fit 2^63
+constexpr int kMaxLen = RTP_MAX_LEN;      // longest supported context: fixed-point masses of every key fit 2^63
 constexpr int kMaxDecodeRows = 4096;      // decode rows (batch * num_ret) of the sparse kernel
 constexpr int kWinSplit = 64;             // keys per workgroup, local-head decode (VALU kernel)
 constexpr int kWinSplitMfma = 128;        // keys per workgroup, local-head decode (bf16 MFMA kernel, D = 128)
@@ -72,6 +72,8 @@ rtp_status check_layer(const rtp_layer* L) {
     if (L->num_sinks < 0) return fail(RTP_EINVAL, "num_sinks %d < 0", L->num_sinks);
     if (!(L->attn_scale > 0.0f) || !std::isfinite(L->attn_scale)) return fail(RTP_EINVAL, "attn_scale");
     if (!(L->idx_scale > 0.0f) || !std::isfinite(L->idx_scale)) return fail(RTP_EINVAL, "idx_scale");
+    if (L->k_max < 0) return fail(RTP_EINVAL, "k_max %d < 0", L->k_max);
+    if (L->flags & ~RTP_FLAG_EXACT_MASS) return fail(RTP_EINVAL, "unknown flags 0x%x", L->flags);
     return RTP_OK;
 }
 
@@ -127,6 +129,9 @@ rtp::Geo make_geo(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
     g.sinks = L->num_sinks;
     g.attn_scale = L->attn_scale;
     g.idx_scale = L->idx_scale;
+    g.sel_k = 0;
+    g.k_max = L->k_max;
+    g.flags = L->flags;
     if (Q) {
         g.kind = Q->kind;
         g.seq = Q->seq;
@@ -290,16 +295,17 @@ size_t rtp_topp_select_workspace_min(const rtp_layer* layer, const rtp_cache* ca
 }
 
 // phase: 0 the whole selection, 1 the scoring pass of the first row group
-// (when every row fits one group), 2 the rest.
+// (when every row fits one group), 2 the rest.  top_k > 0: fixed top-k.
 static rtp_status topp_select_phase(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                                     const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
-                                    size_t workspace_bytes, void* stream, int phase) {
+                                    size_t workspace_bytes, void* stream, int phase, int top_k) {
     rtp_status s = check_all(layer, cache, query);
     if (s) return s;
-    if (!w_q || !top_p) return fail(RTP_EINVAL, "NULL w_q / top_p");
+    if (!w_q || (!top_p && top_k <= 0)) return fail(RTP_EINVAL, "NULL w_q / top_p");
     if (!sel || !sel->row_ptr || !sel->status || (sel->capacity > 0 && !sel->idx) || sel->capacity < 0)
         return fail(RTP_EINVAL, "bad selection buffers");
-    const rtp::Geo g = make_geo(layer, cache, query);
+    rtp::Geo g = make_geo(layer, cache, query);
+    g.sel_k = top_k;
     rtp::SelOut out{sel->row_ptr, sel->idx, sel->capacity, sel->status};
     if (tiled_select(layer, query)) {
         const size_t need = rtp::chunk_select_head_bytes(query->n_tok * layer->num_ret, layer->num_ret,
@@ -335,26 +341,48 @@ static rtp_status topp_select_phase(const rtp_layer* layer, const rtp_cache* cac
 rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                            const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
                            size_t workspace_bytes, void* stream) {
-    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 0);
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 0, 0);
+}
+
+rtp_status rtp_topk_select(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query, const void* w_q,
+                           int32_t k, const rtp_sel* sel, void* workspace, size_t workspace_bytes, void* stream) {
+    if (k < 1) return fail(RTP_EINVAL, "top-k k %d < 1", k);
+    return topp_select_phase(layer, cache, query, w_q, nullptr, sel, workspace, workspace_bytes, stream, 0, k);
+}
+
+rtp_status rtp_topp_select_paths(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                 const void* workspace, size_t workspace_bytes, int32_t* paths, void* stream) {
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    if (!workspace || !paths) return fail(RTP_EINVAL, "NULL workspace / paths");
+    const rtp::Geo g = make_geo(layer, cache, query);
+    if (tiled_select(layer, query)) {
+        const size_t need = rtp::chunk_select_head_bytes(query->n_tok * layer->num_ret, layer->num_ret,
+                                                         query->pos0 + query->n_tok);
+        if (workspace_bytes < need) return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+        return hip_status(rtp::launch_chunk_paths(g, workspace, paths, (hipStream_t)stream), "paths launch");
+    }
+    const SelPlan p = plan_select(layer, cache, query);
+    if (workspace_bytes < p.total) return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, p.total);
+    if (p.group_rows < p.rows_total) return fail(RTP_EUNSUPPORTED, "rows of the call span several workspace passes");
+    const rtp::SelWs w = sel_ws(p, (char*)workspace);
+    return hip_status(rtp::launch_select_paths(w, p.rows_total, paths, (hipStream_t)stream), "paths launch");
 }
 
 rtp_status rtp_topp_select_begin(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                                  const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
                                  size_t workspace_bytes, void* stream) {
-    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 1);
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 1, 0);
 }
 
 rtp_status rtp_topp_select_end(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                                const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 2);
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 2, 0);
 }
 
 rtp_status rtp_indexer_scores(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
-                              const void* w_q, uint16_t* q_low, float* scores, int64_t score_ld,
-                              void* workspace, size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
+                              const void* w_q, uint16_t* q_low, float* scores, int64_t score_ld, void* stream) {
     rtp_status s = check_all(layer, cache, query);
     if (s) return s;
     if (!w_q || !q_low || !scores) return fail(RTP_EINVAL, "NULL w_q / q_low / scores");

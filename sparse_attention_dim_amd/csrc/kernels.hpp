@@ -7,6 +7,21 @@
 namespace rtp {
 
 constexpr int kMaxRet = 64;
+constexpr int kFlagExactMass = 1; // RTP_FLAG_EXACT_MASS
+
+// How a row's selected set was formed (the per-row record that
+// rtp_topp_select_paths reports): low 4 bits the resolver, then flags.
+constexpr int kPathAll = 1;       // every key of the row
+constexpr int kPathTiny = 2;      // chunk path: candidate set of at most 1024 keys
+constexpr int kPathRow = 3;       // chunk path: at most 8192 keys (per-row resolve)
+constexpr int kPathLarge = 4;     // chunk path: at most 16384 keys (large-row resolve)
+constexpr int kPathLevel = 5;     // chunk path: radix levels over every key tile (no buffer)
+constexpr int kPathList = 6;      // decode path: candidate list cut in LDS
+constexpr int kPathScan = 7;      // decode path: cut over the row's scores
+constexpr int kPathBitmap = 16;   // chunk path: ordered through a bitmap of the kept range
+constexpr int kPathMerge = 32;    // chunk path: ordered by merging the writers' runs
+constexpr int kPathExactZ = 64;   // the normaliser was summed exactly over every key
+constexpr int kPathCount = 128;   // the cut counted keys (fixed top-k, or the budget cap)
 
 // Geometry of one call (host-filled, passed by value to kernels).
 struct Geo {
@@ -21,6 +36,9 @@ struct Geo {
     int max_seq_len;              // host bound; device lengths are clamped to [1, max_seq_len]
     int n_hlist;                  // heads computed by a prefill attention launch
     int hlist[256];
+    int sel_k;                    // selection: fixed top-k budget (0: top-p)
+    int k_max;                    // top-p budget cap (0: none)
+    int flags;                    // RTP_FLAG_* of the layer
     const int32_t* block_table;
     const int32_t* seq_lens;
 };
@@ -42,8 +60,10 @@ struct RowState {
     int32_t jT;
     int32_t L;                    // keys of the row
     int32_t count;                // selected keys
-    unsigned long long target;    // ceil(p Z), fixed point
+    unsigned long long target;    // ceil(p Z), fixed point (a key count when unit)
     float d_thr;                  // U = keys with score >= d_thr
+    int32_t unit;                 // the cut counts keys (fixed top-k, or the budget cap)
+    int32_t path;                 // kPath* code of the row
 };
 
 constexpr int kChunk = 4096;      // keys per workgroup of the scoring pass
@@ -89,6 +109,8 @@ enum SelStage {
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
                          int total_rows, int dtype, int stage, hipStream_t s);
+// Path codes (kPath*) of the rows of the last selection, from its workspace.
+hipError_t launch_select_paths(const SelWs& ws, int rows, int32_t* paths, hipStream_t s);
 
 // Selected keys per work item (one wavefront) of the sparse decode: a row of
 // n selected keys makes ceil(n / kSparseItem) partial results, so a call needs
@@ -115,6 +137,7 @@ size_t chunk_select_head_bytes(int rows, int n_ret, int n_keys);
 size_t chunk_select_ws_bytes(int rows, int n_ret, int n_keys);
 hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                                const float* top_p, void* ws, size_t ws_bytes, const SelOut& out, hipStream_t s);
+hipError_t launch_chunk_paths(const Geo& g, const void* ws, int32_t* paths, hipStream_t s);
 
 // Sparse attention of the retrieval heads of a prefill chunk (bf16, D = 128):
 // MFMA over the union of 64 consecutive rows' selected sets, masked per row.

@@ -255,8 +255,8 @@ struct Cut {
 
 __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* srow, int L, uint32_t klo,
                          uint32_t khi, unsigned long long S_hi, unsigned long long target, float m, float s,
-                         unsigned long long* hmb, uint32_t* hcb, unsigned long long* scan_sh, uint32_t* s_u,
-                         unsigned long long* s_S, int* s_i) {
+                         bool unit, unsigned long long* hmb, uint32_t* hcb, unsigned long long* scan_sh,
+                         uint32_t* s_u, unsigned long long* s_S, int* s_i) {
     const int tid = threadIdx.x;
     const bool from_list = n >= 0;
     const int cnt = from_list ? n : L;
@@ -282,11 +282,11 @@ __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* sro
             const uint32_t key = key_at(i, &j);
             if (key < klo || key > khi) continue;
             const uint32_t bk = (khi - key) >> shift;         // bucket 0 holds the highest keys
-            atomicAdd(&hmb[bk], weight_bin(key_score(key), m, s).w);
+            atomicAdd(&hmb[bk], unit ? 1ull : weight_bin(key_score(key), m, s).w);
             atomicAdd(&hcb[bk], 1u);
         }
         __syncthreads();
-        // first bucket (highest keys first) whose cumulative mass reaches target
+        // first bucket (highest keys first) whose cumulative mass (or count) reaches target
         unsigned long long loc = hmb[2 * tid] + hmb[2 * tid + 1];
         unsigned long long tot;
         const unsigned long long ex = S_hi + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
@@ -320,7 +320,7 @@ __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* sro
         S_hi = S_b;
         if (klo == khi) {
             // one score value: its tie group takes the lowest indices first
-            const unsigned long long wT = weight_bin(key_score(klo), m, s).w;
+            const unsigned long long wT = unit ? 1ull : weight_bin(key_score(klo), m, s).w;
             const unsigned long long need = target - S_hi;
             const uint32_t ntie = (uint32_t)min((need + wT - 1ull) / wT, (unsigned long long)n_b);
             Cut c;
@@ -376,9 +376,11 @@ __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* sro
 // of rounding per key) fixes U = {d >= m - X / s}.
 struct Plan {
     float m, d_thr;
-    unsigned long long target;
-    int all;                                          // p >= 1: every key
+    unsigned long long target;                        // mass, or a key count when unit
+    int all;                                          // every key (p >= 1, or a count >= L)
     int ks;                                           // X = ks / 4, or kGB if no grid point suffices
+    int unit;                                         // count cut: fixed top-k, or a capped keep-all row
+    int bad;                                          // top_p is NaN or <= 0
 };
 
 __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const float* __restrict__ top_p,
@@ -392,7 +394,9 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     // thread, nch <= 256) and p
     const uint32_t cm = tid < nch ? cmax[tid] : 0u;
     const unsigned long long ztot = tid < nch ? chist[(size_t)tid * kCB + kCB - 1] : 0ull;
-    const float p = top_p[ri.b];
+    const float p = g.sel_k > 0 ? 1.0f : top_p[ri.b];
+    // a count target: the fixed top-k budget, or the cap of a keep-all row
+    const int kc = g.sel_k > 0 ? g.sel_k : (!(p < 1.0f) && g.k_max > 0 ? g.k_max : 0);
     uint32_t mk = wave_max_u32(cm);
     if ((tid & 63) == 0) ured[tid >> 6] = mk;
     if (tid == 0) {
@@ -415,24 +419,31 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     if ((tid & 63) == 0) dred[tid >> 6] = z;
     __syncthreads();
     const double Z = dred[0] + dred[1] + dred[2] + dred[3];
-    pl.all = !(p < 1.0f);
+    pl.bad = g.sel_k <= 0 && !(p > 0.0f);
+    pl.unit = kc > 0;
+    pl.all = pl.bad || (kc > 0 ? kc >= ri.L : !(p < 1.0f));
     unsigned long long target = (unsigned long long)ceil((double)p * Z);
     if ((double)target > Z) target = (unsigned long long)Z;
     if (target < 1ull) target = 1ull;
-    pl.target = target;
+    pl.target = kc > 0 ? (unsigned long long)kc : target;
     pl.d_thr = -INFINITY;
     pl.ks = kGB;
     if (pl.all) return pl;
     // LB(k) is non-decreasing in k: first at the 16 points k = 16 i + 15, then
     // at the 16 values up to the first point that reaches.  16 lanes share one
-    // k (chunk bin b counts once (b + 1) / 4 + dc <= k / 4).
-    const double need = (double)target * (1.0 + 0x1.0p-40) + (double)ri.L + 1.0;
+    // k (chunk bin b counts once (b + 1) / 4 + dc <= k / 4).  A count cut
+    // bounds the number of keys the same way, from the cumulative counts.
+    const unsigned* ccnt = ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB;
+    const double need = pl.unit ? (double)pl.target : (double)target * (1.0 + 0x1.0p-40) + (double)ri.L + 1.0;
     const int grp = tid >> 4, sub = tid & 15;
     const auto lb_reaches = [&](int k) {
         double lb = 0.0;
         for (int c = sub; c < nch; c += 16) {
             const double bmax = floor((double)(k - 1) - (double)kCBPerUnit * dch[c]);
-            if (bmax >= 0.0) lb += fch[c] * (double)chist[(size_t)c * kCB + (int)fmin(bmax, (double)(kCB - 1))];
+            if (bmax >= 0.0) {
+                const int b = (int)fmin(bmax, (double)(kCB - 1));
+                lb += pl.unit ? (double)ccnt[(size_t)c * kCB + b] : fch[c] * (double)chist[(size_t)c * kCB + b];
+            }
         }
 #pragma unroll
         for (int o = 8; o > 0; o >>= 1) lb += __shfl_xor(lb, o);
@@ -457,7 +468,8 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
 // Gather.  grid (nchunk, rows), 256 threads: the row's plan, then the chunk's
 // keys of U written at the chunk's place in the row's index-ordered list.
 // The first chunk's workgroup records the plan and the size of U.
-__global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws) {
+__global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+                                                    int32_t* __restrict__ status) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
@@ -492,7 +504,10 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
             st.d_thr = pl.d_thr;
             st.mode = 0;
             st.count = ri.L;
+            st.unit = 0;
+            st.path = kPathAll;
             ws.st[ri.lrow] = st;
+            if (pl.bad) *status = 3;                      // invalid top_p: reported, nothing emitted
         }
         return;
     }
@@ -523,6 +538,8 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
         st.d_thr = pl.d_thr;
         st.mode = 1;
         st.count = 0;
+        st.unit = pl.unit;
+        st.path = 0;
         ws.st[ri.lrow] = st;
         ws.row_n[ri.lrow] = (uint32_t)nU;                 // at most 2^20
     }
@@ -554,7 +571,7 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
 // in registers (score key descending, index ascending) and finds the first
 // whose cumulative mass reaches the target.
 __device__ Cut list_cut(const unsigned long long* cand, const unsigned long long* wgt, int n, const float* srow,
-                        int L, uint32_t klo, uint32_t khi, unsigned long long target, float m, float s,
+                        int L, uint32_t klo, uint32_t khi, unsigned long long target, float m, float s, bool unit,
                         unsigned long long* hmb, uint32_t* hcb, unsigned long long* scan_sh, uint32_t* s_u,
                         unsigned long long* s_S, int* s_i, unsigned long long* small_v, unsigned long long* small_w,
                         Cut* s_cut) {
@@ -655,7 +672,7 @@ __device__ Cut list_cut(const unsigned long long* cand, const unsigned long long
         }
         if (klo == khi) {
             // one score value with more than 64 keys: its lowest indices first
-            const unsigned long long wT = weight_bin(key_score(klo), m, s).w;
+            const unsigned long long wT = unit ? 1ull : weight_bin(key_score(klo), m, s).w;
             const unsigned long long need = target - S_hi;
             const uint32_t ntie = (uint32_t)min((need + wT - 1ull) / wT, (unsigned long long)n_b);
             Cut c;
@@ -712,7 +729,8 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int nch = ri.nch;
     const float m = st.m, d_thr = st.d_thr;
-    const unsigned long long target = st.target;
+    unsigned long long target = st.target;
+    bool unit = st.unit != 0;
     const int lane = tid & 63;
     const int nU = (int)ws.row_n[ri.lrow];
     const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
@@ -722,21 +740,33 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
         for (int i = tid; i < nU; i += kRT) {
             const unsigned long long e = ub[i];
             cand[i] = e;
-            wgt[i] = weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
+            wgt[i] = unit ? 1ull : weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
         }
         __syncthreads();
-        const Cut cut = list_cut(cand, wgt, nU, srow, ri.L, klo, khi, target, m, s, hmb, hcb, scan_sh, &s_n, &s_S,
-                                 &s_i, small_v, small_w, &s_cut);
-        // U is in index order: its selected entries, in order, into the row's list
         constexpr int per = kCand / kRT;
-        uint32_t c = 0;
-#pragma unroll
-        for (int x = 0; x < per; ++x) {
-            const int i = tid * per + x;
-            if (i < nU && selected_by(cut, (uint32_t)(cand[i] >> 32), (int)~(uint32_t)cand[i])) ++c;
-        }
+        Cut cut;
+        uint32_t c;
         unsigned long long tot2;
-        uint32_t o = (uint32_t)block_excl_scan_u64<kRT>(c, &tot2, scan_sh);
+        uint32_t o;
+        for (int pass = 0;; ++pass) {
+            cut = list_cut(cand, wgt, nU, srow, ri.L, klo, khi, target, m, s, unit, hmb, hcb, scan_sh, &s_n, &s_S,
+                           &s_i, small_v, small_w, &s_cut);
+            c = 0;
+#pragma unroll
+            for (int x = 0; x < per; ++x) {
+                const int i = tid * per + x;
+                if (i < nU && selected_by(cut, (uint32_t)(cand[i] >> 32), (int)~(uint32_t)cand[i])) ++c;
+            }
+            o = (uint32_t)block_excl_scan_u64<kRT>(c, &tot2, scan_sh);
+            // the budget cap: a top-p set of more than k_max keys is cut
+            // again by count (U holds it, so it holds the first k_max keys)
+            if (pass > 0 || unit || g.k_max <= 0 || tot2 <= (unsigned long long)g.k_max) break;
+            unit = true;
+            target = (unsigned long long)g.k_max;
+            for (int i = tid; i < nU; i += kRT) wgt[i] = 1ull;
+            __syncthreads();
+        }
+        // U is in index order: its selected entries, in order, into the row's list
         uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
 #pragma unroll
         for (int x = 0; x < per; ++x) {
@@ -751,30 +781,41 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
             st.Tkey = cut.Tkey;
             st.jT = cut.jT;
             st.count = (int32_t)tot2;
+            st.unit = unit;
+            st.path = kPathList | (unit ? kPathCount : 0);
             ws.st[ri.lrow] = st;
         }
         return;
     }
     // ---- U too large for LDS: the cut over the row's scores, selected keys per
     // chunk for the ordered compaction
-    for (int c = tid; c < kMaxChunks; c += kRT) ccount[c] = 0u;
-    const Cut cut = radix_cut(cand, -1, srow, ri.L, klo, khi, 0ull, target, m, s, hmb, hcb, scan_sh, &s_n, &s_S,
-                              &s_i);
-    for (int j = tid; j < ri.L; j += kRT) {
-        const bool sel = selected_by(cut, score_key(srow[j]), j);
-        const unsigned long long b = __ballot(sel);
-        if (lane == 0 && b) atomicAdd(&ccount[j / kChunk], (uint32_t)__popcll(b));
+    Cut cut;
+    unsigned long long n_c, tot, ex;
+    for (int pass = 0;; ++pass) {
+        for (int c = tid; c < kMaxChunks; c += kRT) ccount[c] = 0u;
+        __syncthreads();
+        cut = radix_cut(cand, -1, srow, ri.L, klo, khi, 0ull, target, m, s, unit, hmb, hcb, scan_sh, &s_n, &s_S,
+                        &s_i);
+        for (int j = tid; j < ri.L; j += kRT) {
+            const bool sel = selected_by(cut, score_key(srow[j]), j);
+            const unsigned long long b = __ballot(sel);
+            if (lane == 0 && b) atomicAdd(&ccount[j / kChunk], (uint32_t)__popcll(b));
+        }
+        __syncthreads();
+        n_c = tid < nch ? ccount[tid] : 0ull;
+        ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
+        if (pass > 0 || unit || g.k_max <= 0 || tot <= (unsigned long long)g.k_max) break;
+        unit = true;                                      // the budget cap, as above
+        target = (unsigned long long)g.k_max;
     }
-    __syncthreads();
-    unsigned long long n_c = tid < nch ? ccount[tid] : 0ull;
-    unsigned long long tot;
-    const unsigned long long ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
     if (tid < nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)ex;
     if (tid == 0) {
         st.mode = 2;
         st.Tkey = cut.Tkey;
         st.jT = cut.jT;
         st.count = (int32_t)tot;
+        st.unit = unit;
+        st.path = kPathScan | (unit ? kPathCount : 0);
         ws.st[ri.lrow] = st;
     }
 }
@@ -797,7 +838,7 @@ __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut o
         if (i < ws.rows) out.row_ptr[row0 + i + 1] = carry + (int64_t)(ex + c);
         carry += (int64_t)tot;
     }
-    if (tid == 0 && carry > out.capacity) *out.status = 1;
+    if (tid == 0 && carry > out.capacity && *out.status == 0) *out.status = 1;
 }
 
 // ---------------------------------------------------------------------------
@@ -888,7 +929,18 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
     }
 }
 
+// Per-row path codes of the last selection (inspection).  grid (rows / 256 + 1).
+__global__ void k_sel_paths(const RowState* __restrict__ st, int rows, int32_t* __restrict__ paths) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < rows) paths[i] = st[i].path;
+}
+
 }  // namespace
+
+hipError_t launch_select_paths(const SelWs& ws, int rows, int32_t* paths, hipStream_t s) {
+    hipLaunchKernelGGL(k_sel_paths, dim3((rows + 255) / 256), dim3(256), 0, s, ws.st, rows, paths);
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
@@ -912,7 +964,7 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
                                (const bf16_t*)w_q, kl, row0, ws, out);
     }
     if (scores_only || stage == kSelScorePass) return hipGetLastError();
-    hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, top_p, row0, ws);
+    hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, top_p, row0, ws, out.status);
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
     const dim3 egrid(std::min(ws.nchunk, kEmitWG), ws.rows);
     if (ws.rows <= kRowsInEmit) {

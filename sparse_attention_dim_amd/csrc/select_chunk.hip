@@ -90,6 +90,9 @@ struct CRow {
     unsigned long long target;   // fixed-point mass to reach (kLevel)
     unsigned long long seg;      // pool offset of the row's segment (kBuf)
     unsigned long long light;    // approximate fixed-point mass of the keys outside U (kBuf)
+    unsigned long long zex;      // exact fixed-point mass of every key of the row (retried rows), else 0
+    int kcnt;        // > 0: the cut counts keys up to kcnt (fixed top-k or the budget cap); -3: invalid top_p
+    int path;        // kPath* code (written by the resolvers)
 };
 
 // orders this wave's LDS writes before its following LDS reads (other lanes)
@@ -186,7 +189,8 @@ struct CState {
     uint32_t ucount; // keys of U (exact: the runs' counts of pairs of bins <= uend)
     int mode;        // kAll or kLevel
     int uend;        // last P2 bin of U
-    int pad0, pad1;
+    int kcnt;        // > 0: the cut counts keys (fixed top-k, or a keep-all row capped); -3: invalid top_p
+    int pad1;
     unsigned long long seg;     // pool offset of the row's segment, kNoSeg if none
     unsigned long long light;   // approximate fixed-point mass of the keys outside U
 };
@@ -273,7 +277,10 @@ struct HistAcc {
     uint32_t* arrive;    // [n_ret][nt32]
     uint32_t* lrows;     // result records of the rows with U > kSmallU (the large-row resolve's list)
     uint32_t* mrows;     // result records of the rows with kTinyU < U <= kSmallU (the per-row resolve's list)
-    unsigned long long* lctr;   // [0], [1]: entries of lrows and the next one taken; [2], [3]: the same of mrows
+    uint32_t* zrows;     // rows whose cut is retried with the exact normaliser (or counted under the cap)
+    unsigned long long* lctr;   // [0], [1]: entries of lrows and the next one taken; [2], [3]: the same of mrows;
+                                // [4]: entries of zrows, [5], [6]: the next item of the exact-mass pass and
+                                // of the retried resolve
     int nt32, nfw, nsplit;
 };
 
@@ -520,7 +527,10 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     // bins are not wide against delta.
     if (tid < n_valid) {
         const int row = tid;
-        const float p = top_p[g.seq];
+        const float p = g.sel_k > 0 ? 1.0f : top_p[g.seq];
+        const int pos = g.pos0 + t0 + row;
+        // a count target: the fixed top-k budget, or the cap of a keep-all row
+        const int kc = g.sel_k > 0 ? g.sel_k : (!(p < 1.0f) && g.k_max > 0 ? g.k_max : 0);
         CState o;
         o.mp = r_mp[row];
         o.delta = r_delta[row];
@@ -534,31 +544,51 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         o.klo = 0u;
         o.khi = 0u;
         o.shift = 0u;
-        o.pad0 = o.pad1 = 0;
-        if (!(p < 1.0f)) {
+        o.kcnt = 0;
+        o.pad1 = 0;
+        if (g.sel_k <= 0 && !(p > 0.0f)) {
+            o.mode = kAll;                               // NaN or p <= 0: reported, nothing selected
+            o.kcnt = -3;
+        } else if (kc > 0 ? kc >= pos + 1 : !(p < 1.0f)) {
             o.mode = kAll;
         } else {
             const double sd = (double)s * (double)r_delta[row];
-            double Z = 0.0;
-            for (int b = 0; b < kHB; ++b) Z += hist[b][row];
-            const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * Z;
             int bc = kHB - 1;
-            double cum = 0.0;
-            for (int b = 0; b < kHB; ++b) {
-                cum += hist[b][row];
-                if (cum >= tgt_a) {
-                    bc = b;
-                    break;
+            if (kc > 0) {
+                // count cut: the first bin whose cumulative pair count reaches
+                // kc (pairs past kProv are not counted per bin: U is then
+                // every key)
+                o.kcnt = kc;
+                uint32_t cum = 0u;
+                for (int b = 0; b < kProv; ++b) {
+                    for (int zz = 0; zz < acc.nsplit; ++zz)
+                        cum += acc.cnt[(((size_t)(t0 + row) * g.n_ret + r) * acc.nsplit + zz) * kProv + b];
+                    if (cum >= (uint32_t)kc) {
+                        bc = b;
+                        break;
+                    }
+                }
+            } else {
+                double Z = 0.0;
+                for (int b = 0; b < kHB; ++b) Z += hist[b][row];
+                const double tgt_a = (double)p * (1.0 + sd + 0x1.0p-16) * Z;
+                double cum = 0.0;
+                for (int b = 0; b < kHB; ++b) {
+                    cum += hist[b][row];
+                    if (cum >= tgt_a) {
+                        bc = b;
+                        break;
+                    }
                 }
             }
             const int ue = (sd < 1.0 / 64.0) ? min(bc + 1, kHB - 1) : kHB - 1;
             double light = 0.0;
-            for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
+            if (kc == 0)
+                for (int b = ue + 1; b < kHB; ++b) light += hist[b][row];
             // the keys of U in each run of key tiles, exactly: the pairs of
             // bins <= ue counted by every run (every key of the run when U
             // is all of them); the row's segment holds run after run, each
             // with kSegPad slots of slack for its writers' last blocks
-            const int pos = g.pos0 + t0 + row;
             uint32_t uc = 0u, tot = 0u;
             for (int zz = 0; zz < acc.nsplit; ++zz) {
                 uint32_t c = 0u;
@@ -655,6 +685,9 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         out.target = 0ull;
         out.seg = r_seg[tid];
         out.light = c->light;
+        out.zex = 0ull;
+        out.kcnt = c->kcnt;
+        out.path = 0;
         rows_out[rg] = out;
         if (out.count > kSmallU)
             acc.lrows[atomicAdd(&acc.lctr[0], 1ull)] = (uint32_t)rg;
@@ -801,13 +834,46 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
         st[(size_t)(t0 + tid) * g.n_ret + r].seg = kNoSeg;
 }
 
+// The retry route: rows whose cut the approximate normaliser cannot certify
+// are listed for the exact-mass pass and resolved again with the exact
+// normaliser (their counts are written then).
+__device__ __forceinline__ void list_retry(uint32_t* zrows, unsigned long long* zctr, int row) {
+    zrows[atomicAdd(&zctr[0], 1ull)] = (uint32_t)row;
+}
+
+// Certification of a mass cut made with the normaliser Z' = zu + light, where
+// zu is U's exact mass and light the mass of the keys outside U summed from
+// their MFMA scores.  Each such weight carries a relative error of at most
+// eta = s delta / 8 (the score bound, with 1 % to spare) + 2^-16 (the float
+// rounding of its exponent argument, exp2 and the per-tile float sums), so
+// the exact Z lies in [Z' - light eta, Z' + light eta].  The cut (mass P_k
+// through the cut key, P_{k-1} before it) is kept when P_k / Z >= p - band
+// and P_{k-1} / Z < p + band for every Z in that interval; band = 0.9e-6
+// leaves 1e-7 of the 1e-6 acceptance band for the fp32 exp and fixed-point
+// rounding of the exact weights.
+constexpr double kBandCert = 0.9e-6;
+__device__ __forceinline__ double light_eta(float s, float delta) {
+    return (double)s * (double)delta * (0.125 * 1.01) + 0x1.0p-16;
+}
+__device__ __forceinline__ bool mass_certified(double p, unsigned long long zu, unsigned long long light, double eta,
+                                               unsigned long long pk, unsigned long long pk1) {
+    const double zc = (double)zu + (double)light, dl = (double)light * eta;
+    return (double)pk >= (p - kBandCert) * (zc + dl) && (double)pk1 < (p + kBandCert) * (zc - dl);
+}
+
 // ---------------------------------------------------------------------------
 // Radix levels.  grid (ceil(n_tok / 32), n_ret), 256 threads: the rows that
-// have no pool segment (and the keep-all rows' records).
+// have no pool segment (and the keep-all rows' records).  A mass cut that the
+// approximate normaliser cannot certify, or that keeps more than k_max keys,
+// is marked (bad = 2) and listed for the retry route; retry != 0 resolves the
+// marked rows again, with the exact normaliser or by count, and writes their
+// counts.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restrict__ k_low,
                                                    const float* __restrict__ top_p, const uint16_t* __restrict__ qlow,
-                                                   const CState* __restrict__ st, CRow* __restrict__ rows_out) {
+                                                   const CState* __restrict__ st, CRow* __restrict__ rows_out,
+                                                   int retry, int* __restrict__ counts, uint32_t* __restrict__ zrows,
+                                                   unsigned long long* __restrict__ zctr) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int r = blockIdx.y;
     const int t0 = blockIdx.x * kTR;
@@ -825,7 +891,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     __shared__ float r_mp[kTR], r_delta[kTR], r_T[kTR], r_edge[kTR], r_ethr[kTR];
     __shared__ int r_mode[kTR], r_uend[kTR], r_ntie[kTR], r_done[kTR], r_gather[kTR], r_bad[kTR], r_pooled[kTR];
     __shared__ uint32_t r_klo[kTR], r_khi[kTR], r_shift[kTR], r_cnthi[kTR];
-    __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_light[kTR];
+    __shared__ unsigned long long r_shi[kTR], r_target[kTR], r_light[kTR], r_zex[kTR];
+    __shared__ int r_unit[kTR], r_kcnt[kTR], r_rec[kTR];
     __shared__ int s_any;
     __shared__ uint4 ktile[4][32][2];                    // per wave: the 32 keys of the current tile
 
@@ -846,8 +913,14 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         r_pooled[row] = 0;
         r_done[row] = 1;
         r_mode[row] = kLevel;
+        r_unit[row] = 0;
+        r_kcnt[row] = 0;
+        r_zex[row] = 0ull;
+        r_rec[row] = 0;
         if (row < n_valid) {
             const CState c = st[(size_t)(t0 + row) * g.n_ret + r];
+            r_kcnt[row] = c.kcnt;
+            r_unit[row] = c.kcnt > 0;
             r_mp[row] = c.mp;
             r_delta[row] = c.delta;
             r_ethr[row] = c.e_thr;
@@ -860,7 +933,20 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             r_light[row] = c.light;
             r_pooled[row] = c.mode == kLevel && c.seg != kNoSeg;
             r_done[row] = c.mode != kLevel || r_pooled[row];
-            if (!r_pooled[row]) s_any = 1;                // a record to write here
+            r_rec[row] = !r_pooled[row];
+            if (retry) {
+                // only the rows marked for the retry route, from their records
+                const CRow& cw = rows_out[(size_t)(t0 + row) * g.n_ret + r];
+                const bool mine = !r_pooled[row] && cw.mode == kLevel && cw.bad == 2;
+                r_rec[row] = mine;
+                r_done[row] = !mine;
+                if (mine) {
+                    r_kcnt[row] = cw.kcnt;
+                    r_unit[row] = cw.kcnt > 0;
+                    r_zex[row] = cw.zex;
+                }
+            }
+            if (r_rec[row]) s_any = 1;                    // a record to write here
         }
     }
     for (int x = tid; x < kTR * kNBP; x += 256) {
@@ -910,6 +996,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
         const float dl = r_delta[lr];
         const uint32_t klo = r_klo[lr], khi = r_khi[lr], shift = r_shift[lr];
         const float mp_row = r_mp[lr];
+        const bool unit = r_unit[lr] != 0;
         float qv[16];
 #pragma unroll
         for (int c = 0; c < 16; ++c) qv[c] = qs[lr][c];
@@ -943,7 +1030,7 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                             cand[lr][cs] = ((unsigned long long)kd << 32) | (unsigned long long)(~(uint32_t)key);
                     }
                 } else {
-                    const unsigned long long w = weight_bin(d, mp_row, s).w;
+                    const unsigned long long w = unit ? 1ull : weight_bin(d, mp_row, s).w;
                     if (level == 0) zacc += w;
                     if (kd >= klo && kd <= khi) {
                         const uint32_t bk = min((khi - kd) >> shift, (uint32_t)(kNB - 1));
@@ -966,12 +1053,16 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             const int row = tid;
             if (!r_done[row]) {
                 if (level == 0) {
-                    const float p = top_p[g.seq];
-                    const unsigned long long Z = zu[row] + r_light[row];
-                    unsigned long long tgt = (unsigned long long)ceil((double)p * (double)Z);
-                    if (tgt > Z) tgt = Z;
-                    if (tgt < 1ull) tgt = 1ull;
-                    r_target[row] = tgt;
+                    if (r_unit[row]) {
+                        r_target[row] = (unsigned long long)r_kcnt[row];
+                    } else {
+                        const float p = top_p[g.seq];
+                        const unsigned long long Z = retry ? r_zex[row] : zu[row] + r_light[row];
+                        unsigned long long tgt = (unsigned long long)ceil((double)p * (double)Z);
+                        if (tgt > Z) tgt = Z;
+                        if (tgt < 1ull) tgt = 1ull;
+                        r_target[row] = tgt;
+                    }
                 }
                 if (r_gather[row]) {
                     r_done[row] = 1;                     // final sort of the cut bucket's keys below
@@ -1003,7 +1094,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                         const uint32_t n_c = hc[row][bc];
                         if (klo == khi && n_c > (uint32_t)kCapC) {
                             // one score value with many keys: a tie group cut by index
-                            const unsigned long long wT = weight_bin(key_score(khi), r_mp[row], s).w;
+                            const unsigned long long wT =
+                                r_unit[row] ? 1ull : weight_bin(key_score(khi), r_mp[row], s).w;
                             const unsigned long long need = r_target[row] - cum;
                             r_T[row] = key_score(khi);
                             r_ntie[row] = (int)((need + wT - 1ull) / wT);
@@ -1027,7 +1119,9 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     // ---- per-row results; rows resolved by levels sort their candidates here
     if (wid == 0) {
         for (int row = 0; row < n_valid; ++row) {
-            if (r_pooled[row]) continue;                 // written by the recording pass
+            if (!r_rec[row]) continue;                   // pooled rows: written by the histogram pass
+            const bool unit = r_unit[row] != 0;
+            unsigned long long pk = 0ull, pk1 = 0ull;    // mass through the cut key and before it
             CRow out;
             out.mp = r_mp[row];
             out.delta = r_delta[row];
@@ -1041,12 +1135,18 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
             out.count = 0;
             out.target = r_target[row];
             out.light = r_light[row];
+            out.zex = r_zex[row];
+            out.kcnt = r_kcnt[row];
+            out.path = kPathLevel | (retry ? kPathExactZ : 0) | (unit ? kPathCount : 0);
             int bad = r_bad[row];
             if (out.mode == kLevel && !bad) {
                 if (r_gather[row] == 2) {
                     out.T = r_T[row];
                     out.n_tie = r_ntie[row];
                     out.count = (int)r_cnthi[row] + r_ntie[row];
+                    const unsigned long long wT = unit ? 1ull : weight_bin(out.T, r_mp[row], s).w;
+                    pk = r_shi[row] + (unsigned long long)r_ntie[row] * wT;
+                    pk1 = pk - wT;
                 } else {
                     const int n = min((int)cand_n[row], kCapC);
                     if (n == 0 || r_gather[row] != 1 || !r_done[row]) {
@@ -1076,9 +1176,9 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                         const int i0 = 2 * lane, i1 = 2 * lane + 1;
                         const float mpr = r_mp[row];
                         const unsigned long long w0 =
-                            i0 < n ? weight_bin(key_score((uint32_t)(cr[i0] >> 32)), mpr, s).w : 0ull;
+                            i0 < n ? (unit ? 1ull : weight_bin(key_score((uint32_t)(cr[i0] >> 32)), mpr, s).w) : 0ull;
                         const unsigned long long w1 =
-                            i1 < n ? weight_bin(key_score((uint32_t)(cr[i1] >> 32)), mpr, s).w : 0ull;
+                            i1 < n ? (unit ? 1ull : weight_bin(key_score((uint32_t)(cr[i1] >> 32)), mpr, s).w) : 0ull;
                         unsigned long long incl = w0 + w1;
 #pragma unroll
                         for (int o = 1; o < 64; o <<= 1) {
@@ -1095,6 +1195,24 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                         for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
                         if (first >= n) bad = 1;
                         const int ic = first < n ? first : n - 1;
+                        {
+                            // the masses at the cut, from the lane holding rank ic
+                            unsigned long long a = 0ull, b = 0ull;
+                            if (ic == i0) {
+                                a = c0;
+                                b = c0 - w0;
+                            } else if (ic == i1) {
+                                a = c1;
+                                b = c0;
+                            }
+#pragma unroll
+                            for (int o = 32; o > 0; o >>= 1) {
+                                a += __shfl_xor(a, o);
+                                b += __shfl_xor(b, o);
+                            }
+                            pk = a;
+                            pk1 = b;
+                        }
                         const uint32_t kT = (uint32_t)(cr[ic] >> 32);
                         int tie = 0, above = 0;
                         if (i0 <= ic) {
@@ -1115,9 +1233,28 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                 }
                 // certification: no key outside U can reach the cut
                 if (!(out.T > out.d_edge)) bad = 1;
+                if (!bad && !unit) {
+                    const float p = top_p[g.seq];
+                    const bool cap = g.k_max > 0 && out.count > g.k_max;
+                    const bool unsure = !retry && out.light != 0ull &&
+                                        ((g.flags & kFlagExactMass) ||
+                                         !mass_certified((double)p, zu[row], out.light, light_eta(s, out.delta), pk,
+                                                         pk1));
+                    if (retry && cap) {
+                        bad = 1;                         // capped after the exact normaliser: not handled
+                    } else if (cap || unsure) {
+                        bad = 2;                         // the retry route: exact normaliser, or by count
+                        out.kcnt = cap ? g.k_max : 0;
+                        out.zex = 0ull;
+                        if (lane == 0) list_retry(zrows, zctr, (t0 + row) * g.n_ret + r);
+                    }
+                }
             }
             out.bad = bad;
-            if (lane == 0) rows_out[(size_t)(t0 + row) * g.n_ret + r] = out;
+            if (lane == 0) {
+                rows_out[(size_t)(t0 + row) * g.n_ret + r] = out;
+                if (retry) counts[(t0 + row) * g.n_ret + r] = bad ? -1 : out.count;
+            }
             wave_lds_sync();
         }
     }
@@ -1151,20 +1288,29 @@ struct ResolveSmem {
     unsigned long long small_v[64], small_w[64];
     uint32_t kmin, kmax, s_u, tkey;
     int s_i, ntie, fail;
-    unsigned long long s_S;
+    unsigned long long s_S, s_C;
+    unsigned long long pk, pk1, cnt;    // mass through the cut key and before it; keys taken
 };
 
 template <int CAP, int NT, int RBITS = kRBits>
-__device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t* __restrict__ k_low,
-                            const uint16_t* __restrict__ qlow, const float* __restrict__ top_p,
-                            unsigned long long* __restrict__ pool, int* __restrict__ count_out,
-                            unsigned long long* sk, unsigned long long* scan_sh, ResolveSmem<1 << RBITS>& sm) {
+__device__ void resolve_row(const Geo& g, const CRow& cr, int row, int rid, bool retry,
+                            const bf16_t* __restrict__ k_low, const uint16_t* __restrict__ qlow,
+                            const float* __restrict__ top_p, unsigned long long* __restrict__ pool,
+                            int* __restrict__ count_out, int* __restrict__ path_out, uint32_t* __restrict__ zrows,
+                            unsigned long long* __restrict__ zctr, unsigned long long* sk,
+                            unsigned long long* scan_sh, ResolveSmem<1 << RBITS>& sm) {
     constexpr int kRB = 1 << RBITS;                      // radix buckets per level
     constexpr int PER = CAP / NT;
     static_assert(CAP % NT == 0, "whole slots per thread");
     const int tid = threadIdx.x, lane = tid & 63;
     const int slots = cr.count;
     const float s = g.idx_scale;
+    const bool unit0 = cr.kcnt > 0;                      // count cut: fixed top-k (or a capped keep-all row)
+    const float p = unit0 ? 1.0f : top_p[g.seq];
+    if (!retry && !unit0 && cr.light != 0ull && (g.flags & kFlagExactMass)) {
+        if (tid == 0) list_retry(zrows, zctr, row);      // the exact normaliser was asked for
+        return;
+    }
     unsigned long long* ub = pool + cr.seg;
     const int r = row % g.n_ret;
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
@@ -1189,7 +1335,7 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
             const uint4* kp = reinterpret_cast<const uint4*>(
                 k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
             const float d = exact_score(q16, kp[0], kp[1]);
-            zl += weight_bin(d, cr.mp, s).w;
+            zl += unit0 ? 1ull : weight_bin(d, cr.mp, s).w;
             ++nl;
             const uint32_t kd = score_key(d);
             kmn = min(kmn, kd);
@@ -1208,19 +1354,26 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     block_excl_scan_u64<NT>(zl, &zu, scan_sh);
     block_excl_scan_u64<NT>(nl, &n64, scan_sh);
     unsigned long long target;
-    {
-        const float p = top_p[g.seq];
-        const unsigned long long Z = zu + cr.light;
+    if (unit0) {
+        target = (unsigned long long)cr.kcnt;
+    } else {
+        const unsigned long long Z = retry ? cr.zex : zu + cr.light;
         target = (unsigned long long)ceil((double)p * (double)Z);
         if (target > Z) target = Z;
         if (target < 1ull) target = 1ull;
     }
-    const auto wkey = [&](uint32_t key) { return weight_bin(key_score(key), cr.mp, s).w; };
-    // ---- radix cut: Tkey and the number of ties at Tkey taken (lowest indices)
-    uint32_t klo = sm.kmin, khi = sm.kmax;
-    unsigned long long S_hi = 0ull;
-    bool done = n64 == 0ull || zu < target;             // U cannot reach the target: not certified
-    if (done && tid == 0) sm.fail = 1;
+    bool unit = unit0;
+    const auto wkey = [&](uint32_t key) { return unit ? 1ull : weight_bin(key_score(key), cr.mp, s).w; };
+    const uint32_t kmin0 = sm.kmin, kmax0 = sm.kmax;
+    // ---- radix cut: Tkey and the number of ties at Tkey taken (lowest
+    // indices).  A mass cut is certified against the approximate normaliser;
+    // one that keeps more than k_max keys is cut again by count.
+    for (int pass = 0; pass < 2; ++pass) {
+    if (pass) __syncthreads();                           // every thread has read the first cut
+    uint32_t klo = kmin0, khi = kmax0;
+    unsigned long long S_hi = 0ull, C_hi = 0ull;
+    bool done = n64 == 0ull || (unit ? n64 : zu) < target;   // U cannot reach the target: not certified
+    if (tid == 0) sm.fail = done ? 1 : 0;
     for (int level = 0; level < 6 && !done; ++level) {
         const uint32_t span = khi - klo;
         const int bits = span ? 32 - __clz(span) : 0;
@@ -1242,11 +1395,15 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
         __syncthreads();
         constexpr int BPT = kRB / NT;                       // buckets per thread (1 or 2)
         static_assert(BPT >= 1 && kRB % NT == 0, "whole buckets per thread");
-        unsigned long long loc = 0ull;
+        unsigned long long loc = 0ull, locc = 0ull;
 #pragma unroll
-        for (int x = 0; x < BPT; ++x) loc += sm.hm[BPT * tid + x];
+        for (int x = 0; x < BPT; ++x) {
+            loc += sm.hm[BPT * tid + x];
+            locc += sm.hc[BPT * tid + x];
+        }
         unsigned long long tot;
         const unsigned long long ex = S_hi + block_excl_scan_u64<NT>(loc, &tot, scan_sh);
+        const unsigned long long exc = C_hi + block_excl_scan_u64<NT>(locc, &tot, scan_sh);
         if (tid == 0) sm.s_i = kRB;
         __syncthreads();
         {
@@ -1269,13 +1426,18 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
             break;
         }
         if (bk / BPT == tid) {
-            unsigned long long run = ex;
-            for (int b = BPT * tid; b < bk; ++b) run += sm.hm[b];
+            unsigned long long run = ex, runc = exc;
+            for (int b = BPT * tid; b < bk; ++b) {
+                run += sm.hm[b];
+                runc += sm.hc[b];
+            }
             sm.s_S = run;
+            sm.s_C = runc;
             sm.s_u = sm.hc[bk];
         }
         __syncthreads();
         S_hi = sm.s_S;
+        C_hi = sm.s_C;
         const uint32_t n_b = sm.s_u;
         const uint32_t nkhi = khi - ((uint32_t)bk << shift);
         const uint32_t wdt = (1u << shift) - 1u;
@@ -1331,6 +1493,11 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
                     sm.ntie = __popcll(tie);
                     if (!reach) sm.fail = 1;
                 }
+                if (lane == ic) {
+                    sm.pk = S_hi + incl;
+                    sm.pk1 = S_hi + incl - w;
+                    sm.cnt = C_hi + (unsigned long long)ic + 1ull;
+                }
             }
             __syncthreads();
             done = true;
@@ -1341,8 +1508,12 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
             if (tid == 0) {
                 const unsigned long long wT = wkey(klo);
                 const unsigned long long need = target - S_hi;
+                const unsigned long long nt = min((need + wT - 1ull) / wT, (unsigned long long)n_b);
                 sm.tkey = klo;
-                sm.ntie = (int)min((need + wT - 1ull) / wT, (unsigned long long)n_b);
+                sm.ntie = (int)nt;
+                sm.pk = S_hi + nt * wT;
+                sm.pk1 = sm.pk - wT;
+                sm.cnt = C_hi + nt;
             }
             __syncthreads();
             done = true;
@@ -1351,11 +1522,29 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
     }
     if (!done && tid == 0) sm.fail = 1;                  // no level isolated the cut
     __syncthreads();
+    if (pass == 0 && !unit0 && !sm.fail) {
+        if (!retry && cr.light != 0ull &&
+            !mass_certified((double)p, zu, cr.light, light_eta(s, cr.delta), sm.pk, sm.pk1)) {
+            if (tid == 0) list_retry(zrows, zctr, row);   // uniform: shared values after a barrier
+            return;
+        }
+        if (g.k_max > 0 && sm.cnt > (unsigned long long)g.k_max) {
+            unit = true;                                 // the budget cap: the first k_max keys by count
+            target = (unsigned long long)g.k_max;
+            continue;
+        }
+    }
+    break;
+    }
     const uint32_t Tkey = sm.tkey;
     const int ntie = sm.ntie;
     const bool ok = !sm.fail && key_score(Tkey) > cr.d_edge;
+    const int pflags = (retry ? kPathExactZ : 0) | (unit ? kPathCount : 0);
     if (!ok) {
-        if (tid == 0) *count_out = -1;
+        if (tid == 0) {
+            *count_out = -1;
+            *path_out = rid | pflags;
+        }
         __syncthreads();
         return;
     }
@@ -1485,7 +1674,10 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
                     ubi[o++] = bmin + 32u * (uint32_t)w + (uint32_t)b;
                 }
             }
-            if (tid == 0) *count_out = (int)cnt;
+            if (tid == 0) {
+                *count_out = (int)cnt;
+                *path_out = rid | pflags | kPathBitmap;
+            }
             __syncthreads();
             return;
         }
@@ -1578,7 +1770,10 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
             if (tie) ++tr;
         }
     }
-    if (tid == 0) *count_out = (int)cnt;
+    if (tid == 0) {
+        *count_out = (int)cnt;
+        *path_out = rid | pflags | kPathMerge;
+    }
     __syncthreads();
 }
 
@@ -1587,14 +1782,15 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, const bf16_t*
 // counter, so no LDS is held by workgroups of rows that are not theirs.
 constexpr int kRT = 512;
 __global__ __launch_bounds__(kRT) __attribute__((amdgpu_waves_per_eu(4)))   // two workgroups per CU
-void k_csel_resolve(Geo g, const CRow* __restrict__ rows, int n_rows,
+void k_csel_resolve(Geo g, CRow* __restrict__ rows, int n_rows,
                                                       const uint32_t* __restrict__ mrows,
                                                       unsigned long long* __restrict__ mctr,
                                                       const bf16_t* __restrict__ k_low,
                                                       const uint16_t* __restrict__ qlow,
                                                       const float* __restrict__ top_p,
                                                       unsigned long long* __restrict__ pool,
-                                                      int* __restrict__ counts) {
+                                                      int* __restrict__ counts, uint32_t* __restrict__ zrows,
+                                                      unsigned long long* __restrict__ zctr) {
     __shared__ unsigned long long sk[kSmallU + kSmallU / 128];
     __shared__ unsigned long long scan_sh[kRT / 64 + 1];
     __shared__ ResolveSmem<1 << kRBits> sm;
@@ -1609,7 +1805,8 @@ void k_csel_resolve(Geo g, const CRow* __restrict__ rows, int n_rows,
         const int row = (int)mrows[e];
         const CRow cr = rows[row];
         if (cr.mode != kBuf || cr.bad || cr.count <= kTinyU || cr.count > kSmallU) continue;
-        resolve_row<kSmallU, kRT>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+        resolve_row<kSmallU, kRT>(g, cr, row, kPathRow, false, k_low, qlow, top_p, pool, &counts[row],
+                                  &rows[row].path, zrows, zctr, sk, scan_sh, sm);
     }
 }
 
@@ -1618,18 +1815,20 @@ void k_csel_resolve(Geo g, const CRow* __restrict__ rows, int n_rows,
 // the counts of the rows that have no segment.  grid (rows).
 constexpr int kRTS = 128;
 constexpr int kRBitsS = 8;
-__global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* __restrict__ rows,
+__global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, CRow* __restrict__ rows,
                                                              const bf16_t* __restrict__ k_low,
                                                              const uint16_t* __restrict__ qlow,
                                                              const float* __restrict__ top_p,
                                                              unsigned long long* __restrict__ pool,
-                                                             int* __restrict__ counts) {
+                                                             int* __restrict__ counts, uint32_t* __restrict__ zrows,
+                                                             unsigned long long* __restrict__ zctr) {
     const int row = blockIdx.x;
     const CRow cr = rows[row];
     if (cr.mode != kBuf) {
         if (threadIdx.x == 0) {
             const int L = g.pos0 + row / g.n_ret + 1;
-            counts[row] = cr.bad ? -1 : (cr.mode == kAll ? L : cr.count);
+            counts[row] = cr.kcnt == -3 ? -3 : (cr.bad ? -1 : (cr.mode == kAll ? L : cr.count));
+            if (cr.mode == kAll) rows[row].path = kPathAll;
         }
         return;
     }
@@ -1641,41 +1840,96 @@ __global__ __launch_bounds__(kRTS) void k_csel_resolve_small(Geo g, const CRow* 
     __shared__ unsigned long long sk[kTinyU + kTinyU / 128];
     __shared__ unsigned long long scan_sh[kRTS / 64 + 1];
     __shared__ ResolveSmem<1 << kRBitsS> sm;
-    resolve_row<kTinyU, kRTS, kRBitsS>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+    resolve_row<kTinyU, kRTS, kRBitsS>(g, cr, row, kPathTiny, false, k_low, qlow, top_p, pool, &counts[row],
+                                       &rows[row].path, zrows, zctr, sk, scan_sh, sm);
 }
 
 // Rows with U in (kSmallU, kSegMax]: one 512-thread workgroup per CU takes
 // the rows the histogram pass listed, one at a time from a shared counter
 // (rows differ several-fold in cost, so a fixed assignment leaves CUs idle).
 // A listed row that the recording pass sent to the radix levels is skipped.
+// retry: the listed rows are the retry route's (any segment size), resolved
+// with their exact normaliser.  list_n[0] holds the entries, *next the next
+// entry taken.
 constexpr int kRTL = 512;      // threads of the large-row resolve (two waves per SIMD: room for its registers)
-__global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, const CRow* __restrict__ rows, int n_rows,
-                                                             const uint32_t* __restrict__ lrows,
-                                                             unsigned long long* __restrict__ lctr,
+__global__ __launch_bounds__(kRTL) void k_csel_resolve_large(Geo g, CRow* __restrict__ rows, int n_rows,
+                                                             const uint32_t* __restrict__ list,
+                                                             const unsigned long long* __restrict__ list_n,
+                                                             unsigned long long* __restrict__ next, int retry,
                                                              const bf16_t* __restrict__ k_low,
                                                              const uint16_t* __restrict__ qlow,
                                                              const float* __restrict__ top_p,
                                                              unsigned long long* __restrict__ pool,
-                                                             int* __restrict__ counts) {
+                                                             int* __restrict__ counts, uint32_t* __restrict__ zrows,
+                                                             unsigned long long* __restrict__ zctr) {
     __shared__ unsigned long long sk[kSegMax + kSegMax / 128];
     __shared__ unsigned long long scan_sh[kRTL / 64 + 1];
     __shared__ ResolveSmem<1 << kRBits> sm;
     __shared__ unsigned long long s_next;
-    const unsigned long long n_list = min(lctr[0], (unsigned long long)n_rows);
+    const unsigned long long n_list = min(list_n[0], (unsigned long long)n_rows);
     for (;;) {
         __syncthreads();                                 // every thread has read the previous entry number
-        if (threadIdx.x == 0) s_next = atomicAdd(&lctr[1], 1ull);
+        if (threadIdx.x == 0) s_next = atomicAdd(next, 1ull);
         __syncthreads();
         const unsigned long long e = s_next;
         if (e >= n_list) break;
-        const int row = (int)lrows[e];
+        const int row = (int)list[e];
         const CRow cr = rows[row];
-        if (cr.mode != kBuf || cr.count <= kSmallU) continue;
+        if (cr.mode != kBuf || (!retry && cr.count <= kSmallU)) continue;
         if (cr.bad) {
             if (threadIdx.x == 0) counts[row] = -1;
             continue;
         }
-        resolve_row<kSegMax, kRTL>(g, cr, row, k_low, qlow, top_p, pool, &counts[row], sk, scan_sh, sm);
+        resolve_row<kSegMax, kRTL>(g, cr, row, kPathLarge, retry != 0, k_low, qlow, top_p, pool, &counts[row],
+                                   &rows[row].path, zrows, zctr, sk, scan_sh, sm);
+    }
+}
+
+// Exact mass of every key of the rows on the retry route: the fixed-order
+// score and exact fixed-point weight of each key, summed per piece of
+// kZPiece keys and added into the row's record (an exact, order-free sum).
+// Items (listed row, piece) are taken from a shared counter.  256 threads.
+constexpr int kZPiece = 32768;
+__global__ __launch_bounds__(256) void k_csel_zexact(Geo g, CRow* __restrict__ rows, int n_rows,
+                                                     const uint32_t* __restrict__ zrows,
+                                                     unsigned long long* __restrict__ zctr,
+                                                     const bf16_t* __restrict__ k_low,
+                                                     const uint16_t* __restrict__ qlow) {
+    __shared__ unsigned long long s_next;
+    __shared__ unsigned long long red[4];
+    const int tid = threadIdx.x;
+    const unsigned long long n_list = min(zctr[0], (unsigned long long)n_rows);
+    const int npiece = (g.pos0 + g.n_tok + kZPiece - 1) / kZPiece;
+    const unsigned long long n_items = n_list * (unsigned long long)npiece;
+    const float s = g.idx_scale;
+    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
+    for (;;) {
+        __syncthreads();
+        if (tid == 0) s_next = atomicAdd(&zctr[1], 1ull);
+        __syncthreads();
+        const unsigned long long e = s_next;
+        if (e >= n_items) break;
+        const int row = (int)zrows[e / (unsigned long long)npiece];
+        const int k0 = (int)(e % (unsigned long long)npiece) * kZPiece;
+        const int L = g.pos0 + row / g.n_ret + 1;
+        if (k0 >= L) continue;
+        const int r = row % g.n_ret;
+        const float mp = rows[row].mp;
+        float q16[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) q16[c] = bf2f(qlow[(size_t)row * 16 + c]);
+        unsigned long long acc = 0ull;
+        const int k1 = min(L, k0 + kZPiece);
+        for (int key = k0 + tid; key < k1; key += 256) {
+            const int page = bt[key >> 8];
+            const uint4* kp = reinterpret_cast<const uint4*>(
+                k_low + (((size_t)page * g.n_ret + r) * kBlk + (key & 255)) * 16);
+            acc += weight_bin(exact_score(q16, kp[0], kp[1]), mp, s).w;
+        }
+        acc = wave_sum_u64(acc);
+        if ((tid & 63) == 0) red[tid >> 6] = acc;
+        __syncthreads();
+        if (tid == 0) atomicAdd(&rows[row].zex, red[0] + red[1] + red[2] + red[3]);
     }
 }
 
@@ -1694,7 +1948,8 @@ __global__ __launch_bounds__(1024) void k_csel_rowptr(const int* __restrict__ co
     for (int i0 = 0; i0 < rows; i0 += 1024) {
         const int i = i0 + tid;
         const int c = i < rows ? counts[i] : 0;
-        if (c < 0) s_bad = 1;
+        if (c == -3) atomicMax(&s_bad, 3);               // invalid top_p
+        else if (c < 0) atomicMax(&s_bad, 2);            // a cut not certified
         const unsigned long long cu = c > 0 ? (unsigned long long)c : 0ull;
         unsigned long long tot;
         const unsigned long long ex = block_excl_scan_u64<1024>(cu, &tot, scan_sh);
@@ -1702,7 +1957,7 @@ __global__ __launch_bounds__(1024) void k_csel_rowptr(const int* __restrict__ co
         carry += (int64_t)tot;
     }
     __syncthreads();
-    if (tid == 0) *status = s_bad ? 2 : (carry > capacity ? 1 : 0);
+    if (tid == 0) *status = s_bad ? s_bad : (carry > capacity ? 1 : 0);
 }
 
 // Rows held in a segment and keep-all rows: copy into idx.  grid (rows), 256 threads.
@@ -1851,7 +2106,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
                                                     float* __restrict__ knorm, int nblk,
                                                     unsigned long long* __restrict__ pool_ctr) {
     const int r = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
-    if (blk == 0 && r == 0 && tid < 5) pool_ctr[tid] = 0ull;   // pool; the large- and per-row lists, their queues
+    if (blk == 0 && r == 0 && tid < 8) pool_ctr[tid] = 0ull;   // pool; the row lists and their queues
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     float kn = 0.0f;
     for (int i = tid; i < kNormKeys; i += 256) {
@@ -1875,7 +2130,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, mrows, ctr, pool, head;
+    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, mrows, zrows, ctr, pool, head;
     int nblk, nfw, nsplit;
 };
 
@@ -1906,13 +2161,27 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.arrive = w.segoff + up((size_t)rows * w.nsplit * 4);
     w.lrows = w.arrive + up(nrt * 4);
     w.mrows = w.lrows + up((size_t)rows * 4);
-    w.ctr = w.mrows + up((size_t)rows * 4);
+    w.zrows = w.mrows + up((size_t)rows * 4);
+    w.ctr = w.zrows + up((size_t)rows * 4);
     w.pool = w.ctr + 256;
     w.head = w.pool;
     return w;
 }
 
+// Per-row path codes of the last chunk selection (inspection).
+__global__ void k_csel_paths(const CRow* __restrict__ rows, int n, int32_t* __restrict__ paths) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) paths[i] = rows[i].path;
+}
+
 }  // namespace
+
+hipError_t launch_chunk_paths(const Geo& g, const void* ws, int32_t* paths, hipStream_t s) {
+    const int rows = g.n_tok * g.n_ret;
+    const CRow* crow = (const CRow*)((const char*)ws + chunk_ws(rows, g.n_ret, g.pos0 + g.n_tok).crow);
+    hipLaunchKernelGGL(k_csel_paths, dim3((rows + 255) / 256), dim3(256), 0, s, crow, rows, paths);
+    return hipGetLastError();
+}
 
 size_t chunk_select_head_bytes(int rows, int n_ret, int n_keys) { return chunk_ws(rows, n_ret, n_keys).head; }
 
@@ -1948,7 +2217,9 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     acc.nsplit = w.nsplit;
     acc.lrows = (uint32_t*)(base + w.lrows);
     acc.mrows = (uint32_t*)(base + w.mrows);
+    acc.zrows = (uint32_t*)(base + w.zrows);
     acc.lctr = ctr + 1;
+    unsigned long long* zctr = acc.lctr + 4;
     hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
                        w.nblk, ctr);
     hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
@@ -1957,13 +2228,21 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
                        qlow, cst, ctr, pool_cap, acc, crow);
     hipLaunchKernelGGL(k_csel_rec, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, qlow,
                        cst, pool, acc);
-    hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow);
+    hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow, 0, counts,
+                       acc.zrows, zctr);
     hipLaunchKernelGGL(k_csel_resolve, dim3(std::min(rows, 512)), dim3(kRT), 0, s, g, crow, rows, acc.mrows,
-                       acc.lctr + 2, (const bf16_t*)k_low, qlow, top_p, pool, counts);
+                       acc.lctr + 2, (const bf16_t*)k_low, qlow, top_p, pool, counts, acc.zrows, zctr);
     hipLaunchKernelGGL(k_csel_resolve_small, dim3(rows), dim3(kRTS), 0, s, g, crow, (const bf16_t*)k_low, qlow,
-                       top_p, pool, counts);
+                       top_p, pool, counts, acc.zrows, zctr);
     hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 256)), dim3(kRTL), 0, s, g, crow, rows, acc.lrows,
-                       acc.lctr, (const bf16_t*)k_low, qlow, top_p, pool, counts);
+                       acc.lctr, acc.lctr + 1, 0, (const bf16_t*)k_low, qlow, top_p, pool, counts, acc.zrows, zctr);
+    // the retry route (rows listed above; each launch ends at once when none is)
+    hipLaunchKernelGGL(k_csel_zexact, dim3(std::min(rows * ((n_keys + kZPiece - 1) / kZPiece), 1024)), dim3(256), 0,
+                       s, g, crow, rows, acc.zrows, zctr, (const bf16_t*)k_low, qlow);
+    hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow, 1, counts,
+                       acc.zrows, zctr);
+    hipLaunchKernelGGL(k_csel_resolve_large, dim3(std::min(rows, 256)), dim3(kRTL), 0, s, g, crow, rows, acc.zrows,
+                       zctr, zctr + 2, 1, (const bf16_t*)k_low, qlow, top_p, pool, counts, acc.zrows, zctr);
     hipLaunchKernelGGL(k_csel_rowptr, dim3(1), dim3(1024), 0, s, counts, rows, out.row_ptr, out.capacity,
                        out.status);
     hipLaunchKernelGGL(k_csel_copy, dim3(rows), dim3(256), 0, s, crow, pool, out.row_ptr, out.idx, out.status);

@@ -93,6 +93,35 @@ class Dev:
         del ws
         return self.sets()
 
+    def select_mode(self, top_k: int = 0, k_max: int = 0, flags: int = 0, capacity: int | None = None,
+                    ws_bytes: int | None = None, top_p=None):
+        """Selection with another rule: fixed top-k (top_k > 0), the top-p
+        budget cap (k_max), layer flags, or other top_p values.  Returns
+        (status, row_ptr, sets or None, path codes)."""
+        w = self.w
+        layer = rtp.make_layer(w.Hq, w.Hkv, w.D, rtp_dtype(w.dtype), w.ret_heads, w.window, w.sinks,
+                               w.attn_scale, w.idx_scale, k_max=k_max, flags=flags)
+        if capacity is None:
+            capacity = sum(w.row_pos(t) + 1 for t in range(w.n_tok)) * w.n_ret
+        self.row_ptr = torch.zeros(self.rows + 1, dtype=torch.int64, device="cuda")
+        self.idx = torch.full((max(capacity, 1),), -1, dtype=torch.int32, device="cuda")
+        self.status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+        self.sel = rtp.make_sel(self.row_ptr, self.idx, self.status)
+        if ws_bytes is None:
+            ws_bytes = rtp.topp_select_workspace(layer, self.cache, self.query)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        tp = self.top_p if top_p is None else torch.as_tensor(np.asarray(top_p, np.float32)).cuda()
+        if top_k > 0:
+            rtp.topk_select(layer, self.cache, self.query, self.w_q, top_k, self.sel, ws)
+        else:
+            rtp.topp_select(layer, self.cache, self.query, self.w_q, tp, self.sel, ws)
+        paths = torch.full((self.rows,), -1, dtype=torch.int32, device="cuda")
+        rtp.topp_select_paths(layer, self.cache, self.query, ws, paths)
+        torch.cuda.synchronize()
+        del ws
+        st, rp, sets = self.sets()
+        return st, rp, sets, paths.cpu().numpy()
+
     def sets(self):
         rp = self.row_ptr.cpu().numpy()
         st = int(self.status.cpu().item())
@@ -153,6 +182,30 @@ def band_accept(gpu: np.ndarray, order: np.ndarray, cum: np.ndarray, p: float, b
     ok = ck >= pp - band and ck1 < pp + band
     exact = ck >= pp and ck1 < pp
     return ok, exact
+
+
+def band_accept_cap(gpu: np.ndarray, order: np.ndarray, cum: np.ndarray, p: float, k_max: int,
+                    band: float = BAND) -> bool:
+    """A set under the top-p budget cap: the first min(k, k_max) keys of the
+    rank order for a k the band accepts."""
+    if len(gpu) < k_max:
+        return band_accept(gpu, order, cum, p, band)[0]
+    if len(gpu) != k_max or not np.array_equal(np.sort(order[:k_max]), gpu):
+        return False
+    # some k >= k_max is accepted: C_{k_max - 1} < p + band (C_0 = 0)
+    ck1 = cum[k_max - 2] if k_max >= 2 else 0.0
+    return np.float32(p) >= 1.0 or ck1 < float(np.float32(p)) + band
+
+
+def path_counts(paths: np.ndarray) -> dict:
+    """Histogram of route codes (low 4 bits) and flags over the rows."""
+    out = {}
+    for name, code in (("all", 1), ("tiny", 2), ("row", 3), ("large", 4), ("level", 5), ("list", 6),
+                       ("scan", 7)):
+        out[name] = int(np.sum((paths & 15) == code))
+    for name, bit in (("bitmap", 16), ("merge", 32), ("exact_z", 64), ("count", 128)):
+        out[name] = int(np.sum((paths & bit) != 0))
+    return out
 
 
 def check_out(got: np.ndarray, ref: np.ndarray, dtype: str) -> float:

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared():
         assert hasattr(lib, n), n
     assert sorted(declared()) == sorted(rtp.ENTRY_POINTS)
-    assert rtp.version() == 1
+    assert rtp.version() == 2
 
 
 def test_no_cpu_fallback_when_library_missing(tmp_path):
@@ -97,6 +97,8 @@ def _select(layer, cache, query, sel, ws_bytes=1 << 40, fn="rtp_topp_select"):
     (dict(idx_scale=float("nan")), rtp.RTP_EINVAL),
     (dict(dtype=5), rtp.RTP_EINVAL),
     (dict(num_q_heads=64, num_kv_heads=4), rtp.RTP_EUNSUPPORTED),   # 16 query heads per KV head
+    (dict(k_max=-1), rtp.RTP_EINVAL),
+    (dict(flags=4), rtp.RTP_EINVAL),                   # unknown flag
 ])
 def test_layer_checks(kw, code):
     assert _window(_layer(**kw), _cache(), _query()) == code
@@ -202,3 +204,30 @@ def test_chunk_select_minimum_workspace():
     D = _query()
     assert (lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(D)) ==
             lib.rtp_topp_select_workspace_min(ctypes.byref(L), ctypes.byref(C), ctypes.byref(D)))
+
+
+def test_topk_and_paths_checks():
+    lib = rtp.load()
+    L, C, Q = _layer(), _cache(), _query()
+    need = lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    topk = lib.rtp_topk_select
+    for k in (0, -3):
+        assert topk(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, k, ctypes.byref(_sel()), FAKE,
+                    need, None) == rtp.RTP_EINVAL
+    bad = _sel()
+    bad.row_ptr = None
+    assert topk(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, 8, ctypes.byref(bad), FAKE, need,
+                None) == rtp.RTP_EINVAL
+    assert topk(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, 8, ctypes.byref(_sel()), FAKE,
+                need - 1, None) == rtp.RTP_EWORKSPACE
+    # top-p needs its p array; top-k does not (checked before any launch)
+    assert lib.rtp_topp_select(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, None, ctypes.byref(_sel()),
+                               FAKE, need, None) == rtp.RTP_EINVAL
+    paths = lib.rtp_topp_select_paths
+    assert paths(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, need, None, None) == rtp.RTP_EINVAL
+    assert paths(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, need - 1, FAKE, None) == rtp.RTP_EWORKSPACE
+
+
+def test_max_len_constant_matches_header():
+    src = open(HEADER).read()
+    assert "#define RTP_MAX_LEN (1 << 20)" in src and rtp.RTP_MAX_LEN == 1 << 20
