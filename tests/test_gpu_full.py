@@ -19,7 +19,8 @@ import torch
 
 import oracle
 import synth
-from gpu_util import Dev, band_accept, check_out, out_f32, say
+import sparse_attention_dim_amd as rtp
+from gpu_util import Dev, band_accept, check_out, out_f32, path_counts, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -31,39 +32,65 @@ def _free():
     torch.cuda.empty_cache()
 
 
-def _check_rows(w, d, rows, sets, out, k_low_cache):
-    """rows: list of (t, r); checks selection bands and sparse outputs."""
-    def job(tr):
-        t, r = tr
-        b, pos = w.row_seq(t), w.row_pos(t)
-        h = w.ret_heads[r]
-        g = w.kv_head(h)
-        key = (b, r)
-        if key not in k_low_cache:
-            k_low_cache[key] = oracle.project(w.k[b][:, g, :], w.w_k[r])
-        K = synth.as_f32(w.k[b][:, g, :])
-        V = synth.as_f32(w.v[b][:, g, :])
-        res = oracle.retrieval_row(w.q[t, h], K, V, w.w_q[r], w.w_k[r], pos, w.idx_scale,
-                                   float(w.top_p[b]), w.attn_scale, k_low=k_low_cache[key])
-        gset = sets[t * w.n_ret + r]
-        ok, ex = band_accept(gset, res["order"], res["cum"], float(w.top_p[b]))
-        ref = oracle.attend(w.q[t, h], K, V, gset, w.attn_scale)
-        return tr, ok, ex, check_out(out[t, h], ref, w.dtype), len(gset)
+def _check_rows(w, d, rows, sets, out, k_low_cache, p_override=None):
+    """rows: list of (t, r); checks selection bands and sparse outputs.  Rows
+    are grouped by sequence; each sequence's K/V heads are widened to fp32
+    once and dropped after its rows."""
+    by_b = {}
+    for t, r in rows:
+        by_b.setdefault(w.row_seq(t), []).append((t, r))
+    results = []
+    for b, brow in sorted(by_b.items()):
+        heads = sorted({w.kv_head(w.ret_heads[r]) for _, r in brow})
+        kv = {g: (synth.as_f32(w.k[b][:, g, :]), synth.as_f32(w.v[b][:, g, :])) for g in heads}
+        need = sorted({r for _, r in brow if (b, r) not in k_low_cache})
 
-    # fill the indexer keys needed, in parallel, before the row jobs
-    need = sorted({(w.row_seq(t), r) for t, r in rows})
-    def fill(br):
-        b, r = br
-        g = w.kv_head(w.ret_heads[r])
-        return br, oracle.project(w.k[b][:, g, :], w.w_k[r])
-    with cf.ThreadPoolExecutor(THREADS) as ex:
-        for br, kl in ex.map(fill, [x for x in need if x not in k_low_cache]):
-            k_low_cache[br] = kl
-        results = list(ex.map(job, rows))
+        def fill(r):
+            g = w.kv_head(w.ret_heads[r])
+            return r, oracle.project(w.k[b][:, g, :], w.w_k[r])
+
+        def job(tr):
+            t, r = tr
+            pos = w.row_pos(t)
+            h = w.ret_heads[r]
+            K, V = kv[w.kv_head(h)]
+            p = float(w.top_p[b]) if p_override is None else p_override
+            res = oracle.retrieval_row(w.q[t, h], K, V, w.w_q[r], w.w_k[r], pos, w.idx_scale, p,
+                                       w.attn_scale, k_low=k_low_cache[(b, r)])
+            gset = sets[t * w.n_ret + r]
+            ok, ex = band_accept(gset, res["order"], res["cum"], p)
+            ref = oracle.attend(w.q[t, h], K, V, gset, w.attn_scale)
+            err = check_out(out[t, h], ref, w.dtype) if out is not None else 0.0
+            return tr, ok, ex, err, len(gset)
+
+        with cf.ThreadPoolExecutor(THREADS) as ex:
+            for r, kl in ex.map(fill, need):
+                k_low_cache[(b, r)] = kl
+            results += list(ex.map(job, brow))
+        del kv
     for tr, ok, exact, err, n in results:
         assert ok, ("selection outside the band", tr, n)
         assert err <= 1.0, ("sparse attention", tr, err)
     return results
+
+
+def _route_rows(paths, n_ret, per_route, rng):
+    """Up to per_route rows of every route and emit order seen in paths."""
+    picks = set()
+    for code in range(1, 8):
+        idx = np.flatnonzero((paths & 15) == code)
+        picks.update(int(i) for i in rng.choice(idx, min(per_route, len(idx)), replace=False))
+    for bit in (16, 32, 64, 128):
+        idx = np.flatnonzero((paths & bit) != 0)
+        picks.update(int(i) for i in rng.choice(idx, min(per_route, len(idx)), replace=False))
+    return [(i // n_ret, i % n_ret) for i in sorted(picks)]
+
+
+def _assert_routes(paths_checked, need):
+    pc = path_counts(np.asarray(paths_checked, np.int32))
+    say("   oracle-checked rows per route", pc)
+    for name in need:
+        assert pc[name] >= 16, ("route checked on fewer than 16 rows", name, pc[name])
 
 
 def _check_local(w, out, pairs):
@@ -97,15 +124,17 @@ def _decode_case(i, seqs):
     say("[gpu-full] %s: B=%d max L=%d" % (w.name, w.B, int(w.seq_lens.max())))
     d = Dev(w, permute_seed=5)
     say("[gpu-full] %s: select" % w.name)
-    st, rp, sets = d.select(capacity=int(sum(int(l) for l in w.seq_lens) * w.n_ret))
+    st, rp, sets, paths = d.select_mode(capacity=int(sum(int(l) for l in w.seq_lens) * w.n_ret))
     assert st == 0
     say("[gpu-full] %s: sparse + window" % w.name)
     d.out.zero_()
     d.sparse()
     d.window()
     out = out_f32(d.out)
-    rows = [(t, r) for t in seqs for r in range(w.n_ret)]
+    # every row of the step
+    rows = [(t, r) for t in range(w.n_tok) for r in range(w.n_ret)]
     res = _check_rows(w, d, rows, sets, out, {})
+    say("   paths of the rows", path_counts(paths))
     loc = w.local_heads()
     g = np.random.default_rng(i)
     _check_local(w, out, [(t, int(h)) for t in seqs for h in g.choice(loc, 6, replace=False)])
@@ -147,6 +176,24 @@ def test_full_decode_bf16_ragged():
     _decode_case(5, sorted({int(order[0]), int(order[-1]), int(order[32]), 0}))
 
 
+def test_full_decode_bf16_128k_topk():
+    # fixed top-k at the decode workload's full size: bit-exact on every row
+    w = synth.config(2)
+    say("[gpu-full] %s: top-k 512" % w.name)
+    d = Dev(w, permute_seed=5)
+    st, rp, sets, paths = d.select_mode(top_k=512)
+    assert st == 0
+    for b in range(w.B):
+        for r in range(w.n_ret):
+            h = w.ret_heads[r]
+            g = w.kv_head(h)
+            q_low = oracle.project(w.q[b, h].reshape(1, -1), w.w_q[r])[0]
+            dsc = oracle.scores(q_low, oracle.project(w.k[b][:, g, :], w.w_k[r]))
+            np.testing.assert_array_equal(sets[b * w.n_ret + r], oracle.topk(dsc, 512))
+    del d
+    _free()
+
+
 def _prefill_case(i, rows_t):
     w = synth.config(i)
     say("[gpu-full] %s: L=%d chunk %d" % (w.name, int(w.seq_lens[0]), w.n_tok))
@@ -168,11 +215,35 @@ def test_full_prefill_128k():
     rows_t = [0, 1, 2047, 4095] + [int(x) for x in np.random.default_rng(3).choice(4096, 3, replace=False)]
     w, d, out = _prefill_case(3, rows_t)
     say("[gpu-full] %s: select + sparse prefill" % w.name)
-    st, rp, sets = d.select(capacity=int(w.n_tok * w.n_ret * 8192))
+    cap = int(w.n_tok * w.n_ret * 8192)
+    st, rp, sets, paths = d.select_mode(capacity=cap)
     assert st == 0
     d.sparse()
     out = out_f32(d.out)
-    _check_rows(w, d, [(t, r) for t in rows_t for r in range(w.n_ret)], sets, out, {})
+    say("   paths of the rows", path_counts(paths))
+    # every row of the chunk against the oracle
+    k_low = {}
+    rows = [(t, r) for t in range(w.n_tok) for r in range(w.n_ret)]
+    res = _check_rows(w, d, rows, sets, out, k_low)
+    say("   rows checked %d, bit-exact sets %d" % (len(res), sum(1 for x in res if x[2])))
+    _assert_routes(paths, ["tiny", "row", "bitmap", "merge"])
+    rng = np.random.default_rng(31)
+    # a workspace at its minimum: every row takes the radix levels
+    say("[gpu-full] %s: select, minimum workspace" % w.name)
+    low = rtp.topp_select_workspace_min(d.layer, d.cache, d.query)
+    st, rp, sets2, paths2 = d.select_mode(capacity=cap, ws_bytes=low)
+    assert st == 0
+    pick = _route_rows(paths2, w.n_ret, 48, rng)
+    _check_rows(w, d, pick, sets2, None, k_low)
+    _assert_routes([paths2[t * w.n_ret + r] for t, r in pick], ["level"])
+    # the exact normaliser on every row that has keys outside its candidates
+    say("[gpu-full] %s: select, exact normaliser" % w.name)
+    st, rp, sets3, paths3 = d.select_mode(capacity=cap, flags=rtp.RTP_FLAG_EXACT_MASS)
+    assert st == 0
+    say("   paths", path_counts(paths3))
+    pick = _route_rows(paths3, w.n_ret, 48, rng)
+    _check_rows(w, d, pick, sets3, None, k_low)
+    _assert_routes([paths3[t * w.n_ret + r] for t, r in pick], ["exact_z"])
     del d
     _free()
 
@@ -182,17 +253,32 @@ def test_full_prefill_1m():
     w, d, out = _prefill_case(4, rows_t)
     say("[gpu-full] %s: select + sparse prefill" % w.name)
     cap = int(w.n_tok * w.n_ret * 16384)
-    st, rp, sets = d.select(capacity=cap)
+    st, rp, sets, paths = d.select_mode(capacity=cap)
     if st == 1:
         # the selection did not fit: rerun with the exact total it reported
         cap = int(rp[-1])
         say("   capacity %d" % cap)
-        st, rp, sets = d.select(capacity=cap)
+        st, rp, sets, paths = d.select_mode(capacity=cap)
     assert st == 0
     d.sparse()
     out = out_f32(d.out)
-    res = _check_rows(w, d, [(t, r) for t in rows_t for r in range(w.n_ret)], sets, out, {})
-    sizes = [n for *_, n in res]
-    say("   budgets of checked rows: min %d median %d max %d" % (min(sizes), int(np.median(sizes)), max(sizes)))
+    say("   paths of the rows", path_counts(paths))
+    # >= 1024 rows: the 64 largest sets, 32 rows of every route seen, the
+    # chunk's first and last rows, then a seeded sample
+    rng = np.random.default_rng(4)
+    sizes = np.diff(rp)
+    pick = {(int(i) // w.n_ret, int(i) % w.n_ret) for i in np.argsort(sizes, kind="stable")[-64:]}
+    pick |= set(_route_rows(paths, w.n_ret, 32, rng))
+    pick |= {(t, r) for t in rows_t for r in range(w.n_ret)}
+    rest = rng.permutation(d.rows)
+    for i in rest:
+        if len(pick) >= 1024:
+            break
+        pick.add((int(i) // w.n_ret, int(i) % w.n_ret))
+    pick = sorted(pick)
+    res = _check_rows(w, d, pick, sets, out, {})
+    n = [x[4] for x in res]
+    say("   rows checked %d; budgets min %d median %d max %d" % (len(res), min(n), int(np.median(n)), max(n)))
+    _assert_routes([paths[t * w.n_ret + r] for t, r in pick], ["tiny", "row", "large", "bitmap", "merge"])
     del d
     _free()
