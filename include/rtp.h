@@ -210,6 +210,25 @@ rtp_status rtp_topp_select_end(const rtp_layer *layer, const rtp_cache *cache, c
                                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * rtp_topp_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus the workspace),
+ * checks, result and errors as rtp_topp_select; the workspace is a static
+ * device array of RTP_NOALLOC_SCRATCH_BYTES on the current GPU (the stream
+ * must belong to it), which each GPU the library runs on holds until the
+ * process ends.  A query whose selection needs more scratch than that (see
+ * rtp_topp_select_workspace; for bf16 chunks rtp_topp_select_workspace_min)
+ * is rejected with RTP_EWORKSPACE before anything is enqueued.  The call
+ * itself allocates nothing.  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (e.g. on two streams) race and must be
+ * serialised by the caller; the array keeps the last call's contents, and
+ * the selection clears what it needs itself.
+ */
+#define RTP_NOALLOC_SCRATCH_BYTES (64u << 20)
+rtp_status rtp_topp_select_noalloc(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                                   const void *w_q, const float *top_p, const rtp_sel *sel, void *stream);
+
+/*
  * Fixed top-k selection: the fixed-budget rule that the method's dynamic
  * top-p replaces (abstract, observation (3); forum post, "Three Key Insights"
  * item 3).  Same arguments, scores, ranking, output and workspace as

@@ -22,6 +22,7 @@ RTP_BLOCK = 256
 RTP_MAX_RET = 64
 RTP_MAX_LEN = 1 << 20
 RTP_FLAG_EXACT_MASS = 1
+RTP_NOALLOC_SCRATCH_BYTES = 64 << 20
 # selection status word
 SEL_OK, SEL_OVERFLOW, SEL_UNCERTIFIED, SEL_BAD_TOP_P = 0, 1, 2, 3
 # per-row path codes of rtp_topp_select_paths
@@ -31,7 +32,8 @@ PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT = 16, 32, 64, 128
 ENTRY_POINTS = (
     "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_topp_select_workspace",
     "rtp_topp_select_workspace_min",
-    "rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end", "rtp_topk_select",
+    "rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end", "rtp_topp_select_noalloc",
+    "rtp_topk_select",
     "rtp_topp_select_paths", "rtp_indexer_scores",
     "rtp_sparse_attn_workspace",
     "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_window_attn_workspace",
@@ -94,6 +96,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_topp_select": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
         "rtp_topp_select_begin": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
         "rtp_topp_select_end": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
+        "rtp_topp_select_noalloc": ([pl, pc, pq, P, P, ps, P], ctypes.c_int),
         "rtp_topk_select": ([pl, pc, pq, P, i32, ps, P, S, P], ctypes.c_int),
         "rtp_topp_select_paths": ([pl, pc, pq, P, S, P, P], ctypes.c_int),
         "rtp_indexer_scores": ([pl, pc, pq, P, P, P, i64, P], ctypes.c_int),
@@ -233,6 +236,13 @@ def topp_select_end(layer, cache, query, w_q, top_p, sel, ws, stream=None, prepa
     """Second phase of topp_select (cut and selected sets); same arguments as the first."""
     return _run("rtp_topp_select_end", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
                             _ptr(top_p), ctypes.byref(sel), _ptr(ws), _nbytes(ws), _stream(stream)),
+                (layer, cache, query, sel), prepare)
+
+
+def topp_select_noalloc(layer, cache, query, w_q, top_p, sel, stream=None, prepare=False):
+    """topp_select with the library's static scratch array instead of a workspace."""
+    return _run("rtp_topp_select_noalloc", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
+                                            _ptr(w_q), _ptr(top_p), ctypes.byref(sel), _stream(stream)),
                 (layer, cache, query, sel), prepare)
 
 

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/rtp.h"
@@ -37,6 +38,15 @@ rtp_status hip_status(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(RTP_EHIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
 }
+
+// Scratch of rtp_topp_select_noalloc: a static device array, one copy per GPU
+// (each GPU the library runs on holds it until the process ends).  In host
+// code `scratch` only names the symbol; its device address on the current
+// GPU comes from hipGetSymbolAddress, taken once per device and kept.
+static __device__ __align__(256) unsigned char scratch[RTP_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
 
 constexpr int kMaxLen = RTP_MAX_LEN;      // longest supported context: fixed-point masses of every key fit 2^63
 constexpr int kMaxDecodeRows = 4096;      // decode rows (batch * num_ret) of the sparse kernel
@@ -294,6 +304,24 @@ size_t rtp_topp_select_workspace_min(const rtp_layer* layer, const rtp_cache* ca
     return plan_select(layer, cache, query).total;
 }
 
+// Device address of the current GPU's scratch array (looked up on its first use).
+rtp_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RTP_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(RTP_EUNSUPPORTED, "device %d", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(RTP_EHIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return RTP_OK;
+}
+
 // phase: 0 the whole selection, 1 the scoring pass of the first row group
 // (when every row fits one group), 2 the rest.  top_k > 0: fixed top-k.
 static rtp_status topp_select_phase(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
@@ -342,6 +370,32 @@ rtp_status rtp_topp_select(const rtp_layer* layer, const rtp_cache* cache, const
                            const void* w_q, const float* top_p, const rtp_sel* sel, void* workspace,
                            size_t workspace_bytes, void* stream) {
     return topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, workspace_bytes, stream, 0, 0);
+}
+
+rtp_status rtp_topp_select_noalloc(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                   const void* w_q, const float* top_p, const rtp_sel* sel, void* stream) {
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    constexpr size_t cap = (size_t)RTP_NOALLOC_SCRATCH_BYTES;
+    size_t bytes;
+    if (tiled_select(layer, query)) {
+        // the chunk path takes any workspace from its minimum up: the rows
+        // whose candidate set misses the smaller pool take the radix levels
+        const int rows = query->n_tok * layer->num_ret, keys = query->pos0 + query->n_tok;
+        const size_t low = rtp::chunk_select_head_bytes(rows, layer->num_ret, keys);
+        if (low > cap)
+            return fail(RTP_EWORKSPACE, "selection needs %zu bytes of scratch, more than the %zu of the static array",
+                        low, cap);
+        bytes = std::min(cap, rtp::chunk_select_ws_bytes(rows, layer->num_ret, keys));
+    } else {
+        bytes = plan_select(layer, cache, query).total;
+        if (bytes > cap)
+            return fail(RTP_EWORKSPACE, "selection needs %zu bytes of scratch, more than the %zu of the static array",
+                        bytes, cap);
+    }
+    void* ws = nullptr;
+    if ((s = scratch_of_current_device(&ws))) return s;
+    return topp_select_phase(layer, cache, query, w_q, top_p, sel, ws, bytes, stream, 0, 0);
 }
 
 rtp_status rtp_topk_select(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query, const void* w_q,

@@ -231,3 +231,21 @@ def test_topk_and_paths_checks():
 def test_max_len_constant_matches_header():
     src = open(HEADER).read()
     assert "#define RTP_MAX_LEN (1 << 20)" in src and rtp.RTP_MAX_LEN == 1 << 20
+
+
+def test_noalloc_select_rejects_queries_beyond_its_scratch():
+    # 48 decode rows over 2^20 keys need ~200 MB of scores: more than the
+    # static scratch array, so the call fails on the host (nothing enqueued);
+    # bad arguments are reported as by rtp_topp_select
+    lib = rtp.load()
+    L = _layer()
+    C = _cache(batch=16, max_blocks=4096, max_seq_len=1 << 20)
+    Q = _query(n_tok=16)
+    need = lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    assert need > rtp.RTP_NOALLOC_SCRATCH_BYTES
+    fn = lib.rtp_topp_select_noalloc
+    assert fn(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), FAKE, FAKE, ctypes.byref(_sel()),
+              None) == rtp.RTP_EWORKSPACE
+    assert b"scratch" in lib.rtp_last_error()
+    assert fn(ctypes.byref(_layer(window=0)), ctypes.byref(C), ctypes.byref(Q), FAKE, FAKE, ctypes.byref(_sel()),
+              None) == rtp.RTP_EINVAL
