@@ -32,6 +32,17 @@
  *    at slot j % RTP_BLOCK.  Keys are stored after RoPE.
  *  - Indexer pages: k_low is bf16 [num_blocks][num_ret][RTP_BLOCK][16], using
  *    the same page ids as k/v (one 8 KiB run per page and retrieval head).
+ *  - Window-only ring (optional; the cache-side half of the method: the full
+ *    KV cache is kept only for the KV heads that serve a retrieval head).
+ *    When cache->k_ring is set, KV heads none of whose query heads retrieve
+ *    ("ring heads") live in k_ring/v_ring [num_ring_blocks][n_ring][RTP_BLOCK][D]
+ *    in ascending KV-head order, and k/v pages hold only the other KV heads
+ *    ([num_blocks][Hkv - n_ring][RTP_BLOCK][D], ascending).  A sequence's ring
+ *    has ring_pages pages: entry 0 of its ring_table row holds positions
+ *    0..255 (the sinks), entries 1..ring_pages-1 hold later positions in
+ *    rotation (position j >= 256 in entry 1 + (j/256 - 1) % (ring_pages - 1)),
+ *    so only the last (ring_pages - 1) * 256 positions past the first page are
+ *    kept.
  *  - Projections w_q, w_k: [num_ret][head_dim][16], row-major.
  *  - Queries q: [n_tok][num_q_heads][head_dim], after RoPE.
  *  - Output out: [n_tok][num_q_heads][head_dim]; the sparse calls write the
@@ -106,6 +117,10 @@ typedef struct rtp_cache {
     int32_t max_blocks;             /* row stride of block_table */
     int32_t max_seq_len;            /* [host] upper bound of every seq_lens[b], at most RTP_MAX_LEN;
                                        sizes grids and workspaces */
+    const void *k_ring;             /* NULL: no ring (every KV head in k/v); else ring K pages, see above */
+    const void *v_ring;
+    const int32_t *ring_table;      /* [batch][ring_pages] page ids of the ring pools */
+    int32_t ring_pages;             /* [host] >= 2 when k_ring is set */
 } rtp_cache;
 
 /* [host] struct: the query rows of one call. */
@@ -150,6 +165,24 @@ const char *rtp_last_error(void);
  */
 rtp_status rtp_indexer_append(const rtp_layer *layer, const rtp_cache *cache, const void *w_k,
                               const int32_t *seq_id, const int32_t *pos, int32_t n, void *stream);
+
+/*
+ * a1 fused with the K/V append (abstract: retrieval heads keep the full KV
+ * cache, the others a restricted window; forum post, "Three Key Insights"
+ * item 1): stores the K and V rows of n new tokens, k_new / v_new
+ * [n][Hkv][D] (dtype of the layer, 16-byte aligned), at positions pos[i] of
+ * sequences seq_id[i] -- in k/v, or in the ring for the ring heads -- and
+ * writes their indexer keys k_low exactly as rtp_indexer_append would, from
+ * the new K rows, all in one launch.  The cache's k, v, k_ring, v_ring and
+ * k_low are written (the const of rtp_cache's k/v does not apply here).
+ * seq_id, pos: device int32[n]; tokens with an out-of-range seq_id or pos are
+ * skipped.  Two tokens of one call that land in the same ring slot (positions
+ * of a sequence (ring_pages - 1) * 256 or more apart) race: append such
+ * positions in separate calls, in position order.  n == 0 is a no-op.  Errors: RTP_EINVAL for NULL pointers, n < 0
+ * or misaligned k_new / v_new.
+ */
+rtp_status rtp_kv_append(const rtp_layer *layer, const rtp_cache *cache, const void *k_new, const void *v_new,
+                         const void *w_k, const int32_t *seq_id, const int32_t *pos, int32_t n, void *stream);
 
 /* Workspace bytes needed by rtp_topp_select / rtp_indexer_scores for this query.
  * For a bf16 RTP_CHUNK query this size holds a candidate buffer of 8192 keys
@@ -293,13 +326,17 @@ size_t rtp_dense_attn_workspace(const rtp_layer *layer, const rtp_cache *cache, 
  * window; forum "Three Key Insights" item 1): for every non-retrieval head h
  * and query at position pos, exact softmax attention over the keys
  *   {0 .. num_sinks-1} U {pos-window+1 .. pos}, clipped to [0, pos].
+ * With a ring the ring heads read it: it must hold every key a query of the
+ * call needs, so num_sinks <= 256 and (ring_pages - 1) * 256 >= window + 255
+ * (+ n_tok - 1 for chunks); RTP_EINVAL otherwise.
  */
 rtp_status rtp_window_attn(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
                            void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Dense causal attention of every head over keys 0..pos: the same-GPU
- * baseline against which the sparse path's speedup is reported.
+ * baseline against which the sparse path's speedup is reported.  Needs every
+ * key of every head: RTP_EINVAL for a cache with a ring.
  */
 rtp_status rtp_dense_attn(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
                           void *out, void *workspace, size_t workspace_bytes, void *stream);

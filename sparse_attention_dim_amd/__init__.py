@@ -30,7 +30,7 @@ PATH_ALL, PATH_TINY, PATH_ROW, PATH_LARGE, PATH_LEVEL, PATH_LIST, PATH_SCAN = 1,
 PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT = 16, 32, 64, 128
 
 ENTRY_POINTS = (
-    "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_topp_select_workspace",
+    "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_kv_append", "rtp_topp_select_workspace",
     "rtp_topp_select_workspace_min",
     "rtp_topp_select", "rtp_topp_select_begin", "rtp_topp_select_end", "rtp_topp_select_noalloc",
     "rtp_topk_select",
@@ -60,7 +60,9 @@ class Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_low", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
-                ("max_seq_len", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32),
+                ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("ring_table", ctypes.c_void_p),
+                ("ring_pages", ctypes.c_int32)]
 
 
 class Query(ctypes.Structure):
@@ -91,6 +93,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_version": ([], ctypes.c_int),
         "rtp_last_error": ([], ctypes.c_char_p),
         "rtp_indexer_append": ([pl, pc, P, P, P, i32, P], ctypes.c_int),
+        "rtp_kv_append": ([pl, pc, P, P, P, P, P, i32, P], ctypes.c_int),
         "rtp_topp_select_workspace": ([pl, pc, pq], S),
         "rtp_topp_select_workspace_min": ([pl, pc, pq], S),
         "rtp_topp_select": ([pl, pc, pq, P, P, ps, P, S, P], ctypes.c_int),
@@ -179,13 +182,17 @@ def make_layer(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int, r
     return L
 
 
-def make_cache(k, v, k_low, block_table, seq_lens, max_seq_len: int) -> Cache:
+def make_cache(k, v, k_low, block_table, seq_lens, max_seq_len: int, k_ring=None, v_ring=None,
+               ring_table=None) -> Cache:
     C = Cache()
     C.k, C.v, C.k_low = _ptr(k), _ptr(v), _ptr(k_low)
     C.block_table, C.seq_lens = _ptr(block_table), _ptr(seq_lens)
     C.batch = block_table.shape[0]
     C.max_blocks = block_table.shape[1]
     C.max_seq_len = int(max_seq_len)
+    if k_ring is not None:
+        C.k_ring, C.v_ring, C.ring_table = _ptr(k_ring), _ptr(v_ring), _ptr(ring_table)
+        C.ring_pages = ring_table.shape[1]
     return C
 
 
@@ -209,6 +216,12 @@ def version() -> int:
 def indexer_append(layer, cache, w_k, seq_id, pos, stream=None, prepare=False):
     return _run("rtp_indexer_append", (ctypes.byref(layer), ctypes.byref(cache), _ptr(w_k), _ptr(seq_id),
                                        _ptr(pos), seq_id.numel(), _stream(stream)), (layer, cache), prepare)
+
+
+def kv_append(layer, cache, k_new, v_new, w_k, seq_id, pos, stream=None, prepare=False):
+    """K/V rows of new tokens into the cache (and the ring) with their indexer keys, one launch."""
+    return _run("rtp_kv_append", (ctypes.byref(layer), ctypes.byref(cache), _ptr(k_new), _ptr(v_new), _ptr(w_k),
+                                  _ptr(seq_id), _ptr(pos), seq_id.numel(), _stream(stream)), (layer, cache), prepare)
 
 
 def topp_select_workspace(layer, cache, query) -> int:

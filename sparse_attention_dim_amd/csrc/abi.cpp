@@ -96,6 +96,19 @@ rtp_status check_cache(const rtp_cache* C) {
         return fail(RTP_EUNSUPPORTED, "max_seq_len %d out of [1, %d]", C->max_seq_len, kMaxLen);
     if (C->max_blocks < 1 || (int64_t)C->max_blocks * RTP_BLOCK < C->max_seq_len)
         return fail(RTP_EINVAL, "max_blocks %d cannot hold max_seq_len %d", C->max_blocks, C->max_seq_len);
+    if (C->k_ring && (!C->v_ring || !C->ring_table || C->ring_pages < 2))
+        return fail(RTP_EINVAL, "ring: needs v_ring, ring_table and ring_pages >= 2");
+    return RTP_OK;
+}
+
+// The ring holds every key the call's local heads need.
+rtp_status check_ring_window(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
+    if (!C->k_ring) return RTP_OK;
+    if (L->num_sinks > RTP_BLOCK) return fail(RTP_EINVAL, "ring: num_sinks %d > %d", L->num_sinks, RTP_BLOCK);
+    const int64_t span = (int64_t)L->window + 255 + (Q->kind == RTP_CHUNK ? Q->n_tok - 1 : 0);
+    if ((int64_t)(C->ring_pages - 1) * RTP_BLOCK < span)
+        return fail(RTP_EINVAL, "ring of %d pages cannot hold a window span of %lld positions", C->ring_pages,
+                    (long long)span);
     return RTP_OK;
 }
 
@@ -153,6 +166,22 @@ rtp::Geo make_geo(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
     g.max_seq_len = C->max_seq_len;
     g.block_table = C->block_table;
     g.seq_lens = C->seq_lens;
+    // KV layout: with a ring, the KV heads none of whose query heads
+    // retrieve live in it; the rest keep their pages in k/v
+    int serves[256] = {0};
+    for (int r = 0; r < L->num_ret; ++r) serves[L->ret_heads[r] / g.group] = 1;
+    int n_pool = 0, n_ring = 0;
+    for (int kv = 0; kv < g.Hkv; ++kv) {
+        const bool ring = C->k_ring && !serves[kv];
+        g.kv_ring[kv] = ring;
+        g.kv_slot[kv] = (uint8_t)(ring ? n_ring++ : n_pool++);
+    }
+    g.pool_heads = n_pool;
+    g.ring_heads = n_ring;
+    g.ring_pages = C->k_ring ? C->ring_pages : 0;
+    g.ring_table = C->ring_table;
+    g.k_ring = C->k_ring;
+    g.v_ring = C->v_ring;
     return g;
 }
 
@@ -246,6 +275,8 @@ rtp_status window_like(const rtp_layer* L, const rtp_cache* C, const rtp_query* 
     rtp_status s = check_all(L, C, Q);
     if (s) return s;
     if (!out) return fail(RTP_EINVAL, "out is NULL");
+    if (dense && C->k_ring) return fail(RTP_EINVAL, "dense attention needs every key: the cache has a ring");
+    if ((s = check_ring_window(L, C, Q))) return s;
     if (Q->kind == RTP_CHUNK) {
         if (L->dtype != RTP_BF16 || L->head_dim != 128)
             return fail(RTP_EUNSUPPORTED, "chunked %s attention is built for bf16, head_dim 128",
@@ -287,6 +318,21 @@ rtp_status rtp_indexer_append(const rtp_layer* layer, const rtp_cache* cache, co
     return hip_status(rtp::launch_indexer_append(g, cache->k, cache->k_low, w_k, seq_id, pos, n, layer->dtype,
                                                  (hipStream_t)stream),
                       "indexer append launch");
+}
+
+rtp_status rtp_kv_append(const rtp_layer* layer, const rtp_cache* cache, const void* k_new, const void* v_new,
+                         const void* w_k, const int32_t* seq_id, const int32_t* pos, int32_t n, void* stream) {
+    rtp_status s = check_layer(layer);
+    if (s) return s;
+    if ((s = check_cache(cache))) return s;
+    if (n < 0) return fail(RTP_EINVAL, "n %d < 0", n);
+    if (n == 0) return ok();
+    if (!k_new || !v_new || !w_k || !seq_id || !pos) return fail(RTP_EINVAL, "NULL k_new / v_new / w_k / seq_id / pos");
+    if (((uintptr_t)k_new | (uintptr_t)v_new) & 15) return fail(RTP_EINVAL, "k_new / v_new not 16-byte aligned");
+    const rtp::Geo g = make_geo(layer, cache, nullptr);
+    return hip_status(rtp::launch_kv_append(g, k_new, v_new, const_cast<void*>(cache->k), const_cast<void*>(cache->v),
+                                            cache->k_low, w_k, seq_id, pos, n, layer->dtype, (hipStream_t)stream),
+                      "kv append launch");
 }
 
 size_t rtp_topp_select_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {

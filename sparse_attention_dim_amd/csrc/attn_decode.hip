@@ -65,7 +65,7 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ size_t kv_off(const Geo& g, int page, int kvh, int slot, int D) {
-    return (((size_t)page * g.Hkv + kvh) * kBlk + slot) * (size_t)D;
+    return kv_rowidx(g, page, kvh, slot) * (size_t)D;
 }
 
 template <typename T, int D, int NH>
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
         for (int i = 0; i < kItem / 64; ++i) pg[i] = bt[jl[i] >> 8];
 #pragma unroll
         for (int i = 0; i < kItem / 64; ++i)
-            joff[lane + 64 * i] = (uint32_t)(((size_t)pg[i] * g.Hkv + kvh) * kBlk + (jl[i] & 255));
+            joff[lane + 64 * i] = (uint32_t)kv_rowidx(g, pg[i], kvh, jl[i] & 255);
         S st;
         st.init();
         const int sl = (lane % LPK) * EPV;
@@ -352,13 +352,16 @@ __device__ __forceinline__ int win_count(const Geo& g, int pos, int dense, int* 
 
 template <typename T, int D, int NH>
 __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict__ q,
-                                                     const T* __restrict__ kc,
-                                                     const T* __restrict__ vc, float* __restrict__ part,
+                                                     const T* __restrict__ kc_main,
+                                                     const T* __restrict__ vc_main, float* __restrict__ part,
                                                      int nsplit, int split_keys, int dense) {
     using S = Stream<T, D, NH>;
     constexpr int EPV = S::EPV, LPK = S::LPK;
     const int lane = threadIdx.x;
     const int b = blockIdx.y / g.Hkv, kvh = blockIdx.y % g.Hkv;
+    // K/V of this KV head: the paged cache, or the window-only ring
+    const T* __restrict__ kc = g.kv_ring[kvh] ? (const T*)g.k_ring : kc_main;
+    const T* __restrict__ vc = g.kv_ring[kvh] ? (const T*)g.v_ring : vc_main;
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
     const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
@@ -394,7 +397,6 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
     // [v0, v0 + n) are a run of sink positions followed by a run of window
     // positions; each run covers consecutive pages.
     __shared__ int pgs[64];
-    const int32_t* bt = g.block_table + (size_t)b * g.max_blocks;
     const int vS1 = min(v0 + n, ns_end);
     const int pS0 = v0 >> 8;
     const int nPS = vS1 > v0 ? ((vS1 - 1) >> 8) - pS0 + 1 : 0;
@@ -402,8 +404,8 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
     const int jW1 = w_start + (v0 + n) - ns_end;
     const int pW0 = jW0 >> 8;
     const int nPW = jW1 > jW0 ? ((jW1 - 1) >> 8) - pW0 + 1 : 0;
-    if (lane < nPS) pgs[lane] = bt[pS0 + lane];
-    else if (lane < nPS + nPW) pgs[lane] = bt[pW0 + lane - nPS];
+    if (lane < nPS) pgs[lane] = kv_page(g, b, kvh, pS0 + lane);
+    else if (lane < nPS + nPW) pgs[lane] = kv_page(g, b, kvh, pW0 + lane - nPS);
     __syncthreads();
     auto off = [&](int i) {
         const int vi = v0 + i;
@@ -445,12 +447,16 @@ __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
     return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }
 
-__global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc,
-                                                     const bf16_t* __restrict__ vc, float* __restrict__ part,
+__global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __restrict__ q,
+                                                     const bf16_t* __restrict__ kc_main,
+                                                     const bf16_t* __restrict__ vc_main, float* __restrict__ part,
                                                      int nsplit, int split_keys, int dense) {
     constexpr int D = 128;
     const int lane = threadIdx.x, hh = lane >> 5, col = lane & 31;
     const int b = blockIdx.y / g.Hkv, kvh = blockIdx.y % g.Hkv;
+    // K/V of this KV head: the paged cache, or the window-only ring
+    const bf16_t* __restrict__ kc = g.kv_ring[kvh] ? (const bf16_t*)g.k_ring : kc_main;
+    const bf16_t* __restrict__ vc = g.kv_ring[kvh] ? (const bf16_t*)g.v_ring : vc_main;
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
     const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
@@ -471,7 +477,6 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
     // page ids of the split: a run of sink positions, then a run of window positions
     __shared__ int pgs[64];
     __shared__ __align__(16) bf16_t Vt[D * kWVtLd];
-    const int32_t* bt = g.block_table + (size_t)b * g.max_blocks;
     const int vS1 = min(v0 + n, ns_end);
     const int pS0 = v0 >> 8;
     const int nPS = vS1 > v0 ? ((vS1 - 1) >> 8) - pS0 + 1 : 0;
@@ -479,8 +484,8 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
     const int jW1 = w_start + (v0 + n) - ns_end;
     const int pW0 = jW0 >> 8;
     const int nPW = jW1 > jW0 ? ((jW1 - 1) >> 8) - pW0 + 1 : 0;
-    if (lane < nPS) pgs[lane] = bt[pS0 + lane];
-    else if (lane < nPS + nPW) pgs[lane] = bt[pW0 + lane - nPS];
+    if (lane < nPS) pgs[lane] = kv_page(g, b, kvh, pS0 + lane);
+    else if (lane < nPS + nPW) pgs[lane] = kv_page(g, b, kvh, pW0 + lane - nPS);
     __syncthreads();
     auto off = [&](int i) {
         const int vi = v0 + i;

@@ -80,14 +80,17 @@ __device__ __forceinline__ TileRange tile_range(const Geo& g, int p_min, int p_m
 
 // grid (ceil(n_tok / kBM), n_heads): heads[] lists the query heads to compute.
 __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restrict__ q,
-                                                    const bf16_t* __restrict__ kc,
-                                                    const bf16_t* __restrict__ vc, bf16_t* __restrict__ out,
+                                                    const bf16_t* __restrict__ kc_main,
+                                                    const bf16_t* __restrict__ vc_main, bf16_t* __restrict__ out,
                                                     int dense) {
     __shared__ __attribute__((aligned(16))) bf16_t Ks[kBN * kKsLd];
     __shared__ __attribute__((aligned(16))) bf16_t Vs[kBN * kVsLd];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int hq = g.hlist[blockIdx.y];
     const int kvh = hq / g.group;
+    // K/V of this KV head: the paged cache, or the window-only ring
+    const bf16_t* __restrict__ kc = g.kv_ring[kvh] ? (const bf16_t*)g.k_ring : kc_main;
+    const bf16_t* __restrict__ vc = g.kv_ring[kvh] ? (const bf16_t*)g.v_ring : vc_main;
     const int t0 = blockIdx.x * kBM;
     const int n_valid = min(kBM, g.n_tok - t0);
     const int p_min = g.pos0 + t0, p_max = g.pos0 + t0 + n_valid - 1;
@@ -97,7 +100,6 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
     const bool qok = t < g.n_tok;
     const int pq = g.pos0 + t;                       // its position
     const float sc = g.attn_scale * kLog2e;
-    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     // positions of the wave's 32 queries (all of them valid: wave_full)
     const int wt0 = t0 + wid * 32;
     const bool wave_full = wt0 + 31 < g.n_tok;
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void k_fa_prefill(Geo g, const bf16_t* __restr
     // K and V tile starts (the tile is one contiguous run of a page)
     auto tile_base = [&](int it) {
         const int k0 = tile_key0(it);
-        return (((size_t)bt[k0 >> 8] * g.Hkv + kvh) * kBlk + (k0 & 255)) * kD;
+        return kv_rowidx(g, kv_page(g, g.seq, kvh, k0 >> 8), kvh, k0 & 255) * kD;
     };
     uint4 kk0, kk1, kk2, kk3, vv0, vv1, vv2, vv3;
 #define RTP_LOAD_TILE(b)                                                            \

@@ -186,9 +186,10 @@ __device__ __forceinline__ uint32_t bitmap_prefix(const uint32_t* bm, uint32_t* 
     return (uint32_t)tot;
 }
 
-// K/V row number (page * Hkv + kv head) * 256 + slot of a key
+// K/V row number (page * pool heads + slot of the kv head) * 256 + slot of a key
 __device__ __forceinline__ uint32_t kv_row(const Geo& g, const int32_t* bt, int kvh, uint32_t key) {
-    return ((uint32_t)bt[key >> 8] * (uint32_t)g.Hkv + (uint32_t)kvh) * (uint32_t)kBlk + (key & 255u);
+    return ((uint32_t)bt[key >> 8] * (uint32_t)g.pool_heads + (uint32_t)g.kv_slot[kvh]) * (uint32_t)kBlk +
+           (key & 255u);
 }
 
 __global__ void k_sp_reset(uint32_t* ctr) {

@@ -41,7 +41,32 @@ struct Geo {
     int flags;                    // RTP_FLAG_* of the layer
     const int32_t* block_table;
     const int32_t* seq_lens;
+    // KV layout.  k/v pages hold pool_heads KV heads (Hkv, or only the KV
+    // heads that serve a retrieval head when a window-only ring holds the
+    // rest); KV head g sits at slot kv_slot[g] of its pool, in the ring pool
+    // (ring_heads per page, pages from ring_table) when kv_ring[g].
+    int pool_heads, ring_heads, ring_pages;
+    uint8_t kv_slot[256];
+    uint8_t kv_ring[256];
+    const int32_t* ring_table;    // [batch][ring_pages]
+    const void* k_ring;
+    const void* v_ring;
 };
+
+// Physical page of logical page lp (positions 256 lp ...) of sequence b for
+// KV head g: the block table, or for a ring head entry 0 (positions 0..255,
+// kept for the sinks) and entries 1..ring_pages-1 in rotation.
+__device__ __forceinline__ int kv_page(const Geo& g, int b, int kvh, int lp) {
+    if (g.kv_ring[kvh]) {
+        const int e = lp == 0 ? 0 : 1 + (lp - 1) % (g.ring_pages - 1);
+        return g.ring_table[(size_t)b * g.ring_pages + e];
+    }
+    return g.block_table[(size_t)b * g.max_blocks + lp];
+}
+// K/V row number (in units of D elements) of slot `slot` of `page` for KV head g.
+__device__ __forceinline__ size_t kv_rowidx(const Geo& g, int page, int kvh, int slot) {
+    return ((size_t)page * (g.kv_ring[kvh] ? g.ring_heads : g.pool_heads) + g.kv_slot[kvh]) * 256 + slot;
+}
 
 // Position of query token t (keys 0..pos visible) and its sequence.
 __device__ __forceinline__ int row_seq(const Geo& g, int t) { return g.kind == 0 ? t : g.seq; }
@@ -98,6 +123,11 @@ struct SelOut {
 hipError_t launch_indexer_append(const Geo& g, const void* k, void* k_low, const void* w_k,
                                  const int32_t* seq_id, const int32_t* pos, int n, int dtype,
                                  hipStream_t s);
+// K and V of n new tokens ([n][Hkv][D]) into their pages (the ring for the
+// ring heads) and their indexer keys, in one launch.
+hipError_t launch_kv_append(const Geo& g, const void* k_new, const void* v_new, void* k, void* v, void* k_low,
+                            const void* w_k, const int32_t* seq_id, const int32_t* pos, int n, int dtype,
+                            hipStream_t s);
 
 // Selection of rows [row0, row0 + ws.rows) of the call, all of it or one stage.
 enum SelStage {
