@@ -70,6 +70,10 @@ def lib():
             L.orc_f32_to_bf16.restype = ctypes.c_uint16
             L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
             L.orc_bf16_to_f32.restype = f32
+            L.orc_fp8e4m3_to_f32.argtypes = [ctypes.c_uint8]
+            L.orc_fp8e4m3_to_f32.restype = f32
+            L.orc_fp8_dequant.argtypes = [P, i64, f32, P]
+            L.orc_fp8_dequant.restype = None
             _lib = L
     return _lib
 
@@ -160,6 +164,19 @@ def window_set(pos: int, window: int, sinks: int) -> np.ndarray:
     out = np.empty(pos + 1, np.int32)
     n = lib().orc_window_set(pos, window, sinks, _p(out))
     return out[:n].copy()
+
+
+def fp8_to_f32(code: int) -> float:
+    """One FP8 E4M3 code as fp32."""
+    return float(lib().orc_fp8e4m3_to_f32(int(code)))
+
+
+def fp8_dequant(codes: np.ndarray, scale: float) -> np.ndarray:
+    """fp32 values of FP8 E4M3 codes (uint8) times a scale (one fp32 rounding)."""
+    c = np.ascontiguousarray(codes, np.uint8)
+    out = np.empty(c.shape, np.float32)
+    lib().orc_fp8_dequant(_p(c), c.size, float(np.float32(scale)), _p(out))
+    return out
 
 
 def f32_to_bf16(x: float) -> int:

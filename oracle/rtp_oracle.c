@@ -69,6 +69,33 @@ uint16_t orc_f32_to_bf16(float f)
     return (uint16_t)upper;
 }
 
+/*
+ * FP8 E4M3 (OCP "e4m3fn": 1 sign bit, 4 exponent bits with bias 7, 3
+ * mantissa bits, no infinities, S.1111.111 is NaN) to fp32, exact.  K and V
+ * stored in this format carry one fp32 scale each; a stored code c stands for
+ * fl32(f32(c) * scale), the product rounded once to nearest even.
+ */
+float orc_fp8e4m3_to_f32(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    float v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexpf((float)m, -9);                 /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexpf((float)(8 + m), e - 10);        /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+void orc_fp8_dequant(const uint8_t *c, int64_t n, float scale, float *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = orc_fp8e4m3_to_f32(c[i]) * scale;
+}
+
 /* ------------------------------------------------------------------ */
 /* Step 1/2: low-rank indexer projection of keys (on append) and queries */
 /* ------------------------------------------------------------------ */

@@ -41,6 +41,37 @@ def test_bf16_rne(x, bits):
 
 
 # --------------------------------------------------------------------------
+# FP8 E4M3 decoding (the FP8 K/V variant)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x80, -0.0), (0x38, 1.0), (0xB8, -1.0), (0x3C, 1.5), (0x40, 2.0),
+    (0x7E, 448.0),                       # largest finite
+    (0x08, 2.0 ** -6),                   # smallest normal
+    (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9),   # subnormals
+    (0x39, 1.125), (0x47, 3.75),
+])
+def test_fp8_closed_forms(code, value):
+    v = oracle.fp8_to_f32(code)
+    assert v == value and math.copysign(1.0, v) == math.copysign(1.0, value)
+
+
+def test_fp8_matches_torch_e4m3fn_table():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    got = oracle.fp8_dequant(codes, 1.0)
+    nan = np.isnan(ref)
+    assert list(np.flatnonzero(nan)) == [0x7F, 0xFF]
+    assert np.all(np.isnan(got[nan]))
+    np.testing.assert_array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+    # the scale multiplies once, rounded to fp32
+    sc = np.float32(0.0137)
+    np.testing.assert_array_equal(oracle.fp8_dequant(codes[~nan], float(sc)),
+                                  (ref[~nan] * sc).astype(np.float32))
+
+
+# --------------------------------------------------------------------------
 # projection: fp32 FMA chain over d ascending, one bf16 rounding
 # --------------------------------------------------------------------------
 
