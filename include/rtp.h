@@ -104,6 +104,14 @@ typedef struct rtp_layer {
     int32_t k_max;                  /* top-p budget cap: a row keeps at most the first k_max keys of its
                                        rank order (a bound on the CSR capacity); 0 = no cap */
     int32_t flags;                  /* RTP_FLAG_* */
+    int32_t kv_fp8;                 /* 1: K and V (cache pages, ring, rtp_kv_append input) are FP8 E4M3
+                                       codes (OCP: bias 7, no infinities), code c standing for
+                                       fl32(f32(c) * k_scale) (V: v_scale); Q, W and outputs stay in
+                                       dtype, which must be RTP_BF16.  Supported by the decode calls,
+                                       rtp_indexer_append, rtp_kv_append and rtp_sparse_attn_prefill;
+                                       chunked window / dense attention return RTP_EUNSUPPORTED.
+                                       0: K/V in dtype */
+    float k_scale, v_scale;         /* FP8 scales (> 0, finite); ignored when kv_fp8 == 0 */
 } rtp_layer;
 
 /* [host] struct of device pointers: the paged KV cache of a batch. */

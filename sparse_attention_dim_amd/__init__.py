@@ -53,7 +53,8 @@ class Layer(ctypes.Structure):
                 ("num_ret", ctypes.c_int32), ("ret_heads", ctypes.c_int32 * RTP_MAX_RET),
                 ("window", ctypes.c_int32), ("num_sinks", ctypes.c_int32),
                 ("attn_scale", ctypes.c_float), ("idx_scale", ctypes.c_float),
-                ("k_max", ctypes.c_int32), ("flags", ctypes.c_int32)]
+                ("k_max", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("kv_fp8", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 class Cache(ctypes.Structure):
@@ -169,7 +170,7 @@ def _stream(stream) -> int | None:
 
 def make_layer(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int, ret_heads,
                window: int, num_sinks: int, attn_scale: float, idx_scale: float, k_max: int = 0,
-               flags: int = 0) -> Layer:
+               flags: int = 0, kv_fp8: int = 0, k_scale: float = 1.0, v_scale: float = 1.0) -> Layer:
     L = Layer()
     L.num_q_heads, L.num_kv_heads, L.head_dim, L.dtype = num_q_heads, num_kv_heads, head_dim, dtype
     rh = list(ret_heads)
@@ -179,6 +180,7 @@ def make_layer(num_q_heads: int, num_kv_heads: int, head_dim: int, dtype: int, r
     L.window, L.num_sinks = window, num_sinks
     L.attn_scale, L.idx_scale = attn_scale, idx_scale
     L.k_max, L.flags = k_max, flags
+    L.kv_fp8, L.k_scale, L.v_scale = kv_fp8, k_scale, v_scale
     return L
 
 

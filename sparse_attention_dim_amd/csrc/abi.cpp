@@ -56,8 +56,11 @@ constexpr int kDenseSplit = 1024;         // keys per workgroup, dense decode
 
 int win_split(const rtp_layer* L, int dense) {
     if (dense) return kDenseSplit;
-    return (L->dtype == RTP_BF16 && L->head_dim == 128) ? kWinSplitMfma : kWinSplit;
+    return (L->dtype == RTP_BF16 && L->head_dim == 128 && !L->kv_fp8) ? kWinSplitMfma : kWinSplit;
 }
+
+// bf16 D = 128 chunks whose K/V are bf16 run on the MFMA tile kernels
+bool mfma_chunk(const rtp_layer* L) { return L->dtype == RTP_BF16 && L->head_dim == 128 && !L->kv_fp8; }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -84,6 +87,12 @@ rtp_status check_layer(const rtp_layer* L) {
     if (!(L->idx_scale > 0.0f) || !std::isfinite(L->idx_scale)) return fail(RTP_EINVAL, "idx_scale");
     if (L->k_max < 0) return fail(RTP_EINVAL, "k_max %d < 0", L->k_max);
     if (L->flags & ~RTP_FLAG_EXACT_MASS) return fail(RTP_EINVAL, "unknown flags 0x%x", L->flags);
+    if (L->kv_fp8 != 0 && L->kv_fp8 != 1) return fail(RTP_EINVAL, "kv_fp8 %d", L->kv_fp8);
+    if (L->kv_fp8) {
+        if (L->dtype != RTP_BF16) return fail(RTP_EUNSUPPORTED, "FP8 K/V needs dtype RTP_BF16");
+        if (!(L->k_scale > 0.0f) || !std::isfinite(L->k_scale) || !(L->v_scale > 0.0f) || !std::isfinite(L->v_scale))
+            return fail(RTP_EINVAL, "FP8 scales must be finite and > 0");
+    }
     return RTP_OK;
 }
 
@@ -155,6 +164,9 @@ rtp::Geo make_geo(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) {
     g.sel_k = 0;
     g.k_max = L->k_max;
     g.flags = L->flags;
+    g.kv_fp8 = L->kv_fp8;
+    g.k_scale = L->kv_fp8 ? L->k_scale : 1.0f;
+    g.v_scale = L->kv_fp8 ? L->v_scale : 1.0f;
     if (Q) {
         g.kind = Q->kind;
         g.seq = Q->seq;
@@ -278,8 +290,8 @@ rtp_status window_like(const rtp_layer* L, const rtp_cache* C, const rtp_query* 
     if (dense && C->k_ring) return fail(RTP_EINVAL, "dense attention needs every key: the cache has a ring");
     if ((s = check_ring_window(L, C, Q))) return s;
     if (Q->kind == RTP_CHUNK) {
-        if (L->dtype != RTP_BF16 || L->head_dim != 128)
-            return fail(RTP_EUNSUPPORTED, "chunked %s attention is built for bf16, head_dim 128",
+        if (!mfma_chunk(L))
+            return fail(RTP_EUNSUPPORTED, "chunked %s attention is built for bf16 K/V, head_dim 128",
                         dense ? "dense" : "window");
         rtp::Geo g = make_geo(L, C, Q);
         g.n_hlist = 0;
@@ -506,7 +518,7 @@ rtp_status rtp_indexer_scores(const rtp_layer* layer, const rtp_cache* cache, co
 size_t rtp_sparse_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                                  int64_t capacity) {
     if (check_all(layer, cache, query) || capacity < 0) return 0;
-    if (query->kind == RTP_CHUNK && layer->dtype == RTP_BF16 && layer->head_dim == 128)
+    if (query->kind == RTP_CHUNK && mfma_chunk(layer))
         return std::max<size_t>(256, rtp::sparse_prefill_ws_bytes(query->n_tok, layer->num_ret,
                                                                   query->pos0 + query->n_tok));
     const int64_t rows = (int64_t)query->n_tok * layer->num_ret;
@@ -549,7 +561,7 @@ rtp_status rtp_sparse_attn_prefill(const rtp_layer* layer, const rtp_cache* cach
     const size_t need = rtp_sparse_attn_workspace(layer, cache, query, sel->capacity);
     if (!workspace || workspace_bytes < need)
         return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-    if (layer->dtype == RTP_BF16 && layer->head_dim == 128) {
+    if (mfma_chunk(layer)) {
         const rtp::Geo g = make_geo(layer, cache, query);
         return hip_status(rtp::launch_sparse_prefill(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
                                                      sel->capacity, sel->status, out, workspace,

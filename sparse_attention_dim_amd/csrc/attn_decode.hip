@@ -46,6 +46,16 @@ struct Pack<float> {
         f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
     }
 };
+template <>
+struct Pack<fp8e4_t> {              // FP8 K/V codes (their scales are applied outside)
+    static constexpr int N = 16;
+    __device__ static __forceinline__ void unpack(const uint4& a, float* f) {
+        fp8x4_to_f32(a.x, f);
+        fp8x4_to_f32(a.y, f + 4);
+        fp8x4_to_f32(a.z, f + 8);
+        fp8x4_to_f32(a.w, f + 12);
+    }
+};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -190,15 +200,15 @@ struct Stream {
 constexpr int kItem = kSparseItem;
 static_assert(kItem % 64 == 0, "whole wavefronts of selected keys per item");
 
-template <typename T, int D>
+template <typename T, typename TKV, int D>
 __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restrict__ q,
-                                                        const T* __restrict__ kc,
-                                                        const T* __restrict__ vc,
+                                                        const TKV* __restrict__ kc,
+                                                        const TKV* __restrict__ vc,
                                                         const int64_t* __restrict__ row_ptr,
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ status,
                                                         AttnWs ws, int row0, int rows) {
-    using S = Stream<T, D, 1>;
+    using S = Stream<TKV, D, 1>;
     if (*status != 0) return;
     const int lane = threadIdx.x;
     extern __shared__ int64_t dyn[];
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
     if (blockIdx.x == 0)
         for (int r = lane; r <= rows; r += 64) ws.item_start[r] = istart[r];
     const int total = istart[rows];
-    const float sc = g.attn_scale * kLog2e;
+    const float sc = g.attn_scale * kLog2e * g.k_scale;    // the K scale of FP8 codes folded into q
     constexpr int EPV = S::EPV, LPK = S::LPK;
 
     for (int item = blockIdx.x; item < total; item += gridDim.x) {
@@ -281,7 +291,7 @@ constexpr int kMaxParts = 4096;   // partial weights kept in LDS; more are recom
 
 // Merge `n` partial results (stride D + 2: output[D], max, sum) in order.
 template <typename T, int D>
-__device__ void combine_parts(const float* __restrict__ base, int n, T* __restrict__ o, float* wsh) {
+__device__ void combine_parts(const float* __restrict__ base, int n, T* __restrict__ o, float* wsh, float post) {
     const int tid = threadIdx.x;
     __shared__ float red[4];
     float mx = -INFINITY;
@@ -310,7 +320,7 @@ __device__ void combine_parts(const float* __restrict__ base, int n, T* __restri
             const float w = i < kMaxParts ? wsh[i] : exp2f(base[(size_t)i * (D + 2) + D] - M);
             acc = __builtin_fmaf(base[(size_t)i * (D + 2) + d], w, acc);
         }
-        st<T>(o + d, acc / L);
+        st<T>(o + d, acc / L * post);
     }
 }
 
@@ -329,7 +339,7 @@ __global__ __launch_bounds__(128) void k_sparse_dec_combine(Geo g, const int32_t
         for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
         return;
     }
-    combine_parts<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, wsh);
+    combine_parts<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, wsh, g.v_scale);   // V scale of FP8 codes
 }
 
 // ---------------------------------------------------------------------------
@@ -350,18 +360,18 @@ __device__ __forceinline__ int win_count(const Geo& g, int pos, int dense, int* 
     return ne + (pos - ws + 1);
 }
 
-template <typename T, int D, int NH>
+template <typename T, typename TKV, int D, int NH>
 __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict__ q,
-                                                     const T* __restrict__ kc_main,
-                                                     const T* __restrict__ vc_main, float* __restrict__ part,
+                                                     const TKV* __restrict__ kc_main,
+                                                     const TKV* __restrict__ vc_main, float* __restrict__ part,
                                                      int nsplit, int split_keys, int dense) {
-    using S = Stream<T, D, NH>;
+    using S = Stream<TKV, D, NH>;
     constexpr int EPV = S::EPV, LPK = S::LPK;
     const int lane = threadIdx.x;
     const int b = blockIdx.y / g.Hkv, kvh = blockIdx.y % g.Hkv;
     // K/V of this KV head: the paged cache, or the window-only ring
-    const T* __restrict__ kc = g.kv_ring[kvh] ? (const T*)g.k_ring : kc_main;
-    const T* __restrict__ vc = g.kv_ring[kvh] ? (const T*)g.v_ring : vc_main;
+    const TKV* __restrict__ kc = g.kv_ring[kvh] ? (const TKV*)g.k_ring : kc_main;
+    const TKV* __restrict__ vc = g.kv_ring[kvh] ? (const TKV*)g.v_ring : vc_main;
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
     const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
@@ -372,7 +382,7 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
     // slot i serves query head kvh * group + i (group <= NH) if that head
     // needs this kernel; slots are indexed with constants only, so the
     // per-head state stays in registers
-    const float sc = g.attn_scale * kLog2e;
+    const float sc = g.attn_scale * kLog2e * g.k_scale;    // the K scale of FP8 codes folded into q
     const int sl = (lane % LPK) * EPV;
     S st;
     st.init();
@@ -384,7 +394,13 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
         any = any || st.act[i];
         if (st.act[i]) {
             float f[EPV];
-            Pack<T>::unpack(*reinterpret_cast<const uint4*>(q + ((size_t)b * g.Hq + hh) * D + sl), f);
+            const T* qp = q + ((size_t)b * g.Hq + hh) * D + sl;
+            if (Pack<T>::N == EPV) {
+                Pack<T>::unpack(*reinterpret_cast<const uint4*>(qp), f);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) f[e] = ld(qp + e);
+            }
 #pragma unroll
             for (int e = 0; e < EPV; ++e) st.q[i][e] = f[e] * sc;
         } else {
@@ -612,42 +628,42 @@ __global__ __launch_bounds__(128) void k_win_dec_combine(Geo g, const float* __r
     const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
     const int ns = min(nsplit, (n_all + split_keys - 1) / split_keys);
     combine_parts<T, D>(part + ((size_t)b * g.Hq + h) * nsplit * (D + 2), ns,
-                        out + ((size_t)b * g.Hq + h) * D, wsh);
+                        out + ((size_t)b * g.Hq + h) * D, wsh, g.v_scale);
 }
 
-template <typename T, int D>
+template <typename T, typename TKV, int D>
 hipError_t sparse_dec(const Geo& g, const void* q, const void* k, const void* v, const int64_t* row_ptr,
                       const int32_t* idx, const int32_t* status, void* out, const AttnWs& ws, int row0,
                       int rows, hipStream_t s) {
     const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
     const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
-    hipLaunchKernelGGL((k_sparse_dec_part<T, D>), dim3((unsigned)grid), dim3(64), shmem, s, g,
-                       (const T*)q, (const T*)k, (const T*)v, row_ptr, idx, status, ws, row0, rows);
+    hipLaunchKernelGGL((k_sparse_dec_part<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g,
+                       (const T*)q, (const TKV*)k, (const TKV*)v, row_ptr, idx, status, ws, row0, rows);
     hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(128), 0, s, g, status, ws, (T*)out, row0);
     return hipGetLastError();
 }
 
-template <typename T, int D, int NH>
+template <typename T, typename TKV, int D, int NH>
 void win_dec_part(const Geo& g, const void* q, const void* k, const void* v, float* part, int nsplit,
                   int split_keys, int dense, hipStream_t s) {
-    hipLaunchKernelGGL((k_win_dec_part<T, D, NH>), dim3(nsplit, g.batch * g.Hkv), dim3(64), 0, s, g,
-                       (const T*)q, (const T*)k, (const T*)v, part, nsplit, split_keys, dense);
+    hipLaunchKernelGGL((k_win_dec_part<T, TKV, D, NH>), dim3(nsplit, g.batch * g.Hkv), dim3(64), 0, s, g,
+                       (const T*)q, (const TKV*)k, (const TKV*)v, part, nsplit, split_keys, dense);
 }
 
-template <typename T, int D>
+template <typename T, typename TKV, int D>
 hipError_t win_dec(const Geo& g, const void* q, const void* k, const void* v, void* out, float* part,
                    int nsplit, int split_keys, int dense, hipStream_t s) {
-    if (std::is_same<T, bf16_t>::value && D == 128 && g.group <= 32)
+    if (std::is_same<T, bf16_t>::value && std::is_same<TKV, bf16_t>::value && D == 128 && g.group <= 32)
         hipLaunchKernelGGL(k_win_dec_mfma, dim3(nsplit, g.batch * g.Hkv), dim3(64), 0, s, g, (const bf16_t*)q,
                            (const bf16_t*)k, (const bf16_t*)v, part, nsplit, split_keys, dense);
     else if (g.group <= 1)
-        win_dec_part<T, D, 1>(g, q, k, v, part, nsplit, split_keys, dense, s);
+        win_dec_part<T, TKV, D, 1>(g, q, k, v, part, nsplit, split_keys, dense, s);
     else if (g.group <= 2)
-        win_dec_part<T, D, 2>(g, q, k, v, part, nsplit, split_keys, dense, s);
+        win_dec_part<T, TKV, D, 2>(g, q, k, v, part, nsplit, split_keys, dense, s);
     else if (g.group <= 4)
-        win_dec_part<T, D, 4>(g, q, k, v, part, nsplit, split_keys, dense, s);
+        win_dec_part<T, TKV, D, 4>(g, q, k, v, part, nsplit, split_keys, dense, s);
     else
-        win_dec_part<T, D, 8>(g, q, k, v, part, nsplit, split_keys, dense, s);
+        win_dec_part<T, TKV, D, 8>(g, q, k, v, part, nsplit, split_keys, dense, s);
     hipLaunchKernelGGL((k_win_dec_combine<T, D>), dim3(g.Hq, g.batch), dim3(128), 0, s, g, part, (T*)out,
                        nsplit, split_keys, dense);
     return hipGetLastError();
@@ -658,19 +674,24 @@ hipError_t win_dec(const Geo& g, const void* q, const void* k, const void* v, vo
 hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, const void* v,
                                 const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
                                 void* out, const AttnWs& ws, int row0, int rows, int dtype, hipStream_t s) {
-    if (dtype == 0 && g.D == 64) return sparse_dec<float, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
-    if (dtype == 0 && g.D == 128) return sparse_dec<float, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
-    if (dtype == 1 && g.D == 64) return sparse_dec<bf16_t, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
-    return sparse_dec<bf16_t, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (g.kv_fp8 && g.D == 64)
+        return sparse_dec<bf16_t, fp8e4_t, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (g.kv_fp8) return sparse_dec<bf16_t, fp8e4_t, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (dtype == 0 && g.D == 64) return sparse_dec<float, float, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (dtype == 0 && g.D == 128) return sparse_dec<float, float, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    if (dtype == 1 && g.D == 64) return sparse_dec<bf16_t, bf16_t, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+    return sparse_dec<bf16_t, bf16_t, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
 }
 
 hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,
                                 float* part, int nsplit, int split_keys, int dense, int dtype,
                                 hipStream_t s) {
-    if (dtype == 0 && g.D == 64) return win_dec<float, 64>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
-    if (dtype == 0 && g.D == 128) return win_dec<float, 128>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
-    if (dtype == 1 && g.D == 64) return win_dec<bf16_t, 64>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
-    return win_dec<bf16_t, 128>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
+    if (g.kv_fp8 && g.D == 64) return win_dec<bf16_t, fp8e4_t, 64>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
+    if (g.kv_fp8) return win_dec<bf16_t, fp8e4_t, 128>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
+    if (dtype == 0 && g.D == 64) return win_dec<float, float, 64>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
+    if (dtype == 0 && g.D == 128) return win_dec<float, float, 128>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
+    if (dtype == 1 && g.D == 64) return win_dec<bf16_t, bf16_t, 64>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
+    return win_dec<bf16_t, bf16_t, 128>(g, q, k, v, out, part, nsplit, split_keys, dense, s);
 }
 
 }  // namespace rtp

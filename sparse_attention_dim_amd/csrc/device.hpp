@@ -10,8 +10,23 @@ constexpr int kBlk = 256;     // tokens per KV page
 constexpr int kWave = 64;
 
 typedef uint16_t bf16_t;
+struct fp8e4_t {              // FP8 E4M3 (OCP: bias 7, no infinities) storage of K/V
+    uint8_t b;
+};
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// FP8 E4M3 codes to fp32 (exact, hardware conversion): 4 codes of a dword,
+// byte 0 first.
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* f) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    f[0] = lo[0];
+    f[1] = lo[1];
+    f[2] = hi[0];
+    f[3] = hi[1];
+}
+__device__ __forceinline__ float fp82f(uint8_t c) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false)[0]; }
 
 // fp32 -> bf16, round to nearest even (finite inputs)
 __device__ __forceinline__ bf16_t f2bf(float f) {
@@ -23,6 +38,10 @@ __device__ __forceinline__ bf16_t f2bf(float f) {
 template <typename T> __device__ __forceinline__ float ld(const T* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <> __device__ __forceinline__ float ld<fp8e4_t>(const fp8e4_t* p) { return fp82f(p->b); }
+// A stored K element as fp32: FP8 codes stand for fl32(code * scale)
+template <typename T> __device__ __forceinline__ float ldk(const T* p, float) { return ld(p); }
+template <> __device__ __forceinline__ float ldk<fp8e4_t>(const fp8e4_t* p, float scale) { return fp82f(p->b) * scale; }
 
 // Stage n elements (n a multiple of 16 bytes' worth) into LDS as fp32, every
 // thread of a 256-wide group moving 16-byte pieces; falls back to element

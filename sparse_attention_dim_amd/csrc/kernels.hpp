@@ -51,6 +51,8 @@ struct Geo {
     const int32_t* ring_table;    // [batch][ring_pages]
     const void* k_ring;
     const void* v_ring;
+    int kv_fp8;                   // K/V stored as FP8 E4M3 codes
+    float k_scale, v_scale;       // their scales (1 otherwise)
 };
 
 // Physical page of logical page lp (positions 256 lp ...) of sequence b for

@@ -16,7 +16,8 @@ BLOCK = RTP_BLOCK
 
 
 def torch_dtype(dtype: str):
-    return torch.bfloat16 if dtype == "bf16" else torch.float32
+    """Storage type of K/V pages: bf16, fp32, or FP8 E4M3 codes held as uint8."""
+    return {"bf16": torch.bfloat16, "f32": torch.float32, "fp8": torch.uint8}[dtype]
 
 
 def rtp_dtype(dtype: str) -> int:

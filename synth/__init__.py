@@ -429,3 +429,23 @@ def small(i: int, seed: int | None = None) -> Workload:
                               size_dist=("zipf", 1.1, 4, 2048), window=400, sinks=8,
                               name="decode_bf16_ragged_small")
     raise ValueError(i)
+
+
+def fp8_kv(w: "Workload"):
+    """FP8 E4M3 storage of a workload's K and V (the FP8 K/V variant's input):
+    one power-of-two scale per tensor, 2^ceil(log2(max|x| / 448)), and each
+    value x / scale rounded to the nearest E4M3 code (ties to even; no value
+    exceeds 448).  Returns (k_codes, v_codes, k_scale, v_scale), codes as
+    uint8 arrays shaped like w.k[b] / w.v[b]."""
+    import torch
+
+    def quant(arrs):
+        amax = max(float(np.max(np.abs(as_f32(a)))) for a in arrs)
+        scale = float(2.0 ** math.ceil(math.log2(amax / 448.0)))
+        codes = [torch.from_numpy(np.ascontiguousarray(as_f32(a) / np.float32(scale))).to(torch.float8_e4m3fn)
+                 .view(torch.uint8).numpy() for a in arrs]
+        return codes, scale
+
+    kc, ks = quant(w.k)
+    vc, vs = quant(w.v)
+    return kc, vc, ks, vs
