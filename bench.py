@@ -733,11 +733,18 @@ def main():
     rtp.load()
     threads = min(os.cpu_count() or 1, 16)
 
-    if args.only == "prefill128k":
-        print(json.dumps(prefill_leg(3, args.prefill_steps, dense=False)))
-        return
-    if args.only == "prefill1m":
-        print(json.dumps(prefill_leg(4, args.prefill_steps, dense=False)))
+    def calibration_copy():
+        # a copy of known size for the HBM counter runs (1 GiB read, 1 GiB
+        # written): the last dispatch of every run
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    if args.only in ("prefill128k", "prefill1m"):
+        r = prefill_leg(3 if args.only == "prefill128k" else 4, args.prefill_steps, dense=False)
+        calibration_copy()
+        print(json.dumps(r))
         return
 
     def ragged_leg():
@@ -761,9 +768,11 @@ def main():
         return r5
 
     if args.only == "ragged":
-        print(json.dumps(ragged_leg()))
+        r = ragged_leg()
+        calibration_copy()
+        print(json.dumps(r))
         return
-    ragged_res = None if args.no_ragged else ragged_leg()
+    ragged_res = None if (args.no_ragged or args.only) else ragged_leg()
 
     t0 = time.time()
     w = synth.config(2)
@@ -775,15 +784,9 @@ def main():
         head.pop(k, None)
     torch.cuda.empty_cache()
     if args.only == "decode":
+        calibration_copy()
         print(json.dumps(dict(head, roofline=roof, variants=variants)))
         return
-
-    # calibration copy of known size for the HBM counter runs (1 GiB read, 1 GiB write)
-    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
 
     cpu = None
     if not args.no_cpu:
@@ -817,6 +820,7 @@ def main():
                    "1m": prefill_leg(4, args.prefill_steps, cpu_rows=0 if args.no_cpu else 16),
                    "128k_independent_rows": prefill_leg(3, args.prefill_steps, run_mean=1, dense=False)}
 
+    calibration_copy()
     ms = (head["graph_us"] if args.graph else head["us_per_step"]) / 1e3
     res = {
         "metric": METRIC,
