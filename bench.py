@@ -119,23 +119,27 @@ def summarize(kind: str, paths, command: str, out: str):
         }
         json.dump(summary, open(out, "w"), indent=1)
         return
-    # pmc: counters per kernel name, averaged over its dispatches
+    # pmc: counters per kernel name, averaged over its dispatches; each pass's
+    # last dispatch is the 1 GiB calibration copy
     per = {}
+    scale = {"FETCH_SIZE": None, "WRITE_SIZE": None}
     for path in paths:
-        for r in csv.DictReader(open(path)):
+        rows = list(csv.DictReader(open(path)))
+        last = rows[-1]["Dispatch_Id"]
+        for r in rows:
+            if r["Dispatch_Id"] == last:
+                if r["Counter_Name"] in scale:
+                    scale[r["Counter_Name"]] = (1 << 20) / float(r["Counter_Value"])
+                continue
             k = short(r["Kernel_Name"])
             d = per.setdefault(k, {})
             d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
-    scale = {}
-    for cname in ("FETCH_SIZE", "WRITE_SIZE"):
-        calib = [v for k, d in per.items() if "copyBuffer" in k or "elementwise" in k for v in d.get(cname, [])]
-        scale[cname] = (1 << 20) / calib[-1] if calib else None
     lines = ["# rocprofv3 counters per kernel (mean per dispatch)", "", "Command (from the repository root):", "",
              "    " + command, "",
              "HBM bytes: FETCH_SIZE / WRITE_SIZE (KiB) scaled by what each reads for a 1 GiB copy "
              "(the bench's last dispatch): %s." % json.dumps({k: round(v, 4) if v else None for k, v in scale.items()}),
-             "MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs); bf16 MFMA flops = "
-             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", "",
+             "MFMA util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs) (GRBM_GUI_ACTIVE "
+             "is summed over the 8 XCDs); bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512.", "",
              "| kernel | dispatches | MFMA bf16 GFLOP | MFMA util | VALU insts (M) | trans f32 insts (M) | "
              "LDS insts (M) | LDS bank-conflict cycles (M) | HBM read MB | HBM write MB |",
              "|---|---|---|---|---|---|---|---|---|---|"]
@@ -150,7 +154,7 @@ def summarize(kind: str, paths, command: str, out: str):
         n = max(len(v) for v in d.values())
         mops, busy, gui = mean(d, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), mean(d, "SQ_VALU_MFMA_BUSY_CYCLES"), mean(d, "GRBM_GUI_ACTIVE")
         f = lambda x, s=1e6: "%.2f" % (x / s) if x is not None else "-"
-        util = "%.3f" % (busy / (gui * 1024)) if busy is not None and gui else "-"
+        util = "%.3f" % (busy / (gui / 8 * 1024)) if busy is not None and gui else "-"
         rd = mean(d, "FETCH_SIZE")
         wr = mean(d, "WRITE_SIZE")
         lines.append("| %s | %d | %s | %s | %s | %s | %s | %s | %s | %s |" % (
