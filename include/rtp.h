@@ -290,7 +290,9 @@ rtp_status rtp_topk_select(const rtp_layer *layer, const rtp_cache *cache, const
  * was formed: the low 4 bits name the route -- 1 every key, 2 / 3 / 4 the
  * bf16 chunk path's candidate buffer of at most 1024 / 8192 / 16384 keys, 5
  * the chunk path's radix levels over every key tile, 6 the decode path's
- * candidate list, 7 the decode path's cut over the row's scores -- and the
+ * candidate list in LDS, 7 the decode path's cut over the row's scores, 8 the
+ * decode path's candidate list of more than 8192 keys cut from the
+ * workspace -- and the
  * flags 16 (ordered through a bitmap) / 32 (ordered by merging runs), 64 (the
  * normaliser summed exactly over every key), 128 (the cut counted keys: top-k
  * or the k_max cap).  For the decode path and fp32 chunks only when every row

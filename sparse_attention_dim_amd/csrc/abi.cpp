@@ -207,7 +207,7 @@ int64_t max_keys(const rtp_cache* C, const rtp_query* Q) {
 constexpr size_t kScoreBudget = (size_t)4 << 30;   // bytes of scores per row group
 
 struct SelPlan {
-    int rows_total, group_rows, nchunk;
+    int rows_total, group_rows, nchunk, ucap;
     int64_t lpad;
     size_t off_scores, off_cmax, off_qlow, off_chist, off_ccnt, off_st, off_sel, off_chunk, off_ubuf, off_rown, total;
 };
@@ -225,8 +225,9 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     const int64_t keys = max_keys(C, Q);
     p.nchunk = (int)((keys + rtp::kChunk - 1) / rtp::kChunk);
     p.lpad = (int64_t)p.nchunk * rtp::kChunk;
+    p.ucap = (int)std::min<int64_t>(rtp::kCandG, p.lpad);
     const size_t per_row =
-        (size_t)p.lpad * 4 + (size_t)p.nchunk * (4 + 4 + rtp::kCB * 12) + rtp::kCand * 12 + 1024;
+        (size_t)p.lpad * 4 + (size_t)p.nchunk * (4 + 4 + rtp::kCB * 12) + (size_t)p.ucap * 12 + 1024;
     const int64_t by_budget = std::max<int64_t>(1, (int64_t)(kScoreBudget / per_row));
     p.group_rows = (int)std::min<int64_t>({(int64_t)p.rows_total, by_budget, (int64_t)65535});
     const size_t G = (size_t)p.group_rows;
@@ -237,9 +238,9 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     p.off_chist = o; o = align256(o + G * (size_t)p.nchunk * rtp::kCB * 8);
     p.off_ccnt = o; o = align256(o + G * (size_t)p.nchunk * rtp::kCB * 4);
     p.off_st = o; o = align256(o + G * sizeof(rtp::RowState));
-    p.off_sel = o; o = align256(o + G * rtp::kCand * 4);
+    p.off_sel = o; o = align256(o + G * (size_t)p.ucap * 4);
     p.off_chunk = o; o = align256(o + G * (size_t)p.nchunk * 4);
-    p.off_ubuf = o; o = align256(o + G * rtp::kCand * 8);
+    p.off_ubuf = o; o = align256(o + G * (size_t)p.ucap * 8);
     p.off_rown = o; o = align256(o + G * 4);
     p.total = o;
     return p;
@@ -260,6 +261,7 @@ rtp::SelWs sel_ws(const SelPlan& p, char* base) {
     w.row_n = (uint32_t*)(base + p.off_rown);
     w.nchunk = p.nchunk;
     w.rows = p.group_rows;
+    w.ucap = p.ucap;
     return w;
 }
 

@@ -18,6 +18,7 @@ constexpr int kPathLarge = 4;     // chunk path: at most 16384 keys (large-row r
 constexpr int kPathLevel = 5;     // chunk path: radix levels over every key tile (no buffer)
 constexpr int kPathList = 6;      // decode path: candidate list cut in LDS
 constexpr int kPathScan = 7;      // decode path: cut over the row's scores
+constexpr int kPathListG = 8;     // decode path: candidate list cut from the workspace (above 8192 keys)
 constexpr int kPathBitmap = 16;   // chunk path: ordered through a bitmap of the kept range
 constexpr int kPathMerge = 32;    // chunk path: ordered by merging the writers' runs
 constexpr int kPathExactZ = 64;   // the normaliser was summed exactly over every key
@@ -95,7 +96,8 @@ struct RowState {
 
 constexpr int kChunk = 4096;      // keys per workgroup of the scoring pass
 constexpr int kCB = 128;          // mass-histogram bins per chunk (1/4 unit of s (m_c - d) each)
-constexpr int kCand = 8192;       // candidates ranked by one sort
+constexpr int kCand = 8192;       // candidates ranked in LDS
+constexpr int kCandG = 32768;     // candidates ranked from the workspace list (more: a cut over the scores)
 
 // Device workspace of the selection, for `rows` rows of at most Lpad keys.
 struct SelWs {
@@ -105,13 +107,14 @@ struct SelWs {
     uint16_t* qlow;               // [rows][16]
     unsigned long long* chist;    // [rows][nchunk][kCB] chunk mass histograms
     RowState* st;                 // [rows]
-    uint32_t* sel;                // [rows][kCand] selected indices, ascending (mode 1)
-    unsigned long long* ubuf;     // [rows][kCand] U in index order: (score key << 32) | ~index
+    uint32_t* sel;                // [rows][ucap] selected indices, ascending (mode 1)
+    unsigned long long* ubuf;     // [rows][ucap] U in index order: (score key << 32) | ~index
     unsigned* ccnt;               // [rows][nchunk][kCB] cumulative key counts of the chunk bins
     uint32_t* row_n;              // [rows] size of U
     uint32_t* chunk_cnt;          // [rows][nchunk] output offsets per chunk (mode 2)
     int nchunk;
     int rows;                     // rows of this group
+    int ucap;                     // row stride of ubuf / sel: min(kCandG, padded keys)
 };
 
 struct SelOut {

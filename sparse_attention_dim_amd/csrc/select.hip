@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
         ws.st[ri.lrow] = st;
         ws.row_n[ri.lrow] = (uint32_t)nU;                 // at most 2^20
     }
-    if (nU > (unsigned long long)kCand) return;           // the row takes the long path
+    if (nU > (unsigned long long)ws.ucap) return;         // the row takes the long path
     const int bmine = bsel(chunk);
     if (bmine < 0) return;
     const float mc = key_score(ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk]);
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
     __syncthreads();
     unsigned long long tot;
     uint32_t o = s_base + (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
-    unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand;
+    unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * ws.ucap;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
         if (inU & (1u << e))
@@ -570,7 +570,8 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
 // masses; once the cut bucket holds at most 64 keys, one wavefront sorts them
 // in registers (score key descending, index ascending) and finds the first
 // whose cumulative mass reaches the target.
-__device__ Cut list_cut(const unsigned long long* cand, const unsigned long long* wgt, int n, const float* srow,
+template <typename Wt>
+__device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const float* srow,
                         int L, uint32_t klo, uint32_t khi, unsigned long long target, float m, float s, bool unit,
                         unsigned long long* hmb, uint32_t* hcb, unsigned long long* scan_sh, uint32_t* s_u,
                         unsigned long long* s_S, int* s_i, unsigned long long* small_v, unsigned long long* small_w,
@@ -590,7 +591,7 @@ __device__ Cut list_cut(const unsigned long long* cand, const unsigned long long
             const uint32_t key = (uint32_t)(cand[i] >> 32);
             if (key < klo || key > khi) continue;
             const uint32_t bk = (khi - key) >> shift;         // bucket 0 holds the highest keys
-            atomicAdd(&hmb[bk], wgt[i]);
+            atomicAdd(&hmb[bk], wgt(i));
             atomicAdd(&hcb[bk], 1u);
         }
         __syncthreads();
@@ -632,7 +633,7 @@ __device__ Cut list_cut(const unsigned long long* cand, const unsigned long long
                 const uint32_t slot = atomicAdd(s_u, 1u);
                 if (slot < 64u) {
                     small_v[slot] = cand[i];
-                    small_w[slot] = wgt[i];
+                    small_w[slot] = wgt(i);
                 }
             }
             __syncthreads();
@@ -735,27 +736,37 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
     const int nU = (int)ws.row_n[ri.lrow];
     const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
     const auto selected_by = [](const Cut& c, uint32_t key, int j) { return key > c.Tkey || (key == c.Tkey && j <= c.jT); };
-    if (nU <= kCand) {
-        const unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * kCand;
-        for (int i = tid; i < nU; i += kRT) {
-            const unsigned long long e = ub[i];
-            cand[i] = e;
-            wgt[i] = unit ? 1ull : weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
+    if (nU <= ws.ucap) {
+        const unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * ws.ucap;
+        const bool in_lds = nU <= kCand;
+        if (in_lds) {
+            for (int i = tid; i < nU; i += kRT) {
+                const unsigned long long e = ub[i];
+                cand[i] = e;
+                wgt[i] = unit ? 1ull : weight_bin(key_score((uint32_t)(e >> 32)), m, s).w;
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        constexpr int per = kCand / kRT;
+        // the candidate list: in LDS with its exact weights, or (more than
+        // kCand keys) read from the workspace list, weights formed as needed
+        const unsigned long long* cl = in_lds ? cand : ub;
+        const auto w_lds = [&](int i) { return wgt[i]; };
+        const auto w_list = [&](int i) {
+            return unit ? 1ull : weight_bin(key_score((uint32_t)(cl[i] >> 32)), m, s).w;
+        };
+        const int per = (nU + kRT - 1) / kRT;              // contiguous entries per thread, index order
         Cut cut;
-        uint32_t c;
         unsigned long long tot2;
         uint32_t o;
         for (int pass = 0;; ++pass) {
-            cut = list_cut(cand, wgt, nU, srow, ri.L, klo, khi, target, m, s, unit, hmb, hcb, scan_sh, &s_n, &s_S,
-                           &s_i, small_v, small_w, &s_cut);
-            c = 0;
-#pragma unroll
+            cut = in_lds ? list_cut(cl, w_lds, nU, srow, ri.L, klo, khi, target, m, s, unit, hmb, hcb, scan_sh, &s_n,
+                                    &s_S, &s_i, small_v, small_w, &s_cut)
+                         : list_cut(cl, w_list, nU, srow, ri.L, klo, khi, target, m, s, unit, hmb, hcb, scan_sh,
+                                    &s_n, &s_S, &s_i, small_v, small_w, &s_cut);
+            uint32_t c = 0;
             for (int x = 0; x < per; ++x) {
                 const int i = tid * per + x;
-                if (i < nU && selected_by(cut, (uint32_t)(cand[i] >> 32), (int)~(uint32_t)cand[i])) ++c;
+                if (i < nU && selected_by(cut, (uint32_t)(cl[i] >> 32), (int)~(uint32_t)cl[i])) ++c;
             }
             o = (uint32_t)block_excl_scan_u64<kRT>(c, &tot2, scan_sh);
             // the budget cap: a top-p set of more than k_max keys is cut
@@ -763,17 +774,18 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
             if (pass > 0 || unit || g.k_max <= 0 || tot2 <= (unsigned long long)g.k_max) break;
             unit = true;
             target = (unsigned long long)g.k_max;
-            for (int i = tid; i < nU; i += kRT) wgt[i] = 1ull;
-            __syncthreads();
+            if (in_lds) {
+                for (int i = tid; i < nU; i += kRT) wgt[i] = 1ull;
+                __syncthreads();
+            }
         }
         // U is in index order: its selected entries, in order, into the row's list
-        uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
-#pragma unroll
+        uint32_t* sl = ws.sel + (size_t)ri.lrow * ws.ucap;
         for (int x = 0; x < per; ++x) {
             const int i = tid * per + x;
             if (i < nU) {
-                const int j = (int)~(uint32_t)cand[i];
-                if (selected_by(cut, (uint32_t)(cand[i] >> 32), j)) sl[o++] = (uint32_t)j;
+                const int j = (int)~(uint32_t)cl[i];
+                if (selected_by(cut, (uint32_t)(cl[i] >> 32), j)) sl[o++] = (uint32_t)j;
             }
         }
         if (tid == 0) {
@@ -782,7 +794,7 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
             st.jT = cut.jT;
             st.count = (int32_t)tot2;
             st.unit = unit;
-            st.path = kPathList | (unit ? kPathCount : 0);
+            st.path = (in_lds ? kPathList : kPathListG) | (unit ? kPathCount : 0);
             ws.st[ri.lrow] = st;
         }
         return;
@@ -897,7 +909,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
         }
         if (st.mode == 1) {
             if (jbase >= st.count) break;
-            const uint32_t* sl = ws.sel + (size_t)ri.lrow * kCand;
+            const uint32_t* sl = ws.sel + (size_t)ri.lrow * ws.ucap;
             for (int k = tid; k < kChunk && jbase + k < st.count; k += 256)
                 out.idx[rbase + jbase + k] = (int32_t)sl[jbase + k];
             continue;

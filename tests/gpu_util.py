@@ -201,7 +201,7 @@ def path_counts(paths: np.ndarray) -> dict:
     """Histogram of route codes (low 4 bits) and flags over the rows."""
     out = {}
     for name, code in (("all", 1), ("tiny", 2), ("row", 3), ("large", 4), ("level", 5), ("list", 6),
-                       ("scan", 7)):
+                       ("scan", 7), ("list_g", 8)):
         out[name] = int(np.sum((paths & 15) == code))
     for name, bit in (("bitmap", 16), ("merge", 32), ("exact_z", 64), ("count", 128)):
         out[name] = int(np.sum((paths & bit) != 0))

@@ -77,7 +77,7 @@ def _check_rows(w, d, rows, sets, out, k_low_cache, p_override=None):
 def _route_rows(paths, n_ret, per_route, rng):
     """Up to per_route rows of every route and emit order seen in paths."""
     picks = set()
-    for code in range(1, 8):
+    for code in range(1, 9):
         idx = np.flatnonzero((paths & 15) == code)
         picks.update(int(i) for i in rng.choice(idx, min(per_route, len(idx)), replace=False))
     for bit in (16, 32, 64, 128):
@@ -135,6 +135,8 @@ def _decode_case(i, seqs):
     rows = [(t, r) for t in range(w.n_tok) for r in range(w.n_ret)]
     res = _check_rows(w, d, rows, sets, out, {})
     say("   paths of the rows", path_counts(paths))
+    if i == 5:
+        _assert_routes(paths, ["list", "list_g"])
     loc = w.local_heads()
     g = np.random.default_rng(i)
     _check_local(w, out, [(t, int(h)) for t in seqs for h in g.choice(loc, 6, replace=False)])

@@ -185,3 +185,38 @@ def test_large_candidate_set_resolve():
                                    w.row_pos(t), w.idx_scale, 0.999, w.attn_scale)
         ok, _ = band_accept(sets[t * w.n_ret + r], res["order"], res["cum"], 0.999)
         assert ok, (t, r)
+
+
+def test_decode_long_candidate_sets():
+    # flat scores and p = 0.999 on decode rows of 40000, 20000 and 9001 keys:
+    # every key is a candidate, so the rows take the list cut from the
+    # workspace (8192 < U <= 32768) or the cut over the scores (U > 32768);
+    # the set is the lowest indices
+    w = synth.cluster_decode(seed=77, lens=(40000, 20000, 9001), Hq=8, Hkv=2, D=128, n_ret=2, p=0.999,
+                             window=256, sinks=8, rope=1e4, size_dist=("loguniform", 4, 64), name="flat_long")
+    w.w_k = np.zeros_like(w.w_k)
+    say("[gpu] decode long candidate sets")
+    dev = Dev(w)
+    st, rp, sets, paths = dev.select_mode()
+    assert st == 0
+    pc = path_counts(paths)
+    say("   paths", pc)
+    assert pc["scan"] == 2 and pc["list_g"] == 4
+    for t in range(w.n_tok):
+        L = w.row_pos(t) + 1
+        n = int(np.ceil(np.float64(np.float32(0.999)) * L))
+        for r in range(w.n_ret):
+            np.testing.assert_array_equal(sets[t * w.n_ret + r], np.arange(n), err_msg=str((t, r)))
+    # the same rows under the cap and top-k (count cuts on both long routes)
+    st, rp, sets, paths = dev.select_mode(k_max=15000)
+    assert st == 0
+    for t in range(w.n_tok):
+        L = w.row_pos(t) + 1
+        n = min(15000, int(np.ceil(np.float64(np.float32(0.999)) * L)))
+        for r in range(w.n_ret):
+            np.testing.assert_array_equal(sets[t * w.n_ret + r], np.arange(n), err_msg=str(("cap", t, r)))
+    st, rp, sets, paths = dev.select_mode(top_k=12345)
+    for t in range(w.n_tok):
+        L = w.row_pos(t) + 1
+        for r in range(w.n_ret):
+            np.testing.assert_array_equal(sets[t * w.n_ret + r], np.arange(min(12345, L)))
