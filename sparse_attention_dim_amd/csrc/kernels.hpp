@@ -28,15 +28,17 @@ constexpr int kPathCount = 128;   // the cut counted keys (fixed top-k, or the b
 struct Geo {
     int Hq, Hkv, D, group;        // group = Hq / Hkv
     int n_ret;
-    int ret_heads[kMaxRet];
-    int is_ret[256];              // 1 if query head h retrieves (Hq <= 256)
+    // per-head tables as bytes: Geo is passed by value to every kernel, so its
+    // size is kernel-argument traffic on every launch (Hq <= 256)
+    uint8_t ret_heads[kMaxRet];
+    uint8_t is_ret[256];          // 1 if query head h retrieves
     int window, sinks;
     float attn_scale, idx_scale;
     int kind, seq, pos0, n_tok;   // query rows
     int batch, max_blocks;
     int max_seq_len;              // host bound; device lengths are clamped to [1, max_seq_len]
     int n_hlist;                  // heads computed by a prefill attention launch
-    int hlist[256];
+    uint8_t hlist[256];
     int sel_k;                    // selection: fixed top-k budget (0: top-p)
     int k_max;                    // top-p budget cap (0: none)
     int flags;                    // RTP_FLAG_* of the layer
@@ -92,6 +94,7 @@ struct RowState {
     float d_thr;                  // U = keys with score >= d_thr
     int32_t unit;                 // the cut counts keys (fixed top-k, or the budget cap)
     int32_t path;                 // kPath* code of the row
+    int32_t ks;                   // candidate threshold of the plan: U = keys with s (m - d) < ks / 4 (+ margin)
 };
 
 constexpr int kChunk = 4096;      // keys per workgroup of the scoring pass
@@ -111,7 +114,7 @@ struct SelWs {
     unsigned long long* ubuf;     // [rows][ucap] U in index order: (score key << 32) | ~index
     unsigned* ccnt;               // [rows][nchunk][kCB] cumulative key counts of the chunk bins
     uint32_t* row_n;              // [rows] size of U
-    uint32_t* chunk_cnt;          // [rows][nchunk] output offsets per chunk (mode 2)
+    uint32_t* chunk_cnt;          // [rows][nchunk] each chunk's place in U (the plan), then its output offset (mode 2)
     int nchunk;
     int rows;                     // rows of this group
     int ucap;                     // row stride of ubuf / sel: min(kCandG, padded keys)

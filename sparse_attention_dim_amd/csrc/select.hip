@@ -465,22 +465,100 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     return pl;
 }
 
-// Gather.  grid (nchunk, rows), 256 threads: the row's plan, then the chunk's
-// keys of U written at the chunk's place in the row's index-ordered list.
-// The first chunk's workgroup records the plan and the size of U.
-__global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
-                                                    int32_t* __restrict__ status) {
+// Plan: the row's maximum, normaliser, target and candidate threshold, the
+// size of U and each chunk's place in U's index-ordered list (from the chunk
+// bins' cumulative counts, no atomics).  k_sel_plan (grid rows, 256 threads)
+// forms it once per row when the gather grid is larger than the chip holds
+// at once (kGatherResident workgroups); otherwise each gather workgroup forms
+// it.  U: in chunk c, the keys whose chunk bin is at most bsel(c) = ks + 1 - 4 dc
+// (a quarter unit beyond the bins that LB(ks) counts, so U holds every key
+// with s (m - d) < ks / 4 and the cut lies inside it).
+constexpr size_t kGatherResident = 2048;
+
+__device__ __forceinline__ int chunk_bsel(int ks, double dc) {
+    return ks >= kGB ? kCB - 1 : (int)fmin(floor((double)(ks + 1) - (double)kCBPerUnit * dc), (double)(kCB - 1));
+}
+
+// The row's plan and the size of U; the chunk offsets in U from the chunk
+// bins' cumulative counts.  Writes the RowState and the size of U when
+// `write`, every chunk's offset when `offsets`, and returns chunk `mine`'s.
+__device__ void form_plan(const Geo& g, const float* __restrict__ top_p, const RowInfo& ri, const SelWs& ws,
+                          int32_t* __restrict__ status, int mine, bool write, bool offsets, RowState& st,
+                          uint32_t& nU_out, uint32_t& base_out) {
     const int tid = threadIdx.x;
-    const int chunk = blockIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (chunk >= ri.nch) return;
     __shared__ double fch[kMaxChunks], dch[kMaxChunks];
     __shared__ double dred[4];
     __shared__ uint32_t ured[4];
     __shared__ int s_k[2];
     __shared__ unsigned long long scan_sh[256 / 64 + 1];
     __shared__ uint32_t s_base;
-    // the chunk's scores, loaded while the plan is formed
+    const Plan pl = row_plan(g, ri, ws, top_p, fch, dch, dred, ured, s_k);
+    st.m = pl.m;
+    st.L = ri.L;
+    st.Tkey = 0u;
+    st.jT = ri.L;
+    st.target = pl.target;
+    st.d_thr = pl.d_thr;
+    st.ks = pl.ks;
+    nU_out = 0u;
+    base_out = 0u;
+    if (pl.all) {
+        st.mode = 0;
+        st.count = ri.L;
+        st.unit = 0;
+        st.path = kPathAll;
+        if (write && tid == 0) {
+            ws.st[ri.lrow] = st;
+            if (pl.bad) *status = 3;                      // invalid top_p: reported, nothing emitted
+        }
+        return;
+    }
+    st.mode = 1;
+    st.count = 0;
+    st.unit = pl.unit;
+    st.path = 0;
+    const unsigned* ccnt = ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB;
+    unsigned long long cnt_c = 0ull;
+    if (tid < ri.nch) {
+        const int b = chunk_bsel(pl.ks, dch[tid]);
+        cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
+    }
+    unsigned long long nU;
+    const unsigned long long off_c = block_excl_scan_u64<256>(cnt_c, &nU, scan_sh);
+    if (offsets && tid < ri.nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)off_c;
+    if (tid == mine) s_base = (uint32_t)off_c;
+    if (write && tid == 0) {
+        ws.st[ri.lrow] = st;
+        ws.row_n[ri.lrow] = (uint32_t)nU;                 // at most 2^20
+    }
+    nU_out = (uint32_t)nU;
+    if (mine >= 0) {
+        __syncthreads();
+        base_out = s_base;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_sel_plan(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+                                                  int32_t* __restrict__ status) {
+    RowState st;
+    uint32_t nU, base;
+    form_plan(g, top_p, row_info(g, row0, blockIdx.x), ws, status, -1, true, true, st, nU, base);
+}
+
+// Gather.  grid (nchunk, rows), 256 threads: the chunk's keys of U, written
+// at the chunk's place in the row's index-ordered list (rows whose U fits the
+// list).  kPlan: every workgroup forms its row's plan itself (the first
+// chunk's records it), which saves a launch when the grid is resident at
+// once; otherwise the plan comes from k_sel_plan.
+template <bool kPlan>
+__global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+                                                    int32_t* __restrict__ status) {
+    const int tid = threadIdx.x;
+    const int chunk = blockIdx.x;
+    const RowInfo ri = row_info(g, row0, blockIdx.y);
+    if (chunk >= ri.nch) return;
+    __shared__ unsigned long long scan_sh[256 / 64 + 1];
+    // the chunk's scores, loaded while the plan is formed or read
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int j0 = chunk * kChunk + 16 * tid;             // 16 consecutive keys per thread
     float dv[16];
@@ -492,62 +570,20 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
         dv[4 * u + 2] = v.z;
         dv[4 * u + 3] = v.w;
     }
-    const Plan pl = row_plan(g, ri, ws, top_p, fch, dch, dred, ured, s_k);
-    if (pl.all) {
-        if (chunk == 0 && tid == 0) {
-            RowState st;
-            st.m = pl.m;
-            st.L = ri.L;
-            st.Tkey = 0u;
-            st.jT = ri.L;
-            st.target = pl.target;
-            st.d_thr = pl.d_thr;
-            st.mode = 0;
-            st.count = ri.L;
-            st.unit = 0;
-            st.path = kPathAll;
-            ws.st[ri.lrow] = st;
-            if (pl.bad) *status = 3;                      // invalid top_p: reported, nothing emitted
-        }
-        return;
+    RowState st;
+    uint32_t nU, base;
+    if (kPlan) {
+        form_plan(g, top_p, ri, ws, status, chunk, chunk == 0, false, st, nU, base);
+    } else {
+        st = ws.st[ri.lrow];
+        nU = ws.row_n[ri.lrow];
+        base = ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
     }
-    // U: in chunk c, the keys whose chunk bin is at most bsel(c) = ks + 1 - 4 dc
-    // (a quarter unit beyond the bins that LB(ks) counts, so U holds every key
-    // with s (m - d) < ks / 4 and the cut lies inside it).  The cumulative
-    // counts give every chunk's share of U, hence its place in the index-ordered
-    // list, without atomics.
-    const unsigned* ccnt = ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB;
-    const auto bsel = [&](int c) {
-        return pl.ks >= kGB ? kCB - 1 : (int)fmin(floor((double)(pl.ks + 1) - (double)kCBPerUnit * dch[c]), (double)(kCB - 1));
-    };
-    unsigned long long cnt_c = 0ull;
-    if (tid < ri.nch) {
-        const int b = bsel(tid);
-        cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
-    }
-    unsigned long long nU;
-    const unsigned long long off_c = block_excl_scan_u64<256>(cnt_c, &nU, scan_sh);
-    if (tid == chunk) s_base = (uint32_t)off_c;
-    if (chunk == 0 && tid == 0) {
-        RowState st;
-        st.m = pl.m;
-        st.L = ri.L;
-        st.Tkey = 0u;
-        st.jT = ri.L;
-        st.target = pl.target;
-        st.d_thr = pl.d_thr;
-        st.mode = 1;
-        st.count = 0;
-        st.unit = pl.unit;
-        st.path = 0;
-        ws.st[ri.lrow] = st;
-        ws.row_n[ri.lrow] = (uint32_t)nU;                 // at most 2^20
-    }
-    if (nU > (unsigned long long)ws.ucap) return;         // the row takes the long path
-    const int bmine = bsel(chunk);
-    if (bmine < 0) return;
     const float mc = key_score(ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk]);
+    if (st.mode == 0 || nU > (uint32_t)ws.ucap) return;   // every key, or the long path
     const float s = g.idx_scale;
+    const int bmine = chunk_bsel(st.ks, (double)s * ((double)st.m - (double)mc));
+    if (bmine < 0) return;
     uint32_t inU = 0u, c = 0u;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -555,9 +591,8 @@ __global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restri
         inU |= in ? 1u << e : 0u;
         c += in ? 1u : 0u;
     }
-    __syncthreads();
     unsigned long long tot;
-    uint32_t o = s_base + (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
+    uint32_t o = base + (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
     unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * ws.ucap;
 #pragma unroll
     for (int e = 0; e < 16; ++e)
@@ -976,7 +1011,12 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
                                (const bf16_t*)w_q, kl, row0, ws, out);
     }
     if (scores_only || stage == kSelScorePass) return hipGetLastError();
-    hipLaunchKernelGGL(k_sel_gather, grid, dim3(256), 0, s, g, top_p, row0, ws, out.status);
+    if ((size_t)ws.rows * ws.nchunk <= kGatherResident) {
+        hipLaunchKernelGGL(k_sel_gather<true>, grid, dim3(256), 0, s, g, top_p, row0, ws, out.status);
+    } else {
+        hipLaunchKernelGGL(k_sel_plan, dim3(ws.rows), dim3(256), 0, s, g, top_p, row0, ws, out.status);
+        hipLaunchKernelGGL(k_sel_gather<false>, grid, dim3(256), 0, s, g, top_p, row0, ws, out.status);
+    }
     hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
     const dim3 egrid(std::min(ws.nchunk, kEmitWG), ws.rows);
     if (ws.rows <= kRowsInEmit) {
