@@ -292,92 +292,111 @@ __device__ __forceinline__ void split_run(int z, int nsplit, int ntile, int& tb,
 }
 
 // ---------------------------------------------------------------------------
-// P1.  grid (ceil(n_tok / 64), n_ret), 256 threads: q_low of the rows (fixed-
-// order fp32 chain over d, bf16 rounding) and the row maxima of the MFMA
-// scores: m' = max e + delta >= max d (the largest key norm comes from the
-// key-norm pre-pass).  64 rows per workgroup: each key tile read feeds the
-// MFMAs of both 32-row halves.
+// P1.  grid (ceil(n_tok / 256), n_ret, runs), 256 threads: the row maxima of
+// the MFMA scores over one run of key tiles, for 256 rows (eight 32-row
+// slices): every key tile read feeds the eight slices' MFMAs, so the head's
+// indexer keys are streamed once per 256 rows.  The runs' maxima meet in
+// rmaxk by atomicMax (zeroed with q_low by the key-norm pass); the histogram
+// pass forms m' = max e + delta >= max d from them.  The first run writes
+// delta (the largest key norm comes from the key-norm pass) and zeroes the
+// histogram pass's accumulators of its rows.
 // ---------------------------------------------------------------------------
-constexpr int kTR1 = 2 * kTR;
-__global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restrict__ q,
-                                                  const bf16_t* __restrict__ w_q, const bf16_t* __restrict__ k_low,
-                                                  uint16_t* __restrict__ qlow_out, const float* __restrict__ knorm,
-                                                  int nblk, CState* __restrict__ st, HistAcc acc) {
+constexpr int kTRM = 256;                // rows per P1 workgroup
+constexpr int kSlices = kTRM / kTR;
+__global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restrict__ k_low,
+                                                  const uint16_t* __restrict__ qlow, const float* __restrict__ knorm,
+                                                  int nblk, CState* __restrict__ st, uint32_t* __restrict__ rmaxk,
+                                                  HistAcc acc, int nrun) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int r = blockIdx.y, t0 = blockIdx.x * kTR1;
-    const int n_valid = min(kTR1, g.n_tok - t0);
-    // the histogram pass's accumulators of these rows start at zero
-    for (int x = tid; x < n_valid * kHB; x += 256)
-        acc.hist[((size_t)(t0 + x / kHB) * g.n_ret + r) * kHB + x % kHB] = 0.0;
-    for (int hf = 0; hf < 2 && t0 + hf * kTR < g.n_tok; ++hf) {
-        const size_t rt = (size_t)r * acc.nt32 + 2 * blockIdx.x + hf;
-        for (int x = tid; x <= acc.nfw; x += 256) acc.tflags[rt * (acc.nfw + 1) + x] = 0u;
-        if (tid == 0) acc.arrive[rt] = 0u;
+    const int r = blockIdx.y, t0 = blockIdx.x * kTRM, z = blockIdx.z;
+    const int n_valid = min(kTRM, g.n_tok - t0);
+    if (z == 0) {
+        // the histogram pass's accumulators of these rows start at zero
+        for (int x = tid; x < n_valid * kHB; x += 256)
+            acc.hist[((size_t)(t0 + x / kHB) * g.n_ret + r) * kHB + x % kHB] = 0.0;
+        for (int hf = 0; hf < kSlices && t0 + hf * kTR < g.n_tok; ++hf) {
+            const size_t rt = (size_t)r * acc.nt32 + kSlices * blockIdx.x + hf;
+            for (int x = tid; x <= acc.nfw; x += 256) acc.tflags[rt * (acc.nfw + 1) + x] = 0u;
+            if (tid == 0) acc.arrive[rt] = 0u;
+        }
     }
-    const int h_q = g.ret_heads[r];
-    __shared__ __align__(16) float wq[128 * 16];
-    __shared__ float qs[kTR1][16];
-    __shared__ uint32_t rmax[kTR1];
+    __shared__ float qs[kTRM][16];
+    __shared__ uint32_t rmax[kTRM];
     __shared__ uint32_t kmax_bits;
-    stage_f32(w_q + (size_t)r * g.D * 16, wq, g.D * 16, tid);
-    if (tid < kTR1) rmax[tid] = 0u;
+    for (int o = tid; o < kTRM * 16; o += 256) {
+        const int lr = o >> 4, c = o & 15;
+        qs[lr][c] = lr < n_valid ? bf2f(qlow[((size_t)(t0 + lr) * g.n_ret + r) * 16 + c]) : 0.0f;
+    }
+    rmax[tid] = 0u;
     if (tid == 0) kmax_bits = 0u;
     __syncthreads();
-    for (int o = tid; o < kTR1 * 16; o += 256) {
-        const int lr = o >> 4, c = o & 15;
-        float acc = 0.0f;
-        if (lr < n_valid) {
-            const bf16_t* qp = q + ((size_t)(t0 + lr) * g.Hq + h_q) * g.D;
-            for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(bf2f(qp[d]), wq[d * 16 + c], acc);
-        }
-        const bf16_t qb = f2bf(acc);
-        qs[lr][c] = bf2f(qb);
-        if (lr < n_valid) qlow_out[((size_t)(t0 + lr) * g.n_ret + r) * 16 + c] = qb;
+    const int lr = lane & 31, hh = lane >> 5;
+    uint4 qb[kSlices];
+#pragma unroll
+    for (int j = 0; j < kSlices; ++j) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            w4[x] = (__float_as_uint(qs[kTR * j + lr][8 * hh + 2 * x]) >> 16) |
+                    (__float_as_uint(qs[kTR * j + lr][8 * hh + 2 * x + 1]) & 0xFFFF0000u);
+        qb[j] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
-    {
+    const int L_max = g.pos0 + t0 + n_valid;              // keys the group's rows see
+    const int ntile = (L_max + 31) / 32;
+    const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
+    int tb, te;
+    split_run(z, nrun, ntile, tb, te);
+    float mx[kSlices];
+#pragma unroll
+    for (int j = 0; j < kSlices; ++j) mx[j] = -INFINITY;
+    const auto page = [&](int it) { return bt[min(it * 32 + lr, L_max - 1) >> 8]; };
+    const auto load = [&](int it, int pg) {
+        const int kk = min(it * 32 + lr, L_max - 1);
+        return *reinterpret_cast<const uint4*>(k_low + (((size_t)pg * g.n_ret + r) * kBlk + (kk & 255)) * 16 + 8 * hh);
+    };
+    tile_loop<kPreHist>(tb + wid, 4, te, page, load, [&](int it, const uint4& cur) {
+#pragma unroll
+        for (int j = 0; j < kSlices; ++j) {
+            if (kTR * j >= n_valid) continue;                 // (uniform)
+            f32x16_t sc;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sc[i] = 0.0f;
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(cur), as_bf16x8(qb[j]), sc, 0, 0, 0);
+            // tiles below the slice's first row's position hold keys every
+            // row of the slice sees
+            if (it < (g.pos0 + t0 + kTR * j + 1) / 32) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx[j] = fmaxf(mx[j], sc[i]);
+            } else {
+                const int pos = g.pos0 + t0 + kTR * j + lr;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx[j] = fmaxf(mx[j], it * 32 + (i >> 2) * 8 + 4 * hh + (i & 3) <= pos ? sc[i] : -INFINITY);
+            }
+        }
+    });
+#pragma unroll
+    for (int j = 0; j < kSlices; ++j) {
+        const float m = fmaxf(mx[j], __shfl_xor(mx[j], 32));
+        if (hh == 0 && kTR * j + lr < n_valid && m > -INFINITY) atomicMax(&rmax[kTR * j + lr], score_key(m));
+    }
+    if (z == 0) {
         float kn = 0.0f;
         for (int b = tid; b < nblk; b += 256) kn = fmaxf(kn, knorm[(size_t)r * nblk + b]);
         kn = wave_max(kn);
         if (lane == 0) atomicMax(&kmax_bits, __float_as_uint(kn));
     }
     __syncthreads();
-    const int L_max = g.pos0 + t0 + n_valid;
-    const TileCtx ta = tile_ctx_at(g, k_low, qs, t0, min(kTR, n_valid), L_max);
-    const TileCtx tb = tile_ctx_at(g, k_low, qs + kTR, t0 + kTR, max(0, n_valid - kTR), L_max);
-    float ma = -INFINITY, mb = -INFINITY;
-    tile_loop<kPre>(wid, 4, ta.ntile, [&](int it) { return ta.page(it); },
-                    [&](int it, int pg) { return ta.load(it, pg); }, [&](int it, const uint4& cur) {
-        const f32x16_t sa = ta.mfma(cur);
-        const f32x16_t sb = tb.mfma(cur);
-        if (it < ta.nfull) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ma = fmaxf(ma, sa[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ma = fmaxf(ma, ta.key_of(it, i) <= ta.pos ? sa[i] : -INFINITY);
-        }
-        if (it < tb.nfull) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sb[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mb = fmaxf(mb, tb.key_of(it, i) <= tb.pos ? sb[i] : -INFINITY);
-        }
-    });
-    ma = fmaxf(ma, __shfl_xor(ma, 32));
-    mb = fmaxf(mb, __shfl_xor(mb, 32));
-    if (ta.row_ok && ta.hh == 0 && ma > -INFINITY) atomicMax(&rmax[ta.lr], score_key(ma));
-    if (tb.row_ok && tb.hh == 0 && mb > -INFINITY) atomicMax(&rmax[kTR + tb.lr], score_key(mb));
-    __syncthreads();
     if (tid < n_valid) {
-        float qn2 = 0.0f;
-        for (int c = 0; c < 16; ++c) qn2 = __builtin_fmaf(qs[tid][c], qs[tid][c], qn2);
-        // delta exceeds the true deviation bound by a factor >= 8, far more
-        // than the rounding of this sum: m' >= every exact score of the row
-        const float delta = 0x1.0p-16f * sqrtf(qn2) * sqrtf(__uint_as_float(kmax_bits)) * 1.0009765625f;
-        CState* o = st + (size_t)(t0 + tid) * g.n_ret + r;
-        o->mp = key_score(rmax[tid]) + delta;
-        o->delta = delta;
+        if (rmax[tid]) atomicMax(&rmaxk[(size_t)(t0 + tid) * g.n_ret + r], rmax[tid]);
+        if (z == 0) {
+            float qn2 = 0.0f;
+            for (int c = 0; c < 16; ++c) qn2 = __builtin_fmaf(qs[tid][c], qs[tid][c], qn2);
+            // delta exceeds the true deviation bound by a factor >= 8, far more
+            // than the rounding of this sum: m' >= every exact score of the row
+            st[(size_t)(t0 + tid) * g.n_ret + r].delta =
+                0x1.0p-16f * sqrtf(qn2) * sqrtf(__uint_as_float(kmax_bits)) * 1.0009765625f;
+        }
     }
 }
 
@@ -394,6 +413,7 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
 __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restrict__ k_low,
                                                    const float* __restrict__ top_p,
                                                    const uint16_t* __restrict__ qlow, CState* __restrict__ st,
+                                                   const uint32_t* __restrict__ rmaxk,
                                                    unsigned long long* __restrict__ pool_ctr,
                                                    unsigned long long pool_cap, HistAcc acc,
                                                    CRow* __restrict__ rows_out) {
@@ -415,9 +435,10 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     const int r = blockIdx.y, t0 = blockIdx.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     if (tid < kTR) {
-        const CState* c = st + (size_t)(t0 + min(tid, n_valid - 1)) * g.n_ret + r;
-        r_mp[tid] = c->mp;
-        r_delta[tid] = c->delta;
+        // m' = max e + delta from the maximum pass
+        const size_t row = (size_t)(t0 + min(tid, n_valid - 1)) * g.n_ret + r;
+        r_delta[tid] = st[row].delta;
+        r_mp[tid] = key_score(rmaxk[row]) + r_delta[tid];
     }
     for (int x = tid; x < kHB * kTR; x += 256) (&hist[0][0])[x] = 0.0;
     for (int x = tid; x < kProv * kTR; x += 256) (&hcnt[0][0])[x] = 0u;
@@ -436,50 +457,67 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         // Pairs of the open-ended last bin (x >= kProv, weights below e^-10 of
         // the row maximum) are summed in registers: a float sum per tile (16
         // terms, relative error < 2^-20), added to a double per lane.  Only
-        // the pairs below kProv take an LDS atomic of their bin, and a tile
-        // with none of them (no lane maximum below kProv) skips the bins.
+        // the pairs below kProv take an LDS atomic of their bin.  In a full
+        // tile the weights come first, each from one FMA and one exp2:
+        // 2^(e cA + cB) with cA = -sB kW, cB = m' sB kW, whose argument is
+        // within 2^-23 |arg| + 2^-24 s log2(e) (|e| + 2 |m'|) of the exact
+        // s log2(e) (e - m') (the constants' and the FMA's roundings); a
+        // pair with x < kProv weighs more than e^-10 on its own, so a wave
+        // whose lanes all sum below kNearW holds none and skips the bins
+        // and the exact test.
+        const float cA = -sB * kW, cB = mpB * kW;
+        constexpr float kNearW = 4.53e-05f;              // below e^-10 by more than the weights' error
         double* hrow = &hist[0][tc.lr];
         double far = 0.0;
         tile_loop<kPreHist>(tb + wid, 4, te, [&](int it) { return tc.page(it); },
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
-            float mx = sc[0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-            const bool near = __ballot(bin_x(mx, sB, mpB) < (float)kProv) != 0ull;
-            if (near && lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
-            float f = 0.0f;
             if (it < tc.nfull) {
-                if (!near) {
+                float f = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) f += __builtin_amdgcn_exp2f(bin_x(sc[i], sB, mpB) * kW);
-                } else {
+                for (int i = 0; i < 16; ++i) f += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cA, cB));
+                if (__ballot(f >= kNearW) != 0ull) {
+                    float mx = sc[0];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float x = bin_x(sc[i], sB, mpB);
-                        const float w = __builtin_amdgcn_exp2f(x * kW);
-                        const bool nr = x < (float)kProv;
-                        f += nr ? 0.0f : w;
-                        if (nr) {
-                            const int b = bin_of(x);
-                            atomicAdd(&hrow[b * kTR], (double)w);
-                            atomicAdd(&hcnt[b][tc.lr], 1u);
+                    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+                    if (__ballot(bin_x(mx, sB, mpB) < (float)kProv) != 0ull) {
+                        // a pair below kProv: the tile is flagged and binned
+                        if (lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
+                        f = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const float x = bin_x(sc[i], sB, mpB);
+                            const float w = __builtin_amdgcn_exp2f(x * kW);
+                            const bool nr = x < (float)kProv;
+                            f += nr ? 0.0f : w;
+                            if (nr) {
+                                const int b = bin_of(x);
+                                atomicAdd(&hrow[b * kTR], (double)w);
+                                atomicAdd(&hcnt[b][tc.lr], 1u);
+                            }
                         }
                     }
                 }
-            } else {
+                far += (double)f;
+                return;
+            }
+            float mx = sc[0];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float x = bin_x(sc[i], sB, mpB);
-                    const float w = __builtin_amdgcn_exp2f(x * kW);
-                    if (tc.key_of(it, i) <= tc.pos) {
-                        if (x < (float)kProv) {
-                            const int b = bin_of(x);
-                            atomicAdd(&hrow[b * kTR], (double)w);
-                            atomicAdd(&hcnt[b][tc.lr], 1u);
-                        } else {
-                            f += w;
-                        }
+            for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+            if (__ballot(bin_x(mx, sB, mpB) < (float)kProv) != 0ull && lane == 0)
+                atomicOr(&tflag[it >> 5], 1u << (it & 31));
+            float f = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float x = bin_x(sc[i], sB, mpB);
+                const float w = __builtin_amdgcn_exp2f(x * kW);
+                if (tc.key_of(it, i) <= tc.pos) {
+                    if (x < (float)kProv) {
+                        const int b = bin_of(x);
+                        atomicAdd(&hrow[b * kTR], (double)w);
+                        atomicAdd(&hcnt[b][tc.lr], 1u);
+                    } else {
+                        f += w;
                     }
                 }
             }
@@ -844,8 +882,11 @@ __device__ __forceinline__ void list_retry(uint32_t* zrows, unsigned long long* 
 // Certification of a mass cut made with the normaliser Z' = zu + light, where
 // zu is U's exact mass and light the mass of the keys outside U summed from
 // their MFMA scores.  Each such weight carries a relative error of at most
-// eta = s delta / 8 (the score bound, with 1 % to spare) + 2^-16 (the float
-// rounding of its exponent argument, exp2 and the per-tile float sums), so
+// eta = s delta (1/8 + 1/80) + 2^-16: s delta / 8 from the score bound (with
+// 1 % to spare), s delta / 80 from the roundings of the one-FMA exponent
+// argument that scale with |e| and |m'| (both at most 2^16 delta: at most
+// ln2 3 log2(e) 2^-8 s delta < s delta / 85), and 2^-16 from the rest of the
+// argument's rounding, exp2 and the per-tile float sums, so
 // the exact Z lies in [Z' - light eta, Z' + light eta].  The cut (mass P_k
 // through the cut key, P_{k-1} before it) is kept when P_k / Z >= p - band
 // and P_{k-1} / Z < p + band for every Z in that interval; band = 0.9e-6
@@ -853,7 +894,7 @@ __device__ __forceinline__ void list_retry(uint32_t* zrows, unsigned long long* 
 // rounding of the exact weights.
 constexpr double kBandCert = 0.9e-6;
 __device__ __forceinline__ double light_eta(float s, float delta) {
-    return (double)s * (double)delta * (0.125 * 1.01) + 0x1.0p-16;
+    return (double)s * (double)delta * (0.125 * 1.01 + 0.0125) + 0x1.0p-16;
 }
 __device__ __forceinline__ bool mass_certified(double p, unsigned long long zu, unsigned long long light, double eta,
                                                unsigned long long pk, unsigned long long pk1) {
@@ -2100,12 +2141,33 @@ __global__ __launch_bounds__(64) void k_csel_emit(Geo g, const bf16_t* __restric
 
 // Largest squared indexer-key norm of each block of kNormKeys keys of the
 // chunk's sequence, per retrieval head, and the resets of the pool counter and
-// the large-row list.
-// grid (nblk, n_ret), 256 threads.
+// the large-row list; the workgroups past nblk form q_low of 16 rows each.
+// grid (nblk + ceil(n_tok / 16), n_ret), 256 threads.
 __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restrict__ k_low, int n_keys,
                                                     float* __restrict__ knorm, int nblk,
-                                                    unsigned long long* __restrict__ pool_ctr) {
+                                                    unsigned long long* __restrict__ pool_ctr,
+                                                    const bf16_t* __restrict__ q, const bf16_t* __restrict__ w_q,
+                                                    uint16_t* __restrict__ qlow_out, uint32_t* __restrict__ rmaxk) {
     const int r = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+    if (blk >= nblk) {
+        // q_low of 16 rows (fixed-order fp32 chain over d, one bf16 rounding;
+        // the query rows and W_q staged in LDS) and their P1 maxima zeroed
+        __shared__ __align__(16) float wq[128 * 16];
+        __shared__ __align__(16) float qr[16][128];
+        const int t0 = (blk - nblk) * 16, nv = min(16, g.n_tok - t0);
+        stage_f32(w_q + (size_t)r * g.D * 16, wq, g.D * 16, tid);
+        for (int i = 0; i < nv; ++i)
+            stage_f32(q + ((size_t)(t0 + i) * g.Hq + g.ret_heads[r]) * g.D, qr[i], g.D, tid);
+        __syncthreads();
+        const int i = tid >> 4, c = tid & 15;
+        if (i >= nv) return;
+        float acc = 0.0f;
+#pragma unroll 16
+        for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(qr[i][d], wq[d * 16 + c], acc);
+        qlow_out[((size_t)(t0 + i) * g.n_ret + r) * 16 + c] = f2bf(acc);
+        if (c == 0) rmaxk[(size_t)(t0 + i) * g.n_ret + r] = 0u;
+        return;
+    }
     if (blk == 0 && r == 0 && tid < 8) pool_ctr[tid] = 0ull;   // pool; the row lists and their queues
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
     float kn = 0.0f;
@@ -2130,7 +2192,7 @@ __global__ __launch_bounds__(256) void k_csel_knorm(Geo g, const bf16_t* __restr
 }
 
 struct ChunkWs {
-    size_t crow, cst, qlow, counts, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, mrows, zrows, ctr, pool, head;
+    size_t crow, cst, qlow, counts, rmaxk, knorm, tflags, hacc, hcnt, segoff, arrive, lrows, mrows, zrows, ctr, pool, head;
     int nblk, nfw, nsplit;
 };
 
@@ -2142,6 +2204,13 @@ int hist_splits(int n_tok, int n_ret, int n_keys) {
     return std::max(1, std::min({kMaxSplit, (6144 + nwg - 1) / nwg, max_tiles / 1024}));
 }
 
+// key-tile runs per 256-row group of the maximum pass: about two waves of
+// workgroups over the chip, runs of at least ~512 key tiles
+int max_runs(int n_tok, int n_ret, int n_keys) {
+    const int nwg = (n_tok + kTRM - 1) / kTRM * n_ret, max_tiles = (n_keys + 31) / 32;
+    return std::max(1, std::min((2048 + nwg - 1) / nwg, max_tiles / 512));
+}
+
 ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     ChunkWs w;
@@ -2150,7 +2219,8 @@ ChunkWs chunk_ws(int rows, int n_ret, int n_keys) {
     w.cst = w.crow + up((size_t)rows * sizeof(CRow));
     w.qlow = w.cst + up((size_t)rows * sizeof(CState));
     w.counts = w.qlow + up((size_t)rows * 16 * 2);
-    w.knorm = w.counts + up((size_t)rows * 4);
+    w.rmaxk = w.counts + up((size_t)rows * 4);
+    w.knorm = w.rmaxk + up((size_t)rows * 4);
     w.nfw = (n_keys + 1023) / 1024;                     // one bit per 32-key tile
     w.tflags = w.knorm + up((size_t)n_ret * w.nblk * 4);
     const size_t nrt = (size_t)((rows / n_ret + kTR - 1) / kTR) * n_ret;   // row tiles
@@ -2220,12 +2290,15 @@ hipError_t launch_chunk_select(const Geo& g, const void* q, const void* w_q, con
     acc.zrows = (uint32_t*)(base + w.zrows);
     acc.lctr = ctr + 1;
     unsigned long long* zctr = acc.lctr + 4;
-    hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)k_low, n_keys, knorm,
-                       w.nblk, ctr);
-    hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTR1 - 1) / kTR1, g.n_ret), dim3(256), 0, s, g, (const bf16_t*)q,
-                       (const bf16_t*)w_q, (const bf16_t*)k_low, qlow, knorm, w.nblk, cst, acc);
+    uint32_t* rmaxk = (uint32_t*)(base + w.rmaxk);
+    hipLaunchKernelGGL(k_csel_knorm, dim3(w.nblk + (g.n_tok + 15) / 16, g.n_ret), dim3(256), 0, s, g,
+                       (const bf16_t*)k_low, n_keys, knorm, w.nblk, ctr, (const bf16_t*)q, (const bf16_t*)w_q, qlow,
+                       rmaxk);
+    const int nrun = max_runs(g.n_tok, g.n_ret, n_keys);
+    hipLaunchKernelGGL(k_csel_max, dim3((g.n_tok + kTRM - 1) / kTRM, g.n_ret, nrun), dim3(256), 0, s, g,
+                       (const bf16_t*)k_low, qlow, knorm, w.nblk, cst, rmaxk, acc, nrun);
     hipLaunchKernelGGL(k_csel_hist, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, top_p,
-                       qlow, cst, ctr, pool_cap, acc, crow);
+                       qlow, cst, rmaxk, ctr, pool_cap, acc, crow);
     hipLaunchKernelGGL(k_csel_rec, dim3(grid.x, grid.y, acc.nsplit), dim3(256), 0, s, g, (const bf16_t*)k_low, qlow,
                        cst, pool, acc);
     hipLaunchKernelGGL(k_csel_main, grid, dim3(256), 0, s, g, (const bf16_t*)k_low, top_p, qlow, cst, crow, 0, counts,
