@@ -383,13 +383,16 @@ struct Plan {
     int bad;                                          // top_p is NaN or <= 0
 };
 
-__device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const float* __restrict__ top_p,
-                         double* fch, double* dch, double* dred, uint32_t* ured, int* s_k) {
+// NT threads (dred, ured: NT / 64 entries); chist, ccnt, cmax: the row's
+// chunk statistics (device memory or an LDS copy).
+template <int NT>
+__device__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long long* __restrict__ chist,
+                         const unsigned* __restrict__ ccnt, const uint32_t* __restrict__ cmax,
+                         const float* __restrict__ top_p, double* fch, double* dch, double* dred, uint32_t* ured,
+                         int* s_k) {
     const int tid = threadIdx.x;
     const int nch = ri.nch;
     const float s = g.idx_scale;
-    const unsigned long long* chist = ws.chist + (size_t)ri.lrow * ws.nchunk * kCB;
-    const uint32_t* cmax = ws.cmax + (size_t)ri.lrow * ws.nchunk;
     // one round of loads: the chunk's maximum and total mass (one chunk per
     // thread, nch <= 256) and p
     const uint32_t cm = tid < nch ? cmax[tid] : 0u;
@@ -404,7 +407,8 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
         s_k[1] = 16;
     }
     __syncthreads();
-    mk = max(max(ured[0], ured[1]), max(ured[2], ured[3]));
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) mk = max(mk, ured[w]);
     Plan pl;
     pl.m = key_score(mk);
     double z = 0.0;
@@ -418,7 +422,9 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
     if ((tid & 63) == 0) dred[tid >> 6] = z;
     __syncthreads();
-    const double Z = dred[0] + dred[1] + dred[2] + dred[3];
+    double Z = 0.0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) Z += dred[w];
     pl.bad = g.sel_k <= 0 && !(p > 0.0f);
     pl.unit = kc > 0;
     pl.all = pl.bad || (kc > 0 ? kc >= ri.L : !(p < 1.0f));
@@ -433,7 +439,6 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
     // at the 16 values up to the first point that reaches.  16 lanes share one
     // k (chunk bin b counts once (b + 1) / 4 + dc <= k / 4).  A count cut
     // bounds the number of keys the same way, from the cumulative counts.
-    const unsigned* ccnt = ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB;
     const double need = pl.unit ? (double)pl.target : (double)target * (1.0 + 0x1.0p-40) + (double)ri.L + 1.0;
     const int grp = tid >> 4, sub = tid & 15;
     const auto lb_reaches = [&](int k) {
@@ -449,10 +454,10 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const SelWs& ws, const
         for (int o = 8; o > 0; o >>= 1) lb += __shfl_xor(lb, o);
         return sub == 0 && lb >= need;
     };
-    if (lb_reaches(16 * grp + 15)) atomicMin(&s_k[1], grp);
+    if (tid < 256 && lb_reaches(16 * grp + 15)) atomicMin(&s_k[1], grp);
     __syncthreads();
     const int ic = s_k[1];
-    if (ic < 16 && lb_reaches(16 * ic + grp)) atomicMin(&s_k[0], 16 * ic + grp);
+    if (tid < 256 && ic < 16 && lb_reaches(16 * ic + grp)) atomicMin(&s_k[0], 16 * ic + grp);
     __syncthreads();
     const int ks = s_k[0];
     pl.ks = ks;
@@ -492,7 +497,9 @@ __device__ void form_plan(const Geo& g, const float* __restrict__ top_p, const R
     __shared__ int s_k[2];
     __shared__ unsigned long long scan_sh[256 / 64 + 1];
     __shared__ uint32_t s_base;
-    const Plan pl = row_plan(g, ri, ws, top_p, fch, dch, dred, ured, s_k);
+    const Plan pl = row_plan<256>(g, ri, ws.chist + (size_t)ri.lrow * ws.nchunk * kCB,
+                                  ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB, ws.cmax + (size_t)ri.lrow * ws.nchunk,
+                                  top_p, fch, dch, dred, ured, s_k);
     st.m = pl.m;
     st.L = ri.L;
     st.Tkey = 0u;
@@ -745,22 +752,39 @@ __device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const flo
 // Resolve.  One 1024-thread workgroup per row: U with its exact weights, the
 // cut, and the selected indices in order (a list that did not fit: the cut
 // over the row's scores and per-chunk counts).
-__global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) {
+// LDS of a row's cut (kRT threads).
+struct ResolveSm {
+    __align__(16) unsigned long long big[2 * kCand];   // U (index order) and its weights
+    unsigned long long scan_sh[kRT / 64 + 1];
+    unsigned long long hmb[kNR];
+    uint32_t hcb[kNR];
+    uint32_t ccount[kMaxChunks];
+    unsigned long long small_v[64], small_w[64];
+    Cut s_cut;
+    int s_i;
+    uint32_t s_n;
+    unsigned long long s_S;
+};
+
+// The cut of one row with nU keys in U (kRT threads), from its plan st: U
+// copied from the workspace list into LDS, U in the workspace list (weights
+// formed as needed), or the cut over the row's scores; writes the row's state
+// and, for a list, its selected keys.
+__device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, RowState st, int nU,
+                             ResolveSm& sm) {
     const int tid = threadIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.x);
-    RowState st = ws.st[ri.lrow];
-    if (st.mode == 0) return;
-    __shared__ unsigned long long cand[kCand];
-    __shared__ unsigned long long wgt[kCand];
-    __shared__ unsigned long long scan_sh[kRT / 64 + 1];
-    __shared__ unsigned long long hmb[kNR];
-    __shared__ uint32_t hcb[kNR];
-    __shared__ uint32_t ccount[kMaxChunks];
-    __shared__ unsigned long long small_v[64], small_w[64];
-    __shared__ Cut s_cut;
-    __shared__ int s_i;
-    __shared__ uint32_t s_n;
-    __shared__ unsigned long long s_S;
+    unsigned long long* cand = sm.big;
+    unsigned long long* wgt = sm.big + kCand;
+    unsigned long long* scan_sh = sm.scan_sh;
+    unsigned long long* hmb = sm.hmb;
+    uint32_t* hcb = sm.hcb;
+    uint32_t* ccount = sm.ccount;
+    unsigned long long* small_v = sm.small_v;
+    unsigned long long* small_w = sm.small_w;
+    Cut& s_cut = sm.s_cut;
+    int& s_i = sm.s_i;
+    uint32_t& s_n = sm.s_n;
+    unsigned long long& s_S = sm.s_S;
     const float s = g.idx_scale;
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int nch = ri.nch;
@@ -768,7 +792,6 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
     unsigned long long target = st.target;
     bool unit = st.unit != 0;
     const int lane = tid & 63;
-    const int nU = (int)ws.row_n[ri.lrow];
     const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
     const auto selected_by = [](const Cut& c, uint32_t key, int j) { return key > c.Tkey || (key == c.Tkey && j <= c.jT); };
     if (nU <= ws.ucap) {
@@ -866,6 +889,15 @@ __global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) 
         ws.st[ri.lrow] = st;
     }
 }
+
+__global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) {
+    const RowInfo ri = row_info(g, row0, blockIdx.x);
+    const RowState st = ws.st[ri.lrow];
+    if (st.mode == 0) return;
+    __shared__ ResolveSm sm;
+    resolve_body(g, ri, ws, st, (int)ws.row_n[ri.lrow], sm);
+}
+
 
 // ---------------------------------------------------------------------------
 // CSR row pointers of the group's rows and the capacity check (groups of more
