@@ -195,6 +195,31 @@ struct CState {
     unsigned long long light;   // approximate fixed-point mass of the keys outside U
 };
 
+// Coordinates (row tile, retrieval head, run of key tiles) of a workgroup
+// of an (nt, n_ret, runs) grid, remapped so that the workgroups one XCD
+// receives (the dispatcher deals consecutive workgroups out over the 8 XCDs
+// in turn) share one (head, run) and walk its row tiles in order: they stream
+// the same key tiles at about the same time, which that XCD's L2 then serves
+// once (long contexts, where a head's indexer keys overflow what the L2s and
+// the last-level cache keep between passes).  Grids whose size is not a
+// multiple of 8, and short contexts, keep their order.
+constexpr int kXcd = 8;
+constexpr int kXcdMinKeys = 1 << 19;
+struct Blk {
+    int x, y, z;
+};
+__device__ __forceinline__ Blk xcd_blk(const Geo& g) {
+    const int nx = gridDim.x, ny = gridDim.y, n = nx * ny * gridDim.z;
+    Blk b{(int)blockIdx.x, (int)blockIdx.y, (int)blockIdx.z};
+    if (n % kXcd || g.pos0 + g.n_tok < kXcdMinKeys) return b;
+    const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+    const int lam = (lin % kXcd) * (n / kXcd) + lin / kXcd;
+    b.x = lam % nx;
+    b.y = (lam / nx) % ny;
+    b.z = lam / (nx * ny);
+    return b;
+}
+
 // The MFMA tile view of one workgroup: rows t0 .. t0 + 31 of retrieval head r,
 // lane row lr = lane % 32 and half hh = lane / 32; tile `it` covers keys
 // it*32 .. it*32 + 31 (A operand: k_low[key it*32 + lr][8 hh .. 8 hh + 7],
@@ -221,11 +246,11 @@ struct TileCtx {
 };
 
 // rows t0 .. t0 + n_valid - 1 with q_low in qs; keys below L_max are visited
-__device__ TileCtx tile_ctx_at(const Geo& g, const bf16_t* k_low, const float (*qs)[16], int t0, int n_valid,
+__device__ TileCtx tile_ctx_at(const Geo& g, const bf16_t* k_low, const float (*qs)[16], int r, int t0, int n_valid,
                                int L_max) {
     TileCtx c;
     const int lane = threadIdx.x & 63;
-    c.r = blockIdx.y;
+    c.r = r;
     c.t0 = t0;
     c.n_valid = n_valid;
     c.lr = lane & 31;
@@ -247,14 +272,15 @@ __device__ TileCtx tile_ctx_at(const Geo& g, const bf16_t* k_low, const float (*
     return c;
 }
 
-__device__ TileCtx tile_ctx(const Geo& g, const bf16_t* k_low, const float (*qs)[16]) {
-    const int t0 = blockIdx.x * kTR, n_valid = min(kTR, g.n_tok - t0);
-    return tile_ctx_at(g, k_low, qs, t0, n_valid, g.pos0 + t0 + n_valid);
+// the view of row tile rt (rows 32 rt ...) of retrieval head r
+__device__ TileCtx tile_ctx(const Geo& g, const bf16_t* k_low, const float (*qs)[16], int rt, int r) {
+    const int t0 = rt * kTR, n_valid = min(kTR, g.n_tok - t0);
+    return tile_ctx_at(g, k_low, qs, r, t0, n_valid, g.pos0 + t0 + n_valid);
 }
 
-// q_low of the workgroup's rows as floats (zero for rows past the chunk)
-__device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (*qs)[16]) {
-    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
+// q_low of row tile rt of retrieval head r as floats (zero for rows past the chunk)
+__device__ void load_qs(const Geo& g, const uint16_t* __restrict__ qlow, float (*qs)[16], int rt, int r) {
+    const int t0 = rt * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     for (int o = threadIdx.x; o < kTR * 16; o += 256) {
         const int lr = o >> 4, c = o & 15;
@@ -308,14 +334,15 @@ __global__ __launch_bounds__(256) void k_csel_max(Geo g, const bf16_t* __restric
                                                   int nblk, CState* __restrict__ st, uint32_t* __restrict__ rmaxk,
                                                   HistAcc acc, int nrun) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int r = blockIdx.y, t0 = blockIdx.x * kTRM, z = blockIdx.z;
+    const Blk bk = xcd_blk(g);
+    const int r = bk.y, t0 = bk.x * kTRM, z = bk.z;
     const int n_valid = min(kTRM, g.n_tok - t0);
     if (z == 0) {
         // the histogram pass's accumulators of these rows start at zero
         for (int x = tid; x < n_valid * kHB; x += 256)
             acc.hist[((size_t)(t0 + x / kHB) * g.n_ret + r) * kHB + x % kHB] = 0.0;
         for (int hf = 0; hf < kSlices && t0 + hf * kTR < g.n_tok; ++hf) {
-            const size_t rt = (size_t)r * acc.nt32 + kSlices * blockIdx.x + hf;
+            const size_t rt = (size_t)r * acc.nt32 + kSlices * bk.x + hf;
             for (int x = tid; x <= acc.nfw; x += 256) acc.tflags[rt * (acc.nfw + 1) + x] = 0u;
             if (tid == 0) acc.arrive[rt] = 0u;
         }
@@ -431,8 +458,9 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     __shared__ uint32_t r_tot[kTR], r_cz[kTR][kMaxSplit];
     __shared__ unsigned long long r_seg[kTR];
     __shared__ int r_mode[kTR], r_uend[kTR];
-    load_qs(g, qlow, qs);
-    const int r = blockIdx.y, t0 = blockIdx.x * kTR;
+    const Blk bk = xcd_blk(g);
+    load_qs(g, qlow, qs, bk.x, bk.y);
+    const int r = bk.y, t0 = bk.x * kTR;
     const int n_valid = min(kTR, g.n_tok - t0);
     if (tid < kTR) {
         // m' = max e + delta from the maximum pass
@@ -445,11 +473,11 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
     for (int x = tid; x < nfw; x += 256) tflag[x] = 0u;
     if (tid == 0) s_full = 0;
     __syncthreads();
-    const TileCtx tc = tile_ctx(g, k_low, qs);
+    const TileCtx tc = tile_ctx(g, k_low, qs, bk.x, bk.y);
     const float mpB = r_mp[tc.lr] * sB;
     // this workgroup's run of key tiles (none when the row tile has fewer
     // tiles than splits)
-    const int z = blockIdx.z;
+    const int z = bk.z;
     int tb, te;
     split_run(z, acc.nsplit, tc.ntile, tb, te);
     if (te > tb) {
@@ -526,7 +554,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         atomicAdd(&hrow[(kHB - 1) * kTR], far);
     }
     __syncthreads();
-    const size_t rt = (size_t)r * acc.nt32 + blockIdx.x;     // the row tile
+    const size_t rt = (size_t)r * acc.nt32 + bk.x;          // the row tile
     uint32_t* tf = acc.tflags + rt * (nfw + 1);
     for (int x = tid; x < kProv * n_valid; x += 256) {
         const int row = x / kProv, b = x - row * kProv;
@@ -750,7 +778,8 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
                                                   const uint16_t* __restrict__ qlow, CState* __restrict__ st,
                                                   unsigned long long* __restrict__ pool, HistAcc acc) {
     const int tid = threadIdx.x, wid = tid >> 6;
-    const int r = blockIdx.y, t0 = blockIdx.x * kTR, z = blockIdx.z;
+    const Blk bk = xcd_blk(g);
+    const int r = bk.y, t0 = bk.x * kTR, z = bk.z;
     const int n_valid = min(kTR, g.n_tok - t0);
     const int nfw = acc.nfw;
     __shared__ float qs[kTR][16];
@@ -779,15 +808,15 @@ __global__ __launch_bounds__(256) void k_csel_rec(Geo g, const bf16_t* __restric
     }
     __syncthreads();
     if (!s_any) return;
-    load_qs(g, qlow, qs);
+    load_qs(g, qlow, qs, bk.x, bk.y);
     __syncthreads();                                     // qs complete before the tile view reads it
-    const TileCtx tc = tile_ctx(g, k_low, qs);
+    const TileCtx tc = tile_ctx(g, k_low, qs, bk.x, bk.y);
     int tb, te;
     split_run(z, acc.nsplit, tc.ntile, tb, te);
     // The run's key tiles that can hold a key of U (flagged by the histogram
     // pass), listed in LDS; every tile of the run when a row's U reaches past
     // the flagged bins or the list does not fit.
-    const uint32_t* tf = acc.tflags + ((size_t)r * acc.nt32 + blockIdx.x) * (nfw + 1);
+    const uint32_t* tf = acc.tflags + ((size_t)r * acc.nt32 + bk.x) * (nfw + 1);
     int nlist = -1;                                      // -1: every tile of the run
     if (tf[nfw] == 0u) {
         constexpr int kPerT = kFlagWords / 256;          // flag words per thread
@@ -996,9 +1025,9 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
     }
     __syncthreads();
     if (!s_any) return;
-    load_qs(g, qlow, qs);
+    load_qs(g, qlow, qs, blockIdx.x, blockIdx.y);
     __syncthreads();
-    const TileCtx tc = tile_ctx(g, k_low, qs);
+    const TileCtx tc = tile_ctx(g, k_low, qs, blockIdx.x, blockIdx.y);
     const int lr = tc.lr, hh = tc.hh;
     const bool row_ok = tc.row_ok;
     const int pos = tc.pos;
