@@ -45,7 +45,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBM = 64;            // rows per tile
-constexpr int kNT = 256;           // threads of the union and tile kernels
+constexpr int kNT = 256;           // threads of the tile kernel
+constexpr int kNTU = 512;          // threads of the union kernel (its entry scans take kNTU * kUL pieces a round)
 constexpr int kBN = 64;            // union keys per block
 constexpr int kD = 128;
 constexpr int kKsLd = kD + 8;      // K row stride in LDS (bf16)
@@ -103,12 +104,12 @@ __device__ __forceinline__ void set_ranges(int64_t b, int64_t e, Ranges& R) {
 // Visit the tile's entries in the window: every thread takes kUL pieces per
 // round (16-byte loads where idx is 16-byte aligned and the piece lies inside
 // idx_n), and f(row, k[4], valid bits) runs per piece; a piece's keys ascend.
-template <typename F>
+template <int NT, typename F>
 __device__ __forceinline__ void for_pieces(const Ranges& R, const int32_t* __restrict__ idx, int64_t idx_n, F&& f) {
     const int tid = threadIdx.x;
     const int total = R.cp[kBM];
     const bool vec = (reinterpret_cast<uintptr_t>(idx) & 15) == 0;
-    for (int base = 0; base < total; base += kNT * kUL) {
+    for (int base = 0; base < total; base += NT * kUL) {
         // the row whose pieces hold piece c: the last i with cp[i] <= c, by six
         // halving steps run for all kUL pieces together
         int lo[kUL];
@@ -118,12 +119,12 @@ __device__ __forceinline__ void for_pieces(const Ranges& R, const int32_t* __res
         for (int step = kBM / 2; step > 0; step >>= 1)
 #pragma unroll
             for (int u = 0; u < kUL; ++u)
-                if (R.cp[lo[u] + step] <= base + u * kNT + tid) lo[u] += step;
+                if (R.cp[lo[u] + step] <= base + u * NT + tid) lo[u] += step;
         int k[kUL][4];
         uint32_t vm[kUL];
 #pragma unroll
         for (int u = 0; u < kUL; ++u) {
-            const int c = base + u * kNT + tid;
+            const int c = base + u * NT + tid;
             const int64_t p = R.ra[lo[u]] + 4 * (int64_t)(c - R.cp[lo[u]]);
             const int64_t b = R.rb[lo[u]], e = c < total ? R.re[lo[u]] : 0;
             vm[u] = 0u;
@@ -170,14 +171,15 @@ __device__ __forceinline__ int union_rank(const uint32_t* bm, const uint32_t* wp
 }
 
 // Bitmap popcount prefix: wpre[w] = set bits of words 0..w-1; returns the total.
+template <int NT>
 __device__ __forceinline__ uint32_t bitmap_prefix(const uint32_t* bm, uint32_t* wpre, unsigned long long* scan) {
     const int tid = threadIdx.x;
-    constexpr int per = kWords / kNT;
+    constexpr int per = kWords / NT;
     uint32_t loc = 0;
 #pragma unroll
     for (int k = 0; k < per; ++k) loc += __popc(bm[tid * per + k]);
     unsigned long long tot;
-    uint32_t ex = (uint32_t)block_excl_scan_u64<kNT>(loc, &tot, scan);
+    uint32_t ex = (uint32_t)block_excl_scan_u64<NT>(loc, &tot, scan);
 #pragma unroll
     for (int k = 0; k < per; ++k) {
         wpre[tid * per + k] = ex;
@@ -203,11 +205,11 @@ struct PoolBlock {
     uint32_t mask[kBM][2];
 };
 
-// grid (ntile * nwin, n_ret), kNT threads.  A (tile, window) whose union has
+// grid (ntile * nwin, n_ret), kNTU threads.  A (tile, window) whose union has
 // at most kPoolG groups takes its blocks from the pool (ctr counts the blocks
 // handed out) and writes them whole; otherwise (or when the pool is full) it
 // leaves the bitmap for the tile kernel, which then builds each group itself.
-__global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restrict__ row_ptr, int nwin, int nsplit,
+__global__ __launch_bounds__(kNTU) void k_sp_union(Geo g, const int64_t* __restrict__ row_ptr, int nwin, int nsplit,
                                                   const int32_t* __restrict__ idx, int64_t idx_n,
                                                   const int32_t* __restrict__ status, int64_t* __restrict__ wr,
                                                   uint32_t* __restrict__ tw_n, int32_t* __restrict__ tw_off,
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
     __shared__ __attribute__((aligned(16))) uint32_t bm[kWords];
     __shared__ uint32_t wpre[kWords];
     __shared__ __attribute__((aligned(16))) uint32_t mk[kPoolG * kMB][kBM][2];
-    __shared__ unsigned long long scan[kNT / 64 + 1];
+    __shared__ unsigned long long scan[kNTU / 64 + 1];
     __shared__ int64_t bnd[2][kBM];
     __shared__ int s_base;
     const int tid = threadIdx.x;
@@ -230,9 +232,9 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
     const int kvh = g.ret_heads[r] / g.group;
     const size_t tw = ((size_t)r * ntile + tile) * nwin + win;
     const int32_t* bt = g.block_table + (size_t)g.seq * g.max_blocks;
-    for (int x = tid; x < kWords; x += kNT) bm[x] = 0u;
+    for (int x = tid; x < kWords; x += kNTU) bm[x] = 0u;
     // empty partial results of the tile's rows for this window
-    for (int x = tid; x < kBM * nsplit; x += kNT) {
+    for (int x = tid; x < kBM * nsplit; x += kNTU) {
         const int i = x / nsplit, sp = x - i * nsplit;
         const int t = t0 + i;
         if (t < g.n_tok) {
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
     }
     __syncthreads();
     // the union bitmap
-    for_pieces(R, idx, idx_n, [&](int, const int (&k)[4], uint32_t vm) {
+    for_pieces<kNTU>(R, idx, idx_n, [&](int, const int (&k)[4], uint32_t vm) {
         int a[4];
         uint32_t bit[4];
 #pragma unroll
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
         merged_or(bm, a, bit, vm);
     });
     __syncthreads();
-    const uint32_t nU = bitmap_prefix(bm, wpre, scan);
+    const uint32_t nU = bitmap_prefix<kNTU>(bm, wpre, scan);
     const int nb = (int)((nU + kBN - 1) / kBN);
     if (tid == 0) {
         tw_n[tw] = nU;
@@ -296,18 +298,18 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
         tw_off[tw] = base;
         s_base = base;
     }
-    for (int x = tid; x < kPoolG * kMB * kBM * 2; x += kNT) (&mk[0][0][0])[x] = 0u;
+    for (int x = tid; x < kPoolG * kMB * kBM * 2; x += kNTU) (&mk[0][0][0])[x] = 0u;
     __syncthreads();
     const int base = s_base;
     if (nU == 0) return;
     if (base < 0) {
         uint4* dst = reinterpret_cast<uint4*>(tw_bm + tw * kWords);
-        for (int x = tid; x < kWords / 4; x += kNT) dst[x] = *reinterpret_cast<const uint4*>(&bm[4 * x]);
+        for (int x = tid; x < kWords / 4; x += kNTU) dst[x] = *reinterpret_cast<const uint4*>(&bm[4 * x]);
         return;
     }
     // the blocks: every key's K/V row number, every row's masks
     {
-        constexpr int per = kWords / kNT;
+        constexpr int per = kWords / kNTU;
 #pragma unroll
         for (int k = 0; k < per; ++k) {
             const int wd = tid * per + k;
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
             if (u < nb * kBN) pool[base + (u >> 6)].kvrow[u & 63] = 0u;
         }
     }
-    for_pieces(R, idx, idx_n, [&](int row, const int (&k)[4], uint32_t vm) {
+    for_pieces<kNTU>(R, idx, idx_n, [&](int row, const int (&k)[4], uint32_t vm) {
         int a[4];
         uint32_t bit[4];
 #pragma unroll
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(kNT) void k_sp_union(Geo g, const int64_t* __restri
         merged_or(&mk[0][0][0], a, bit, vm);
     });
     __syncthreads();
-    for (int x = tid; x < nb * kBM * 2; x += kNT) {
+    for (int x = tid; x < nb * kBM * 2; x += kNTU) {
         const int b = x / (kBM * 2), y = x - b * (kBM * 2);
         (&pool[base + b].mask[0][0])[y] = (&mk[b][0][0])[y];
     }
@@ -401,7 +403,7 @@ __device__ void build_group(const Geo& g, S& sm, const int32_t* __restrict__ idx
     }
     __syncthreads();
     const int klo = sm.klo, khi = sm.khi;
-    for_pieces(sm.R, idx, idx_n, [&](int row, const int (&k)[4], uint32_t vm) {
+    for_pieces<kNT>(sm.R, idx, idx_n, [&](int row, const int (&k)[4], uint32_t vm) {
         int a[4];
         uint32_t bit[4];
 #pragma unroll
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(kNT) void k_sp_tile(Geo g, const bf16_t* __restrict
         const uint4* src = reinterpret_cast<const uint4*>(tw_bm + tw * kWords);
         for (int x = tid; x < kWords / 4; x += kNT) *reinterpret_cast<uint4*>(&sm.bm[4 * x]) = src[x];
         __syncthreads();
-        bitmap_prefix(sm.bm, sm.wpre, sm.scan);
+        bitmap_prefix<kNT>(sm.bm, sm.wpre, sm.scan);
         if (tid < kBM) {
             int64_t b = 0, e = 0;
             if (t0 + tid < g.n_tok) {
@@ -738,7 +740,7 @@ hipError_t launch_sparse_prefill(const Geo& g, const void* q, const void* k, con
     PoolBlock* pool = (PoolBlock*)(base + p.off_pool);
     float* part = (float*)(base + p.off_part);
     hipLaunchKernelGGL(k_sp_reset, dim3(1), dim3(64), 0, s, ctr);
-    hipLaunchKernelGGL(k_sp_union, dim3(p.ntile * p.nwin, g.n_ret), dim3(kNT), 0, s, g, row_ptr, p.nwin, p.nsplit,
+    hipLaunchKernelGGL(k_sp_union, dim3(p.ntile * p.nwin, g.n_ret), dim3(kNTU), 0, s, g, row_ptr, p.nwin, p.nsplit,
                        idx, idx_n, status, wr, tw_n, tw_off, tw_bm, ctr, pool, p.pool_blocks, part);
     hipLaunchKernelGGL(k_sp_tile, dim3(p.ntile * p.nwin * p.nsplit, g.n_ret), dim3(kNT), 0, s, g, (const bf16_t*)q,
                        (const bf16_t*)k, (const bf16_t*)v, wr, p.nwin, p.nsplit, idx, idx_n, status, tw_n, tw_off, tw_bm,
