@@ -115,6 +115,7 @@ def summarize(kind: str, paths, command: str, out: str):
             "counters": res,
             "hbm_bytes_per_launch": int(res["FETCH_SIZE"]["score_kernel_bytes"] + res["WRITE_SIZE"]["score_kernel_bytes"]),
             "algorithmic_read_bytes": 8 * 131072 * 6 * 32,
+            "algorithmic_write_bytes": 8 * 131072 * 6 * 4,
             "source_sha256_16": source_hash(SCORE_SRC),
         }
         json.dump(summary, open(out, "w"), indent=1)
@@ -527,12 +528,16 @@ def score_roofline(res, w, steps: int):
     k1.record()
     torch.cuda.synchronize()
     k_ms = k0.elapsed_time(k1) / steps
-    achieved = res["_bytes_klow"] / (k_ms * 1e-3) / 1e9
+    # algorithmic bytes of the call: the indexer keys read (32 B per (row,
+    # key)) and the scores it returns (4 B per (row, key))
+    alg = res["_bytes_klow"] + res["_bytes_klow"] // 8
+    achieved = alg / (k_ms * 1e-3) / 1e9
     del score_bufs
     return {"kernel": "k_sel_score<bf16, scores only> (rtp_indexer_scores, decode)", "bound": "hbm",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(),
-            "algorithmic_bytes": res["_bytes_klow"], "avg_launch_us": round(k_ms * 1e3, 2)}
+            "algorithmic_bytes": alg, "algorithmic_read_bytes": res["_bytes_klow"],
+            "avg_launch_us": round(k_ms * 1e3, 2)}
 
 
 # ---------------------------------------------------------------------------
