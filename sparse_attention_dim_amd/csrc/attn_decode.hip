@@ -522,21 +522,32 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dd][i] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;
-    for (int k0 = 0; k0 < n; k0 += 32) {
-        // this lane's key row: K for the A operand, V for the transposed tile
-        const bool live = k0 + col < n;
-        const size_t ro = off(min(k0 + col, n - 1)) + 8 * hh;
-        uint4 ka[8], va[8];
+    // this lane's key row of a block: K for the A operand, V for the
+    // transposed tile.  The next block's K rows are requested once this
+    // block's S MFMAs have taken theirs, its V rows once this block's V^T
+    // tile is written, so they arrive while this block finishes.
+    uint4 ka[8], va[8];
+    {
+        const size_t ro = off(min(col, n - 1)) + 8 * hh;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(kc + ro + 16 * kk);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) va[kk] = *reinterpret_cast<const uint4*>(vc + ro + 16 * kk);
+    }
+    for (int k0 = 0; k0 < n; k0 += 32) {
+        const bool live = k0 + col < n;
+        const bool more = k0 + 32 < n;
+        const size_t ro_n = off(min(k0 + 32 + col, n - 1)) + 8 * hh;
         f32x16_t s;
 #pragma unroll
         for (int i = 0; i < 16; ++i) s[i] = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kk]), as_bf16x8(qreg[kk]), s, 0, 0, 0);
+        if (more) {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(kc + ro_n + 16 * kk);
+        }
         __syncthreads();                                  // the previous block's V^T reads are done
         // V^T[d][key col]: d = 16 kk + 8 hh + e; rows past the split stored as zeros
 #pragma unroll
@@ -549,6 +560,10 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
                 Vt[d * kWVtLd + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w4[x] & 0xFFFFu));
                 Vt[(d + 1) * kWVtLd + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w4[x] >> 16));
             }
+        }
+        if (more) {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) va[kk] = *reinterpret_cast<const uint4*>(vc + ro_n + 16 * kk);
         }
         // scale, mask, block maximum of this lane's head
         float mt = -INFINITY;
