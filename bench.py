@@ -93,7 +93,7 @@ def summarize(kind: str, paths, command: str, out: str):
         lines = ["# rocprofv3 kernel statistics", "", "Command (from the repository root):", "",
                  "    " + command, "", "| kernel | calls | avg us | min us | max us | total % |",
                  "|---|---|---|---|---|---|"]
-        for r in rows[:30]:
+        for r in rows[:60]:
             lines.append("| %s | %s | %.2f | %.2f | %.2f | %.1f |" % (
                 short(r["Name"])[:70], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
