@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
         // s log2(e) (e - m') (the constants' and the FMA's roundings); a
         // pair with x < kProv weighs more than e^-10 on its own, so a wave
         // whose lanes all sum below kNearW holds none and skips the bins
-        // and the exact test.
+        // and the exact test (the binned loop reuses the weights).
         const float cA = -sB * kW, cB = mpB * kW;
         constexpr float kNearW = 4.53e-05f;              // below e^-10 by more than the weights' error
         double* hrow = &hist[0][tc.lr];
@@ -501,30 +501,32 @@ __global__ __launch_bounds__(256) void k_csel_hist(Geo g, const bf16_t* __restri
                     [&](int it, int pg) { return tc.load(it, pg); }, [&](int it, const uint4& cur) {
             const f32x16_t sc = tc.mfma(cur);
             if (it < tc.nfull) {
+                float w[16];
                 float f = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) f += __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cA, cB));
+                for (int i = 0; i < 16; ++i) {
+                    w[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[i], cA, cB));
+                    f += w[i];
+                }
                 if (__ballot(f >= kNearW) != 0ull) {
-                    float mx = sc[0];
+                    // a lane may hold a pair below kProv: the exact test per
+                    // pair; those pairs take their bins with the weights
+                    // above, the others are summed again without them
+                    f = 0.0f;
+                    bool any = false;
 #pragma unroll
-                    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-                    if (__ballot(bin_x(mx, sB, mpB) < (float)kProv) != 0ull) {
-                        // a pair below kProv: the tile is flagged and binned
-                        if (lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
-                        f = 0.0f;
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const float x = bin_x(sc[i], sB, mpB);
-                            const float w = __builtin_amdgcn_exp2f(x * kW);
-                            const bool nr = x < (float)kProv;
-                            f += nr ? 0.0f : w;
-                            if (nr) {
-                                const int b = bin_of(x);
-                                atomicAdd(&hrow[b * kTR], (double)w);
-                                atomicAdd(&hcnt[b][tc.lr], 1u);
-                            }
+                    for (int i = 0; i < 16; ++i) {
+                        const float x = bin_x(sc[i], sB, mpB);
+                        const bool nr = x < (float)kProv;
+                        any |= nr;
+                        f += nr ? 0.0f : w[i];
+                        if (nr) {
+                            const int b = bin_of(x);
+                            atomicAdd(&hrow[b * kTR], (double)w[i]);
+                            atomicAdd(&hcnt[b][tc.lr], 1u);
                         }
                     }
+                    if (__ballot(any) != 0ull && lane == 0) atomicOr(&tflag[it >> 5], 1u << (it & 31));
                 }
                 far += (double)f;
                 return;
