@@ -450,13 +450,14 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
 // keys: S^T[key][head] = K . Q^T with the K rows straight from memory (each
 // lane one key, 16 bytes per k-step); online softmax per head in-lane (a lane
 // holds 16 of the block's keys of its head, the other half-wave the other 16);
-// O^T[d][head] += V^T . P^T with V^T from a transposed LDS tile and P^T taken
+// O^T[d][head] += V^T . P^T with V^T read by gfx950's transposing LDS loads
+// from the block's row-major V tile (16-byte row stores) and P^T taken
 // straight from the S^T registers (a fixed key permutation matches their
 // layout).  Writes the same partials as k_win_dec_part.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kWVtLd = 32 + 4;     // V^T row stride in LDS (bf16): 8-byte aligned 4-key reads
+constexpr int kWVsLd = 128 + 32;   // V row stride in LDS (bf16), 320 B: the four rows of a transposing load hit disjoint banks
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 __device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
@@ -492,7 +493,7 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
     }
     // page ids of the split: a run of sink positions, then a run of window positions
     __shared__ int pgs[64];
-    __shared__ __align__(16) bf16_t Vt[D * kWVtLd];
+    __shared__ __align__(16) bf16_t Vs[32 * kWVsLd];
     const int vS1 = min(v0 + n, ns_end);
     const int pS0 = v0 >> 8;
     const int nPS = vS1 > v0 ? ((vS1 - 1) >> 8) - pS0 + 1 : 0;
@@ -549,18 +550,11 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
             for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(kc + ro_n + 16 * kk);
         }
         __syncthreads();                                  // the previous block's V^T reads are done
-        // V^T[d][key col]: d = 16 kk + 8 hh + e; rows past the split stored as zeros
+        // the block's V rows, row-major (key col, d = 16 kk + 8 hh ..); rows
+        // past the split stored as zeros
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const uint32_t w4[4] = {live ? va[kk].x : 0u, live ? va[kk].y : 0u, live ? va[kk].z : 0u,
-                                    live ? va[kk].w : 0u};
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                const int d = 16 * kk + 8 * hh + 2 * x;
-                Vt[d * kWVtLd + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w4[x] & 0xFFFFu));
-                Vt[(d + 1) * kWVtLd + col] = __builtin_bit_cast(bf16_t, (uint16_t)(w4[x] >> 16));
-            }
-        }
+        for (int kk = 0; kk < 8; ++kk)
+            *reinterpret_cast<uint4*>(&Vs[col * kWVsLd + 16 * kk + 8 * hh]) = live ? va[kk] : make_uint4(0, 0, 0, 0);
         if (more) {
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) va[kk] = *reinterpret_cast<const uint4*>(vc + ro_n + 16 * kk);
@@ -596,17 +590,22 @@ __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __rest
 #pragma unroll
             for (int x = 0; x < 8; ++x) pb[x] = pack_bf2(p[2 * x], p[2 * x + 1]);
         }
-        __syncthreads();                                  // the V^T tile is written
-        // O^T += V^T P^T; k-step kk covers keys 16 kk + 4 hh + {0..3, 8..11}
+        __syncthreads();                                  // the V tile is written
+        // O^T += V^T P^T; k-step kk covers keys 16 kk + 4 hh + {0..3, 8..11}:
+        // lane (d = 32 dd + col, half hh) reads V^T[d][those keys] from the
+        // row-major tile by transposing loads (lane j of a 16-lane group
+        // addresses key row kc0 + j / 4 (+ 8) at columns 32 dd + 16 (group &
+        // 1) + 4 (j % 4))
+        const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const uint4 bp = make_uint4(pb[4 * kk], pb[4 * kk + 1], pb[4 * kk + 2], pb[4 * kk + 3]);
             const int kc0 = 16 * kk + 4 * hh;
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd) {
-                const bf16_t* vr = &Vt[(32 * dd + col) * kWVtLd + kc0];
-                const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vr + 8);
+                const bf16_t* vr = &Vs[(kc0 + trr) * kWVsLd + 32 * dd + trc];
+                const uint2 lo = lds_tr16(vr);
+                const uint2 hi = lds_tr16(vr + 8 * kWVsLd);
                 const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 oacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), oacc[dd], 0, 0, 0);
             }

@@ -39,17 +39,6 @@ constexpr int kVsLd = kD + 32;     // V row stride in LDS (bf16), 320 B: the fou
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-
-// Transposing LDS load: within each 16-lane group, lane 4 r + c supplies the
-// address of 4 consecutive 16-bit elements (row r of a 4 x 16 block, columns
-// 4 c .. 4 c + 3); lane i receives column i of the block, rows 0..3.
-__device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
-    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4_t*)(p));
-    return __builtin_bit_cast(uint2, v);
-}
-
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
 }

@@ -71,6 +71,17 @@ template <typename T> __device__ __forceinline__ void st(T* p, float v);
 template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
 template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
 
+// Transposing LDS load (gfx950): within each 16-lane group, lane 4 r + c
+// supplies the address of 4 consecutive 16-bit elements (row r of a 4 x 16
+// block, columns 4 c .. 4 c + 3); lane i receives column i of the block,
+// rows 0..3.
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4_t*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 // Order-preserving uint32 key of an fp32 score; -0 and +0 map to one key.
 __device__ __forceinline__ uint32_t score_key(float f) {
     uint32_t u = __float_as_uint(f);
