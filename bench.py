@@ -326,26 +326,43 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
         sel = rtp.make_sel(row_ptr, idx, status)
         ws_sel = torch.empty(rtp.topp_select_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
         ws_sp = torch.empty(rtp.sparse_attn_workspace(layer, cache, query, cap), dtype=torch.uint8, device=dev)
+        ws_ret = torch.empty(rtp.retrieval_decode_workspace(layer, cache, query, cap), dtype=torch.uint8,
+                             device=dev)
         ws_win = torch.empty(rtp.window_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
         out = torch.zeros_like(q)
         inst.append(dict(pc=pc, cache=cache, q=q, w_q=w_q, w_k=w_k, top_p=top_p, query=query,
                          sid=torch.arange(B, dtype=torch.int32, device=dev), pos=(pc.seq_lens - 1).to(torch.int32),
                          sel=sel, row_ptr=row_ptr, idx=idx, status=status, ws_sel=ws_sel, ws_sp=ws_sp,
-                         ws_win=ws_win, out=out))
+                         ws_ret=ws_ret, ws_win=ws_win, out=out))
     torch.cuda.synchronize()
     log("[bench] %s: %d layer instances resident (%.1f GB allocated)" %
         (tag, instances, torch.cuda.memory_allocated() / 1e9))
     side = torch.cuda.Stream()
 
-    def make_step(I, main):
+    def make_step(I, main, fused=True):
         sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
         append = rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"], stream=main, prepare=True)
+        window = rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side, prepare=True)
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        if fused:
+            # the retrieval heads' selection and attention in one call; the
+            # local heads' window attention on the second stream beside it
+            retrieval = rtp.retrieval_decode(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"],
+                                             I["out"], I["ws_ret"], stream=main, prepare=True)
+
+            def run():
+                append()
+                fork.record(main)
+                side.wait_event(fork)
+                window()
+                retrieval()
+                join.record(side)
+                main.wait_event(join)
+            return run
         begin = rtp.topp_select_begin(*sel_args, stream=main, prepare=True)
         end = rtp.topp_select_end(*sel_args, stream=main, prepare=True)
         sparse = rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"], stream=main,
                                         prepare=True)
-        window = rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side, prepare=True)
-        fork, join = torch.cuda.Event(), torch.cuda.Event()
 
         def run():
             append()
@@ -384,6 +401,14 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     torch.cuda.synchronize()
     per_call = {c: round(float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3, 2)
                 for i, c in enumerate(calls)}
+    # the fused call alone (selection + sparse attention of the retrieval heads)
+    for s, e in enumerate(evs):
+        I = inst[s % n_i]
+        e[0].record()
+        rtp.retrieval_decode(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["out"], I["ws_ret"])
+        e[1].record()
+    torch.cuda.synchronize()
+    per_call["retrieval_fused"] = round(float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3, 2)
 
     # the timed region: exactly `steps` steps between synchronisations
     a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -403,6 +428,18 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
         e1.record()
     torch.cuda.synchronize()
     step_us = stats([e0.elapsed_time(e1) * 1e3 for e0, e1 in pe])
+    # the same step with the selection and the sparse attention as separate
+    # calls (rtp_topp_select_begin / _end, rtp_sparse_attn_decode)
+    runs2 = [make_step(I, main_stream, fused=False) for I in inst]
+    for s in range(warmup):
+        runs2[s % n_i]()
+    torch.cuda.synchronize()
+    a.record()
+    for s in range(steps):
+        runs2[s % n_i]()
+    b_.record()
+    torch.cuda.synchronize()
+    two_call_us = round(a.elapsed_time(b_) / steps * 1e3, 2)
 
     graph_ms = None
     if graph:
@@ -432,7 +469,8 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     bytes_win = int(sum(min(w.window + w.sinks, int(l)) for l in lens)) * w.Hkv * kv_row
     step_bytes = bytes_klow + bytes_sparse + bytes_win
     res = {"workload": w.name + ("_fp8kv" if fp8 else ""), "batch": B, "max_context": L,
-           "us_per_step": round(ms * 1e3, 2), "step_us": step_us, "per_call_us": per_call,
+           "us_per_step": round(ms * 1e3, 2), "step_us": step_us, "two_call_step_us": two_call_us,
+           "per_call_us": per_call,
            "graph_us": round(graph_ms * 1e3, 2) if graph_ms else None,
            "step_algorithmic_bytes": step_bytes,
            "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

@@ -295,7 +295,8 @@ rtp_status rtp_topk_select(const rtp_layer *layer, const rtp_cache *cache, const
  * workspace -- and the
  * flags 16 (ordered through a bitmap) / 32 (ordered by merging runs), 64 (the
  * normaliser summed exactly over every key), 128 (the cut counted keys: top-k
- * or the k_max cap).  For the decode path and fp32 chunks only when every row
+ * or the k_max cap), 256 (decode path: the candidate set was taken from the
+ * scoring pass's per-chunk candidate lists rather than the row's scores).  For the decode path and fp32 chunks only when every row
  * fits one pass of the workspace (RTP_EUNSUPPORTED otherwise).
  */
 rtp_status rtp_topp_select_paths(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
@@ -326,6 +327,29 @@ rtp_status rtp_sparse_attn_decode(const rtp_layer *layer, const rtp_cache *cache
 rtp_status rtp_sparse_attn_prefill(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
                                    const rtp_sel *sel, void *out, void *workspace, size_t workspace_bytes,
                                    void *stream);
+
+/*
+ * a2-a5 of the retrieval heads of one decode step in one call: the selection
+ * of rtp_topp_select and the attention of rtp_sparse_attn_decode over it
+ * (abstract: retrieval heads score every cached token with the lightweight
+ * indexer and attend sparsely over the full KV cache; forum post, "Open
+ * Questions and Limitations": per-query token counts vary, so here the
+ * attention reads each row's selected keys straight from the selection's row
+ * records, with no host round trip and no separate pass that writes the CSR
+ * before the attention reads it).  Same arguments, selection, CSR output, status
+ * codes and attention output as rtp_topp_select followed by
+ * rtp_sparse_attn_decode with the same sel; on capacity overflow
+ * (*status = 1, row_ptr complete, idx untouched) and for an invalid top_p
+ * (*status = 3) no attention output is written.  RTP_DECODE queries only.
+ * workspace: rtp_retrieval_decode_workspace(layer, cache, query,
+ * sel->capacity) bytes.  Errors: as the two calls; RTP_EINVAL for another
+ * query kind.
+ */
+size_t rtp_retrieval_decode_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                                      int64_t capacity);
+rtp_status rtp_retrieval_decode(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                                const void *w_q, const float *top_p, const rtp_sel *sel, void *out,
+                                void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes for rtp_window_attn / rtp_dense_attn. */
 size_t rtp_window_attn_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query);

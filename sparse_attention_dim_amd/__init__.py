@@ -27,7 +27,7 @@ RTP_NOALLOC_SCRATCH_BYTES = 64 << 20
 SEL_OK, SEL_OVERFLOW, SEL_UNCERTIFIED, SEL_BAD_TOP_P = 0, 1, 2, 3
 # per-row path codes of rtp_topp_select_paths
 PATH_ALL, PATH_TINY, PATH_ROW, PATH_LARGE, PATH_LEVEL, PATH_LIST, PATH_SCAN, PATH_LIST_G = 1, 2, 3, 4, 5, 6, 7, 8
-PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT = 16, 32, 64, 128
+PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT, PATH_CHUNK_LISTS = 16, 32, 64, 128, 256
 
 ENTRY_POINTS = (
     "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_kv_append", "rtp_topp_select_workspace",
@@ -36,7 +36,8 @@ ENTRY_POINTS = (
     "rtp_topk_select",
     "rtp_topp_select_paths", "rtp_indexer_scores",
     "rtp_sparse_attn_workspace",
-    "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_window_attn_workspace",
+    "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_retrieval_decode_workspace",
+    "rtp_retrieval_decode", "rtp_window_attn_workspace",
     "rtp_dense_attn_workspace", "rtp_window_attn", "rtp_dense_attn",
 )
 
@@ -107,6 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_sparse_attn_workspace": ([pl, pc, pq, i64], S),
         "rtp_sparse_attn_decode": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
         "rtp_sparse_attn_prefill": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
+        "rtp_retrieval_decode_workspace": ([pl, pc, pq, i64], S),
+        "rtp_retrieval_decode": ([pl, pc, pq, P, P, ps, P, P, S, P], ctypes.c_int),
         "rtp_window_attn_workspace": ([pl, pc, pq], S),
         "rtp_dense_attn_workspace": ([pl, pc, pq], S),
         "rtp_window_attn": ([pl, pc, pq, P, P, S, P], ctypes.c_int),
@@ -295,6 +298,18 @@ def sparse_attn_prefill(layer, cache, query, sel, out, ws, stream=None, prepare=
     return _run("rtp_sparse_attn_prefill", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
                                             ctypes.byref(sel), _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)),
                 (layer, cache, query, sel), prepare)
+
+
+def retrieval_decode_workspace(layer, cache, query, capacity: int) -> int:
+    return load().rtp_retrieval_decode_workspace(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
+                                                 capacity)
+
+
+def retrieval_decode(layer, cache, query, w_q, top_p, sel, out, ws, stream=None, prepare=False):
+    """Selection and sparse attention of the retrieval heads of a decode step in one call."""
+    return _run("rtp_retrieval_decode", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                                         _ptr(top_p), ctypes.byref(sel), _ptr(out), _ptr(ws), _nbytes(ws),
+                                         _stream(stream)), (layer, cache, query, sel), prepare)
 
 
 def window_attn_workspace(layer, cache, query) -> int:

@@ -209,7 +209,7 @@ constexpr size_t kScoreBudget = (size_t)4 << 30;   // bytes of scores per row gr
 struct SelPlan {
     int rows_total, group_rows, nchunk, ucap;
     int64_t lpad;
-    size_t off_scores, off_cmax, off_qlow, off_chist, off_ccnt, off_st, off_sel, off_chunk, off_ubuf, off_rown, total;
+    size_t off_scores, off_cmax, off_qlow, off_chist, off_ccnt, off_st, off_sel, off_ubuf, off_clist, off_chdr, total;
 };
 
 // Prefill chunks in bf16 take the tiled selection (the rows of one retrieval
@@ -227,7 +227,7 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     p.lpad = (int64_t)p.nchunk * rtp::kChunk;
     p.ucap = (int)std::min<int64_t>(rtp::kCandG, p.lpad);
     const size_t per_row =
-        (size_t)p.lpad * 4 + (size_t)p.nchunk * (4 + 4 + rtp::kCB * 12) + (size_t)p.ucap * 12 + 1024;
+        (size_t)p.lpad * 4 + (size_t)p.nchunk * (4 + 4 + rtp::kCB * 12 + rtp::kNc * 8) + (size_t)p.ucap * 12 + 1024;
     const int64_t by_budget = std::max<int64_t>(1, (int64_t)(kScoreBudget / per_row));
     p.group_rows = (int)std::min<int64_t>({(int64_t)p.rows_total, by_budget, (int64_t)65535});
     const size_t G = (size_t)p.group_rows;
@@ -239,9 +239,9 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     p.off_ccnt = o; o = align256(o + G * (size_t)p.nchunk * rtp::kCB * 4);
     p.off_st = o; o = align256(o + G * sizeof(rtp::RowState));
     p.off_sel = o; o = align256(o + G * (size_t)p.ucap * 4);
-    p.off_chunk = o; o = align256(o + G * (size_t)p.nchunk * 4);
     p.off_ubuf = o; o = align256(o + G * (size_t)p.ucap * 8);
-    p.off_rown = o; o = align256(o + G * 4);
+    p.off_clist = o; o = align256(o + G * (size_t)p.nchunk * rtp::kNc * 8);
+    p.off_chdr = o; o = align256(o + G * (size_t)p.nchunk * 4);
     p.total = o;
     return p;
 }
@@ -255,10 +255,10 @@ rtp::SelWs sel_ws(const SelPlan& p, char* base) {
     w.chist = (unsigned long long*)(base + p.off_chist);
     w.st = (rtp::RowState*)(base + p.off_st);
     w.sel = (uint32_t*)(base + p.off_sel);
-    w.chunk_cnt = (uint32_t*)(base + p.off_chunk);
     w.ubuf = (unsigned long long*)(base + p.off_ubuf);
     w.ccnt = (unsigned*)(base + p.off_ccnt);
-    w.row_n = (uint32_t*)(base + p.off_rown);
+    w.clist = (unsigned long long*)(base + p.off_clist);
+    w.chdr = (uint32_t*)(base + p.off_chdr);
     w.nchunk = p.nchunk;
     w.rows = p.group_rows;
     w.ucap = p.ucap;
@@ -586,6 +586,59 @@ rtp_status rtp_sparse_attn_prefill(const rtp_layer* layer, const rtp_cache* cach
         if (e != hipSuccess) return hip_status(e, "sparse prefill launch");
     }
     return ok();
+}
+
+static size_t sparse_dec_ws_bytes(const rtp_layer* layer, const rtp_query* query, int64_t capacity) {
+    const int64_t rows = (int64_t)query->n_tok * layer->num_ret;
+    const int64_t items = sparse_max_items(layer, query, capacity);
+    return align256((size_t)items * (layer->head_dim + 2) * 4) + align256((size_t)(rows + 1) * 4);
+}
+
+size_t rtp_retrieval_decode_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                      int64_t capacity) {
+    if (check_all(layer, cache, query) || capacity < 0 || query->kind != RTP_DECODE) return 0;
+    return plan_select(layer, cache, query).total + sparse_dec_ws_bytes(layer, query, capacity);
+}
+
+rtp_status rtp_retrieval_decode(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                const void* w_q, const float* top_p, const rtp_sel* sel, void* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    rtp_status s = check_all(layer, cache, query);
+    if (s) return s;
+    if (query->kind != RTP_DECODE) return fail(RTP_EINVAL, "rtp_retrieval_decode needs RTP_DECODE queries");
+    if (!w_q || !top_p || !out) return fail(RTP_EINVAL, "NULL w_q / top_p / out");
+    if (!sel || !sel->row_ptr || !sel->status || (sel->capacity > 0 && !sel->idx) || sel->capacity < 0)
+        return fail(RTP_EINVAL, "bad selection buffers");
+    const int rows = query->n_tok * layer->num_ret;
+    if (rows > kMaxDecodeRows) return fail(RTP_EUNSUPPORTED, "batch * num_ret %d > %d", rows, kMaxDecodeRows);
+    const SelPlan p = plan_select(layer, cache, query);
+    const size_t need = p.total + sparse_dec_ws_bytes(layer, query, sel->capacity);
+    if (!workspace || workspace_bytes < need)
+        return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+    const int64_t items = sparse_max_items(layer, query, sel->capacity);
+    char* aw = (char*)workspace + p.total;
+    rtp::AttnWs w;
+    w.part = (float*)aw;
+    w.item_start = (int32_t*)(aw + align256((size_t)items * (layer->head_dim + 2) * 4));
+    w.max_items = items;
+    if (p.group_rows < p.rows_total) {
+        // rows beyond one workspace pass: the two calls in sequence
+        if ((s = topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, p.total, stream, 0, 0)))
+            return s;
+        const rtp::Geo g = make_geo(layer, cache, query);
+        return hip_status(rtp::launch_sparse_decode(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
+                                                    sel->status, out, w, 0, rows, layer->dtype, (hipStream_t)stream),
+                          "sparse decode launch");
+    }
+    const rtp::Geo g = make_geo(layer, cache, query);
+    const rtp::SelWs sw = sel_ws(p, (char*)workspace);
+    const rtp::SelOut so{sel->row_ptr, sel->idx, sel->capacity, sel->status};
+    hipError_t e = rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p, 0, sw, so, rows,
+                                      layer->dtype, rtp::kSelRows, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "top-p select launch");
+    return hip_status(rtp::launch_sparse_decode_sel(g, query->q, cache->k, cache->v, sw, so, out, w, rows,
+                                                    layer->dtype, (hipStream_t)stream),
+                      "sparse decode launch");
 }
 
 size_t rtp_window_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {

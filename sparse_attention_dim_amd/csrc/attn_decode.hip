@@ -287,6 +287,151 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
     }
 }
 
+// Merge the n partial results of a row (stride D + 2: output[D], max, sum) in
+// item order on one wavefront: o[d] = sum_i 2^(m_i - M) o_i[d] / L * post.
+template <typename T, int D>
+__device__ void combine_wave(const float* __restrict__ base, int n, T* __restrict__ o, float post) {
+    const int lane = threadIdx.x & 63;
+    float mx = -INFINITY;
+    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, base[(size_t)i * (D + 2) + D]);
+    const float M = wave_max(mx);
+    float ls = 0.0f;
+    for (int i = lane; i < n; i += 64)
+        ls += exp2f(base[(size_t)i * (D + 2) + D] - M) * base[(size_t)i * (D + 2) + D + 1];
+    const float L = wave_sum(ls);
+    for (int d = lane; d < D; d += 64) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int i = 0; i < n; ++i)
+            acc = __builtin_fmaf(base[(size_t)i * (D + 2) + d], exp2f(base[(size_t)i * (D + 2) + D] - M), acc);
+        st<T>(o + d, acc / L * post);
+    }
+}
+
+// Sparse decode straight from the selection's row records (the work items of
+// k_sparse_dec_part): each row's selected keys are read from the selection
+// workspace (its ordered list, its score array overwritten by the indices, or
+// every key), and the items also write the CSR output -- the first workgroup
+// the row pointers and the capacity check, every item its own slice of idx.
+// The last item of a row to finish (a device-scope counter in the row's
+// record, after a release fence) merges the row's partials into the output.
+// Rows of one call only (row0 = 0).
+template <typename T, typename TKV, int D>
+__global__ __launch_bounds__(64) void k_sparse_dec_sel(Geo g, const T* __restrict__ q,
+                                                       const TKV* __restrict__ kc,
+                                                       const TKV* __restrict__ vc, SelWs sw, SelOut so,
+                                                       AttnWs ws, T* __restrict__ out, int rows) {
+    using S = Stream<TKV, D, 1>;
+    if (*so.status != 0) return;                          // an invalid top_p was reported: nothing emitted
+    const int lane = threadIdx.x;
+    extern __shared__ int64_t dyn[];
+    int64_t* rp = dyn;                                    // rows + 1
+    int32_t* istart = reinterpret_cast<int32_t*>(dyn + rows + 1);   // rows + 1
+    __shared__ uint32_t joff[kItem];
+    {   // selected keys and pieces per row, and their prefixes (every workgroup)
+        const int per = (rows + 63) / 64;
+        const int r0 = lane * per;
+        long long cs = 0;
+        int run = 0;
+        for (int i = 0; i < per; ++i) {
+            const int r = r0 + i;
+            if (r < rows) {
+                const int c = sw.st[r].count;
+                cs += c;
+                run += (c + kItem - 1) / kItem;
+            }
+        }
+        long long exs = cs;
+        int ex = run;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const long long ys = __shfl_up(exs, o);
+            const int y = __shfl_up(ex, o);
+            if (lane >= o) {
+                exs += ys;
+                ex += y;
+            }
+        }
+        const long long total_s = __shfl(exs, 63);
+        const int total = __shfl(ex, 63);
+        exs -= cs;
+        ex -= run;
+        for (int i = 0; i < per; ++i) {
+            const int r = r0 + i;
+            if (r < rows) {
+                const int c = sw.st[r].count;
+                rp[r] = exs;
+                istart[r] = ex;
+                exs += c;
+                ex += (c + kItem - 1) / kItem;
+            }
+        }
+        if (lane == 0) {
+            rp[rows] = total_s;
+            istart[rows] = total;
+        }
+    }
+    __syncthreads();
+    const bool fits = rp[rows] <= so.capacity;
+    if (blockIdx.x == 0) {
+        for (int r = lane; r <= rows; r += 64) {
+            so.row_ptr[r] = rp[r];
+            ws.item_start[r] = fits ? istart[r] : 0;
+        }
+        if (!fits && lane == 0) *so.status = 1;           // capacity overflow: the size needed is row_ptr[rows]
+    }
+    if (!fits) return;
+    const int total = istart[rows];
+    const float sc = g.attn_scale * kLog2e * g.k_scale;    // the K scale of FP8 codes folded into q
+    constexpr int EPV = S::EPV, LPK = S::LPK;
+    static_assert(kItem == 64, "one selected key per lane of an item");
+
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        int lo = 0, hi = rows - 1;       // last row with istart <= item
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (istart[mid] <= item) lo = mid; else hi = mid - 1;
+        }
+        const int row = lo;
+        const int t = row / g.n_ret, r = row - t * g.n_ret;
+        const int h = g.ret_heads[r], kvh = h / g.group;
+        const int k0 = (item - istart[row]) * kItem;
+        const int n = (int)min<int64_t>(kItem, rp[row + 1] - rp[row] - k0);
+        const int mode = sw.st[row].mode;
+        const int32_t* bt = g.block_table + (size_t)row_seq(g, t) * g.max_blocks;
+        const int i = k0 + min(lane, n - 1);
+        const int j = mode == 0 ? i
+                    : mode == 1 ? (int)sw.sel[(size_t)row * sw.ucap + i]
+                                : reinterpret_cast<const int32_t*>(sw.scores + (size_t)row * sw.score_ld)[i];
+        if (lane < n) so.idx[rp[row] + k0 + lane] = j;
+        joff[lane] = (uint32_t)kv_rowidx(g, bt[j >> 8], kvh, j & 255);
+        S st;
+        st.init();
+        const int sl = (lane % LPK) * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) st.q[0][e] = ld(q + ((size_t)t * g.Hq + h) * D + sl + e) * sc;
+        __syncthreads();
+        auto off = [&](int x) { return (size_t)joff[x] * D; };
+        st.act[0] = true;
+        st.run(n, off, kc, vc);
+        st.merge();
+        st.write(0, ws.part + (size_t)item * (D + 2));
+        // the row's last item to finish merges the row's partial results
+        // (the row pass zeroed the row's arrival count)
+        const int nit = istart[row + 1] - istart[row];
+        __threadfence();
+        int last = 0;
+        if (lane == 0) last = atomicAdd(&sw.st[row].arrive, 1) == nit - 1;
+        last = __shfl(last, 0);
+        if (last) {
+            __threadfence();
+            combine_wave<T, D>(ws.part + (size_t)istart[row] * (D + 2), nit, out + ((size_t)t * g.Hq + h) * D,
+                               g.v_scale);   // the V scale of FP8 codes
+        }
+        __syncthreads();
+    }
+}
+
 constexpr int kMaxParts = 4096;   // partial weights kept in LDS; more are recomputed
 
 // Merge `n` partial results (stride D + 2: output[D], max, sum) in order.
@@ -325,10 +470,9 @@ __device__ void combine_parts(const float* __restrict__ base, int n, T* __restri
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(128) void k_sparse_dec_combine(Geo g, const int32_t* __restrict__ status,
-                                                            AttnWs ws, T* __restrict__ out, int row0) {
+__global__ __launch_bounds__(64) void k_sparse_dec_combine(Geo g, const int32_t* __restrict__ status,
+                                                           AttnWs ws, T* __restrict__ out, int row0) {
     if (*status != 0) return;
-    __shared__ float wsh[kMaxParts];
     const int row = blockIdx.x;
     const int grow = row0 + row;
     const int t = grow / g.n_ret, r = grow - t * g.n_ret;
@@ -339,7 +483,7 @@ __global__ __launch_bounds__(128) void k_sparse_dec_combine(Geo g, const int32_t
         for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
         return;
     }
-    combine_parts<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, wsh, g.v_scale);   // V scale of FP8 codes
+    combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);   // V scale of FP8 codes
 }
 
 // ---------------------------------------------------------------------------
@@ -653,7 +797,17 @@ hipError_t sparse_dec(const Geo& g, const void* q, const void* k, const void* v,
     const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
     hipLaunchKernelGGL((k_sparse_dec_part<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g,
                        (const T*)q, (const TKV*)k, (const TKV*)v, row_ptr, idx, status, ws, row0, rows);
-    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(128), 0, s, g, status, ws, (T*)out, row0);
+    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, status, ws, (T*)out, row0);
+    return hipGetLastError();
+}
+
+template <typename T, typename TKV, int D>
+hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
+                          const SelOut& so, void* out, const AttnWs& ws, int rows, hipStream_t s) {
+    const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
+    const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
+    hipLaunchKernelGGL((k_sparse_dec_sel<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
+                       (const TKV*)k, (const TKV*)v, sw, so, ws, (T*)out, rows);
     return hipGetLastError();
 }
 
@@ -695,6 +849,17 @@ hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, cons
     if (dtype == 0 && g.D == 128) return sparse_dec<float, float, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
     if (dtype == 1 && g.D == 64) return sparse_dec<bf16_t, bf16_t, 64>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
     return sparse_dec<bf16_t, bf16_t, 128>(g, q, k, v, row_ptr, idx, status, out, ws, row0, rows, s);
+}
+
+hipError_t launch_sparse_decode_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
+                                    const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
+                                    hipStream_t s) {
+    if (g.kv_fp8 && g.D == 64) return sparse_dec_sel<bf16_t, fp8e4_t, 64>(g, q, k, v, sw, so, out, ws, rows, s);
+    if (g.kv_fp8) return sparse_dec_sel<bf16_t, fp8e4_t, 128>(g, q, k, v, sw, so, out, ws, rows, s);
+    if (dtype == 0 && g.D == 64) return sparse_dec_sel<float, float, 64>(g, q, k, v, sw, so, out, ws, rows, s);
+    if (dtype == 0 && g.D == 128) return sparse_dec_sel<float, float, 128>(g, q, k, v, sw, so, out, ws, rows, s);
+    if (dtype == 1 && g.D == 64) return sparse_dec_sel<bf16_t, bf16_t, 64>(g, q, k, v, sw, so, out, ws, rows, s);
+    return sparse_dec_sel<bf16_t, bf16_t, 128>(g, q, k, v, sw, so, out, ws, rows, s);
 }
 
 hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,

@@ -23,6 +23,7 @@ constexpr int kPathBitmap = 16;   // chunk path: ordered through a bitmap of the
 constexpr int kPathMerge = 32;    // chunk path: ordered by merging the writers' runs
 constexpr int kPathExactZ = 64;   // the normaliser was summed exactly over every key
 constexpr int kPathCount = 128;   // the cut counted keys (fixed top-k, or the budget cap)
+constexpr int kPathChunkLists = 256;  // decode path: U taken from the scoring pass's per-chunk candidate lists
 
 // Geometry of one call (host-filled, passed by value to kernels).
 struct Geo {
@@ -85,7 +86,8 @@ __device__ __forceinline__ int row_pos(const Geo& g, int t) {
 // Per-row state of the top-p selection (device workspace).
 struct RowState {
     float m;                      // row maximum score
-    int32_t mode;                 // 0 every key, 1 ordered list in SelWs::sel, 2 threshold (Tkey, jT)
+    int32_t mode;                 // 0 every key, 1 ordered list in SelWs::sel, 2 ordered list over the row's
+                                  // scores (int32 indices written in place; the cut is (Tkey, jT))
     uint32_t Tkey;                // threshold: keys with score key > Tkey, or == Tkey and index <= jT
     int32_t jT;
     int32_t L;                    // keys of the row
@@ -95,12 +97,15 @@ struct RowState {
     int32_t unit;                 // the cut counts keys (fixed top-k, or the budget cap)
     int32_t path;                 // kPath* code of the row
     int32_t ks;                   // candidate threshold of the plan: U = keys with s (m - d) < ks / 4 (+ margin)
+    int32_t arrive;               // sparse decode from the row records: items of the row finished (zeroed
+                                  // by the row pass)
 };
 
 constexpr int kChunk = 4096;      // keys per workgroup of the scoring pass
 constexpr int kCB = 128;          // mass-histogram bins per chunk (1/4 unit of s (m_c - d) each)
 constexpr int kCand = 8192;       // candidates ranked in LDS
 constexpr int kCandG = 32768;     // candidates ranked from the workspace list (more: a cut over the scores)
+constexpr int kNc = 256;          // candidate-list entries per chunk written by the scoring pass
 
 // Device workspace of the selection, for `rows` rows of at most Lpad keys.
 struct SelWs {
@@ -111,10 +116,12 @@ struct SelWs {
     unsigned long long* chist;    // [rows][nchunk][kCB] chunk mass histograms
     RowState* st;                 // [rows]
     uint32_t* sel;                // [rows][ucap] selected indices, ascending (mode 1)
-    unsigned long long* ubuf;     // [rows][ucap] U in index order: (score key << 32) | ~index
+    unsigned long long* ubuf;     // [rows][ucap] U in index order when it is gathered from the scores and
+                                  // exceeds LDS: (score key << 32) | ~index
     unsigned* ccnt;               // [rows][nchunk][kCB] cumulative key counts of the chunk bins
-    uint32_t* row_n;              // [rows] size of U
-    uint32_t* chunk_cnt;          // [rows][nchunk] each chunk's place in U (the plan), then its output offset (mode 2)
+    unsigned long long* clist;    // [rows][nchunk][kNc] each chunk's highest-ranked keys, index order:
+                                  // (score key << 32) | (chunk bin << 12) | (index - chunk start)
+    uint32_t* chdr;               // [rows][nchunk] (entries << 8) | (last chunk bin in the list + 1)
     int nchunk;
     int rows;                     // rows of this group
     int ucap;                     // row stride of ubuf / sel: min(kCandG, padded keys)
@@ -143,6 +150,7 @@ enum SelStage {
     kSelScoresOnly = 1,           // projection and scores only (rtp_indexer_scores)
     kSelScorePass = 2,            // the first part of kSelAll
     kSelFinish = 3,               // the rest of kSelAll
+    kSelRows = 4,                 // kSelAll without the emit: the row records hold the sets
 };
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
@@ -165,6 +173,13 @@ struct AttnWs {
 hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, const void* v,
                                 const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
                                 void* out, const AttnWs& ws, int row0, int rows, int dtype, hipStream_t s);
+
+// The same from the selection's workspace (rows of one selection call, one
+// group): each row's selected keys are read from its row record, and the
+// items write the CSR output (row pointers, capacity check, indices).
+hipError_t launch_sparse_decode_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
+                                    const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
+                                    hipStream_t s);
 
 // Top-p selection of the rows of one prefill chunk (bf16, D <= 128): indexer
 // scores of 32-row x 32-key tiles by MFMA as a filter, exact fixed-order

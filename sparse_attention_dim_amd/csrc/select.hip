@@ -14,22 +14,23 @@
 //   score:   q_low = bf16(fp32 chain over d of q . W_q) (every workgroup of the
 //            row forms it while its first indexer-key loads are in flight),
 //            fp32 chain scores of every key of a chunk, the chunk maximum m_c,
-//            and the chunk's cumulative mass histogram: exact fixed-point
-//            weights exp(s (d - m_c)) summed over bins of x_c = s (m_c - d)
-//            (1/4 wide)
-//   gather / resolve: every workgroup of the gather pass forms its row's plan
-//            (below) and gathers its chunk's part of U; one workgroup per row
-//            then resolves the cut.  Row maximum m and total mass
+//            the chunk's cumulative mass histogram (exact fixed-point weights
+//            exp(s (d - m_c)) summed over bins of x_c = s (m_c - d), 1/4 wide)
+//            and the chunk's candidate list: its keys in the lowest bins, up to
+//            kNc of them, in index order
+//   row:     one workgroup per row.  Row maximum m and total mass
 //            Z = sum_c exp(s (m_c - m)) Z_c; every chunk bin whose upper edge
 //            lies below a threshold X on the row's x axis certainly holds
 //            keys with x < X, which gives a lower bound of the mass above
 //            any X.  The smallest X whose bound reaches the target fixes the
 //            candidate set U = {d >= m - X / s}: it holds every key ranked at
-//            or above the cut.  U is gathered from the scores into LDS and the
+//            or above the cut.  U is taken from the chunks' candidate lists
+//            when they hold it (else from the row's scores) into LDS, and the
 //            cut is found by radix selection over its score keys with exact
 //            masses per bucket (ties: lowest indices first); when U does not
-//            fit LDS the same selection runs over the row's scores.  U is
-//            gathered in index order, so the selected keys are its filter.
+//            fit the workspace list the same selection runs over the row's
+//            scores.  U is gathered in index order, so the selected keys are
+//            its filter.
 //   emit:    CSR row pointers, the capacity check, and the selected indices
 //            of every row
 // Workgroups of one pass never wait on each other: every hand-off between
@@ -78,7 +79,8 @@ __device__ __forceinline__ RowInfo row_info(const Geo& g, int row0, int lrow) {
 // Scores.  grid (nchunk, rows), 256 threads.  Thread i of chunk c scores keys
 // c*4096 + 256*k + i, k = 0..15, i.e. slot i of the chunk's 16 pages: every
 // iteration reads one page's 8 KiB run of the head's indexer keys, coalesced.
-// STATS: also the chunk maximum and the chunk's mass histogram.
+// STATS: also the chunk maximum, the chunk's mass histogram and its candidate
+// list (the keys of its lowest bins, at most kNc, in index order).
 // ---------------------------------------------------------------------------
 template <typename T, int STATS>
 __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ q, const T* __restrict__ w_q,
@@ -98,6 +100,8 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     __shared__ __align__(16) float qrow[128];
     __shared__ __align__(16) float wq[128 * kIdx];
     __shared__ float qs[kIdx];
+    __shared__ int s_cbin;                                // last chunk bin of the candidate list
+    __shared__ uint32_t lcnt[64], loff[64];               // list entries per (key step, wave)
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int jbase = chunk * kChunk;
@@ -157,6 +161,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     if (STATS && tid < kCB) {
         hist[tid] = 0ull;
         hcnt[tid] = 0u;
+        if (tid == 0) s_cbin = -1;
     }
     __syncthreads();
     if (tid < kIdx) {
@@ -203,14 +208,19 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     const float mc = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     if (tid == 0) ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk] = score_key(mc);
     const float s = g.idx_scale;
+    // chunk bins of the thread's keys, one byte each (255: past the row's end)
+    uint32_t binp[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int j = jbase + k * 256 + tid;
+        uint32_t b = 255u;
         if (j < ri.L) {
             const WeightBin wb = weight_bin(dv[k], mc, s);
-            atomicAdd(&hist[wb.bin >> 4], wb.w);         // 64 level-1 bins per unit -> 4 per unit
-            atomicAdd(&hcnt[wb.bin >> 4], 1u);
+            b = (uint32_t)(wb.bin >> 4);                  // 64 level-1 bins per unit -> 4 per unit
+            atomicAdd(&hist[b], wb.w);
+            atomicAdd(&hcnt[b], 1u);
         }
+        binp[k >> 2] |= b << (8 * (k & 3));
     }
     __syncthreads();
     // cumulative over bins (the mass of keys with x_c < (b + 1) / 4)
@@ -237,6 +247,47 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         unsigned* cc = ws.ccnt + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
         cc[2 * t] = incl - b;
         cc[2 * t + 1] = incl;
+        // the list takes the lowest bins whose keys number at most kNc
+        if (incl - b <= (unsigned)kNc) atomicMax(&s_cbin, 2 * t);
+        if (incl <= (unsigned)kNc) atomicMax(&s_cbin, 2 * t + 1);
+    }
+    __syncthreads();
+    // the candidate list in index order (key j = jbase + 256 k + 64 wave + lane):
+    // per (k, wave) counts, their prefix by one wavefront, then the entries
+    const int cbin = s_cbin;
+    const int lane = tid & 63, wv = tid >> 6;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int b = (int)((binp[k >> 2] >> (8 * (k & 3))) & 255u);
+        const unsigned long long bal = __ballot(b <= cbin);
+        if (lane == 0) lcnt[4 * k + wv] = (uint32_t)__popcll(bal);
+    }
+    __syncthreads();
+    if (tid < 64) {
+        const uint32_t v = lcnt[tid];
+        uint32_t incl = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(incl, o);
+            if (tid >= o) incl += y;
+        }
+        loff[tid] = incl - v;
+        if (tid == 63)
+            ws.chdr[(size_t)ri.lrow * ws.nchunk + chunk] = (incl << 8) | (uint32_t)(cbin + 1);
+    }
+    __syncthreads();
+    unsigned long long* cl = ws.clist + ((size_t)ri.lrow * ws.nchunk + chunk) * kNc;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int b = (int)((binp[k >> 2] >> (8 * (k & 3))) & 255u);
+        const bool in = b <= cbin;
+        const unsigned long long bal = __ballot(in);
+        if (in) {
+            const uint32_t o = loff[4 * k + wv] + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            cl[o] = ((unsigned long long)score_key(dv[k]) << 32) | ((unsigned long long)b << 12) |
+                    (unsigned long long)(k * 256 + tid);
+        }
     }
 }
 
@@ -367,8 +418,7 @@ __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* sro
     return c;
 }
 
-// Plan of one row, computed by every workgroup of the gather pass (256
-// threads): row maximum m, total mass Z = sum_c exp(s (m_c - m)) Z_c, the
+// Plan of one row, formed by the row's workgroup: row maximum m, total mass Z = sum_c exp(s (m_c - m)) Z_c, the
 // target, and the threshold d_thr of the candidate set U.  Every chunk bin
 // whose upper edge, moved to the row's axis, lies below X = k / 4 certainly
 // holds keys with s (m - d) < X: that gives a lower bound LB(k) of the mass
@@ -470,141 +520,11 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long lo
     return pl;
 }
 
-// Plan: the row's maximum, normaliser, target and candidate threshold, the
-// size of U and each chunk's place in U's index-ordered list (from the chunk
-// bins' cumulative counts, no atomics).  k_sel_plan (grid rows, 256 threads)
-// forms it once per row when the gather grid is larger than the chip holds
-// at once (kGatherResident workgroups); otherwise each gather workgroup forms
-// it.  U: in chunk c, the keys whose chunk bin is at most bsel(c) = ks + 1 - 4 dc
+// U: in chunk c, the keys whose chunk bin is at most bsel(c) = ks + 1 - 4 dc
 // (a quarter unit beyond the bins that LB(ks) counts, so U holds every key
-// with s (m - d) < ks / 4 and the cut lies inside it).
-constexpr size_t kGatherResident = 2048;
-
+// with s (m - d) < ks / 4 and the cut lies inside it); dc = s (m - m_c).
 __device__ __forceinline__ int chunk_bsel(int ks, double dc) {
     return ks >= kGB ? kCB - 1 : (int)fmin(floor((double)(ks + 1) - (double)kCBPerUnit * dc), (double)(kCB - 1));
-}
-
-// The row's plan and the size of U; the chunk offsets in U from the chunk
-// bins' cumulative counts.  Writes the RowState and the size of U when
-// `write`, every chunk's offset when `offsets`, and returns chunk `mine`'s.
-__device__ void form_plan(const Geo& g, const float* __restrict__ top_p, const RowInfo& ri, const SelWs& ws,
-                          int32_t* __restrict__ status, int mine, bool write, bool offsets, RowState& st,
-                          uint32_t& nU_out, uint32_t& base_out) {
-    const int tid = threadIdx.x;
-    __shared__ double fch[kMaxChunks], dch[kMaxChunks];
-    __shared__ double dred[4];
-    __shared__ uint32_t ured[4];
-    __shared__ int s_k[2];
-    __shared__ unsigned long long scan_sh[256 / 64 + 1];
-    __shared__ uint32_t s_base;
-    const Plan pl = row_plan<256>(g, ri, ws.chist + (size_t)ri.lrow * ws.nchunk * kCB,
-                                  ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB, ws.cmax + (size_t)ri.lrow * ws.nchunk,
-                                  top_p, fch, dch, dred, ured, s_k);
-    st.m = pl.m;
-    st.L = ri.L;
-    st.Tkey = 0u;
-    st.jT = ri.L;
-    st.target = pl.target;
-    st.d_thr = pl.d_thr;
-    st.ks = pl.ks;
-    nU_out = 0u;
-    base_out = 0u;
-    if (pl.all) {
-        st.mode = 0;
-        st.count = ri.L;
-        st.unit = 0;
-        st.path = kPathAll;
-        if (write && tid == 0) {
-            ws.st[ri.lrow] = st;
-            if (pl.bad) *status = 3;                      // invalid top_p: reported, nothing emitted
-        }
-        return;
-    }
-    st.mode = 1;
-    st.count = 0;
-    st.unit = pl.unit;
-    st.path = 0;
-    const unsigned* ccnt = ws.ccnt + (size_t)ri.lrow * ws.nchunk * kCB;
-    unsigned long long cnt_c = 0ull;
-    if (tid < ri.nch) {
-        const int b = chunk_bsel(pl.ks, dch[tid]);
-        cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
-    }
-    unsigned long long nU;
-    const unsigned long long off_c = block_excl_scan_u64<256>(cnt_c, &nU, scan_sh);
-    if (offsets && tid < ri.nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)off_c;
-    if (tid == mine) s_base = (uint32_t)off_c;
-    if (write && tid == 0) {
-        ws.st[ri.lrow] = st;
-        ws.row_n[ri.lrow] = (uint32_t)nU;                 // at most 2^20
-    }
-    nU_out = (uint32_t)nU;
-    if (mine >= 0) {
-        __syncthreads();
-        base_out = s_base;
-    }
-}
-
-__global__ __launch_bounds__(256) void k_sel_plan(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
-                                                  int32_t* __restrict__ status) {
-    RowState st;
-    uint32_t nU, base;
-    form_plan(g, top_p, row_info(g, row0, blockIdx.x), ws, status, -1, true, true, st, nU, base);
-}
-
-// Gather.  grid (nchunk, rows), 256 threads: the chunk's keys of U, written
-// at the chunk's place in the row's index-ordered list (rows whose U fits the
-// list).  kPlan: every workgroup forms its row's plan itself (the first
-// chunk's records it), which saves a launch when the grid is resident at
-// once; otherwise the plan comes from k_sel_plan.
-template <bool kPlan>
-__global__ __launch_bounds__(256) void k_sel_gather(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
-                                                    int32_t* __restrict__ status) {
-    const int tid = threadIdx.x;
-    const int chunk = blockIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.y);
-    if (chunk >= ri.nch) return;
-    __shared__ unsigned long long scan_sh[256 / 64 + 1];
-    // the chunk's scores, loaded while the plan is formed or read
-    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int j0 = chunk * kChunk + 16 * tid;             // 16 consecutive keys per thread
-    float dv[16];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const float4 v = *reinterpret_cast<const float4*>(srow + j0 + 4 * u);
-        dv[4 * u] = v.x;
-        dv[4 * u + 1] = v.y;
-        dv[4 * u + 2] = v.z;
-        dv[4 * u + 3] = v.w;
-    }
-    RowState st;
-    uint32_t nU, base;
-    if (kPlan) {
-        form_plan(g, top_p, ri, ws, status, chunk, chunk == 0, false, st, nU, base);
-    } else {
-        st = ws.st[ri.lrow];
-        nU = ws.row_n[ri.lrow];
-        base = ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
-    }
-    const float mc = key_score(ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk]);
-    if (st.mode == 0 || nU > (uint32_t)ws.ucap) return;   // every key, or the long path
-    const float s = g.idx_scale;
-    const int bmine = chunk_bsel(st.ks, (double)s * ((double)st.m - (double)mc));
-    if (bmine < 0) return;
-    uint32_t inU = 0u, c = 0u;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const bool in = j0 + e < ri.L && (weight_bin(dv[e], mc, s).bin >> 4) <= bmine;
-        inU |= in ? 1u << e : 0u;
-        c += in ? 1u : 0u;
-    }
-    unsigned long long tot;
-    uint32_t o = base + (uint32_t)block_excl_scan_u64<256>(c, &tot, scan_sh);
-    unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * ws.ucap;
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-        if (inU & (1u << e))
-            ub[o++] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)(j0 + e));
 }
 
 // Cut among a candidate list held in LDS (cand = (score key << 32) | ~index,
@@ -749,36 +669,48 @@ __device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const flo
     return c;
 }
 
-// Resolve.  One 1024-thread workgroup per row: U with its exact weights, the
-// cut, and the selected indices in order (a list that did not fit: the cut
-// over the row's scores and per-chunk counts).
-// LDS of a row's cut (kRT threads).
+// The row's cut (kRT threads).  U with its exact weights, the cut, and the
+// selected indices in order.
+// LDS of a row's cut.
 struct ResolveSm {
     __align__(16) unsigned long long big[2 * kCand];   // U (index order) and its weights
     unsigned long long scan_sh[kRT / 64 + 1];
-    unsigned long long hmb[kNR];
-    uint32_t hcb[kNR];
-    uint32_t ccount[kMaxChunks];
+    union {
+        struct {
+            unsigned long long hmb[kNR];
+            uint32_t hcb[kNR];
+        } cut;
+        struct {                                      // the plan, before any cut
+            double fch[kMaxChunks], dch[kMaxChunks];
+            uint32_t uoff[kMaxChunks];                // each chunk's place in U
+            int16_t bsel[kMaxChunks];                 // each chunk's last bin in U (-1: none)
+            uint16_t nlist[kMaxChunks];               // entries of each chunk's candidate list
+        } plan;
+    };
     unsigned long long small_v[64], small_w[64];
+    double dred[kRT / 64];
+    uint32_t ured[kRT / 64];
+    int s_k[2];
     Cut s_cut;
     int s_i;
     uint32_t s_n;
     unsigned long long s_S;
 };
 
-// The cut of one row with nU keys in U (kRT threads), from its plan st: U
-// copied from the workspace list into LDS, U in the workspace list (weights
-// formed as needed), or the cut over the row's scores; writes the row's state
-// and, for a list, its selected keys.
-__device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, RowState st, int nU,
-                             ResolveSm& sm) {
+// The cut of one row with nU keys in U, from its plan st.  U is in LDS with
+// its weights (nU <= kCand, `loaded`), in the workspace list (nU <= ucap: read
+// into LDS, or read from there with weights formed as needed), or not
+// gathered (nU > ucap: the cut over the row's scores).  Writes the row's state
+// and its selected keys: the workspace list of the row (mode 1), or the
+// row's score array overwritten in place by the indices (mode 2).
+__device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, RowState st, int nU, bool loaded,
+                             int pflags, ResolveSm& sm) {
     const int tid = threadIdx.x;
     unsigned long long* cand = sm.big;
     unsigned long long* wgt = sm.big + kCand;
     unsigned long long* scan_sh = sm.scan_sh;
-    unsigned long long* hmb = sm.hmb;
-    uint32_t* hcb = sm.hcb;
-    uint32_t* ccount = sm.ccount;
+    unsigned long long* hmb = sm.cut.hmb;
+    uint32_t* hcb = sm.cut.hcb;
     unsigned long long* small_v = sm.small_v;
     unsigned long long* small_w = sm.small_w;
     Cut& s_cut = sm.s_cut;
@@ -786,18 +718,16 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
     uint32_t& s_n = sm.s_n;
     unsigned long long& s_S = sm.s_S;
     const float s = g.idx_scale;
-    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int nch = ri.nch;
+    float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const float m = st.m, d_thr = st.d_thr;
     unsigned long long target = st.target;
     bool unit = st.unit != 0;
-    const int lane = tid & 63;
     const uint32_t klo = d_thr == -INFINITY ? 0u : score_key(d_thr), khi = score_key(m);
     const auto selected_by = [](const Cut& c, uint32_t key, int j) { return key > c.Tkey || (key == c.Tkey && j <= c.jT); };
     if (nU <= ws.ucap) {
         const unsigned long long* ub = ws.ubuf + (size_t)ri.lrow * ws.ucap;
         const bool in_lds = nU <= kCand;
-        if (in_lds) {
+        if (in_lds && !loaded) {
             for (int i = tid; i < nU; i += kRT) {
                 const unsigned long long e = ub[i];
                 cand[i] = e;
@@ -852,33 +782,57 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
             st.jT = cut.jT;
             st.count = (int32_t)tot2;
             st.unit = unit;
-            st.path = (in_lds ? kPathList : kPathListG) | (unit ? kPathCount : 0);
+            st.path = (in_lds ? kPathList : kPathListG) | (unit ? kPathCount : 0) | pflags;
             ws.st[ri.lrow] = st;
         }
         return;
     }
-    // ---- U too large for LDS: the cut over the row's scores, selected keys per
-    // chunk for the ordered compaction
+    // ---- U larger than the workspace list: the cut over the row's scores
     Cut cut;
-    unsigned long long n_c, tot, ex;
+    unsigned long long tot;
     for (int pass = 0;; ++pass) {
-        for (int c = tid; c < kMaxChunks; c += kRT) ccount[c] = 0u;
-        __syncthreads();
         cut = radix_cut(cand, -1, srow, ri.L, klo, khi, 0ull, target, m, s, unit, hmb, hcb, scan_sh, &s_n, &s_S,
                         &s_i);
-        for (int j = tid; j < ri.L; j += kRT) {
-            const bool sel = selected_by(cut, score_key(srow[j]), j);
-            const unsigned long long b = __ballot(sel);
-            if (lane == 0 && b) atomicAdd(&ccount[j / kChunk], (uint32_t)__popcll(b));
-        }
-        __syncthreads();
-        n_c = tid < nch ? ccount[tid] : 0ull;
-        ex = block_excl_scan_u64<kRT>(n_c, &tot, scan_sh);
+        unsigned long long c = 0ull;
+        for (int j = tid; j < ri.L; j += kRT) c += selected_by(cut, score_key(srow[j]), j) ? 1ull : 0ull;
+        block_excl_scan_u64<kRT>(c, &tot, scan_sh);
         if (pass > 0 || unit || g.k_max <= 0 || tot <= (unsigned long long)g.k_max) break;
         unit = true;                                      // the budget cap, as above
         target = (unsigned long long)g.k_max;
     }
-    if (tid < nch) ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + tid] = (uint32_t)ex;
+    // the selected indices, ascending, over the row's scores (int32): blocks
+    // of 16 consecutive keys per thread; a block is read into registers before
+    // the block scan, and its writes land below its end, so no later read
+    // sees them
+    int32_t* orow = reinterpret_cast<int32_t*>(srow);
+    uint32_t base = 0u;
+    for (int j0 = 0; j0 < ri.L; j0 += 16 * kRT) {
+        const int jj = j0 + 16 * tid;
+        float dv[16];
+        if (jj < ri.L) {                                  // jj + 16 <= Lpad: the row is padded to whole chunks
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 v = *reinterpret_cast<const float4*>(srow + jj + 4 * u);
+                dv[4 * u] = v.x;
+                dv[4 * u + 1] = v.y;
+                dv[4 * u + 2] = v.z;
+                dv[4 * u + 3] = v.w;
+            }
+        }
+        uint32_t msk = 0u, c = 0u;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (jj + e < ri.L && selected_by(cut, score_key(dv[e]), jj + e)) {
+                msk |= 1u << e;
+                ++c;
+            }
+        unsigned long long t2;
+        uint32_t o = base + (uint32_t)block_excl_scan_u64<kRT>(c, &t2, scan_sh);
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            if (msk & (1u << e)) orow[o++] = jj + e;
+        base += (uint32_t)t2;
+    }
     if (tid == 0) {
         st.mode = 2;
         st.Tkey = cut.Tkey;
@@ -890,12 +844,143 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
     }
 }
 
-__global__ __launch_bounds__(kRT) void k_sel_resolve(Geo g, int row0, SelWs ws) {
+// Row pass.  One kRT-thread workgroup per row: the plan (from the scoring
+// pass's chunk statistics), U, the cut and the row's selected keys.  U comes
+// from the chunks' candidate lists when every chunk's part of U lies in its
+// list and U fits LDS; otherwise from the row's scores (into LDS, or into the
+// workspace list); beyond the workspace list the cut runs over the scores.
+__global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+                                                 int32_t* __restrict__ status) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const RowInfo ri = row_info(g, row0, blockIdx.x);
-    const RowState st = ws.st[ri.lrow];
-    if (st.mode == 0) return;
     __shared__ ResolveSm sm;
-    resolve_body(g, ri, ws, st, (int)ws.row_n[ri.lrow], sm);
+    const size_t crow = (size_t)ri.lrow * ws.nchunk;
+    const unsigned* ccnt = ws.ccnt + crow * kCB;
+    const Plan pl = row_plan<kRT>(g, ri, ws.chist + crow * kCB, ccnt, ws.cmax + crow, top_p, sm.plan.fch,
+                                  sm.plan.dch, sm.dred, sm.ured, sm.s_k);
+    RowState st;
+    st.m = pl.m;
+    st.L = ri.L;
+    st.Tkey = 0u;
+    st.jT = ri.L;
+    st.target = pl.target;
+    st.d_thr = pl.d_thr;
+    st.ks = pl.ks;
+    st.arrive = 0;
+    if (pl.all) {
+        if (tid == 0) {
+            st.mode = 0;
+            st.count = ri.L;
+            st.unit = 0;
+            st.path = kPathAll;
+            ws.st[ri.lrow] = st;
+            if (pl.bad) *status = 3;                      // invalid top_p: reported, nothing emitted
+        }
+        return;
+    }
+    st.mode = 1;
+    st.count = 0;
+    st.unit = pl.unit;
+    st.path = 0;
+    const bool unit = pl.unit != 0;
+    const float s = g.idx_scale;
+    // each chunk's part of U (its keys in bins <= bsel), and whether its
+    // candidate list holds that part
+    unsigned long long cnt_c = 0ull;
+    int cov = 1;
+    if (tid < ri.nch) {
+        const int b = chunk_bsel(pl.ks, sm.plan.dch[tid]);
+        const uint32_t h = ws.chdr[crow + tid];
+        cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
+        cov = b <= (int)(h & 255u) - 1;
+        sm.plan.bsel[tid] = (int16_t)b;
+        sm.plan.nlist[tid] = (uint16_t)(h >> 8);
+    }
+    unsigned long long nU;
+    const unsigned long long off_c = block_excl_scan_u64<kRT>(cnt_c, &nU, sm.scan_sh);
+    if (tid < ri.nch) sm.plan.uoff[tid] = (uint32_t)off_c;
+    const bool lists = __syncthreads_and(cov) && nU <= (unsigned long long)kCand;
+    const float m = pl.m;
+    bool loaded = false;                              // U and its weights in LDS
+    const int pflags = lists ? kPathChunkLists : 0;
+    if (lists) {
+        // U from the candidate lists: wave w takes chunks w, w + kRT / 64, ...;
+        // a list is in index order, so its filtered entries are too
+        unsigned long long* cand = sm.big;
+        unsigned long long* wgt = sm.big + kCand;
+        for (int c = wv; c < ri.nch; c += kRT / 64) {
+            const int bs = sm.plan.bsel[c];
+            if (bs < 0) continue;
+            const int n = sm.plan.nlist[c];
+            uint32_t o = sm.plan.uoff[c];
+            const unsigned long long* lp = ws.clist + (crow + c) * kNc;
+            unsigned long long e[kNc / 64];
+#pragma unroll
+            for (int t = 0; t < kNc / 64; ++t) e[t] = lane + 64 * t < n ? lp[lane + 64 * t] : 0ull;
+#pragma unroll
+            for (int t = 0; t < kNc / 64; ++t) {
+                const bool keep = lane + 64 * t < n && (int)((e[t] >> 12) & 127u) <= bs;
+                const unsigned long long bal = __ballot(keep);
+                if (keep) {
+                    const uint32_t at = o + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                    const uint32_t key = (uint32_t)(e[t] >> 32);
+                    const int j = c * kChunk + (int)(e[t] & 4095u);
+                    cand[at] = ((unsigned long long)key << 32) | (unsigned long long)(~(uint32_t)j);
+                    wgt[at] = unit ? 1ull : weight_bin(key_score(key), m, s).w;
+                }
+                o += (uint32_t)__popcll(bal);
+            }
+        }
+        loaded = true;
+    } else if (nU <= (unsigned long long)ws.ucap) {
+        // U from the row's scores, 16 consecutive keys per thread (one chunk),
+        // compacted in index order into LDS (with weights) or the workspace list
+        const bool to_lds = nU <= (unsigned long long)kCand;
+        unsigned long long* dst = to_lds ? sm.big : ws.ubuf + (size_t)ri.lrow * ws.ucap;
+        const uint32_t dcap = to_lds ? (uint32_t)kCand : (uint32_t)ws.ucap;
+        const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
+        uint32_t base = 0u;
+        for (int j0 = 0; j0 < ri.L; j0 += 16 * kRT) {
+            const int jj = j0 + 16 * tid;
+            uint32_t msk = 0u, c = 0u;
+            float dv[16];
+            if (jj < ri.L) {
+                const int ch = jj / kChunk;
+                const int bs = sm.plan.bsel[ch];
+                const float mc = key_score(ws.cmax[crow + ch]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float4 v = *reinterpret_cast<const float4*>(srow + jj + 4 * u);
+                    dv[4 * u] = v.x;
+                    dv[4 * u + 1] = v.y;
+                    dv[4 * u + 2] = v.z;
+                    dv[4 * u + 3] = v.w;
+                }
+                if (bs >= 0) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (jj + e < ri.L && (weight_bin(dv[e], mc, s).bin >> 4) <= bs) {
+                            msk |= 1u << e;
+                            ++c;
+                        }
+                }
+            }
+            unsigned long long t2;
+            uint32_t o = base + (uint32_t)block_excl_scan_u64<kRT>(c, &t2, sm.scan_sh);
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if ((msk & (1u << e)) && o < dcap) {
+                    dst[o] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)(jj + e));
+                    if (to_lds) sm.big[kCand + o] = unit ? 1ull : weight_bin(key_score(score_key(dv[e])), m, s).w;
+                    ++o;
+                }
+            base += (uint32_t)t2;
+        }
+        loaded = to_lds;
+    }
+    __syncthreads();
+    resolve_body(g, ri, ws, st, (int)nU, loaded, pflags, sm);
 }
 
 
@@ -921,11 +1006,11 @@ __global__ __launch_bounds__(kRT) void k_sel_rowptr(int row0, SelWs ws, SelOut o
 }
 
 // ---------------------------------------------------------------------------
-// Emit.  grid (min(nchunk, kEmitWG), rows), 256 threads: workgroup x writes the
-// parts of a row's output that belong to 4096-key chunks x, x + kEmitWG, ...
-// (slices of the ordered list, or the ordered compaction of a chunk's selected
-// keys).  ROWPTR: the group is small, so every workgroup sums the counts before
-// its row itself; the first one writes the row pointer and checks the capacity.
+// Emit.  grid (min(nchunk, kEmitWG), rows), 256 threads: workgroup x copies the
+// 4096-entry slices x, x + kEmitWG, ... of a row's ordered selected list (the
+// workspace list, the row's score array overwritten by indices, or every key).
+// ROWPTR: the group is small, so every workgroup sums the counts before its
+// row itself; the first one writes the row pointer and checks the capacity.
 // ---------------------------------------------------------------------------
 constexpr int kEmitWG = 4;
 
@@ -936,7 +1021,7 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
     const RowInfo ri = row_info(g, row0, blockIdx.y);
     const RowState st = ws.st[ri.lrow];
     if (first >= ri.nch) return;
-    if (first > 0 && st.mode == 1 && first * kChunk >= st.count) return;   // nothing of this row here
+    if (first > 0 && first * kChunk >= st.count) return;   // nothing of this row here
     int64_t rbase;
     if (ROWPTR) {
         __shared__ unsigned long long red[8];
@@ -965,46 +1050,12 @@ __global__ __launch_bounds__(256) void k_sel_emit(Geo g, int row0, SelWs ws, Sel
         rbase = out.row_ptr[ri.row];
     }
     if (*out.status != 0) return;
-    __shared__ uint32_t wcnt[4];
-    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
-    const int lane = tid & 63, wid = tid >> 6;
-    for (int chunk = first; chunk < ri.nch; chunk += gridDim.x) {
+    const uint32_t* src = st.mode == 1 ? ws.sel + (size_t)ri.lrow * ws.ucap
+                                       : reinterpret_cast<const uint32_t*>(ws.scores + (size_t)ri.lrow * ws.score_ld);
+    for (int chunk = first; chunk * kChunk < st.count; chunk += gridDim.x) {
         const int jbase = chunk * kChunk;
-        if (st.mode == 0) {
-            for (int k = tid; k < kChunk && jbase + k < ri.L; k += 256) out.idx[rbase + jbase + k] = jbase + k;
-            continue;
-        }
-        if (st.mode == 1) {
-            if (jbase >= st.count) break;
-            const uint32_t* sl = ws.sel + (size_t)ri.lrow * ws.ucap;
-            for (int k = tid; k < kChunk && jbase + k < st.count; k += 256)
-                out.idx[rbase + jbase + k] = (int32_t)sl[jbase + k];
-            continue;
-        }
-        int64_t base = rbase + ws.chunk_cnt[(size_t)ri.lrow * ws.nchunk + chunk];
-        float dv[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) dv[k] = srow[min(jbase + k * 256 + tid, ri.L - 1)];
-        for (int k = 0; k < 16; ++k) {
-            if (jbase + k * 256 >= ri.L) break;
-            const int j = jbase + k * 256 + tid;
-            bool sel = false;
-            if (j < ri.L) {
-                const uint32_t key = score_key(dv[k]);
-                sel = key > st.Tkey || (key == st.Tkey && j <= st.jT);
-            }
-            const unsigned long long bal = __ballot(sel);
-            const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-            if (lane == 0) wcnt[wid] = __popcll(bal);
-            __syncthreads();
-            uint32_t wbase = 0;
-            for (int w = 0; w < wid; ++w) wbase += wcnt[w];
-            const uint32_t tot = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-            const int64_t o = base + wbase + before;
-            if (sel && o < out.capacity) out.idx[o] = j;
-            base += tot;
-            __syncthreads();
-        }
+        for (int k = tid; k < kChunk && jbase + k < st.count; k += 256)
+            out.idx[rbase + jbase + k] = st.mode == 0 ? jbase + k : (int32_t)src[jbase + k];
     }
 }
 
@@ -1043,13 +1094,8 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
                                (const bf16_t*)w_q, kl, row0, ws, out);
     }
     if (scores_only || stage == kSelScorePass) return hipGetLastError();
-    if ((size_t)ws.rows * ws.nchunk <= kGatherResident) {
-        hipLaunchKernelGGL(k_sel_gather<true>, grid, dim3(256), 0, s, g, top_p, row0, ws, out.status);
-    } else {
-        hipLaunchKernelGGL(k_sel_plan, dim3(ws.rows), dim3(256), 0, s, g, top_p, row0, ws, out.status);
-        hipLaunchKernelGGL(k_sel_gather<false>, grid, dim3(256), 0, s, g, top_p, row0, ws, out.status);
-    }
-    hipLaunchKernelGGL(k_sel_resolve, dim3(ws.rows), dim3(kRT), 0, s, g, row0, ws);
+    hipLaunchKernelGGL(k_sel_row, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws, out.status);
+    if (stage == kSelRows) return hipGetLastError();
     const dim3 egrid(std::min(ws.nchunk, kEmitWG), ws.rows);
     if (ws.rows <= kRowsInEmit) {
         hipLaunchKernelGGL(k_sel_emit<1>, egrid, dim3(256), 0, s, g, row0, ws, out);

@@ -249,3 +249,27 @@ def test_noalloc_select_rejects_queries_beyond_its_scratch():
     assert b"scratch" in lib.rtp_last_error()
     assert fn(ctypes.byref(_layer(window=0)), ctypes.byref(C), ctypes.byref(Q), FAKE, FAKE, ctypes.byref(_sel()),
               None) == rtp.RTP_EINVAL
+
+
+def test_retrieval_decode_checks():
+    # the fused decode call checks its arguments on the host like the two
+    # calls it stands for (nothing is enqueued on an error)
+    lib = rtp.load()
+    L, C, Q = _layer(), _cache(), _query()
+    need = lib.rtp_retrieval_decode_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), 100)
+    sel_need = lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    sp_need = lib.rtp_sparse_attn_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), 100)
+    assert need == sel_need + sp_need
+    fn = lib.rtp_retrieval_decode
+
+    def call(layer=L, cache=C, query=Q, sel=None, out=FAKE, ws_bytes=need):
+        return fn(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), FAKE, FAKE,
+                  ctypes.byref(sel or _sel()), out, FAKE, ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == rtp.RTP_EWORKSPACE
+    assert call(out=None) == rtp.RTP_EINVAL
+    assert call(layer=_layer(window=0)) == rtp.RTP_EINVAL
+    assert call(query=_query(kind=rtp.RTP_CHUNK, n_tok=10)) == rtp.RTP_EINVAL
+    assert call(sel=_sel(capacity=-1)) == rtp.RTP_EINVAL
+    big = _cache(batch=1500, max_blocks=4, max_seq_len=1000)       # 4500 rows: more than the sparse kernel's 4096
+    assert call(cache=big, query=_query(n_tok=1500), ws_bytes=1 << 40) == rtp.RTP_EUNSUPPORTED

@@ -1,0 +1,173 @@
+"""GPU parity of rtp_retrieval_decode (the selection and sparse attention of a
+decode step's retrieval heads in one call) against rtp_topp_select followed by
+rtp_sparse_attn_decode, and against the oracle: same status, row pointers,
+selected indices and retrieval-head outputs, on every selection route (every
+key, candidate sets from the per-chunk lists, from the row's scores into LDS
+or the workspace list, and the cut over the row's scores)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import sparse_attention_dim_amd as rtp
+from gpu_util import Dev, band_accept, check_out, out_f32, path_counts, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _fused(d: Dev, capacity=None, top_p=None):
+    w = d.w
+    if capacity is None:
+        capacity = sum(w.row_pos(t) + 1 for t in range(w.n_tok)) * w.n_ret
+    row_ptr = torch.zeros(d.rows + 1, dtype=torch.int64, device="cuda")
+    idx = torch.full((max(capacity, 1),), -1, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    sel = rtp.make_sel(row_ptr, idx, status)
+    out = torch.zeros_like(d.q)
+    ws = torch.empty(rtp.retrieval_decode_workspace(d.layer, d.cache, d.query, sel.capacity), dtype=torch.uint8,
+                     device="cuda")
+    tp = d.top_p if top_p is None else torch.as_tensor(np.asarray(top_p, np.float32)).cuda()
+    rtp.retrieval_decode(d.layer, d.cache, d.query, d.w_q, tp, sel, out, ws)
+    torch.cuda.synchronize()
+    return int(status.item()), row_ptr.cpu().numpy(), idx.cpu().numpy(), out
+
+
+def _two_calls(d: Dev, capacity=None):
+    d.out.zero_()
+    st, rp, sets = d.select(capacity=capacity)
+    if st == 0:
+        d.sparse()
+    return st, rp, d.idx.cpu().numpy(), d.out.clone()
+
+
+def _same(d: Dev, a, b):
+    st1, rp1, ix1, o1 = a
+    st2, rp2, ix2, o2 = b
+    assert st1 == st2
+    np.testing.assert_array_equal(rp1, rp2)
+    n = int(rp1[-1]) if st1 == 0 else 0
+    np.testing.assert_array_equal(ix1[:n], ix2[:n])
+    ret = list(d.w.ret_heads)
+    assert torch.equal(o1[:, ret], o2[:, ret]), "retrieval-head outputs differ"
+
+
+@pytest.fixture(scope="module", params=[1, 2, 5], ids=["needle_f32", "cluster_bf16", "ragged_bf16"])
+def dev(request):
+    w = synth.small(request.param)
+    say("[gpu] fused retrieval decode", w.name, "lens", list(w.seq_lens))
+    return Dev(w)
+
+
+def test_fused_equals_two_calls_and_oracle(dev):
+    w = dev.w
+    a = _fused(dev)
+    b = _two_calls(dev)
+    _same(dev, a, b)
+    st, rp, ix, out = a
+    assert st == 0
+    o = out_f32(out)
+    for t in range(w.n_tok):
+        bq, pos = w.row_seq(t), w.row_pos(t)
+        for r, h in enumerate(w.ret_heads):
+            g = w.kv_head(h)
+            res = oracle.retrieval_row(w.q[t, h], w.k[bq][:, g, :], w.v[bq][:, g, :], w.w_q[r], w.w_k[r], pos,
+                                       w.idx_scale, float(w.top_p[bq]), w.attn_scale)
+            row = t * w.n_ret + r
+            got = ix[rp[row]: rp[row + 1]]
+            ok, _ = band_accept(got, res["order"], res["cum"], float(w.top_p[bq]))
+            assert ok, (t, r)
+            ref = oracle.attend(w.q[t, h], w.k[bq][:, g, :], w.v[bq][:, g, :], got, w.attn_scale)
+            assert check_out(o[t, h], ref, w.dtype) <= 1.0, (t, r)
+
+
+def test_candidate_lists_route_taken(dev):
+    # the planted workloads' candidate sets come from the scoring pass's
+    # per-chunk lists on most rows
+    st, rp, sets, paths = dev.select_mode()
+    assert st == 0
+    pc = path_counts(paths)
+    n_lists = int(np.sum((paths & rtp.PATH_CHUNK_LISTS) != 0))
+    say("   paths", pc, "chunk lists", n_lists, "of", dev.rows)
+    assert n_lists >= dev.rows // 2
+
+
+def _flat(lens, p, seed=77):
+    w = synth.cluster_decode(seed=seed, lens=lens, Hq=8, Hkv=2, D=128, n_ret=2, p=p, window=256, sinks=8,
+                             rope=1e4, size_dist=("loguniform", 4, 64), name="flat")
+    w.w_k = np.zeros_like(w.w_k)
+    return w
+
+
+def test_fused_long_rows_every_route():
+    # flat scores (one tie group per row): rows of 40000 keys take the cut
+    # over the scores (selected indices written over the scores), 20000 and
+    # 9001 keys the workspace list, 5000 keys the list gathered from the
+    # scores into LDS; p = 1 rows keep every key
+    w = _flat((40000, 20000, 9001, 5000, 3000), 0.999)
+    w.top_p[4] = 1.0
+    say("[gpu] fused retrieval decode, flat long rows")
+    d = Dev(w)
+    a = _fused(d)
+    b = _two_calls(d)
+    _same(d, a, b)
+    st, rp, ix, out = a
+    assert st == 0
+    _, _, _, paths = d.select_mode()
+    pc = path_counts(paths)
+    say("   paths", pc)
+    assert pc["scan"] == 2 and pc["list_g"] == 4 and pc["list"] == 2 and pc["all"] == 2
+    for t in range(w.n_tok):
+        L = w.row_pos(t) + 1
+        n = L if w.top_p[t] >= 1 else int(np.ceil(np.float64(np.float32(0.999)) * L))
+        for r in range(w.n_ret):
+            row = t * w.n_ret + r
+            np.testing.assert_array_equal(ix[rp[row]: rp[row + 1]], np.arange(n), err_msg=str((t, r)))
+    o = out_f32(out)
+    for t in range(w.n_tok):
+        for r, h in enumerate(w.ret_heads):
+            g = w.kv_head(h)
+            row = t * w.n_ret + r
+            ref = oracle.attend(w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], ix[rp[row]: rp[row + 1]],
+                                w.attn_scale)
+            assert check_out(o[t, h], ref, w.dtype) <= 1.0, (t, r)
+
+
+def test_fused_capacity_overflow():
+    w = synth.small(2)
+    say("[gpu] fused retrieval decode, capacity overflow")
+    d = Dev(w)
+    st, rp, ix, out = _fused(d)
+    need = int(rp[-1])
+    st2, rp2, ix2, out2 = _fused(d, capacity=need - 1)
+    assert st2 == 1 and int(rp2[-1]) == need
+    np.testing.assert_array_equal(rp2, rp)
+    assert np.all(ix2 == -1)
+    assert not torch.any(out2 != 0), "no attention output on overflow"
+    st3, rp3, ix3, out3 = _fused(d, capacity=need)
+    assert st3 == 0
+    assert torch.equal(out3, out)
+
+
+def test_fused_invalid_top_p():
+    w = synth.small(2)
+    say("[gpu] fused retrieval decode, invalid top_p")
+    d = Dev(w)
+    p = w.top_p.astype(np.float32).copy()
+    p[0] = float("nan")
+    st, rp, ix, out = _fused(d, top_p=p)
+    assert st == 3
+    assert np.all(ix == -1)
+    assert not torch.any(out != 0)
+
+
+def test_fused_repeated_calls_identical():
+    # every call rewrites the row records: calls with other top_p values in
+    # between leave the result unchanged
+    w = synth.small(5)
+    say("[gpu] fused retrieval decode, repeated calls")
+    d = Dev(w)
+    a = _fused(d)
+    _fused(d, top_p=np.full_like(w.top_p, 0.5))
+    b = _fused(d)
+    _same(d, a, b)
