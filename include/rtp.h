@@ -295,8 +295,9 @@ rtp_status rtp_topk_select(const rtp_layer *layer, const rtp_cache *cache, const
  * workspace -- and the
  * flags 16 (ordered through a bitmap) / 32 (ordered by merging runs), 64 (the
  * normaliser summed exactly over every key), 128 (the cut counted keys: top-k
- * or the k_max cap), 256 (decode path: the candidate set was taken from the
- * scoring pass's per-chunk candidate lists rather than the row's scores).  For the decode path and fp32 chunks only when every row
+ * or the k_max cap), 256 (decode path: the candidate set was gathered from
+ * the row's scores because it reaches past the keys the scoring pass flags,
+ * those within 4 units of s * (chunk maximum - score)).  For the decode path and fp32 chunks only when every row
  * fits one pass of the workspace (RTP_EUNSUPPORTED otherwise).
  */
 rtp_status rtp_topp_select_paths(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,

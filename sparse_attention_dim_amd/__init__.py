@@ -27,7 +27,7 @@ RTP_NOALLOC_SCRATCH_BYTES = 64 << 20
 SEL_OK, SEL_OVERFLOW, SEL_UNCERTIFIED, SEL_BAD_TOP_P = 0, 1, 2, 3
 # per-row path codes of rtp_topp_select_paths
 PATH_ALL, PATH_TINY, PATH_ROW, PATH_LARGE, PATH_LEVEL, PATH_LIST, PATH_SCAN, PATH_LIST_G = 1, 2, 3, 4, 5, 6, 7, 8
-PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT, PATH_CHUNK_LISTS = 16, 32, 64, 128, 256
+PATH_BITMAP, PATH_MERGE, PATH_EXACT_Z, PATH_COUNT, PATH_FROM_SCORES = 16, 32, 64, 128, 256
 
 ENTRY_POINTS = (
     "rtp_version", "rtp_last_error", "rtp_indexer_append", "rtp_kv_append", "rtp_topp_select_workspace",

@@ -78,12 +78,12 @@ __device__ __forceinline__ size_t kv_off(const Geo& g, int page, int kvh, int sl
     return kv_rowidx(g, page, kvh, slot) * (size_t)D;
 }
 
-template <typename T, int D, int NH>
+template <typename T, int D, int NH, int UR = (NH > 4 ? 4 : 8)>
 struct Stream {
     static constexpr int EPV = Pack<T>::N;      // elements per lane slice
     static constexpr int LPK = D / EPV;         // lanes per key row
     static constexpr int GPW = 64 / LPK;        // key rows per load instruction
-    static constexpr int U = NH > 4 ? 4 : 8;    // rows per group per iteration
+    static constexpr int U = UR;                // rows per group per iteration
 
     float q[NH][EPV];
     float m[NH], l[NH], o[NH][EPV];
@@ -200,6 +200,13 @@ struct Stream {
 constexpr int kItem = kSparseItem;
 static_assert(kItem % 64 == 0, "whole wavefronts of selected keys per item");
 
+// Rows per group and iteration of the sparse kernels: a whole item's K and V
+// rows are requested in one round (at most 16 row pairs per lane group).
+template <typename TKV, int D>
+constexpr int sparse_u() {
+    return kItem * D / (64 * Pack<TKV>::N) < 16 ? kItem * D / (64 * Pack<TKV>::N) : 16;
+}
+
 template <typename T, typename TKV, int D>
 __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restrict__ q,
                                                         const TKV* __restrict__ kc,
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
                                                         const int32_t* __restrict__ idx,
                                                         const int32_t* __restrict__ status,
                                                         AttnWs ws, int row0, int rows) {
-    using S = Stream<TKV, D, 1>;
+    using S = Stream<TKV, D, 1, sparse_u<TKV, D>()>;
     if (*status != 0) return;
     const int lane = threadIdx.x;
     extern __shared__ int64_t dyn[];
@@ -289,8 +296,11 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
 
 // Merge the n partial results of a row (stride D + 2: output[D], max, sum) in
 // item order on one wavefront: o[d] = sum_i 2^(m_i - M) o_i[d] / L * post.
+// Lane l owns dims l, l + 64, ...; the partials are read 16 items per round.
 template <typename T, int D>
 __device__ void combine_wave(const float* __restrict__ base, int n, T* __restrict__ o, float post) {
+    constexpr int DPL = D / 64;
+    constexpr int B = 16;
     const int lane = threadIdx.x & 63;
     float mx = -INFINITY;
     for (int i = lane; i < n; i += 64) mx = fmaxf(mx, base[(size_t)i * (D + 2) + D]);
@@ -299,34 +309,49 @@ __device__ void combine_wave(const float* __restrict__ base, int n, T* __restric
     for (int i = lane; i < n; i += 64)
         ls += exp2f(base[(size_t)i * (D + 2) + D] - M) * base[(size_t)i * (D + 2) + D + 1];
     const float L = wave_sum(ls);
-    for (int d = lane; d < D; d += 64) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int i = 0; i < n; ++i)
-            acc = __builtin_fmaf(base[(size_t)i * (D + 2) + d], exp2f(base[(size_t)i * (D + 2) + D] - M), acc);
-        st<T>(o + d, acc / L * post);
+    float acc[DPL];
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] = 0.0f;
+    for (int i0 = 0; i0 < n; i0 += B) {
+        float ov[B][DPL], mv[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int i = min(i0 + b, n - 1);
+            mv[b] = base[(size_t)i * (D + 2) + D];
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) ov[b][x] = base[(size_t)i * (D + 2) + lane + 64 * x];
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (i0 + b >= n) break;
+            const float w = exp2f(mv[b] - M);
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) acc[x] = __builtin_fmaf(ov[b][x], w, acc[x]);
+        }
     }
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) st<T>(o + lane + 64 * x, acc[x] / L * post);
 }
 
 // Sparse decode straight from the selection's row records (the work items of
 // k_sparse_dec_part): each row's selected keys are read from the selection
-// workspace (its ordered list, its score array overwritten by the indices, or
-// every key), and the items also write the CSR output -- the first workgroup
-// the row pointers and the capacity check, every item its own slice of idx.
-// The last item of a row to finish (a device-scope counter in the row's
-// record, after a release fence) merges the row's partials into the output.
-// Rows of one call only (row0 = 0).
+// workspace (its ordered list -- with the keys' K/V row numbers when the row
+// pass wrote them --, its score array overwritten by the indices, or every
+// key), and the items also write the CSR output: the first workgroup the row
+// pointers and the capacity check, every item its own slice of idx.  The
+// combine kernel merges each row's partials.  Rows of one call only (row0 = 0).
 template <typename T, typename TKV, int D>
 __global__ __launch_bounds__(64) void k_sparse_dec_sel(Geo g, const T* __restrict__ q,
                                                        const TKV* __restrict__ kc,
                                                        const TKV* __restrict__ vc, SelWs sw, SelOut so,
-                                                       AttnWs ws, T* __restrict__ out, int rows) {
-    using S = Stream<TKV, D, 1>;
+                                                       AttnWs ws, int rows) {
+    using S = Stream<TKV, D, 1, sparse_u<TKV, D>()>;
     if (*so.status != 0) return;                          // an invalid top_p was reported: nothing emitted
     const int lane = threadIdx.x;
     extern __shared__ int64_t dyn[];
     int64_t* rp = dyn;                                    // rows + 1
     int32_t* istart = reinterpret_cast<int32_t*>(dyn + rows + 1);   // rows + 1
+    int32_t* rinfo = istart + rows + 1;                   // rows: mode | has_jo << 8
     __shared__ uint32_t joff[kItem];
     {   // selected keys and pieces per row, and their prefixes (every workgroup)
         const int per = (rows + 63) / 64;
@@ -337,6 +362,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_sel(Geo g, const T* __restric
             const int r = r0 + i;
             if (r < rows) {
                 const int c = sw.st[r].count;
+                rinfo[r] = sw.st[r].mode | (sw.st[r].has_jo << 8);
                 cs += c;
                 run += (c + kItem - 1) / kItem;
             }
@@ -397,14 +423,15 @@ __global__ __launch_bounds__(64) void k_sparse_dec_sel(Geo g, const T* __restric
         const int h = g.ret_heads[r], kvh = h / g.group;
         const int k0 = (item - istart[row]) * kItem;
         const int n = (int)min<int64_t>(kItem, rp[row + 1] - rp[row] - k0);
-        const int mode = sw.st[row].mode;
+        const int mode = rinfo[row] & 255;
         const int32_t* bt = g.block_table + (size_t)row_seq(g, t) * g.max_blocks;
         const int i = k0 + min(lane, n - 1);
         const int j = mode == 0 ? i
                     : mode == 1 ? (int)sw.sel[(size_t)row * sw.ucap + i]
                                 : reinterpret_cast<const int32_t*>(sw.scores + (size_t)row * sw.score_ld)[i];
         if (lane < n) so.idx[rp[row] + k0 + lane] = j;
-        joff[lane] = (uint32_t)kv_rowidx(g, bt[j >> 8], kvh, j & 255);
+        joff[lane] = (rinfo[row] >> 8) ? reinterpret_cast<const uint32_t*>(sw.ubuf + (size_t)row * sw.ucap)[i]
+                                       : (uint32_t)kv_rowidx(g, bt[j >> 8], kvh, j & 255);
         S st;
         st.init();
         const int sl = (lane % LPK) * EPV;
@@ -416,18 +443,6 @@ __global__ __launch_bounds__(64) void k_sparse_dec_sel(Geo g, const T* __restric
         st.run(n, off, kc, vc);
         st.merge();
         st.write(0, ws.part + (size_t)item * (D + 2));
-        // the row's last item to finish merges the row's partial results
-        // (the row pass zeroed the row's arrival count)
-        const int nit = istart[row + 1] - istart[row];
-        __threadfence();
-        int last = 0;
-        if (lane == 0) last = atomicAdd(&sw.st[row].arrive, 1) == nit - 1;
-        last = __shfl(last, 0);
-        if (last) {
-            __threadfence();
-            combine_wave<T, D>(ws.part + (size_t)istart[row] * (D + 2), nit, out + ((size_t)t * g.Hq + h) * D,
-                               g.v_scale);   // the V scale of FP8 codes
-        }
         __syncthreads();
     }
 }
@@ -805,9 +820,10 @@ template <typename T, typename TKV, int D>
 hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
                           const SelOut& so, void* out, const AttnWs& ws, int rows, hipStream_t s) {
     const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
-    const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
+    const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1) + sizeof(int32_t) * rows;
     hipLaunchKernelGGL((k_sparse_dec_sel<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
-                       (const TKV*)k, (const TKV*)v, sw, so, ws, (T*)out, rows);
+                       (const TKV*)k, (const TKV*)v, sw, so, ws, rows);
+    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, so.status, ws, (T*)out, 0);
     return hipGetLastError();
 }
 

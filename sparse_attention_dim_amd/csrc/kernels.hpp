@@ -23,7 +23,7 @@ constexpr int kPathBitmap = 16;   // chunk path: ordered through a bitmap of the
 constexpr int kPathMerge = 32;    // chunk path: ordered by merging the writers' runs
 constexpr int kPathExactZ = 64;   // the normaliser was summed exactly over every key
 constexpr int kPathCount = 128;   // the cut counted keys (fixed top-k, or the budget cap)
-constexpr int kPathChunkLists = 256;  // decode path: U taken from the scoring pass's per-chunk candidate lists
+constexpr int kPathFromScores = 256;  // decode path: U gathered from the row's scores (not from the key masks)
 
 // Geometry of one call (host-filled, passed by value to kernels).
 struct Geo {
@@ -97,15 +97,15 @@ struct RowState {
     int32_t unit;                 // the cut counts keys (fixed top-k, or the budget cap)
     int32_t path;                 // kPath* code of the row
     int32_t ks;                   // candidate threshold of the plan: U = keys with s (m - d) < ks / 4 (+ margin)
-    int32_t arrive;               // sparse decode from the row records: items of the row finished (zeroed
-                                  // by the row pass)
+    int32_t has_jo;               // mode 1 cut in LDS: the K/V row numbers of the selected keys follow the
+                                  // list, as uint32 in the row's SelWs::ubuf
 };
 
 constexpr int kChunk = 4096;      // keys per workgroup of the scoring pass
 constexpr int kCB = 128;          // mass-histogram bins per chunk (1/4 unit of s (m_c - d) each)
 constexpr int kCand = 8192;       // candidates ranked in LDS
 constexpr int kCandG = 32768;     // candidates ranked from the workspace list (more: a cut over the scores)
-constexpr int kNc = 256;          // candidate-list entries per chunk written by the scoring pass
+constexpr int kLowBin = 15;       // chunk bins flagged per key by the scoring pass (x_c < 4 units)
 
 // Device workspace of the selection, for `rows` rows of at most Lpad keys.
 struct SelWs {
@@ -119,9 +119,7 @@ struct SelWs {
     unsigned long long* ubuf;     // [rows][ucap] U in index order when it is gathered from the scores and
                                   // exceeds LDS: (score key << 32) | ~index
     unsigned* ccnt;               // [rows][nchunk][kCB] cumulative key counts of the chunk bins
-    unsigned long long* clist;    // [rows][nchunk][kNc] each chunk's highest-ranked keys, index order:
-                                  // (score key << 32) | (chunk bin << 12) | (index - chunk start)
-    uint32_t* chdr;               // [rows][nchunk] (entries << 8) | (last chunk bin in the list + 1)
+    unsigned long long* kmask;    // [rows][Lpad / 64] bit j: key j lies in chunk bin <= kLowBin of its chunk
     int nchunk;
     int rows;                     // rows of this group
     int ucap;                     // row stride of ubuf / sel: min(kCandG, padded keys)

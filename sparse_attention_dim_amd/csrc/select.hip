@@ -47,7 +47,7 @@ namespace {
 
 constexpr float kCBPerUnit = 4.0f;   // chunk histogram bins per unit of x
 constexpr int kGB = 256;             // row threshold grid (same width), X = k / 4
-constexpr int kRT = 1024;            // resolve workgroup
+constexpr int kRT = 512;             // row workgroup
 constexpr int kNR = 2048;            // radix buckets of the narrowing fallback
 constexpr int kMaxChunks = 256;      // 2^20 keys
 
@@ -79,8 +79,8 @@ __device__ __forceinline__ RowInfo row_info(const Geo& g, int row0, int lrow) {
 // Scores.  grid (nchunk, rows), 256 threads.  Thread i of chunk c scores keys
 // c*4096 + 256*k + i, k = 0..15, i.e. slot i of the chunk's 16 pages: every
 // iteration reads one page's 8 KiB run of the head's indexer keys, coalesced.
-// STATS: also the chunk maximum, the chunk's mass histogram and its candidate
-// list (the keys of its lowest bins, at most kNc, in index order).
+// STATS: also the chunk maximum, the chunk's mass histogram and a bit per key
+// flagging chunk bins <= kLowBin.
 // ---------------------------------------------------------------------------
 template <typename T, int STATS>
 __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ q, const T* __restrict__ w_q,
@@ -100,8 +100,6 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     __shared__ __align__(16) float qrow[128];
     __shared__ __align__(16) float wq[128 * kIdx];
     __shared__ float qs[kIdx];
-    __shared__ int s_cbin;                                // last chunk bin of the candidate list
-    __shared__ uint32_t lcnt[64], loff[64];               // list entries per (key step, wave)
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int jbase = chunk * kChunk;
@@ -161,7 +159,6 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     if (STATS && tid < kCB) {
         hist[tid] = 0ull;
         hcnt[tid] = 0u;
-        if (tid == 0) s_cbin = -1;
     }
     __syncthreads();
     if (tid < kIdx) {
@@ -208,19 +205,22 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     const float mc = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     if (tid == 0) ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk] = score_key(mc);
     const float s = g.idx_scale;
-    // chunk bins of the thread's keys, one byte each (255: past the row's end)
-    uint32_t binp[4] = {0u, 0u, 0u, 0u};
+    // a bit per key for the row pass's gather of U: the key lies in chunk bin
+    // <= kLowBin (the wave's 64 consecutive keys of step k are one 64-bit word)
+    unsigned long long* km = ws.kmask + ((size_t)ri.lrow * ws.score_ld + jbase) / 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int j = jbase + k * 256 + tid;
-        uint32_t b = 255u;
+        bool low = false;
         if (j < ri.L) {
             const WeightBin wb = weight_bin(dv[k], mc, s);
-            b = (uint32_t)(wb.bin >> 4);                  // 64 level-1 bins per unit -> 4 per unit
+            const int b = wb.bin >> 4;                    // 64 level-1 bins per unit -> 4 per unit
             atomicAdd(&hist[b], wb.w);
             atomicAdd(&hcnt[b], 1u);
+            low = b <= kLowBin;
         }
-        binp[k >> 2] |= b << (8 * (k & 3));
+        const unsigned long long bal = __ballot(low);
+        if ((tid & 63) == 0) km[4 * k + (tid >> 6)] = bal;
     }
     __syncthreads();
     // cumulative over bins (the mass of keys with x_c < (b + 1) / 4)
@@ -247,47 +247,6 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         unsigned* cc = ws.ccnt + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
         cc[2 * t] = incl - b;
         cc[2 * t + 1] = incl;
-        // the list takes the lowest bins whose keys number at most kNc
-        if (incl - b <= (unsigned)kNc) atomicMax(&s_cbin, 2 * t);
-        if (incl <= (unsigned)kNc) atomicMax(&s_cbin, 2 * t + 1);
-    }
-    __syncthreads();
-    // the candidate list in index order (key j = jbase + 256 k + 64 wave + lane):
-    // per (k, wave) counts, their prefix by one wavefront, then the entries
-    const int cbin = s_cbin;
-    const int lane = tid & 63, wv = tid >> 6;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int b = (int)((binp[k >> 2] >> (8 * (k & 3))) & 255u);
-        const unsigned long long bal = __ballot(b <= cbin);
-        if (lane == 0) lcnt[4 * k + wv] = (uint32_t)__popcll(bal);
-    }
-    __syncthreads();
-    if (tid < 64) {
-        const uint32_t v = lcnt[tid];
-        uint32_t incl = v;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o);
-            if (tid >= o) incl += y;
-        }
-        loff[tid] = incl - v;
-        if (tid == 63)
-            ws.chdr[(size_t)ri.lrow * ws.nchunk + chunk] = (incl << 8) | (uint32_t)(cbin + 1);
-    }
-    __syncthreads();
-    unsigned long long* cl = ws.clist + ((size_t)ri.lrow * ws.nchunk + chunk) * kNc;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int b = (int)((binp[k >> 2] >> (8 * (k & 3))) & 255u);
-        const bool in = b <= cbin;
-        const unsigned long long bal = __ballot(in);
-        if (in) {
-            const uint32_t o = loff[4 * k + wv] + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            cl[o] = ((unsigned long long)score_key(dv[k]) << 32) | ((unsigned long long)b << 12) |
-                    (unsigned long long)(k * 256 + tid);
-        }
     }
 }
 
@@ -303,6 +262,53 @@ struct Cut {
     uint32_t Tkey;
     int32_t jT;
 };
+
+// One radix level's bucket search (kRT threads, kBPT buckets each; nb buckets
+// in use): the first bucket, highest keys first, whose cumulative mass (or
+// count) from S_hi reaches target and that holds a key -- or, when rounding
+// leaves the target unreached, the last bucket.  Leaves the mass ranked above
+// that bucket in *s_S and its key count in *s_u; returns its index.
+constexpr int kBPT = kNR / kRT;
+
+__device__ int bucket_search(const unsigned long long* hmb, const uint32_t* hcb, unsigned long long S_hi,
+                             unsigned long long target, int nb, unsigned long long* scan_sh, int* s_i,
+                             unsigned long long* s_S, uint32_t* s_u) {
+    const int tid = threadIdx.x;
+    unsigned long long loc = 0ull;
+#pragma unroll
+    for (int b = 0; b < kBPT; ++b) loc += hmb[kBPT * tid + b];
+    unsigned long long tot;
+    const unsigned long long ex = S_hi + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
+    if (tid == 0) *s_i = kNR;
+    __syncthreads();
+    unsigned long long run = ex;
+#pragma unroll
+    for (int b = 0; b < kBPT; ++b) {
+        const int i = kBPT * tid + b;
+        if (run + hmb[i] >= target && hcb[i]) {
+            atomicMin(s_i, i);
+            break;
+        }
+        run += hmb[i];
+    }
+    __syncthreads();
+    int bk = *s_i;
+    // the mass ranked above the bucket, from the thread that holds it
+    if (bk < kNR && bk / kBPT == tid) {
+        unsigned long long above = ex;
+        for (int b = 0; b < bk % kBPT; ++b) above += hmb[kBPT * tid + b];
+        *s_S = above;
+        *s_u = hcb[bk];
+    }
+    if (bk >= kNR && tid == 0) {
+        // the target is not reached (rounding): the last bucket
+        *s_S = S_hi + tot - hmb[nb - 1];
+        *s_u = hcb[nb - 1];
+    }
+    if (bk >= kNR) bk = nb - 1;
+    __syncthreads();
+    return bk;
+}
 
 __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* srow, int L, uint32_t klo,
                          uint32_t khi, unsigned long long S_hi, unsigned long long target, float m, float s,
@@ -338,28 +344,8 @@ __device__ Cut radix_cut(const unsigned long long* cand, int n, const float* sro
         }
         __syncthreads();
         // first bucket (highest keys first) whose cumulative mass (or count) reaches target
-        unsigned long long loc = hmb[2 * tid] + hmb[2 * tid + 1];
-        unsigned long long tot;
-        const unsigned long long ex = S_hi + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
-        if (tid == 0) *s_i = kNR;
-        __syncthreads();
-        if (ex + hmb[2 * tid] >= target && hcb[2 * tid]) atomicMin(s_i, 2 * tid);
-        else if (ex + loc >= target && hcb[2 * tid + 1]) atomicMin(s_i, 2 * tid + 1);
-        __syncthreads();
         const int nb = (int)(span >> shift) + 1;
-        int bk = *s_i;
-        // the mass ranked above the bucket, from the thread that holds it
-        if (bk < kNR && (bk >> 1) == tid) {
-            *s_S = (bk & 1) ? ex + hmb[2 * tid] : ex;
-            *s_u = hcb[bk];
-        }
-        if (bk >= kNR && tid == 0) {
-            // the target is not reached (rounding): the last bucket
-            *s_S = S_hi + tot - hmb[nb - 1];
-            *s_u = hcb[nb - 1];
-        }
-        if (bk >= kNR) bk = nb - 1;
-        __syncthreads();
+        const int bk = bucket_search(hmb, hcb, S_hi, target, nb, scan_sh, s_i, s_S, s_u);
         const unsigned long long S_b = *s_S;
         const uint32_t n_b = *s_u;
         const uint32_t nkhi = khi - ((uint32_t)bk << shift);
@@ -437,17 +423,15 @@ struct Plan {
 // chunk statistics (device memory or an LDS copy).
 template <int NT>
 __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long long* __restrict__ chist,
-                         const unsigned* __restrict__ ccnt, const uint32_t* __restrict__ cmax,
-                         const float* __restrict__ top_p, double* fch, double* dch, double* dred, uint32_t* ured,
-                         int* s_k) {
+                         const unsigned* __restrict__ ccnt, const uint32_t* __restrict__ cmax, float p,
+                         double* fch, double* dch, double* dred, uint32_t* ured, int* s_k) {
     const int tid = threadIdx.x;
     const int nch = ri.nch;
     const float s = g.idx_scale;
-    // one round of loads: the chunk's maximum and total mass (one chunk per
-    // thread, nch <= 256) and p
+    // the chunk's maximum and total mass (one chunk per thread, nch <= 256);
+    // p is the row's top_p (1 for a fixed top-k)
     const uint32_t cm = tid < nch ? cmax[tid] : 0u;
     const unsigned long long ztot = tid < nch ? chist[(size_t)tid * kCB + kCB - 1] : 0ull;
-    const float p = g.sel_k > 0 ? 1.0f : top_p[ri.b];
     // a count target: the fixed top-k budget, or the cap of a keep-all row
     const int kc = g.sel_k > 0 ? g.sel_k : (!(p < 1.0f) && g.k_max > 0 ? g.k_max : 0);
     uint32_t mk = wave_max_u32(cm);
@@ -557,26 +541,8 @@ __device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const flo
             atomicAdd(&hcb[bk], 1u);
         }
         __syncthreads();
-        const unsigned long long loc = hmb[2 * tid] + hmb[2 * tid + 1];
-        unsigned long long tot;
-        const unsigned long long ex = S_hi + block_excl_scan_u64<kRT>(loc, &tot, scan_sh);
-        if (tid == 0) *s_i = kNR;
-        __syncthreads();
-        if (ex + hmb[2 * tid] >= target && hcb[2 * tid]) atomicMin(s_i, 2 * tid);
-        else if (ex + loc >= target && hcb[2 * tid + 1]) atomicMin(s_i, 2 * tid + 1);
-        __syncthreads();
         const int nb = (int)(span >> shift) + 1;
-        int bk = *s_i;
-        if (bk < kNR && (bk >> 1) == tid) {
-            *s_S = (bk & 1) ? ex + hmb[2 * tid] : ex;
-            *s_u = hcb[bk];
-        }
-        if (bk >= kNR && tid == 0) {
-            *s_S = S_hi + tot - hmb[nb - 1];
-            *s_u = hcb[nb - 1];
-        }
-        if (bk >= kNR) bk = nb - 1;
-        __syncthreads();
+        const int bk = bucket_search(hmb, hcb, S_hi, target, nb, scan_sh, s_i, s_S, s_u);
         S_hi = *s_S;
         const uint32_t n_b = *s_u;
         const uint32_t nkhi = khi - ((uint32_t)bk << shift);
@@ -671,6 +637,7 @@ __device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const flo
 
 // The row's cut (kRT threads).  U with its exact weights, the cut, and the
 // selected indices in order.
+constexpr int kBtCache = 1536;                        // page ids cached in LDS: rows of up to 393216 keys
 // LDS of a row's cut.
 struct ResolveSm {
     __align__(16) unsigned long long big[2 * kCand];   // U (index order) and its weights
@@ -682,12 +649,12 @@ struct ResolveSm {
         } cut;
         struct {                                      // the plan, before any cut
             double fch[kMaxChunks], dch[kMaxChunks];
-            uint32_t uoff[kMaxChunks];                // each chunk's place in U
             int16_t bsel[kMaxChunks];                 // each chunk's last bin in U (-1: none)
-            uint16_t nlist[kMaxChunks];               // entries of each chunk's candidate list
+            float mc[kMaxChunks];                     // each chunk's maximum score (the gather of U)
         } plan;
     };
     unsigned long long small_v[64], small_w[64];
+    int32_t btc[kBtCache];                            // the row's page ids (rows of at most kBtCache pages)
     double dred[kRT / 64];
     uint32_t ured[kRT / 64];
     int s_k[2];
@@ -704,7 +671,7 @@ struct ResolveSm {
 // and its selected keys: the workspace list of the row (mode 1), or the
 // row's score array overwritten in place by the indices (mode 2).
 __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, RowState st, int nU, bool loaded,
-                             int pflags, ResolveSm& sm) {
+                             bool bt_cached, ResolveSm& sm) {
     const int tid = threadIdx.x;
     unsigned long long* cand = sm.big;
     unsigned long long* wgt = sm.big + kCand;
@@ -767,13 +734,21 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
                 __syncthreads();
             }
         }
-        // U is in index order: its selected entries, in order, into the row's list
+        // U is in index order: its selected entries, in order, into the row's
+        // list; a list cut in LDS also gets the K/V row numbers of its keys
+        // (page ids from the LDS cache) in the row's unused workspace list
         uint32_t* sl = ws.sel + (size_t)ri.lrow * ws.ucap;
+        uint32_t* jo = reinterpret_cast<uint32_t*>(ws.ubuf + (size_t)ri.lrow * ws.ucap);
+        const bool with_jo = in_lds && bt_cached;
+        const int kvh = g.ret_heads[ri.r] / g.group;
         for (int x = 0; x < per; ++x) {
             const int i = tid * per + x;
             if (i < nU) {
                 const int j = (int)~(uint32_t)cl[i];
-                if (selected_by(cut, (uint32_t)(cl[i] >> 32), j)) sl[o++] = (uint32_t)j;
+                if (selected_by(cut, (uint32_t)(cl[i] >> 32), j)) {
+                    if (with_jo) jo[o] = (uint32_t)kv_rowidx(g, sm.btc[j >> 8], kvh, j & 255);
+                    sl[o++] = (uint32_t)j;
+                }
             }
         }
         if (tid == 0) {
@@ -782,7 +757,8 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
             st.jT = cut.jT;
             st.count = (int32_t)tot2;
             st.unit = unit;
-            st.path = (in_lds ? kPathList : kPathListG) | (unit ? kPathCount : 0) | pflags;
+            st.path = (in_lds ? kPathList : kPathListG) | (unit ? kPathCount : 0) | st.path;
+            st.has_jo = with_jo;
             ws.st[ri.lrow] = st;
         }
         return;
@@ -844,20 +820,79 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
     }
 }
 
-// Row pass.  One kRT-thread workgroup per row: the plan (from the scoring
-// pass's chunk statistics), U, the cut and the row's selected keys.  U comes
-// from the chunks' candidate lists when every chunk's part of U lies in its
-// list and U fits LDS; otherwise from the row's scores (into LDS, or into the
-// workspace list); beyond the workspace list the cut runs over the scores.
+// Row pass.  One kRT-thread workgroup per row: the plan, from the scoring
+// pass's chunk statistics (staged in LDS with the row's key masks when the
+// row has at most kStageChunks chunks, so that the plan makes no dependent
+// global round); U; the cut; the row's selected keys.  U is found without
+// reading the row's scores when every chunk's part of U lies in its chunk bins
+// <= kLowBin: the keys the masks flag in those chunks (S0, a superset of U)
+// are compacted in index order, their scores read (all loads in flight), their
+// chunk bins formed again and U kept in place.  Otherwise U comes from a pass
+// over the row's scores.
+constexpr int kStageChunks = 48;   // chist (48 KiB) + ccnt (24 KiB) + key masks (24 KiB) + cmax of 48 chunks
+
 __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
                                                  int32_t* __restrict__ status) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.x);
     __shared__ ResolveSm sm;
     const size_t crow = (size_t)ri.lrow * ws.nchunk;
+    const unsigned long long* chist = ws.chist + crow * kCB;
     const unsigned* ccnt = ws.ccnt + crow * kCB;
-    const Plan pl = row_plan<kRT>(g, ri, ws.chist + crow * kCB, ccnt, ws.cmax + crow, top_p, sm.plan.fch,
-                                  sm.plan.dch, sm.dred, sm.ured, sm.s_k);
+    const uint32_t* cmax = ws.cmax + crow;
+    const unsigned long long* kmask = ws.kmask + (size_t)ri.lrow * ws.score_ld / 64;
+    const int nwd = (ri.L + 63) / 64;                     // mask words of the row
+    const float p = g.sel_k > 0 ? 1.0f : top_p[ri.b];
+    const int npg = (ri.L + kBlk - 1) / kBlk;
+    const bool bt_cached = npg <= kBtCache;
+    if (bt_cached) {
+        const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
+        for (int i = tid; i < npg; i += kRT) sm.btc[i] = bt[i];
+    }
+    if (ri.nch <= kStageChunks) {
+        // one round of loads: every chunk's histograms, maximum and key masks into LDS
+        unsigned long long* hs = sm.big;
+        unsigned* cs = reinterpret_cast<unsigned*>(sm.big + kStageChunks * kCB);
+        unsigned long long* ks = sm.big + kStageChunks * kCB * 3 / 2;
+        uint32_t* ms = reinterpret_cast<uint32_t*>(ks + kStageChunks * (kChunk / 64));
+        constexpr int kPer = kStageChunks * kCB / kRT;
+        constexpr int kPerM = kStageChunks * (kChunk / 64) / kRT;
+        const int n = ri.nch * kCB;
+        unsigned long long hv[kPer], kv[kPerM];
+        unsigned cv[kPer];
+        const uint32_t mv = tid < ri.nch ? cmax[tid] : 0u;
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {                  // every load in flight before the first store
+            const int i = tid + kRT * x;
+            hv[x] = i < n ? chist[i] : 0ull;
+            cv[x] = i < n ? ccnt[i] : 0u;
+        }
+#pragma unroll
+        for (int x = 0; x < kPerM; ++x) {
+            const int i = tid + kRT * x;
+            kv[x] = i < nwd ? kmask[i] : 0ull;
+        }
+#pragma unroll
+        for (int x = 0; x < kPer; ++x) {
+            const int i = tid + kRT * x;
+            if (i < n) {
+                hs[i] = hv[x];
+                cs[i] = cv[x];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < kPerM; ++x) {
+            const int i = tid + kRT * x;
+            if (i < nwd) ks[i] = kv[x];
+        }
+        if (tid < ri.nch) ms[tid] = mv;
+        __syncthreads();
+        chist = hs;
+        ccnt = cs;
+        cmax = ms;
+        kmask = ks;
+    }
+    const Plan pl = row_plan<kRT>(g, ri, chist, ccnt, cmax, p, sm.plan.fch, sm.plan.dch, sm.dred, sm.ured, sm.s_k);
     RowState st;
     st.m = pl.m;
     st.L = ri.L;
@@ -866,7 +901,7 @@ __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict_
     st.target = pl.target;
     st.d_thr = pl.d_thr;
     st.ks = pl.ks;
-    st.arrive = 0;
+    st.has_jo = 0;
     if (pl.all) {
         if (tid == 0) {
             st.mode = 0;
@@ -884,62 +919,107 @@ __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict_
     st.path = 0;
     const bool unit = pl.unit != 0;
     const float s = g.idx_scale;
-    // each chunk's part of U (its keys in bins <= bsel), and whether its
-    // candidate list holds that part
+    const float m = pl.m;
+    // each chunk's part of U: its keys in chunk bins <= bsel; the masks hold
+    // it when bsel <= kLowBin
     unsigned long long cnt_c = 0ull;
     int cov = 1;
     if (tid < ri.nch) {
         const int b = chunk_bsel(pl.ks, sm.plan.dch[tid]);
-        const uint32_t h = ws.chdr[crow + tid];
         cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
-        cov = b <= (int)(h & 255u) - 1;
+        cov = b <= kLowBin;
         sm.plan.bsel[tid] = (int16_t)b;
-        sm.plan.nlist[tid] = (uint16_t)(h >> 8);
+        sm.plan.mc[tid] = key_score(cmax[tid]);           // out of the staging area, which U overwrites
     }
     unsigned long long nU;
-    const unsigned long long off_c = block_excl_scan_u64<kRT>(cnt_c, &nU, sm.scan_sh);
-    if (tid < ri.nch) sm.plan.uoff[tid] = (uint32_t)off_c;
-    const bool lists = __syncthreads_and(cov) && nU <= (unsigned long long)kCand;
-    const float m = pl.m;
-    bool loaded = false;                              // U and its weights in LDS
-    const int pflags = lists ? kPathChunkLists : 0;
-    if (lists) {
-        // U from the candidate lists: wave w takes chunks w, w + kRT / 64, ...;
-        // a list is in index order, so its filtered entries are too
-        unsigned long long* cand = sm.big;
-        unsigned long long* wgt = sm.big + kCand;
-        for (int c = wv; c < ri.nch; c += kRT / 64) {
-            const int bs = sm.plan.bsel[c];
-            if (bs < 0) continue;
-            const int n = sm.plan.nlist[c];
-            uint32_t o = sm.plan.uoff[c];
-            const unsigned long long* lp = ws.clist + (crow + c) * kNc;
-            unsigned long long e[kNc / 64];
+    block_excl_scan_u64<kRT>(cnt_c, &nU, sm.scan_sh);
+    const bool covered = __syncthreads_and(cov) != 0;
+    const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
+    unsigned long long* gdst = ws.ubuf + (size_t)ri.lrow * ws.ucap;
+    // S0: the flagged keys of the chunks with a part of U (covered rows)
+    uint32_t nS0 = 0u;
+    if (covered) {
+        uint32_t c = 0u;
+        for (int wi = tid; wi < nwd; wi += kRT)
+            if (sm.plan.bsel[wi / (kChunk / 64)] >= 0) c += (uint32_t)__popcll(kmask[wi]);
+        nS0 = block_sum_u32<kRT>(c, sm.ured);
+    }
+    bool loaded = false;                                  // U and its weights in LDS
+    if (covered && nS0 <= (uint32_t)ws.ucap) {
+        const bool to_lds = nS0 <= (uint32_t)kCand;
+        // pass 1: S0's indices in index order (4 mask words = 256 keys per thread and step)
+        uint32_t base = 0u;
+        for (int w0 = 0; w0 < nwd; w0 += 4 * kRT) {
+            unsigned long long mw[4];
+            uint32_t c = 0u;
 #pragma unroll
-            for (int t = 0; t < kNc / 64; ++t) e[t] = lane + 64 * t < n ? lp[lane + 64 * t] : 0ull;
-#pragma unroll
-            for (int t = 0; t < kNc / 64; ++t) {
-                const bool keep = lane + 64 * t < n && (int)((e[t] >> 12) & 127u) <= bs;
-                const unsigned long long bal = __ballot(keep);
-                if (keep) {
-                    const uint32_t at = o + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                    const uint32_t key = (uint32_t)(e[t] >> 32);
-                    const int j = c * kChunk + (int)(e[t] & 4095u);
-                    cand[at] = ((unsigned long long)key << 32) | (unsigned long long)(~(uint32_t)j);
-                    wgt[at] = unit ? 1ull : weight_bin(key_score(key), m, s).w;
-                }
-                o += (uint32_t)__popcll(bal);
+            for (int x = 0; x < 4; ++x) {
+                const int wi = w0 + 4 * tid + x;
+                mw[x] = wi < nwd && sm.plan.bsel[wi / (kChunk / 64)] >= 0 ? kmask[wi] : 0ull;
+                c += (uint32_t)__popcll(mw[x]);
             }
+            unsigned long long t2;
+            uint32_t o = base + (uint32_t)block_excl_scan_u64<kRT>(c, &t2, sm.scan_sh);
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                unsigned long long mm = mw[x];
+                while (mm) {
+                    const int e = __ffsll((long long)mm) - 1;
+                    mm &= mm - 1ull;
+                    const unsigned long long ent = (unsigned long long)(~(uint32_t)(64 * (w0 + 4 * tid + x) + e));
+                    if (to_lds) sm.big[o] = ent; else gdst[o] = ent;
+                    ++o;
+                }
+            }
+            base += (uint32_t)t2;
         }
-        loaded = true;
+        __syncthreads();
+        // pass 2: S0's scores (every load of a batch in flight together), their
+        // chunk bins formed again, U kept in place in index order (a batch's
+        // entries are all read before the block scan that orders its writes)
+        constexpr int R = 16;
+        uint32_t ubase = 0u;
+        for (uint32_t i0 = 0; i0 < nS0; i0 += R * kRT) {
+            const uint32_t ib = i0 + R * tid;             // the thread's R consecutive entries
+            uint32_t jx[R];
+            float dv[R];
+#pragma unroll
+            for (int x = 0; x < R; ++x)
+                jx[x] = ib + x < nS0 ? ~(uint32_t)(to_lds ? sm.big[ib + x] : gdst[ib + x]) : 0u;
+#pragma unroll
+            for (int x = 0; x < R; ++x) dv[x] = ib + x < nS0 ? srow[jx[x]] : 0.0f;
+            uint32_t keep = 0u;
+#pragma unroll
+            for (int x = 0; x < R; ++x) {
+                if (ib + x >= nS0) continue;
+                const int ch = (int)(jx[x] / kChunk);
+                if ((weight_bin(dv[x], sm.plan.mc[ch], s).bin >> 4) <= sm.plan.bsel[ch]) keep |= 1u << x;
+            }
+            unsigned long long t2;
+            uint32_t o = ubase + (uint32_t)block_excl_scan_u64<kRT>((unsigned long long)__popc(keep), &t2, sm.scan_sh);
+#pragma unroll
+            for (int x = 0; x < R; ++x) {
+                if (!((keep >> x) & 1u)) continue;
+                const uint32_t key = score_key(dv[x]);
+                const unsigned long long ent = ((unsigned long long)key << 32) | (unsigned long long)(~jx[x]);
+                if (to_lds) {
+                    sm.big[o] = ent;
+                    sm.big[kCand + o] = unit ? 1ull : weight_bin(key_score(key), m, s).w;
+                } else {
+                    gdst[o] = ent;
+                }
+                ++o;
+            }
+            ubase += (uint32_t)t2;
+        }
+        nU = ubase;
+        loaded = to_lds;
     } else if (nU <= (unsigned long long)ws.ucap) {
+        st.path = kPathFromScores;
         // U from the row's scores, 16 consecutive keys per thread (one chunk),
         // compacted in index order into LDS (with weights) or the workspace list
         const bool to_lds = nU <= (unsigned long long)kCand;
-        unsigned long long* dst = to_lds ? sm.big : ws.ubuf + (size_t)ri.lrow * ws.ucap;
         const uint32_t dcap = to_lds ? (uint32_t)kCand : (uint32_t)ws.ucap;
-        const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
         uint32_t base = 0u;
         for (int j0 = 0; j0 < ri.L; j0 += 16 * kRT) {
             const int jj = j0 + 16 * tid;
@@ -948,7 +1028,7 @@ __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict_
             if (jj < ri.L) {
                 const int ch = jj / kChunk;
                 const int bs = sm.plan.bsel[ch];
-                const float mc = key_score(ws.cmax[crow + ch]);
+                const float mc = sm.plan.mc[ch];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const float4 v = *reinterpret_cast<const float4*>(srow + jj + 4 * u);
@@ -971,8 +1051,14 @@ __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict_
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 if ((msk & (1u << e)) && o < dcap) {
-                    dst[o] = ((unsigned long long)score_key(dv[e]) << 32) | (unsigned long long)(~(uint32_t)(jj + e));
-                    if (to_lds) sm.big[kCand + o] = unit ? 1ull : weight_bin(key_score(score_key(dv[e])), m, s).w;
+                    const uint32_t key = score_key(dv[e]);
+                    const unsigned long long ent = ((unsigned long long)key << 32) | (unsigned long long)(~(uint32_t)(jj + e));
+                    if (to_lds) {
+                        sm.big[o] = ent;
+                        sm.big[kCand + o] = unit ? 1ull : weight_bin(key_score(key), m, s).w;
+                    } else {
+                        gdst[o] = ent;
+                    }
                     ++o;
                 }
             base += (uint32_t)t2;
@@ -980,7 +1066,7 @@ __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict_
         loaded = to_lds;
     }
     __syncthreads();
-    resolve_body(g, ri, ws, st, (int)nU, loaded, pflags, sm);
+    resolve_body(g, ri, ws, st, (int)nU, loaded, bt_cached, sm);
 }
 
 

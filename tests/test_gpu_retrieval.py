@@ -2,8 +2,8 @@
 decode step's retrieval heads in one call) against rtp_topp_select followed by
 rtp_sparse_attn_decode, and against the oracle: same status, row pointers,
 selected indices and retrieval-head outputs, on every selection route (every
-key, candidate sets from the per-chunk lists, from the row's scores into LDS
-or the workspace list, and the cut over the row's scores)."""
+key, candidate sets cut in LDS or from the workspace list, and the cut over
+the row's scores)."""
 import numpy as np
 import pytest
 import torch
@@ -81,15 +81,13 @@ def test_fused_equals_two_calls_and_oracle(dev):
             assert check_out(o[t, h], ref, w.dtype) <= 1.0, (t, r)
 
 
-def test_candidate_lists_route_taken(dev):
-    # the planted workloads' candidate sets come from the scoring pass's
-    # per-chunk lists on most rows
+def test_lds_route_taken(dev):
+    # the planted workloads' candidate sets are small: most rows are cut in LDS
     st, rp, sets, paths = dev.select_mode()
     assert st == 0
     pc = path_counts(paths)
-    n_lists = int(np.sum((paths & rtp.PATH_CHUNK_LISTS) != 0))
-    say("   paths", pc, "chunk lists", n_lists, "of", dev.rows)
-    assert n_lists >= dev.rows // 2
+    say("   paths", pc, "of", dev.rows)
+    assert pc["list"] >= dev.rows // 2
 
 
 def _flat(lens, p, seed=77):
@@ -130,6 +128,38 @@ def test_fused_long_rows_every_route():
             row = t * w.n_ret + r
             ref = oracle.attend(w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], ix[rp[row]: rp[row + 1]],
                                 w.attn_scale)
+            assert check_out(o[t, h], ref, w.dtype) <= 1.0, (t, r)
+
+
+def test_fused_spread_rows_gather_from_scores():
+    # indexer keys scaled x4 spread the scores: the top-p sets reach more than
+    # 4 units below their chunk maxima, past the keys the scoring pass flags,
+    # so U is gathered from the rows' scores
+    w = synth.small(2)
+    w.w_k = synth.to_storage(synth.as_f32(w.w_k) * np.float32(4.0), w.dtype)     # exact: a power of two
+    w.top_p = np.full_like(w.top_p, 0.99)
+    say("[gpu] fused retrieval decode, spread scores")
+    d = Dev(w)
+    a = _fused(d)
+    b = _two_calls(d)
+    _same(d, a, b)
+    st, rp, ix, out = a
+    assert st == 0
+    _, _, _, paths = d.select_mode()
+    pc = path_counts(paths)
+    say("   paths", pc)
+    assert pc["from_scores"] >= 1
+    o = out_f32(out)
+    for t in range(w.n_tok):
+        for r, h in enumerate(w.ret_heads):
+            g = w.kv_head(h)
+            res = oracle.retrieval_row(w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], w.w_q[r], w.w_k[r],
+                                       w.row_pos(t), w.idx_scale, float(w.top_p[t]), w.attn_scale)
+            row = t * w.n_ret + r
+            got = ix[rp[row]: rp[row + 1]]
+            ok, _ = band_accept(got, res["order"], res["cum"], float(w.top_p[t]))
+            assert ok, (t, r)
+            ref = oracle.attend(w.q[t, h], w.k[t][:, g, :], w.v[t][:, g, :], got, w.attn_scale)
             assert check_out(o[t, h], ref, w.dtype) <= 1.0, (t, r)
 
 
