@@ -326,8 +326,7 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
         sel = rtp.make_sel(row_ptr, idx, status)
         ws_sel = torch.empty(rtp.topp_select_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
         ws_sp = torch.empty(rtp.sparse_attn_workspace(layer, cache, query, cap), dtype=torch.uint8, device=dev)
-        ws_ret = torch.empty(rtp.retrieval_decode_workspace(layer, cache, query, cap), dtype=torch.uint8,
-                             device=dev)
+        ws_ret = torch.empty(rtp.decode_attn_workspace(layer, cache, query, cap), dtype=torch.uint8, device=dev)
         ws_win = torch.empty(rtp.window_attn_workspace(layer, cache, query), dtype=torch.uint8, device=dev)
         out = torch.zeros_like(q)
         inst.append(dict(pc=pc, cache=cache, q=q, w_q=w_q, w_k=w_k, top_p=top_p, query=query,
@@ -339,26 +338,22 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
         (tag, instances, torch.cuda.memory_allocated() / 1e9))
     side = torch.cuda.Stream()
 
+    # one call for the step's attention when its row pass can run the local
+    # heads' window items on its spare CUs (at most 128 retrieval rows)
+    fused_ok = B * w.n_ret <= 128
+
     def make_step(I, main, fused=True):
         sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
         append = rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"], stream=main, prepare=True)
         window = rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side, prepare=True)
         fork, join = torch.cuda.Event(), torch.cuda.Event()
-        if fused:
-            # the retrieval heads' selection and attention in one call; the
-            # local heads' window attention on the second stream beside it
-            retrieval = rtp.retrieval_decode(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"],
-                                             I["out"], I["ws_ret"], stream=main, prepare=True)
-
-            def run():
-                append()
-                fork.record(main)
-                side.wait_event(fork)
-                window()
-                retrieval()
-                join.record(side)
-                main.wait_event(join)
-            return run
+        if fused and fused_ok:
+            # the step's indexer-key append, the selection and sparse attention
+            # of the retrieval heads and the window attention of the local
+            # heads in one call, on one stream
+            step_attn = rtp.decode_attn(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["out"],
+                                        I["ws_ret"], w_k=I["w_k"], stream=main, prepare=True)
+            return step_attn
         begin = rtp.topp_select_begin(*sel_args, stream=main, prepare=True)
         end = rtp.topp_select_end(*sel_args, stream=main, prepare=True)
         sparse = rtp.sparse_attn_decode(layer, I["cache"], I["query"], I["sel"], I["out"], I["ws_sp"], stream=main,
@@ -401,14 +396,15 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     torch.cuda.synchronize()
     per_call = {c: round(float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3, 2)
                 for i, c in enumerate(calls)}
-    # the fused call alone (selection + sparse attention of the retrieval heads)
+    # the step's attention in one call (rtp_decode_attn: every head)
     for s, e in enumerate(evs):
         I = inst[s % n_i]
         e[0].record()
-        rtp.retrieval_decode(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["out"], I["ws_ret"])
+        rtp.decode_attn(layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["out"], I["ws_ret"],
+                        w_k=I["w_k"])
         e[1].record()
     torch.cuda.synchronize()
-    per_call["retrieval_fused"] = round(float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3, 2)
+    per_call["decode_attn"] = round(float(np.median([e[0].elapsed_time(e[1]) for e in evs])) * 1e3, 2)
 
     # the timed region: exactly `steps` steps between synchronisations
     a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

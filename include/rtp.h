@@ -330,27 +330,35 @@ rtp_status rtp_sparse_attn_prefill(const rtp_layer *layer, const rtp_cache *cach
                                    void *stream);
 
 /*
- * a2-a5 of the retrieval heads of one decode step in one call: the selection
- * of rtp_topp_select and the attention of rtp_sparse_attn_decode over it
- * (abstract: retrieval heads score every cached token with the lightweight
- * indexer and attend sparsely over the full KV cache; forum post, "Open
- * Questions and Limitations": per-query token counts vary, so here the
- * attention reads each row's selected keys straight from the selection's row
- * records, with no host round trip and no separate pass that writes the CSR
- * before the attention reads it).  Same arguments, selection, CSR output, status
- * codes and attention output as rtp_topp_select followed by
- * rtp_sparse_attn_decode with the same sel; on capacity overflow
- * (*status = 1, row_ptr complete, idx untouched) and for an invalid top_p
- * (*status = 3) no attention output is written.  RTP_DECODE queries only.
- * workspace: rtp_retrieval_decode_workspace(layer, cache, query,
- * sel->capacity) bytes.  Errors: as the two calls; RTP_EINVAL for another
- * query kind.
+ * a2-a6 of one decode step in one call: the selection of rtp_topp_select and
+ * the attention of rtp_sparse_attn_decode over it for the retrieval heads, and
+ * the window attention of rtp_window_attn for the local heads (abstract:
+ * retrieval heads score every cached token with the lightweight indexer and
+ * attend sparsely over the full KV cache, the other heads use a restricted
+ * window; forum post, "Open Questions and Limitations": per-query token counts
+ * vary, so here the attention reads each row's selected keys straight from the
+ * selection's row records, with no host round trip and no pass that writes the
+ * CSR before the attention reads it; with bf16 K/V and head_dim 128 the local
+ * heads' window attention runs on the compute units the per-row selection
+ * leaves free).  w_k: NULL, or the indexer projections: then the step's
+ * tokens' indexer keys (position seq_lens[b]-1 of every sequence) are written
+ * first, exactly as rtp_indexer_append would write them (a1; their K rows must
+ * be in the cache), by the scoring pass itself.  Otherwise the same arguments
+ * as rtp_topp_select plus `out`; the same
+ * selection, CSR output and status codes as rtp_topp_select, the same
+ * retrieval-head outputs as rtp_sparse_attn_decode with that sel, and the same
+ * local-head outputs as rtp_window_attn.  On capacity overflow (*status = 1,
+ * row_ptr complete, idx untouched) and for an invalid top_p (*status = 3) the
+ * retrieval heads' outputs are not written; the local heads' always are.
+ * RTP_DECODE queries only.  workspace: rtp_decode_attn_workspace(layer, cache,
+ * query, sel->capacity) bytes.  Errors: as the three calls; RTP_EINVAL for
+ * another query kind.
  */
-size_t rtp_retrieval_decode_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
-                                      int64_t capacity);
-rtp_status rtp_retrieval_decode(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
-                                const void *w_q, const float *top_p, const rtp_sel *sel, void *out,
-                                void *workspace, size_t workspace_bytes, void *stream);
+size_t rtp_decode_attn_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                                 int64_t capacity);
+rtp_status rtp_decode_attn(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query,
+                           const void *w_q, const void *w_k, const float *top_p, const rtp_sel *sel, void *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Workspace bytes for rtp_window_attn / rtp_dense_attn. */
 size_t rtp_window_attn_workspace(const rtp_layer *layer, const rtp_cache *cache, const rtp_query *query);

@@ -36,8 +36,8 @@ ENTRY_POINTS = (
     "rtp_topk_select",
     "rtp_topp_select_paths", "rtp_indexer_scores",
     "rtp_sparse_attn_workspace",
-    "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_retrieval_decode_workspace",
-    "rtp_retrieval_decode", "rtp_window_attn_workspace",
+    "rtp_sparse_attn_decode", "rtp_sparse_attn_prefill", "rtp_decode_attn_workspace",
+    "rtp_decode_attn", "rtp_window_attn_workspace",
     "rtp_dense_attn_workspace", "rtp_window_attn", "rtp_dense_attn",
 )
 
@@ -108,8 +108,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "rtp_sparse_attn_workspace": ([pl, pc, pq, i64], S),
         "rtp_sparse_attn_decode": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
         "rtp_sparse_attn_prefill": ([pl, pc, pq, ps, P, P, S, P], ctypes.c_int),
-        "rtp_retrieval_decode_workspace": ([pl, pc, pq, i64], S),
-        "rtp_retrieval_decode": ([pl, pc, pq, P, P, ps, P, P, S, P], ctypes.c_int),
+        "rtp_decode_attn_workspace": ([pl, pc, pq, i64], S),
+        "rtp_decode_attn": ([pl, pc, pq, P, P, P, ps, P, P, S, P], ctypes.c_int),
         "rtp_window_attn_workspace": ([pl, pc, pq], S),
         "rtp_dense_attn_workspace": ([pl, pc, pq], S),
         "rtp_window_attn": ([pl, pc, pq, P, P, S, P], ctypes.c_int),
@@ -300,16 +300,17 @@ def sparse_attn_prefill(layer, cache, query, sel, out, ws, stream=None, prepare=
                 (layer, cache, query, sel), prepare)
 
 
-def retrieval_decode_workspace(layer, cache, query, capacity: int) -> int:
-    return load().rtp_retrieval_decode_workspace(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query),
-                                                 capacity)
+def decode_attn_workspace(layer, cache, query, capacity: int) -> int:
+    return load().rtp_decode_attn_workspace(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), capacity)
 
 
-def retrieval_decode(layer, cache, query, w_q, top_p, sel, out, ws, stream=None, prepare=False):
-    """Selection and sparse attention of the retrieval heads of a decode step in one call."""
-    return _run("rtp_retrieval_decode", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
-                                         _ptr(top_p), ctypes.byref(sel), _ptr(out), _ptr(ws), _nbytes(ws),
-                                         _stream(stream)), (layer, cache, query, sel), prepare)
+def decode_attn(layer, cache, query, w_q, top_p, sel, out, ws, w_k=None, stream=None, prepare=False):
+    """The attention of one decode step in one call: selection and sparse
+    attention of the retrieval heads, window attention of the local heads
+    (with w_k: the step's indexer keys appended first)."""
+    return _run("rtp_decode_attn", (ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), _ptr(w_q),
+                                    _ptr(w_k), _ptr(top_p), ctypes.byref(sel), _ptr(out), _ptr(ws), _nbytes(ws),
+                                    _stream(stream)), (layer, cache, query, sel), prepare)
 
 
 def window_attn_workspace(layer, cache, query) -> int:

@@ -593,25 +593,32 @@ static size_t sparse_dec_ws_bytes(const rtp_layer* layer, const rtp_query* query
     return align256((size_t)items * (layer->head_dim + 2) * 4) + align256((size_t)(rows + 1) * 4);
 }
 
-size_t rtp_retrieval_decode_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
-                                      int64_t capacity) {
+size_t rtp_decode_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
+                                 int64_t capacity) {
     if (check_all(layer, cache, query) || capacity < 0 || query->kind != RTP_DECODE) return 0;
-    return plan_select(layer, cache, query).total + sparse_dec_ws_bytes(layer, query, capacity);
+    return plan_select(layer, cache, query).total + sparse_dec_ws_bytes(layer, query, capacity) +
+           win_ws_bytes(layer, cache, query, 0);
 }
 
-rtp_status rtp_retrieval_decode(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
-                                const void* w_q, const float* top_p, const rtp_sel* sel, void* out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Rows of one decode step up to which the row pass runs the window items on
+// its spare workgroups (each row takes a CU; the items need free CUs).
+constexpr int kRowsWithWindow = 128;
+
+rtp_status rtp_decode_attn(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query, const void* w_q,
+                           const void* w_k, const float* top_p, const rtp_sel* sel, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     rtp_status s = check_all(layer, cache, query);
     if (s) return s;
-    if (query->kind != RTP_DECODE) return fail(RTP_EINVAL, "rtp_retrieval_decode needs RTP_DECODE queries");
+    if (query->kind != RTP_DECODE) return fail(RTP_EINVAL, "rtp_decode_attn needs RTP_DECODE queries");
     if (!w_q || !top_p || !out) return fail(RTP_EINVAL, "NULL w_q / top_p / out");
     if (!sel || !sel->row_ptr || !sel->status || (sel->capacity > 0 && !sel->idx) || sel->capacity < 0)
         return fail(RTP_EINVAL, "bad selection buffers");
+    if ((s = check_ring_window(layer, cache, query))) return s;
     const int rows = query->n_tok * layer->num_ret;
     if (rows > kMaxDecodeRows) return fail(RTP_EUNSUPPORTED, "batch * num_ret %d > %d", rows, kMaxDecodeRows);
     const SelPlan p = plan_select(layer, cache, query);
-    const size_t need = p.total + sparse_dec_ws_bytes(layer, query, sel->capacity);
+    const size_t sp_bytes = sparse_dec_ws_bytes(layer, query, sel->capacity);
+    const size_t need = p.total + sp_bytes + win_ws_bytes(layer, cache, query, 0);
     if (!workspace || workspace_bytes < need)
         return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
     const int64_t items = sparse_max_items(layer, query, sel->capacity);
@@ -620,24 +627,44 @@ rtp_status rtp_retrieval_decode(const rtp_layer* layer, const rtp_cache* cache, 
     w.part = (float*)aw;
     w.item_start = (int32_t*)(aw + align256((size_t)items * (layer->head_dim + 2) * 4));
     w.max_items = items;
-    if (p.group_rows < p.rows_total) {
-        // rows beyond one workspace pass: the two calls in sequence
-        if ((s = topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, p.total, stream, 0, 0)))
-            return s;
-        const rtp::Geo g = make_geo(layer, cache, query);
-        return hip_status(rtp::launch_sparse_decode(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
-                                                    sel->status, out, w, 0, rows, layer->dtype, (hipStream_t)stream),
-                          "sparse decode launch");
-    }
+    float* wpart = (float*)(aw + sp_bytes);
     const rtp::Geo g = make_geo(layer, cache, query);
+    const hipStream_t st = (hipStream_t)stream;
+    const int split = win_split(layer, 0);
+    const int nsplit = (win_keys(layer, cache, 0) + split - 1) / split;
+    if (p.group_rows < p.rows_total) {
+        // rows beyond one workspace pass: the calls in sequence (the indexer
+        // keys appended first, at each sequence's last position)
+        if (w_k) {
+            hipError_t e = rtp::launch_indexer_append_last(g, cache->k, cache->k_low, w_k, layer->dtype, st);
+            if (e != hipSuccess) return hip_status(e, "indexer append launch");
+        }
+        if ((s = topp_select_phase(layer, cache, query, w_q, top_p, sel, workspace, p.total, stream, 0, 0))) return s;
+        hipError_t e = rtp::launch_sparse_decode(g, query->q, cache->k, cache->v, sel->row_ptr, sel->idx,
+                                                 sel->status, out, w, 0, rows, layer->dtype, st);
+        if (e != hipSuccess) return hip_status(e, "sparse decode launch");
+        return hip_status(rtp::launch_window_decode(g, query->q, cache->k, cache->v, out, wpart, nsplit, split, 0,
+                                                    layer->dtype, st),
+                          "window decode launch");
+    }
     const rtp::SelWs sw = sel_ws(p, (char*)workspace);
     const rtp::SelOut so{sel->row_ptr, sel->idx, sel->capacity, sel->status};
+    // the window items run inside the row pass when they are MFMA items (bf16
+    // K/V, D = 128) and the rows leave CUs free
+    const bool merged = split == kWinSplitMfma && g.group <= 32 && rows <= kRowsWithWindow;
+    rtp::WinWork win{(const uint16_t*)query->q, (const uint16_t*)cache->k, (const uint16_t*)cache->v, wpart, nsplit,
+                     split, nsplit * cache->batch * layer->num_kv_heads};
+    const rtp::KeyAppend app{cache->k, w_k};
     hipError_t e = rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p, 0, sw, so, rows,
-                                      layer->dtype, rtp::kSelRows, (hipStream_t)stream);
+                                      layer->dtype, rtp::kSelRows, st, merged ? &win : nullptr, &app);
     if (e != hipSuccess) return hip_status(e, "top-p select launch");
-    return hip_status(rtp::launch_sparse_decode_sel(g, query->q, cache->k, cache->v, sw, so, out, w, rows,
-                                                    layer->dtype, (hipStream_t)stream),
-                      "sparse decode launch");
+    e = rtp::launch_sparse_decode_sel(g, query->q, cache->k, cache->v, sw, so, out, w, rows, layer->dtype,
+                                      merged ? &win : nullptr, st);
+    if (e != hipSuccess) return hip_status(e, "sparse decode launch");
+    if (merged) return ok();
+    return hip_status(rtp::launch_window_decode(g, query->q, cache->k, cache->v, out, wpart, nsplit, split, 0,
+                                                layer->dtype, st),
+                      "window decode launch");
 }
 
 size_t rtp_window_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query) {

@@ -59,12 +59,13 @@ template <typename T, typename TK, int D>
 __global__ __launch_bounds__(64) void k_append_few(Geo g, const TK* __restrict__ kc, bf16_t* __restrict__ k_low,
                                                    const T* __restrict__ w_k, const int32_t* __restrict__ seq_id,
                                                    const int32_t* __restrict__ pos) {
-    // grid (n, ceil(num_ret / 4)): lane 16 h + c serves retrieval head 4 blockIdx.y + h
+    // grid (n, ceil(num_ret / 4)): lane 16 h + c serves retrieval head 4 blockIdx.y + h;
+    // seq_id == nullptr: token i is sequence i's last position (a decode step)
     const int lane = threadIdx.x;
     const int i = blockIdx.x;
     const int r = blockIdx.y * 4 + (lane >> 4), c = lane & 15;
     if (r >= g.n_ret) return;
-    const int b = seq_id[i], j = pos[i];
+    const int b = seq_id ? seq_id[i] : i, j = seq_id ? pos[i] : seq_len(g, i) - 1;
     if (b < 0 || b >= g.batch || j < 0 || j >= g.max_blocks * kBlk) return;
     const int page = g.block_table[(size_t)b * g.max_blocks + (j >> 8)];
     const int kvh = g.ret_heads[r] / g.group;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(64) void k_append_few(Geo g, const TK* __restrict__
 template <typename T, typename TK, int D>
 hipError_t append(const Geo& g, const void* k, void* k_low, const void* w_k, const int32_t* seq_id,
                   const int32_t* pos, int n, hipStream_t s) {
-    if (n <= 256)
+    if (n <= 256 || !seq_id)          // no seq_id: the last positions of a decode step
         hipLaunchKernelGGL((k_append_few<T, TK, D>), dim3((unsigned)n, (g.n_ret + 3) / 4), dim3(64), 0, s, g,
                            (const TK*)k, (bf16_t*)k_low, (const T*)w_k, seq_id, pos);
     else
@@ -178,6 +179,11 @@ hipError_t launch_kv_append(const Geo& g, const void* k_new, const void* v_new, 
     if (dtype == 1 && g.D == 64)
         return kv_append<bf16_t, bf16_t, 64>(g, k_new, v_new, k, v, k_low, w_k, seq_id, pos, n, s);
     return kv_append<bf16_t, bf16_t, 128>(g, k_new, v_new, k, v, k_low, w_k, seq_id, pos, n, s);
+}
+
+hipError_t launch_indexer_append_last(const Geo& g, const void* k, void* k_low, const void* w_k, int dtype,
+                                      hipStream_t s) {
+    return launch_indexer_append(g, k, k_low, w_k, nullptr, nullptr, g.batch, dtype, s);
 }
 
 hipError_t launch_indexer_append(const Geo& g, const void* k, void* k_low, const void* w_k,

@@ -19,6 +19,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "win_mfma.hpp"
 
 namespace rtp {
 
@@ -74,9 +75,6 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ size_t kv_off(const Geo& g, int page, int kvh, int slot, int D) {
-    return kv_rowidx(g, page, kvh, slot) * (size_t)D;
-}
 
 template <typename T, int D, int NH, int UR = (NH > 4 ? 4 : 8)>
 struct Stream {
@@ -501,23 +499,42 @@ __global__ __launch_bounds__(64) void k_sparse_dec_combine(Geo g, const int32_t*
     combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);   // V scale of FP8 codes
 }
 
+// The decode step's combine: workgroups [0, rows) merge the retrieval rows'
+// partials (nothing when the selection reported an error), the others the
+// window partials of (sequence, local head) pairs, workgroup rows + b Hq + h.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void k_dec_combine_all(Geo g, const int32_t* __restrict__ status, AttnWs ws,
+                                                        T* __restrict__ out, int rows, const float* __restrict__ wpart,
+                                                        int nsplit, int split_keys) {
+    const int blk = blockIdx.x;
+    if (blk < rows) {
+        if (*status != 0) return;
+        const int t = blk / g.n_ret, r = blk - t * g.n_ret;
+        const int h = g.ret_heads[r];
+        const int i0 = ws.item_start[blk], i1 = ws.item_start[blk + 1];
+        T* o = out + ((size_t)t * g.Hq + h) * D;
+        if (i1 <= i0) {
+            for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
+            return;
+        }
+        combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);
+        return;
+    }
+    const int bh = blk - rows, b = bh / g.Hq, h = bh - b * g.Hq;
+    if (g.is_ret[h]) return;
+    const int pos = seq_len(g, b) - 1;
+    int ns_end, w_start;
+    const int n_all = win_count(g, pos, 0, &ns_end, &w_start);
+    const int ns = min(nsplit, (n_all + split_keys - 1) / split_keys);
+    combine_wave<T, D>(wpart + ((size_t)b * g.Hq + h) * nsplit * (D + 2), ns, out + ((size_t)b * g.Hq + h) * D,
+                       g.v_scale);
+}
+
 // ---------------------------------------------------------------------------
 // Window / dense decode: grid (nsplit, batch * Hkv), one wavefront each.  The
 // wavefront serves every head of the KV group that needs it (the local heads,
 // or all heads when dense), reading each key and value row once.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int win_count(const Geo& g, int pos, int dense, int* ns_end, int* w_start) {
-    if (dense) {
-        *ns_end = pos + 1;
-        *w_start = pos + 1;
-        return pos + 1;
-    }
-    const int ne = min(g.sinks, pos + 1);
-    const int ws = max(pos - g.window + 1, ne);
-    *ns_end = ne;
-    *w_start = ws;
-    return ne + (pos - ws + 1);
-}
 
 template <typename T, typename TKV, int D, int NH>
 __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict__ q,
@@ -603,190 +620,15 @@ __global__ __launch_bounds__(64) void k_win_dec_part(Geo g, const T* __restrict_
 
 // ---------------------------------------------------------------------------
 // Local-head (or dense) decode on bf16 MFMA, D = 128: one wavefront per
-// (sequence, KV head, split).  The query heads of the KV group are the 32
-// columns of v_mfma_f32_32x32x16_bf16 (heads that do not need the kernel are
-// zero columns), so every K/V row is read once for the group.  Per block of 32
-// keys: S^T[key][head] = K . Q^T with the K rows straight from memory (each
-// lane one key, 16 bytes per k-step); online softmax per head in-lane (a lane
-// holds 16 of the block's keys of its head, the other half-wave the other 16);
-// O^T[d][head] += V^T . P^T with V^T read by gfx950's transposing LDS loads
-// from the block's row-major V tile (16-byte row stores) and P^T taken
-// straight from the S^T registers (a fixed key permutation matches their
-// layout).  Writes the same partials as k_win_dec_part.
+// (sequence, KV head, split), the work item of win_mfma.hpp.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-constexpr int kWVsLd = 128 + 32;   // V row stride in LDS (bf16), 320 B: the four rows of a transposing load hit disjoint banks
-
-__device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
-__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
-    return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
-}
-
 __global__ __launch_bounds__(64) void k_win_dec_mfma(Geo g, const bf16_t* __restrict__ q,
                                                      const bf16_t* __restrict__ kc_main,
                                                      const bf16_t* __restrict__ vc_main, float* __restrict__ part,
                                                      int nsplit, int split_keys, int dense) {
-    constexpr int D = 128;
-    const int lane = threadIdx.x, hh = lane >> 5, col = lane & 31;
-    const int b = blockIdx.y / g.Hkv, kvh = blockIdx.y % g.Hkv;
-    // K/V of this KV head: the paged cache, or the window-only ring
-    const bf16_t* __restrict__ kc = g.kv_ring[kvh] ? (const bf16_t*)g.k_ring : kc_main;
-    const bf16_t* __restrict__ vc = g.kv_ring[kvh] ? (const bf16_t*)g.v_ring : vc_main;
-    const int pos = seq_len(g, b) - 1;
-    int ns_end, w_start;
-    const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
-    const int v0 = blockIdx.x * split_keys;
-    if (v0 >= n_all) return;
-    const int n = min(split_keys, n_all - v0);
-    const int hq = kvh * g.group + col;
-    const bool act = col < g.group && (dense || !g.is_ret[col < g.group ? hq : 0]);
-    if (__ballot(act) == 0ull) return;
-    // B operand Q^T: lane holds q[hq][16 kk + 8 hh .. +8]
-    uint4 qreg[8];
-    {
-        const bf16_t* qp = q + ((size_t)b * g.Hq + (act ? hq : 0)) * D + 8 * hh;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            qreg[kk] = act ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-    }
-    // page ids of the split: a run of sink positions, then a run of window positions
     __shared__ int pgs[64];
     __shared__ __align__(16) bf16_t Vs[32 * kWVsLd];
-    const int vS1 = min(v0 + n, ns_end);
-    const int pS0 = v0 >> 8;
-    const int nPS = vS1 > v0 ? ((vS1 - 1) >> 8) - pS0 + 1 : 0;
-    const int jW0 = w_start + max(v0, ns_end) - ns_end;
-    const int jW1 = w_start + (v0 + n) - ns_end;
-    const int pW0 = jW0 >> 8;
-    const int nPW = jW1 > jW0 ? ((jW1 - 1) >> 8) - pW0 + 1 : 0;
-    if (lane < nPS) pgs[lane] = kv_page(g, b, kvh, pS0 + lane);
-    else if (lane < nPS + nPW) pgs[lane] = kv_page(g, b, kvh, pW0 + lane - nPS);
-    __syncthreads();
-    auto off = [&](int i) {
-        const int vi = v0 + i;
-        int j, pi;
-        if (vi < ns_end) {
-            j = vi;
-            pi = (j >> 8) - pS0;
-        } else {
-            j = w_start + (vi - ns_end);
-            pi = nPS + (j >> 8) - pW0;
-        }
-        return kv_off(g, pgs[pi], kvh, j & 255, D);
-    };
-    const float sc = g.attn_scale * kLog2e;
-    f32x16_t oacc[4];
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dd][i] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
-    // this lane's key row of a block: K for the A operand, V for the
-    // transposed tile.  The next block's K rows are requested once this
-    // block's S MFMAs have taken theirs, its V rows once this block's V^T
-    // tile is written, so they arrive while this block finishes.
-    uint4 ka[8], va[8];
-    {
-        const size_t ro = off(min(col, n - 1)) + 8 * hh;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(kc + ro + 16 * kk);
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) va[kk] = *reinterpret_cast<const uint4*>(vc + ro + 16 * kk);
-    }
-    for (int k0 = 0; k0 < n; k0 += 32) {
-        const bool live = k0 + col < n;
-        const bool more = k0 + 32 < n;
-        const size_t ro_n = off(min(k0 + 32 + col, n - 1)) + 8 * hh;
-        f32x16_t s;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = 0.0f;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kk]), as_bf16x8(qreg[kk]), s, 0, 0, 0);
-        if (more) {
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) ka[kk] = *reinterpret_cast<const uint4*>(kc + ro_n + 16 * kk);
-        }
-        __syncthreads();                                  // the previous block's V^T reads are done
-        // the block's V rows, row-major (key col, d = 16 kk + 8 hh ..); rows
-        // past the split stored as zeros
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            *reinterpret_cast<uint4*>(&Vs[col * kWVsLd + 16 * kk + 8 * hh]) = live ? va[kk] : make_uint4(0, 0, 0, 0);
-        if (more) {
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) va[kk] = *reinterpret_cast<const uint4*>(vc + ro_n + 16 * kk);
-        }
-        // scale, mask, block maximum of this lane's head
-        float mt = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int key = k0 + (i >> 2) * 8 + 4 * hh + (i & 3);
-            const float v = key < n ? s[i] * sc : -INFINITY;
-            s[i] = v;
-            mt = fmaxf(mt, v);
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);             // finite: the block has a live key
-        if (__ballot(m_new > m_run) != 0ull) {            // some head's maximum rose: rescale
-            const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= corr;
-#pragma unroll
-            for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) oacc[dd][i] *= corr;
-        }
-        m_run = m_new;
-        uint32_t pb[8];
-        {
-            float p[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(s[i] - m_new);
-                l_run += p[i];
-            }
-#pragma unroll
-            for (int x = 0; x < 8; ++x) pb[x] = pack_bf2(p[2 * x], p[2 * x + 1]);
-        }
-        __syncthreads();                                  // the V tile is written
-        // O^T += V^T P^T; k-step kk covers keys 16 kk + 4 hh + {0..3, 8..11}:
-        // lane (d = 32 dd + col, half hh) reads V^T[d][those keys] from the
-        // row-major tile by transposing loads (lane j of a 16-lane group
-        // addresses key row kc0 + j / 4 (+ 8) at columns 32 dd + 16 (group &
-        // 1) + 4 (j % 4))
-        const int trr = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const uint4 bp = make_uint4(pb[4 * kk], pb[4 * kk + 1], pb[4 * kk + 2], pb[4 * kk + 3]);
-            const int kc0 = 16 * kk + 4 * hh;
-#pragma unroll
-            for (int dd = 0; dd < 4; ++dd) {
-                const bf16_t* vr = &Vs[(kc0 + trr) * kWVsLd + 32 * dd + trc];
-                const uint2 lo = lds_tr16(vr);
-                const uint2 hi = lds_tr16(vr + 8 * kWVsLd);
-                const uint4 a = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                oacc[dd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(bp), oacc[dd], 0, 0, 0);
-            }
-        }
-    }
-    // partials: lane holds O^T[32 dd + 8 (i/4) + 4 hh + (i%4)][head col]
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (act) {
-        float* pp = part + (((size_t)b * g.Hq + hq) * nsplit + blockIdx.x) * (D + 2);
-#pragma unroll
-        for (int dd = 0; dd < 4; ++dd)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * dd + 8 * r4 + 4 * hh;    // partial records are 8-byte aligned
-                *reinterpret_cast<float2*>(pp + d0) = make_float2(oacc[dd][4 * r4], oacc[dd][4 * r4 + 1]);
-                *reinterpret_cast<float2*>(pp + d0 + 2) = make_float2(oacc[dd][4 * r4 + 2], oacc[dd][4 * r4 + 3]);
-            }
-        if (hh == 0) {
-            pp[D] = m_run;
-            pp[D + 1] = l_tot;
-        }
-    }
+    win_mfma_item<false>(g, q, kc_main, vc_main, part, nsplit, split_keys, dense, blockIdx.x, blockIdx.y, pgs, Vs);
 }
 
 template <typename T, int D>
@@ -800,6 +642,14 @@ __global__ __launch_bounds__(128) void k_win_dec_combine(Geo g, const float* __r
     int ns_end, w_start;
     const int n_all = win_count(g, pos, dense, &ns_end, &w_start);
     const int ns = min(nsplit, (n_all + split_keys - 1) / split_keys);
+    if (!dense) {
+        // the window's few splits: the one-wavefront combine (the decode
+        // step's combine merges the same partials the same way)
+        if (threadIdx.x < 64)
+            combine_wave<T, D>(part + ((size_t)b * g.Hq + h) * nsplit * (D + 2), ns, out + ((size_t)b * g.Hq + h) * D,
+                               g.v_scale);
+        return;
+    }
     combine_parts<T, D>(part + ((size_t)b * g.Hq + h) * nsplit * (D + 2), ns,
                         out + ((size_t)b * g.Hq + h) * D, wsh, g.v_scale);
 }
@@ -818,12 +668,17 @@ hipError_t sparse_dec(const Geo& g, const void* q, const void* k, const void* v,
 
 template <typename T, typename TKV, int D>
 hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
-                          const SelOut& so, void* out, const AttnWs& ws, int rows, hipStream_t s) {
+                          const SelOut& so, void* out, const AttnWs& ws, int rows, const WinWork* win,
+                          hipStream_t s) {
     const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
     const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1) + sizeof(int32_t) * rows;
     hipLaunchKernelGGL((k_sparse_dec_sel<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
                        (const TKV*)k, (const TKV*)v, sw, so, ws, rows);
-    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, so.status, ws, (T*)out, 0);
+    if (win && win->items > 0)
+        hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + g.batch * g.Hq), dim3(64), 0, s, g, so.status, ws,
+                           (T*)out, rows, win->part, win->nsplit, win->split_keys);
+    else
+        hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, so.status, ws, (T*)out, 0);
     return hipGetLastError();
 }
 
@@ -869,13 +724,13 @@ hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, cons
 
 hipError_t launch_sparse_decode_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
                                     const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
-                                    hipStream_t s) {
-    if (g.kv_fp8 && g.D == 64) return sparse_dec_sel<bf16_t, fp8e4_t, 64>(g, q, k, v, sw, so, out, ws, rows, s);
-    if (g.kv_fp8) return sparse_dec_sel<bf16_t, fp8e4_t, 128>(g, q, k, v, sw, so, out, ws, rows, s);
-    if (dtype == 0 && g.D == 64) return sparse_dec_sel<float, float, 64>(g, q, k, v, sw, so, out, ws, rows, s);
-    if (dtype == 0 && g.D == 128) return sparse_dec_sel<float, float, 128>(g, q, k, v, sw, so, out, ws, rows, s);
-    if (dtype == 1 && g.D == 64) return sparse_dec_sel<bf16_t, bf16_t, 64>(g, q, k, v, sw, so, out, ws, rows, s);
-    return sparse_dec_sel<bf16_t, bf16_t, 128>(g, q, k, v, sw, so, out, ws, rows, s);
+                                    const WinWork* win, hipStream_t s) {
+    if (g.kv_fp8 && g.D == 64) return sparse_dec_sel<bf16_t, fp8e4_t, 64>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    if (g.kv_fp8) return sparse_dec_sel<bf16_t, fp8e4_t, 128>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    if (dtype == 0 && g.D == 64) return sparse_dec_sel<float, float, 64>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    if (dtype == 0 && g.D == 128) return sparse_dec_sel<float, float, 128>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    if (dtype == 1 && g.D == 64) return sparse_dec_sel<bf16_t, bf16_t, 64>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    return sparse_dec_sel<bf16_t, bf16_t, 128>(g, q, k, v, sw, so, out, ws, rows, win, s);
 }
 
 hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,

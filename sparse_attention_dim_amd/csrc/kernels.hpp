@@ -136,6 +136,9 @@ struct SelOut {
 hipError_t launch_indexer_append(const Geo& g, const void* k, void* k_low, const void* w_k,
                                  const int32_t* seq_id, const int32_t* pos, int n, int dtype,
                                  hipStream_t s);
+// The indexer keys of every sequence's last position (a decode step's tokens).
+hipError_t launch_indexer_append_last(const Geo& g, const void* k, void* k_low, const void* w_k, int dtype,
+                                      hipStream_t s);
 // K and V of n new tokens ([n][Hkv][D]) into their pages (the ring for the
 // ring heads) and their indexer keys, in one launch.
 hipError_t launch_kv_append(const Geo& g, const void* k_new, const void* v_new, void* k, void* v, void* k_low,
@@ -150,9 +153,27 @@ enum SelStage {
     kSelFinish = 3,               // the rest of kSelAll
     kSelRows = 4,                 // kSelAll without the emit: the row records hold the sets
 };
+// Local-head window work (bf16, D = 128, MFMA items) that the row pass of a
+// decode step runs on its spare workgroups (kSelRows only): items = nsplit *
+// batch * Hkv, partials [batch][Hq][nsplit][D + 2].
+struct WinWork {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    float* part;
+    int nsplit, split_keys, items;
+};
+constexpr int kWinCUs = 256;      // compute units of the part: the row pass and its window items fill them
+// Indexer-key append fused into a decode step's scoring pass: the K cache
+// (holding the new tokens' K rows) and W_k; w_k == nullptr: no append.
+struct KeyAppend {
+    const void* k;
+    const void* w_k;
+};
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
-                         int total_rows, int dtype, int stage, hipStream_t s);
+                         int total_rows, int dtype, int stage, hipStream_t s, const WinWork* win = nullptr,
+                         const KeyAppend* app = nullptr);
 // Path codes (kPath*) of the rows of the last selection, from its workspace.
 hipError_t launch_select_paths(const SelWs& ws, int rows, int32_t* paths, hipStream_t s);
 
@@ -175,9 +196,11 @@ hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, cons
 // The same from the selection's workspace (rows of one selection call, one
 // group): each row's selected keys are read from its row record, and the
 // items write the CSR output (row pointers, capacity check, indices).
+// win (bf16 D = 128 only): the window partials written by the row pass are
+// merged by the same combine launch.
 hipError_t launch_sparse_decode_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
                                     const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
-                                    hipStream_t s);
+                                    const WinWork* win, hipStream_t s);
 
 // Top-p selection of the rows of one prefill chunk (bf16, D <= 128): indexer
 // scores of 32-row x 32-key tiles by MFMA as a filter, exact fixed-order

@@ -40,6 +40,7 @@
 
 #include "device.hpp"
 #include "kernels.hpp"
+#include "win_mfma.hpp"
 
 namespace rtp {
 
@@ -84,8 +85,8 @@ __device__ __forceinline__ RowInfo row_info(const Geo& g, int row0, int lrow) {
 // ---------------------------------------------------------------------------
 template <typename T, int STATS>
 __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ q, const T* __restrict__ w_q,
-                                                   const bf16_t* __restrict__ k_low, int row0, SelWs ws,
-                                                   SelOut out) {
+                                                   bf16_t* __restrict__ k_low, int row0, SelWs ws, SelOut out,
+                                                   KeyAppend ap) {
     const int tid = threadIdx.x;
     const int chunk = blockIdx.x;
     const RowInfo ri = row_info(g, row0, blockIdx.y);
@@ -100,6 +101,9 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     __shared__ __align__(16) float qrow[128];
     __shared__ __align__(16) float wq[128 * kIdx];
     __shared__ float qs[kIdx];
+    __shared__ float knew[kIdx];                          // the appended token's indexer key (fused append)
+    __shared__ __align__(16) float krow[STATS ? 128 : 1];
+    __shared__ __align__(16) float wkn[STATS ? 128 * kIdx : 1];
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int jbase = chunk * kChunk;
@@ -122,8 +126,27 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         wreg[k] = vec && (tid + 256 * k) * V < g.D * kIdx ? reinterpret_cast<const uint4*>(wp)[tid + 256 * k]
                                                            : make_uint4(0, 0, 0, 0);
     if (vec && tid * V < g.D) qreg = reinterpret_cast<const uint4*>(qp)[tid];
-    uint4 buf[8];
-    auto load_group = [&](int k0) {
+    // a decode step with the indexer-key append fused in: the workgroup of the
+    // chunk holding the query's position forms that token's indexer key for
+    // this row's head from its K row and W_k (the fixed-order chain of
+    // rtp_indexer_append), stores it, and scores the position with it
+    const bool app = STATS && ap.w_k != nullptr && g.kind == 0 && chunk == (ri.L - 1) / kChunk;
+    const int jnew = app ? ri.L - 1 : -1;
+    int new_page = 0;
+    if (app) {
+        // W_k and the K row straight into LDS (only this workgroup of the row waits on them)
+        const T* wk = (const T*)ap.w_k + (size_t)ri.r * g.D * kIdx;
+        for (int x = tid; x < g.D * kIdx; x += 256) wkn[x] = ld(wk + x);
+        new_page = bt[jnew >> 8];
+        if (tid < g.D) {
+            const size_t ko = kv_rowidx(g, new_page, h / g.group, jnew & 255) * (size_t)g.D + tid;
+            krow[tid] = g.kv_fp8 ? ldk((const fp8e4_t*)ap.k + ko, g.k_scale) : ldk((const T*)ap.k + ko, 1.0f);
+        }
+    }
+    // two groups of four pages in flight: group g + 1 is requested before
+    // group g is scored (16 x 16-byte loads per thread outstanding)
+    uint4 bufA[8], bufB[8];
+    auto load_group = [&](int k0, uint4* buf) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int page = __builtin_amdgcn_readlane(my_page, k0 + u);
@@ -133,7 +156,8 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             buf[2 * u + 1] = kp[1];
         }
     };
-    load_group(0);
+    load_group(0, bufA);
+    load_group(4, bufB);
     // q_low: the query row and W_q staged through LDS, the fixed-order chain
     // over d run by 16 lanes while the first key loads are in flight
     if (vec) {
@@ -168,6 +192,14 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
         const bf16_t qb = f2bf(acc);
         qs[tid] = bf2f(qb);
         if (chunk == 0) ws.qlow[(size_t)ri.lrow * kIdx + tid] = qb;
+    } else if (app && tid >= 64 && tid < 64 + kIdx) {   // another wavefront: the two chains run side by side
+        const int c = tid - 64;
+        float acc = 0.0f;
+#pragma unroll 16
+        for (int d = 0; d < g.D; ++d) acc = __builtin_fmaf(krow[d], wkn[d * kIdx + c], acc);
+        const bf16_t kb = f2bf(acc);
+        knew[c] = bf2f(kb);
+        k_low[(((size_t)new_page * g.n_ret + ri.r) * kBlk + (jnew & 255)) * kIdx + c] = kb;
     }
     __syncthreads();
     float qv[kIdx];
@@ -176,9 +208,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 
     float dv[16];
     float mx = -INFINITY;
-#pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += 4) {
-        if (k0) load_group(k0);
+    auto score_group = [&](int k0, const uint4* buf) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int j = jbase + (k0 + u) * 256 + tid;
@@ -189,9 +219,28 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 #pragma unroll
             for (int c = 0; c < kIdx; ++c) acc = __builtin_fmaf(qv[c], kf[c], acc);
             dv[k0 + u] = acc;
-            if (j < ri.L) mx = fmaxf(mx, acc);
+            (void)j;
         }
+    };
+    score_group(0, bufA);
+    load_group(8, bufA);
+    score_group(4, bufB);
+    load_group(12, bufB);
+    score_group(8, bufA);
+    score_group(12, bufB);
+    if (app && (jnew & 255) == tid && jnew >= jbase) {
+        // the appended position, scored with the key formed above
+        const int k = (jnew - jbase) >> 8;
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < kIdx; ++c) acc = __builtin_fmaf(qv[c], knew[c], acc);
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk)
+            if (kk == k) dv[kk] = acc;
     }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (jbase + k * 256 + tid < ri.L) mx = fmaxf(mx, dv[k]);
     // the scores, after every key load was issued
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -831,11 +880,9 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
 // over the row's scores.
 constexpr int kStageChunks = 48;   // chist (48 KiB) + ccnt (24 KiB) + key masks (24 KiB) + cmax of 48 chunks
 
-__global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
-                                                 int32_t* __restrict__ status) {
+__device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const RowInfo& ri, const SelWs& ws,
+                         int32_t* __restrict__ status, ResolveSm& sm) {
     const int tid = threadIdx.x;
-    const RowInfo ri = row_info(g, row0, blockIdx.x);
-    __shared__ ResolveSm sm;
     const size_t crow = (size_t)ri.lrow * ws.nchunk;
     const unsigned long long* chist = ws.chist + crow * kCB;
     const unsigned* ccnt = ws.ccnt + crow * kCB;
@@ -1069,6 +1116,39 @@ __global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict_
     resolve_body(g, ri, ws, st, (int)nU, loaded, bt_cached, sm);
 }
 
+__global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+                                                 int32_t* __restrict__ status) {
+    __shared__ ResolveSm sm;
+    row_pass(g, top_p, row_info(g, row0, blockIdx.x), ws, status, sm);
+}
+
+// The row pass with the decode step's local-head window attention on its
+// spare workgroups: workgroups [0, rows) take the rows (one CU each, for their
+// LDS), the others run window items of win_mfma.hpp, one per wavefront, on the
+// CUs the rows leave free -- so the window's K/V stream overlaps the rows'
+// latency-bound selection.  The window's partials are merged by the combine.
+struct WinSm {
+    int pgs[64];
+    __align__(16) bf16_t Vs[32 * kWVsLd];
+};
+
+__global__ __launch_bounds__(kRT) void k_sel_row_win(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+                                                     int32_t* __restrict__ status, WinWork wa) {
+    __shared__ union {
+        ResolveSm rs;
+        WinSm w[kRT / 64];
+    } u;
+    if ((int)blockIdx.x < ws.rows) {
+        row_pass(g, top_p, row_info(g, row0, blockIdx.x), ws, status, u.rs);
+        return;
+    }
+    const int wv = threadIdx.x >> 6;
+    const int stride = ((int)gridDim.x - ws.rows) * (kRT / 64);
+    for (int it = ((int)blockIdx.x - ws.rows) * (kRT / 64) + wv; it < wa.items; it += stride)
+        win_mfma_item<true>(g, wa.q, wa.k, wa.v, wa.part, wa.nsplit, wa.split_keys, 0, it % wa.nsplit,
+                            it / wa.nsplit, u.w[wv].pgs, u.w[wv].Vs);
+}
+
 
 // ---------------------------------------------------------------------------
 // CSR row pointers of the group's rows and the capacity check (groups of more
@@ -1160,27 +1240,34 @@ hipError_t launch_select_paths(const SelWs& ws, int rows, int32_t* paths, hipStr
 
 hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uint16_t* k_low,
                          const float* top_p, int row0, const SelWs& ws, const SelOut& out,
-                         int total_rows, int dtype, int stage, hipStream_t s) {
+                         int total_rows, int dtype, int stage, hipStream_t s, const WinWork* win,
+                         const KeyAppend* app) {
     (void)total_rows;
     const dim3 grid(ws.nchunk, ws.rows);
-    const bf16_t* kl = (const bf16_t*)k_low;
+    bf16_t* kl = (bf16_t*)const_cast<uint16_t*>(k_low);
+    const KeyAppend ap = app && stage != kSelScoresOnly ? *app : KeyAppend{nullptr, nullptr};
     const bool scores_only = stage == kSelScoresOnly;
     if (stage != kSelFinish) {
         if (dtype == 0 && scores_only)
             hipLaunchKernelGGL((k_sel_score<float, 0>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q,
-                               kl, row0, ws, out);
+                               kl, row0, ws, out, ap);
         else if (dtype == 0)
             hipLaunchKernelGGL((k_sel_score<float, 1>), grid, dim3(256), 0, s, g, (const float*)q, (const float*)w_q,
-                               kl, row0, ws, out);
+                               kl, row0, ws, out, ap);
         else if (scores_only)
             hipLaunchKernelGGL((k_sel_score<bf16_t, 0>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
-                               (const bf16_t*)w_q, kl, row0, ws, out);
+                               (const bf16_t*)w_q, kl, row0, ws, out, ap);
         else
             hipLaunchKernelGGL((k_sel_score<bf16_t, 1>), grid, dim3(256), 0, s, g, (const bf16_t*)q,
-                               (const bf16_t*)w_q, kl, row0, ws, out);
+                               (const bf16_t*)w_q, kl, row0, ws, out, ap);
     }
     if (scores_only || stage == kSelScorePass) return hipGetLastError();
-    hipLaunchKernelGGL(k_sel_row, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws, out.status);
+    if (stage == kSelRows && win && win->items > 0) {
+        const int nw = std::min((win->items + kRT / 64 - 1) / (kRT / 64), std::max(1, kWinCUs - ws.rows));
+        hipLaunchKernelGGL(k_sel_row_win, dim3(ws.rows + nw), dim3(kRT), 0, s, g, top_p, row0, ws, out.status, *win);
+    } else {
+        hipLaunchKernelGGL(k_sel_row, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws, out.status);
+    }
     if (stage == kSelRows) return hipGetLastError();
     const dim3 egrid(std::min(ws.nchunk, kEmitWG), ws.rows);
     if (ws.rows <= kRowsInEmit) {

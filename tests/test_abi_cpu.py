@@ -251,19 +251,20 @@ def test_noalloc_select_rejects_queries_beyond_its_scratch():
               None) == rtp.RTP_EINVAL
 
 
-def test_retrieval_decode_checks():
-    # the fused decode call checks its arguments on the host like the two
+def test_decode_attn_checks():
+    # the decode step's call checks its arguments on the host like the
     # calls it stands for (nothing is enqueued on an error)
     lib = rtp.load()
     L, C, Q = _layer(), _cache(), _query()
-    need = lib.rtp_retrieval_decode_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), 100)
+    need = lib.rtp_decode_attn_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), 100)
     sel_need = lib.rtp_topp_select_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
     sp_need = lib.rtp_sparse_attn_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q), 100)
-    assert need == sel_need + sp_need
-    fn = lib.rtp_retrieval_decode
+    win_need = lib.rtp_window_attn_workspace(ctypes.byref(L), ctypes.byref(C), ctypes.byref(Q))
+    assert need == sel_need + sp_need + win_need
+    fn = lib.rtp_decode_attn
 
     def call(layer=L, cache=C, query=Q, sel=None, out=FAKE, ws_bytes=need):
-        return fn(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), FAKE, FAKE,
+        return fn(ctypes.byref(layer), ctypes.byref(cache), ctypes.byref(query), FAKE, None, FAKE,
                   ctypes.byref(sel or _sel()), out, FAKE, ws_bytes, None)
 
     assert call(ws_bytes=need - 1) == rtp.RTP_EWORKSPACE

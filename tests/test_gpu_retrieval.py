@@ -1,9 +1,10 @@
-"""GPU parity of rtp_retrieval_decode (the selection and sparse attention of a
-decode step's retrieval heads in one call) against rtp_topp_select followed by
-rtp_sparse_attn_decode, and against the oracle: same status, row pointers,
-selected indices and retrieval-head outputs, on every selection route (every
-key, candidate sets cut in LDS or from the workspace list, and the cut over
-the row's scores)."""
+"""GPU parity of rtp_decode_attn (the attention of a decode step in one call:
+selection and sparse attention of the retrieval heads, window attention of
+the local heads) against rtp_topp_select, rtp_sparse_attn_decode and
+rtp_window_attn, and against the oracle: same status, row pointers, selected
+indices and outputs of every head, on every selection route (every key,
+candidate sets cut in LDS or from the workspace list, gathered from the key
+flags or the scores, and the cut over the row's scores)."""
 import numpy as np
 import pytest
 import torch
@@ -11,12 +12,12 @@ import torch
 import oracle
 import synth
 import sparse_attention_dim_amd as rtp
-from gpu_util import Dev, band_accept, check_out, out_f32, path_counts, say
+from gpu_util import Dev, band_accept, check_out, oracle_k_low, out_f32, path_counts, say
 
 pytestmark = pytest.mark.gpu
 
 
-def _fused(d: Dev, capacity=None, top_p=None):
+def _fused(d: Dev, capacity=None, top_p=None, w_k=None):
     w = d.w
     if capacity is None:
         capacity = sum(w.row_pos(t) + 1 for t in range(w.n_tok)) * w.n_ret
@@ -25,10 +26,10 @@ def _fused(d: Dev, capacity=None, top_p=None):
     status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
     sel = rtp.make_sel(row_ptr, idx, status)
     out = torch.zeros_like(d.q)
-    ws = torch.empty(rtp.retrieval_decode_workspace(d.layer, d.cache, d.query, sel.capacity), dtype=torch.uint8,
+    ws = torch.empty(rtp.decode_attn_workspace(d.layer, d.cache, d.query, sel.capacity), dtype=torch.uint8,
                      device="cuda")
     tp = d.top_p if top_p is None else torch.as_tensor(np.asarray(top_p, np.float32)).cuda()
-    rtp.retrieval_decode(d.layer, d.cache, d.query, d.w_q, tp, sel, out, ws)
+    rtp.decode_attn(d.layer, d.cache, d.query, d.w_q, tp, sel, out, ws, w_k=w_k)
     torch.cuda.synchronize()
     return int(status.item()), row_ptr.cpu().numpy(), idx.cpu().numpy(), out
 
@@ -38,6 +39,7 @@ def _two_calls(d: Dev, capacity=None):
     st, rp, sets = d.select(capacity=capacity)
     if st == 0:
         d.sparse()
+    d.window()
     return st, rp, d.idx.cpu().numpy(), d.out.clone()
 
 
@@ -48,14 +50,17 @@ def _same(d: Dev, a, b):
     np.testing.assert_array_equal(rp1, rp2)
     n = int(rp1[-1]) if st1 == 0 else 0
     np.testing.assert_array_equal(ix1[:n], ix2[:n])
-    ret = list(d.w.ret_heads)
-    assert torch.equal(o1[:, ret], o2[:, ret]), "retrieval-head outputs differ"
+    if st1 == 0:
+        assert torch.equal(o1, o2), "outputs differ"
+    else:
+        loc = d.w.local_heads()
+        assert torch.equal(o1[:, loc], o2[:, loc]), "local-head outputs differ"
 
 
 @pytest.fixture(scope="module", params=[1, 2, 5], ids=["needle_f32", "cluster_bf16", "ragged_bf16"])
 def dev(request):
     w = synth.small(request.param)
-    say("[gpu] fused retrieval decode", w.name, "lens", list(w.seq_lens))
+    say("[gpu] decode step attention", w.name, "lens", list(w.seq_lens))
     return Dev(w)
 
 
@@ -79,6 +84,37 @@ def test_fused_equals_two_calls_and_oracle(dev):
             assert ok, (t, r)
             ref = oracle.attend(w.q[t, h], w.k[bq][:, g, :], w.v[bq][:, g, :], got, w.attn_scale)
             assert check_out(o[t, h], ref, w.dtype) <= 1.0, (t, r)
+        for h in w.local_heads():
+            g = w.kv_head(h)
+            ref = oracle.local_row(w.q[t, h], w.k[bq][:, g, :], w.v[bq][:, g, :], pos, w.window, w.sinks,
+                                   w.attn_scale)
+            assert check_out(o[t, h], ref, w.dtype) <= 1.0, ("local", t, h)
+
+
+def test_fused_indexer_key_append(dev):
+    # the step's own indexer keys (each sequence's last position) overwritten
+    # with garbage, then written by the call itself (w_k given): bit-exact keys
+    # and the same selection and outputs as with the keys appended beforehand
+    w = dev.w
+    a = _fused(dev)
+    pc = dev.pc
+    saved = []
+    for b in range(w.B):
+        j = int(pc.lens[b]) - 1
+        page = int(pc.table[b, j // 256])
+        saved.append(pc.k_low[page, :, j % 256, :].clone())
+        pc.k_low[page, :, j % 256, :] = 7.0
+    torch.cuda.synchronize()
+    b_ = _fused(dev, w_k=dev.w_k)
+    _same(dev, a, b_)
+    for b in range(w.B):
+        j = int(pc.lens[b]) - 1
+        page = int(pc.table[b, j // 256])
+        assert torch.equal(pc.k_low[page, :, j % 256, :], saved[b]), b
+        for r in range(w.n_ret):
+            want = oracle_k_low(w, b, r)[j]
+            got = pc.k_low[page, r, j % 256, :].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            np.testing.assert_array_equal(got, want, err_msg=str((b, r)))
 
 
 def test_lds_route_taken(dev):
@@ -104,7 +140,7 @@ def test_fused_long_rows_every_route():
     # scores into LDS; p = 1 rows keep every key
     w = _flat((40000, 20000, 9001, 5000, 3000), 0.999)
     w.top_p[4] = 1.0
-    say("[gpu] fused retrieval decode, flat long rows")
+    say("[gpu] decode step attention, flat long rows")
     d = Dev(w)
     a = _fused(d)
     b = _two_calls(d)
@@ -138,7 +174,7 @@ def test_fused_spread_rows_gather_from_scores():
     w = synth.small(2)
     w.w_k = synth.to_storage(synth.as_f32(w.w_k) * np.float32(4.0), w.dtype)     # exact: a power of two
     w.top_p = np.full_like(w.top_p, 0.99)
-    say("[gpu] fused retrieval decode, spread scores")
+    say("[gpu] decode step attention, spread scores")
     d = Dev(w)
     a = _fused(d)
     b = _two_calls(d)
@@ -165,7 +201,7 @@ def test_fused_spread_rows_gather_from_scores():
 
 def test_fused_capacity_overflow():
     w = synth.small(2)
-    say("[gpu] fused retrieval decode, capacity overflow")
+    say("[gpu] decode step attention, capacity overflow")
     d = Dev(w)
     st, rp, ix, out = _fused(d)
     need = int(rp[-1])
@@ -173,7 +209,10 @@ def test_fused_capacity_overflow():
     assert st2 == 1 and int(rp2[-1]) == need
     np.testing.assert_array_equal(rp2, rp)
     assert np.all(ix2 == -1)
-    assert not torch.any(out2 != 0), "no attention output on overflow"
+    ret = list(w.ret_heads)
+    assert not torch.any(out2[:, ret] != 0), "no retrieval-head output on overflow"
+    loc = w.local_heads()
+    assert torch.equal(out2[:, loc], out[:, loc]), "local heads are written regardless"
     st3, rp3, ix3, out3 = _fused(d, capacity=need)
     assert st3 == 0
     assert torch.equal(out3, out)
@@ -181,21 +220,21 @@ def test_fused_capacity_overflow():
 
 def test_fused_invalid_top_p():
     w = synth.small(2)
-    say("[gpu] fused retrieval decode, invalid top_p")
+    say("[gpu] decode step attention, invalid top_p")
     d = Dev(w)
     p = w.top_p.astype(np.float32).copy()
     p[0] = float("nan")
     st, rp, ix, out = _fused(d, top_p=p)
     assert st == 3
     assert np.all(ix == -1)
-    assert not torch.any(out != 0)
+    assert not torch.any(out[:, list(w.ret_heads)] != 0)
 
 
 def test_fused_repeated_calls_identical():
     # every call rewrites the row records: calls with other top_p values in
     # between leave the result unchanged
     w = synth.small(5)
-    say("[gpu] fused retrieval decode, repeated calls")
+    say("[gpu] decode step attention, repeated calls")
     d = Dev(w)
     a = _fused(d)
     _fused(d, top_p=np.full_like(w.top_p, 0.5))
