@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             krow[tid] = g.kv_fp8 ? ldk((const fp8e4_t*)ap.k + ko, g.k_scale) : ldk((const T*)ap.k + ko, 1.0f);
         }
     }
-    // two groups of four pages in flight: group g + 1 is requested before
-    // group g is scored (16 x 16-byte loads per thread outstanding)
+    // all four groups of four pages in flight before the first is scored (32 x
+    // 16-byte loads per thread outstanding)
     uint4 bufA[8], bufB[8];
     auto load_group = [&](int k0, uint4* buf) {
 #pragma unroll
@@ -222,12 +222,13 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             (void)j;
         }
     };
+    uint4 bufC[8], bufD[8];
+    load_group(8, bufC);
+    load_group(12, bufD);
     score_group(0, bufA);
-    load_group(8, bufA);
     score_group(4, bufB);
-    load_group(12, bufB);
-    score_group(8, bufA);
-    score_group(12, bufB);
+    score_group(8, bufC);
+    score_group(12, bufD);
     if (app && (jnew & 255) == tid && jnew >= jbase) {
         // the appended position, scored with the key formed above
         const int k = (jnew - jbase) >> 8;
@@ -241,13 +242,14 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
 #pragma unroll
     for (int k = 0; k < 16; ++k)
         if (jbase + k * 256 + tid < ri.L) mx = fmaxf(mx, dv[k]);
-    // the scores, after every key load was issued
+    if (!STATS) {
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        const int j = jbase + k * 256 + tid;
-        if (j < ri.L) srow[j] = dv[k];
+        for (int k = 0; k < 16; ++k) {
+            const int j = jbase + k * 256 + tid;
+            if (j < ri.L) srow[j] = dv[k];
+        }
+        return;
     }
-    if (!STATS) return;
     mx = wave_max(mx);
     if ((tid & 63) == 0) wmax[tid >> 6] = mx;
     __syncthreads();
@@ -255,7 +257,9 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     if (tid == 0) ws.cmax[(size_t)ri.lrow * ws.nchunk + chunk] = score_key(mc);
     const float s = g.idx_scale;
     // a bit per key for the row pass's gather of U: the key lies in chunk bin
-    // <= kLowBin (the wave's 64 consecutive keys of step k are one 64-bit word)
+    // <= kLowBin (the wave's 64 consecutive keys of step k are one 64-bit word);
+    // only those keys' scores are stored (the row pass forms any other score
+    // it needs again from the indexer keys)
     unsigned long long* km = ws.kmask + ((size_t)ri.lrow * ws.score_ld + jbase) / 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -267,6 +271,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             atomicAdd(&hist[b], wb.w);
             atomicAdd(&hcnt[b], 1u);
             low = b <= kLowBin;
+            if (low) srow[j] = dv[k];
         }
         const unsigned long long bal = __ballot(low);
         if ((tid & 63) == 0) km[4 * k + (tid >> 6)] = bal;
@@ -869,6 +874,41 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
     }
 }
 
+// The fixed-order chain scores of every key of chunk c of a row, formed again
+// from the indexer keys (q_low from the scoring pass) into the row's score
+// array: the scoring pass stores only the keys it flags.  kRT threads, 8
+// keys per thread, every load in flight before the first is used.
+__device__ void rescore_chunk(const Geo& g, const RowInfo& ri, const SelWs& ws, const bf16_t* __restrict__ k_low,
+                              const int32_t* btc, bool bt_cached, int c) {
+    const int tid = threadIdx.x;
+    float qv[kIdx];
+#pragma unroll
+    for (int x = 0; x < kIdx; ++x) qv[x] = bf2f(ws.qlow[(size_t)ri.lrow * kIdx + x]);
+    float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
+    const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
+    constexpr int K = kChunk / kRT;
+    uint4 kb[K][2];
+#pragma unroll
+    for (int x = 0; x < K; ++x) {
+        const int j = min(c * kChunk + tid + kRT * x, ri.L - 1);
+        const int page = bt_cached ? btc[j >> 8] : bt[j >> 8];
+        const uint4* kp = reinterpret_cast<const uint4*>(k_low + (((size_t)page * g.n_ret + ri.r) * kBlk + (j & 255)) * kIdx);
+        kb[x][0] = kp[0];
+        kb[x][1] = kp[1];
+    }
+#pragma unroll
+    for (int x = 0; x < K; ++x) {
+        const int j = c * kChunk + tid + kRT * x;
+        float kf[kIdx];
+        unpack8(kb[x][0], kf);
+        unpack8(kb[x][1], kf + 8);
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kIdx; ++i) acc = __builtin_fmaf(qv[i], kf[i], acc);
+        if (j < ri.L) srow[j] = acc;
+    }
+}
+
 // Row pass.  One kRT-thread workgroup per row: the plan, from the scoring
 // pass's chunk statistics (staged in LDS with the row's key masks when the
 // row has at most kStageChunks chunks, so that the plan makes no dependent
@@ -880,8 +920,8 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
 // over the row's scores.
 constexpr int kStageChunks = 48;   // chist (48 KiB) + ccnt (24 KiB) + key masks (24 KiB) + cmax of 48 chunks
 
-__device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const RowInfo& ri, const SelWs& ws,
-                         int32_t* __restrict__ status, ResolveSm& sm) {
+__device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf16_t* __restrict__ k_low,
+                         const RowInfo& ri, const SelWs& ws, int32_t* __restrict__ status, ResolveSm& sm) {
     const int tid = threadIdx.x;
     const size_t crow = (size_t)ri.lrow * ws.nchunk;
     const unsigned long long* chist = ws.chist + crow * kCB;
@@ -992,7 +1032,8 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const Ro
         nS0 = block_sum_u32<kRT>(c, sm.ured);
     }
     bool loaded = false;                                  // U and its weights in LDS
-    if (covered && nS0 <= (uint32_t)ws.ucap) {
+    const bool covered_path = covered && nS0 <= (uint32_t)ws.ucap;
+    if (covered_path) {
         const bool to_lds = nS0 <= (uint32_t)kCand;
         // pass 1: S0's indices in index order (4 mask words = 256 keys per thread and step)
         uint32_t base = 0u;
@@ -1061,7 +1102,16 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const Ro
         }
         nU = ubase;
         loaded = to_lds;
-    } else if (nU <= (unsigned long long)ws.ucap) {
+    } else {
+        // U is gathered from the scores, or the cut runs over the whole row:
+        // every chunk it reads gets all its scores (the scoring pass stored
+        // only the flagged keys')
+        const bool whole = nU > (unsigned long long)ws.ucap;
+        for (int c = 0; c < ri.nch; ++c)
+            if (whole || sm.plan.bsel[c] >= 0) rescore_chunk(g, ri, ws, k_low, sm.btc, bt_cached, c);
+        __syncthreads();
+    }
+    if (!covered_path && nU <= (unsigned long long)ws.ucap) {
         st.path = kPathFromScores;
         // U from the row's scores, 16 consecutive keys per thread (one chunk),
         // compacted in index order into LDS (with weights) or the workspace list
@@ -1116,10 +1166,11 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const Ro
     resolve_body(g, ri, ws, st, (int)nU, loaded, bt_cached, sm);
 }
 
-__global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+__global__ __launch_bounds__(kRT) void k_sel_row(Geo g, const float* __restrict__ top_p,
+                                                 const bf16_t* __restrict__ k_low, int row0, SelWs ws,
                                                  int32_t* __restrict__ status) {
     __shared__ ResolveSm sm;
-    row_pass(g, top_p, row_info(g, row0, blockIdx.x), ws, status, sm);
+    row_pass(g, top_p, k_low, row_info(g, row0, blockIdx.x), ws, status, sm);
 }
 
 // The row pass with the decode step's local-head window attention on its
@@ -1132,14 +1183,15 @@ struct WinSm {
     __align__(16) bf16_t Vs[32 * kWVsLd];
 };
 
-__global__ __launch_bounds__(kRT) void k_sel_row_win(Geo g, const float* __restrict__ top_p, int row0, SelWs ws,
+__global__ __launch_bounds__(kRT) void k_sel_row_win(Geo g, const float* __restrict__ top_p,
+                                                     const bf16_t* __restrict__ k_low, int row0, SelWs ws,
                                                      int32_t* __restrict__ status, WinWork wa) {
     __shared__ union {
         ResolveSm rs;
         WinSm w[kRT / 64];
     } u;
     if ((int)blockIdx.x < ws.rows) {
-        row_pass(g, top_p, row_info(g, row0, blockIdx.x), ws, status, u.rs);
+        row_pass(g, top_p, k_low, row_info(g, row0, blockIdx.x), ws, status, u.rs);
         return;
     }
     const int wv = threadIdx.x >> 6;
@@ -1264,9 +1316,10 @@ hipError_t launch_select(const Geo& g, const void* q, const void* w_q, const uin
     if (scores_only || stage == kSelScorePass) return hipGetLastError();
     if (stage == kSelRows && win && win->items > 0) {
         const int nw = std::min((win->items + kRT / 64 - 1) / (kRT / 64), std::max(1, kWinCUs - ws.rows));
-        hipLaunchKernelGGL(k_sel_row_win, dim3(ws.rows + nw), dim3(kRT), 0, s, g, top_p, row0, ws, out.status, *win);
+        hipLaunchKernelGGL(k_sel_row_win, dim3(ws.rows + nw), dim3(kRT), 0, s, g, top_p, kl, row0, ws, out.status,
+                           *win);
     } else {
-        hipLaunchKernelGGL(k_sel_row, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, row0, ws, out.status);
+        hipLaunchKernelGGL(k_sel_row, dim3(ws.rows), dim3(kRT), 0, s, g, top_p, kl, row0, ws, out.status);
     }
     if (stage == kSelRows) return hipGetLastError();
     const dim3 egrid(std::min(ws.nchunk, kEmitWG), ws.rows);
