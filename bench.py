@@ -339,8 +339,10 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     side = torch.cuda.Stream()
 
     # one call for the step's attention when its row pass can run the local
-    # heads' window items on its spare CUs (at most 128 retrieval rows)
-    fused_ok = B * w.n_ret <= 128
+    # heads' window items on its spare CUs (at most 128 retrieval rows, bf16
+    # K/V with head_dim 128: the MFMA window items); otherwise the window runs
+    # on a second stream beside the selection
+    fused_ok = B * w.n_ret <= 128 and not fp8 and w.dtype == "bf16" and w.D == 128
 
     def make_step(I, main, fused=True):
         sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])

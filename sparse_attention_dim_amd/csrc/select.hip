@@ -259,7 +259,9 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     // a bit per key for the row pass's gather of U: the key lies in chunk bin
     // <= kLowBin (the wave's 64 consecutive keys of step k are one 64-bit word);
     // only those keys' scores are stored (the row pass forms any other score
-    // it needs again from the indexer keys)
+    // it needs again from the indexer keys) -- except under a fixed top-k
+    // budget, whose cut usually lies below the flagged bins: then every score
+    // is stored
     unsigned long long* km = ws.kmask + ((size_t)ri.lrow * ws.score_ld + jbase) / 64;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             atomicAdd(&hist[b], wb.w);
             atomicAdd(&hcnt[b], 1u);
             low = b <= kLowBin;
-            if (low) srow[j] = dv[k];
+            if (low || g.sel_k > 0) srow[j] = dv[k];
         }
         const unsigned long long bal = __ballot(low);
         if ((tid & 63) == 0) km[4 * k + (tid >> 6)] = bal;
@@ -1048,15 +1050,46 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
             }
             unsigned long long t2;
             uint32_t o = base + (uint32_t)block_excl_scan_u64<kRT>(c, &t2, sm.scan_sh);
+            // each lane expands its own words bit by bit, or (when fewer
+            // steps: clustered flags, one thread's words holding hundreds of
+            // them) the wavefront expands its non-zero words one at a time, a
+            // lane per bit
+            const int lane = tid & 63;
+            const unsigned long long below = (1ull << lane) - 1ull;
+            int nzw = 0;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                unsigned long long mm = mw[x];
-                while (mm) {
-                    const int e = __ffsll((long long)mm) - 1;
-                    mm &= mm - 1ull;
-                    const unsigned long long ent = (unsigned long long)(~(uint32_t)(64 * (w0 + 4 * tid + x) + e));
-                    if (to_lds) sm.big[o] = ent; else gdst[o] = ent;
-                    ++o;
+            for (int x = 0; x < 4; ++x) nzw += __popcll(__ballot(mw[x] != 0ull));
+            if ((uint32_t)nzw >= wave_max_u32(c)) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    unsigned long long mm = mw[x];
+                    while (mm) {
+                        const int e = __ffsll((long long)mm) - 1;
+                        mm &= mm - 1ull;
+                        const unsigned long long ent = (unsigned long long)(~(uint32_t)(64 * (w0 + 4 * tid + x) + e));
+                        if (to_lds) sm.big[o] = ent; else gdst[o] = ent;
+                        ++o;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    unsigned long long nz = __ballot(mw[x] != 0ull);
+                    while (nz) {
+                        const int l = __ffsll((long long)nz) - 1;
+                        nz &= nz - 1ull;
+                        const unsigned long long wv =
+                            ((unsigned long long)(uint32_t)__builtin_amdgcn_readlane((int)(mw[x] >> 32), l) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mw[x], l);
+                        const uint32_t ow = (uint32_t)__builtin_amdgcn_readlane((int)o, l);
+                        if ((wv >> lane) & 1ull) {
+                            const uint32_t at = ow + (uint32_t)__popcll(wv & below);
+                            const int wi = w0 + 4 * (tid - lane + l) + x;
+                            const unsigned long long ent = (unsigned long long)(~(uint32_t)(64 * wi + lane));
+                            if (to_lds) sm.big[at] = ent; else gdst[at] = ent;
+                        }
+                    }
+                    o += (uint32_t)__popcll(mw[x]);
                 }
             }
             base += (uint32_t)t2;
@@ -1066,20 +1099,23 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
         // chunk bins formed again, U kept in place in index order (a batch's
         // entries are all read before the block scan that orders its writes)
         constexpr int R = 16;
+        // per thread and batch: per <= R consecutive entries, spread evenly
+        const uint32_t per = min((nS0 + kRT - 1) / kRT, (uint32_t)R);
         uint32_t ubase = 0u;
-        for (uint32_t i0 = 0; i0 < nS0; i0 += R * kRT) {
-            const uint32_t ib = i0 + R * tid;             // the thread's R consecutive entries
+        for (uint32_t i0 = 0; i0 < nS0; i0 += per * kRT) {
+            const uint32_t ib = i0 + per * tid;           // the thread's consecutive entries
+            const uint32_t ie = min(ib + per, nS0);
             uint32_t jx[R];
             float dv[R];
 #pragma unroll
             for (int x = 0; x < R; ++x)
-                jx[x] = ib + x < nS0 ? ~(uint32_t)(to_lds ? sm.big[ib + x] : gdst[ib + x]) : 0u;
+                jx[x] = ib + x < ie ? ~(uint32_t)(to_lds ? sm.big[ib + x] : gdst[ib + x]) : 0u;
 #pragma unroll
-            for (int x = 0; x < R; ++x) dv[x] = ib + x < nS0 ? srow[jx[x]] : 0.0f;
+            for (int x = 0; x < R; ++x) dv[x] = ib + x < ie ? srow[jx[x]] : 0.0f;
             uint32_t keep = 0u;
 #pragma unroll
             for (int x = 0; x < R; ++x) {
-                if (ib + x >= nS0) continue;
+                if (ib + x >= ie) continue;
                 const int ch = (int)(jx[x] / kChunk);
                 if ((weight_bin(dv[x], sm.plan.mc[ch], s).bin >> 4) <= sm.plan.bsel[ch]) keep |= 1u << x;
             }
@@ -1105,11 +1141,13 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
     } else {
         // U is gathered from the scores, or the cut runs over the whole row:
         // every chunk it reads gets all its scores (the scoring pass stored
-        // only the flagged keys')
+        // only the flagged keys', or every key's under a fixed top-k)
         const bool whole = nU > (unsigned long long)ws.ucap;
-        for (int c = 0; c < ri.nch; ++c)
-            if (whole || sm.plan.bsel[c] >= 0) rescore_chunk(g, ri, ws, k_low, sm.btc, bt_cached, c);
-        __syncthreads();
+        if (g.sel_k <= 0) {
+            for (int c = 0; c < ri.nch; ++c)
+                if (whole || sm.plan.bsel[c] >= 0) rescore_chunk(g, ri, ws, k_low, sm.btc, bt_cached, c);
+            __syncthreads();
+        }
     }
     if (!covered_path && nU <= (unsigned long long)ws.ucap) {
         st.path = kPathFromScores;
@@ -1118,22 +1156,33 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
         const bool to_lds = nU <= (unsigned long long)kCand;
         const uint32_t dcap = to_lds ? (uint32_t)kCand : (uint32_t)ws.ucap;
         uint32_t base = 0u;
+        // the next step's scores are requested before this step's are used;
+        // chunks without a part of U are not read
+        float4 nx[4];
+        const auto fetch = [&](int jj) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                nx[u] = jj < ri.L && sm.plan.bsel[jj / kChunk] >= 0
+                            ? *reinterpret_cast<const float4*>(srow + jj + 4 * u)
+                            : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        };
+        fetch(16 * tid);
         for (int j0 = 0; j0 < ri.L; j0 += 16 * kRT) {
             const int jj = j0 + 16 * tid;
             uint32_t msk = 0u, c = 0u;
             float dv[16];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                dv[4 * u] = nx[u].x;
+                dv[4 * u + 1] = nx[u].y;
+                dv[4 * u + 2] = nx[u].z;
+                dv[4 * u + 3] = nx[u].w;
+            }
+            fetch(jj + 16 * kRT);
             if (jj < ri.L) {
                 const int ch = jj / kChunk;
                 const int bs = sm.plan.bsel[ch];
                 const float mc = sm.plan.mc[ch];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float4 v = *reinterpret_cast<const float4*>(srow + jj + 4 * u);
-                    dv[4 * u] = v.x;
-                    dv[4 * u + 1] = v.y;
-                    dv[4 * u + 2] = v.z;
-                    dv[4 * u + 3] = v.w;
-                }
                 if (bs >= 0) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
