@@ -209,7 +209,7 @@ constexpr size_t kScoreBudget = (size_t)4 << 30;   // bytes of scores per row gr
 struct SelPlan {
     int rows_total, group_rows, nchunk, ucap;
     int64_t lpad;
-    size_t off_scores, off_cmax, off_qlow, off_chist, off_ccnt, off_st, off_sel, off_ubuf, off_kmask, total;
+    size_t off_scores, off_cmax, off_qlow, off_chist, off_ccnt, off_st, off_sel, off_ubuf, off_kmask, off_flist, total;
 };
 
 // Prefill chunks in bf16 take the tiled selection (the rows of one retrieval
@@ -227,7 +227,8 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     p.lpad = (int64_t)p.nchunk * rtp::kChunk;
     p.ucap = (int)std::min<int64_t>(rtp::kCandG, p.lpad);
     const size_t per_row =
-        (size_t)p.lpad * 4 + (size_t)p.lpad / 8 + (size_t)p.nchunk * (4 + 4 + rtp::kCB * 12) + (size_t)p.ucap * 12 +
+        (size_t)p.lpad * 4 + (size_t)p.lpad / 8 + (size_t)p.nchunk * (4 + 4 + rtp::kCB * 12 + rtp::kFl * 8) +
+        (size_t)p.ucap * 12 +
         1024;
     const int64_t by_budget = std::max<int64_t>(1, (int64_t)(kScoreBudget / per_row));
     p.group_rows = (int)std::min<int64_t>({(int64_t)p.rows_total, by_budget, (int64_t)65535});
@@ -242,6 +243,7 @@ SelPlan plan_select(const rtp_layer* L, const rtp_cache* C, const rtp_query* Q) 
     p.off_sel = o; o = align256(o + G * (size_t)p.ucap * 4);
     p.off_ubuf = o; o = align256(o + G * (size_t)p.ucap * 8);
     p.off_kmask = o; o = align256(o + G * (size_t)p.lpad / 8);
+    p.off_flist = o; o = align256(o + G * (size_t)p.nchunk * rtp::kFl * 8);
     p.total = o;
     return p;
 }
@@ -258,6 +260,7 @@ rtp::SelWs sel_ws(const SelPlan& p, char* base) {
     w.ubuf = (unsigned long long*)(base + p.off_ubuf);
     w.ccnt = (unsigned*)(base + p.off_ccnt);
     w.kmask = (unsigned long long*)(base + p.off_kmask);
+    w.flist = (unsigned long long*)(base + p.off_flist);
     w.nchunk = p.nchunk;
     w.rows = p.group_rows;
     w.ucap = p.ucap;

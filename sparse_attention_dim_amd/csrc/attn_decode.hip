@@ -230,13 +230,8 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
             const int r = r0 + i;
             if (r < rows) run += (int)((rp[r + 1] - rp[r] + kItem - 1) / kItem);
         }
-        int ex = run;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(ex, o);
-            if (lane >= o) ex += y;
-        }
-        const int total = __shfl(ex, 63);
+        int ex = (int)wave_incl_scan_u32((uint32_t)run);
+        const int total = (int)lane_u32((uint32_t)ex, 63);
         ex -= run;
         for (int i = 0; i < per; ++i) {
             const int r = r0 + i;
@@ -365,19 +360,10 @@ __global__ __launch_bounds__(64) void k_sparse_dec_sel(Geo g, const T* __restric
                 run += (c + kItem - 1) / kItem;
             }
         }
-        long long exs = cs;
-        int ex = run;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const long long ys = __shfl_up(exs, o);
-            const int y = __shfl_up(ex, o);
-            if (lane >= o) {
-                exs += ys;
-                ex += y;
-            }
-        }
-        const long long total_s = __shfl(exs, 63);
-        const int total = __shfl(ex, 63);
+        long long exs = (long long)wave_incl_scan_u64((unsigned long long)cs);
+        int ex = (int)wave_incl_scan_u32((uint32_t)run);
+        const long long total_s = (long long)lane_u64((unsigned long long)exs, 63);
+        const int total = (int)lane_u32((uint32_t)ex, 63);
         exs -= cs;
         ex -= run;
         for (int i = 0; i < per; ++i) {

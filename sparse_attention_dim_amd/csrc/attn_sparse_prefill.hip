@@ -91,12 +91,7 @@ __device__ __forceinline__ void set_ranges(int64_t b, int64_t e, Ranges& R) {
     R.rb[tid] = b;
     R.re[tid] = e;
     R.ra[tid] = a;
-    int x = n;                                         // inclusive scan over the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (tid >= o) x += y;
-    }
+    const int x = (int)wave_incl_scan_u32((uint32_t)n);   // inclusive scan over the wave
     R.cp[tid + 1] = x;
     if (tid == 0) R.cp[0] = 0;
 }

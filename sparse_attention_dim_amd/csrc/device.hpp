@@ -93,31 +93,100 @@ __device__ __forceinline__ float key_score(uint32_t k) {
     return __uint_as_float(u);
 }
 
-// ---- wave reductions (wave64) ----
+// ---- wave reductions and scans (wave64) ----
+// Lane exchanges inside a row of 16 lanes are DPP operand modifiers of the
+// VALU op itself (no LDS round trip, unlike a ds_bpermute shuffle); the four
+// rows are joined through scalar lane reads.  Every lane gets the result.
+// DPP controls: quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1, xor 2), the
+// half-row mirror (lane i <-> 7 - i of each 8), the row mirror (i <-> 15 - i),
+// and row_shr:n (lane i reads lane i - n of its row; 0 below the row's start).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp64(unsigned long long x) {
+    return (unsigned long long)dpp32<CTRL>((uint32_t)x) | ((unsigned long long)dpp32<CTRL>((uint32_t)(x >> 32)) << 32);
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t x, int l) { return (uint32_t)__builtin_amdgcn_readlane((int)x, l); }
+__device__ __forceinline__ unsigned long long lane_u64(unsigned long long x, int l) {
+    return (unsigned long long)lane_u32((uint32_t)x, l) | ((unsigned long long)lane_u32((uint32_t)(x >> 32), l) << 32);
+}
+// all-lane reduction of a 32-bit value under op (commutative, associative)
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce32(uint32_t x, Op op) {
+    x = op(x, dpp32<kDppXor1>(x));
+    x = op(x, dpp32<kDppXor2>(x));
+    x = op(x, dpp32<kDppHalfMirror>(x));
+    x = op(x, dpp32<kDppMirror>(x));
+    return op(op(lane_u32(x, 0), lane_u32(x, 16)), op(lane_u32(x, 32), lane_u32(x, 48)));
+}
+template <typename Op>
+__device__ __forceinline__ unsigned long long wave_reduce64(unsigned long long x, Op op) {
+    x = op(x, dpp64<kDppXor1>(x));
+    x = op(x, dpp64<kDppXor2>(x));
+    x = op(x, dpp64<kDppHalfMirror>(x));
+    x = op(x, dpp64<kDppMirror>(x));
+    return op(op(lane_u64(x, 0), lane_u64(x, 16)), op(lane_u64(x, 32), lane_u64(x, 48)));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    return __uint_as_float(wave_reduce32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return __uint_as_float(wave_reduce32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    return __longlong_as_double((long long)wave_reduce64((unsigned long long)__double_as_longlong(v),
+        [](unsigned long long a, unsigned long long b) {
+            return (unsigned long long)__double_as_longlong(__longlong_as_double((long long)a) +
+                                                           __longlong_as_double((long long)b));
+        }));
+}
+// sum over each row of 16 lanes (every lane of the row gets it)
+__device__ __forceinline__ double row_sum_f64(double v) {
+    const auto add = [](unsigned long long a, unsigned long long b) {
+        return (unsigned long long)__double_as_longlong(__longlong_as_double((long long)a) +
+                                                       __longlong_as_double((long long)b));
+    };
+    unsigned long long x = (unsigned long long)__double_as_longlong(v);
+    x = add(x, dpp64<kDppXor1>(x));
+    x = add(x, dpp64<kDppXor2>(x));
+    x = add(x, dpp64<kDppHalfMirror>(x));
+    x = add(x, dpp64<kDppMirror>(x));
+    return __longlong_as_double((long long)x);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) { uint32_t w = __shfl_xor(v, o); v = w > v ? w : v; }
-    return v;
+    return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce32(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    return wave_reduce64(v, [](unsigned long long a, unsigned long long b) { return a + b; });
+}
+// inclusive prefix sums over the wave's lanes (lane order)
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+    x += dpp32<0x111>(x);
+    x += dpp32<0x112>(x);
+    x += dpp32<0x114>(x);
+    x += dpp32<0x118>(x);
+    const uint32_t t0 = lane_u32(x, 15), t1 = lane_u32(x, 31), t2 = lane_u32(x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
+}
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long x) {
+    x += dpp64<0x111>(x);
+    x += dpp64<0x112>(x);
+    x += dpp64<0x114>(x);
+    x += dpp64<0x118>(x);
+    const unsigned long long t0 = lane_u64(x, 15), t1 = lane_u64(x, 31), t2 = lane_u64(x, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return x + (row >= 1 ? t0 : 0ull) + (row >= 2 ? t1 : 0ull) + (row >= 3 ? t2 : 0ull);
 }
 
 // Coherent (L2) loads of values written by other workgroups of the same grid.
@@ -179,12 +248,7 @@ template <int NT>
 __device__ __forceinline__ unsigned long long block_excl_scan_u64(unsigned long long v, unsigned long long* total,
                                                   unsigned long long* sh /* NT/64 */) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    unsigned long long x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        unsigned long long y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    const unsigned long long x = wave_incl_scan_u64(v);
     if (lane == 63) sh[wid] = x;
     __syncthreads();
     // every thread sums the wave totals itself (broadcast LDS reads)

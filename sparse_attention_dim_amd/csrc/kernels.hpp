@@ -24,6 +24,7 @@ constexpr int kPathMerge = 32;    // chunk path: ordered by merging the writers'
 constexpr int kPathExactZ = 64;   // the normaliser was summed exactly over every key
 constexpr int kPathCount = 128;   // the cut counted keys (fixed top-k, or the budget cap)
 constexpr int kPathFromScores = 256;  // decode path: U gathered from the row's scores (not from the key masks)
+constexpr int kPathFlagList = 512;    // decode path: U taken from the scoring pass's per-chunk lists of flagged keys
 
 // Geometry of one call (host-filled, passed by value to kernels).
 struct Geo {
@@ -106,6 +107,7 @@ constexpr int kCB = 128;          // mass-histogram bins per chunk (1/4 unit of 
 constexpr int kCand = 8192;       // candidates ranked in LDS
 constexpr int kCandG = 32768;     // candidates ranked from the workspace list (more: a cut over the scores)
 constexpr int kLowBin = 15;       // chunk bins flagged per key by the scoring pass (x_c < 4 units)
+constexpr int kFl = 512;         // entries of a chunk's list of flagged keys (more: the row takes the key masks)
 
 // Device workspace of the selection, for `rows` rows of at most Lpad keys.
 struct SelWs {
@@ -120,6 +122,8 @@ struct SelWs {
                                   // exceeds LDS: (score key << 32) | ~index
     unsigned* ccnt;               // [rows][nchunk][kCB] cumulative key counts of the chunk bins
     unsigned long long* kmask;    // [rows][Lpad / 64] bit j: key j lies in chunk bin <= kLowBin of its chunk
+    unsigned long long* flist;    // [rows][nchunk][kFl] each chunk's flagged keys in index order,
+                                  // (score key << 32) | ~index (its first kFl of them)
     int nchunk;
     int rows;                     // rows of this group
     int ucap;                     // row stride of ubuf / sel: min(kCandG, padded keys)

@@ -98,6 +98,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     __shared__ float wmax[4];
     __shared__ unsigned long long hist[kCB];
     __shared__ unsigned hcnt[kCB];
+    __shared__ uint32_t wcnt[STATS ? 64 : 1];            // flagged keys per 64-key word of the chunk
     __shared__ __align__(16) float qrow[128];
     __shared__ __align__(16) float wq[128 * kIdx];
     __shared__ float qs[kIdx];
@@ -263,6 +264,7 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
     // budget, whose cut usually lies below the flagged bins: then every score
     // is stored
     unsigned long long* km = ws.kmask + ((size_t)ri.lrow * ws.score_ld + jbase) / 64;
+    uint32_t lowm = 0u;                                   // bit k: this thread's key of step k is flagged
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int j = jbase + k * 256 + tid;
@@ -275,31 +277,44 @@ __global__ __launch_bounds__(256) void k_sel_score(Geo g, const T* __restrict__ 
             low = b <= kLowBin;
             if (low || g.sel_k > 0) srow[j] = dv[k];
         }
+        lowm |= low ? 1u << k : 0u;
         const unsigned long long bal = __ballot(low);
-        if ((tid & 63) == 0) km[4 * k + (tid >> 6)] = bal;
+        if ((tid & 63) == 0) {
+            km[4 * k + (tid >> 6)] = bal;
+            wcnt[4 * k + (tid >> 6)] = (uint32_t)__popcll(bal);
+        }
     }
     __syncthreads();
+    // the chunk's flagged keys in index order (word 4k + w holds keys
+    // jbase + 256 k + 64 w + lane): each key's place is the flagged count of
+    // the words before its own plus the flagged lanes below it in its word;
+    // the first kFl of them are listed (a chunk with more takes the masks)
+    {
+        const int lane = tid & 63, wv = tid >> 6;
+        const uint32_t wc = wcnt[lane];
+        const uint32_t wex = wave_incl_scan_u32(wc) - wc;
+        unsigned long long* fl = ws.flist + ((size_t)ri.lrow * ws.nchunk + chunk) * kFl;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const bool low = (lowm >> k) & 1u;
+            const unsigned long long bal = __ballot(low);
+            const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            const uint32_t at = lane_u32(wex, 4 * k + wv) + below;
+            if (low && at < (uint32_t)kFl)
+                fl[at] = ((unsigned long long)score_key(dv[k]) << 32) | (unsigned long long)(~(uint32_t)(jbase + k * 256 + tid));
+        }
+    }
     // cumulative over bins (the mass of keys with x_c < (b + 1) / 4)
     if (tid < 64) {
         const unsigned long long a = hist[2 * tid], b = hist[2 * tid + 1];
-        unsigned long long incl = a + b;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned long long y = __shfl_up(incl, o);
-            if (tid >= o) incl += y;
-        }
+        const unsigned long long incl = wave_incl_scan_u64(a + b);
         unsigned long long* ch = ws.chist + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
         ch[2 * tid] = incl - b;
         ch[2 * tid + 1] = incl;
     } else if (tid < 128) {
         const int t = tid - 64;
         const unsigned a = hcnt[2 * t], b = hcnt[2 * t + 1];
-        unsigned incl = a + b;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const unsigned y = __shfl_up(incl, o);
-            if (t >= o) incl += y;
-        }
+        const unsigned incl = wave_incl_scan_u32(a + b);
         unsigned* cc = ws.ccnt + ((size_t)ri.lrow * ws.nchunk + chunk) * kCB;
         cc[2 * t] = incl - b;
         cc[2 * t + 1] = incl;
@@ -509,7 +524,7 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long lo
         fch[tid] = f;
         z = f * (double)ztot;
     }
-    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);
+    z = wave_sum_f64(z);
     if ((tid & 63) == 0) dred[tid >> 6] = z;
     __syncthreads();
     double Z = 0.0;
@@ -540,8 +555,7 @@ __device__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long lo
                 lb += pl.unit ? (double)ccnt[(size_t)c * kCB + b] : fch[c] * (double)chist[(size_t)c * kCB + b];
             }
         }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) lb += __shfl_xor(lb, o);
+        lb = row_sum_f64(lb);                             // the 16 lanes of k are one DPP row
         return sub == 0 && lb >= need;
     };
     if (tid < 256 && lb_reaches(16 * grp + 15)) atomicMin(&s_k[1], grp);
@@ -638,15 +652,10 @@ __device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const flo
                             w = ow;
                         }
                     }
-                unsigned long long incl = w;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const unsigned long long y = __shfl_up(incl, o);
-                    if (lane >= o) incl += y;
-                }
+                const unsigned long long incl = wave_incl_scan_u64(w);
                 const unsigned long long reach = __ballot(lane < nbk && S_hi + incl >= target);
                 const int ic = reach ? __ffsll((long long)reach) - 1 : nbk - 1;
-                const unsigned long long vc = __shfl(v, ic);
+                const unsigned long long vc = lane_u64(v, ic);
                 if (lane == 0) {
                     s_cut->Tkey = (uint32_t)(vc >> 32);
                     s_cut->jT = (int32_t)~(uint32_t)vc;
@@ -707,6 +716,7 @@ struct ResolveSm {
             double fch[kMaxChunks], dch[kMaxChunks];
             int16_t bsel[kMaxChunks];                 // each chunk's last bin in U (-1: none)
             float mc[kMaxChunks];                     // each chunk's maximum score (the gather of U)
+            int32_t fofs[kMaxChunks];                 // each chunk's first place in S0 (the flagged-key lists)
         } plan;
     };
     unsigned long long small_v[64], small_w[64];
@@ -922,7 +932,7 @@ __device__ void rescore_chunk(const Geo& g, const RowInfo& ri, const SelWs& ws, 
 // over the row's scores.
 constexpr int kStageChunks = 48;   // chist (48 KiB) + ccnt (24 KiB) + key masks (24 KiB) + cmax of 48 chunks
 
-__device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf16_t* __restrict__ k_low,
+__device__ __forceinline__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf16_t* __restrict__ k_low,
                          const RowInfo& ri, const SelWs& ws, int32_t* __restrict__ status, ResolveSm& sm) {
     const int tid = threadIdx.x;
     const size_t crow = (size_t)ri.lrow * ws.nchunk;
@@ -1012,22 +1022,34 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
     // each chunk's part of U: its keys in chunk bins <= bsel; the masks hold
     // it when bsel <= kLowBin
     unsigned long long cnt_c = 0ull;
-    int cov = 1;
+    int cov = 1, flok = 1;
+    uint32_t nfl = 0u;                                    // the chunk's flagged keys, when it has a part of U
     if (tid < ri.nch) {
         const int b = chunk_bsel(pl.ks, sm.plan.dch[tid]);
         cnt_c = b >= 0 ? (unsigned long long)ccnt[(size_t)tid * kCB + b] : 0ull;
         cov = b <= kLowBin;
+        if (b >= 0) {
+            nfl = ccnt[(size_t)tid * kCB + kLowBin];      // keys of chunk bins <= kLowBin: the flagged ones
+            flok = nfl <= (uint32_t)kFl;
+        }
         sm.plan.bsel[tid] = (int16_t)b;
         sm.plan.mc[tid] = key_score(cmax[tid]);           // out of the staging area, which U overwrites
     }
-    unsigned long long nU;
-    block_excl_scan_u64<kRT>(cnt_c, &nU, sm.scan_sh);
+    // one scan for both counts (each sum < 2^32): U's keys (low half) and the flagged keys (high half)
+    unsigned long long both;
+    const unsigned long long pre = block_excl_scan_u64<kRT>(cnt_c | ((unsigned long long)nfl << 32), &both, sm.scan_sh);
+    if (tid < ri.nch) sm.plan.fofs[tid] = (int32_t)(pre >> 32);
+    unsigned long long nU = both & 0xFFFFFFFFull;
     const bool covered = __syncthreads_and(cov) != 0;
+    // every chunk with a part of U lists all its flagged keys: S0 is their lists, concatenated
+    const bool fl_route = covered && __syncthreads_and(flok) != 0;
     const float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     unsigned long long* gdst = ws.ubuf + (size_t)ri.lrow * ws.ucap;
     // S0: the flagged keys of the chunks with a part of U (covered rows)
     uint32_t nS0 = 0u;
-    if (covered) {
+    if (fl_route) {
+        nS0 = (uint32_t)(both >> 32);
+    } else if (covered) {
         uint32_t c = 0u;
         for (int wi = tid; wi < nwd; wi += kRT)
             if (sm.plan.bsel[wi / (kChunk / 64)] >= 0) c += (uint32_t)__popcll(kmask[wi]);
@@ -1036,7 +1058,36 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
     bool loaded = false;                                  // U and its weights in LDS
     const bool covered_path = covered && nS0 <= (uint32_t)ws.ucap;
     if (covered_path) {
-        const bool to_lds = nS0 <= (uint32_t)kCand;
+      const bool to_lds = nS0 <= (uint32_t)kCand;
+      if (fl_route) {
+        // pass 1: S0 from the chunks' lists (entries carry their score keys);
+        // entry i belongs to the last chunk whose first place is <= i (chunks
+        // without a part of U list nothing here)
+        const unsigned long long* flr = ws.flist + (size_t)ri.lrow * ws.nchunk * kFl;
+        constexpr int F = 16;
+        for (uint32_t i0 = 0; i0 < nS0; i0 += F * kRT) {
+            unsigned long long e[F];
+#pragma unroll
+            for (int x = 0; x < F; ++x) {
+                const uint32_t i = i0 + x * kRT + tid;
+                e[x] = 0ull;
+                if (i < nS0) {
+                    int lo = 0;                           // fofs is non-decreasing, fofs[0] = 0
+#pragma unroll
+                    for (int step = kMaxChunks / 2; step > 0; step >>= 1)
+                        if (lo + step < ri.nch && (uint32_t)sm.plan.fofs[lo + step] <= i) lo += step;
+                    e[x] = flr[(size_t)lo * kFl + (i - (uint32_t)sm.plan.fofs[lo])];
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < F; ++x) {
+                const uint32_t i = i0 + x * kRT + tid;
+                if (i < nS0) {
+                    if (to_lds) sm.big[i] = e[x]; else gdst[i] = e[x];
+                }
+            }
+        }
+      } else {
         // pass 1: S0's indices in index order (4 mask words = 256 keys per thread and step)
         uint32_t base = 0u;
         for (int w0 = 0; w0 < nwd; w0 += 4 * kRT) {
@@ -1094,8 +1145,10 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
             }
             base += (uint32_t)t2;
         }
+      }
         __syncthreads();
-        // pass 2: S0's scores (every load of a batch in flight together), their
+        // pass 2: S0's scores (every load of a batch in flight together, or
+        // the score keys of the listed entries), their
         // chunk bins formed again, U kept in place in index order (a batch's
         // entries are all read before the block scan that orders its writes)
         constexpr int R = 16;
@@ -1108,10 +1161,15 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
             uint32_t jx[R];
             float dv[R];
 #pragma unroll
-            for (int x = 0; x < R; ++x)
-                jx[x] = ib + x < ie ? ~(uint32_t)(to_lds ? sm.big[ib + x] : gdst[ib + x]) : 0u;
+            for (int x = 0; x < R; ++x) {
+                const unsigned long long e = ib + x < ie ? (to_lds ? sm.big[ib + x] : gdst[ib + x]) : 0ull;
+                jx[x] = ib + x < ie ? ~(uint32_t)e : 0u;
+                dv[x] = key_score((uint32_t)(e >> 32));
+            }
+            if (!fl_route) {
 #pragma unroll
-            for (int x = 0; x < R; ++x) dv[x] = ib + x < ie ? srow[jx[x]] : 0.0f;
+                for (int x = 0; x < R; ++x) dv[x] = ib + x < ie ? srow[jx[x]] : 0.0f;
+            }
             uint32_t keep = 0u;
 #pragma unroll
             for (int x = 0; x < R; ++x) {
@@ -1138,6 +1196,7 @@ __device__ void row_pass(const Geo& g, const float* __restrict__ top_p, const bf
         }
         nU = ubase;
         loaded = to_lds;
+        if (fl_route) st.path = kPathFlagList;
     } else {
         // U is gathered from the scores, or the cut runs over the whole row:
         // every chunk it reads gets all its scores (the scoring pass stored

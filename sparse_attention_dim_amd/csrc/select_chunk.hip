@@ -1251,20 +1251,14 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                             i0 < n ? (unit ? 1ull : weight_bin(key_score((uint32_t)(cr[i0] >> 32)), mpr, s).w) : 0ull;
                         const unsigned long long w1 =
                             i1 < n ? (unit ? 1ull : weight_bin(key_score((uint32_t)(cr[i1] >> 32)), mpr, s).w) : 0ull;
-                        unsigned long long incl = w0 + w1;
-#pragma unroll
-                        for (int o = 1; o < 64; o <<= 1) {
-                            const unsigned long long y = __shfl_up(incl, o);
-                            if (lane >= o) incl += y;
-                        }
+                        const unsigned long long incl = wave_incl_scan_u64(w0 + w1);
                         const unsigned long long c0 = r_shi[row] + incl - w1;   // through rank i0
                         const unsigned long long c1 = c0 + w1;                  // through rank i1
                         const unsigned long long tgt = r_target[row];
                         int first = 1 << 30;
                         if (i0 < n && c0 >= tgt) first = i0;
                         else if (i1 < n && c1 >= tgt) first = i1;
-#pragma unroll
-                        for (int o = 32; o > 0; o >>= 1) first = min(first, __shfl_xor(first, o));
+                        first = (int)wave_reduce32((uint32_t)first, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
                         if (first >= n) bad = 1;
                         const int ic = first < n ? first : n - 1;
                         {
@@ -1277,11 +1271,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                                 a = c1;
                                 b = c0;
                             }
-#pragma unroll
-                            for (int o = 32; o > 0; o >>= 1) {
-                                a += __shfl_xor(a, o);
-                                b += __shfl_xor(b, o);
-                            }
+                            a = wave_sum_u64(a);
+                            b = wave_sum_u64(b);
                             pk = a;
                             pk1 = b;
                         }
@@ -1293,11 +1284,8 @@ __global__ __launch_bounds__(256) void k_csel_main(Geo g, const bf16_t* __restri
                         if (i1 <= ic) {
                             if ((uint32_t)(cr[i1] >> 32) == kT) ++tie; else ++above;
                         }
-#pragma unroll
-                        for (int o = 32; o > 0; o >>= 1) {
-                            tie += __shfl_xor(tie, o);
-                            above += __shfl_xor(above, o);
-                        }
+                        tie = (int)wave_sum_u32((uint32_t)tie);
+                        above = (int)wave_sum_u32((uint32_t)above);
                         out.T = key_score(kT);
                         out.n_tie = tie;
                         out.count = (int)r_cnthi[row] + above + tie;
@@ -1550,15 +1538,10 @@ __device__ void resolve_row(const Geo& g, const CRow& cr, int row, int rid, bool
                             w = ow;
                         }
                     }
-                unsigned long long incl = w;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const unsigned long long y = __shfl_up(incl, o);
-                    if (lane >= o) incl += y;
-                }
+                const unsigned long long incl = wave_incl_scan_u64(w);
                 const unsigned long long reach = __ballot(lane < nbk && S_hi + incl >= target);
                 const int ic = reach ? __ffsll((long long)reach) - 1 : nbk - 1;
-                const uint32_t tk = (uint32_t)(__shfl(v, ic) >> 32);
+                const uint32_t tk = (uint32_t)(lane_u64(v, ic) >> 32);
                 const unsigned long long tie = __ballot(lane <= ic && lane < nbk && (uint32_t)(v >> 32) == tk);
                 if (lane == 0) {
                     sm.tkey = tk;

@@ -72,7 +72,7 @@ __device__ __forceinline__ void item_sync() {
 // one wavefront (lane = threadIdx.x % 64); pgs (64 ints) and Vs (32 x kWVsLd
 // bf16) are the wavefront's own LDS.
 template <bool kInWave>
-__device__ void win_mfma_item(const Geo& g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc_main,
+__device__ __forceinline__ void win_mfma_item(const Geo& g, const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc_main,
                               const bf16_t* __restrict__ vc_main, float* __restrict__ part, int nsplit,
                               int split_keys, int dense, int split, int bkv, int* pgs, bf16_t* Vs) {
     constexpr int D = 128;

@@ -203,7 +203,8 @@ def path_counts(paths: np.ndarray) -> dict:
     for name, code in (("all", 1), ("tiny", 2), ("row", 3), ("large", 4), ("level", 5), ("list", 6),
                        ("scan", 7), ("list_g", 8)):
         out[name] = int(np.sum((paths & 15) == code))
-    for name, bit in (("bitmap", 16), ("merge", 32), ("exact_z", 64), ("count", 128), ("from_scores", 256)):
+    for name, bit in (("bitmap", 16), ("merge", 32), ("exact_z", 64), ("count", 128), ("from_scores", 256),
+                      ("flag_list", 512)):
         out[name] = int(np.sum((paths & bit) != 0))
     return out
 
