@@ -656,7 +656,9 @@ template <typename T, typename TKV, int D>
 hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
                           const SelOut& so, void* out, const AttnWs& ws, int rows, const WinWork* win,
                           hipStream_t s) {
-    const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), 4096);
+    // enough workgroups for every item of a small batch at once (a workgroup
+    // past the last item only reads the row records)
+    const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), rows <= 128 ? 1024 : 4096);
     const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1) + sizeof(int32_t) * rows;
     hipLaunchKernelGGL((k_sparse_dec_sel<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
                        (const TKV*)k, (const TKV*)v, sw, so, ws, rows);

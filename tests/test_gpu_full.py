@@ -146,6 +146,24 @@ def _decode_case(i, seqs):
     _check_dense(w, out_f32(dense), [(t, int(h)) for t in seqs for h in g.choice(w.Hq, 3, replace=False)])
     sizes = [n for *_, n in res]
     say("   budgets of checked rows: min %d median %d max %d" % (min(sizes), int(np.median(sizes)), max(sizes)))
+    # the step's attention in one call (rtp_decode_attn, as the benchmark runs
+    # it): the same sets and bit-identical outputs as the oracle-checked calls
+    say("[gpu-full] %s: rtp_decode_attn" % w.name)
+    cap = int(sum(int(l) for l in w.seq_lens) * w.n_ret)
+    row_ptr = torch.zeros(d.rows + 1, dtype=torch.int64, device="cuda")
+    idx = torch.full((cap,), -1, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    sel = rtp.make_sel(row_ptr, idx, status)
+    fout = torch.zeros_like(d.q)
+    ws = torch.empty(rtp.decode_attn_workspace(d.layer, d.cache, d.query, cap), dtype=torch.uint8, device="cuda")
+    for _ in range(2):                                  # twice: a call leaves no state behind
+        rtp.decode_attn(d.layer, d.cache, d.query, d.w_q, d.top_p, sel, fout, ws)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        np.testing.assert_array_equal(row_ptr.cpu().numpy(), rp)
+        n = int(rp[-1])
+        np.testing.assert_array_equal(idx[:n].cpu().numpy(), d.idx[:n].cpu().numpy())
+        assert torch.equal(fout, d.out), "rtp_decode_attn outputs differ from the separate calls"
     del d
     _free()
 
