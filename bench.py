@@ -540,6 +540,61 @@ def select_variants(res, w, steps: int):
     return out
 
 
+def gqa_variant(res, w, steps: int):
+    """The step's attention in one call with and without RTP_FLAG_GQA_SHARED
+    (the retrieval heads of one KV head gather the union of their selected
+    keys once) on a decode leg's instances: median step time of each, and the
+    K/V rows the sparse attention gathers (the union of a group's sets when
+    the group's lists together hold at most 8192 keys, which the union pass
+    merges; otherwise the lists one after another)."""
+    import numpy as np
+    import torch
+
+    import sparse_attention_dim_amd as rtp
+
+    inst = res["_inst"]
+    I = inst[0]
+    out = {}
+    for name, flags in (("separate", 0), ("shared", rtp.RTP_FLAG_GQA_SHARED)):
+        lay = rtp.make_layer(w.Hq, w.Hkv, w.D, rtp.RTP_BF16, w.ret_heads, w.window, w.sinks, w.attn_scale,
+                             w.idx_scale, flags=flags)
+        calls = []
+        for J in inst:
+            ws = torch.empty(rtp.decode_attn_workspace(lay, J["cache"], J["query"], J["sel"].capacity),
+                             dtype=torch.uint8, device="cuda")
+            J["_ws_gqa"] = ws
+            calls.append(rtp.decode_attn(lay, J["cache"], J["query"], J["w_q"], J["top_p"], J["sel"], J["out"], ws,
+                                         prepare=True))
+        for c in calls:
+            c()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for s_, (e0, e1) in enumerate(ev):
+            e0.record()
+            calls[s_ % len(calls)]()
+            e1.record()
+        torch.cuda.synchronize()
+        out[name + "_step_us"] = stats([e0.elapsed_time(e1) * 1e3 for e0, e1 in ev])
+        for J in inst:
+            J.pop("_ws_gqa", None)
+    rp = I["row_ptr"].cpu().numpy()
+    ix = I["idx"].cpu().numpy()
+    total = union = gathered = 0
+    for t in range(w.B):
+        groups = {}
+        for r, h in enumerate(w.ret_heads):
+            groups.setdefault(h // (w.Hq // w.Hkv), []).append(ix[rp[t * w.n_ret + r]: rp[t * w.n_ret + r + 1]])
+        for sets in groups.values():
+            n = sum(len(x) for x in sets)
+            u = len(np.unique(np.concatenate(sets)))
+            total += n
+            union += u
+            gathered += u if (len(sets) > 1 and n <= 8192) else n
+    kv_row = w.D * 2 * 2
+    out.update({"selected_keys": int(total), "union_keys": int(union), "gathered_keys": int(gathered),
+                "sparse_kv_bytes_separate": int(total) * kv_row, "sparse_kv_bytes_shared": int(gathered) * kv_row})
+    return out
+
+
 def score_roofline(res, w, steps: int):
     """The dominant kernel: the indexer score pass (k_sel_score), timed live
     with HIP events around back-to-back rtp_indexer_scores calls on the
@@ -825,9 +880,20 @@ def main():
     head = decode_leg(w, args, args.instances, args.steps, args.warmup, extras=True, tag="decode")
     roof = score_roofline(head, w, args.steps)
     variants = {} if args.no_variants else select_variants(head, w, max(50, args.steps))
+    if not args.no_variants:
+        variants["gqa_shared_gathers"] = {"independent_clusters": gqa_variant(head, w, max(50, args.steps))}
     for k in ("_inst", "_layer", "_bytes_klow"):
         head.pop(k, None)
     torch.cuda.empty_cache()
+    if not args.no_variants:
+        # the same shapes with the retrieval heads of a KV head sharing their
+        # planted cluster (overlapping sets): the bytes a shared gather saves
+        ws_ = synth.cluster_decode(seed=1002, shared_kv=True, name="decode_bf16_B8_L131072_shared_clusters")
+        rs = decode_leg(ws_, args, 2, args.steps, args.warmup, dense=False, graph=False, extras=True,
+                        tag="decode shared clusters")
+        variants["gqa_shared_gathers"]["shared_clusters"] = gqa_variant(rs, ws_, max(50, args.steps))
+        del rs, ws_
+        torch.cuda.empty_cache()
     if args.only == "decode":
         calibration_copy()
         print(json.dumps(dict(head, roofline=roof, variants=variants)))

@@ -73,6 +73,14 @@ extern "C" {
 #define RTP_FLAG_EXACT_MASS 1  /* bf16 chunk selection: sum the indexer-softmax normaliser exactly over
                                   every key of every row (an extra pass over the indexer keys of each
                                   row; the selected sets are those of the default, certified route) */
+#define RTP_FLAG_GQA_SHARED 2  /* rtp_decode_attn: the retrieval heads of one KV head (at most 4 per KV
+                                  head) gather the union of their selected keys once, each key row
+                                  read once and scored for every head whose set holds it (abstract:
+                                  retrieval heads keep the full KV cache; grouped-query attention
+                                  shares it between query heads).  Same sets, same CSR; outputs as
+                                  rtp_sparse_attn_decode up to the order of the partial merges.
+                                  bf16 or fp32 K/V, decode queries whose selection fits one
+                                  workspace pass; ignored by the other calls */
 
 typedef enum {
     RTP_OK = 0,

@@ -22,6 +22,7 @@ RTP_BLOCK = 256
 RTP_MAX_RET = 64
 RTP_MAX_LEN = 1 << 20
 RTP_FLAG_EXACT_MASS = 1
+RTP_FLAG_GQA_SHARED = 2
 RTP_NOALLOC_SCRATCH_BYTES = 64 << 20
 # selection status word
 SEL_OK, SEL_OVERFLOW, SEL_UNCERTIFIED, SEL_BAD_TOP_P = 0, 1, 2, 3

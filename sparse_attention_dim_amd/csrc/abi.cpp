@@ -86,7 +86,7 @@ rtp_status check_layer(const rtp_layer* L) {
     if (!(L->attn_scale > 0.0f) || !std::isfinite(L->attn_scale)) return fail(RTP_EINVAL, "attn_scale");
     if (!(L->idx_scale > 0.0f) || !std::isfinite(L->idx_scale)) return fail(RTP_EINVAL, "idx_scale");
     if (L->k_max < 0) return fail(RTP_EINVAL, "k_max %d < 0", L->k_max);
-    if (L->flags & ~RTP_FLAG_EXACT_MASS) return fail(RTP_EINVAL, "unknown flags 0x%x", L->flags);
+    if (L->flags & ~(RTP_FLAG_EXACT_MASS | RTP_FLAG_GQA_SHARED)) return fail(RTP_EINVAL, "unknown flags 0x%x", L->flags);
     if (L->kv_fp8 != 0 && L->kv_fp8 != 1) return fail(RTP_EINVAL, "kv_fp8 %d", L->kv_fp8);
     if (L->kv_fp8) {
         if (L->dtype != RTP_BF16) return fail(RTP_EUNSUPPORTED, "FP8 K/V needs dtype RTP_BF16");
@@ -544,7 +544,7 @@ rtp_status rtp_sparse_attn_decode(const rtp_layer* layer, const rtp_cache* cache
     if (!workspace || workspace_bytes < need)
         return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
     const int64_t items = sparse_max_items(layer, query, sel->capacity);
-    rtp::AttnWs w;
+    rtp::AttnWs w{};
     w.part = (float*)workspace;
     w.item_start = (int32_t*)((char*)workspace + align256((size_t)items * (layer->head_dim + 2) * 4));
     w.max_items = items;
@@ -574,7 +574,7 @@ rtp_status rtp_sparse_attn_prefill(const rtp_layer* layer, const rtp_cache* cach
     }
     const int rows = query->n_tok * layer->num_ret;
     const int64_t items = sparse_max_items(layer, query, sel->capacity);
-    rtp::AttnWs w;
+    rtp::AttnWs w{};
     w.part = (float*)workspace;
     w.item_start = (int32_t*)((char*)workspace + align256((size_t)items * (layer->head_dim + 2) * 4));
     w.max_items = items;
@@ -596,11 +596,34 @@ static size_t sparse_dec_ws_bytes(const rtp_layer* layer, const rtp_query* query
     return align256((size_t)items * (layer->head_dim + 2) * 4) + align256((size_t)(rows + 1) * 4);
 }
 
+// Shared gathers: at most kGqaMax retrieval heads per KV head.
+static int gqa_max_group(const rtp_layer* L) {
+    int best = 0, run = 0;
+    for (int r = 0; r < L->num_ret; ++r) {
+        run = (r && L->ret_heads[r - 1] / (L->num_q_heads / L->num_kv_heads) ==
+                        L->ret_heads[r] / (L->num_q_heads / L->num_kv_heads)) ? run + 1 : 1;
+        best = std::max(best, run);
+    }
+    return best;
+}
+
+// Extra workspace of the shared gathers: kGqaMax partial slots per item, the
+// unions' keys and membership bytes (one padded row of keys per row), counts.
+static size_t gqa_ws_bytes(const rtp_layer* layer, const rtp_query* query, int64_t capacity, int64_t lpad) {
+    const int64_t rows = (int64_t)query->n_tok * layer->num_ret;
+    const int64_t items = sparse_max_items(layer, query, capacity);
+    return align256((size_t)items * rtp::kGqaMax * (layer->head_dim + 2) * 4) +
+           align256((size_t)rows * lpad * 4) + align256((size_t)rows * lpad) + align256((size_t)rows * 4);
+}
+
+static bool gqa_on(const rtp_layer* layer) { return (layer->flags & RTP_FLAG_GQA_SHARED) && layer->kv_fp8 == 0; }
+
 size_t rtp_decode_attn_workspace(const rtp_layer* layer, const rtp_cache* cache, const rtp_query* query,
                                  int64_t capacity) {
     if (check_all(layer, cache, query) || capacity < 0 || query->kind != RTP_DECODE) return 0;
-    return plan_select(layer, cache, query).total + sparse_dec_ws_bytes(layer, query, capacity) +
-           win_ws_bytes(layer, cache, query, 0);
+    const SelPlan p = plan_select(layer, cache, query);
+    return p.total + sparse_dec_ws_bytes(layer, query, capacity) + win_ws_bytes(layer, cache, query, 0) +
+           (gqa_on(layer) ? gqa_ws_bytes(layer, query, capacity, p.lpad) : 0);
 }
 
 // Rows of one decode step up to which the row pass runs the window items on
@@ -620,13 +643,17 @@ rtp_status rtp_decode_attn(const rtp_layer* layer, const rtp_cache* cache, const
     const int rows = query->n_tok * layer->num_ret;
     if (rows > kMaxDecodeRows) return fail(RTP_EUNSUPPORTED, "batch * num_ret %d > %d", rows, kMaxDecodeRows);
     const SelPlan p = plan_select(layer, cache, query);
+    const bool gqa = gqa_on(layer);
+    if (gqa && gqa_max_group(layer) > rtp::kGqaMax)
+        return fail(RTP_EUNSUPPORTED, "RTP_FLAG_GQA_SHARED serves at most %d retrieval heads per KV head", rtp::kGqaMax);
     const size_t sp_bytes = sparse_dec_ws_bytes(layer, query, sel->capacity);
-    const size_t need = p.total + sp_bytes + win_ws_bytes(layer, cache, query, 0);
+    const size_t win_bytes = win_ws_bytes(layer, cache, query, 0);
+    const size_t need = p.total + sp_bytes + win_bytes + (gqa ? gqa_ws_bytes(layer, query, sel->capacity, p.lpad) : 0);
     if (!workspace || workspace_bytes < need)
         return fail(RTP_EWORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
     const int64_t items = sparse_max_items(layer, query, sel->capacity);
     char* aw = (char*)workspace + p.total;
-    rtp::AttnWs w;
+    rtp::AttnWs w{};
     w.part = (float*)aw;
     w.item_start = (int32_t*)(aw + align256((size_t)items * (layer->head_dim + 2) * 4));
     w.max_items = items;
@@ -661,8 +688,21 @@ rtp_status rtp_decode_attn(const rtp_layer* layer, const rtp_cache* cache, const
     hipError_t e = rtp::launch_select(g, query->q, w_q, (const uint16_t*)cache->k_low, top_p, 0, sw, so, rows,
                                       layer->dtype, rtp::kSelRows, st, merged ? &win : nullptr, &app);
     if (e != hipSuccess) return hip_status(e, "top-p select launch");
-    e = rtp::launch_sparse_decode_sel(g, query->q, cache->k, cache->v, sw, so, out, w, rows, layer->dtype,
-                                      merged ? &win : nullptr, st);
+    if (gqa) {
+        // the shared gathers' partials ([item][kGqaMax][D + 2]) and unions after the window's partials
+        char* gw = aw + sp_bytes + win_bytes;
+        const size_t part_bytes = align256((size_t)items * rtp::kGqaMax * (layer->head_dim + 2) * 4);
+        w.part = (float*)gw;
+        w.ukey = (uint32_t*)(gw + part_bytes);
+        w.umask = (uint8_t*)(gw + part_bytes + align256((size_t)rows * p.lpad * 4));
+        w.ucnt = (int32_t*)(gw + part_bytes + align256((size_t)rows * p.lpad * 4) + align256((size_t)rows * p.lpad));
+        w.ulen = p.lpad;
+        e = rtp::launch_sparse_decode_gqa(g, query->q, cache->k, cache->v, sw, so, out, w, rows, layer->dtype,
+                                          merged ? &win : nullptr, st);
+    } else {
+        e = rtp::launch_sparse_decode_sel(g, query->q, cache->k, cache->v, sw, so, out, w, rows, layer->dtype,
+                                          merged ? &win : nullptr, st);
+    }
     if (e != hipSuccess) return hip_status(e, "sparse decode launch");
     if (merged) return ok();
     return hip_status(rtp::launch_window_decode(g, query->q, cache->k, cache->v, out, wpart, nsplit, split, 0,

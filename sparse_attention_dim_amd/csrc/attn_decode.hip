@@ -101,6 +101,11 @@ struct Stream {
     // (valid for 0 <= i < n).  Group g of the wave takes keys g, g + GPW, ...
     template <typename F>
     __device__ void run(int n, F off, const T* __restrict__ kc, const T* __restrict__ vc) {
+        run(n, off, kc, vc, [](int) { return ~0u; });
+    }
+    // The same, with msk(i): bit h set when key i is one of head slot h's keys.
+    template <typename F, typename MK>
+    __device__ void run(int n, F off, const T* __restrict__ kc, const T* __restrict__ vc, MK msk) {
         const int lane = threadIdx.x & 63;
         const int g = lane / LPK, sl = (lane % LPK) * EPV;
         for (int base = 0; base < n; base += GPW * U) {
@@ -118,13 +123,14 @@ struct Stream {
                 float f[EPV];
                 Pack<T>::unpack(kb[u], f);
                 const bool ok = base + u * GPW + g < n;
+                const uint32_t km = msk(min(base + u * GPW + g, n - 1));
 #pragma unroll
                 for (int h = 0; h < NH; ++h) {
                     float acc = 0.0f;
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) acc = __builtin_fmaf(q[h][e], f[e], acc);
                     acc = group_sum<LPK>(acc);
-                    s[u][h] = ok ? acc : -INFINITY;
+                    s[u][h] = ok && ((km >> h) & 1u) ? acc : -INFINITY;
                 }
             }
 #pragma unroll
@@ -291,16 +297,20 @@ __global__ __launch_bounds__(64) void k_sparse_dec_part(Geo g, const T* __restri
 // item order on one wavefront: o[d] = sum_i 2^(m_i - M) o_i[d] / L * post.
 // Lane l owns dims l, l + 64, ...; the partials are read 16 items per round.
 template <typename T, int D>
-__device__ void combine_wave(const float* __restrict__ base, int n, T* __restrict__ o, float post) {
+__device__ void combine_wave(const float* __restrict__ base, int n, T* __restrict__ o, float post,
+                             int stride = D + 2) {
     constexpr int DPL = D / 64;
     constexpr int B = 16;
     const int lane = threadIdx.x & 63;
     float mx = -INFINITY;
-    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, base[(size_t)i * (D + 2) + D]);
+    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, base[(size_t)i * stride + D]);
     const float M = wave_max(mx);
     float ls = 0.0f;
-    for (int i = lane; i < n; i += 64)
-        ls += exp2f(base[(size_t)i * (D + 2) + D] - M) * base[(size_t)i * (D + 2) + D + 1];
+    for (int i = lane; i < n; i += 64) {
+        const float mi = base[(size_t)i * stride + D];
+        // a partial holding none of the row's keys (a shared gather's item) weighs nothing
+        if (mi != -INFINITY) ls += exp2f(mi - M) * base[(size_t)i * stride + D + 1];
+    }
     const float L = wave_sum(ls);
     float acc[DPL];
 #pragma unroll
@@ -310,13 +320,14 @@ __device__ void combine_wave(const float* __restrict__ base, int n, T* __restric
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             const int i = min(i0 + b, n - 1);
-            mv[b] = base[(size_t)i * (D + 2) + D];
+            mv[b] = base[(size_t)i * stride + D];
 #pragma unroll
-            for (int x = 0; x < DPL; ++x) ov[b][x] = base[(size_t)i * (D + 2) + lane + 64 * x];
+            for (int x = 0; x < DPL; ++x) ov[b][x] = base[(size_t)i * stride + lane + 64 * x];
         }
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             if (i0 + b >= n) break;
+            if (mv[b] == -INFINITY) continue;
             const float w = exp2f(mv[b] - M);
 #pragma unroll
             for (int x = 0; x < DPL; ++x) acc[x] = __builtin_fmaf(ov[b][x], w, acc[x]);
@@ -485,25 +496,257 @@ __global__ __launch_bounds__(64) void k_sparse_dec_combine(Geo g, const int32_t*
     combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);   // V scale of FP8 codes
 }
 
+// ---------------------------------------------------------------------------
+// Shared gathers (GQA): the retrieval heads of one KV head form a group of
+// consecutive retrieval rows of a token (retrieval heads are ascending, so
+// heads of one KV head are adjacent); the group's first row holds the union
+// of their selected keys and each key's membership bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int gqa_first(const Geo& g, int r) {
+    const int kv = g.ret_heads[r] / g.group;
+    while (r > 0 && g.ret_heads[r - 1] / g.group == kv) --r;
+    return r;
+}
+__device__ __forceinline__ int gqa_size(const Geo& g, int r0) {
+    const int kv = g.ret_heads[r0] / g.group;
+    int n = 1;
+    while (r0 + n < g.n_ret && g.ret_heads[r0 + n] / g.group == kv) ++n;
+    return n;
+}
+
+// Key i of a row's selected set (ascending): every key (mode 0), the ordered
+// list (mode 1) or the row's score array overwritten by the indices (mode 2).
+__device__ __forceinline__ uint32_t sel_key(const SelWs& sw, int lrow, int mode, int i) {
+    return mode == 0 ? (uint32_t)i
+         : mode == 1 ? sw.sel[(size_t)lrow * sw.ucap + i]
+                     : (uint32_t)reinterpret_cast<const int32_t*>(sw.scores + (size_t)lrow * sw.score_ld)[i];
+}
+
+constexpr int kUnionT = 512;      // union pass threads
+constexpr int kUnionLds = 8192;   // keys of a group merged in LDS (a larger group concatenates its lists)
+
+// Union pass, one workgroup per row: the row's CSR (row pointer, and its keys
+// into idx), and for a group's first row the group's union.  Lists are merged
+// in LDS with duplicates adjacent (a key of list a lands after the keys of the
+// other lists below it, and after equal keys of lists before a), then each
+// run of equal keys becomes one union entry carrying the run's membership
+// bits, in ascending key order.
+__global__ __launch_bounds__(kUnionT) void k_gqa_union(Geo g, SelWs sw, SelOut so, AttnWs ws, int rows) {
+    const int tid = threadIdx.x;
+    if (*so.status != 0) return;                          // an invalid top_p was reported: nothing emitted
+    const int row = blockIdx.x;
+    __shared__ unsigned long long red[2][kUnionT / 64];
+    __shared__ uint32_t lst[kUnionLds], mrg[kUnionLds];
+    __shared__ int32_t s_cnt[kGqaMax], s_mode[kGqaMax], s_off[kGqaMax + 1];
+    __shared__ unsigned long long scan_sh[kUnionT / 64 + 1];
+    unsigned long long before = 0ull, all = 0ull;
+    for (int i = tid; i < rows; i += kUnionT) {
+        const unsigned long long c = (unsigned long long)sw.st[i].count;
+        all += c;
+        if (i < row) before += c;
+    }
+    before = wave_sum_u64(before);
+    all = wave_sum_u64(all);
+    if ((tid & 63) == 0) {
+        red[0][tid >> 6] = before;
+        red[1][tid >> 6] = all;
+    }
+    __syncthreads();
+    before = 0ull;
+    all = 0ull;
+#pragma unroll
+    for (int w = 0; w < kUnionT / 64; ++w) {
+        before += red[0][w];
+        all += red[1][w];
+    }
+    const RowState st = sw.st[row];
+    if (tid == 0) {
+        so.row_ptr[row + 1] = (int64_t)(before + (unsigned long long)st.count);
+        if (row == 0 && (int64_t)all > so.capacity) *so.status = 1;   // the size needed is row_ptr[rows]
+    }
+    if ((int64_t)all > so.capacity) return;
+    for (int i = tid; i < st.count; i += kUnionT) so.idx[before + i] = (int32_t)sel_key(sw, row, st.mode, i);
+    const int t = row / g.n_ret, r = row - t * g.n_ret;
+    if (gqa_first(g, r) != r) return;
+    const int n = gqa_size(g, r);
+    if (tid < n) {
+        const RowState sr = sw.st[row + tid];
+        s_cnt[tid] = sr.count;
+        s_mode[tid] = sr.mode;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        s_off[0] = 0;
+        for (int i = 0; i < n; ++i) s_off[i + 1] = s_off[i] + s_cnt[i];
+    }
+    __syncthreads();
+    const int tot = s_off[n];
+    uint32_t* uk = ws.ukey + (size_t)row * ws.ulen;      // the group's rows' regions, together >= tot entries
+    uint8_t* um = ws.umask + (size_t)row * ws.ulen;
+    if (n < 2 || tot > kUnionLds) {
+        // one row, or too many keys to merge here: the lists one after another
+        for (int i = 0; i < n; ++i)
+            for (int k = tid; k < s_cnt[i]; k += kUnionT) {
+                uk[s_off[i] + k] = sel_key(sw, row + i, s_mode[i], k);
+                um[s_off[i] + k] = (uint8_t)(1u << i);
+            }
+        if (tid == 0) ws.ucnt[row] = tot;
+        return;
+    }
+    for (int e = tid; e < tot; e += kUnionT) {
+        int i = 0;
+        while (e >= s_off[i + 1]) ++i;
+        lst[e] = sel_key(sw, row + i, s_mode[i], e - s_off[i]);
+    }
+    __syncthreads();
+    for (int e = tid; e < tot; e += kUnionT) {
+        int i = 0;
+        while (e >= s_off[i + 1]) ++i;
+        const uint32_t x = lst[e];
+        int pos = e - s_off[i];
+        for (int b = 0; b < n; ++b) {
+            if (b == i) continue;
+            // keys of list b below x (and equal to x when b comes first)
+            int lo = s_off[b], hi = s_off[b + 1];
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (lst[mid] < x || (b < i && lst[mid] == x)) lo = mid + 1; else hi = mid;
+            }
+            pos += lo - s_off[b];
+        }
+        mrg[pos] = (x << 2) | (uint32_t)i;
+    }
+    __syncthreads();
+    // each thread a run of consecutive merged entries: one scan orders the kept ones
+    const int per = (tot + kUnionT - 1) / kUnionT;
+    const int e0 = min(tid * per, tot), e1 = min(e0 + per, tot);
+    uint32_t nkeep = 0u;
+    for (int e = e0; e < e1; ++e) nkeep += e == 0 || (mrg[e - 1] >> 2) != (mrg[e] >> 2);
+    unsigned long long t2;
+    uint32_t o = (uint32_t)block_excl_scan_u64<kUnionT>(nkeep, &t2, scan_sh);
+    for (int e = e0; e < e1; ++e) {
+        const uint32_t x = mrg[e] >> 2;
+        if (e > 0 && (mrg[e - 1] >> 2) == x) continue;
+        uint32_t msk = 0u;
+        for (int q2 = e; q2 < tot && (mrg[q2] >> 2) == x; ++q2) msk |= 1u << (mrg[q2] & 3u);
+        uk[o] = x;
+        um[o] = (uint8_t)msk;
+        ++o;
+    }
+    if (tid == 0) ws.ucnt[row] = (int32_t)t2;
+}
+
+// Sparse decode over the groups' unions: one wavefront per (group, piece of
+// kItem union keys); each key row is read once and scored for every head of
+// the group whose set holds it (the others see it masked out).  Partials:
+// [item][kGqaMax][D + 2].
+template <typename T, typename TKV, int D>
+__global__ __launch_bounds__(64) void k_sparse_dec_gqa(Geo g, const T* __restrict__ q,
+                                                       const TKV* __restrict__ kc,
+                                                       const TKV* __restrict__ vc, SelOut so, AttnWs ws, int rows) {
+    using S = Stream<TKV, D, kGqaMax, 8>;
+    if (*so.status != 0) return;
+    const int lane = threadIdx.x;
+    extern __shared__ int32_t istart[];                   // rows + 1
+    __shared__ uint32_t joff[kItem];
+    __shared__ uint32_t jm[kItem];
+    {
+        const int per = (rows + 63) / 64;
+        const int r0 = lane * per;
+        int run = 0;
+        for (int i = 0; i < per; ++i) {
+            const int rr = r0 + i;
+            if (rr < rows) {
+                const int tt = rr / g.n_ret, r = rr - tt * g.n_ret;
+                if (gqa_first(g, r) == r) run += (ws.ucnt[rr] + kItem - 1) / kItem;
+            }
+        }
+        int ex = (int)wave_incl_scan_u32((uint32_t)run);
+        const int total = (int)lane_u32((uint32_t)ex, 63);
+        ex -= run;
+        for (int i = 0; i < per; ++i) {
+            const int rr = r0 + i;
+            if (rr < rows) {
+                istart[rr] = ex;
+                const int tt = rr / g.n_ret, r = rr - tt * g.n_ret;
+                if (gqa_first(g, r) == r) ex += (ws.ucnt[rr] + kItem - 1) / kItem;
+            }
+        }
+        if (lane == 0) istart[rows] = total;
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+        for (int r = lane; r <= rows; r += 64) ws.item_start[r] = istart[r];
+    const int total = istart[rows];
+    const float sc = g.attn_scale * kLog2e * g.k_scale;
+    constexpr int EPV = S::EPV, LPK = S::LPK;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        // the last row with istart <= item: istart[row + 1] > item, so the row
+        // has items, i.e. it is the first row of its group
+        int lo = 0, hi = rows - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (istart[mid] <= item) lo = mid; else hi = mid - 1;
+        }
+        const int row = lo;
+        const int t = row / g.n_ret, r0 = row - t * g.n_ret;
+        const int n = gqa_size(g, r0);
+        const int kvh = g.ret_heads[r0] / g.group;
+        const int k0 = (item - istart[row]) * kItem;
+        const int nk = min(kItem, ws.ucnt[row] - k0);
+        const int32_t* bt = g.block_table + (size_t)row_seq(g, t) * g.max_blocks;
+        const int i = k0 + min(lane, nk - 1);
+        const uint32_t j = ws.ukey[(size_t)row * ws.ulen + i];
+        jm[lane] = ws.umask[(size_t)row * ws.ulen + i];
+        joff[lane] = (uint32_t)kv_rowidx(g, bt[j >> 8], kvh, j & 255);
+        S st;
+        st.init();
+        const int sl = (lane % LPK) * EPV;
+#pragma unroll
+        for (int hh = 0; hh < kGqaMax; ++hh) {
+            st.act[hh] = hh < n;
+            const int h = g.ret_heads[min(r0 + hh, g.n_ret - 1)];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) st.q[hh][e] = hh < n ? ld(q + ((size_t)t * g.Hq + h) * D + sl + e) * sc : 0.0f;
+        }
+        __syncthreads();
+        auto off = [&](int x) { return (size_t)joff[x] * D; };
+        auto msk = [&](int x) { return jm[x]; };
+        st.run(nk, off, kc, vc, msk);
+        st.merge();
+#pragma unroll
+        for (int hh = 0; hh < kGqaMax; ++hh)
+            if (hh < n) st.write(hh, ws.part + ((size_t)item * kGqaMax + hh) * (D + 2));
+        __syncthreads();
+    }
+}
+
 // The decode step's combine: workgroups [0, rows) merge the retrieval rows'
 // partials (nothing when the selection reported an error), the others the
 // window partials of (sequence, local head) pairs, workgroup rows + b Hq + h.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_dec_combine_all(Geo g, const int32_t* __restrict__ status, AttnWs ws,
                                                         T* __restrict__ out, int rows, const float* __restrict__ wpart,
-                                                        int nsplit, int split_keys) {
+                                                        int nsplit, int split_keys, int gqa) {
     const int blk = blockIdx.x;
     if (blk < rows) {
         if (*status != 0) return;
         const int t = blk / g.n_ret, r = blk - t * g.n_ret;
         const int h = g.ret_heads[r];
-        const int i0 = ws.item_start[blk], i1 = ws.item_start[blk + 1];
+        // shared gathers: the row's slot among the partials of its group's items
+        const int r0 = gqa ? gqa_first(g, r) : r;
+        const int lrow0 = t * g.n_ret + r0;
+        const int i0 = ws.item_start[lrow0], i1 = ws.item_start[lrow0 + 1];
         T* o = out + ((size_t)t * g.Hq + h) * D;
         if (i1 <= i0) {
             for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
             return;
         }
-        combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);
+        if (gqa)
+            combine_wave<T, D>(ws.part + ((size_t)i0 * kGqaMax + (r - r0)) * (D + 2), i1 - i0, o, g.v_scale,
+                               kGqaMax * (D + 2));
+        else
+            combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);
         return;
     }
     const int bh = blk - rows, b = bh / g.Hq, h = bh - b * g.Hq;
@@ -664,7 +907,7 @@ hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void
                        (const TKV*)k, (const TKV*)v, sw, so, ws, rows);
     if (win && win->items > 0)
         hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + g.batch * g.Hq), dim3(64), 0, s, g, so.status, ws,
-                           (T*)out, rows, win->part, win->nsplit, win->split_keys);
+                           (T*)out, rows, win->part, win->nsplit, win->split_keys, 0);
     else
         hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, so.status, ws, (T*)out, 0);
     return hipGetLastError();
@@ -719,6 +962,31 @@ hipError_t launch_sparse_decode_sel(const Geo& g, const void* q, const void* k, 
     if (dtype == 0 && g.D == 128) return sparse_dec_sel<float, float, 128>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
     if (dtype == 1 && g.D == 64) return sparse_dec_sel<bf16_t, bf16_t, 64>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
     return sparse_dec_sel<bf16_t, bf16_t, 128>(g, q, k, v, sw, so, out, ws, rows, win, s);
+}
+
+template <typename T, typename TKV, int D>
+hipError_t sparse_dec_gqa(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
+                          const SelOut& so, void* out, const AttnWs& ws, int rows, const WinWork* win,
+                          hipStream_t s) {
+    hipLaunchKernelGGL(k_gqa_union, dim3(rows), dim3(kUnionT), 0, s, g, sw, so, ws, rows);
+    const int64_t grid = std::min<int64_t>(std::max<int64_t>(ws.max_items, 1), rows <= 128 ? 1024 : 4096);
+    const size_t shmem = sizeof(int32_t) * (rows + 1);
+    hipLaunchKernelGGL((k_sparse_dec_gqa<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
+                       (const TKV*)k, (const TKV*)v, so, ws, rows);
+    const bool wc = win && win->items > 0;
+    hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + (wc ? g.batch * g.Hq : 0)), dim3(64), 0, s, g,
+                       so.status, ws, (T*)out, rows, wc ? win->part : (const float*)nullptr, wc ? win->nsplit : 0,
+                       wc ? win->split_keys : 0, 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_sparse_decode_gqa(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
+                                    const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
+                                    const WinWork* win, hipStream_t s) {
+    if (dtype == 0 && g.D == 64) return sparse_dec_gqa<float, float, 64>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    if (dtype == 0 && g.D == 128) return sparse_dec_gqa<float, float, 128>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    if (dtype == 1 && g.D == 64) return sparse_dec_gqa<bf16_t, bf16_t, 64>(g, q, k, v, sw, so, out, ws, rows, nullptr, s);
+    return sparse_dec_gqa<bf16_t, bf16_t, 128>(g, q, k, v, sw, so, out, ws, rows, win, s);
 }
 
 hipError_t launch_window_decode(const Geo& g, const void* q, const void* k, const void* v, void* out,

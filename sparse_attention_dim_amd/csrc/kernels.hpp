@@ -188,10 +188,18 @@ constexpr int kSparseItem = 64;
 
 // Split-K partial attention of retrieval rows over their selected sets and the combine.
 struct AttnWs {
-    float* part;                  // [items][D + 2]
+    float* part;                  // [items][D + 2] ([items][kGqaMax][D + 2] for shared gathers)
     int32_t* item_start;          // [rows + 1]
     int64_t max_items;
+    // shared gathers of the retrieval heads of one KV head (a group of
+    // consecutive retrieval rows of a token): the union of their selected keys
+    // in the region of the group's first row
+    uint32_t* ukey;               // [rows][ulen] union keys
+    uint8_t* umask;               // [rows][ulen] bit i: key selected by the group's row i
+    int32_t* ucnt;                // [rows] union size (first row of a group)
+    int64_t ulen;
 };
+constexpr int kGqaMax = 4;        // retrieval heads per KV head served by one shared gather
 // Rows [row0, row0 + rows) of the call (rows <= 4096); row_ptr is the full CSR array.
 hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, const void* v,
                                 const int64_t* row_ptr, const int32_t* idx, const int32_t* status,
@@ -203,6 +211,12 @@ hipError_t launch_sparse_decode(const Geo& g, const void* q, const void* k, cons
 // win (bf16 D = 128 only): the window partials written by the row pass are
 // merged by the same combine launch.
 hipError_t launch_sparse_decode_sel(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
+                                    const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
+                                    const WinWork* win, hipStream_t s);
+// The same with the retrieval heads of one KV head gathering the union of
+// their selected keys once (bf16 or fp32 K/V): a union pass (which also writes
+// the CSR), the sparse items over the unions, and the combine.
+hipError_t launch_sparse_decode_gqa(const Geo& g, const void* q, const void* k, const void* v, const SelWs& sw,
                                     const SelOut& so, void* out, const AttnWs& ws, int rows, int dtype,
                                     const WinWork* win, hipStream_t s);
 

@@ -270,8 +270,11 @@ def _plant(vec_f32: np.ndarray, dims: np.ndarray, a: float, u: np.ndarray,
 
 def cluster_decode(seed=2, lens=(131072,) * 8, Hq=32, Hkv=8, D=128, n_ret=6, p=0.95,
                    window=2048, sinks=64, rope=5e5, dtype="bf16", size_dist=("loguniform", 16, 4096),
-                   ret_heads=None, name="cluster_decode"):
-    """Decode with one planted relevance cluster per (sequence, retrieval head)."""
+                   ret_heads=None, name="cluster_decode", shared_kv=False):
+    """Decode with one planted relevance cluster per (sequence, retrieval head).
+    shared_kv: retrieval heads that share a KV head share their cluster (the
+    first head of the group draws its positions and direction, the others
+    plant only their queries along it), so their selected sets overlap."""
     lens = np.asarray(lens, np.int64)
     B = len(lens)
     ret = sample_ret_heads(seed, Hq, n_ret) if ret_heads is None else list(ret_heads)
@@ -287,19 +290,25 @@ def cluster_decode(seed=2, lens=(131072,) * 8, Hq=32, Hkv=8, D=128, n_ret=6, p=0
         L = int(lens[b])
         a = amplitude(n_min, L, 0.25)
         amps[b] = a
+        first = {}                                        # KV head -> the group's cluster (shared_kv)
         for r, h in enumerate(ret):
             gen = rng(seed, 2, b, h)
-            n = _draw_size(gen, size_dist, L)
-            sizes[(b, h)] = n
-            if n == 0:
-                continue
-            pos = gen.choice(L - 1, size=n, replace=False)
-            u = gen.standard_normal(16)
-            u /= np.linalg.norm(u)
             g = h // (Hq // Hkv)
-            kf = as_f32(K[b][pos, g, :]).copy()
-            _plant(kf, dims, a, u, gen.standard_normal((n, 16)))
-            K[b][pos, g, :] = to_storage(kf, dtype)
+            if shared_kv and g in first:
+                n, u = first[g]
+                sizes[(b, h)] = n
+            else:
+                n = _draw_size(gen, size_dist, L)
+                sizes[(b, h)] = n
+                if n == 0:
+                    continue
+                pos = gen.choice(L - 1, size=n, replace=False)
+                u = gen.standard_normal(16)
+                u /= np.linalg.norm(u)
+                first[g] = (n, u)
+                kf = as_f32(K[b][pos, g, :]).copy()
+                _plant(kf, dims, a, u, gen.standard_normal((n, 16)))
+                K[b][pos, g, :] = to_storage(kf, dtype)
             qf = as_f32(q[b, h]).copy()
             _plant(qf, dims, a, u, gen.standard_normal(16))
             q[b, h] = to_storage(qf, dtype)

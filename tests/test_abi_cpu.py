@@ -274,3 +274,25 @@ def test_decode_attn_checks():
     assert call(sel=_sel(capacity=-1)) == rtp.RTP_EINVAL
     big = _cache(batch=1500, max_blocks=4, max_seq_len=1000)       # 4500 rows: more than the sparse kernel's 4096
     assert call(cache=big, query=_query(n_tok=1500), ws_bytes=1 << 40) == rtp.RTP_EUNSUPPORTED
+
+
+def test_decode_attn_gqa_shared_checks():
+    # shared gathers: more workspace (partials of every head slot, the unions),
+    # and at most four retrieval heads per KV head
+    lib = rtp.load()
+    C, Q = _cache(), _query()
+    L0 = _layer()
+    L1 = _layer(flags=rtp.RTP_FLAG_GQA_SHARED)
+    n0 = lib.rtp_decode_attn_workspace(ctypes.byref(L0), ctypes.byref(C), ctypes.byref(Q), 100)
+    n1 = lib.rtp_decode_attn_workspace(ctypes.byref(L1), ctypes.byref(C), ctypes.byref(Q), 100)
+    assert n1 > n0
+    many = rtp.make_layer(16, 2, 128, rtp.RTP_BF16, [0, 1, 2, 3, 4], 64, 4, 0.088, 0.25,
+                          flags=rtp.RTP_FLAG_GQA_SHARED)     # five retrieval heads on KV head 0
+    need = lib.rtp_decode_attn_workspace(ctypes.byref(many), ctypes.byref(C), ctypes.byref(Q), 100)
+    assert need > 0
+    r = lib.rtp_decode_attn(ctypes.byref(many), ctypes.byref(C), ctypes.byref(Q), FAKE, None, FAKE,
+                            ctypes.byref(_sel()), FAKE, FAKE, need, None)
+    assert r == rtp.RTP_EUNSUPPORTED
+    assert b"KV head" in lib.rtp_last_error()
+    bad = _layer(flags=8)
+    assert lib.rtp_decode_attn_workspace(ctypes.byref(bad), ctypes.byref(C), ctypes.byref(Q), 100) == 0
