@@ -493,7 +493,7 @@ struct Plan {
 // NT threads (dred, ured: NT / 64 entries); chist, ccnt, cmax: the row's
 // chunk statistics (device memory or an LDS copy).
 template <int NT>
-__device__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long long* __restrict__ chist,
+__device__ __forceinline__ Plan row_plan(const Geo& g, const RowInfo& ri, const unsigned long long* __restrict__ chist,
                          const unsigned* __restrict__ ccnt, const uint32_t* __restrict__ cmax, float p,
                          double* fch, double* dch, double* dred, uint32_t* ured, int* s_k) {
     const int tid = threadIdx.x;
@@ -637,21 +637,26 @@ __device__ Cut list_cut(const unsigned long long* cand, Wt wgt, int n, const flo
             __syncthreads();
             if (tid < 64) {
                 const int nbk = (int)min(*s_u, 64u);
-                unsigned long long v = lane < nbk ? small_v[lane] : 0ull;
-                unsigned long long w = lane < nbk ? small_w[lane] : 0ull;
+                const unsigned long long v0 = lane < nbk ? small_v[lane] : 0ull;
+                const unsigned long long w0 = lane < nbk ? small_w[lane] : 0ull;
+                // each key's place in descending order: the keys above it (the
+                // entries are distinct), counted from broadcast LDS reads
+                int rank = 0;
+                for (int j0 = 0; j0 < nbk; j0 += 16) {
+                    unsigned long long c[16];
 #pragma unroll
-                for (int k = 2; k <= 64; k <<= 1)
+                    for (int u = 0; u < 16; ++u) c[u] = small_v[min(j0 + u, 63)];
 #pragma unroll
-                    for (int j = k >> 1; j > 0; j >>= 1) {
-                        const unsigned long long ov = __shfl_xor(v, j), ow = __shfl_xor(w, j);
-                        const bool desc = (lane & k) == 0 || k == 64;
-                        const bool lower = (lane & j) == 0;
-                        const bool take = desc == lower ? ov > v : ov < v;
-                        if (take) {
-                            v = ov;
-                            w = ow;
-                        }
-                    }
+                    for (int u = 0; u < 16; ++u) rank += (j0 + u < nbk && c[u] > v0) ? 1 : 0;
+                }
+                // (one wavefront: every lane's reads above precede the writes)
+                if (lane < nbk) {
+                    small_v[rank] = v0;
+                    small_w[rank] = w0;
+                }
+                __builtin_amdgcn_wave_barrier();
+                const unsigned long long v = lane < nbk ? small_v[lane] : 0ull;
+                const unsigned long long w = lane < nbk ? small_w[lane] : 0ull;
                 const unsigned long long incl = wave_incl_scan_u64(w);
                 const unsigned long long reach = __ballot(lane < nbk && S_hi + incl >= target);
                 const int ic = reach ? __ffsll((long long)reach) - 1 : nbk - 1;
@@ -736,7 +741,7 @@ struct ResolveSm {
 // gathered (nU > ucap: the cut over the row's scores).  Writes the row's state
 // and its selected keys: the workspace list of the row (mode 1), or the
 // row's score array overwritten in place by the indices (mode 2).
-__device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, RowState st, int nU, bool loaded,
+__device__ __forceinline__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, RowState st, int nU, bool loaded,
                              bool bt_cached, ResolveSm& sm) {
     const int tid = threadIdx.x;
     unsigned long long* cand = sm.big;
@@ -890,7 +895,7 @@ __device__ void resolve_body(const Geo& g, const RowInfo& ri, const SelWs& ws, R
 // from the indexer keys (q_low from the scoring pass) into the row's score
 // array: the scoring pass stores only the keys it flags.  kRT threads, 8
 // keys per thread, every load in flight before the first is used.
-__device__ void rescore_chunk(const Geo& g, const RowInfo& ri, const SelWs& ws, const bf16_t* __restrict__ k_low,
+__device__ __forceinline__ void rescore_chunk(const Geo& g, const RowInfo& ri, const SelWs& ws, const bf16_t* __restrict__ k_low,
                               const int32_t* btc, bool bt_cached, int c) {
     const int tid = threadIdx.x;
     float qv[kIdx];
@@ -1151,11 +1156,14 @@ __device__ __forceinline__ void row_pass(const Geo& g, const float* __restrict__
         // the score keys of the listed entries), their
         // chunk bins formed again, U kept in place in index order (a batch's
         // entries are all read before the block scan that orders its writes)
-        constexpr int R = 16;
-        // per thread and batch: per <= R consecutive entries, spread evenly
-        const uint32_t per = min((nS0 + kRT - 1) / kRT, (uint32_t)R);
+        // per thread and batch: per <= 16 consecutive entries, spread evenly;
+        // the loop is unrolled for the smallest R >= per (a row of a few
+        // hundred keys does not step through 16 predicated slots)
+        const uint32_t per = min((nS0 + kRT - 1) / kRT, 16u);
         uint32_t ubase = 0u;
-        for (uint32_t i0 = 0; i0 < nS0; i0 += per * kRT) {
+        auto pass2 = [&](auto RC) {
+          constexpr int R = decltype(RC)::value;
+          for (uint32_t i0 = 0; i0 < nS0; i0 += per * kRT) {
             const uint32_t ib = i0 + per * tid;           // the thread's consecutive entries
             const uint32_t ie = min(ib + per, nS0);
             uint32_t jx[R];
@@ -1193,7 +1201,12 @@ __device__ __forceinline__ void row_pass(const Geo& g, const float* __restrict__
                 ++o;
             }
             ubase += (uint32_t)t2;
-        }
+          }
+        };
+        if (per <= 2) pass2(std::integral_constant<int, 2>{});
+        else if (per <= 4) pass2(std::integral_constant<int, 4>{});
+        else if (per <= 8) pass2(std::integral_constant<int, 8>{});
+        else pass2(std::integral_constant<int, 16>{});
         nU = ubase;
         loaded = to_lds;
         if (fl_route) st.path = kPathFlagList;
