@@ -338,11 +338,12 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
         (tag, instances, torch.cuda.memory_allocated() / 1e9))
     side = torch.cuda.Stream()
 
-    # one call for the step's attention when its row pass can run the local
-    # heads' window items on its spare CUs (at most 128 retrieval rows, bf16
-    # K/V with head_dim 128: the MFMA window items); otherwise the window runs
-    # on a second stream beside the selection
-    fused_ok = B * w.n_ret <= 128 and not fp8 and w.dtype == "bf16" and w.D == 128
+    # one call for the step's attention (rtp_decode_attn) for batches of at
+    # most 128 retrieval rows with bf16 or fp32 K/V (with bf16, D = 128 its row
+    # pass also runs the local heads' window items on its spare CUs); the
+    # ragged batch of 64 (384 rows) and FP8 K/V run the separate calls, the
+    # window on a second stream beside the selection (measured faster there)
+    fused_ok = B * w.n_ret <= 128 and not fp8
 
     def make_step(I, main, fused=True):
         sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
