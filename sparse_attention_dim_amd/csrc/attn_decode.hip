@@ -337,6 +337,78 @@ __device__ void combine_wave(const float* __restrict__ base, int n, T* __restric
     for (int x = 0; x < DPL; ++x) st<T>(o + lane + 64 * x, acc[x] / L * post);
 }
 
+// Merge the n partials of a retrieval row on kCombW wavefronts: wave w merges
+// its own run of partials (relative to the run's maximum), and wave 0 merges
+// the runs in order, so a row of hundreds of pieces is not one wavefront's
+// serial loop.  Deterministic for a given n.  sh: kCombW * (D + 2) floats.
+constexpr int kCombW = 8;
+template <typename T, int D>
+__device__ void combine_block(const float* __restrict__ base, int n, T* __restrict__ o, float post, int stride,
+                              float* sh) {
+    constexpr int DPL = D / 64;
+    constexpr int B = 16;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int per = (n + kCombW - 1) / kCombW;
+    const int i0 = min(wv * per, n), i1 = min(i0 + per, n);
+    float mx = -INFINITY;
+    for (int i = i0 + lane; i < i1; i += 64) mx = fmaxf(mx, base[(size_t)i * stride + D]);
+    const float Mw = wave_max(mx);
+    float ls = 0.0f;
+    for (int i = i0 + lane; i < i1; i += 64) {
+        const float mi = base[(size_t)i * stride + D];
+        if (mi != -INFINITY) ls += exp2f(mi - Mw) * base[(size_t)i * stride + D + 1];
+    }
+    const float Lw = wave_sum(ls);
+    float acc[DPL];
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) acc[x] = 0.0f;
+    for (int j0 = i0; j0 < i1; j0 += B) {
+        float ov[B][DPL], mv[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const int i = min(j0 + b, i1 - 1);
+            mv[b] = base[(size_t)i * stride + D];
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) ov[b][x] = base[(size_t)i * stride + lane + 64 * x];
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (j0 + b >= i1) break;
+            if (mv[b] == -INFINITY) continue;
+            const float w = exp2f(mv[b] - Mw);
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) acc[x] = __builtin_fmaf(ov[b][x], w, acc[x]);
+        }
+    }
+    float* me = sh + wv * (D + 2);
+#pragma unroll
+    for (int x = 0; x < DPL; ++x) me[lane + 64 * x] = acc[x];
+    if (lane == 0) {
+        me[D] = Mw;
+        me[D + 1] = Lw;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kCombW; ++w) M = fmaxf(M, sh[w * (D + 2) + D]);
+        float L = 0.0f, a[DPL];
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) a[x] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kCombW; ++w) {
+            const float mw = sh[w * (D + 2) + D];
+            if (mw == -INFINITY) continue;
+            const float f = exp2f(mw - M);
+            L = __builtin_fmaf(f, sh[w * (D + 2) + D + 1], L);
+#pragma unroll
+            for (int x = 0; x < DPL; ++x) a[x] = __builtin_fmaf(sh[w * (D + 2) + lane + 64 * x], f, a[x]);
+        }
+#pragma unroll
+        for (int x = 0; x < DPL; ++x) st<T>(o + lane + 64 * x, a[x] / L * post);
+    }
+}
+
 // Sparse decode straight from the selection's row records (the work items of
 // k_sparse_dec_part): each row's selected keys are read from the selection
 // workspace (its ordered list -- with the keys' K/V row numbers when the row
@@ -480,7 +552,7 @@ __device__ void combine_parts(const float* __restrict__ base, int n, T* __restri
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_sparse_dec_combine(Geo g, const int32_t* __restrict__ status,
+__global__ __launch_bounds__(64 * kCombW) void k_sparse_dec_combine(Geo g, const int32_t* __restrict__ status,
                                                            AttnWs ws, T* __restrict__ out, int row0) {
     if (*status != 0) return;
     const int row = blockIdx.x;
@@ -493,7 +565,8 @@ __global__ __launch_bounds__(64) void k_sparse_dec_combine(Geo g, const int32_t*
         for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
         return;
     }
-    combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);   // V scale of FP8 codes
+    __shared__ float sh[kCombW * (D + 2)];
+    combine_block<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale, D + 2, sh);   // V scale of FP8 codes
 }
 
 // ---------------------------------------------------------------------------
@@ -725,7 +798,7 @@ __global__ __launch_bounds__(64) void k_sparse_dec_gqa(Geo g, const T* __restric
 // partials (nothing when the selection reported an error), the others the
 // window partials of (sequence, local head) pairs, workgroup rows + b Hq + h.
 template <typename T, int D>
-__global__ __launch_bounds__(64) void k_dec_combine_all(Geo g, const int32_t* __restrict__ status, AttnWs ws,
+__global__ __launch_bounds__(64 * kCombW) void k_dec_combine_all(Geo g, const int32_t* __restrict__ status, AttnWs ws,
                                                         T* __restrict__ out, int rows, const float* __restrict__ wpart,
                                                         int nsplit, int split_keys, int gqa) {
     const int blk = blockIdx.x;
@@ -742,15 +815,16 @@ __global__ __launch_bounds__(64) void k_dec_combine_all(Geo g, const int32_t* __
             for (int d = threadIdx.x; d < D; d += blockDim.x) st<T>(o + d, 0.0f);
             return;
         }
+        __shared__ float sh[kCombW * (D + 2)];
         if (gqa)
-            combine_wave<T, D>(ws.part + ((size_t)i0 * kGqaMax + (r - r0)) * (D + 2), i1 - i0, o, g.v_scale,
-                               kGqaMax * (D + 2));
+            combine_block<T, D>(ws.part + ((size_t)i0 * kGqaMax + (r - r0)) * (D + 2), i1 - i0, o, g.v_scale,
+                                kGqaMax * (D + 2), sh);
         else
-            combine_wave<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale);
+            combine_block<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale, D + 2, sh);
         return;
     }
     const int bh = blk - rows, b = bh / g.Hq, h = bh - b * g.Hq;
-    if (g.is_ret[h]) return;
+    if (g.is_ret[h] || threadIdx.x >= 64) return;         // a window pair: one wavefront
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
     const int n_all = win_count(g, pos, 0, &ns_end, &w_start);
@@ -891,7 +965,7 @@ hipError_t sparse_dec(const Geo& g, const void* q, const void* k, const void* v,
     const size_t shmem = (sizeof(int64_t) + sizeof(int32_t)) * (rows + 1);
     hipLaunchKernelGGL((k_sparse_dec_part<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g,
                        (const T*)q, (const TKV*)k, (const TKV*)v, row_ptr, idx, status, ws, row0, rows);
-    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, status, ws, (T*)out, row0);
+    hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64 * kCombW), 0, s, g, status, ws, (T*)out, row0);
     return hipGetLastError();
 }
 
@@ -906,10 +980,10 @@ hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void
     hipLaunchKernelGGL((k_sparse_dec_sel<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
                        (const TKV*)k, (const TKV*)v, sw, so, ws, rows);
     if (win && win->items > 0)
-        hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + g.batch * g.Hq), dim3(64), 0, s, g, so.status, ws,
+        hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + g.batch * g.Hq), dim3(64 * kCombW), 0, s, g, so.status, ws,
                            (T*)out, rows, win->part, win->nsplit, win->split_keys, 0);
     else
-        hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64), 0, s, g, so.status, ws, (T*)out, 0);
+        hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64 * kCombW), 0, s, g, so.status, ws, (T*)out, 0);
     return hipGetLastError();
 }
 
@@ -974,7 +1048,7 @@ hipError_t sparse_dec_gqa(const Geo& g, const void* q, const void* k, const void
     hipLaunchKernelGGL((k_sparse_dec_gqa<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
                        (const TKV*)k, (const TKV*)v, so, ws, rows);
     const bool wc = win && win->items > 0;
-    hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + (wc ? g.batch * g.Hq : 0)), dim3(64), 0, s, g,
+    hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + (wc ? g.batch * g.Hq : 0)), dim3(64 * kCombW), 0, s, g,
                        so.status, ws, (T*)out, rows, wc ? win->part : (const float*)nullptr, wc ? win->nsplit : 0,
                        wc ? win->split_keys : 0, 1);
     return hipGetLastError();
