@@ -345,7 +345,7 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     # window on a second stream beside the selection (measured faster there)
     fused_ok = B * w.n_ret <= 128 and not fp8
 
-    def make_step(I, main, fused=True):
+    def make_step(I, main, fused=True, window_first=False):
         sel_args = (layer, I["cache"], I["query"], I["w_q"], I["top_p"], I["sel"], I["ws_sel"])
         append = rtp.indexer_append(layer, I["cache"], I["w_k"], I["sid"], I["pos"], stream=main, prepare=True)
         window = rtp.window_attn(layer, I["cache"], I["query"], I["out"], I["ws_win"], stream=side, prepare=True)
@@ -363,11 +363,16 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
                                         prepare=True)
 
         def run():
+            if window_first:                             # the window beside the whole selection
+                fork.record(main)
+                side.wait_event(fork)
+                window()
             append()
             begin()
-            fork.record(main)
-            side.wait_event(fork)
-            window()
+            if not window_first:                         # the window beside the cut and the sparse attention
+                fork.record(main)
+                side.wait_event(fork)
+                window()
             end()
             sparse()
             join.record(side)
@@ -439,6 +444,19 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     b_.record()
     torch.cuda.synchronize()
     two_call_us = round(a.elapsed_time(b_) / steps * 1e3, 2)
+    window_first_us = None
+    if not fused_ok:
+        # the separate calls with the window forked before the scoring pass
+        runs3 = [make_step(I, main_stream, fused=False, window_first=True) for I in inst]
+        for s in range(warmup):
+            runs3[s % n_i]()
+        torch.cuda.synchronize()
+        a.record()
+        for s in range(steps):
+            runs3[s % n_i]()
+        b_.record()
+        torch.cuda.synchronize()
+        window_first_us = round(a.elapsed_time(b_) / steps * 1e3, 2)
 
     graph_ms = None
     if graph:
@@ -469,6 +487,7 @@ def decode_leg(w, args, instances: int, steps: int, warmup: int, fp8: bool = Fal
     step_bytes = bytes_klow + bytes_sparse + bytes_win
     res = {"workload": w.name + ("_fp8kv" if fp8 else ""), "batch": B, "max_context": L,
            "us_per_step": round(ms * 1e3, 2), "step_us": step_us, "two_call_step_us": two_call_us,
+           "window_first_step_us": window_first_us,
            "per_call_us": per_call,
            "graph_us": round(graph_ms * 1e3, 2) if graph_ms else None,
            "step_algorithmic_bytes": step_bytes,
