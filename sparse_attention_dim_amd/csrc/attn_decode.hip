@@ -795,8 +795,9 @@ __global__ __launch_bounds__(64) void k_sparse_dec_gqa(Geo g, const T* __restric
 }
 
 // The decode step's combine: workgroups [0, rows) merge the retrieval rows'
-// partials (nothing when the selection reported an error), the others the
-// window partials of (sequence, local head) pairs, workgroup rows + b Hq + h.
+// partials on kCombW wavefronts each (nothing when the selection reported an
+// error), the others the window partials of (sequence, local head) pairs, one
+// pair b Hq + h per wavefront, kCombW pairs per workgroup.
 template <typename T, int D>
 __global__ __launch_bounds__(64 * kCombW) void k_dec_combine_all(Geo g, const int32_t* __restrict__ status, AttnWs ws,
                                                         T* __restrict__ out, int rows, const float* __restrict__ wpart,
@@ -823,8 +824,11 @@ __global__ __launch_bounds__(64 * kCombW) void k_dec_combine_all(Geo g, const in
             combine_block<T, D>(ws.part + (size_t)i0 * (D + 2), i1 - i0, o, g.v_scale, D + 2, sh);
         return;
     }
-    const int bh = blk - rows, b = bh / g.Hq, h = bh - b * g.Hq;
-    if (g.is_ret[h] || threadIdx.x >= 64) return;         // a window pair: one wavefront
+    // window pairs (sequence, head): one per wavefront, kCombW per workgroup
+    const int bh = (blk - rows) * kCombW + (int)(threadIdx.x >> 6);
+    if (bh >= g.batch * g.Hq) return;
+    const int b = bh / g.Hq, h = bh - b * g.Hq;
+    if (g.is_ret[h]) return;
     const int pos = seq_len(g, b) - 1;
     int ns_end, w_start;
     const int n_all = win_count(g, pos, 0, &ns_end, &w_start);
@@ -980,7 +984,8 @@ hipError_t sparse_dec_sel(const Geo& g, const void* q, const void* k, const void
     hipLaunchKernelGGL((k_sparse_dec_sel<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
                        (const TKV*)k, (const TKV*)v, sw, so, ws, rows);
     if (win && win->items > 0)
-        hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + g.batch * g.Hq), dim3(64 * kCombW), 0, s, g, so.status, ws,
+        hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + (g.batch * g.Hq + kCombW - 1) / kCombW),
+                           dim3(64 * kCombW), 0, s, g, so.status, ws,
                            (T*)out, rows, win->part, win->nsplit, win->split_keys, 0);
     else
         hipLaunchKernelGGL((k_sparse_dec_combine<T, D>), dim3(rows), dim3(64 * kCombW), 0, s, g, so.status, ws, (T*)out, 0);
@@ -1048,7 +1053,8 @@ hipError_t sparse_dec_gqa(const Geo& g, const void* q, const void* k, const void
     hipLaunchKernelGGL((k_sparse_dec_gqa<T, TKV, D>), dim3((unsigned)grid), dim3(64), shmem, s, g, (const T*)q,
                        (const TKV*)k, (const TKV*)v, so, ws, rows);
     const bool wc = win && win->items > 0;
-    hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + (wc ? g.batch * g.Hq : 0)), dim3(64 * kCombW), 0, s, g,
+    hipLaunchKernelGGL((k_dec_combine_all<T, D>), dim3(rows + (wc ? (g.batch * g.Hq + kCombW - 1) / kCombW : 0)),
+                       dim3(64 * kCombW), 0, s, g,
                        so.status, ws, (T*)out, rows, wc ? win->part : (const float*)nullptr, wc ? win->nsplit : 0,
                        wc ? win->split_keys : 0, 1);
     return hipGetLastError();
