@@ -90,3 +90,28 @@ def test_amplitude_formula():
     s = 0.25
     share = 16 * np.exp(s * a * a) / (16 * np.exp(s * a * a) + 131072 * np.exp(s * s * a * a / 2))
     assert abs(share - 0.999) < 1e-9 and 8.4 < a < 8.6
+
+
+def test_shared_kv_clusters():
+    # grouped retrieval heads share their KV head's planted cluster: the same
+    # size, and the first head's planted keys score high for the second head's
+    # query too; without the option the heads draw independent clusters, and the
+    # option leaves every other draw (and the ungrouped heads) unchanged
+    kw = dict(seed=41, lens=(5000, 7000), Hq=32, Hkv=8, D=128, n_ret=3, p=0.9, window=256, sinks=8,
+              rope=1e4, size_dist=("loguniform", 64, 256), ret_heads=[4, 5, 20])
+    a = synth.cluster_decode(shared_kv=True, **kw)
+    b = synth.cluster_decode(shared_kv=False, **kw)
+    for bq in range(2):
+        assert a.info["sizes"][(bq, 4)] == a.info["sizes"][(bq, 5)]
+        assert a.info["sizes"][(bq, 20)] == b.info["sizes"][(bq, 20)]
+    np.testing.assert_array_equal(a.k[0][:, 5, :], b.k[0][:, 5, :])      # KV head 5 (head 20) untouched
+    np.testing.assert_array_equal(a.q[:, 4], b.q[:, 4])                  # the group's first head as before
+    assert not np.array_equal(a.q[:, 5], b.q[:, 5])                      # the second head follows the shared cluster
+    # head 5's query, projected on the planted low-frequency coordinates,
+    # points along head 4's: both were planted along the same direction
+    dims = synth.low_freq_dims(128)
+    for bq in range(2):
+        u4 = synth.as_f32(a.q[bq, 4])[dims]
+        u5 = synth.as_f32(a.q[bq, 5])[dims]
+        cos = float(u4 @ u5 / np.linalg.norm(u4) / np.linalg.norm(u5))
+        assert cos > 0.9, cos
