@@ -15,24 +15,27 @@
 //            row forms it while its first indexer-key loads are in flight),
 //            fp32 chain scores of every key of a chunk, the chunk maximum m_c,
 //            the chunk's cumulative mass histogram (exact fixed-point weights
-//            exp(s (d - m_c)) summed over bins of x_c = s (m_c - d), 1/4 wide)
-//            and the chunk's candidate list: its keys in the lowest bins, up to
-//            kNc of them, in index order
+//            exp(s (d - m_c)) summed over bins of x_c = s (m_c - d), 1/4 wide),
+//            a bit per key flagging the lowest kLowBin + 1 bins, and the
+//            chunk's list of those flagged keys (score key and index, index
+//            order, the first kFl of them)
 //   row:     one workgroup per row.  Row maximum m and total mass
 //            Z = sum_c exp(s (m_c - m)) Z_c; every chunk bin whose upper edge
 //            lies below a threshold X on the row's x axis certainly holds
 //            keys with x < X, which gives a lower bound of the mass above
 //            any X.  The smallest X whose bound reaches the target fixes the
 //            candidate set U = {d >= m - X / s}: it holds every key ranked at
-//            or above the cut.  U is taken from the chunks' candidate lists
-//            when they hold it (else from the row's scores) into LDS, and the
+//            or above the cut.  U is taken from the chunks' flagged-key lists
+//            when they hold it (else from the key flags and the stored
+//            scores, or from the row's scores formed again) into LDS, and the
 //            cut is found by radix selection over its score keys with exact
 //            masses per bucket (ties: lowest indices first); when U does not
 //            fit the workspace list the same selection runs over the row's
 //            scores.  U is gathered in index order, so the selected keys are
 //            its filter.
 //   emit:    CSR row pointers, the capacity check, and the selected indices
-//            of every row
+//            of every row (the one-call decode step writes them from its
+//            sparse attention items instead)
 // Workgroups of one pass never wait on each other: every hand-off between
 // workgroups is a kernel boundary (a device-scope fence per workgroup costs an
 // L2 write-back and invalidate on this multi-XCD part).
