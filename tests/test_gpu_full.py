@@ -190,6 +190,51 @@ def test_full_decode_bf16_128k():
     _decode_case(2, [0, 3, 7])
 
 
+def test_full_decode_bf16_128k_gqa_shared():
+    # the shared gathers at the 128K decode shapes, with the grouped heads
+    # sharing their planted cluster (overlapping sets): every row's set and
+    # attention against the oracle, the CSR identical to the call without the
+    # flag, the local heads bit-identical
+    w = synth.cluster_decode(seed=1002, shared_kv=True, name="decode_bf16_B8_L131072_shared_clusters")
+    say("[gpu-full] %s: B=%d L=%d, RTP_FLAG_GQA_SHARED" % (w.name, w.B, int(w.seq_lens.max())))
+    d = Dev(w, permute_seed=5)
+    cap = int(sum(int(l) for l in w.seq_lens) * w.n_ret)
+
+    def call(flags):
+        lay = rtp.make_layer(w.Hq, w.Hkv, w.D, rtp.RTP_BF16, w.ret_heads, w.window, w.sinks, w.attn_scale,
+                             w.idx_scale, flags=flags)
+        row_ptr = torch.zeros(d.rows + 1, dtype=torch.int64, device="cuda")
+        idx = torch.full((cap,), -1, dtype=torch.int32, device="cuda")
+        status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+        sel = rtp.make_sel(row_ptr, idx, status)
+        out = torch.zeros_like(d.q)
+        ws = torch.empty(rtp.decode_attn_workspace(lay, d.cache, d.query, cap), dtype=torch.uint8, device="cuda")
+        rtp.decode_attn(lay, d.cache, d.query, d.w_q, d.top_p, sel, out, ws)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        return row_ptr.cpu().numpy(), idx.cpu().numpy(), out
+
+    rp, ix, out = call(rtp.RTP_FLAG_GQA_SHARED)
+    rp0, ix0, out0 = call(0)
+    np.testing.assert_array_equal(rp, rp0)
+    np.testing.assert_array_equal(ix[: rp[-1]], ix0[: rp[-1]])
+    loc = w.local_heads()
+    assert torch.equal(out[:, loc], out0[:, loc])
+    sets = [ix[rp[i]: rp[i + 1]] for i in range(d.rows)]
+    rows = [(t, r) for t in range(w.n_tok) for r in range(w.n_ret)]
+    _check_rows(w, d, rows, sets, out_f32(out), {})
+    shared = 0
+    for t in range(w.n_tok):
+        for r in range(w.n_ret):
+            for r2 in range(r + 1, w.n_ret):
+                if w.kv_head(w.ret_heads[r]) == w.kv_head(w.ret_heads[r2]):
+                    shared += len(np.intersect1d(sets[t * w.n_ret + r], sets[t * w.n_ret + r2]))
+    say("   keys selected by two retrieval heads of one KV head:", shared, "of", int(rp[-1]))
+    assert shared > 0
+    del d
+    _free()
+
+
 def test_full_decode_bf16_ragged():
     lens = synth.ragged_lens(1005, 64, 32768, 524288)
     order = np.argsort(lens)
