@@ -88,6 +88,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError("librtp.so is not built (%s); run __graft_entry__.build()" % path)
+    # PyTorch (the memory and stream provider) first, so that the library
+    # binds to the HIP runtime torch has loaded: a second runtime loaded ahead
+    # of it would not see the device memory torch hands out
+    import torch  # noqa: F401
     L = ctypes.CDLL(path)
     P, S, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
     pl, pc, pq, ps = (ctypes.POINTER(Layer), ctypes.POINTER(Cache), ctypes.POINTER(Query),

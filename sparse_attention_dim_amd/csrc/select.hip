@@ -894,12 +894,14 @@ __device__ __forceinline__ void resolve_body(const Geo& g, const RowInfo& ri, co
     }
 }
 
-// The fixed-order chain scores of every key of chunk c of a row, formed again
-// from the indexer keys (q_low from the scoring pass) into the row's score
-// array: the scoring pass stores only the keys it flags.  kRT threads, 8
-// keys per thread, every load in flight before the first is used.
-__device__ __forceinline__ void rescore_chunk(const Geo& g, const RowInfo& ri, const SelWs& ws, const bf16_t* __restrict__ k_low,
-                              const int32_t* btc, bool bt_cached, int c) {
+// The fixed-order chain scores of every key of chunks ca and cb (cb < 0: ca
+// only) of a row, formed again from the indexer keys (q_low from the scoring
+// pass) into the row's score array: the scoring pass stores only the keys it
+// flags.  kRT threads, 8 keys per thread and chunk; both chunks' loads are in
+// flight before the first is used.
+__device__ __forceinline__ void rescore_chunks(const Geo& g, const RowInfo& ri, const SelWs& ws,
+                                               const bf16_t* __restrict__ k_low, const int32_t* btc, bool bt_cached,
+                                               int ca, int cb) {
     const int tid = threadIdx.x;
     float qv[kIdx];
 #pragma unroll
@@ -907,25 +909,35 @@ __device__ __forceinline__ void rescore_chunk(const Geo& g, const RowInfo& ri, c
     float* srow = ws.scores + (size_t)ri.lrow * ws.score_ld;
     const int32_t* bt = g.block_table + (size_t)ri.b * g.max_blocks;
     constexpr int K = kChunk / kRT;
-    uint4 kb[K][2];
+    uint4 kb[2][K][2];
 #pragma unroll
-    for (int x = 0; x < K; ++x) {
-        const int j = min(c * kChunk + tid + kRT * x, ri.L - 1);
-        const int page = bt_cached ? btc[j >> 8] : bt[j >> 8];
-        const uint4* kp = reinterpret_cast<const uint4*>(k_low + (((size_t)page * g.n_ret + ri.r) * kBlk + (j & 255)) * kIdx);
-        kb[x][0] = kp[0];
-        kb[x][1] = kp[1];
+    for (int h = 0; h < 2; ++h) {
+        const int c = h == 0 || cb < 0 ? ca : cb;
+#pragma unroll
+        for (int x = 0; x < K; ++x) {
+            const int j = min(c * kChunk + tid + kRT * x, ri.L - 1);
+            const int page = bt_cached ? btc[j >> 8] : bt[j >> 8];
+            const uint4* kp =
+                reinterpret_cast<const uint4*>(k_low + (((size_t)page * g.n_ret + ri.r) * kBlk + (j & 255)) * kIdx);
+            kb[h][x][0] = kp[0];
+            kb[h][x][1] = kp[1];
+        }
     }
 #pragma unroll
-    for (int x = 0; x < K; ++x) {
-        const int j = c * kChunk + tid + kRT * x;
-        float kf[kIdx];
-        unpack8(kb[x][0], kf);
-        unpack8(kb[x][1], kf + 8);
-        float acc = 0.0f;
+    for (int h = 0; h < 2; ++h) {
+        if (h == 1 && cb < 0) break;
+        const int c = h == 0 ? ca : cb;
 #pragma unroll
-        for (int i = 0; i < kIdx; ++i) acc = __builtin_fmaf(qv[i], kf[i], acc);
-        if (j < ri.L) srow[j] = acc;
+        for (int x = 0; x < K; ++x) {
+            const int j = c * kChunk + tid + kRT * x;
+            float kf[kIdx];
+            unpack8(kb[h][x][0], kf);
+            unpack8(kb[h][x][1], kf + 8);
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kIdx; ++i) acc = __builtin_fmaf(qv[i], kf[i], acc);
+            if (j < ri.L) srow[j] = acc;
+        }
     }
 }
 
@@ -1219,8 +1231,17 @@ __device__ __forceinline__ void row_pass(const Geo& g, const float* __restrict__
         // only the flagged keys', or every key's under a fixed top-k)
         const bool whole = nU > (unsigned long long)ws.ucap;
         if (g.sel_k <= 0) {
+            int pend = -1;                                // chunks taken in pairs
             for (int c = 0; c < ri.nch; ++c)
-                if (whole || sm.plan.bsel[c] >= 0) rescore_chunk(g, ri, ws, k_low, sm.btc, bt_cached, c);
+                if (whole || sm.plan.bsel[c] >= 0) {
+                    if (pend < 0) {
+                        pend = c;
+                    } else {
+                        rescore_chunks(g, ri, ws, k_low, sm.btc, bt_cached, pend, c);
+                        pend = -1;
+                    }
+                }
+            if (pend >= 0) rescore_chunks(g, ri, ws, k_low, sm.btc, bt_cached, pend, -1);
             __syncthreads();
         }
     }
