@@ -3,7 +3,8 @@ benchmark uses, on sampled rows the oracle computes one by one:
 
   decode fp32 L=4096 (every row), decode bf16 B=8 L=131072, decode bf16 B=64
   ragged 32K..512K, prefill chunk 4096 at L=131072, prefill chunk 8192 at
-  L=1048576.
+  L=1048576; and decode bf16 B=21 L=131072, whose seed sends one row's
+  candidate set past the keys the scoring pass flags (the from-scores route).
 
 Sampled rows cover the first/last sequence and row, the longest and shortest
 contexts, and a seeded random choice.  The same acceptance rules as the small
@@ -231,6 +232,51 @@ def test_full_decode_bf16_128k_gqa_shared():
                     shared += len(np.intersect1d(sets[t * w.n_ret + r], sets[t * w.n_ret + r2]))
     say("   keys selected by two retrieval heads of one KV head:", shared, "of", int(rp[-1]))
     assert shared > 0
+    del d
+    _free()
+
+
+def test_full_decode_bf16_128k_from_scores():
+    # 21 sequences of 131072 keys (126 rows, the one-call step): with this
+    # seed one row's candidate set reaches past the keys the scoring pass
+    # flags in a chunk, so its row pass re-scores the chunks and gathers U
+    # from the row's scores; that row and a sample of the others against the
+    # oracle, the one-call step identical to the separate calls
+    w = synth.cluster_decode(seed=3021, lens=(131072,) * 21, name="decode_bf16_B21_L131072")
+    say("[gpu-full] %s: B=%d L=%d" % (w.name, w.B, int(w.seq_lens.max())))
+    d = Dev(w, permute_seed=5)
+    cap = int(sum(int(l) for l in w.seq_lens) * w.n_ret)
+    say("[gpu-full] %s: select" % w.name)
+    st, rp, sets, paths = d.select_mode(capacity=cap)
+    assert st == 0
+    pc = path_counts(paths)
+    say("   paths of the rows", pc)
+    fs = [int(i) for i in np.flatnonzero((paths & 256) != 0)]
+    assert len(fs) >= 1
+    say("[gpu-full] %s: sparse + window" % w.name)
+    d.out.zero_()
+    d.sparse()
+    d.window()
+    out = out_f32(d.out)
+    g = np.random.default_rng(21)
+    pick = set(fs) | {0, d.rows - 1} | {int(i) for i in g.choice(d.rows, 14, replace=False)}
+    rows = [(i // w.n_ret, i % w.n_ret) for i in sorted(pick)]
+    _check_rows(w, d, rows, sets, out, {})
+    say("   oracle-checked rows: %d (from-scores rows %s)" % (len(rows), fs))
+    say("[gpu-full] %s: rtp_decode_attn" % w.name)
+    row_ptr = torch.zeros(d.rows + 1, dtype=torch.int64, device="cuda")
+    idx = torch.full((cap,), -1, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    sel = rtp.make_sel(row_ptr, idx, status)
+    fout = torch.zeros_like(d.q)
+    ws = torch.empty(rtp.decode_attn_workspace(d.layer, d.cache, d.query, cap), dtype=torch.uint8, device="cuda")
+    rtp.decode_attn(d.layer, d.cache, d.query, d.w_q, d.top_p, sel, fout, ws)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    np.testing.assert_array_equal(row_ptr.cpu().numpy(), rp)
+    n = int(rp[-1])
+    np.testing.assert_array_equal(idx[:n].cpu().numpy(), d.idx[:n].cpu().numpy())
+    assert torch.equal(fout, d.out), "rtp_decode_attn outputs differ from the separate calls"
     del d
     _free()
 
